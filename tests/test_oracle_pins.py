@@ -1,0 +1,345 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle against something the paper prints (fixtures under tests/golden/),
+a closed form, an invariant, a library routine or a brute-force evaluation by a different route,
+chosen so that a plausible slip in the oracle (a dropped term, a wrong sign, index or bit order,
+a transposed operand) fails at least one of them.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import dfssm_oracle as O
+from synth import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _tiny_dims(**kw):
+    base = dict(d_model=64, d_inner=128, d_state=8, headdim=32, ngroups=1, d_conv=4,
+                n_in_proj=2 * 128 + 2 * 8 + 4, rank_in=4, rank_out=4)
+    base.update(kw)
+    return gen.Dims(**base)
+
+
+# ------------------------------------------------------------------ packing
+def test_unpack_matches_pure_python_bit_extraction():
+    rng = np.random.default_rng(1)
+    packed = rng.integers(0, 256, size=(5, 4), dtype=np.uint8)
+    dense = O.unpack_signs(packed, 32)
+    for n in range(5):
+        for k in range(32):
+            bit = (int(packed[n, k // 8]) >> (k % 8)) & 1
+            assert dense[n, k] == (1 if bit else -1)
+
+
+def test_packing_is_64bit_little_endian_words():
+    fx = _golden("avx512_packing.json")
+    K = fx["row_elements"]
+    assert K // fx["weights_per_load"] == fx["instructions_per_row"]
+    rng = np.random.default_rng(2)
+    words = rng.integers(0, 2**63, size=K // 64, dtype=np.uint64)
+    row = words.astype("<u8").view(np.uint8)[None, :]          # bytes of LE 64-bit words
+    assert row.shape[1] == (K // fx["weights_per_load"]) * fx["bytes_per_load"]
+    dense = O.unpack_signs(row, K)[0]
+    for k in range(0, K, 37):
+        bit = (int(words[k // 64]) >> (k % 64)) & 1
+        assert dense[k] == (1 if bit else -1)
+
+
+# ------------------------------------------------------------------ Table 1 byte model
+def test_table1_scaffold_and_lora_sizes():
+    fx = _golden("table1_model_size.json")
+    sh = _golden("model_shape_facts.json")
+    d = gen.DIMS["1p3b"]
+    assert d.d_model == sh["d_model"] and d.d_state == sh["d_state"]
+    b = O.table1_bytes(d.d_model, d.d_inner, d.n_in_proj, fx["n_layers"], fx["lora_rank"])
+    # 1 bit per scaffold weight reproduces the printed 155 MB
+    assert round(b["scaffold"] / 1e6) == fx["scaffold_MB"]
+    # the printed LoRA size is given to the MB
+    assert abs(b["lora"] / 1e6 - fx["lora_MB"]) < 1.0
+    # a 2-bit scaffold or a missing in_proj block does not
+    assert round(2 * b["scaffold"] / 1e6) != fx["scaffold_MB"]
+    b2 = O.table1_bytes(d.d_model, d.d_inner, 2 * d.d_inner, fx["n_layers"], fx["lora_rank"])
+    assert round(b2["scaffold"] / 1e6) != fx["scaffold_MB"]
+    # the fixed state: d_inner * d_state = 524,288 values ("524 KB")
+    assert round(d.nheads * d.headdim * d.d_state / 1000) == sh["ssm_state_KB"]
+    assert fx["scaffold_MB"] + fx["embedding_MB"] + fx["lora_MB"] + fx["other_MB"] == fx["total_MB"]
+
+
+# ------------------------------------------------------------------ quantizer
+def test_quantizer_ties_round_to_even_and_amax_maps_to_127():
+    u = np.array([127.0, 0.5, 1.5, 2.5, -0.5, -2.5, 3.5, -126.5], np.float32)
+    q, s = O.quantize_token(u)          # a = 127 -> inv = 1 exactly
+    assert q.tolist() == [127, 0, 2, 2, 0, -2, 4, -126]
+    assert s == np.float32(1.0)
+    # Python's round() is also half-to-even: same codes by a different routine
+    assert q.tolist() == [round(float(v)) for v in u]
+
+
+def test_quantizer_zero_symmetry_and_error_bound():
+    q, s = O.quantize_token(np.zeros(16, np.float32))
+    assert not q.any() and s == 0
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        u = (rng.standard_normal(257) * rng.uniform(1e-3, 1e3)).astype(np.float32)
+        q, s = O.quantize_token(u)
+        qn, sn = O.quantize_token(-u)
+        assert (qn == -q).all() and sn == s
+        i = np.argmax(np.abs(u))
+        assert abs(int(q[i])) == 127 and np.sign(q[i]) == np.sign(u[i])
+        assert np.abs(q.astype(int)).max() <= 127
+        # dequantized values are within half a step of the input
+        err = np.abs(u.astype(np.float64) - float(s) * q.astype(np.float64))
+        assert err.max() <= float(s) * (0.5 + 1e-4)
+
+
+# ------------------------------------------------------------------ projection
+def _proj(n_out, n_in, rank, seed, per_channel=True):
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 256, size=(n_out, n_in // 8), dtype=np.uint8)
+    return gen.ProjWeights(
+        sign=sign,
+        row_scale=rng.uniform(0.01, 0.05, n_out).astype(np.float16),
+        lora_dn=rng.integers(-127, 128, size=(rank, n_in)).astype(np.int8),
+        dn_scale=(rng.uniform(0.5, 1.5, rank) * 1e-3).astype(np.float32) if per_channel else np.full(rank, 1e-3, np.float32),
+        lora_up=rng.integers(-127, 128, size=(n_out, rank)).astype(np.int8),
+        up_scale=(rng.uniform(0.5, 1.5, n_out) * 1e-3).astype(np.float32) if per_channel else np.full(n_out, 1e-3, np.float32),
+    )
+
+
+def test_project_brute_force_exact():
+    P = _proj(6, 16, 3, seed=4)
+    rng = np.random.default_rng(5)
+    q = rng.integers(-127, 128, 16).astype(np.int8)
+    s = np.float32(0.0371)
+    y, acc, t = O.project(q, s, P)
+    for n in range(6):
+        a = 0
+        for k in range(16):
+            bit = (int(P.sign[n, k // 8]) >> (k % 8)) & 1
+            a += int(q[k]) if bit else -int(q[k])
+        assert acc[n] == a
+    tt = [sum(int(P.lora_dn[j, k]) * int(q[k]) for k in range(16)) for j in range(3)]
+    assert t.tolist() == tt
+    S = Fraction(float(s))
+    for n in range(6):
+        exact = S * Fraction(float(P.row_scale[n])) * acc[n]
+        for j in range(3):
+            exact += (Fraction(float(P.up_scale[n])) * int(P.lora_up[n, j])
+                      * Fraction(float(P.dn_scale[j])) * S * tt[j])
+        assert abs(float(exact) - y[n]) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def test_project_equals_dense_effective_matrix():
+    # Eq. (3) as one dense matrix: W = diag(sc) sgn + diag(us) L_up diag(ds) L_dn, applied to s*q
+    P = _proj(40, 64, 5, seed=6)
+    rng = np.random.default_rng(7)
+    q = rng.integers(-127, 128, 64).astype(np.int8)
+    s = np.float32(0.021)
+    y, _, _ = O.project(q, s, P)
+    bits = np.array([[(int(P.sign[n, k // 8]) >> (k % 8)) & 1 for k in range(64)] for n in range(40)])
+    W = (P.row_scale.astype(np.float64)[:, None] * (2.0 * bits - 1.0)
+         + (P.up_scale.astype(np.float64)[:, None] * P.lora_up.astype(np.float64))
+         @ (P.dn_scale.astype(np.float64)[:, None] * P.lora_dn.astype(np.float64)))
+    np.testing.assert_allclose(y, W @ (float(s) * q.astype(np.float64)), rtol=1e-12, atol=1e-12)
+
+
+def test_project_complement_parity_and_bounds():
+    P = _proj(8, 64, 2, seed=8)
+    rng = np.random.default_rng(9)
+    q = rng.integers(-127, 128, 64).astype(np.int8)
+    _, acc, _ = O.project(q, np.float32(1), P)
+    Pc = gen.ProjWeights(~P.sign, P.row_scale, P.lora_dn, P.dn_scale, P.lora_up, P.up_scale)
+    _, accc, _ = O.project(q, np.float32(1), Pc)
+    assert (accc == -acc).all()
+    assert ((acc - int(q.astype(int).sum())) % 2 == 0).all()
+    assert np.abs(acc).max() <= 64 * 127
+    ones = gen.ProjWeights(np.full_like(P.sign, 255), P.row_scale, P.lora_dn, P.dn_scale, P.lora_up, P.up_scale)
+    _, acc1, _ = O.project(q, np.float32(1), ones)
+    assert (acc1 == int(q.astype(int).sum())).all()
+
+
+# ------------------------------------------------------------------ conv
+def test_conv_matches_numpy_convolve_and_first_step():
+    rng = np.random.default_rng(10)
+    C, T = 7, 12
+    w = rng.uniform(-0.5, 0.5, (C, 4))
+    b = rng.uniform(-0.5, 0.5, C)
+    xs = rng.standard_normal((T, C))
+    st = np.zeros((C, 3))
+    outs = []
+    for t in range(T):
+        o, st = O.conv_step(st, xs[t], w, b)
+        outs.append(o)
+    outs = np.array(outs)
+    for c in range(C):
+        v = np.convolve(xs[:, c], w[c, ::-1])[:T] + b[c]
+        np.testing.assert_allclose(outs[:, c], v / (1 + np.exp(-v)), rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(st, xs[-3:].T)
+    o0, _ = O.conv_step(np.zeros((C, 3)), xs[0], w, b)
+    v0 = w[:, 3] * xs[0] + b
+    np.testing.assert_allclose(o0, v0 / (1 + np.exp(-v0)), rtol=1e-14)
+
+
+# ------------------------------------------------------------------ ssm
+def _ssm_inputs(H=4, P=3, N=5, G=1, seed=11):
+    rng = np.random.default_rng(seed)
+    return dict(S=rng.standard_normal((H, P, N)) * 0.3, x=rng.standard_normal(H * P),
+                Bm=rng.standard_normal((G, N)), Cm=rng.standard_normal((G, N)),
+                dt=rng.uniform(1e-3, 0.1, H), A=-rng.uniform(1, 16, H), D=rng.standard_normal(H))
+
+
+def test_ssm_closed_forms():
+    d = _ssm_inputs()
+    H, P, N = d["S"].shape
+    # B = 0 from zero state: y = D x, state stays exactly zero
+    y, S = O.ssm_step(np.zeros_like(d["S"]), d["x"], np.zeros_like(d["Bm"]), d["Cm"], d["dt"], d["A"], d["D"], 1)
+    assert not S.any()
+    np.testing.assert_array_equal(y, np.repeat(d["D"], P) * d["x"])
+    # dt = 0: the state is unchanged bit for bit, y = C.S + D x
+    y, S = O.ssm_step(d["S"], d["x"], d["Bm"], d["Cm"], np.zeros(H), d["A"], d["D"], 1)
+    np.testing.assert_array_equal(S, d["S"])
+    # one step from zero: y = dt (C.B) x + D x   (x is scaled by dt: App. B Table 12, row 1)
+    y, S = O.ssm_step(np.zeros_like(d["S"]), d["x"], d["Bm"], d["Cm"], d["dt"], d["A"], d["D"], 1)
+    cb = float(d["Cm"][0] @ d["Bm"][0])
+    np.testing.assert_allclose(y, np.repeat(d["dt"], P) * cb * d["x"] + np.repeat(d["D"], P) * d["x"], rtol=1e-12)
+    # A -> -inf: memoryless, the old state is forgotten
+    y1, _ = O.ssm_step(d["S"], d["x"], d["Bm"], d["Cm"], d["dt"], np.full(H, -1e300), d["D"], 1)
+    y2, _ = O.ssm_step(np.zeros_like(d["S"]), d["x"], d["Bm"], d["Cm"], d["dt"], np.full(H, -1e300), d["D"], 1)
+    np.testing.assert_allclose(y1, y2, rtol=1e-12)
+
+
+def test_ssm_group_mapping():
+    d = _ssm_inputs(H=4, G=2)
+    Bm = d["Bm"].copy()
+    Bm[1] = 0.0                                   # heads 2 and 3 read group 1
+    y, S = O.ssm_step(np.zeros_like(d["S"]), d["x"], Bm, d["Cm"], d["dt"], d["A"], d["D"], 2)
+    P = d["S"].shape[1]
+    assert not S[2:].any() and S[:2].any()
+    np.testing.assert_array_equal(y[2 * P:], np.repeat(d["D"][2:], P) * d["x"][2 * P:])
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_ssd_chunked_equals_sequential(G):
+    rng = np.random.default_rng(12)
+    T, H, P, N = 100, 4, 3, 6
+    xs = rng.standard_normal((T, H, P))
+    dts = rng.uniform(1e-3, 0.2, (T, H))
+    A = -rng.uniform(1, 16, H)
+    Bs, Cs = rng.standard_normal((T, G, N)), rng.standard_normal((T, G, N))
+    D = rng.standard_normal(H)
+    S0 = rng.standard_normal((H, P, N)) * 0.5
+    ys, ST = O.ssm_scan_sequential(xs, dts, A, Bs, Cs, D, S0, G)
+    for Q in (1, 3, 16, 64, 100, 256):
+        yc, SC = O.ssd_chunked(xs, dts, A, Bs, Cs, D, S0, G, Q)
+        np.testing.assert_allclose(yc, ys, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(SC, ST, rtol=1e-10, atol=1e-12)
+
+
+def test_ssd_quadratic_form_equals_sequential():
+    rng = np.random.default_rng(13)
+    T, H, P, N, G = 40, 2, 3, 4, 1
+    xs = rng.standard_normal((T, H, P))
+    dts = rng.uniform(1e-3, 0.3, (T, H))
+    A = -rng.uniform(1, 16, H)
+    Bs, Cs = rng.standard_normal((T, G, N)), rng.standard_normal((T, G, N))
+    D = rng.standard_normal(H)
+    ys, _ = O.ssm_scan_sequential(xs, dts, A, Bs, Cs, D, np.zeros((H, P, N)), G)
+    yq = O.ssd_quadratic(xs, dts, A, Bs, Cs, D, G)
+    np.testing.assert_allclose(yq, ys, rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------------------------ norms
+def test_gated_norm_order_and_rmsnorm_closed_form():
+    rng = np.random.default_rng(14)
+    y = rng.standard_normal(64)
+    w = rng.uniform(0.5, 1.5, 64)
+    z0 = 3.0
+    c = z0 / (1 + np.exp(-z0))
+    out, _ = O.gated_rmsnorm(y, np.full(64, z0), w, 1e-5)
+    # gate first: a constant gate c only rescales eps, norm(c y) = norm_{eps/c^2}(y)
+    np.testing.assert_allclose(out, O.rmsnorm(y, w, 1e-5 / c ** 2), rtol=1e-13)
+    assert not np.allclose(out, c * O.rmsnorm(y, w, 1e-5), rtol=1e-3)
+    h = np.full(32, 0.7)
+    np.testing.assert_allclose(O.rmsnorm(h, np.ones(32), 1e-5), 0.7 / np.sqrt(0.49 + 1e-5), rtol=1e-14)
+
+
+# ------------------------------------------------------------------ layer
+def _zero_z_rows(W):
+    E = W.dims.d_inner
+    W.in_proj.row_scale[:E] = 0
+    W.in_proj.up_scale[:E] = 0
+    return W
+
+
+def test_layer_zero_gate_is_identity():
+    dm = _tiny_dims()
+    W = _zero_z_rows(gen.layer_weights(dm, 0, 21, random_norms=True, per_channel_lora=True))
+    cs, ss = gen.initial_states(dm, 1, 0, 21, std=0.3)
+    h = gen.token_inputs(dm, (1,), 21)[0]
+    h_out, _, ss2, tp = O.layer_decode(h, W, cs[0], ss[0])
+    assert not tp.out_q.any() and tp.out_s == 0
+    np.testing.assert_array_equal(h_out, h.astype(np.float64))
+
+
+def test_layer_dt_to_zero_keeps_state():
+    dm = _tiny_dims()
+    W = gen.layer_weights(dm, 0, 22)
+    W.dt_bias[:] = -100.0
+    cs, ss = gen.initial_states(dm, 1, 0, 22, std=0.3)
+    h = gen.token_inputs(dm, (1,), 22)[0]
+    _, _, ss2, _ = O.layer_decode(h, W, cs[0], ss[0])
+    np.testing.assert_array_equal(ss2, ss[0].astype(np.float64))
+
+
+def test_layer_B_zero_gives_Dx_and_zero_state():
+    dm = _tiny_dims()
+    W = gen.layer_weights(dm, 0, 23)
+    E, N = dm.d_inner, dm.d_state
+    rows = slice(2 * E, 2 * E + N)             # B rows of in_proj: after z (E) and x (E)
+    W.in_proj.row_scale[rows] = 0
+    W.in_proj.up_scale[rows] = 0
+    W.conv_b[E:E + N] = 0                       # conv channels of B
+    cs, ss = gen.initial_states(dm, 1)
+    h = gen.token_inputs(dm, (1,), 23)[0]
+    _, _, ss2, _ = O.layer_decode(h, W, cs[0], ss[0])
+    assert not ss2.any()
+
+
+def test_layer_forced_codes_reproduce_free_run_and_state_handoff():
+    dm = _tiny_dims()
+    W = gen.layer_weights(dm, 0, 24, random_norms=True)
+    cs, ss = gen.initial_states(dm, 1)
+    xs = gen.token_inputs(dm, (9,), 24)
+    o_all, cs_all, ss_all, taps = O.layer_decode_steps(xs, W, cs[0], ss[0])
+    o_a, cs_a, ss_a, _ = O.layer_prefill(xs[:4], W, cs[0], ss[0])
+    o_b, cs_b, ss_b, _ = O.layer_decode_steps(xs[4:], W, cs_a, ss_a)
+    np.testing.assert_array_equal(np.concatenate([o_a, o_b]), o_all)
+    np.testing.assert_array_equal(ss_b, ss_all)
+    np.testing.assert_array_equal(cs_b, cs_all)
+    # forcing the oracle's own codes changes nothing
+    t0 = taps[0]
+    o_f, _, _, _ = O.layer_decode(xs[0], W, cs[0], ss[0],
+                                  force=dict(in_q=t0.in_q, in_s=t0.in_s, out_q=t0.out_q, out_s=t0.out_s))
+    np.testing.assert_array_equal(o_f, o_all[0])
+
+
+def test_stack_feedback_is_normalised():
+    dm = _tiny_dims()
+    layers = gen.stack_weights(dm, 2, seed=25)
+    states = [gen.initial_states(dm, 1, l) for l in range(2)]
+    x0 = gen.token_inputs(dm, (1,), 25)[0]
+    ys, _, _ = O.stack_decode(x0, layers, [s[0][0] for s in states], [s[1][0] for s in states],
+                              3, np.ones(dm.d_model), dm.eps)
+    rms = np.sqrt(np.mean(ys ** 2, axis=1))
+    np.testing.assert_allclose(rms, 1.0, rtol=1e-4)
+    assert not np.allclose(ys[0], ys[1])
