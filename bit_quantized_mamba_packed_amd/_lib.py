@@ -1,0 +1,129 @@
+"""ctypes binding of libdfssm.so: the C structs of include/dfssm.h and the exported functions,
+under the same names. Argument marshalling only: every step of the computation runs in the
+HIP library. Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdfssm.so")
+
+DFSSM_OK = 0
+DFSSM_EINVAL = -1
+DFSSM_EUNSUPPORTED = -2
+DFSSM_EWORKSPACE = -3
+DFSSM_EHIP = -4
+
+DFSSM_OP_LAYER_DECODE = 0
+DFSSM_OP_LAYER_PREFILL = 1
+DFSSM_OP_STACK_DECODE = 2
+
+DFSSM_F32 = 0
+DFSSM_BF16 = 1
+
+# every symbol include/dfssm.h declares
+EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_prefill",
+           "dfssm_stack_decode", "dfssm_strerror")
+
+
+class dfssm_dims(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("d_inner", C.c_int32), ("d_state", C.c_int32),
+                ("headdim", C.c_int32), ("ngroups", C.c_int32), ("d_conv", C.c_int32),
+                ("n_in_proj", C.c_int32), ("rank_in", C.c_int32), ("rank_out", C.c_int32),
+                ("norm_eps", C.c_float)]
+
+
+class dfssm_proj(C.Structure):
+    _fields_ = [("sign", C.c_void_p), ("row_scale", C.c_void_p), ("lora_dn", C.c_void_p),
+                ("lora_dn_scale", C.c_void_p), ("lora_up", C.c_void_p), ("lora_up_scale", C.c_void_p)]
+
+
+class dfssm_layer_weights(C.Structure):
+    _fields_ = [("in_proj", dfssm_proj), ("out_proj", dfssm_proj),
+                ("conv_w", C.c_void_p), ("conv_b", C.c_void_p),
+                ("dt_bias", C.c_void_p), ("A_log", C.c_void_p), ("D", C.c_void_p),
+                ("norm_w", C.c_void_p), ("gnorm_w", C.c_void_p)]
+
+
+class dfssm_layer_state(C.Structure):
+    _fields_ = [("conv", C.c_void_p), ("ssm", C.c_void_p)]
+
+
+class dfssm_taps(C.Structure):
+    _fields_ = [("h_in", C.c_void_p),
+                ("in_u", C.c_void_p), ("in_q", C.c_void_p), ("in_s", C.c_void_p),
+                ("in_acc", C.c_void_p), ("in_t", C.c_void_p),
+                ("out_u", C.c_void_p), ("out_q", C.c_void_p), ("out_s", C.c_void_p),
+                ("out_acc", C.c_void_p), ("out_t", C.c_void_p)]
+
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load libdfssm.so once; raises if it is missing (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m bit_quantized_mamba_packed_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    P = C.c_void_p
+    lib.dfssm_workspace_bytes.argtypes = [C.POINTER(dfssm_dims), C.c_int32, C.c_int32, C.c_int32, C.c_int32]
+    lib.dfssm_workspace_bytes.restype = C.c_size_t
+    lib.dfssm_layer_decode.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
+                                       C.POINTER(dfssm_layer_state), P, P, C.c_int32, P, C.c_size_t,
+                                       C.POINTER(dfssm_taps), P]
+    lib.dfssm_layer_decode.restype = C.c_int
+    lib.dfssm_layer_prefill.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
+                                        C.POINTER(dfssm_layer_state), P, C.c_int32, P, C.c_int32,
+                                        C.c_int32, C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
+    lib.dfssm_layer_prefill.restype = C.c_int
+    lib.dfssm_stack_decode.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
+                                       C.POINTER(dfssm_layer_state), C.c_int32, P, P, P, C.c_int32,
+                                       C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
+    lib.dfssm_stack_decode.restype = C.c_int
+    lib.dfssm_strerror.argtypes = [C.c_int]
+    lib.dfssm_strerror.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ref(x):
+    return None if x is None else C.byref(x)
+
+
+def dfssm_workspace_bytes(dims: dfssm_dims, op: int, batch: int, seqlen: int = 0, n_layers: int = 0) -> int:
+    return int(load().dfssm_workspace_bytes(C.byref(dims), op, batch, seqlen, n_layers))
+
+
+def dfssm_layer_decode(dims, w, state, x_in, x_out, batch, ws, ws_bytes, taps=None, stream=None) -> int:
+    return int(load().dfssm_layer_decode(C.byref(dims), C.byref(w), C.byref(state), x_in, x_out, batch,
+                                         ws, ws_bytes, _ref(taps), stream))
+
+
+def dfssm_layer_prefill(dims, w, state, x_in, x_dtype, x_out, batch, seqlen, chunk, ws, ws_bytes,
+                        taps=None, stream=None) -> int:
+    return int(load().dfssm_layer_prefill(C.byref(dims), C.byref(w), C.byref(state), x_in, x_dtype, x_out,
+                                          batch, seqlen, chunk, ws, ws_bytes, _ref(taps), stream))
+
+
+def dfssm_stack_decode(dims, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, ws, ws_bytes,
+                       taps=None, stream=None) -> int:
+    """layers / states: ctypes arrays (dfssm_layer_weights * n) / (dfssm_layer_state * n)."""
+    return int(load().dfssm_stack_decode(C.byref(dims), layers, states, n_layers, final_norm_w, x0, y, batch,
+                                         n_steps, ws, ws_bytes, _ref(taps), stream))
+
+
+def dfssm_strerror(status: int) -> str:
+    return load().dfssm_strerror(status).decode()
+
+
+class DfssmError(RuntimeError):
+    pass
+
+
+def check(status: int, what: str = "dfssm call") -> None:
+    if status != DFSSM_OK:
+        raise DfssmError(f"{what} failed: {dfssm_strerror(status)} ({status})")

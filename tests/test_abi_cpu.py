@@ -1,0 +1,141 @@
+"""CPU-only checks of the C ABI: the header compiles as C99, the built library exports every
+symbol the header declares, the ctypes structs match the C layout, and argument validation
+rejects bad calls before anything touches a device."""
+import ctypes as C
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from bit_quantized_mamba_packed_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dfssm.h")
+
+
+def _declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dfssm_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_is_c99():
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        open(src, "w").write('#include "dfssm.h"\nint main(void){return 0;}\n')
+        r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+                            f"-I{os.path.dirname(HEADER)}", src], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    decl = _declared_functions()
+    assert set(decl) == set(L.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    for name in decl:
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_struct_layout_matches_c():
+    prog = r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "dfssm.h"
+int main(void){
+ printf("%zu %zu %zu %zu %zu\n", sizeof(dfssm_dims), sizeof(dfssm_proj), sizeof(dfssm_layer_weights),
+        sizeof(dfssm_layer_state), sizeof(dfssm_taps));
+ printf("%zu %zu %zu %zu\n", offsetof(dfssm_dims, norm_eps), offsetof(dfssm_layer_weights, conv_w),
+        offsetof(dfssm_layer_weights, gnorm_w), offsetof(dfssm_taps, out_t));
+ return 0;}
+'''
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-std=c99", f"-I{os.path.dirname(HEADER)}", src, "-o", exe], check=True)
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    sizes = [int(v) for v in lines[0].split()]
+    offs = [int(v) for v in lines[1].split()]
+    assert sizes == [C.sizeof(L.dfssm_dims), C.sizeof(L.dfssm_proj), C.sizeof(L.dfssm_layer_weights),
+                     C.sizeof(L.dfssm_layer_state), C.sizeof(L.dfssm_taps)]
+    assert offs == [L.dfssm_dims.norm_eps.offset, L.dfssm_layer_weights.conv_w.offset,
+                    L.dfssm_layer_weights.gnorm_w.offset, L.dfssm_taps.out_t.offset]
+
+
+def _dims(**kw):
+    d = dict(d_model=256, d_inner=512, d_state=16, headdim=64, ngroups=1, d_conv=4, n_in_proj=1072,
+             rank_in=8, rank_out=8, norm_eps=1e-5)
+    d.update(kw)
+    return L.dfssm_dims(**d)
+
+
+FAKE = 0x7f0000001000   # aligned, never dereferenced: every call below fails validation first
+
+
+def _fake_weights():
+    p = L.dfssm_proj(*([FAKE] * 6))
+    return L.dfssm_layer_weights(p, p, *([FAKE] * 7))
+
+
+def test_workspace_bytes_and_shape_validation():
+    assert L.dfssm_workspace_bytes(_dims(), L.DFSSM_OP_LAYER_DECODE, 1) > 0
+    assert L.dfssm_workspace_bytes(_dims(), L.DFSSM_OP_STACK_DECODE, 1, 0, 48) > \
+        L.dfssm_workspace_bytes(_dims(), L.DFSSM_OP_LAYER_DECODE, 1)
+    for bad in (dict(d_model=200), dict(headdim=32), dict(d_state=24), dict(d_conv=3), dict(n_in_proj=1000),
+                dict(rank_in=65), dict(ngroups=3), dict(norm_eps=0.0), dict(d_model=0)):
+        assert L.dfssm_workspace_bytes(_dims(**bad), L.DFSSM_OP_LAYER_DECODE, 1) == 0, bad
+    assert L.dfssm_workspace_bytes(_dims(), L.DFSSM_OP_LAYER_DECODE, 0) == 0
+    assert L.dfssm_workspace_bytes(_dims(), 99, 1) == 0
+
+
+def test_layer_decode_rejects_bad_arguments_without_touching_a_device():
+    d = _dims()
+    w = _fake_weights()
+    st = L.dfssm_layer_state(FAKE, FAKE)
+    need = L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_DECODE, 2)
+    ok = dict(x_in=FAKE, x_out=FAKE, batch=2, ws=FAKE, ws_bytes=need)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.dfssm_layer_decode(d, w, st, a["x_in"], a["x_out"], a["batch"], a["ws"], a["ws_bytes"])
+
+    assert call(x_in=None) == L.DFSSM_EINVAL
+    assert call(x_out=FAKE + 4) == L.DFSSM_EINVAL          # misaligned
+    assert call(batch=0) == L.DFSSM_EINVAL
+    assert call(batch=5000) == L.DFSSM_EUNSUPPORTED
+    assert call(ws=None) == L.DFSSM_EINVAL
+    assert call(ws_bytes=need - 1) == L.DFSSM_EWORKSPACE
+    assert L.dfssm_layer_decode(_dims(d_conv=2), w, st, FAKE, FAKE, 1, FAKE, need) == L.DFSSM_EUNSUPPORTED
+    w_bad = _fake_weights()
+    w_bad.in_proj.lora_up = None
+    assert L.dfssm_layer_decode(d, w_bad, st, FAKE, FAKE, 1, FAKE, need) == L.DFSSM_EINVAL
+    st_bad = L.dfssm_layer_state(FAKE, None)
+    assert L.dfssm_layer_decode(d, w, st_bad, FAKE, FAKE, 1, FAKE, need) == L.DFSSM_EINVAL
+    taps = L.dfssm_taps()
+    taps.in_q = FAKE + 1
+    assert L.dfssm_layer_decode(d, w, st, FAKE, FAKE, 1, FAKE, need, taps) == L.DFSSM_EINVAL
+
+
+def test_stack_decode_rejects_bad_arguments():
+    d = _dims()
+    n = 3
+    ws_need = L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_DECODE, 1, 0, n)
+    arr_w = (L.dfssm_layer_weights * n)(*[_fake_weights() for _ in range(n)])
+    arr_s = (L.dfssm_layer_state * n)(*[L.dfssm_layer_state(FAKE, FAKE) for _ in range(n)])
+    f = L.dfssm_stack_decode
+    assert f(d, arr_w, arr_s, 0, FAKE, FAKE, FAKE, 1, 4, FAKE, ws_need) == L.DFSSM_EINVAL
+    assert f(d, arr_w, arr_s, n, FAKE, FAKE, FAKE, 1, 0, FAKE, ws_need) == L.DFSSM_EINVAL
+    assert f(d, arr_w, arr_s, n, FAKE, FAKE, FAKE, 1, 4, FAKE, ws_need - 1) == L.DFSSM_EWORKSPACE
+    arr_s[2].ssm = None
+    assert f(d, arr_w, arr_s, n, FAKE, FAKE, FAKE, 1, 4, FAKE, ws_need) == L.DFSSM_EINVAL
+
+
+def test_strerror():
+    for s in (L.DFSSM_OK, L.DFSSM_EINVAL, L.DFSSM_EUNSUPPORTED, L.DFSSM_EWORKSPACE, L.DFSSM_EHIP):
+        assert len(L.dfssm_strerror(s)) > 3
+    assert L.dfssm_strerror(12345) == "unknown status"

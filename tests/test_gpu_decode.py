@@ -1,0 +1,325 @@
+"""GPU parity of the decode path (dfssm_layer_decode, dfssm_stack_decode) against the CPU oracle.
+
+Every case runs the HIP kernels through the C ABI on seeded synthetic inputs and checks the
+results with the P1/P2/P3 protocol of dfssm_parity."""
+import numpy as np
+import pytest
+import torch
+
+from synth import gen
+from oracle import dfssm_oracle as O
+import dfssm_parity as PY
+
+pytestmark = pytest.mark.gpu
+
+TINY = gen.DIMS["tiny"]
+BIG = gen.DIMS["1p3b"]
+
+
+def _lib():
+    assert torch.cuda.is_available(), "the gpu tests need a ROCm device"
+    from bit_quantized_mamba_packed_amd import _lib as L, device as Dv
+    L.load()
+    return L, Dv
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_layer(dims, lw, xs, conv0, ssm0, taps=True, snap_steps=()):
+    """Run len(xs) decode steps of one layer on the GPU; xs [T][B][D]."""
+    L, Dv = _lib()
+    T, B = xs.shape[:2]
+    dev = Dv.DeviceLayer(lw)
+    st = Dv.DeviceState(conv0, ssm0)
+    ws = Dv.workspace(dims, L.DFSSM_OP_LAYER_DECODE, B)
+    outs, tps, snaps = [], [], {}
+    for t in range(T):
+        if t in snap_steps:
+            snaps[t] = (st.conv.cpu().numpy().copy(), st.ssm.cpu().numpy().copy())
+        x = torch.from_numpy(np.ascontiguousarray(xs[t])).cuda()
+        y = torch.empty_like(x)
+        tp = Dv.Taps(dims, B) if taps else None
+        Dv.layer_decode(dims, dev, st, x, y, ws, tp)
+        outs.append(y.cpu().numpy())
+        tps.append(tp.numpy() if taps else None)
+    torch.cuda.synchronize()
+    return np.stack(outs), tps, (st.conv.cpu().numpy(), st.ssm.cpu().numpy()), snaps
+
+
+def forced_chain(lw, xs, conv0, ssm0, outs, tps, final, b=0, dense=None):
+    """Oracle chain driven by the GPU's codes; asserts P1 + P2 at every step, returns max errors."""
+    cs, ss = conv0[b].astype(np.float64), ssm0[b].astype(np.float64)
+    worst = 0.0
+    for t in range(xs.shape[0]):
+        tap = PY.tap_record(tps[t], b)
+        PY.assert_codes_exact(tap["in_u"], tap["in_q"], tap["in_s"][0], f"t={t} in")
+        PY.assert_codes_exact(tap["out_u"], tap["out_q"], tap["out_s"][0], f"t={t} out")
+        PY.assert_products_exact(lw.in_proj, tap["in_q"], tap["in_acc"], tap["in_t"],
+                                 None if dense is None else dense["in"], f"t={t} in")
+        PY.assert_products_exact(lw.out_proj, tap["out_q"], tap["out_acc"], tap["out_t"],
+                                 None if dense is None else dense["out"], f"t={t} out")
+        force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
+        h, cs, ss, tpo = O.layer_decode(xs[t][b], lw, cs, ss, force=force, dense=dense)
+        e = PY.normwise(outs[t][b], h)
+        assert e < PY.TOL_LAYER, f"step {t} row {b}: output err {e}"
+        assert PY.normwise(tap["in_u"], tpo.in_u) < 1e-5
+        worst = max(worst, e)
+    ec, es = PY.normwise(final[0][b], cs), PY.normwise(final[1][b], ss)
+    assert ec < PY.TOL_LAYER and es < PY.TOL_LAYER, (ec, es)
+    return worst, ec, es
+
+
+def free_running(lw, xs, conv0, ssm0, outs, tps, b=0, n=None):
+    n = xs.shape[0] if n is None else n
+    o_out, _, _, o_taps = O.layer_decode_steps(xs[:n, b], lw, conv0[b], ssm0[b])
+    errs, flips = [], 0
+    for t in range(n):
+        f1, ok1 = PY.flips_at_ties(o_taps[t].in_u, o_taps[t].in_q, tps[t]["in_q"][b])
+        f2, ok2 = PY.flips_at_ties(o_taps[t].out_u, o_taps[t].out_q, tps[t]["out_q"][b])
+        if f1 or f2:
+            # the causally first flip must sit at a rounding tie; later steps inherit its effect
+            assert (ok1 if f1 else ok2), f"step {t}: a code flip away from a rounding tie"
+            flips = f1 + f2
+            break
+        errs.append(PY.normwise(outs[t][b], o_out[t]))
+    if errs:
+        assert max(errs) < PY.TOL_LAYER, errs
+    return (max(errs) if errs else 0.0), flips
+
+
+def test_layer_decode_tiny_16_steps():
+    lw = gen.layer_weights(TINY, 0, 0)
+    conv0, ssm0 = gen.initial_states(TINY, 1)
+    xs = gen.token_inputs(TINY, (16, 1), 0)
+    say("case: tiny layer decode, 16 steps, batch 1, seed 0")
+    outs, tps, final, _ = run_layer(TINY, lw, xs, conv0, ssm0)
+    worst, ec, es = forced_chain(lw, xs, conv0, ssm0, outs, tps, final)
+    fr, flips = free_running(lw, xs, conv0, ssm0, outs, tps)
+    say(f"tiny: forced max err {worst:.2e} conv {ec:.2e} ssm {es:.2e}; free-running {fr:.2e} flips {flips}")
+
+
+def test_layer_decode_batch_random_norms_nonzero_state():
+    lw = gen.layer_weights(TINY, 3, 5, random_norms=True, per_channel_lora=True)
+    B = 6   # two token groups of the packed-sign GEMV
+    conv0, ssm0 = gen.initial_states(TINY, B, 3, 5, std=0.3)
+    xs = gen.token_inputs(TINY, (5, B), 5, tag=3)
+    say("case: tiny layer decode, 5 steps, batch 6, random norms, per-channel LoRA, nonzero state")
+    outs, tps, final, _ = run_layer(TINY, lw, xs, conv0, ssm0)
+    for b in range(B):
+        forced_chain(lw, xs, conv0, ssm0, outs, tps, final, b=b)
+
+
+def test_layer_decode_1p3b_256_steps_sampled():
+    lw = gen.layer_weights(BIG, 0, 0)
+    conv0, ssm0 = gen.initial_states(BIG, 1)
+    xs = gen.token_inputs(BIG, (256, 1), 0)
+    sampled = (0, 1, 2, 100, 255)
+    snap = set(sampled) | {t + 1 for t in sampled if t + 1 < 256}
+    say("case: 1.3B-shaped layer decode, 256 steps, batch 1, seed 0")
+    outs, tps, final, snaps = run_layer(BIG, lw, xs, conv0, ssm0, snap_steps=snap)
+    dense = O.dense_signs(lw)
+    # P1 on every step
+    for t in range(256):
+        tap = PY.tap_record(tps[t], 0)
+        PY.assert_codes_exact(tap["in_u"], tap["in_q"], tap["in_s"][0], f"t={t} in")
+        PY.assert_codes_exact(tap["out_u"], tap["out_q"], tap["out_s"][0], f"t={t} out")
+        PY.assert_products_exact(lw.in_proj, tap["in_q"], tap["in_acc"], tap["in_t"], dense["in"], f"t={t} in")
+        PY.assert_products_exact(lw.out_proj, tap["out_q"], tap["out_acc"], tap["out_t"], dense["out"], f"t={t} out")
+    # P2 on sampled steps, each from the GPU's own state before it
+    for t in sampled:
+        before = snaps[t]
+        after = snaps[t + 1] if t + 1 < 256 else final
+        errs = PY.check_layer_step(lw, xs[t][0], before[0][0], before[1][0], PY.tap_record(tps[t], 0),
+                                   outs[t][0], after[0][0], after[1][0], dense, what=f"t={t}")
+        say(f"1p3b step {t}: {errs}")
+    fr, flips = free_running(lw, xs, conv0, ssm0, outs, tps, n=8)
+    say(f"1p3b free-running 8 steps: max err {fr:.2e}, flips {flips}")
+
+
+def test_layer_decode_degenerate_cases():
+    L, Dv = _lib()
+    # z rows zero: the gate is 0, out-proj codes are 0 (a == 0 path) and the layer is the identity
+    lw = gen.layer_weights(TINY, 1, 7)
+    lw.in_proj.row_scale[:TINY.d_inner] = 0
+    lw.in_proj.up_scale[:TINY.d_inner] = 0
+    conv0, ssm0 = gen.initial_states(TINY, 2, 1, 7, std=0.3)
+    xs = gen.token_inputs(TINY, (2, 2), 7)
+    say("case: degenerate z == 0")
+    outs, tps, final, _ = run_layer(TINY, lw, xs, conv0, ssm0)
+    assert (outs == xs).all()
+    assert not tps[0]["out_q"].any() and not tps[0]["out_s"].any()
+    # dt -> 0: the SSM state is unchanged bit for bit
+    lw = gen.layer_weights(TINY, 2, 8)
+    lw.dt_bias[:] = -100.0
+    conv0, ssm0 = gen.initial_states(TINY, 1, 2, 8, std=0.3)
+    say("case: degenerate dt -> 0")
+    outs, tps, final, _ = run_layer(TINY, lw, gen.token_inputs(TINY, (2, 1), 8), conv0, ssm0)
+    assert (final[1] == ssm0).all()
+    # B == 0 from a zero state: the state stays exactly zero
+    lw = gen.layer_weights(TINY, 3, 9)
+    E, N = TINY.d_inner, TINY.d_state
+    lw.in_proj.row_scale[2 * E:2 * E + N] = 0
+    lw.in_proj.up_scale[2 * E:2 * E + N] = 0
+    lw.conv_b[E:E + N] = 0
+    conv0, ssm0 = gen.initial_states(TINY, 1)
+    say("case: degenerate B == 0")
+    outs, tps, final, _ = run_layer(TINY, lw, gen.token_inputs(TINY, (3, 1), 9), conv0, ssm0)
+    assert not final[1].any()
+    # all-zero token: quantizer a == 0 path gives q = 0, s = 0, still matches the oracle
+    lw = gen.layer_weights(TINY, 4, 10)
+    conv0, ssm0 = gen.initial_states(TINY, 1, 4, 10, std=0.3)
+    xs = np.zeros((1, 1, TINY.d_model), np.float32)
+    say("case: degenerate all-zero token")
+    outs, tps, final, _ = run_layer(TINY, lw, xs, conv0, ssm0)
+    assert not tps[0]["in_q"].any() and tps[0]["in_s"][0, 0] == 0
+    forced_chain(lw, xs, conv0, ssm0, outs, tps, final)
+
+
+def run_stack(dims, layers, x0, states0, n_steps, taps=False, final_w=None):
+    L, Dv = _lib()
+    B = x0.shape[0]
+    devs = [Dv.DeviceLayer(lw) for lw in layers]
+    sts = [Dv.DeviceState(c, s) for c, s in states0]
+    fw = torch.from_numpy(np.ones(dims.d_model, np.float32) if final_w is None else final_w).cuda()
+    xt = torch.from_numpy(x0).cuda()
+    y = torch.empty((n_steps, B, dims.d_model), dtype=torch.float32, device="cuda")
+    ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, B, 0, len(layers))
+    tp = Dv.Taps(dims, n_steps * len(layers) * B) if taps else None
+    Dv.stack_decode(dims, devs, sts, fw, xt, y, n_steps, ws, tp)
+    torch.cuda.synchronize()
+    return (y.cpu().numpy(), [(s.conv.cpu().numpy(), s.ssm.cpu().numpy()) for s in sts],
+            None if tp is None else tp.numpy())
+
+
+def test_stack_decode_tiny_forced_and_free_running():
+    nL, T, B = 3, 12, 2
+    layers = gen.stack_weights(TINY, nL, seed=1, random_norms=True)
+    states0 = [gen.initial_states(TINY, B, l, 1, std=0.1) for l in range(nL)]
+    x0 = gen.token_inputs(TINY, (B,), 1, tag=9)
+    fw = np.random.default_rng(0).uniform(0.5, 1.5, TINY.d_model).astype(np.float32)
+    say("case: tiny stack decode, 3 layers, 12 steps, batch 2, with taps")
+    y, states, taps = run_stack(TINY, layers, x0, states0, T, taps=True, final_w=fw)
+    dense = [O.dense_signs(lw) for lw in layers]
+    for b in range(B):
+        cs = [s[0][b].astype(np.float64) for s in states0]
+        ss = [s[1][b].astype(np.float64) for s in states0]
+        for t in range(T):
+            for l in range(nL):
+                r = (t * nL + l) * B + b
+                tap = PY.tap_record(taps, r)
+                # the layer input the GPU used is the oracle's next input (lock-step per layer)
+                h_in = tap["h_in"]
+                if l == 0:
+                    ref_in = x0[b] if t == 0 else y[t - 1][b]
+                    assert (h_in == ref_in).all()
+                force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
+                PY.assert_codes_exact(tap["in_u"], tap["in_q"], tap["in_s"][0], f"t{t} l{l}")
+                PY.assert_codes_exact(tap["out_u"], tap["out_q"], tap["out_s"][0], f"t{t} l{l}")
+                PY.assert_products_exact(layers[l].in_proj, tap["in_q"], tap["in_acc"], tap["in_t"], dense[l]["in"])
+                PY.assert_products_exact(layers[l].out_proj, tap["out_q"], tap["out_acc"], tap["out_t"],
+                                         dense[l]["out"])
+                h, cs[l], ss[l], _ = O.layer_decode(h_in, layers[l], cs[l], ss[l], force=force, dense=dense[l])
+                if l + 1 < nL:
+                    nxt = PY.tap_record(taps, (t * nL + l + 1) * B + b)["h_in"]
+                    assert PY.normwise(nxt, h) < PY.TOL_LAYER
+                else:
+                    assert PY.normwise(y[t][b], O.rmsnorm(h, fw, TINY.eps)) < PY.TOL_LAYER
+        for l in range(nL):
+            assert PY.normwise(states[l][0][b], cs[l]) < PY.TOL_LAYER
+            assert PY.normwise(states[l][1][b], ss[l]) < PY.TOL_LAYER
+    # free-running P3
+    for b in range(B):
+        yo, _, _ = O.stack_decode(x0[b], layers, [s[0][b] for s in states0], [s[1][b] for s in states0],
+                                  T, fw, TINY.eps)
+        errs = [PY.normwise(y[t][b], yo[t]) for t in range(T)]
+        say(f"tiny stack free-running row {b}: max err {max(errs):.2e}")
+        assert max(errs) < PY.TOL_STACK
+
+
+def test_stack_decode_1p3b_48_layers_512_steps_sampled():
+    """The benchmarked workload: 48 layers, batch 1, 512 steps. The whole run is checked for
+    determinism against a split run, and the last step is checked layer by layer."""
+    nL, T = 48, 512
+    layers = gen.stack_weights(BIG, nL, seed=0)
+    states0 = [gen.initial_states(BIG, 1, l) for l in range(nL)]
+    x0 = gen.token_inputs(BIG, (1,), 0, tag=7)
+    say("case: 1.3B stack decode, 48 layers, 512 steps, batch 1 (benchmark configuration)")
+    y_full, st_full, _ = run_stack(BIG, layers, x0, states0, T)
+    assert np.isfinite(y_full).all()
+    say("case: same stack, 511 steps then 1 tapped step")
+    y_a, st_a, _ = run_stack(BIG, layers, x0, states0, T - 1)
+    y_b, st_b, taps = run_stack(BIG, layers, y_a[-1], st_a, 1, taps=True)
+    assert (y_full[:T - 1] == y_a).all(), "the decode is not deterministic across runs"
+    assert (y_full[T - 1] == y_b[0]).all()
+    for l in range(nL):
+        assert (st_full[l][0] == st_b[l][0]).all() and (st_full[l][1] == st_b[l][1]).all()
+    # last step, each layer in isolation from the GPU's own state and input
+    worst = {}
+    for l in range(nL):
+        lw = layers[l]
+        dense = O.dense_signs(lw)
+        tap = PY.tap_record(taps, l)
+        if l + 1 < nL:
+            out_gpu = PY.tap_record(taps, l + 1)["h_in"]
+        else:
+            out_gpu = None
+        errs_tap = dict()
+        force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
+        PY.assert_codes_exact(tap["in_u"], tap["in_q"], tap["in_s"][0], f"layer {l} in")
+        PY.assert_codes_exact(tap["out_u"], tap["out_q"], tap["out_s"][0], f"layer {l} out")
+        PY.assert_products_exact(lw.in_proj, tap["in_q"], tap["in_acc"], tap["in_t"], dense["in"], f"layer {l}")
+        PY.assert_products_exact(lw.out_proj, tap["out_q"], tap["out_acc"], tap["out_t"], dense["out"], f"layer {l}")
+        h, cs, ss, _ = O.layer_decode(tap["h_in"], lw, st_a[l][0][0], st_a[l][1][0], force=force, dense=dense)
+        errs_tap["conv"] = PY.normwise(st_b[l][0][0], cs)
+        errs_tap["ssm"] = PY.normwise(st_b[l][1][0], ss)
+        if out_gpu is not None:
+            errs_tap["out"] = PY.normwise(out_gpu, h)
+        else:
+            errs_tap["out"] = PY.normwise(y_b[0][0], O.rmsnorm(h, np.ones(BIG.d_model), BIG.eps))
+        for k, v in errs_tap.items():
+            assert v < PY.TOL_LAYER, (l, errs_tap)
+            worst[k] = max(worst.get(k, 0.0), v)
+    say(f"1p3b stack last step per-layer worst errors: {worst}")
+    # P3: a 4-step tapped run from the initial state; the oracle runs the whole stack on its own
+    # float trajectory with the GPU's codes forced in (the random-weight stack is chaotic under the
+    # quantizer: a 1e-7 input perturbation of the oracle itself flips codes by layer 3 and moves
+    # the 48th layer's output by ~0.2, so free-running runs are compared up to their first flip)
+    T2 = 4
+    say("case: same stack, 4 tapped steps from the initial state")
+    y4, _, taps4 = run_stack(BIG, layers, x0, states0, T2, taps=True)
+    assert (y4 == y_full[:T2]).all()
+    dense_all = [O.dense_signs(lw) for lw in layers]
+    cs = [s[0][0].astype(np.float64) for s in states0]
+    ss = [s[1][0].astype(np.float64) for s in states0]
+    x = x0[0].astype(np.float64)
+    errs = []
+    for t in range(T2):
+        h = x
+        for l in range(nL):
+            tap = PY.tap_record(taps4, t * nL + l)
+            force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
+            h, cs[l], ss[l], _ = O.layer_decode(h, layers[l], cs[l], ss[l], force=force, dense=dense_all[l])
+        yo = O.rmsnorm(h, np.ones(BIG.d_model), BIG.eps)
+        errs.append(PY.normwise(y4[t][0], yo))
+        x = yo
+    say(f"1p3b stack code-forced {T2} steps: {errs}")
+    assert max(errs) < PY.TOL_STACK
+    # free-running first step, layer by layer, up to the first code flip (which must sit at a tie)
+    h = x0[0].astype(np.float64)
+    for l in range(nL):
+        tap = PY.tap_record(taps4, l)
+        ho, _, _, tpo = O.layer_decode(h, layers[l], states0[l][0][0], states0[l][1][0], dense=dense_all[l])
+        f1, ok1 = PY.flips_at_ties(tpo.in_u, tpo.in_q, tap["in_q"])
+        f2, ok2 = PY.flips_at_ties(tpo.out_u, tpo.out_q, tap["out_q"])
+        if f1 or f2:
+            # an in-code flip changes the gated input of the same layer's out-projection, so only
+            # the causally first flip (in before out) has to sit at a rounding tie
+            say(f"first code flip at layer {l}: {f1} in, {f2} out codes, at ties: {ok1}, {ok2}")
+            assert ok1 if f1 else ok2
+            break
+        nxt = PY.tap_record(taps4, l + 1)["h_in"] if l + 1 < nL else None
+        if nxt is not None:
+            assert PY.normwise(nxt, ho) < PY.TOL_LAYER
+        h = ho
