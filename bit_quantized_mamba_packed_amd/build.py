@@ -24,7 +24,7 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument", "-Wno-pass-failed",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

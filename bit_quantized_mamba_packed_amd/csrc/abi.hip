@@ -1,5 +1,7 @@
 // C ABI of the DF-SSM hot path: argument validation, workspace carving and launch sequencing.
 // Every check happens before the first enqueue, so a rejected call has no side effect.
+#include <stdlib.h>
+
 #include "dfssm_internal.h"
 
 namespace dfssm {
@@ -79,9 +81,14 @@ int check_taps(const dfssm_taps *t) {
     return DFSSM_OK;
 }
 
-size_t decode_ws_bytes(const Shape &s, int batch, bool stack) {
+size_t decode_ws_bytes(const Shape &s, int batch, bool stack, int n_layers = 0) {
     DecodeWs w = carve_decode_ws(s, batch, nullptr, stack);
-    return w.bytes;
+    return w.bytes + (stack && stack_persistent_ok(s, batch) ? stack_extra_ws_bytes(s, batch, n_layers) : 0);
+}
+
+int env_int(const char *name, int dflt) {
+    const char *v = getenv(name);
+    return v ? atoi(v) : dflt;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DFSSM_OK : DFSSM_EHIP; }
@@ -147,7 +154,7 @@ size_t dfssm_workspace_bytes(const dfssm_dims *dims, int32_t op, int32_t batch, 
         case DFSSM_OP_LAYER_DECODE: return decode_ws_bytes(s, batch, false);
         case DFSSM_OP_STACK_DECODE:
             if (n_layers <= 0) return 0;
-            return decode_ws_bytes(s, batch, true);
+            return decode_ws_bytes(s, batch, true, n_layers);
         case DFSSM_OP_LAYER_PREFILL:
             (void)seqlen;
             return 0;
@@ -197,10 +204,16 @@ int dfssm_stack_decode(const dfssm_dims *dims, const dfssm_layer_weights *layers
     if (bad_ptr(final_norm_w) || bad_ptr(x0) || bad_ptr(y)) return DFSSM_EINVAL;
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
     const Shape s = shape_of(*dims);
-    if (ws_bytes < decode_ws_bytes(s, batch, true)) return DFSSM_EWORKSPACE;
+    if (ws_bytes < decode_ws_bytes(s, batch, true, n_layers)) return DFSSM_EWORKSPACE;
     const DecodeWs wsp = carve_decode_ws(s, batch, ws, true);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (stack_persistent_ok(s, batch)) {
+        // DFSSM_STACK_MAX_WGS caps the resident grid (a tuning knob; 0 = as many as useful)
+        e = launch_stack_persistent(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, wsp,
+                                    static_cast<char *>(ws) + wsp.bytes, taps, env_int("DFSSM_STACK_MAX_WGS", 0), st);
+        return hip_status(e);
+    }
     const int64_t rowsz = (int64_t)batch * s.D;
     for (int t = 0; t < n_steps; ++t) {
         const float *xin = t == 0 ? x0 : y + (t - 1) * rowsz;

@@ -15,319 +15,34 @@
 // bit-planes, sum_k sgn_k q_k = 2*sum_{bit_k=1} q_k - sum_k q_k and
 // sum_{bit=1} q = sum_p c_p * popcount(bits & plane_p), c_p = 2^p (p < 7), c_7 = -128,
 // i.e. one AND and one accumulating popcount per 32 weights per plane.
-#include "dfssm_internal.h"
+#include "decode_device.h"
 
 namespace dfssm {
 
 namespace {
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-__device__ __forceinline__ int wave_isum(int v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
-
-// Block-wide reductions with a fixed combination order, so every workgroup that reduces the
-// same data obtains bit-identical results. `red` is >= kWaves floats of LDS.
-__device__ __forceinline__ float block_sum(float v, float *red) {
-    v = wave_sum(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float r = (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
-    return r;
-}
-__device__ __forceinline__ float block_max(float v, float *red) {
-    v = wave_max(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    return r;
-}
-__device__ __forceinline__ int block_isum(int v, int *red) {
-    v = wave_isum(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    int r = (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
-    return (float)__builtin_bit_cast(_Float16, b);
-}
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
-__device__ __forceinline__ float softplus_f(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
-
-// int8 code of one value: clamp(rint_half_even(u * inv), -127, 127)
-__device__ __forceinline__ int quant1(float u, float inv) {
-    float r = rintf(u * inv);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-}
-
-struct QuantGemvArgs {
-    const float *X;       // [batch][x_stride] input vectors (K used)
-    int64_t x_stride;
-    const float *W;       // [K] norm weight
-    int K;
-    float eps;
-    const uint8_t *sign;  // [n_out][K/8]
-    int n_out;
-    int rows_per_wg;
-    int n_row_wgs;
-    const int8_t *lora_dn;  // [rank][K]
-    int rank;
-    int32_t *acc;         // [batch][n_out]
-    int32_t *t;           // [batch][rank]
-    float *s;             // [batch]
-    // taps, record-major [batch][...]; null when absent
-    float *tap_h, *tap_u, *tap_s;
-    int8_t *tap_q;
-    int32_t *tap_acc, *tap_t;
-};
-
-// RMSNorm + quantizer of NB input vectors into LDS: codes sq[NB][K] and bit-planes
-// spl[NB][8][K/32] (word g of plane p holds bit p of codes 32g..32g+31), sum of codes sqsum[NB].
-template <int NB>
-__device__ void norm_quant_prologue(const QuantGemvArgs &a, int8_t *sq, uint32_t *spl, int *sqsum,
-                                    float *red, int *ired) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int K = a.K;
-    const bool tap_wg = blockIdx.x == 0;
-    for (int b = 0; b < NB; ++b) {
-        const float *x = a.X + (int64_t)b * a.x_stride;
-        float4 hv[kMaxK / 1024];
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < kMaxK / 1024; ++i) {
-            const int e = (i * kBlock + tid) * 4;
-            if (e < K) {
-                hv[i] = *reinterpret_cast<const float4 *>(x + e);
-                ss += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
-            }
-        }
-        const float tot = block_sum(ss, red);
-        const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < kMaxK / 1024; ++i) {
-            const int e = (i * kBlock + tid) * 4;
-            if (e < K) {
-                const float4 w = *reinterpret_cast<const float4 *>(a.W + e);
-                float4 u;
-                u.x = (hv[i].x * r) * w.x;
-                u.y = (hv[i].y * r) * w.y;
-                u.z = (hv[i].z * r) * w.z;
-                u.w = (hv[i].w * r) * w.w;
-                hv[i] = u;
-                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))));
-            }
-        }
-        amax = block_max(amax, red);
-        const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-        const float s = amax > 0.f ? amax / 127.0f : 0.f;
-        int qs = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxK / 1024; ++i) {
-            const int e = (i * kBlock + tid) * 4;
-            if (e < K) {
-                const int q0 = quant1(hv[i].x, inv), q1 = quant1(hv[i].y, inv);
-                const int q2 = quant1(hv[i].z, inv), q3 = quant1(hv[i].w, inv);
-                qs += q0 + q1 + q2 + q3;
-                const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
-                                        ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
-                *reinterpret_cast<uint32_t *>(sq + b * K + e) = packed;
-                if (tap_wg) {
-                    if (a.tap_u) *reinterpret_cast<float4 *>(a.tap_u + (int64_t)b * K + e) = hv[i];
-                    if (a.tap_q) *reinterpret_cast<uint32_t *>(a.tap_q + (int64_t)b * K + e) = packed;
-                    if (a.tap_h)
-                        *reinterpret_cast<float4 *>(a.tap_h + (int64_t)b * K + e) =
-                            *reinterpret_cast<const float4 *>(x + e);
-                }
-            }
-        }
-        qs = block_isum(qs, ired);
-        if (tid == 0) {
-            sqsum[b] = qs;
-            if (tap_wg) {
-                a.s[b] = s;
-                if (a.tap_s) a.tap_s[b] = s;
-            }
-        }
-    }
-    __syncthreads();
-    // bit-planes via wave ballots over 64 consecutive codes
-    const int G32 = K >> 5;
-    for (int b = 0; b < NB; ++b) {
-        for (int c = wave; c < (K >> 6); c += kWaves) {
-            const uint32_t v = (uint8_t)sq[b * K + c * 64 + lane];
-            uint64_t mine = 0;
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const uint64_t m = __ballot((v >> p) & 1u);
-                if ((lane & 7) == p) mine = m;
-            }
-            if (lane < 16) {
-                const int p = lane & 7;
-                const uint32_t word = lane < 8 ? (uint32_t)mine : (uint32_t)(mine >> 32);
-                spl[(b * 8 + p) * G32 + 2 * c + (lane >> 3)] = word;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-template <int NB>
-__device__ void gemv_rows(const QuantGemvArgs &a, int row_begin, int row_end, const uint32_t *spl,
-                          const int *sqsum) {
-    const int K = a.K, chunks = K >> 7, G32 = K >> 5;
-    int lpr = 1;
-    while (lpr * 2 <= chunks && lpr < 64) lpr *= 2;  // lanes per row: power of two
-    const int rpw = 64 / lpr;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rin = lane / lpr, lir = lane & (lpr - 1);
-    for (int n0 = row_begin + wave * rpw; n0 < row_end; n0 += kWaves * rpw) {
-        const int n = n0 + rin;
-        const bool valid = n < row_end;
-        uint32_t cnt[NB][8];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int p = 0; p < 8; ++p) cnt[b][p] = 0;
-        const uint4 *row = reinterpret_cast<const uint4 *>(a.sign + (int64_t)(valid ? n : row_begin) * (K >> 3));
-        for (int c = lir; c < chunks; c += lpr) {
-            const uint4 bits = valid ? row[c] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const uint4 pl = *reinterpret_cast<const uint4 *>(spl + (b * 8 + p) * G32 + c * 4);
-                    cnt[b][p] = __popc(bits.x & pl.x) + __popc(bits.y & pl.y) + __popc(bits.z & pl.z) +
-                                __popc(bits.w & pl.w) + cnt[b][p];
-                }
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            int pos = 0;
-#pragma unroll
-            for (int p = 0; p < 7; ++p) pos += (int)cnt[b][p] << p;
-            pos -= (int)cnt[b][7] << 7;
-            for (int m = lpr >> 1; m >= 1; m >>= 1) pos += __shfl_xor(pos, m, 64);
-            if (lir == 0 && valid) {
-                const int accv = 2 * pos - sqsum[b];
-                a.acc[(int64_t)b * a.n_out + n] = accv;
-                if (a.tap_acc) a.tap_acc[(int64_t)b * a.n_out + n] = accv;
-            }
-        }
-    }
-}
-
-template <int NB>
-__device__ void lora_dn_rows(const QuantGemvArgs &a, int j_begin, int j_end, const int8_t *sq) {
-    const int K = a.K;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int j = j_begin + wave; j < j_end; j += kWaves) {
-        int sacc[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) sacc[b] = 0;
-        const int8_t *row = a.lora_dn + (int64_t)j * K;
-        for (int off = lane * 16; off < K; off += 1024) {
-            const int4 lw = *reinterpret_cast<const int4 *>(row + off);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const int4 qv = *reinterpret_cast<const int4 *>(sq + b * K + off);
-                int v = sacc[b];
-                v = __builtin_amdgcn_sdot4(lw.x, qv.x, v, false);
-                v = __builtin_amdgcn_sdot4(lw.y, qv.y, v, false);
-                v = __builtin_amdgcn_sdot4(lw.z, qv.z, v, false);
-                v = __builtin_amdgcn_sdot4(lw.w, qv.w, v, false);
-                sacc[b] = v;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int tv = wave_isum(sacc[b]);
-            if (lane == 0) {
-                a.t[b * a.rank + j] = tv;
-                if (a.tap_t) a.tap_t[(int64_t)b * a.rank + j] = tv;
-            }
-        }
-    }
-}
-
 template <int NB>
 __global__ __launch_bounds__(kBlock) void k_quant_gemv(QuantGemvArgs a) {
     extern __shared__ __align__(16) char smem[];
-    __shared__ float red[kWaves];
+    __shared__ float red[2 * kWaves];
     __shared__ int ired[kWaves];
     __shared__ int sqsum[NB];
+    __shared__ float ssc[NB];
     int8_t *sq = reinterpret_cast<int8_t *>(smem);
     uint32_t *spl = reinterpret_cast<uint32_t *>(smem + NB * a.K);
-    norm_quant_prologue<NB>(a, sq, spl, sqsum, red, ired);
+    const PlainSource<kMaxK / 1024> src{a.X, a.x_stride};
+    const PlainSink sink{a.acc, a.t, a.n_out, a.rank};
+    norm_quant_prologue<NB, kMaxK / 1024>(a, src, sq, spl, sqsum, ssc, red, ired, nullptr);
     if ((int)blockIdx.x < a.n_row_wgs) {
         const int r0 = blockIdx.x * a.rows_per_wg;
-        gemv_rows<NB>(a, r0, min(r0 + a.rows_per_wg, a.n_out), spl, sqsum);
+        gemv_rows<NB>(a, sink, r0, min(r0 + a.rows_per_wg, a.n_out), spl, sqsum, GemvPre{}, false);
     } else {
         const int j0 = (blockIdx.x - a.n_row_wgs) * kWaves;
-        lora_dn_rows<NB>(a, j0, min(j0 + kWaves, a.rank), sq);
+        lora_dn_rows<NB>(a, sink, j0, min(j0 + kWaves, a.rank), sq);
     }
 }
 
-// ---------------------------------------------------------------- rescale + LoRA-up epilogue
-struct EpiCommon {
-    const int32_t *acc;     // [batch][n_out]
-    const int32_t *t;       // [batch][rank]
-    const float *s;         // [batch]
-    int n_out, rank;
-    const uint16_t *row_scale;
-    const int8_t *lora_up;  // [n_out][rank]
-    const float *up_scale, *dn_scale;
-};
-
-// v[j] = dn_scale[j] * s * t[j] into LDS (rank <= 64); returns s.
-__device__ __forceinline__ float epi_prepare(const EpiCommon &c, int b, float *v) {
-    const float s = c.s[b];
-    if ((int)threadIdx.x < c.rank) v[threadIdx.x] = c.dn_scale[threadIdx.x] * s * (float)c.t[b * c.rank + threadIdx.x];
-    __syncthreads();
-    return s;
-}
-
-// y[n] = s*row_scale[n]*acc[n] + up_scale[n] * sum_j lora_up[n,j] * v[j]
-__device__ __forceinline__ float epi_row(const EpiCommon &c, int b, int n, float s, const float *v) {
-    const int8_t *up = c.lora_up + (int64_t)n * c.rank;
-    float lr = 0.f;
-    if ((c.rank & 15) == 0) {
-        for (int j = 0; j < c.rank; j += 16) {
-            const int4 w4 = *reinterpret_cast<const int4 *>(up + j);
-            const int ws[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) lr += (float)(int8_t)(ws[i] >> (8 * k)) * v[j + 4 * i + k];
-        }
-    } else {
-        for (int j = 0; j < c.rank; ++j) lr += (float)up[j] * v[j];
-    }
-    const float acc = (float)c.acc[(int64_t)b * c.n_out + n];
-    return s * half_bits_to_float(c.row_scale[n]) * acc + c.up_scale[n] * lr;
-}
-
+// ---------------------------------------------------------------- epilogues
 struct EpiConvArgs {
     EpiCommon c;
     int E, Cd, H;
@@ -429,7 +144,7 @@ __global__ __launch_bounds__(kBlock) void k_ssm(SsmArgs a) {
 // ---------------------------------------------------------------- final RMSNorm of the stack
 __global__ __launch_bounds__(kBlock) void k_final_norm(const float *h, const float *w, float *y, float *y2,
                                                        int D, float eps) {
-    __shared__ float red[kWaves];
+    __shared__ float red[2 * kWaves];
     const int b = blockIdx.x;
     const float *hb = h + (int64_t)b * D;
     float ss = 0.f;
@@ -451,10 +166,7 @@ hipError_t launch_qg(const QuantGemvArgs &a, int n_lora_wgs, hipStream_t stream)
 }
 
 hipError_t launch_quant_gemv(QuantGemvArgs a, int nb, hipStream_t stream) {
-    const int chunks = a.K >> 7;
-    int lpr = 1;
-    while (lpr * 2 <= chunks && lpr < 64) lpr *= 2;
-    a.rows_per_wg = kWaves * (64 / lpr);
+    a.rows_per_wg = kWaves * (64 / gemv_lanes_per_row(a.K));
     a.n_row_wgs = (a.n_out + a.rows_per_wg - 1) / a.rows_per_wg;
     const int n_lora_wgs = (a.rank + kWaves - 1) / kWaves;
     switch (nb) {

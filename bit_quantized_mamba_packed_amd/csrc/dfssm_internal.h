@@ -52,6 +52,15 @@ hipError_t launch_layer_decode(const Shape &s, const dfssm_layer_weights &w,
                                int batch, const DecodeWs &ws, const TapPtrs &taps,
                                hipStream_t stream);
 
+// Extra workspace of the persistent stack kernel (layer table, barrier counter, error flag,
+// raw B/C values) and its launcher; batch <= kGemvMaxBatch.
+size_t stack_extra_ws_bytes(const Shape &s, int batch, int n_layers);
+hipError_t launch_stack_persistent(const Shape &s, const dfssm_layer_weights *layers,
+                                   const dfssm_layer_state *states, int n_layers, const float *final_w,
+                                   const float *x0, float *y, int batch, int n_steps, const DecodeWs &ws,
+                                   void *extra, const dfssm_taps *taps, int max_wgs, hipStream_t stream);
+bool stack_persistent_ok(const Shape &s, int batch);
+
 // Enqueue y = RMSNorm(h) * w for `batch` rows of length D, also copying y to `y2` when non-null.
 hipError_t launch_final_norm(const float *h, const float *w, float *y, float *y2, int D, float eps,
                              int batch, hipStream_t stream);

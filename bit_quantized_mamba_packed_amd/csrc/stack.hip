@@ -1,0 +1,747 @@
+// Persistent stack decode: ONE cooperative launch runs every step of every layer for up to
+// kGemvMaxBatch tokens (the DF-SSM paper §4.1 captures the 48-layer forward in a graph to cut
+// launch overhead; here the whole decode is a single resident grid instead).
+//
+// There are no grid barriers. Work is split into items; every value an item hands to another
+// workgroup is written as a 64-bit word {payload, epoch} with an agent-coherent store, and
+// after its words the item publishes a completion flag (epoch = step * n_layers + layer + 1).
+// A consumer polls only the flags of the items it depends on, then reads the words with plain
+// loads, re-reading with coherent loads any word whose epoch shows a stale cached copy. Every
+// layer has its own buffers (a ring of n_layers slots), so a slot is reused one token later.
+// Per layer:
+//   A  every workgroup with in_proj work reads the residual h, recomputes RMSNorm + int8
+//      quantizer, and publishes packed-sign GEMV rows / LoRA-down rows             -> xa, fa
+//   B  one item per (token, head, block of headdim rows): its z, x, B, C, dt rows and the LoRA
+//      vector -> rescale + LoRA-up epilogue, conv step, SSM update + readout, SiLU(z) gate
+//                                                                                  -> xb, fb
+//   D  every workgroup with out_proj work reads all of xb, recomputes the gated RMSNorm +
+//      quantizer, publishes out_proj GEMV / LoRA-down rows                          -> xd, fd
+//      (workgroup 0 also shifts the B/C conv state, after every phase-B reader of it)
+//   E  residual items: h = h_prev + epilogue of their xd rows                       -> xe, fe
+// Weights and the state a workgroup owns are loaded before it polls, so HBM latency overlaps
+// the wait. The stack's final RMSNorm of token t is folded into phase A of token t+1.
+//
+// A producer publishes a flag only after s_waitcnt has drained its stores, and a consumer reads
+// words only after __syncthreads has followed its flag polls, so a flag implies its words. A
+// slot of epoch e is rewritten at epoch e + n_layers, which transitively depends on every
+// consumer of epoch e having finished (every in_proj item holds consumed rows: padding rows are
+// folded into the last natural item).
+//
+// hipLaunchCooperativeKernel guarantees that every workgroup is resident (the launch fails
+// otherwise), and every wait is bounded: on a timeout the kernel flags the workspace, stops
+// waiting and poisons y with NaN, so every wave still reaches the end.
+#include "decode_device.h"
+
+namespace dfssm {
+
+namespace {
+
+constexpr unsigned kSpinLimit = 1u << 21;
+#ifndef DFSSM_POLL_SLEEP
+#define DFSSM_POLL_SLEEP 8
+#endif
+constexpr int kPollSleep = DFSSM_POLL_SLEEP;  // s_sleep units (64 clocks) between polls
+constexpr int kLayersPerTableLaunch = 16;
+
+struct LayerEntry {
+    dfssm_layer_weights w;
+    dfssm_layer_state st;
+};
+
+struct LayerChunk {
+    LayerEntry e[kLayersPerTableLaunch];
+};
+
+struct FlowArgs {
+    int n_layers, n_steps, batch;
+    int D, E, N, P, H, G, Cd, Nin, Ninp, Rin, Rout;
+    float eps;
+    const LayerEntry *layers;
+    const float *final_w, *x0;
+    float *y;
+    // per-layer slots of tagged words (slot stride in words) and completion flags
+    uint64_t *xa, *xb, *xd, *xe, *bc;   // [L][batch][sa], [L][batch][E], [L][batch][sd], [L][batch][D], [L][batch][2GN]
+    uint64_t *fa, *fb, *fd, *fe;        // [L][nA], [L][ssm_items], [L][nDi], [L][res_items]
+    int *err;
+    int in_rows_per_item, in_row_items, in_lora_items;
+    int out_rows_per_item, out_row_items, out_lora_items;
+    int ssm_rpw, ssm_items, res_items;
+    dfssm_taps taps;
+};
+
+__device__ __forceinline__ uint64_t tagged(uint32_t bits, uint32_t tag) { return ((uint64_t)tag << 32) | bits; }
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+__device__ void flag_error(const FlowArgs &a) {
+    __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float nan = __builtin_nanf("");
+    a.y[0] = nan;
+    a.y[(int64_t)(a.n_steps - 1) * a.batch * a.D] = nan;
+}
+
+// Coherently poll one tagged word until its epoch is `tag`; bounded. Returns the payload bits.
+__device__ __forceinline__ uint32_t poll_word(const FlowArgs &a, const uint64_t *p, uint32_t tag) {
+    uint64_t v = ld_x(p);
+    unsigned spins = 0;
+    while ((uint32_t)(v >> 32) != tag) {
+        __builtin_amdgcn_s_sleep(kPollSleep);
+        ++spins;
+        if ((spins & 15) == 0 && ld_x(a.err)) break;
+        if (spins > kSpinLimit) {
+            flag_error(a);
+            break;
+        }
+        v = ld_x(p);
+    }
+    return (uint32_t)v;
+}
+
+// Wait until completion flag *f holds `tag` (a flag word is the bare epoch).
+__device__ __forceinline__ void wait_flag(const FlowArgs &a, const uint64_t *f, uint32_t tag) {
+    unsigned spins = 0;
+    while ((uint32_t)ld_x(f) != tag) {
+        __builtin_amdgcn_s_sleep(kPollSleep);
+        ++spins;
+        if ((spins & 15) == 0 && ld_x(a.err)) break;
+        if (spins > kSpinLimit) {
+            flag_error(a);
+            break;
+        }
+    }
+}
+
+// Read a tagged word whose producer has already flagged it: a plain load, and coherent loads
+// only if this XCD's cache returned an older epoch.
+__device__ __forceinline__ uint32_t read_word(const FlowArgs &a, const uint64_t *p, uint32_t tag) {
+    const uint64_t v = *p;
+    if ((uint32_t)(v >> 32) == tag) return (uint32_t)v;
+    return poll_word(a, p, tag);
+}
+
+// Drain this workgroup's stores, then publish completion flag *f = tag.
+__device__ __forceinline__ void publish(uint64_t *f, uint32_t tag) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) st_x(f, (uint64_t)tag);
+}
+
+// Prologue input: flagged tagged words of epoch `tag` (all of a thread's words requested first).
+template <int KCH>
+struct TaggedSource {
+    const FlowArgs *a;
+    const uint64_t *X;
+    int64_t stride;
+    uint32_t tag;
+    __device__ __forceinline__ void load(int b, int K, float4 *hv) const {
+        uint64_t w[KCH][4];
+        const uint64_t *xb = X + (int64_t)b * stride;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int e = (i * kBlock + (int)threadIdx.x) * 4;
+            if (e < K) {
+                const ulonglong2 v0 = *reinterpret_cast<const ulonglong2 *>(xb + e);
+                const ulonglong2 v1 = *reinterpret_cast<const ulonglong2 *>(xb + e + 2);
+                w[i][0] = v0.x;
+                w[i][1] = v0.y;
+                w[i][2] = v1.x;
+                w[i][3] = v1.y;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int e = (i * kBlock + (int)threadIdx.x) * 4;
+            if (e < K) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if ((uint32_t)(w[i][c] >> 32) != tag) w[i][c] = poll_word(*a, xb + e + c, tag);
+                hv[i] = make_float4(bitsf((uint32_t)w[i][0]), bitsf((uint32_t)w[i][1]), bitsf((uint32_t)w[i][2]),
+                                    bitsf((uint32_t)w[i][3]));
+            }
+        }
+    }
+};
+
+// Plain fp32 input (the stack's x0), KCH chunks per thread.
+template <int KCH>
+struct InputSource {
+    const float *X;
+    int64_t stride;
+    __device__ __forceinline__ void load(int b, int K, float4 *hv) const {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int e = (i * kBlock + (int)threadIdx.x) * 4;
+            if (e < K) hv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * stride + e);
+        }
+    }
+};
+
+// GEMV results published as tagged words: acc at [b][n], low-rank sums at [b][t_off + j].
+struct TaggedSink {
+    uint64_t *base;
+    int64_t stride;
+    int t_off;
+    uint32_t tag;
+    __device__ __forceinline__ void put_acc(int b, int n, int v) const {
+        st_x(base + (int64_t)b * stride + n, tagged((uint32_t)v, tag));
+    }
+    __device__ __forceinline__ void put_t(int b, int j, int v) const {
+        st_x(base + (int64_t)b * stride + t_off + j, tagged((uint32_t)v, tag));
+    }
+};
+
+__global__ void k_store_layers(LayerEntry *dst, LayerChunk c, int n) {
+    if ((int)threadIdx.x < n) dst[threadIdx.x] = c.e[threadIdx.x];
+}
+
+__global__ void k_zero_words(uint64_t *p, int64_t n, int *err) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
+}
+
+struct SsmLds {
+    float z[64], x[64], B[256], C[256], dt, s;
+};
+
+// LoRA-up row held in registers (rank a multiple of 16, at most 64).
+struct UpRow {
+    int4 w[kMaxRank / 16];
+};
+__device__ __forceinline__ void load_up_row(UpRow &r, const int8_t *lora_up, int rank, int n) {
+    const int4 *p = reinterpret_cast<const int4 *>(lora_up + (int64_t)n * rank);
+#pragma unroll
+    for (int i = 0; i < kMaxRank / 16; ++i)
+        if (i * 16 < rank) r.w[i] = p[i];
+}
+__device__ __forceinline__ float up_dot(const UpRow &r, int rank, const float *v) {
+    float lr = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxRank / 16; ++i) {
+        if (i * 16 < rank) {
+            const int ws[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) lr += (float)(int8_t)(ws[q] >> (8 * k)) * v[i * 16 + 4 * q + k];
+        }
+    }
+    return lr;
+}
+
+// Which in_proj row / conv channel the k-th epilogue slot of an SSM item covers.
+struct SlotMap {
+    int n, ch;  // row of in_proj, conv channel (-1 for z and dt rows)
+};
+__device__ __forceinline__ SlotMap slot_of(const FlowArgs &a, int k, int h, int p0, int g) {
+    const int rpw = a.ssm_rpw, N = a.N, E = a.E;
+    SlotMap m{0, -1};
+    if (k < rpw) {
+        m.n = h * a.P + p0 + k;
+    } else if (k < 2 * rpw) {
+        m.ch = h * a.P + p0 + (k - rpw);
+    } else if (k < 2 * rpw + N) {
+        m.ch = E + g * N + (k - 2 * rpw);
+    } else if (k < 2 * rpw + 2 * N) {
+        m.ch = E + a.G * N + g * N + (k - 2 * rpw - N);
+    } else {
+        m.n = E + a.Cd + h;
+    }
+    if (m.ch >= 0) m.n = E + m.ch;
+    return m;
+}
+
+__device__ __forceinline__ int in_item_of_row(const FlowArgs &a, int n) {
+    const int it = n / a.in_rows_per_item;
+    return it < a.in_row_items ? it : a.in_row_items - 1;
+}
+
+// Phase B item: epilogue of the rows one (token, head, row block) consumes, conv, SSM, gate.
+__device__ void ssm_item(const FlowArgs &a, const LayerEntry &L, int l, int it, uint32_t tag, float *vsh,
+                         SsmLds &sh) {
+    const int per_head = a.P / a.ssm_rpw;
+    const int per_b = a.H * per_head;
+    const int b = it / per_b;
+    const int r = it - b * per_b;
+    const int h = r / per_head;
+    const int p0 = (r - h * per_head) * a.ssm_rpw;
+    const int g = h * a.G / a.H;
+    const int rpw = a.ssm_rpw, N = a.N, E = a.E, tid = threadIdx.x;
+    const bool bc_owner = p0 == 0 && h == g * (a.H / a.G);
+    const dfssm_proj &pj = L.w.in_proj;
+    const bool up_regs = (a.Rin & 15) == 0;
+    const int total = 2 * rpw + 2 * N + 1;
+    const int n4 = N >> 2;
+    const int nch = rpw * n4;
+    const int64_t sa = a.Ninp + a.Rin + 1;
+    const uint64_t *xa = a.xa + ((int64_t)l * a.batch + b) * sa;
+    // ---- loads that do not depend on this layer's activations
+    float4 S[2];
+    float4 *sp[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ci = tid + i * kBlock;
+        sp[i] = nullptr;
+        if (ci < nch) {
+            const int pr = ci / n4, c4 = ci - pr * n4;
+            sp[i] = reinterpret_cast<float4 *>(L.st.ssm + (((int64_t)b * a.H + h) * a.P + p0 + pr) * N) + c4;
+            S[i] = *sp[i];
+        }
+    }
+    SlotMap m[2];
+    UpRow up[2];
+    float sc[2], us[2], cw[2][4], cb[2], cs[2][3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = tid + i * kBlock;
+        if (k < total) {
+            m[i] = slot_of(a, k, h, p0, g);
+            if (up_regs) load_up_row(up[i], pj.lora_up, a.Rin, m[i].n);
+            sc[i] = half_bits_to_float(pj.row_scale[m[i].n]);
+            us[i] = pj.lora_up_scale[m[i].n];
+            if (m[i].ch >= 0) {
+                const float4 w = *reinterpret_cast<const float4 *>(L.w.conv_w + (int64_t)m[i].ch * kConvTaps);
+                cw[i][0] = w.x;
+                cw[i][1] = w.y;
+                cw[i][2] = w.z;
+                cw[i][3] = w.w;
+                cb[i] = L.w.conv_b[m[i].ch];
+                const float *st = L.st.conv + ((int64_t)b * a.Cd + m[i].ch) * (kConvTaps - 1);
+                if (m[i].ch < E) {           // owned by this item
+                    cs[i][0] = st[0];
+                    cs[i][1] = st[1];
+                    cs[i][2] = st[2];
+                } else {                     // shifted by workgroup 0 in phase D
+                    cs[i][0] = ld_x(st);
+                    cs[i][1] = ld_x(st + 1);
+                    cs[i][2] = ld_x(st + 2);
+                }
+            }
+        }
+    }
+    const float dtb = L.w.dt_bias[h], Alog = L.w.A_log[h], Dh = L.w.D[h];
+    // ---- this layer's in_proj results: every word this thread needs is requested at once with a
+    // coherent load, then the ones not yet carrying this epoch are polled
+    uint64_t w_s = ld_x(xa + a.Ninp + a.Rin);
+    uint64_t w_t = tid < a.Rin ? ld_x(xa + a.Ninp + tid) : tagged(0, tag);
+    uint64_t w_acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) w_acc[i] = tid + i * kBlock < total ? ld_x(xa + m[i].n) : tagged(0, tag);
+    if ((uint32_t)(w_s >> 32) != tag) w_s = tagged(poll_word(a, xa + a.Ninp + a.Rin, tag), tag);
+    if ((uint32_t)(w_t >> 32) != tag) w_t = tagged(poll_word(a, xa + a.Ninp + tid, tag), tag);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if ((uint32_t)(w_acc[i] >> 32) != tag) w_acc[i] = tagged(poll_word(a, xa + m[i].n, tag), tag);
+    const float s = bitsf((uint32_t)w_s);
+    if (tid < a.Rin) vsh[tid] = pj.lora_dn_scale[tid] * s * (float)(int)(uint32_t)w_t;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = tid + i * kBlock;
+        if (k < total) {
+            const int acc = (int)(uint32_t)w_acc[i];
+            const float lr = up_regs ? up_dot(up[i], a.Rin, vsh) : lowrank_row(pj.lora_up, a.Rin, m[i].n, vsh);
+            const float yv = s * sc[i] * (float)acc + us[i] * lr;
+            const int ch = m[i].ch;
+            if (ch >= 0) {
+                const float pre = cb[i] + cw[i][0] * cs[i][0] + cw[i][1] * cs[i][1] + cw[i][2] * cs[i][2] + cw[i][3] * yv;
+                const float act = silu_f(pre);
+                if (ch < E) {
+                    float *st = L.st.conv + ((int64_t)b * a.Cd + ch) * (kConvTaps - 1);
+                    st[0] = cs[i][1];
+                    st[1] = cs[i][2];
+                    st[2] = yv;
+                    sh.x[ch - h * a.P - p0] = act;
+                } else {
+                    if (bc_owner)
+                        st_x(a.bc + ((int64_t)l * a.batch + b) * 2 * a.G * N + (ch - E), tagged(fbits(yv), tag));
+                    const int j = ch - E - g * N;
+                    if (j < N) sh.B[j] = act;
+                    else sh.C[ch - E - a.G * N - g * N] = act;
+                }
+            } else if (k < rpw) {
+                sh.z[k] = yv;
+            } else {
+                sh.dt = softplus_f(yv + dtb);
+            }
+        }
+    }
+    __syncthreads();
+    const float dt = sh.dt;
+    const float dA = expf(dt * -expf(Alog));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ci = tid + i * kBlock;
+        if (ci < nch) {
+            const int pr = ci / n4, c4 = ci - pr * n4;
+            const float x = sh.x[pr];
+            const float dtx = dt * x;
+            const float4 Bn = *reinterpret_cast<const float4 *>(&sh.B[c4 * 4]);
+            const float4 Cn = *reinterpret_cast<const float4 *>(&sh.C[c4 * 4]);
+            float4 v = S[i];
+            v.x = dA * v.x + dtx * Bn.x;
+            v.y = dA * v.y + dtx * Bn.y;
+            v.z = dA * v.z + dtx * Bn.z;
+            v.w = dA * v.w + dtx * Bn.w;
+            *sp[i] = v;
+            float part = (v.x * Cn.x + v.y * Cn.y) + (v.z * Cn.z + v.w * Cn.w);
+            for (int mm = n4 >> 1; mm >= 1; mm >>= 1) part += __shfl_xor(part, mm, 64);
+            if (c4 == 0) {
+                const int p = p0 + pr;
+                st_x(a.xb + ((int64_t)l * a.batch + b) * E + h * a.P + p,
+                     tagged(fbits((part + Dh * x) * silu_f(sh.z[pr])), tag));
+            }
+        }
+    }
+    publish(a.fb + (int64_t)l * a.ssm_items + it, tag);
+}
+
+// B/C conv-state shift of one layer by workgroup 0, after every phase-B reader of the old state
+// (phase D starts only once every SSM item has published).
+__device__ void bc_conv_shift(const FlowArgs &a, const LayerEntry &L, int l, uint32_t tag) {
+    const int nbc = 2 * a.G * a.N;
+    const uint64_t *bc = a.bc + (int64_t)l * a.batch * nbc;
+    for (int k = threadIdx.x; k < a.batch * nbc; k += kBlock) {
+        const int b = k / nbc, j = k - b * nbc;
+        const float raw = bitsf(read_word(a, bc + (int64_t)b * nbc + j, tag));
+        float *st = L.st.conv + ((int64_t)b * a.Cd + a.E + j) * (kConvTaps - 1);
+        const float s1 = ld_x(st + 1), s2 = ld_x(st + 2);
+        st_x(st, s1);
+        st_x(st + 1, s2);
+        st_x(st + 2, raw);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+template <int NB, int KCH>
+__global__ __launch_bounds__(kBlock, 3) void k_stack_flow(FlowArgs a) {
+    extern __shared__ __align__(16) char smem[];
+    __shared__ float red[2 * kWaves];
+    __shared__ int ired[kWaves];
+    __shared__ int sqsum[NB];
+    __shared__ float ssc[NB];
+    __shared__ float vsh[kMaxRank];
+    __shared__ SsmLds ssh;
+    const int Kmax = a.D > a.E ? a.D : a.E;
+    int8_t *sq = reinterpret_cast<int8_t *>(smem);
+    uint32_t *spl = reinterpret_cast<uint32_t *>(smem + NB * Kmax);
+    float *xsave = reinterpret_cast<float *>(smem + 2 * NB * Kmax);
+    const int nwg = gridDim.x, wg = blockIdx.x, tid = threadIdx.x;
+    const int nA = a.in_row_items + a.in_lora_items;
+    const int nDi = a.out_row_items + a.out_lora_items;
+    const int64_t BD = (int64_t)a.batch * a.D;
+    const int64_t sa = a.Ninp + a.Rin + 1, sd = a.D + a.Rout + 1;
+    const int rpi = a.in_rows_per_item, last = a.in_row_items - 1;
+    const dfssm_taps &T = a.taps;
+    for (int t = 0; t < a.n_steps; ++t) {
+        for (int l = 0; l < a.n_layers; ++l) {
+            const LayerEntry &L = a.layers[l];
+            const uint32_t tag = (uint32_t)(t * a.n_layers + l + 1);
+            const int lp = l == 0 ? a.n_layers - 1 : l - 1;   // slot of the previous layer step
+            const int64_t rec = ((int64_t)t * a.n_layers + l) * a.batch;
+            uint64_t *xa = a.xa + (int64_t)l * a.batch * sa;
+            uint64_t *xb = a.xb + (int64_t)l * a.batch * a.E;
+            uint64_t *xd = a.xd + (int64_t)l * a.batch * sd;
+            uint64_t *xe = a.xe + (int64_t)l * BD;
+            const uint64_t *xe_prev = a.xe + (int64_t)lp * BD;
+            // ================= phase A: in_proj
+            if (wg < nA) {
+                QuantGemvArgs q{};
+                q.W = L.w.norm_w;
+                q.K = a.D;
+                q.eps = a.eps;
+                q.sign = L.w.in_proj.sign;
+                q.n_out = a.Ninp;
+                q.lora_dn = L.w.in_proj.lora_dn;
+                q.rank = a.Rin;
+                q.tap_h = T.h_in ? T.h_in + rec * a.D : nullptr;
+                q.tap_u = T.in_u ? T.in_u + rec * a.D : nullptr;
+                q.tap_q = T.in_q ? T.in_q + rec * a.D : nullptr;
+                q.tap_s = T.in_s ? T.in_s + rec : nullptr;
+                q.tap_acc = T.in_acc ? T.in_acc + rec * a.Ninp : nullptr;
+                q.tap_t = T.in_t ? T.in_t + rec * a.Rin : nullptr;
+                GemvPre pf{};
+                if (wg < a.in_row_items)
+                    gemv_prefetch(pf, q.sign, a.D, wg * rpi, wg == last ? a.Ninp : min((wg + 1) * rpi, a.Nin));
+                if (l == 0 && t == 0) {
+                    const InputSource<KCH> src{a.x0, a.D};
+                    norm_quant_prologue<NB, KCH>(q, src, sq, spl, sqsum, ssc, red, ired, xsave);
+                } else {
+                    if (l == 0) {
+                        q.pre_w = a.final_w;
+                        q.pre_out = a.y + (int64_t)(t - 1) * BD;
+                    }
+                    if (tid < a.res_items) wait_flag(a, a.fe + (int64_t)lp * a.res_items + tid, tag - 1);
+                    __syncthreads();
+                    const TaggedSource<KCH> src{&a, xe_prev, a.D, tag - 1};
+                    norm_quant_prologue<NB, KCH>(q, src, sq, spl, sqsum, ssc, red, ired, l == 0 ? xsave : nullptr);
+                }
+                if (wg == 0 && tid < NB) st_x(xa + tid * sa + a.Ninp + a.Rin, tagged(fbits(ssc[tid]), tag));
+                const TaggedSink sink{xa, sa, a.Ninp, tag};
+                for (int it = wg; it < nA; it += nwg) {
+                    if (it < a.in_row_items) {
+                        const int r1 = it == last ? a.Ninp : min((it + 1) * rpi, a.Nin);
+                        gemv_rows<NB>(q, sink, it * rpi, r1, spl, sqsum, pf, it == wg);
+                    } else {
+                        const int j0 = (it - a.in_row_items) * kWaves;
+                        lora_dn_rows<NB>(q, sink, j0, min(j0 + kWaves, a.Rin), sq);
+                    }
+                }
+            }
+            // ================= phase B: epilogue + conv + SSM + gate
+            for (int it = wg; it < a.ssm_items; it += nwg) ssm_item(a, L, l, it, tag, vsh, ssh);
+            // ================= phase D: out_proj
+            if (wg < nDi) {
+                QuantGemvArgs q{};
+                q.W = L.w.gnorm_w;
+                q.K = a.E;
+                q.eps = a.eps;
+                q.sign = L.w.out_proj.sign;
+                q.n_out = a.D;
+                q.lora_dn = L.w.out_proj.lora_dn;
+                q.rank = a.Rout;
+                q.tap_u = T.out_u ? T.out_u + rec * a.E : nullptr;
+                q.tap_q = T.out_q ? T.out_q + rec * a.E : nullptr;
+                q.tap_s = T.out_s ? T.out_s + rec : nullptr;
+                q.tap_acc = T.out_acc ? T.out_acc + rec * a.D : nullptr;
+                q.tap_t = T.out_t ? T.out_t + rec * a.Rout : nullptr;
+                GemvPre pf{};
+                if (wg < a.out_row_items)
+                    gemv_prefetch(pf, q.sign, a.E, wg * a.out_rows_per_item, min((wg + 1) * a.out_rows_per_item, a.D));
+                for (int i = tid; i < a.ssm_items; i += kBlock) wait_flag(a, a.fb + (int64_t)l * a.ssm_items + i, tag);
+                __syncthreads();
+                const TaggedSource<KCH> src{&a, xb, a.E, tag};
+                norm_quant_prologue<NB, KCH>(q, src, sq, spl, sqsum, ssc, red, ired, nullptr);
+                if (wg == 0) {
+                    bc_conv_shift(a, L, l, tag);
+                    if (tid < NB) st_x(xd + tid * sd + a.D + a.Rout, tagged(fbits(ssc[tid]), tag));
+                }
+                const TaggedSink sink{xd, sd, a.D, tag};
+                for (int it = wg; it < nDi; it += nwg) {
+                    if (it < a.out_row_items) {
+                        const int r0 = it * a.out_rows_per_item;
+                        gemv_rows<NB>(q, sink, r0, min(r0 + a.out_rows_per_item, a.D), spl, sqsum, pf, it == wg);
+                    } else {
+                        const int j0 = (it - a.out_row_items) * kWaves;
+                        lora_dn_rows<NB>(q, sink, j0, min(j0 + kWaves, a.Rout), sq);
+                    }
+                }
+            }
+            // ================= phase E: out_proj epilogue + residual
+            {
+                const dfssm_proj &pj = L.w.out_proj;
+                const bool up_regs = (a.Rout & 15) == 0;
+                const int per_b = (a.D + kBlock - 1) / kBlock;
+                for (int it = wg; it < a.res_items; it += nwg) {
+                    const int b = it / per_b;
+                    const int n = (it - b * per_b) * kBlock + tid;
+                    const bool valid = n < a.D;
+                    const uint64_t *xdb = xd + (int64_t)b * sd;
+                    UpRow up;
+                    float sc = 0.f, us = 0.f;
+                    if (valid) {
+                        if (up_regs) load_up_row(up, pj.lora_up, a.Rout, n);
+                        sc = half_bits_to_float(pj.row_scale[n]);
+                        us = pj.lora_up_scale[n];
+                    }
+                    // every word this thread needs, requested at once, then polled if stale
+                    const uint64_t *p_s = xdb + a.D + a.Rout, *p_t = xdb + a.D + tid, *p_acc = xdb + n;
+                    const uint64_t *p_prev = xe_prev + (int64_t)b * a.D + n;
+                    const bool need_t = tid < a.Rout, need_prev = valid && l > 0;
+                    const uint32_t tag_prev = tag - 1;
+                    uint64_t w_s = ld_x(p_s);
+                    uint64_t w_t = need_t ? ld_x(p_t) : tagged(0, tag);
+                    uint64_t w_acc = valid ? ld_x(p_acc) : tagged(0, tag);
+                    uint64_t w_prev = need_prev ? ld_x(p_prev) : tagged(0, tag_prev);
+                    if ((uint32_t)(w_s >> 32) != tag) w_s = tagged(poll_word(a, p_s, tag), tag);
+                    if ((uint32_t)(w_t >> 32) != tag) w_t = tagged(poll_word(a, p_t, tag), tag);
+                    if ((uint32_t)(w_acc >> 32) != tag) w_acc = tagged(poll_word(a, p_acc, tag), tag);
+                    if ((uint32_t)(w_prev >> 32) != tag_prev) w_prev = tagged(poll_word(a, p_prev, tag_prev), tag_prev);
+                    const float s = bitsf((uint32_t)w_s);
+                    if (need_t) vsh[tid] = pj.lora_dn_scale[tid] * s * (float)(int)(uint32_t)w_t;
+                    __syncthreads();
+                    if (valid) {
+                        const float prev = l == 0 ? xsave[b * a.D + n] : bitsf((uint32_t)w_prev);
+                        const float lr = up_regs ? up_dot(up, a.Rout, vsh) : lowrank_row(pj.lora_up, a.Rout, n, vsh);
+                        st_x(xe + (int64_t)b * a.D + n,
+                             tagged(fbits(prev + (s * sc * (float)(int)(uint32_t)w_acc + us * lr)), tag));
+                    }
+                    publish(a.fe + (int64_t)l * a.res_items + it, tag);
+                }
+            }
+        }
+    }
+    // final RMSNorm of the last token
+    if (wg == 0) {
+        const uint32_t tag = (uint32_t)(a.n_steps * a.n_layers);
+        const int lp = a.n_layers - 1;
+        const uint64_t *xe = a.xe + (int64_t)lp * BD;
+        if (tid < a.res_items) wait_flag(a, a.fe + (int64_t)lp * a.res_items + tid, tag);
+        __syncthreads();
+        float *yt = a.y + (int64_t)(a.n_steps - 1) * BD;
+        for (int b = 0; b < a.batch; ++b) {
+            float ss = 0.f;
+            for (int e = tid; e < a.D; e += kBlock) {
+                const float v = bitsf(read_word(a, xe + (int64_t)b * a.D + e, tag));
+                ss += v * v;
+            }
+            const float tot = block_sum(ss, red);
+            const float r = 1.0f / sqrtf(tot / (float)a.D + a.eps);
+            for (int e = tid; e < a.D; e += kBlock)
+                yt[(int64_t)b * a.D + e] = (bitsf(read_word(a, xe + (int64_t)b * a.D + e, tag)) * r) * a.final_w[e];
+        }
+    }
+}
+
+size_t flow_lds_bytes(const Shape &s, int nb) {
+    return (size_t)nb * 2 * (s.D > s.E ? s.D : s.E) + (size_t)nb * s.D * 4;
+}
+
+// Rows of one head per SSM item: 1024 state values (one float4 per thread).
+int ssm_rows_per_item(const Shape &s) { return min(s.P, max(1, 1024 / s.N)); }
+
+// Item sizes: GEMV items are one or more workgroup row passes, grown until each phase has at
+// most `target` items (one resident workgroup each, all prefetched).
+void plan_items(FlowArgs &a, const Shape &s, int batch, int target) {
+    const int in_pass = kWaves * (64 / gemv_lanes_per_row(s.D));
+    const int out_pass = kWaves * (64 / gemv_lanes_per_row(s.E));
+    a.in_lora_items = (s.Rin + kWaves - 1) / kWaves;
+    a.out_lora_items = (s.Rout + kWaves - 1) / kWaves;
+    int m = 1;
+    while ((s.Nin + in_pass * m - 1) / (in_pass * m) + a.in_lora_items > target && m < 64) m *= 2;
+    a.in_rows_per_item = in_pass * m;
+    a.in_row_items = (s.Nin + a.in_rows_per_item - 1) / a.in_rows_per_item;
+    m = 1;
+    while ((s.D + out_pass * m - 1) / (out_pass * m) + a.out_lora_items > target && m < 64) m *= 2;
+    a.out_rows_per_item = out_pass * m;
+    a.out_row_items = (s.D + a.out_rows_per_item - 1) / a.out_rows_per_item;
+    a.ssm_rpw = ssm_rows_per_item(s);
+    a.ssm_items = batch * s.H * (s.P / a.ssm_rpw);
+    a.res_items = batch * ((s.D + kBlock - 1) / kBlock);
+}
+
+template <int NB, int KCH>
+hipError_t launch_flow(FlowArgs &a, const Shape &s, int max_wgs, hipStream_t stream) {
+    const size_t lds = flow_lds_bytes(s, NB);
+    int dev = 0, ncu = 0, per_cu = 0;
+    hipError_t e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_stack_flow<NB, KCH>),
+                                                           kBlock, lds)) != hipSuccess)
+        return e;
+    const int resident = per_cu * ncu;
+    if (resident < 1) return hipErrorInvalidConfiguration;
+    plan_items(a, s, a.batch, resident);
+    // flag regions [L][nA] | [L][ssm_items] | [L][nDi] | [L][res_items]; the item counts never
+    // exceed the finest-item counts flags_per_layer() reserves
+    const int64_t L = a.n_layers;
+    a.fb = a.fa + L * (a.in_row_items + a.in_lora_items);
+    a.fd = a.fb + L * a.ssm_items;
+    a.fe = a.fd + L * (a.out_row_items + a.out_lora_items);
+    const int want = max(max(a.in_row_items + a.in_lora_items, a.out_row_items + a.out_lora_items),
+                         max(a.ssm_items, a.res_items));
+    int grid = min(want, resident);
+    if (max_wgs > 0) grid = min(grid, max_wgs);
+    // residual items read the pre-normalised token input from the LDS of a phase-A workgroup
+    if (a.res_items > a.in_row_items + a.in_lora_items) return hipErrorInvalidConfiguration;
+    void *args[] = {&a};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_stack_flow<NB, KCH>), dim3(grid), dim3(kBlock),
+                                      args, lds, stream);
+}
+
+template <int NB>
+hipError_t launch_flow_nb(FlowArgs &a, const Shape &s, int max_wgs, hipStream_t stream) {
+    const int kmax = a.D > a.E ? a.D : a.E;
+    if (kmax <= 1024) return launch_flow<NB, 1>(a, s, max_wgs, stream);
+    if (kmax <= 2048) return launch_flow<NB, 2>(a, s, max_wgs, stream);
+    if (kmax <= 4096) return launch_flow<NB, 4>(a, s, max_wgs, stream);
+    return launch_flow<NB, 8>(a, s, max_wgs, stream);
+}
+
+// Upper bounds of the per-layer word and flag counts (item counts at the finest item size).
+size_t words_per_layer(const Shape &s, int batch) {
+    return (size_t)batch * ((size_t)(s.Ninp + s.Rin + 1) + s.E + (s.D + s.Rout + 1) + s.D + 2 * s.G * s.N);
+}
+size_t flags_per_layer(const Shape &s, int batch) {
+    const int in_pass = kWaves * (64 / gemv_lanes_per_row(s.D));
+    const int out_pass = kWaves * (64 / gemv_lanes_per_row(s.E));
+    const int rpw = ssm_rows_per_item(s);
+    return (size_t)(s.Nin + in_pass - 1) / in_pass + (s.Rin + kWaves - 1) / kWaves + (s.D + out_pass - 1) / out_pass +
+           (s.Rout + kWaves - 1) / kWaves + (size_t)batch * s.H * (s.P / rpw) + (size_t)batch * ((s.D + kBlock - 1) / kBlock);
+}
+
+}  // namespace
+
+bool stack_persistent_ok(const Shape &s, int batch) {
+    return batch >= 1 && batch <= kGemvMaxBatch && flow_lds_bytes(s, batch) <= (size_t)kGemvLdsBytes;
+}
+
+size_t stack_extra_ws_bytes(const Shape &s, int batch, int n_layers) {
+    return align_up((size_t)n_layers * sizeof(LayerEntry), 256) + 256 /*err*/ +
+           align_up((size_t)n_layers * (words_per_layer(s, batch) + flags_per_layer(s, batch)) * 8, 256);
+}
+
+hipError_t launch_stack_persistent(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states,
+                                   int n_layers, const float *final_w, const float *x0, float *y, int batch,
+                                   int n_steps, const DecodeWs &ws, void *extra, const dfssm_taps *taps,
+                                   int max_wgs, hipStream_t stream) {
+    (void)ws;
+    char *p = static_cast<char *>(extra);
+    LayerEntry *table = reinterpret_cast<LayerEntry *>(p);
+    p += align_up((size_t)n_layers * sizeof(LayerEntry), 256);
+    int *err = reinterpret_cast<int *>(p);
+    p += 256;
+    uint64_t *words = reinterpret_cast<uint64_t *>(p);
+    const int64_t nwords = (int64_t)n_layers * (words_per_layer(s, batch) + flags_per_layer(s, batch));
+    FlowArgs a{};
+    a.n_layers = n_layers;
+    a.n_steps = n_steps;
+    a.batch = batch;
+    a.D = s.D;
+    a.E = s.E;
+    a.N = s.N;
+    a.P = s.P;
+    a.H = s.H;
+    a.G = s.G;
+    a.Cd = s.Cd;
+    a.Nin = s.Nin;
+    a.Ninp = s.Ninp;
+    a.Rin = s.Rin;
+    a.Rout = s.Rout;
+    a.eps = s.eps;
+    a.layers = table;
+    a.final_w = final_w;
+    a.x0 = x0;
+    a.y = y;
+    const int64_t L = n_layers;
+    a.xa = words;
+    a.xb = a.xa + L * batch * (s.Ninp + s.Rin + 1);
+    a.xd = a.xb + L * batch * s.E;
+    a.xe = a.xd + L * batch * (s.D + s.Rout + 1);
+    a.bc = a.xe + L * batch * s.D;
+    uint64_t *flags = a.bc + L * batch * 2 * s.G * s.N;
+    a.fa = flags;                 // the other flag regions follow once the item counts are planned
+    a.err = err;
+    if (taps) a.taps = *taps;
+    hipError_t e;
+    for (int l0 = 0; l0 < n_layers; l0 += kLayersPerTableLaunch) {
+        LayerChunk c{};
+        const int n = min(kLayersPerTableLaunch, n_layers - l0);
+        for (int i = 0; i < n; ++i) c.e[i] = LayerEntry{layers[l0 + i], states[l0 + i]};
+        k_store_layers<<<1, 64, 0, stream>>>(table + l0, c, n);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    k_zero_words<<<256, 256, 0, stream>>>(words, nwords, err);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    switch (batch) {
+        case 1: return launch_flow_nb<1>(a, s, max_wgs, stream);
+        case 2: return launch_flow_nb<2>(a, s, max_wgs, stream);
+        case 3: return launch_flow_nb<3>(a, s, max_wgs, stream);
+        case 4: return launch_flow_nb<4>(a, s, max_wgs, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dfssm

@@ -323,3 +323,25 @@ def test_stack_decode_1p3b_48_layers_512_steps_sampled():
         if nxt is not None:
             assert PY.normwise(nxt, ho) < PY.TOL_LAYER
         h = ho
+
+
+def test_stack_decode_grid_size_invariance():
+    """The persistent kernel gives bit-identical results whatever the resident grid size, so every
+    work item is computed exactly once and the barriers order the phases."""
+    import os
+    nL, T, B = 3, 5, 2
+    layers = gen.stack_weights(TINY, nL, seed=4, random_norms=True, per_channel_lora=True)
+    states0 = [gen.initial_states(TINY, B, l, 4, std=0.2) for l in range(nL)]
+    x0 = gen.token_inputs(TINY, (B,), 4, tag=2)
+    say("case: tiny stack decode, default grid")
+    y_ref, st_ref, _ = run_stack(TINY, layers, x0, states0, T)
+    try:
+        for g in (1, 7, 64):
+            os.environ["DFSSM_STACK_MAX_WGS"] = str(g)
+            say(f"case: tiny stack decode, grid capped at {g} workgroups")
+            y, st, _ = run_stack(TINY, layers, x0, states0, T)
+            assert (y == y_ref).all(), g
+            for l in range(nL):
+                assert (st[l][0] == st_ref[l][0]).all() and (st[l][1] == st_ref[l][1]).all(), (g, l)
+    finally:
+        os.environ.pop("DFSSM_STACK_MAX_WGS", None)
