@@ -2,6 +2,8 @@
 // Every check happens before the first enqueue, so a rejected call has no side effect.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "dfssm_internal.h"
 
 namespace dfssm {
@@ -83,7 +85,27 @@ int check_taps(const dfssm_taps *t) {
 
 size_t decode_ws_bytes(const Shape &s, int batch, bool stack, int n_layers = 0) {
     DecodeWs w = carve_decode_ws(s, batch, nullptr, stack);
-    return w.bytes + (stack && stack_persistent_ok(s, batch) ? stack_extra_ws_bytes(s, batch, n_layers) : 0);
+    size_t extra = 0;
+    if (stack && stack_persistent_ok(s, batch)) extra = stack_extra_ws_bytes(s, batch, n_layers);
+    else if (decode_uses_mfma(s, batch)) extra = carve_prefill_ws(s, batch, 1, 1, nullptr).bytes;
+    return w.bytes + extra;
+}
+
+bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128 || chunk == 256; }
+
+size_t prefill_ws_bytes(const Shape &s, int batch, int seqlen, int chunk) {
+    return carve_prefill_ws(s, batch, seqlen, chunk, nullptr).bytes;
+}
+
+// One decode step of one layer through whichever projection path suits the batch.
+hipError_t decode_step(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st, const float *x_in,
+                       float *x_out, int batch, void *ws, bool stack, const TapPtrs &tp, hipStream_t stream) {
+    const DecodeWs d = carve_decode_ws(s, batch, ws, stack);
+    if (decode_uses_mfma(s, batch)) {
+        const PrefillWs p = carve_prefill_ws(s, batch, 1, 1, static_cast<char *>(ws) + d.bytes);
+        return launch_layer_decode_mfma(s, w, st, x_in, x_out, batch, d, p, tp, stream);
+    }
+    return launch_layer_decode(s, w, st, x_in, x_out, batch, d, tp, stream);
 }
 
 int env_int(const char *name, int dflt) {
@@ -156,8 +178,14 @@ size_t dfssm_workspace_bytes(const dfssm_dims *dims, int32_t op, int32_t batch, 
             if (n_layers <= 0) return 0;
             return decode_ws_bytes(s, batch, true, n_layers);
         case DFSSM_OP_LAYER_PREFILL:
-            (void)seqlen;
-            return 0;
+            if (seqlen <= 0 || seqlen > 65536 || batch > 64 || (int64_t)batch * seqlen > (1 << 20) || s.Rin % 8 ||
+                s.Rout % 8)
+                return 0;
+            {   // enough for every supported chunk length
+                size_t mx = 0;
+                for (int c = 16; c <= 256; c *= 2) mx = std::max(mx, prefill_ws_bytes(s, batch, seqlen, c));
+                return mx;
+            }
         default: return 0;
     }
 }
@@ -173,10 +201,8 @@ int dfssm_layer_decode(const dfssm_dims *dims, const dfssm_layer_weights *w, con
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
     const Shape s = shape_of(*dims);
     if (ws_bytes < decode_ws_bytes(s, batch, false)) return DFSSM_EWORKSPACE;
-    const DecodeWs wsp = carve_decode_ws(s, batch, ws, false);
     const TapPtrs tp = tap_offset(taps, s, 0);
-    return hip_status(launch_layer_decode(s, *w, *state, x_in, x_out, batch, wsp, tp,
-                                          static_cast<hipStream_t>(stream)));
+    return hip_status(decode_step(s, *w, *state, x_in, x_out, batch, ws, false, tp, static_cast<hipStream_t>(stream)));
 }
 
 int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w, const dfssm_layer_state *state,
@@ -187,8 +213,16 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w, co
     if ((r = check_weights(w)) || (r = check_state(state)) || (r = check_taps(taps))) return r;
     if (bad_ptr(x_in) || bad_ptr(x_out) || batch <= 0 || seqlen <= 0) return DFSSM_EINVAL;
     if (x_dtype != DFSSM_F32 && x_dtype != DFSSM_BF16) return DFSSM_EINVAL;
-    (void)chunk; (void)ws; (void)ws_bytes; (void)stream;
-    return DFSSM_EUNSUPPORTED;
+    if (x_in == static_cast<const void *>(x_out)) return DFSSM_EINVAL;
+    if (!chunk_ok(chunk)) return DFSSM_EUNSUPPORTED;
+    if (seqlen > 65536 || batch > 64 || (int64_t)batch * seqlen > (1 << 20)) return DFSSM_EUNSUPPORTED;
+    const Shape s = shape_of(*dims);
+    if (s.Rin % 8 || s.Rout % 8) return DFSSM_EUNSUPPORTED;
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
+    if (ws_bytes < prefill_ws_bytes(s, batch, seqlen, chunk)) return DFSSM_EWORKSPACE;
+    const PrefillWs p = carve_prefill_ws(s, batch, seqlen, chunk, ws);
+    return hip_status(launch_layer_prefill(s, *w, *state, x_in, x_dtype == DFSSM_BF16, x_out, batch, seqlen, chunk, p,
+                                           taps, static_cast<hipStream_t>(stream)));
 }
 
 int dfssm_stack_decode(const dfssm_dims *dims, const dfssm_layer_weights *layers, const dfssm_layer_state *states,
@@ -219,7 +253,7 @@ int dfssm_stack_decode(const dfssm_dims *dims, const dfssm_layer_weights *layers
         const float *xin = t == 0 ? x0 : y + (t - 1) * rowsz;
         for (int l = 0; l < n_layers; ++l) {
             const TapPtrs tp = tap_offset(taps, s, ((int64_t)t * n_layers + l) * batch);
-            e = launch_layer_decode(s, layers[l], states[l], l == 0 ? xin : wsp.hbuf, wsp.hbuf, batch, wsp, tp, st);
+            e = decode_step(s, layers[l], states[l], l == 0 ? xin : wsp.hbuf, wsp.hbuf, batch, ws, true, tp, st);
             if (e != hipSuccess) return DFSSM_EHIP;
         }
         e = launch_final_norm(wsp.hbuf, final_norm_w, y + t * rowsz, nullptr, s.D, s.eps, batch, st);

@@ -179,6 +179,28 @@ hipError_t launch_quant_gemv(QuantGemvArgs a, int nb, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_ssm_step(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
+                           const DecodeWs &ws, int batch, hipStream_t stream) {
+    SsmArgs a{};
+    a.xbc = ws.xbc;
+    a.zbuf = ws.zbuf;
+    a.dtbuf = ws.dtbuf;
+    a.ssm = st.ssm;
+    a.A_log = w.A_log;
+    a.D = w.D;
+    a.gbuf = ws.gbuf;
+    a.E = s.E;
+    a.H = s.H;
+    a.P = s.P;
+    a.N = s.N;
+    a.G = s.G;
+    a.Cd = s.Cd;
+    a.rows_per_wg = min(s.P, 2048 / s.N);
+    dim3 grid(s.H * (s.P / a.rows_per_wg), batch);
+    k_ssm<<<grid, kBlock, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_layer_decode(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
                                const float *x_in, float *x_out, int batch, const DecodeWs &ws,
                                const TapPtrs &tp, hipStream_t stream) {
@@ -230,26 +252,7 @@ hipError_t launch_layer_decode(const Shape &s, const dfssm_layer_weights &w, con
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 3. SSM step + gate
-    {
-        SsmArgs a{};
-        a.xbc = ws.xbc;
-        a.zbuf = ws.zbuf;
-        a.dtbuf = ws.dtbuf;
-        a.ssm = st.ssm;
-        a.A_log = w.A_log;
-        a.D = w.D;
-        a.gbuf = ws.gbuf;
-        a.E = s.E;
-        a.H = s.H;
-        a.P = s.P;
-        a.N = s.N;
-        a.G = s.G;
-        a.Cd = s.Cd;
-        a.rows_per_wg = min(s.P, 2048 / s.N);
-        dim3 grid(s.H * (s.P / a.rows_per_wg), batch);
-        k_ssm<<<grid, kBlock, 0, stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    if ((e = launch_ssm_step(s, w, st, ws, batch, stream)) != hipSuccess) return e;
     // 4. out-proj
     for (int b0 = 0; b0 < batch; b0 += grp_out) {
         const int nb = min(grp_out, batch - b0);

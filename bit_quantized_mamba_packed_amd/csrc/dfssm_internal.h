@@ -61,6 +61,78 @@ hipError_t launch_stack_persistent(const Shape &s, const dfssm_layer_weights *la
                                    void *extra, const dfssm_taps *taps, int max_wgs, hipStream_t stream);
 bool stack_persistent_ok(const Shape &s, int batch);
 
+// int8-code x (+-1 scaffold) GEMM with the projection epilogue (gemm.hip):
+//   y[m][n] = s[m]*row_scale[n]*acc[m][n] + up_scale[n] * sum_j t'[m][j]*lora_up[n][j] (+ res[m][n])
+// acc = sum_k sgn[n][k]*q[m][k]; t' = thi + tlo (bf16 split of dn_scale*s*t). rank % 8 == 0, K % 64 == 0.
+struct GemmArgs {
+    const int8_t *q;
+    int64_t ldq;
+    const int32_t *qsum;
+    const float *s;
+    const uint8_t *sign;
+    int M, N, K;
+    const uint16_t *row_scale;
+    const float *up_scale;
+    const int8_t *lora_up;
+    int rank;
+    const __bf16 *thi, *tlo;
+    float *y;
+    int64_t ldy;
+    const float *res;      // optional
+    int64_t ldres;
+    int32_t *acc_tap;      // optional
+    int64_t ldacc;
+};
+hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream);
+
+// Per-token RMSNorm + int8 quantizer + int8 LoRA-down for M tokens (prefill / batched decode):
+// writes codes q [M][K], s, sum of codes, and t' = dn_scale * s * t split into bf16 hi/lo [M][rank].
+struct TokQuantArgs {
+    const void *X;         // [M][ldx] fp32 or bf16 bit patterns
+    int x_bf16;
+    int64_t ldx;
+    const float *W;        // norm weight [K]
+    int M, K;
+    float eps;
+    const int8_t *lora_dn; // [rank][K]
+    const float *dn_scale; // [rank]
+    int rank;
+    int8_t *q;             // [M][K]
+    float *s;
+    int32_t *qsum;
+    __bf16 *thi, *tlo;     // [M][rank]
+    float *tap_h, *tap_u, *tap_s;
+    int8_t *tap_q;
+    int32_t *tap_t;
+};
+hipError_t launch_tok_quant(const TokQuantArgs &a, hipStream_t stream);
+
+// Prefill workspace carve-up (tokens M = batch * seqlen, chunk Q).
+struct PrefillWs {
+    int8_t *q_in, *q_out;
+    float *s_in, *s_out;
+    int32_t *qsum_in, *qsum_out;
+    __bf16 *thi_in, *tlo_in, *thi_out, *tlo_out;
+    float *Y, *xbc, *dt, *lam, *lam_end, *cb, *ydiag, *sloc, *gbuf;
+    size_t bytes;
+};
+PrefillWs carve_prefill_ws(const Shape &s, int batch, int seqlen, int chunk, void *base);
+
+hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
+                                const void *x_in, int x_bf16, float *x_out, int batch, int seqlen, int chunk,
+                                const PrefillWs &ws, const dfssm_taps *taps, hipStream_t stream);
+
+// Per-layer SSM step + gate for `batch` tokens from ws.xbc/zbuf/dtbuf into ws.gbuf (decode.hip).
+hipError_t launch_ssm_step(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
+                           const DecodeWs &ws, int batch, hipStream_t stream);
+
+// One decode step of one layer for many tokens through the int8-MFMA projections (prefill.hip);
+// pws is a prefill workspace carved for (batch, seqlen 1, chunk 1).
+hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
+                                    const float *x_in, float *x_out, int batch, const DecodeWs &dws,
+                                    const PrefillWs &pws, const TapPtrs &taps, hipStream_t stream);
+bool decode_uses_mfma(const Shape &s, int batch);
+
 // Enqueue y = RMSNorm(h) * w for `batch` rows of length D, also copying y to `y2` when non-null.
 hipError_t launch_final_norm(const float *h, const float *w, float *y, float *y2, int D, float eps,
                              int batch, hipStream_t stream);

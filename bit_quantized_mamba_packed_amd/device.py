@@ -121,3 +121,14 @@ def stack_decode(d, layers: list, states: list, final_w: torch.Tensor, x0: torch
                               x0.shape[0], n_steps, ws.data_ptr(), ws.numel(),
                               None if taps is None else taps.struct, stream_handle())
     L.check(st, "dfssm_stack_decode")
+
+
+def layer_prefill(d, layer: DeviceLayer, state: DeviceState, x_in: torch.Tensor, x_out: torch.Tensor, chunk: int,
+                  ws: torch.Tensor, taps: Taps = None) -> None:
+    """x_in [batch][seqlen][d_model] fp32 or bf16 (torch.bfloat16 is passed as its bit patterns)."""
+    batch, seqlen = x_in.shape[0], x_in.shape[1]
+    dtype = L.DFSSM_BF16 if x_in.dtype == torch.bfloat16 else L.DFSSM_F32
+    st = L.dfssm_layer_prefill(dims_struct(d), layer.struct, state.struct, x_in.data_ptr(), dtype, x_out.data_ptr(),
+                               batch, seqlen, chunk, ws.data_ptr(), ws.numel(),
+                               None if taps is None else taps.struct, stream_handle())
+    L.check(st, "dfssm_layer_prefill")

@@ -27,7 +27,7 @@
  *  - Every pointer is a DEVICE pointer (hipMalloc'd or equivalent) unless marked HOST.
  *  - The caller owns all memory. Weights are read-only; states are updated in place; no pointer
  *    is retained after the enqueued work completes. The library allocates no device memory
- *    inside these calls (stack_decode creates and destroys a HIP graph, see below).
+ *    inside these calls; every intermediate lives in the caller's workspace.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream). A return of
  *    DFSSM_OK means the work was enqueued; device faults surface at the caller's next sync.
  *  - Every argument is validated before anything is enqueued, so a call that returns an error
@@ -135,9 +135,9 @@ typedef struct dfssm_taps {
 
 /*
  * Bytes of device workspace `op` needs for this shape, batch, sequence length and layer count
- * (seqlen is ignored by the decode ops, n_layers by the single-layer ops). Returns 0 for an
- * invalid or unsupported shape. The workspace needs no initialisation and holds nothing
- * between calls.
+ * (seqlen is ignored by the decode ops, n_layers by the single-layer ops; for the prefill op the
+ * size covers every supported chunk length). Returns 0 for an invalid or unsupported shape.
+ * The workspace needs no initialisation and holds nothing between calls.
  */
 size_t dfssm_workspace_bytes(const dfssm_dims *dims, int32_t op, int32_t batch, int32_t seqlen,
                              int32_t n_layers);
@@ -147,7 +147,9 @@ size_t dfssm_workspace_bytes(const dfssm_dims *dims, int32_t op, int32_t batch, 
  * paper's headline; Table 2 runs batches up to 512).
  *   dims, w, state, taps: HOST pointers to the structs above (their members are device pointers);
  *   x_in [batch][d_model] fp32 residual input; x_out [batch][d_model] fp32 = x_in + mixer output
- *   (x_out may alias x_in). state is read and updated in place. 1 <= batch <= 4096.
+ *   (x_out may alias x_in). state is read and updated in place. 1 <= batch <= 4096. Up to 4 tokens
+ *   share one pass of a packed-sign GEMV; larger batches (with ranks that are multiples of 8) run the
+ *   projections as int8 MFMA GEMMs.
  * Returns DFSSM_OK or a negative status.
  */
 int dfssm_layer_decode(const dfssm_dims *dims, const dfssm_layer_weights *w,
@@ -162,7 +164,9 @@ int dfssm_layer_decode(const dfssm_dims *dims, const dfssm_layer_weights *w,
  * `chunk` (the state-space-duality block form of Mamba-2, which the paper builds on, §2).
  *   x_in  [batch][seqlen][d_model], fp32 (x_dtype DFSSM_F32) or bf16 bit patterns (DFSSM_BF16)
  *   x_out [batch][seqlen][d_model] fp32 (must not alias x_in)
- *   chunk in {16, 32, 64, 128, 256}; 1 <= seqlen <= 65536; 1 <= batch <= 64.
+ *   chunk in {16, 32, 64, 128, 256}; 1 <= seqlen <= 65536; 1 <= batch <= 64; batch*seqlen <= 2^20;
+ *   rank_in and rank_out
+ *   multiples of 8 (the projections run as int8 MFMA GEMMs over all batch*seqlen tokens).
  */
 int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w,
                         const dfssm_layer_state *state, const void *x_in, int32_t x_dtype,
@@ -173,9 +177,11 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w,
  * Autoregressive-style decode through a stack of n_layers layers for n_steps tokens:
  *   x(0) = x0;  for t: h = x(t); h = layer_l(h) for l = 0..n_layers-1;
  *   y[t] = RMSNorm(h) * final_norm_w;  x(t+1) = y[t].
- * The per-token layer sequence is launched as one HIP graph replayed n_steps times (paper
- * §4.1 captures the whole forward pass in a graph); the graph is created and destroyed inside
- * the call.
+ * The whole token loop runs as ONE persistent kernel launch (the paper's §4.1 captures the forward
+ * pass in a graph to remove per-kernel launch cost; here the layers hand their partial results to
+ * each other through tagged words in the workspace instead of kernel boundaries). When the device
+ * cannot keep the needed workgroups resident at once, the call falls back to per-layer kernels
+ * with the same results.
  *   layers, states: HOST arrays [n_layers] of the structs above; final_norm_w [d_model] fp32;
  *   x0 [batch][d_model] fp32; y [n_steps][batch][d_model] fp32 (must not alias x0);
  *   taps: NULL or records laid out [n_steps][n_layers][batch][...].

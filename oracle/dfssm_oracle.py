@@ -34,6 +34,8 @@ What each function follows and what pins it (the pins live in tests/test_oracle_
                     chunk sizes and the SSD quadratic (masked-attention) form
   layer_prefill     defined as sequential decode steps (quantization is per token).
                     pinned by: prefill(L1) then decode(L2) == decode(L1 + L2)
+  layer_tokens      the same steps run stage by stage over the sequence (batched projections).
+                    pinned by: equals layer_decode_steps (codes, integer sums and floats)
   table1_bytes      [DF-SSM] §3.3 Table 1.  pinned by the table's printed sizes
 
 Readings where the page is silent (also listed in the design doc):
@@ -127,6 +129,20 @@ def project(q: np.ndarray, s, P, dense_sign: Optional[np.ndarray] = None) -> tup
     sc = np.asarray(P.row_scale, np.float16).astype(F64)
     v = np.asarray(P.dn_scale, F64) * s64 * t
     y = s64 * sc * acc + np.asarray(P.up_scale, F64) * (np.asarray(P.lora_up, F64) @ v)
+    return y, acc.astype(np.int64), t.astype(np.int64)
+
+
+def project_tokens(q: np.ndarray, s, P, dense_sign: Optional[np.ndarray] = None) -> tuple:
+    """project() for many tokens at once: q int8 [M][n_in], s [M] -> (y [M][n_out], acc, t).
+    The same definition evaluated with one matrix product per factor (every token is independent)."""
+    sgn = unpack_signs(P.sign, P.n_in) if dense_sign is None else dense_sign
+    qf = np.asarray(q, F64)
+    acc = qf @ sgn.astype(F64).T
+    t = qf @ np.asarray(P.lora_dn, F64).T
+    s64 = np.asarray(s, np.float32).astype(F64)[:, None]
+    sc = np.asarray(P.row_scale, np.float16).astype(F64)[None, :]
+    v = np.asarray(P.dn_scale, F64)[None, :] * s64 * t
+    y = s64 * sc * acc + np.asarray(P.up_scale, F64)[None, :] * (v @ np.asarray(P.lora_up, F64).T)
     return y, acc.astype(np.int64), t.astype(np.int64)
 
 
@@ -245,6 +261,50 @@ def layer_prefill(xs, W, conv_state, ssm_state):
     Quantization is per token, so this is the method's exact semantics; the chunked scan a
     prefill kernel uses is an evaluation order of the same result (see ssd_chunked)."""
     return layer_decode_steps(xs, W, conv_state, ssm_state)
+
+
+def layer_tokens(xs, W, conv_state, ssm_state, force: Optional[dict] = None, dense: Optional[dict] = None):
+    """layer_decode_steps evaluated stage by stage over a sequence xs [T][d_model].
+
+    Stage k of token t needs only stage k-1 of tokens <= t, so running each stage over all T
+    tokens before the next (projections as one matrix product, conv and recurrence as loops over
+    t) gives the sequential-decode result. ``force`` may hold per-token arrays 'in_q' [T][D],
+    'in_s' [T], 'out_q' [T][E], 'out_s' [T] (see layer_decode).
+    Returns (outs [T][d_model], conv_state, ssm_state, taps dict of arrays [T][...])."""
+    dm = W.dims
+    E, H, N, G = dm.d_inner, dm.nheads, dm.d_state, dm.ngroups
+    Cd = dm.conv_dim
+    xs = np.asarray(xs, F64)
+    T = xs.shape[0]
+    dense = dense_signs(W) if dense is None else dense
+    u = rmsnorm(xs, W.norm_w, dm.eps).astype(F32)
+    q = np.empty((T, dm.d_model), np.int8)
+    s = np.empty(T, F32)
+    for t in range(T):
+        q[t], s[t] = quantize_token(u[t])
+    if force is not None and "in_q" in force:
+        q, s = np.asarray(force["in_q"], np.int8), np.asarray(force["in_s"], F32)
+    Y, acc, tt = project_tokens(q, s, W.in_proj, dense["in"])
+    z = Y[:, :E]
+    dt = softplus(Y[:, E + Cd:E + Cd + H] + np.asarray(W.dt_bias, F64))
+    A = -np.exp(np.asarray(W.A_log, F64))
+    cs, ss = np.asarray(conv_state, F64), np.asarray(ssm_state, F64)
+    y = np.empty((T, E))
+    for t in range(T):
+        xbc_act, cs = conv_step(cs, Y[t, E:E + Cd], W.conv_w, W.conv_b)
+        Bm = xbc_act[E:E + G * N].reshape(G, N)
+        Cm = xbc_act[E + G * N:E + 2 * G * N].reshape(G, N)
+        y[t], ss = ssm_step(ss, xbc_act[:E], Bm, Cm, dt[t], A, W.D, G)
+    u2 = gated_rmsnorm(y, z, W.gnorm_w, dm.eps)[0].astype(F32)
+    q2 = np.empty((T, E), np.int8)
+    s2 = np.empty(T, F32)
+    for t in range(T):
+        q2[t], s2[t] = quantize_token(u2[t])
+    if force is not None and "out_q" in force:
+        q2, s2 = np.asarray(force["out_q"], np.int8), np.asarray(force["out_s"], F32)
+    o, acc2, t2 = project_tokens(q2, s2, W.out_proj, dense["out"])
+    taps = dict(in_u=u, in_q=q, in_s=s, in_acc=acc, in_t=tt, out_u=u2, out_q=q2, out_s=s2, out_acc=acc2, out_t=t2)
+    return xs + o, cs, ss, taps
 
 
 def stack_decode(x0, layers, conv_states, ssm_states, n_steps: int, final_w, eps: float,

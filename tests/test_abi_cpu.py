@@ -139,3 +139,46 @@ def test_strerror():
     for s in (L.DFSSM_OK, L.DFSSM_EINVAL, L.DFSSM_EUNSUPPORTED, L.DFSSM_EWORKSPACE, L.DFSSM_EHIP):
         assert len(L.dfssm_strerror(s)) > 3
     assert L.dfssm_strerror(12345) == "unknown status"
+
+
+def test_prefill_workspace_and_rejects_bad_arguments():
+    d = _dims()
+    ws1 = L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_PREFILL, 1, 300)
+    assert ws1 > 0
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_PREFILL, 2, 300) > ws1
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_PREFILL, 1, 0) == 0
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_PREFILL, 1, 65537) == 0
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_PREFILL, 65, 16) == 0
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_PREFILL, 32, 65536) == 0     # > 2^20 tokens
+    assert L.dfssm_workspace_bytes(_dims(rank_in=4), L.DFSSM_OP_LAYER_PREFILL, 1, 16) == 0
+    w = _fake_weights()
+    st = L.dfssm_layer_state(FAKE, FAKE)
+    X2 = FAKE + 0x100000
+    ok = dict(x_in=FAKE, dt=L.DFSSM_F32, x_out=X2, batch=1, seqlen=300, chunk=64, ws=FAKE, ws_bytes=ws1)
+
+    def call(dims=d, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.dfssm_layer_prefill(dims, w, st, a["x_in"], a["dt"], a["x_out"], a["batch"], a["seqlen"],
+                                     a["chunk"], a["ws"], a["ws_bytes"])
+
+    assert call(x_in=None) == L.DFSSM_EINVAL
+    assert call(x_out=FAKE) == L.DFSSM_EINVAL                 # aliases x_in
+    assert call(dt=7) == L.DFSSM_EINVAL
+    assert call(seqlen=0) == L.DFSSM_EINVAL
+    assert call(chunk=48) == L.DFSSM_EUNSUPPORTED
+    assert call(chunk=512) == L.DFSSM_EUNSUPPORTED
+    assert call(batch=65) == L.DFSSM_EUNSUPPORTED
+    assert call(seqlen=65537) == L.DFSSM_EUNSUPPORTED
+    assert call(dims=_dims(rank_out=12)) == L.DFSSM_EUNSUPPORTED
+    assert call(ws_bytes=4096) == L.DFSSM_EWORKSPACE       # below what any chunk length needs
+    assert call(ws=FAKE + 8) == L.DFSSM_EINVAL
+
+
+def test_batched_decode_workspace_covers_the_mfma_path():
+    d = _dims()
+    w4 = L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_DECODE, 4)
+    w5 = L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_DECODE, 5)
+    # beyond 4 tokens the projections run as GEMMs over per-token codes held in the workspace
+    assert w5 > w4 * 5 // 4 + 5 * d.d_model
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_DECODE, 64, 0, 48) > 0

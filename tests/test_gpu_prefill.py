@@ -1,0 +1,190 @@
+"""GPU parity of dfssm_layer_prefill against the CPU oracle.
+
+Prefill is defined as sequential decode steps (quantization is per token); the kernels evaluate
+the projections as int8 MFMA GEMMs over all tokens and the recurrence as a chunked scan. Every
+case checks the P1/P2 protocol of dfssm_parity per token: codes exact against the oracle
+quantizer of the GPU's own u, integer sums exact, and the oracle run with the GPU's codes forced
+in within 1e-3 on outputs and on the final conv/SSM states."""
+import numpy as np
+import pytest
+import torch
+
+from synth import gen
+from oracle import dfssm_oracle as O
+import dfssm_parity as PY
+from test_gpu_decode import _lib, say, run_layer
+
+pytestmark = pytest.mark.gpu
+
+TINY = gen.DIMS["tiny"]
+BIG = gen.DIMS["1p3b"]
+
+
+def run_prefill(dims, lw, xs, conv0, ssm0, chunk, bf16=False, taps=True):
+    """xs [B][L][D] fp32 (bf16-representable when bf16) -> (out [B][L][D], taps [B][L][...], states)."""
+    L, Dv = _lib()
+    B, T = xs.shape[:2]
+    dev = Dv.DeviceLayer(lw)
+    st = Dv.DeviceState(conv0, ssm0)
+    x = torch.from_numpy(np.ascontiguousarray(xs)).cuda()
+    if bf16:
+        x = x.to(torch.bfloat16)
+        assert (x.float().cpu().numpy() == xs).all(), "inputs must be bf16-representable"
+    y = torch.empty((B, T, dims.d_model), dtype=torch.float32, device="cuda")
+    ws = Dv.workspace(dims, L.DFSSM_OP_LAYER_PREFILL, B, T)
+    tp = Dv.Taps(dims, B * T) if taps else None
+    Dv.layer_prefill(dims, dev, st, x, y, chunk, ws, tp)
+    torch.cuda.synchronize()
+    tps = None
+    if taps:
+        tps = {k: v.reshape(B, T, *v.shape[1:]) for k, v in tp.numpy().items()}
+    return y.cpu().numpy(), tps, (st.conv.cpu().numpy(), st.ssm.cpu().numpy())
+
+
+def check_sequence(lw, xs, conv0, ssm0, out, tps, final, dense=None, tol=PY.TOL_LAYER, what=""):
+    """P1 + P2 over one sequence (batch row): xs [T][D], tps dict of [T][...]."""
+    T = xs.shape[0]
+    assert (tps["h_in"] == xs).all(), f"{what}: h_in tap is not the layer input"
+    for t in range(T):
+        PY.assert_codes_exact(tps["in_u"][t], tps["in_q"][t], tps["in_s"][t][0], f"{what} t={t} in")
+        PY.assert_codes_exact(tps["out_u"][t], tps["out_q"][t], tps["out_s"][t][0], f"{what} t={t} out")
+    force = dict(in_q=tps["in_q"], in_s=tps["in_s"][:, 0], out_q=tps["out_q"], out_s=tps["out_s"][:, 0])
+    o, cs, ss, otp = O.layer_tokens(xs, lw, conv0, ssm0, force=force, dense=dense)
+    # the oracle's integer sums of the GPU's codes (P1)
+    assert (tps["in_acc"].astype(np.int64)[:, :otp["in_acc"].shape[1]] == otp["in_acc"]).all(), f"{what}: in acc"
+    assert (tps["in_t"].astype(np.int64) == otp["in_t"]).all(), f"{what}: in t"
+    assert (tps["out_acc"].astype(np.int64) == otp["out_acc"]).all(), f"{what}: out acc"
+    assert (tps["out_t"].astype(np.int64) == otp["out_t"]).all(), f"{what}: out t"
+    e_in = max(PY.normwise(tps["in_u"][t], otp["in_u"][t]) for t in range(T))
+    e_ou = max(PY.normwise(tps["out_u"][t], otp["out_u"][t]) for t in range(T))
+    e_o = max(PY.normwise(out[t], o[t]) for t in range(T))
+    e_c, e_s = PY.normwise(final[0], cs), PY.normwise(final[1], ss)
+    errs = dict(in_u=e_in, out_u=e_ou, out=e_o, conv=e_c, ssm=e_s)
+    assert e_in < 1e-5, f"{what}: {errs}"
+    for k in ("out_u", "out", "conv", "ssm"):
+        assert errs[k] < tol, f"{what}: {k} {errs}"
+    return errs
+
+
+def free_running_sequence(lw, xs, conv0, ssm0, out, tps, dense=None, what=""):
+    """The oracle on its own codes. In-codes depend only on the inputs, so every in-code flip must
+    sit at a rounding tie; out-codes and outputs are compared up to the first in-code flip."""
+    o, _, _, otp = O.layer_tokens(xs, lw, conv0, ssm0, dense=dense)
+    T = xs.shape[0]
+    first = T
+    for t in range(T):
+        f, ok = PY.flips_at_ties(otp["in_u"][t], otp["in_q"][t], tps["in_q"][t])
+        if f:
+            assert ok, f"{what} t={t}: an in-code flip away from a rounding tie"
+            first = min(first, t)
+    errs = []
+    for t in range(first):
+        f, ok = PY.flips_at_ties(otp["out_u"][t], otp["out_q"][t], tps["out_q"][t])
+        if f:
+            assert ok, f"{what} t={t}: an out-code flip away from a rounding tie"
+            continue
+        errs.append(PY.normwise(out[t], o[t]))
+    if errs:
+        assert max(errs) < PY.TOL_LAYER, f"{what}: {max(errs)}"
+    return (max(errs) if errs else 0.0), first
+
+
+@pytest.mark.parametrize("chunk", [16, 64, 256])
+def test_prefill_tiny_ragged_nonzero_state(chunk):
+    B, T = 2, 300      # 300 = ragged for every chunk length
+    lw = gen.layer_weights(TINY, 5, 11, random_norms=True, per_channel_lora=True)
+    conv0, ssm0 = gen.initial_states(TINY, B, 5, 11, std=0.3)
+    xs = gen.token_inputs(TINY, (B, T), 11, tag=1)
+    say(f"case: tiny prefill, batch {B}, seqlen {T}, chunk {chunk}, nonzero state, fp32 input")
+    out, tps, final = run_prefill(TINY, lw, xs, conv0, ssm0, chunk)
+    dense = O.dense_signs(lw)
+    for b in range(B):
+        tb = {k: v[b] for k, v in tps.items()}
+        errs = check_sequence(lw, xs[b], conv0[b], ssm0[b], out[b], tb, (final[0][b], final[1][b]), dense,
+                              what=f"chunk {chunk} row {b}")
+        fr, first = free_running_sequence(lw, xs[b], conv0[b], ssm0[b], out[b], tb, dense, what=f"row {b}")
+        say(f"chunk {chunk} row {b}: forced {errs}; free-running {fr:.2e} up to token {first}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 33])
+def test_prefill_tiny_short_sequences_bf16(T):
+    """Sequences shorter than the conv window (the new conv state still holds old entries) and
+    than one chunk, with bf16 inputs."""
+    B = 3
+    lw = gen.layer_weights(TINY, 6, 12, random_norms=True)
+    conv0, ssm0 = gen.initial_states(TINY, B, 6, 12, std=0.3)
+    xs = gen.token_inputs(TINY, (B, T), 12, tag=2, bf16=True)
+    say(f"case: tiny prefill, batch {B}, seqlen {T}, chunk 32, bf16 input")
+    out, tps, final = run_prefill(TINY, lw, xs, conv0, ssm0, 32, bf16=True)
+    dense = O.dense_signs(lw)
+    for b in range(B):
+        tb = {k: v[b] for k, v in tps.items()}
+        check_sequence(lw, xs[b], conv0[b], ssm0[b], out[b], tb, (final[0][b], final[1][b]), dense,
+                       what=f"T={T} row {b}")
+
+
+def test_prefill_then_decode_state_handoff():
+    """prefill(L1) leaves the state that L2 decode steps continue from: the oracle runs all
+    L1 + L2 tokens in one sequence with the GPU's codes forced in."""
+    L1, L2 = 100, 6
+    lw = gen.layer_weights(TINY, 7, 13, per_channel_lora=True)
+    conv0, ssm0 = gen.initial_states(TINY, 1, 7, 13, std=0.2)
+    xs = gen.token_inputs(TINY, (1, L1 + L2), 13, tag=3)
+    say(f"case: tiny prefill {L1} tokens (chunk 32) then {L2} decode steps")
+    out_p, tps_p, mid = run_prefill(TINY, lw, xs[:, :L1], conv0, ssm0, 32)
+    xs_d = np.ascontiguousarray(np.transpose(xs[:, L1:], (1, 0, 2)))     # [L2][1][D]
+    out_d, tps_d, final, _ = run_layer(TINY, lw, xs_d, mid[0], mid[1])
+    tps = {k: np.concatenate([tps_p[k][0], np.stack([tp[k][0] for tp in tps_d])]) for k in tps_p}
+    out = np.concatenate([out_p[0], out_d[:, 0]])
+    errs = check_sequence(lw, xs[0], conv0[0], ssm0[0], out, tps, (final[0][0], final[1][0]), what="handoff")
+    say(f"handoff: {errs}")
+
+
+def test_prefill_degenerate_zero_tokens_and_dt_zero():
+    """All-zero tokens take the a == 0 quantizer path; dt -> 0 leaves the SSM state unchanged."""
+    lw = gen.layer_weights(TINY, 8, 14)
+    conv0, ssm0 = gen.initial_states(TINY, 1, 8, 14, std=0.3)
+    xs = gen.token_inputs(TINY, (1, 40), 14, tag=4)
+    xs[0, 3] = 0
+    xs[0, 17] = 0
+    say("case: tiny prefill with all-zero tokens, chunk 16")
+    out, tps, final = run_prefill(TINY, lw, xs, conv0, ssm0, 16)
+    assert not tps["in_q"][0, 3].any() and tps["in_s"][0, 3, 0] == 0
+    check_sequence(lw, xs[0], conv0[0], ssm0[0], out[0], {k: v[0] for k, v in tps.items()},
+                   (final[0][0], final[1][0]), what="zero tokens")
+    lw.dt_bias[:] = -100.0
+    say("case: tiny prefill with dt -> 0, chunk 64")
+    out, tps, final = run_prefill(TINY, lw, xs, conv0, ssm0, 64, taps=False)
+    assert (final[1] == ssm0).all()
+
+
+def test_prefill_1p3b_2048_tokens_bf16_chunk256():
+    """One layer of the 2048-token bf16 prefill workload (1.3B shape, chunk 256): every token."""
+    T = 2048
+    lw = gen.layer_weights(BIG, 0, 0)
+    conv0, ssm0 = gen.initial_states(BIG, 1)
+    xs = gen.token_inputs(BIG, (1, T), 0, tag=5, bf16=True)
+    say(f"case: 1.3B-shaped layer prefill, seqlen {T}, chunk 256, bf16 input")
+    out, tps, final = run_prefill(BIG, lw, xs, conv0, ssm0, 256, bf16=True)
+    dense = O.dense_signs(lw)
+    tb = {k: v[0] for k, v in tps.items()}
+    errs = check_sequence(lw, xs[0], conv0[0], ssm0[0], out[0], tb, (final[0][0], final[1][0]), dense,
+                          what="1p3b prefill")
+    fr, first = free_running_sequence(lw, xs[0], conv0[0], ssm0[0], out[0], tb, dense, what="1p3b")
+    say(f"1p3b prefill: forced {errs}; free-running {fr:.2e} up to token {first}")
+
+
+def test_prefill_chunk_lengths_agree():
+    """Every chunk length evaluates the same recurrence: codes agree except at rounding ties and
+    outputs agree within the layer tolerance."""
+    lw = gen.layer_weights(TINY, 9, 15)
+    conv0, ssm0 = gen.initial_states(TINY, 1, 9, 15, std=0.2)
+    xs = gen.token_inputs(TINY, (1, 257), 15, tag=6)
+    outs = {}
+    for c in (16, 32, 64, 128, 256):
+        say(f"case: tiny prefill seqlen 257 chunk {c}")
+        outs[c] = run_prefill(TINY, lw, xs, conv0, ssm0, c, taps=False)
+    for c in (16, 32, 64, 128):
+        e = max(PY.normwise(outs[c][0][0, t], outs[256][0][0, t]) for t in range(257))
+        assert e < PY.TOL_LAYER, (c, e)
+        assert PY.normwise(outs[c][2][1], outs[256][2][1]) < PY.TOL_LAYER

@@ -343,3 +343,36 @@ def test_stack_feedback_is_normalised():
     rms = np.sqrt(np.mean(ys ** 2, axis=1))
     np.testing.assert_allclose(rms, 1.0, rtol=1e-4)
     assert not np.allclose(ys[0], ys[1])
+
+
+def test_project_tokens_equals_per_token_project():
+    P = _proj(24, 64, 8, seed=30)
+    rng = np.random.default_rng(31)
+    q = rng.integers(-127, 128, size=(5, 64)).astype(np.int8)
+    s = rng.uniform(0.01, 0.1, 5).astype(np.float32)
+    y, acc, t = O.project_tokens(q, s, P)
+    for m in range(5):
+        y1, a1, t1 = O.project(q[m], s[m], P)
+        np.testing.assert_array_equal(acc[m], a1)
+        np.testing.assert_array_equal(t[m], t1)
+        np.testing.assert_allclose(y[m], y1, rtol=1e-13, atol=1e-13)
+
+
+def test_layer_tokens_equals_sequential_decode():
+    d = _tiny_dims()
+    lw = gen.layer_weights(d, 2, 40, random_norms=True, per_channel_lora=True)
+    conv0, ssm0 = gen.initial_states(d, 1, 2, 40, std=0.2)
+    xs = gen.token_inputs(d, (9, 1), 40)[:, 0]
+    o1, c1, s1, taps = O.layer_decode_steps(xs, lw, conv0[0], ssm0[0])
+    o2, c2, s2, tp2 = O.layer_tokens(xs, lw, conv0[0], ssm0[0])
+    for t in range(9):
+        for k in ("in_q", "in_acc", "in_t", "out_q", "out_acc", "out_t"):
+            np.testing.assert_array_equal(getattr(taps[t], k), tp2[k][t])
+        assert taps[t].in_s == tp2["in_s"][t] and taps[t].out_s == tp2["out_s"][t]
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(c2, c1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s2, s1, rtol=1e-12, atol=1e-12)
+    # forcing the codes it would choose anyway changes nothing
+    f = dict(in_q=tp2["in_q"], in_s=tp2["in_s"], out_q=tp2["out_q"], out_s=tp2["out_s"])
+    o3, _, _, _ = O.layer_tokens(xs, lw, conv0[0], ssm0[0], force=f)
+    np.testing.assert_array_equal(o3, o2)
