@@ -1,18 +1,26 @@
 #!/usr/bin/env python3
-"""Benchmark: 48-layer DF-SSM (Mamba-2 1.3B-shaped) stack decode at batch 1 on one MI355X.
+"""Benchmark of the DF-SSM inference hot path (Mamba-2 1.3B-shaped layers) on one MI355X.
 
-One step = one dfssm_stack_decode call that decodes `--tokens` tokens (default 512) through all
-48 layers with feedback (x(t+1) = RMSNorm of the stack output), continuing from the previous
-step's conv/SSM states. Inputs are seeded synthetic tensors already resident in HBM. The timed
-region is K steps bracketed by torch.cuda.synchronize(); every step is also timed with HIP events
-on the stream the library launches on (the persistent stack kernel is the only long-running
-kernel of a call), which gives the kernel's average launch duration for the roofline.
+Primary workload (the JSON line's metric): 48-layer stack decode at batch 1. One step = one
+dfssm_stack_decode call that decodes `--tokens` tokens (default 512) through all 48 layers with
+feedback (x(t+1) = RMSNorm of the stack output), continuing from the previous step's conv/SSM
+states. Inputs are seeded synthetic tensors already resident in HBM. The timed region is K steps
+bracketed by torch.cuda.synchronize(); every step is also timed with HIP events on the stream the
+library launches on (the persistent stack kernel is the only long-running kernel of a call),
+which gives the kernel's average launch duration for the roofline.
 
-Prints ONE JSON line. `roofline.achieved` = algorithmic bytes of one launch (per-token bytes x
-tokens, see bytes_per_token) / that launch's duration. `roofline.traffic` = HBM bytes per launch
-from the committed rocprofv3 FETCH_SIZE + WRITE_SIZE counters (profiles/), or null when the
-kernel source differs from the one the counters were taken on. `cpu_baseline` times the CPU
-oracle on one token of the same 48-layer stack.
+Secondary workloads (reported under "secondary", or alone with --workload):
+  prefill2048  48 dfssm_layer_prefill calls over 2048 bf16 tokens (chunk 256) from zero states,
+               then 16 stack-decode steps from the handed-off states (checked, not timed);
+               roofline: int8 MFMA ops of the scaffold GEMMs / time.
+  decode_b64   48-layer stack decode at batch 64 (states ~ N(0, 0.1)), 128 tokens per sequence
+               per step; roofline: algorithmic HBM bytes (weights once per token step, every
+               sequence's conv/SSM state read and written) / time.
+
+Prints ONE JSON line. `roofline.achieved` = algorithmic bytes (ops) of one launch / that launch's
+duration. `roofline.traffic` = HBM bytes per launch from the committed rocprofv3 FETCH_SIZE +
+WRITE_SIZE counters (profiles/), or null when the kernel source differs from the one the counters
+were taken on. `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -111,72 +119,63 @@ def write_counters(fetch_csv: str, write_csv: str, tokens: int) -> dict:
     return out
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--tokens", type=int, default=512, help="tokens decoded per step")
-    ap.add_argument("--layers", type=int, default=48)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after the timed region, copy 512 MiB once (calibrates rocprofv3 byte counters)")
-    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/ and exit (no GPU)")
-    args = ap.parse_args()
-    if args.write_counters:
-        print(json.dumps(write_counters(*args.write_counters, args.tokens), indent=1))
-        return 0
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
-              "the batch-1 decode does not shard usefully, see DESIGN.md.", file=sys.stderr)
-        return 2
+def int8_ops_per_token(d) -> int:
+    """Int8 MAC-pairs (2 ops per multiply-add) of the two scaffold contractions for one token."""
+    return 2 * (d.n_in_proj * d.d_model + d.d_model * d.d_inner)
 
-    import numpy as np
-    import torch
-    from synth import gen
-    from bit_quantized_mamba_packed_amd import _lib as L, device as Dv
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a ROCm GPU", file=sys.stderr)
+def decode_b64_bytes_per_step(d, n_layers: int, batch: int) -> int:
+    """Algorithmic HBM bytes of one batched token step: every weight once, every sequence's conv
+    and SSM state read and written once."""
+    b = bytes_per_token(d, n_layers)["per_layer"]
+    per_seq = b["ssm_state_rw"] + b["conv_state_rw"]
+    weights = sum(v for k, v in b.items() if k not in ("ssm_state_rw", "conv_state_rw"))
+    return n_layers * (weights + batch * per_seq) + d.d_model * 4
+
+
+def threads_in_use() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
         return 1
-    L.load()
-    dims = gen.DIMS["1p3b"]
+
+
+def timed(fn, steps: int, warmup: int, torch):
+    """Run fn() warmup times, then `steps` times bracketed by synchronize(); every call is also
+    bracketed by HIP events on the current stream. Returns (wall seconds, per-call ms list)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, [a.elapsed_time(b) for a, b in evs]
+
+
+def run_decode_b1(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     nL, T = args.layers, args.tokens
-    layers_np = gen.stack_weights(dims, nL, seed=0)
-    layers = [Dv.DeviceLayer(lw) for lw in layers_np]
     states = [Dv.DeviceState(*gen.initial_states(dims, 1, l)) for l in range(nL)]
     fw = torch.ones(dims.d_model, dtype=torch.float32, device="cuda")
     x0_np = gen.token_inputs(dims, (1,), 0, tag=7)
     x0 = torch.from_numpy(x0_np).cuda()
     y = torch.empty((T, 1, dims.d_model), dtype=torch.float32, device="cuda")
     ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
-
-    for _ in range(args.warmup):
-        Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record(stream)
-        Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws), args.steps,
+                            args.warmup, torch)
     if not torch.isfinite(y).all():
-        print("non-finite decode output", file=sys.stderr)
-        return 1
+        raise SystemExit("non-finite decode output")
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-
-    tokens = args.steps * T
-    value = tokens / wall
     bpt = bytes_per_token(dims, nL)
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
     achieved = bpt["token_total"] * T / avg_launch_s / 1e9
@@ -187,7 +186,7 @@ def main() -> int:
             traffic = c.get("hbm_bytes_per_launch")
     out = {
         "metric": "decode tokens/s batch=1, 48-layer 1.3B shape; achieved HBM GB/s vs peak",
-        "value": round(value, 2),
+        "value": round(args.steps * T / wall, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -209,6 +208,156 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(dims, layers_np, x0_np[0].astype(np.float64), dims.eps)
+    return out
+
+
+def run_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
+    """48 layer prefills of 2048 bf16 tokens (chunk 256) from zero states; one step = the stack."""
+    nL, S, Q = args.layers, 2048, 256
+    states = [Dv.DeviceState(np.zeros((1, dims.conv_dim, dims.d_conv - 1), np.float32),
+                             np.zeros((1, dims.nheads, dims.headdim, dims.d_state), np.float32)) for _ in range(nL)]
+    x_np = gen.token_inputs(dims, (1, S), 0, tag=11, bf16=True)
+    xb = torch.from_numpy(x_np).cuda().to(torch.bfloat16)
+    h = [torch.empty((1, S, dims.d_model), dtype=torch.float32, device="cuda") for _ in range(2)]
+    ws = Dv.workspace(dims, L.DFSSM_OP_LAYER_PREFILL, 1, S)
+
+    def step():
+        for st in states:
+            st.conv.zero_()
+            st.ssm.zero_()
+        for l in range(nL):
+            src = xb if l == 0 else h[(l - 1) % 2]
+            Dv.layer_prefill(dims, layers[l], states[l], src, h[l % 2], Q, ws)
+
+    wall, launch_ms = timed(step, args.steps, args.warmup, torch)
+    out_last = h[(nL - 1) % 2]
+    if not torch.isfinite(out_last).all():
+        raise SystemExit("non-finite prefill output")
+    # hand the final states to 16 decode steps (not timed), fed the RMSNorm of the last position
+    fw = torch.ones(dims.d_model, dtype=torch.float32, device="cuda")
+    x_last = out_last[:, -1, :].contiguous()
+    x0 = x_last * torch.rsqrt(x_last.pow(2).mean(-1, keepdim=True) + dims.eps)
+    y = torch.empty((16, 1, dims.d_model), dtype=torch.float32, device="cuda")
+    wsd = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
+    Dv.stack_decode(dims, layers, states, fw, x0, y, 16, wsd)
+    torch.cuda.synchronize()
+    if not torch.isfinite(y).all():
+        raise SystemExit("non-finite decode after prefill")
+    ops = int8_ops_per_token(dims) * S * nL
+    avg_s = sum(launch_ms) / len(launch_ms) / 1e3
+    achieved = ops / avg_s / 1e12
+    out = {
+        "metric": "prefill tokens/s batch=1, L=2048 bf16, 48-layer 1.3B shape; int8 MFMA TOP/s vs peak",
+        "value": round(args.steps * S / wall, 2), "unit": "tokens/s", "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True,
+        "dtype": "int8 codes x 1-bit signs on int8 MFMA (int32 acc), fp32 SSD/epilogue",
+        "config": {"workload": "stack48_1p3b_prefill2048", "layers": nL, "batch": 1, "seqlen": S, "chunk": Q,
+                   "input": "bf16", "decode_after": 16},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": 5000.0, "unit": "TFLOP/s",
+                     "frac": round(achieved / 5000.0, 5), "traffic": None,
+                     "kernel": "whole prefill step (all kernels of 48 layers); scaffold int8 ops only",
+                     "algorithmic_ops_per_launch": ops, "avg_launch_ms": round(avg_s * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import dfssm_oracle as O
+        ns = 128
+        t0 = time.perf_counter()
+        O.layer_tokens(x_np[0, :ns], layers_np[0], np.zeros((dims.conv_dim, dims.d_conv - 1)),
+                       np.zeros((dims.nheads, dims.headdim, dims.d_state)))
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(ns / (dt * nL), 4), "unit": "tokens/s", "cores": threads_in_use(),
+                               "kind": "oracle",
+                               "sample": f"{ns} tokens through 1 layer ({dt:.1f} s), scaled to 48 layers"}
+    return out
+
+
+def run_decode_b64(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
+    nL, B, T = args.layers, 64, 128
+    states = []
+    for l in range(nL):
+        c, s_ = gen.initial_states(dims, B, l, 0, std=0.1)
+        states.append(Dv.DeviceState(c, s_))
+    fw = torch.ones(dims.d_model, dtype=torch.float32, device="cuda")
+    x0 = torch.from_numpy(gen.token_inputs(dims, (B,), 0, tag=8)).cuda()
+    y = torch.empty((T, B, dims.d_model), dtype=torch.float32, device="cuda")
+    ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, B, 0, nL)
+    steps = max(1, min(args.steps, 2))
+    wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws), steps,
+                            min(args.warmup, 1), torch)
+    if not torch.isfinite(y).all():
+        raise SystemExit("non-finite batched decode output")
+    per_step = decode_b64_bytes_per_step(dims, nL, B)
+    avg_s = sum(launch_ms) / len(launch_ms) / 1e3
+    achieved = per_step * T / avg_s / 1e9
+    return {
+        "metric": "decode tokens/s batch=64, 48-layer 1.3B shape; achieved HBM GB/s vs peak",
+        "value": round(steps * T * B / wall, 2), "unit": "tokens/s", "steps": steps,
+        "ms_per_step": round(wall / steps * 1e3, 3), "higher_is_better": True,
+        "dtype": "int8 codes x 1-bit signs on int8 MFMA (int32 acc), fp32 state/epilogue",
+        "config": {"workload": "stack48_1p3b_b64_decode128", "layers": nL, "batch": B, "tokens_per_step": T,
+                   "state_init": "N(0, 0.1)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "whole step (all kernels of 128 x 48 layer steps)",
+                     "algorithmic_bytes_per_launch": per_step * T, "avg_launch_ms": round(avg_s * 1e3, 3)},
+    }
+
+
+WORKLOADS = {"decode_b1": run_decode_b1, "prefill2048": run_prefill, "decode_b64": run_decode_b64}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--tokens", type=int, default=512, help="tokens decoded per step (batch-1 decode)")
+    ap.add_argument("--layers", type=int, default=48)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=None,
+                    help="run one workload alone and print its line (default: batch-1 decode + secondaries)")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, copy 512 MiB once (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/ and exit (no GPU)")
+    args = ap.parse_args()
+    if args.write_counters:
+        print(json.dumps(write_counters(*args.write_counters, args.tokens), indent=1))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "the batch-1 decode does not shard usefully (its per-layer all-reduces would cost more than the layer), "
+              "and batched decode and prefill would shard by sequence, which this single-GPU build does not run.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from synth import gen
+    from bit_quantized_mamba_packed_amd import _lib as L, device as Dv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    L.load()
+    dims = gen.DIMS["1p3b"]
+    layers_np = gen.stack_weights(dims, args.layers, seed=0)
+    layers = [Dv.DeviceLayer(lw) for lw in layers_np]
+    common = (args, dims, layers_np, layers, np, torch, gen, L, Dv)
+    if args.workload is not None:
+        out = WORKLOADS[args.workload](*common)
+        out.setdefault("n_gpus", 1)
+        print(json.dumps(out), flush=True)
+        return 0
+    out = run_decode_b1(*common)
+    if not args.no_secondary:
+        sec = {}
+        for name in ("prefill2048", "decode_b64"):
+            r = WORKLOADS[name](*common)
+            torch.cuda.empty_cache()
+            sec[name] = {k: r[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",
+                                           "cpu_baseline") if k in r}
+        out["secondary"] = sec
     print(json.dumps(out), flush=True)
     return 0
 

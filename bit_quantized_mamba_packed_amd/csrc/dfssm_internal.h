@@ -63,7 +63,10 @@ bool stack_persistent_ok(const Shape &s, int batch);
 
 // int8-code x (+-1 scaffold) GEMM with the projection epilogue (gemm.hip):
 //   y[m][n] = s[m]*row_scale[n]*acc[m][n] + up_scale[n] * sum_j t'[m][j]*lora_up[n][j] (+ res[m][n])
-// acc = sum_k sgn[n][k]*q[m][k]; t' = thi + tlo (bf16 split of dn_scale*s*t). rank % 8 == 0, K % 64 == 0.
+// acc = sum_k sgn[n][k]*q[m][k]; t' = thi + tlo (bf16 split of dn_scale*s*t). rank % 8 == 0, K % 128 == 0.
+// When the output has few tiles the K range is split over several workgroups; their exact int32
+// partial sums and per-tile arrival counters live in `scratch` (gemm_scratch_bytes of workspace,
+// no initialisation needed: the launch clears the counters itself).
 struct GemmArgs {
     const int8_t *q;
     int64_t ldq;
@@ -82,7 +85,9 @@ struct GemmArgs {
     int64_t ldres;
     int32_t *acc_tap;      // optional
     int64_t ldacc;
+    void *scratch;         // split-K scratch (gemm_scratch_bytes), 256-byte aligned
 };
+size_t gemm_scratch_bytes(int M, int N, int K);
 hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream);
 
 // Per-token RMSNorm + int8 quantizer + int8 LoRA-down for M tokens (prefill / batched decode):
@@ -114,6 +119,7 @@ struct PrefillWs {
     int32_t *qsum_in, *qsum_out;
     __bf16 *thi_in, *tlo_in, *thi_out, *tlo_out;
     float *Y, *xbc, *dt, *lam, *lam_end, *cb, *ydiag, *sloc, *gbuf;
+    void *gemm_scratch;    // split-K scratch shared by the two projections (they run one after the other)
     size_t bytes;
 };
 PrefillWs carve_prefill_ws(const Shape &s, int batch, int seqlen, int chunk, void *base);

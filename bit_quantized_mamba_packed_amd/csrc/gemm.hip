@@ -1,18 +1,26 @@
 // int8-code x (+-1 scaffold) GEMM with the DF-SSM projection epilogue, on gfx950 MFMA.
 //
 // For M tokens at once (prefill, batched decode) a projection is a real dense contraction
-// (DF-SSM paper §4.1 runs it on INT8 tensor cores). Here:
-//   C[m][n] = sum_k q[m][k] * bit[n][k]           v_mfma_i32_32x32x32_i8, bits unpacked to 0/1
+// (the DF-SSM paper's §4.1 runs it on INT8 tensor cores). Here:
+//   C[m][n] = sum_k q[m][k] * bit[n][k]           v_mfma_i32_32x32x32_i8, bits expanded to 0/1 bytes
 //   acc     = 2*C - sum_k q[m][k]                  (sgn = 2*bit - 1)
 //   y[m][n] = s[m]*row_scale[n]*acc + up_scale[n] * sum_j t'[m][j] * lora_up[n][j]   (Eq. (3))
 // with t' = dn_scale * s * t (the LoRA-down result, fp32) split as t' = hi + lo in bf16 so that
-// the rank-r product runs on v_mfma_f32_32x32x16_bf16 (lora_up is int8, exact in bf16; the
-// split keeps ~16 mantissa bits of t'). An optional residual is added (out_proj), and the int32
-// acc can be written out (taps).
+// the rank-r product runs on v_mfma_f32_32x32x16_bf16 (lora_up is int8, exact in bf16; the split
+// keeps ~16 mantissa bits of t'). An optional residual is added (out_proj) and the int32 acc can
+// be written out (taps).
 //
-// Tiles: 128 x 128 outputs per workgroup, 4 waves as 2 x 2 of 64 x 64 (2 x 2 MFMA blocks each),
-// K in steps of 64 through double-buffered LDS. Sign bits are unpacked once per workgroup into
-// LDS (bytes 0/1), shared by the two waves of each column half. Ragged M and N are zero-filled.
+// Operand paths. The codes (A, int8 [M][K]) are staged through LDS, shared by the waves of a
+// workgroup. The sign bits (B) never touch LDS: each lane loads the 16 bytes (128 k) of its
+// column's bit row for the current K step straight into registers and expands the 16 bits each
+// MFMA needs into 16 bytes with a multiply-and-mask, so LDS carries only A.
+//
+// k_gemm_tile (M > 64): workgroup tile 128 x (64*WNB), 4 waves as 2 x 2, each wave 64 x (32*WNB)
+// = 2 x WNB MFMA blocks; K in steps of 128 through double-buffered LDS, one barrier per step.
+// The ragged last column tile is dispatched first so that the short workgroups do not trail.
+// k_gemm_skinny (M <= 64): one workgroup per 32 columns, its 4 waves split K and reduce their
+// int32 partial sums through LDS; A comes straight from global memory (it is 64 x K bytes and
+// stays in L2), B as above.
 #include "decode_device.h"
 
 namespace dfssm {
@@ -24,160 +32,468 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 128, BN = 128, KT = 64;
-constexpr int LDS_ROW = KT + 16;  // bytes per LDS row (padding staggers banks)
+constexpr int BM = 128, KT = 128;
+constexpr int LDS_ROW = KT + 16;  // bytes per LDS row of A (the pad staggers the banks of the fragment reads)
 
 __device__ __forceinline__ uint32_t nibble_to_bytes(uint32_t nib) { return (nib * 0x00204081u) & 0x01010101u; }
 
-__global__ __launch_bounds__(kBlock) void k_gemm_pm1(GemmArgs a) {
-    __shared__ __align__(16) int8_t As[2][BM * LDS_ROW];
-    __shared__ __align__(16) int8_t Bs[2][BN * LDS_ROW];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int K = a.K;
-    // staging: thread -> row tid/2 of the tile, half (32 k) tid%2
-    const int srow = tid >> 1, shalf = tid & 1;
-    const int gm = m0 + srow, gn = n0 + srow;
-    const bool am = gm < a.M, bn_ok = gn < a.N;
-    const int8_t *qrow = a.q + (int64_t)(am ? gm : 0) * a.ldq + shalf * 32;
-    const uint8_t *brow = a.sign + (int64_t)(bn_ok ? gn : 0) * (K >> 3) + shalf * 4;
-    int4 ra0, ra1;
-    uint32_t rb;
-    auto gload = [&](int k0) {
-        if (am) {
-            ra0 = *reinterpret_cast<const int4 *>(qrow + k0);
-            ra1 = *reinterpret_cast<const int4 *>(qrow + k0 + 16);
-        } else {
-            ra0 = make_int4(0, 0, 0, 0);
-            ra1 = ra0;
-        }
-        rb = bn_ok ? *reinterpret_cast<const uint32_t *>(brow + (k0 >> 3)) : 0u;
-    };
-    auto sstore = [&](int buf) {
-        int8_t *ad = As[buf] + srow * LDS_ROW + shalf * 32;
-        *reinterpret_cast<int4 *>(ad) = ra0;
-        *reinterpret_cast<int4 *>(ad + 16) = ra1;
-        int8_t *bd = Bs[buf] + srow * LDS_ROW + shalf * 32;
-        int4 w0, w1;
-        w0.x = (int)nibble_to_bytes(rb & 15u);
-        w0.y = (int)nibble_to_bytes((rb >> 4) & 15u);
-        w0.z = (int)nibble_to_bytes((rb >> 8) & 15u);
-        w0.w = (int)nibble_to_bytes((rb >> 12) & 15u);
-        w1.x = (int)nibble_to_bytes((rb >> 16) & 15u);
-        w1.y = (int)nibble_to_bytes((rb >> 20) & 15u);
-        w1.z = (int)nibble_to_bytes((rb >> 24) & 15u);
-        w1.w = (int)nibble_to_bytes(rb >> 28);
-        *reinterpret_cast<int4 *>(bd) = w0;
-        *reinterpret_cast<int4 *>(bd + 16) = w1;
-    };
-    v16i acc[2][2];
+// 16 sign bits -> 16 bytes of 0/1, byte e = bit e
+__device__ __forceinline__ v4i expand16(uint32_t b16) {
+    v4i r;
+    r.x = (int)nibble_to_bytes(b16 & 15u);
+    r.y = (int)nibble_to_bytes((b16 >> 4) & 15u);
+    r.z = (int)nibble_to_bytes((b16 >> 8) & 15u);
+    r.w = (int)nibble_to_bytes((b16 >> 12) & 15u);
+    return r;
+}
+
+__device__ __forceinline__ uint32_t u4_get(const uint4 &v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Low-rank term of one 32 x 32 block (rows m0.., columns n0..) on bf16 MFMA from global memory:
+// lacc[r] = sum_j t'[m][j] * lora_up[n][j] for this lane's 16 outputs (used by the skinny kernel).
+__device__ __forceinline__ v16f lowrank_block(const GemmArgs &a, int mrow, int ncol, int lane) {
+    v16f lacc;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-    const int nk = K / KT;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int lr = lane & 31, lk = (lane >> 5) * 16;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * KT);
-#pragma unroll
-        for (int kk = 0; kk < KT; kk += 32) {
-            v4i af[2], bf[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const v4i *>(As[cur] + (wm * 64 + i * 32 + lr) * LDS_ROW + kk + lk);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const v4i *>(Bs[cur] + (wn * 64 + j * 32 + lr) * LDS_ROW + kk + lk);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) sstore(cur ^ 1);
-        __syncthreads();
-    }
-    // ---- low-rank term on bf16 MFMA: lacc[m][n] = sum_j t'[m][j] * lora_up[n][j]
-    v16f lacc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) lacc[i][j][r] = 0.f;
+    for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
     const int lj = (lane >> 5) * 8;
     for (int kr = 0; kr < a.rank; kr += 16) {
         const bool inr = kr + lj + 8 <= a.rank;
-        v8bf ahi[2], alo[2], bup[2];
+        v8bf ahi, alo, bup;
+        if (inr && mrow < a.M) {
+            ahi = *reinterpret_cast<const v8bf *>(a.thi + (int64_t)mrow * a.rank + kr + lj);
+            alo = *reinterpret_cast<const v8bf *>(a.tlo + (int64_t)mrow * a.rank + kr + lj);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int m = m0 + wm * 64 + i * 32 + lr;
-            if (inr && m < a.M) {
-                ahi[i] = *reinterpret_cast<const v8bf *>(a.thi + (int64_t)m * a.rank + kr + lj);
-                alo[i] = *reinterpret_cast<const v8bf *>(a.tlo + (int64_t)m * a.rank + kr + lj);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    ahi[i][e] = (__bf16)0.f;
-                    alo[i][e] = (__bf16)0.f;
-                }
+            for (int e = 0; e < 8; ++e) {
+                ahi[e] = (__bf16)0.f;
+                alo[e] = (__bf16)0.f;
             }
         }
+        uint2 w = make_uint2(0u, 0u);
+        if (inr && ncol < a.N) w = *reinterpret_cast<const uint2 *>(a.lora_up + (int64_t)ncol * a.rank + kr + lj);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn * 64 + j * 32 + lr;
-            uint2 w = make_uint2(0u, 0u);
-            if (inr && n < a.N) w = *reinterpret_cast<const uint2 *>(a.lora_up + (int64_t)n * a.rank + kr + lj);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bup[j][e] = (__bf16)(float)(int8_t)(w.x >> (8 * e));
-                bup[j][4 + e] = (__bf16)(float)(int8_t)(w.y >> (8 * e));
-            }
+        for (int e = 0; e < 4; ++e) {
+            bup[e] = (__bf16)(float)(int8_t)(w.x >> (8 * e));
+            bup[4 + e] = (__bf16)(float)(int8_t)(w.y >> (8 * e));
         }
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bup, lacc, 0, 0, 0);
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bup, lacc, 0, 0, 0);
+    }
+    return lacc;
+}
+
+// Epilogue of one 32 x 32 block: lane holds column (lane % 32), rows 8*(r/4) + 4*(lane/32) + r%4.
+__device__ __forceinline__ void store_block(const GemmArgs &a, const v16i &acc, const v16f &lacc, int mb, int n,
+                                            int lane) {
+    if (n >= a.N) return;
+    const float sc = half_bits_to_float(a.row_scale[n]);
+    const float us = a.up_scale[n];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m >= a.M) continue;
+        const int accv = 2 * acc[r] - a.qsum[m];
+        float v = a.s[m] * sc * (float)accv + us * lacc[r];
+        if (a.res) v += a.res[(int64_t)m * a.ldres + n];
+        a.y[(int64_t)m * a.ldy + n] = v;
+        if (a.acc_tap) a.acc_tap[(int64_t)m * a.ldacc + n] = accv;
+    }
+}
+
+// LDS of the tile kernel. Main loop: A[2][BM][A_ROW] int8 codes, B[2][BN][16] sign bytes (kMainLds).
+// Epilogue operands: s[BM] f32, qsum[BM] i32, thi/tlo [BM][rank+8] bf16, lora_up [BN][rank+8] int8.
+// For rank <= 32 they get their own region behind the main-loop buffers and are loaded before the
+// main loop (their latency hides behind it); larger ranks reuse the main-loop buffers afterwards.
+constexpr int A_BYTES = BM * LDS_ROW;
+constexpr int kCntBytes = 4096;
+constexpr int kMainLds = 2 * A_BYTES + 2 * 256 * 16;
+constexpr int kEarlyRank = 32;
+constexpr int epi_lds_bytes(int rank) { return 1024 + 2 * BM * (rank + 8) * 2 + 256 * (rank + 8); }
+constexpr int kTileSmem = kMainLds + epi_lds_bytes(kEarlyRank);
+static_assert(epi_lds_bytes(kMaxRank) <= kTileSmem, "tile LDS");
+
+// Workgroup barrier that orders LDS only: outstanding global stores (the epilogue's) are not waited for.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Stage the epilogue operands of tile (m0, n0) into LDS at `base`.
+template <int BN>
+__device__ __forceinline__ void stage_epilogue(const GemmArgs &a, char *base, int m0, int n0, int tid) {
+    const int rank = a.rank, RS = rank + 8, rc = rank >> 3;
+    float *s_l = reinterpret_cast<float *>(base);
+    int *q_l = reinterpret_cast<int *>(base + 512);
+    __bf16 *th_l = reinterpret_cast<__bf16 *>(base + 1024);
+    __bf16 *tl_l = th_l + BM * RS;
+    int8_t *u_l = reinterpret_cast<int8_t *>(tl_l + BM * RS);
+    // every load first, then every LDS store (the trip counts are fixed so the loads are in flight together)
+    constexpr int NT = BM * (kMaxRank / 8) / kBlock, NU = BN * (kMaxRank / 8) / kBlock;
+    uint4 h[NT], l[NT];
+    uint2 w[NU];
+    float sv = 0.f;
+    int qv = 0;
+    if (tid < BM && m0 + tid < a.M) {
+        sv = a.s[m0 + tid];
+        qv = a.qsum[m0 + tid];
+    }
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+        const int idx = tid + it * kBlock, row = idx / rc, c = idx - row * rc, m = m0 + row;
+        h[it] = make_uint4(0u, 0u, 0u, 0u);
+        l[it] = h[it];
+        if (idx < BM * rc && m < a.M) {
+            h[it] = *reinterpret_cast<const uint4 *>(a.thi + (int64_t)m * rank + c * 8);
+            l[it] = *reinterpret_cast<const uint4 *>(a.tlo + (int64_t)m * rank + c * 8);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < NU; ++it) {
+        const int idx = tid + it * kBlock, col = idx / rc, c = idx - col * rc, n = n0 + col;
+        w[it] = make_uint2(0u, 0u);
+        if (idx < BN * rc && n < a.N) w[it] = *reinterpret_cast<const uint2 *>(a.lora_up + (int64_t)n * rank + c * 8);
+    }
+    if (tid < BM) {
+        s_l[tid] = sv;
+        q_l[tid] = qv;
+    }
+#pragma unroll
+    for (int it = 0; it < NT; ++it) {
+        const int idx = tid + it * kBlock, row = idx / rc, c = idx - row * rc;
+        if (idx < BM * rc) {
+            *reinterpret_cast<uint4 *>(th_l + row * RS + c * 8) = h[it];
+            *reinterpret_cast<uint4 *>(tl_l + row * RS + c * 8) = l[it];
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < NU; ++it) {
+        const int idx = tid + it * kBlock, col = idx / rc, c = idx - col * rc;
+        if (idx < BN * rc) *reinterpret_cast<uint2 *>(u_l + col * RS + c * 8) = w[it];
+    }
+}
+
+// two waves per SIMD (<= 256 registers incl. accumulators), so two workgroups share a compute unit
+template <int WNB, bool SPLIT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tile(GemmArgs a, int ntm,
+                                                                                              int ntn, int splitk) {
+    constexpr int BN = 64 * WNB;
+    __shared__ __align__(16) char smem[kTileSmem];
+    __shared__ int last_flag;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = lane & 31, hsel = lane >> 5;
+    // tile order: the ragged last column tile of every row first, then row-fastest
+    const int bid = blockIdx.x, z = blockIdx.y;
+    int tm, tn;
+    {
+        const bool ragged = (a.N % BN) != 0;
+        if (ragged && bid < ntm) {
+            tm = bid;
+            tn = ntn - 1;
+        } else {
+            const int idx = ragged ? bid - ntm : bid;
+            tm = idx % ntm;
+            tn = idx / ntm;
+        }
+    }
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int K = a.K, nk = K / KT;
+    const int kt0 = z * nk / splitk, kt1 = (z + 1) * nk / splitk;
+    auto As = [&](int b) { return reinterpret_cast<int8_t *>(smem) + b * A_BYTES; };
+    auto Bs = [&](int b) { return reinterpret_cast<uint8_t *>(smem) + 2 * A_BYTES + b * (BN * 16); };
+    // A staging: thread -> row tid/2, 64-byte half tid%2;  B staging: thread -> column tid (< BN)
+    const int srow = tid >> 1, shalf = tid & 1;
+    const bool arow_ok = m0 + srow < a.M;
+    const int8_t *qrow = a.q + (int64_t)(arow_ok ? m0 + srow : 0) * a.ldq + shalf * 64;
+    const bool bcol_ok = tid < BN && n0 + tid < a.N;
+    const uint8_t *bsrc = a.sign + (int64_t)(bcol_ok ? n0 + tid : 0) * (K >> 3);
+    int4 ra[4];
+    uint4 rb;
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ra[i] = arow_ok ? *reinterpret_cast<const int4 *>(qrow + k0 + 16 * i) : make_int4(0, 0, 0, 0);
+        rb = bcol_ok ? *reinterpret_cast<const uint4 *>(bsrc + (k0 >> 3)) : make_uint4(0u, 0u, 0u, 0u);
+    };
+    auto sstore = [&](int buf) {
+        int8_t *d = As(buf) + srow * LDS_ROW + shalf * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<int4 *>(d + 16 * i) = ra[i];
+        if (tid < BN) *reinterpret_cast<uint4 *>(Bs(buf) + tid * 16) = rb;
+    };
+    v16i acc[2][WNB];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < WNB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    gload(kt0 * KT);
+    const bool early = a.rank <= kEarlyRank;
+    char *epi = smem + (early ? kMainLds : 0);
+    if (early) stage_epilogue<BN>(a, epi, m0, n0, tid);
+    sstore(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int cur = (kt - kt0) & 1;
+        const bool more = kt + 1 < kt1;
+        if (more) gload((kt + 1) * KT);
+        const int8_t *abase = As(cur) + (wm * 64 + lr) * LDS_ROW + hsel * 16;
+        uint4 bw[WNB];
+#pragma unroll
+        for (int j = 0; j < WNB; ++j)
+            bw[j] = *reinterpret_cast<const uint4 *>(Bs(cur) + (wn * (32 * WNB) + j * 32 + lr) * 16);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v4i af[2], bf[WNB];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const v4i *>(abase + i * 32 * LDS_ROW + s * 32);
+#pragma unroll
+            for (int j = 0; j < WNB; ++j) bf[j] = expand16((u4_get(bw[j], s) >> (16 * hsel)) & 0xffffu);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < WNB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) sstore(cur ^ 1);
+        lds_barrier();
+    }
+    // ---- split K: publish the exact int32 partial sums; the last workgroup of the tile to arrive
+    // adds the others' and runs the epilogue (no workgroup ever waits for another)
+    if (SPLIT) {
+        const int tile = bid;
+        const int64_t tsz = (int64_t)BM * BN;
+        uint32_t *cnt = static_cast<uint32_t *>(a.scratch);
+        int32_t *part = reinterpret_cast<int32_t *>(static_cast<char *>(a.scratch) + kCntBytes);
+        int32_t *mine = part + ((int64_t)tile * splitk + z) * tsz;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                lacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], bup[j], lacc[i][j], 0, 0, 0);
-                lacc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], bup[j], lacc[i][j], 0, 0, 0);
-            }
-    }
-    // ---- epilogue: lane holds column lr of each 32-wide block, rows 8*(r/4) + 4*(lane/32) + r%4
+            for (int j = 0; j < WNB; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + lr;
-        if (n >= a.N) continue;
-        const float sc = half_bits_to_float(a.row_scale[n]);
-        const float us = a.up_scale[n];
+                for (int r = 0; r < 16; ++r) st_x(mine + ((((wave * 2 + i) * WNB + j) * 16 + r) * 64 + lane), acc[i][j][r]);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = old == (uint32_t)(splitk - 1);
+        }
+        __syncthreads();
+        if (!last_flag) return;
+        for (int z2 = 0; z2 < splitk; ++z2) {
+            if (z2 == z) continue;
+            const int32_t *o = part + ((int64_t)tile * splitk + z2) * tsz;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < WNB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += ld_x(o + ((((wave * 2 + i) * WNB + j) * 16 + r) * 64 + lane));
+        }
+    }
+    // ---- epilogue: operands from LDS (staged before the main loop, or now for ranks above 32)
+    if (!early) {
+        stage_epilogue<BN>(a, epi, m0, n0, tid);
+        __syncthreads();
+    }
+    const int rank = a.rank, RS = rank + 8;
+    const float *s_l = reinterpret_cast<const float *>(epi);
+    const int *q_l = reinterpret_cast<const int *>(epi + 512);
+    const __bf16 *th_l = reinterpret_cast<const __bf16 *>(epi + 1024);
+    const __bf16 *tl_l = th_l + BM * RS;
+    const int8_t *u_l = reinterpret_cast<const int8_t *>(tl_l + BM * RS);
+    float sc[WNB], us[WNB];
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) {
+        const int n = n0 + wn * (32 * WNB) + j * 32 + lr;
+        sc[j] = n < a.N ? half_bits_to_float(a.row_scale[n]) : 0.f;
+        us[j] = n < a.N ? a.up_scale[n] : 0.f;
+    }
+    const int lj = hsel * 8;
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) {
+        const int cl = wn * (32 * WNB) + j * 32 + lr;
+        const int n = n0 + cl;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
+            const int rl = wm * 64 + i * 32;
+            v16f lacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+            for (int kr = 0; kr < rank; kr += 16) {
+                const bool inr = kr + lj + 8 <= rank;
+                v8bf ahi, alo, bup;
+                uint2 w = make_uint2(0u, 0u);
+                if (inr) {
+                    ahi = *reinterpret_cast<const v8bf *>(th_l + (rl + lr) * RS + kr + lj);
+                    alo = *reinterpret_cast<const v8bf *>(tl_l + (rl + lr) * RS + kr + lj);
+                    w = *reinterpret_cast<const uint2 *>(u_l + cl * RS + kr + lj);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        ahi[e] = (__bf16)0.f;
+                        alo[e] = (__bf16)0.f;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bup[e] = (__bf16)(float)(int8_t)(w.x >> (8 * e));
+                    bup[4 + e] = (__bf16)(float)(int8_t)(w.y >> (8 * e));
+                }
+                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bup, lacc, 0, 0, 0);
+                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bup, lacc, 0, 0, 0);
+            }
+            if (n >= a.N) continue;
+            // residual first (y may alias it; each element is read, then written, by this lane only)
+            float rv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m >= a.M) continue;
-                const int accv = 2 * acc[i][j][r] - a.qsum[m];
-                float v = a.s[m] * sc * (float)accv + us * lacc[i][j][r];
-                if (a.res) v += a.res[(int64_t)m * a.ldres + n];
-                a.y[(int64_t)m * a.ldy + n] = v;
-                if (a.acc_tap) a.acc_tap[(int64_t)m * a.ldacc + n] = accv;
+                const int m = m0 + rl + 8 * (r >> 2) + 4 * hsel + (r & 3);
+                rv[r] = (a.res && m < a.M) ? a.res[(int64_t)m * a.ldres + n] : 0.f;
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ml = rl + 8 * g + 4 * hsel;
+                const float4 sv = *reinterpret_cast<const float4 *>(s_l + ml);
+                const int4 qv = *reinterpret_cast<const int4 *>(q_l + ml);
+                const float svs[4] = {sv.x, sv.y, sv.z, sv.w};
+                const int qvs[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g + e, m = m0 + ml + e;
+                    if (m >= a.M) continue;
+                    const int accv = 2 * acc[i][j][r] - qvs[e];
+                    float v = svs[e] * sc[j] * (float)accv + us[j] * lacc[r];
+                    if (a.res) v += rv[r];
+                    a.y[(int64_t)m * a.ldy + n] = v;
+                    if (a.acc_tap) a.acc_tap[(int64_t)m * a.ldacc + n] = accv;
+                }
             }
         }
     }
 }
 
+__global__ void k_clear_u32(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// M <= 64: one workgroup per 32 output columns; wave w takes K steps [w*nk/4, (w+1)*nk/4).
+__global__ __launch_bounds__(kBlock) void k_gemm_skinny(GemmArgs a) {
+    __shared__ int red[kWaves - 1][2][16][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, hsel = lane >> 5;
+    const int n0 = blockIdx.x * 32;
+    const int n = n0 + lr;
+    const bool nok = n < a.N;
+    const int K = a.K, nkt = K / KT;
+    const int kb = (wave * nkt / kWaves) * KT, ke = ((wave + 1) * nkt / kWaves) * KT;  // may be empty
+    const uint8_t *brow = a.sign + (int64_t)(nok ? n : 0) * (K >> 3);
+    const int8_t *arow[2];
+    bool aok[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = i * 32 + lr;
+        aok[i] = m < a.M;
+        arow[i] = a.q + (int64_t)(aok[i] ? m : 0) * a.ldq + hsel * 16;
+    }
+    v16i acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0;
+    for (int k0 = kb; k0 < ke; k0 += KT) {
+        const uint4 bw = nok ? *reinterpret_cast<const uint4 *>(brow + (k0 >> 3)) : make_uint4(0u, 0u, 0u, 0u);
+        v4i af[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                af[i][s] = aok[i] ? *reinterpret_cast<const v4i *>(arow[i] + k0 + 32 * s) : v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const v4i bf = expand16((u4_get(bw, s) >> (16 * hsel)) & 0xffffu);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][s], bf, acc[i], 0, 0, 0);
+        }
+    }
+    // integer partial sums of waves 1..3 -> wave 0 (exact, fixed order)
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[wave - 1][i][r][lane] = acc[i][r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] += red[0][i][r][lane] + red[1][i][r][lane] + red[2][i][r][lane];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (i * 32 >= a.M) break;
+        const v16f lacc = lowrank_block(a, i * 32 + lr, n, lane);
+        store_block(a, acc[i], lacc, i * 32, n, lane);
+    }
+}
+
 }  // namespace
 
+namespace {
+
+// Launch plan of the tile kernel: column-tile width, tile count and K split (only with <= 256 tiles,
+// so the arrival counters fit the fixed kCntBytes block at the start of the scratch).
+struct GemmPlan {
+    int wnb, ntm, ntn, splitk;
+};
+
+GemmPlan plan_gemm(int M, int N, int K) {
+    GemmPlan p{};
+    p.ntm = (M + BM - 1) / BM;
+    const int nk = K / KT;
+    const int64_t wide = (int64_t)p.ntm * ((N + 255) / 256);
+    // wide tiles (128 x 256) when they still give two workgroups per compute unit
+    if (wide >= 512) {
+        p.wnb = 4;
+        p.ntn = (N + 255) / 256;
+        p.splitk = 1;
+        return p;
+    }
+    p.wnb = 2;
+    p.ntn = (N + 127) / 128;
+    const int64_t tiles = (int64_t)p.ntm * p.ntn;
+    p.splitk = 1;
+    while (tiles * p.splitk * 2 <= 512 && p.splitk * 2 <= nk && p.splitk < 8) p.splitk *= 2;
+    return p;
+}
+
+}  // namespace
+
+size_t gemm_scratch_bytes(int M, int N, int K) {
+    if (M <= 64) return 0;
+    const GemmPlan p = plan_gemm(M, N, K);
+    if (p.splitk == 1) return 0;
+    const size_t tiles = (size_t)p.ntm * p.ntn;
+    return kCntBytes + tiles * p.splitk * BM * (64 * p.wnb) * 4;
+}
+
 hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
-    if (a.K % KT || a.rank % 8 || a.rank > kMaxRank) return hipErrorInvalidValue;
-    dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
-    k_gemm_pm1<<<grid, kBlock, 0, stream>>>(a);
+    if (a.K % KT || a.rank % 8 || a.rank > kMaxRank || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
+    if (a.M <= 64) {
+        k_gemm_skinny<<<(a.N + 31) / 32, kBlock, 0, stream>>>(a);
+        return hipGetLastError();
+    }
+    const GemmPlan p = plan_gemm(a.M, a.N, a.K);
+    const int tiles = p.ntm * p.ntn;
+    if (p.splitk > 1) {
+        if (!a.scratch || tiles * 4 > kCntBytes) return hipErrorInvalidValue;
+        k_clear_u32<<<(tiles + kBlock - 1) / kBlock, kBlock, 0, stream>>>(static_cast<uint32_t *>(a.scratch), tiles);
+    }
+    const dim3 grid(tiles, p.splitk);
+    if (p.wnb == 4) k_gemm_tile<4, false><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
+    else if (p.splitk > 1) k_gemm_tile<2, true><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, p.splitk);
+    else k_gemm_tile<2, false><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
     return hipGetLastError();
 }
 

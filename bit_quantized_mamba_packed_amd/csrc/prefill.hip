@@ -133,25 +133,40 @@ struct ConvSeqArgs {
     float *dt;             // [M][H]
 };
 
+// One thread per channel and run of kConvRun consecutive tokens of one sequence: the window of
+// the last d_conv-1 inputs slides in registers, so every Y element is read about once.
+constexpr int kConvRun = 32;
 __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
-    const int m = blockIdx.x;
+    const int runs = (a.L + kConvRun - 1) / kConvRun;
+    const int b = blockIdx.x / runs, t0 = (blockIdx.x - b * runs) * kConvRun;
     const int col = blockIdx.y * kBlock + threadIdx.x;
     if (col >= a.Cd + a.H) return;
-    const int b = m / a.L, t = m - b * a.L;
+    const int t1 = min(a.L, t0 + kConvRun);
+    const int64_t mb = (int64_t)b * a.L;
     if (col < a.Cd) {
-        const float *w = a.conv_w + (int64_t)col * kConvTaps;
-        float v = a.conv_b[col];
+        const float4 w = *reinterpret_cast<const float4 *>(a.conv_w + (int64_t)col * kConvTaps);
+        const float bias = a.conv_b[col];
+        // window = inputs at t0-3, t0-2, t0-1 (conv state entries for negative positions)
+        float win[kConvTaps - 1];
 #pragma unroll
-        for (int k = 0; k < kConvTaps; ++k) {
-            const int tok = t - (kConvTaps - 1) + k;
-            const float xin = tok >= 0 ? a.Y[(int64_t)(m - (kConvTaps - 1) + k) * a.ldY + a.E + col]
-                                       : a.conv_state[((int64_t)b * a.Cd + col) * (kConvTaps - 1) + (kConvTaps - 1) + tok];
-            v += w[k] * xin;
+        for (int k = 0; k < kConvTaps - 1; ++k) {
+            const int tok = t0 - (kConvTaps - 1) + k;
+            win[k] = tok >= 0 ? a.Y[(mb + tok) * a.ldY + a.E + col]
+                              : a.conv_state[((int64_t)b * a.Cd + col) * (kConvTaps - 1) + (kConvTaps - 1) + tok];
         }
-        a.xbc[(int64_t)m * a.Cd + col] = silu_f(v);
+        for (int t = t0; t < t1; ++t) {
+            const float x = a.Y[(mb + t) * a.ldY + a.E + col];
+            const float v = bias + w.x * win[0] + w.y * win[1] + w.z * win[2] + w.w * x;
+            a.xbc[(mb + t) * a.Cd + col] = silu_f(v);
+            win[0] = win[1];
+            win[1] = win[2];
+            win[2] = x;
+        }
     } else {
         const int h = col - a.Cd;
-        a.dt[(int64_t)m * a.H + h] = softplus_f(a.Y[(int64_t)m * a.ldY + a.E + a.Cd + h] + a.dt_bias[h]);
+        const float db = a.dt_bias[h];
+        for (int t = t0; t < t1; ++t)
+            a.dt[(mb + t) * a.H + h] = softplus_f(a.Y[(mb + t) * a.ldY + a.E + a.Cd + h] + db);
     }
 }
 
@@ -188,18 +203,28 @@ struct SsdArgs {
     float *g;              // [M][E] gated output
 };
 
-__global__ void k_ssd_lam(SsdArgs a) {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // (b, h, c)
-    if (idx >= a.B * a.H * a.nch) return;
+// Lam_t = inclusive cumsum of dt_t * A within each chunk: one workgroup per (b, h, c), one token
+// per thread (chunk <= 256), wave scans combined through LDS.
+__global__ __launch_bounds__(kBlock) void k_ssd_lam(SsdArgs a) {
+    __shared__ float wsum[kWaves];
+    const int idx = blockIdx.x;  // (b, h, c)
     const int c = idx % a.nch, bh = idx / a.nch, h = bh % a.H, b = bh / a.H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = c * a.Q + tid;
+    const bool ok = tid < a.Q && t < a.L;
     const float A = -expf(a.A_log[h]);
-    const int t0 = c * a.Q, t1 = min(a.L, t0 + a.Q);
-    float acc = 0.f;
-    for (int t = t0; t < t1; ++t) {
-        acc += a.dt[((int64_t)b * a.L + t) * a.H + h] * A;
-        a.lam[((int64_t)b * a.H + h) * a.L + t] = acc;
+    float v = ok ? a.dt[((int64_t)b * a.L + t) * a.H + h] * A : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
     }
-    a.lam_end[idx] = acc;
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) v += wsum[w];
+    if (ok) a.lam[((int64_t)b * a.H + h) * a.L + t] = v;
+    const int last = min(a.Q, a.L - c * a.Q) - 1;
+    if (tid == last) a.lam_end[idx] = v;
 }
 
 // CB tile (ti, si) of chunk c for group g: 64 x 64 outputs, 4 x 4 per thread, N in tiles of 64.
@@ -304,48 +329,57 @@ __global__ __launch_bounds__(kBlock) void k_ssd_ydiag(SsdArgs a) {
     }
 }
 
-// Chunk-local state S_loc[p][n] = sum_s exp(Lam_end - Lam_s) dt_s x_s[p] B_s[n] for (b, h, c).
-// Thread: p = tid / 4, n in a quarter of N; s in tiles of 32 through LDS.
-constexpr int TS = 32;
+// Chunk-local state S_loc[p][n] = sum_s exp(Lam_end - Lam_s) dt_s x_s[p] B_s[n] for (b, h, c):
+// a (P x chunk) x (chunk x N) product, 64 x 64 outputs per workgroup (4 x 4 per thread), s in tiles of 64.
 __global__ __launch_bounds__(kBlock) void k_ssd_sloc(SsdArgs a) {
-    __shared__ __align__(16) float Xw[TS][TT + 4];     // [s][p] scaled by w_s
-    __shared__ __align__(16) float Bsh[TS][256 + 4];   // [s][n]
+    __shared__ __align__(16) float Xw[TT][TT + 4];  // [s][p], scaled by the decay weight
+    __shared__ __align__(16) float Bs[TT][TT + 4];  // [s][n]
+    __shared__ float wgt[TT];
     const int bhc = blockIdx.x, c = bhc % a.nch, h = (bhc / a.nch) % a.H, b = bhc / (a.nch * a.H);
+    const int n0 = blockIdx.y * TT;
     const int len = min(a.Q, a.L - c * a.Q);
     const int g = h * a.G / a.H;
-    const int tid = threadIdx.x, p = tid >> 2, nq = a.N >> 2, nb = (tid & 3) * nq;
+    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
     const int64_t mbase = (int64_t)b * a.L + c * a.Q;
     const float *lamh = a.lam + ((int64_t)b * a.H + h) * a.L + c * a.Q;
     const float lend = a.lam_end[((int64_t)b * a.H + h) * a.nch + c];
-    float acc[64];
-#pragma unroll
-    for (int j = 0; j < 64; ++j) acc[j] = 0.f;
-    for (int s0 = 0; s0 < len; s0 += TS) {
+    float acc[4][4] = {};
+    for (int s0 = 0; s0 < len; s0 += TT) {
         __syncthreads();
-        for (int k = tid; k < TS * TT; k += kBlock) {
-            const int r = k / TT, q = k % TT;
-            const int s = s0 + r;
-            float v = 0.f;
-            if (s < len) v = a.xbc[(mbase + s) * a.Cd + h * a.P + q] * expf(lend - lamh[s]) * a.dt[(mbase + s) * a.H + h];
-            Xw[r][q] = v;
-        }
-        for (int k = tid; k < TS * a.N; k += kBlock) {
-            const int r = k / a.N, n = k % a.N;
-            const int s = s0 + r;
-            Bsh[r][n] = s < len ? a.xbc[(mbase + s) * a.Cd + a.E + g * a.N + n] : 0.f;
+        if (tid < TT) {
+            const int s = s0 + tid;
+            wgt[tid] = s < len ? expf(lend - lamh[s]) * a.dt[(mbase + s) * a.H + h] : 0.f;
         }
         __syncthreads();
-        for (int r = 0; r < TS; ++r) {
-            const float xv = Xw[r][p];
+        for (int k = tid; k < TT * TT; k += kBlock) {
+            const int r = k / TT, q = k % TT;  // r: token within the tile, q: feature
+            const int s = s0 + r;
+            const bool sin_ = s < len;
+            Xw[r][q] = sin_ ? a.xbc[(mbase + s) * a.Cd + h * a.P + q] * wgt[r] : 0.f;
+            Bs[r][q] = sin_ && n0 + q < a.N ? a.xbc[(mbase + s) * a.Cd + a.E + g * a.N + n0 + q] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int r = 0; r < TT; ++r) {
+            const float4 xv = *reinterpret_cast<const float4 *>(&Xw[r][ty * 4]);
+            const float4 bv = *reinterpret_cast<const float4 *>(&Bs[r][tx * 4]);
+            const float xr[4] = {xv.x, xv.y, xv.z, xv.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-            for (int j = 0; j < 64; ++j)
-                if (j < nq) acc[j] += xv * Bsh[r][nb + j];
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += xr[i] * br[j];
         }
     }
-    float *out = a.sloc + ((((int64_t)b * a.H + h) * a.nch + c) * a.P + p) * a.N + nb;
+    float *out = a.sloc + (((int64_t)b * a.H + h) * a.nch + c) * a.P * a.N;
 #pragma unroll
-    for (int j = 0; j < 64; ++j)
-        if (j < nq) out[j] = acc[j];
+    for (int i = 0; i < 4; ++i) {
+        const int p = ty * 4 + i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx * 4 + j;
+            if (n < a.N) out[(int64_t)p * a.N + n] = acc[i][j];
+        }
+    }
 }
 
 // Sequential carry over chunks; sloc[c] is replaced by the state entering chunk c.
@@ -505,6 +539,7 @@ hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w
         a.ldy = s.Ninp;
         a.acc_tap = tp.in_acc;
         a.ldacc = s.Ninp;
+        a.scratch = pws.gemm_scratch;
         if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
     }
     {
@@ -557,6 +592,7 @@ hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w
         a.ldres = s.D;
         a.acc_tap = tp.out_acc;
         a.ldacc = s.D;
+        a.scratch = pws.gemm_scratch;
         if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
     }
     return hipSuccess;
@@ -598,6 +634,7 @@ PrefillWs carve_prefill_ws(const Shape &s, int batch, int seqlen, int chunk, voi
     w.qsum_out = static_cast<int32_t *>(take(M * 4));
     w.thi_out = static_cast<__bf16 *>(take(M * s.Rout * 2));
     w.tlo_out = static_cast<__bf16 *>(take(M * s.Rout * 2));
+    w.gemm_scratch = take(std::max(gemm_scratch_bytes((int)M, s.Ninp, s.D), gemm_scratch_bytes((int)M, s.D, s.E)));
     w.bytes = off;
     return w;
 }
@@ -655,12 +692,13 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.ldy = s.Ninp;
         a.acc_tap = tp.in_acc;
         a.ldacc = s.Ninp;
+        a.scratch = ws.gemm_scratch;
         if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
     }
     // 3/4. conv over the sequence, dt, conv-state handoff
     ConvSeqArgs cv{ws.Y, s.Ninp, s.E, s.Cd, s.H, seqlen, M, w.conv_w, w.conv_b, w.dt_bias, st.conv, ws.xbc, ws.dt};
     {
-        dim3 grid(M, (s.Cd + s.H + kBlock - 1) / kBlock);
+        dim3 grid(batch * ((seqlen + kConvRun - 1) / kConvRun), (s.Cd + s.H + kBlock - 1) / kBlock);
         k_conv_seq<<<grid, kBlock, 0, stream>>>(cv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_conv_handoff<<<(batch * s.Cd + kBlock - 1) / kBlock, kBlock, 0, stream>>>(cv, st.conv, batch);
@@ -694,13 +732,13 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.g = ws.gbuf;
         const int tq = (chunk + TT - 1) / TT;
         const int nbhc = batch * s.H * nch;
-        k_ssd_lam<<<(nbhc + 63) / 64, 64, 0, stream>>>(a);
+        k_ssd_lam<<<nbhc, kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_ssd_cb<<<dim3(batch * s.G * nch, tq * tq), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_ssd_ydiag<<<dim3(nbhc, tq), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ssd_sloc<<<nbhc, kBlock, 0, stream>>>(a);
+        k_ssd_sloc<<<dim3(nbhc, (s.N + TT - 1) / TT), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_ssd_scan<<<dim3((s.P * s.N + kBlock - 1) / kBlock, batch * s.H), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -763,6 +801,7 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.ldres = s.D;
         a.acc_tap = tp.out_acc;
         a.ldacc = s.D;
+        a.scratch = ws.gemm_scratch;
         if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
     }
     return hipSuccess;
