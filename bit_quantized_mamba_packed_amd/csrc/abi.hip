@@ -86,7 +86,8 @@ int check_taps(const dfssm_taps *t) {
 size_t decode_ws_bytes(const Shape &s, int batch, bool stack, int n_layers = 0) {
     DecodeWs w = carve_decode_ws(s, batch, nullptr, stack);
     size_t extra = 0;
-    if (stack && stack_persistent_ok(s, batch)) extra = stack_extra_ws_bytes(s, batch, n_layers);
+    if (stack && stack_persistent_ok(s, batch))
+        extra = std::max(stack_extra_ws_bytes(s, batch, n_layers), stack2_extra_ws_bytes(s, batch, n_layers));
     else if (decode_uses_mfma(s, batch)) extra = carve_prefill_ws(s, batch, 1, 1, nullptr).bytes;
     return w.bytes + extra;
 }
@@ -242,6 +243,9 @@ int dfssm_stack_decode(const dfssm_dims *dims, const dfssm_layer_weights *layers
     const DecodeWs wsp = carve_decode_ws(s, batch, ws, true);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (stack_persistent_ok(s, batch) && stack2_ok(s, batch))
+        return hip_status(launch_stack2(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps,
+                                        static_cast<char *>(ws) + wsp.bytes, taps, st));
     if (stack_persistent_ok(s, batch)) {
         // DFSSM_STACK_MAX_WGS caps the resident grid (a tuning knob; 0 = as many as useful)
         e = launch_stack_persistent(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, wsp,

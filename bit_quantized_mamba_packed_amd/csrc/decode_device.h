@@ -83,6 +83,49 @@ __device__ __forceinline__ float4 ld_x4(const float *p) {
     return make_float4(ld_x(p), ld_x(p + 1), ld_x(p + 2), ld_x(p + 3));
 }
 
+// 2*KCH coherent (sc1) 16-byte loads of a thread's 4*KCH consecutive tagged words, waited for
+// inside the same asm block. Word 2j is (r[j].x payload, r[j].y epoch), word 2j+1 is (r[j].z, r[j].w).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <int KCH>
+__device__ __forceinline__ void load_words_sc1(const uint64_t *p, u32x4 (&r)[2 * KCH]);
+template <>
+__device__ __forceinline__ void load_words_sc1<1>(const uint64_t *p, u32x4 (&r)[2]) {
+    asm volatile("global_load_dwordx4 %0, %2, off sc1\n\t"
+                 "global_load_dwordx4 %1, %2, off offset:16 sc1\n\t"
+                 "s_waitcnt vmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]) : "v"(p) : "memory");
+}
+template <>
+__device__ __forceinline__ void load_words_sc1<2>(const uint64_t *p, u32x4 (&r)[4]) {
+    asm volatile("global_load_dwordx4 %0, %4, off sc1\n\t"
+                 "global_load_dwordx4 %1, %4, off offset:16 sc1\n\t"
+                 "global_load_dwordx4 %2, %4, off offset:32 sc1\n\t"
+                 "global_load_dwordx4 %3, %4, off offset:48 sc1\n\t"
+                 "s_waitcnt vmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]) : "v"(p) : "memory");
+}
+template <>
+__device__ __forceinline__ void load_words_sc1<4>(const uint64_t *p, u32x4 (&r)[8]) {
+    asm volatile("global_load_dwordx4 %0, %8, off sc1\n\t"
+                 "global_load_dwordx4 %1, %8, off offset:16 sc1\n\t"
+                 "global_load_dwordx4 %2, %8, off offset:32 sc1\n\t"
+                 "global_load_dwordx4 %3, %8, off offset:48 sc1\n\t"
+                 "global_load_dwordx4 %4, %8, off offset:64 sc1\n\t"
+                 "global_load_dwordx4 %5, %8, off offset:80 sc1\n\t"
+                 "global_load_dwordx4 %6, %8, off offset:96 sc1\n\t"
+                 "global_load_dwordx4 %7, %8, off offset:112 sc1\n\t"
+                 "s_waitcnt vmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+                   "=&v"(r[7])
+                 : "v"(p)
+                 : "memory");
+}
+template <>
+__device__ __forceinline__ void load_words_sc1<8>(const uint64_t *p, u32x4 (&r)[16]) {
+    load_words_sc1<4>(p, *reinterpret_cast<u32x4(*)[8]>(&r[0]));
+    load_words_sc1<4>(p + 16, *reinterpret_cast<u32x4(*)[8]>(&r[8]));
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
@@ -94,6 +137,13 @@ __device__ __forceinline__ int quant1(float u, float inv) {
     float r = rintf(u * inv);
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (int)r;
+}
+
+// Element of chunk i (4 consecutive inputs) a thread handles in the norm + quantizer prologue:
+// each thread owns KCH chunks in a row, so its inputs are one contiguous run of 4*KCH values.
+template <int KCH>
+__device__ __forceinline__ int prologue_elem(int i) {
+    return ((int)threadIdx.x * KCH + i) * 4;
 }
 
 struct QuantGemvArgs {
@@ -130,7 +180,7 @@ struct PlainSource {
     __device__ __forceinline__ void load(int b, int K, float4 *hv) const {
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int e = (i * kBlock + (int)threadIdx.x) * 4;
+            const int e = prologue_elem<KCH>(i);
             if (e < K) hv[i] = ld_x4(X + (int64_t)b * stride + e);
         }
     }
@@ -160,7 +210,7 @@ __device__ void norm_quant_prologue(const QuantGemvArgs &a, const Src &src, int8
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int e = (i * kBlock + tid) * 4;
+            const int e = prologue_elem<KCH>(i);
             if (e < K) ss += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
         }
         if (a.pre_w) {
@@ -169,7 +219,7 @@ __device__ void norm_quant_prologue(const QuantGemvArgs &a, const Src &src, int8
             ss = 0.f;
 #pragma unroll
             for (int i = 0; i < KCH; ++i) {
-                const int e = (i * kBlock + tid) * 4;
+                const int e = prologue_elem<KCH>(i);
                 if (e < K) {
                     const float4 w = *reinterpret_cast<const float4 *>(a.pre_w + e);
                     hv[i].x = (hv[i].x * r0) * w.x;
@@ -183,7 +233,7 @@ __device__ void norm_quant_prologue(const QuantGemvArgs &a, const Src &src, int8
         }
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int e = (i * kBlock + tid) * 4;
+            const int e = prologue_elem<KCH>(i);
             if (e < K) {
                 if (tap_wg && a.tap_h) *reinterpret_cast<float4 *>(a.tap_h + (int64_t)b * K + e) = hv[i];
                 if (xsave) *reinterpret_cast<float4 *>(xsave + b * K + e) = hv[i];
@@ -194,7 +244,7 @@ __device__ void norm_quant_prologue(const QuantGemvArgs &a, const Src &src, int8
         float pm = 0.f;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int e = (i * kBlock + tid) * 4;
+            const int e = prologue_elem<KCH>(i);
             if (e < K) {
                 const float4 w = *reinterpret_cast<const float4 *>(a.W + e);
                 hv[i].x = hv[i].x * w.x;
@@ -213,7 +263,7 @@ __device__ void norm_quant_prologue(const QuantGemvArgs &a, const Src &src, int8
         int qs = 0;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int e = (i * kBlock + tid) * 4;
+            const int e = prologue_elem<KCH>(i);
             if (e < K) {
                 hv[i].x = hv[i].x * r;
                 hv[i].y = hv[i].y * r;

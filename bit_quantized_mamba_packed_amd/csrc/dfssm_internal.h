@@ -61,6 +61,14 @@ hipError_t launch_stack_persistent(const Shape &s, const dfssm_layer_weights *la
                                    void *extra, const dfssm_taps *taps, int max_wgs, hipStream_t stream);
 bool stack_persistent_ok(const Shape &s, int batch);
 
+// Two-exchange persistent stack decode (flow2.hip), used when the shape and batch fit it and
+// DFSSM_STACK_V1=1 is not set.
+bool stack2_ok(const Shape &s, int batch);
+size_t stack2_extra_ws_bytes(const Shape &s, int batch, int n_layers);
+hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states, int n_layers,
+                         const float *final_w, const float *x0, float *y, int batch, int n_steps, void *extra,
+                         const dfssm_taps *taps, hipStream_t stream);
+
 // int8-code x (+-1 scaffold) GEMM with the projection epilogue (gemm.hip):
 //   y[m][n] = s[m]*row_scale[n]*acc[m][n] + up_scale[n] * sum_j t'[m][j]*lora_up[n][j] (+ res[m][n])
 // acc = sum_k sgn[n][k]*q[m][k]; t' = thi + tlo (bf16 split of dn_scale*s*t). rank % 8 == 0, K % 128 == 0.

@@ -1,0 +1,959 @@
+// Persistent stack decode with two exchanges per layer, for one token per step (batch 1: every
+// weight and state a workgroup needs stays in registers or LDS without spilling).
+//
+// One cooperative launch runs every step of every layer. The workgroups have two roles:
+//   role 1, item w < n1: head h = w / S, channels [p0, p0 + pr) of that head (pr = P / S):
+//            gather the residual h (all D values), RMSNorm + int8 quantizer, LoRA-down t, the
+//            packed-sign GEMV of exactly the in_proj rows this item consumes (its z and x channels,
+//            its head's dt row, and the group's B and C rows, which every item computes itself
+//            instead of exchanging them), rescale + LoRA-up epilogue, conv step, SSM update +
+//            readout, SiLU(z) gate -> publish this item's gated outputs g
+//   role 2, item w >= n1: out_proj rows [(w - n1) * R2, ...): gather g (all E values), gated
+//            RMSNorm + quantizer, LoRA-down, GEMV of its rows, epilogue, residual add -> publish
+//            those rows of h (it keeps them: they are its next residual input)
+// Each exchange is an all-gather of tagged 64-bit words {payload, epoch}, written with
+// agent-coherent stores and read with 16-byte agent-coherent loads until every epoch matches;
+// there are no flags and no barriers. Every layer has its own word slots, rewritten one token
+// later; every workgroup reads all of a layer's words before anything of the next token's same
+// layer can be produced, so a slot is never rewritten while a reader still needs it.
+//
+// A workgroup works on one phase per layer, so right after publishing it loads what its next
+// layer needs that does not depend on the token (sign rows and LoRA-down factors straight into
+// LDS, scales, conv taps and windows, SSM state into registers): that latency hides behind the
+// other role's work. Every wait is bounded: on a timeout the kernel flags the workspace, stops
+// waiting and poisons y with NaN, so every wave still reaches the end.
+//
+// The B and C conv windows are per-workgroup copies in the workspace (each role-1 workgroup
+// computes those channels itself); workgroup 0 writes its copy back to the caller's conv state.
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "decode_device.h"
+
+namespace dfssm {
+
+namespace {
+
+constexpr int F2_MAXI = 21;   // in_proj rows per GEMV thread: rows rg + NG * i
+constexpr int F2_SBLK = 21;   // 1 KB blocks of in_proj sign rows each wave copies per layer
+constexpr int F2_UPC = 2;     // LoRA-up chunks (16 B) per row: rank <= 32
+constexpr int F2_MAXO = 4;    // out_proj sign chunks per thread
+constexpr int F2_FPT = 4;     // SSM state float4s per thread and token
+constexpr int F2_ROWS = 512;  // item rows (incl. padding rows) per workgroup, at most
+constexpr unsigned kSpin2 = 1u << 21;
+constexpr int kSleep2 = 1;
+constexpr int kTable2 = 16;
+constexpr int kMaxDevices2 = 64;
+constexpr size_t kF2MaxLds = 159 * 1024;
+
+struct Entry2 {
+    dfssm_layer_weights w;
+    dfssm_layer_state st;
+};
+struct Chunk2 {
+    Entry2 e[kTable2];
+};
+
+struct F2Args {
+    int n_layers, n_steps, batch;
+    int D, E, N, P, H, G, Cd, Nin, Ninp, Rin, Rout;
+    float eps;
+    int S, pr, R1, npad, R2, fpt, n1, n2;
+    const Entry2 *layers;
+    const float *final_w, *x0;
+    float *y;
+    uint64_t *hx, *gx;  // [L][batch][D], [L][batch][E] tagged words
+    uint64_t *rx;       // the stack's final RMSNorm factor of the previous token (tagged)
+    float *bcp;         // [nwg][L][batch][2GN][3] private B/C conv windows
+    int *err;
+    dfssm_taps taps;
+};
+
+__device__ __forceinline__ size_t f2_round_kb(size_t v) { return (v + 1023) & ~(size_t)1023; }
+__device__ __forceinline__ uint64_t tag2(uint32_t bits, uint32_t tag) { return ((uint64_t)tag << 32) | bits; }
+__device__ __forceinline__ uint32_t fbits2(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf2(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+__device__ void f2_error(const F2Args &a) {
+    __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float nan = __builtin_nanf("");
+    a.y[0] = nan;
+    a.y[(int64_t)(a.n_steps - 1) * a.batch * a.D] = nan;
+}
+
+// This thread's 4*KCH consecutive words at p, reloaded until every epoch equals `tag` (bounded).
+template <int KCH>
+__device__ __forceinline__ void f2_gather(const F2Args &a, const uint64_t *p, uint32_t tag, u32x4 (&r)[2 * KCH]) {
+    unsigned spins = 0;
+    for (;;) {
+        load_words_sc1<KCH>(p, r);
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 2 * KCH; ++j) ok = ok && r[j].y == tag && r[j].w == tag;
+        if (ok) return;
+        __builtin_amdgcn_s_sleep(kSleep2);
+        ++spins;
+        if ((spins & 63) == 0 && ld_x(a.err)) return;
+        if (spins > kSpin2) {
+            f2_error(a);
+            return;
+        }
+    }
+}
+
+// Gather NB vectors of K tagged words, RMSNorm (after the stack's final RMSNorm when pre_w is set),
+// int8 quantizer -> codes sq[b][K], bit-planes spl[b][8][K/32], sum of codes, scale; xs (optional)
+// keeps the normalised input. wr: this thread's norm weights. Taps are written by workgroup 0.
+template <int NB, int KCH>
+__device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t tag, const float4 (&wr)[KCH],
+                            const float *pre_w, float *pre_out, int8_t *sq, uint32_t *spl, int *sqsum, float *ssc,
+                            float *red, int *ired, float *xs, bool tapwg, float *r0_out, float *tap_h, float *tap_u,
+                            int8_t *tap_q, float *tap_s) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e0 = prologue_elem<KCH>(0);
+    const bool mine = e0 < K;   // K is a multiple of 4*KCH: a thread has all of its chunks or none
+    for (int b = 0; b < NB; ++b) {
+        float4 hv[KCH];
+        if (mine) {
+            u32x4 r[2 * KCH];
+            f2_gather<KCH>(a, X + (int64_t)b * K + e0, tag, r);
+#pragma unroll
+            for (int i = 0; i < KCH; ++i)
+                hv[i] = make_float4(bitsf2(r[2 * i].x), bitsf2(r[2 * i].z), bitsf2(r[2 * i + 1].x), bitsf2(r[2 * i + 1].z));
+        } else {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) hv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) ss += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
+        if (pre_w) {
+            const float tot0 = block_sum(ss, red);
+            const float r0 = 1.0f / sqrtf(tot0 / (float)K + a.eps);
+            if (r0_out && tid == 0) *r0_out = r0;
+            ss = 0.f;
+            if (mine) {
+#pragma unroll
+                for (int i = 0; i < KCH; ++i) {
+                    const int e = prologue_elem<KCH>(i);
+                    const float4 w = *reinterpret_cast<const float4 *>(pre_w + e);
+                    hv[i].x = (hv[i].x * r0) * w.x;
+                    hv[i].y = (hv[i].y * r0) * w.y;
+                    hv[i].z = (hv[i].z * r0) * w.z;
+                    hv[i].w = (hv[i].w * r0) * w.w;
+                    ss += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
+                    if (tapwg && pre_out) *reinterpret_cast<float4 *>(pre_out + (int64_t)b * K + e) = hv[i];
+                }
+            }
+        }
+        float pm = 0.f;
+        if (mine) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const int e = prologue_elem<KCH>(i);
+                if (xs) *reinterpret_cast<float4 *>(xs + b * K + e) = hv[i];
+                if (tapwg && tap_h) *reinterpret_cast<float4 *>(tap_h + (int64_t)b * K + e) = hv[i];
+                const float4 w = wr[i];
+                hv[i].x = hv[i].x * w.x;
+                hv[i].y = hv[i].y * w.y;
+                hv[i].z = hv[i].z * w.z;
+                hv[i].w = hv[i].w * w.w;
+                pm = fmaxf(pm, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)), fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
+            }
+        }
+        // u = fl(fl(h * w) * r): with r > 0 the largest |u| is fl(max|h * w| * r) exactly
+        float tot;
+        block_sum_max(ss, pm, red, tot, pm);
+        const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
+        const float amax = pm * r;
+        const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+        const float s = amax > 0.f ? amax / 127.0f : 0.f;
+        int qs = 0;
+        if (mine) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const int e = prologue_elem<KCH>(i);
+                hv[i].x = hv[i].x * r;
+                hv[i].y = hv[i].y * r;
+                hv[i].z = hv[i].z * r;
+                hv[i].w = hv[i].w * r;
+                const int q0 = quant1(hv[i].x, inv), q1 = quant1(hv[i].y, inv);
+                const int q2 = quant1(hv[i].z, inv), q3 = quant1(hv[i].w, inv);
+                qs += q0 + q1 + q2 + q3;
+                const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
+                                        ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+                *reinterpret_cast<uint32_t *>(sq + b * K + e) = packed;
+                if (tapwg) {
+                    if (tap_u) *reinterpret_cast<float4 *>(tap_u + (int64_t)b * K + e) = hv[i];
+                    if (tap_q) *reinterpret_cast<uint32_t *>(tap_q + (int64_t)b * K + e) = packed;
+                }
+            }
+        }
+        qs = block_isum(qs, ired);
+        if (tid == 0) {
+            sqsum[b] = qs;
+            ssc[b] = s;
+            if (tapwg && tap_s) tap_s[b] = s;
+        }
+    }
+    __syncthreads();
+    // bit-planes via wave ballots over 64 consecutive codes
+    const int G32 = K >> 5;
+    for (int b = 0; b < NB; ++b) {
+        for (int c = wave; c < (K >> 6); c += kWaves) {
+            const uint32_t v = (uint8_t)sq[b * K + c * 64 + lane];
+            uint64_t m8 = 0;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint64_t m = __ballot((v >> p) & 1u);
+                if ((lane & 7) == p) m8 = m;
+            }
+            if (lane < 16) spl[(b * 8 + (lane & 7)) * G32 + 2 * c + (lane >> 3)] = lane < 8 ? (uint32_t)m8 : (uint32_t)(m8 >> 32);
+        }
+    }
+    __syncthreads();
+}
+
+// sum_k sgn * q of one 16-byte sign chunk against the bit-planes of the same 128 codes:
+// 2 * (sum over set bits of q) - sum(q) is finished by the caller; this returns sum over set bits.
+__device__ __forceinline__ int chunk_pos(const uint4 &bits, const uint4 (&pl)[8]) {
+    int pos = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int c = __popc(bits.x & pl[p].x) + __popc(bits.y & pl[p].y) + __popc(bits.z & pl[p].z) +
+                      __popc(bits.w & pl[p].w);
+        pos += p < 7 ? (c << p) : -(c << 7);
+    }
+    return pos;
+}
+
+// Sum over groups of w consecutive lanes (w a power of two <= 64) with DPP row operations; the
+// group's total is valid in its last lane (lane % w == w - 1).
+__device__ __forceinline__ int dpp_group_sum(int v, int w) {
+    if (w >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    if (w >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    if (w >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    if (w >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true); // row_shr:8
+    if (w >= 32) v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+    if (w >= 64) v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
+    return v;
+}
+template <int CTRL, int RMASK, bool BC>
+__device__ __forceinline__ float dpp_add_f(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, RMASK, 0xF, BC));
+}
+__device__ __forceinline__ float dpp_group_sum_f(float v, int w) {
+    if (w >= 2) v = dpp_add_f<0xB1, 0xF, true>(v);
+    if (w >= 4) v = dpp_add_f<0x4E, 0xF, true>(v);
+    if (w >= 8) v = dpp_add_f<0x114, 0xF, true>(v);
+    if (w >= 16) v = dpp_add_f<0x118, 0xF, true>(v);
+    if (w >= 32) v = dpp_add_f<0x142, 0xA, false>(v);
+    if (w >= 64) v = dpp_add_f<0x143, 0xC, false>(v);
+    return v;
+}
+
+__device__ __forceinline__ int sdot_chunk(const uint4 &w, const int4 &q, int acc) {
+    acc = __builtin_amdgcn_sdot4((int)w.x, q.x, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w.y, q.y, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w.z, q.z, acc, false);
+    acc = __builtin_amdgcn_sdot4((int)w.w, q.w, acc, false);
+    return acc;
+}
+
+template <int KCH>
+__device__ __forceinline__ void load_norm_w(float4 (&wr)[KCH], const float *w, int K) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+        const int e = prologue_elem<KCH>(i);
+        wr[i] = e < K ? *reinterpret_cast<const float4 *>(w + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// Direct-to-LDS copies (no registers): a wave instruction moves 64 lanes x 16 bytes into 1 KB of
+// consecutive LDS. Chunk i of the destination comes from src(i); lanes past n copy chunk 0 into the
+// padding (regions are whole KB). Every workgroup reads the same weights at the same moment, so each
+// starts at a different 1 KB block (rot) and wraps: the concurrent requests spread over all L2
+// channels instead of queueing on the one that holds the block everybody wants.
+__device__ __forceinline__ int f2_rot(int nblk) { return nblk > 0 ? (int)((blockIdx.x * 37u) % (unsigned)nblk) : 0; }
+
+__device__ __forceinline__ void lds_copy_contig(char *dst, const char *src, int n16) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nblk = (n16 + 63) >> 6, rot = f2_rot(nblk);
+    for (int k = wave; k < nblk; k += kWaves) {
+        int kb = k + rot;
+        if (kb >= nblk) kb -= nblk;
+        const int base = kb * 64, i = base + lane;
+        __builtin_amdgcn_global_load_lds(src + (size_t)(i < n16 ? i : 0) * 16, dst + (size_t)base * 16, 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ float up_dot2(const int4 (&w)[F2_UPC], int rank, const float *v) {
+    float lr = 0.f;
+#pragma unroll
+    for (int i = 0; i < F2_UPC; ++i) {
+        if (i * 16 < rank) {
+            const int ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) lr += (float)(int8_t)(ws[q] >> (8 * k)) * v[i * 16 + 4 * q + k];
+        }
+    }
+    return lr;
+}
+
+__device__ __forceinline__ void load_up(int4 (&w)[F2_UPC], const int8_t *lora_up, int rank, int n) {
+    const int8_t *p = lora_up + (int64_t)n * rank;
+#pragma unroll
+    for (int i = 0; i < F2_UPC; ++i) {
+        if (i * 16 < rank) {
+            if (i * 16 + 16 <= rank) {
+                w[i] = reinterpret_cast<const int4 *>(p)[i];
+            } else {   // rank 8: half a chunk
+                const int2 h = reinterpret_cast<const int2 *>(p)[2 * i];
+                w[i] = make_int4(h.x, h.y, 0, 0);
+            }
+        } else {
+            w[i] = make_int4(0, 0, 0, 0);
+        }
+    }
+}
+
+// Which in_proj row / conv channel the r-th row of an item covers.
+struct ItemRow {
+    int n, ch;  // in_proj row, conv channel (-1: z, dt or padding)
+};
+__device__ __forceinline__ ItemRow item_row(const F2Args &a, int r, int h, int p0, int g) {
+    const int pr = a.pr, N = a.N, E = a.E;
+    ItemRow m{0, -1};
+    if (r < pr) {
+        m.n = h * a.P + p0 + r;
+    } else if (r < 2 * pr) {
+        m.ch = h * a.P + p0 + (r - pr);
+    } else if (r == 2 * pr) {
+        m.n = E + a.Cd + h;
+    } else if (r < 2 * pr + 1 + N) {
+        m.ch = E + g * N + (r - 2 * pr - 1);
+    } else if (r < a.R1) {
+        m.ch = E + a.G * N + g * N + (r - 2 * pr - 1 - N);
+    } else {
+        m.n = a.Nin + (r - a.R1);   // padding row (computed only for the taps)
+    }
+    if (m.ch >= 0) m.n = E + m.ch;
+    return m;
+}
+
+// Per-thread state of one epilogue row (rows tid and tid + 256 of the item).
+template <int NB>
+struct RowRegs {
+    ItemRow m;
+    float sc, us, cb;
+    float4 cw;
+    int4 up[F2_UPC];
+    float win[NB][3];
+};
+
+template <int NB, int KCH>
+__global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
+    extern __shared__ __align__(16) char smem[];
+    __shared__ float red[2 * kWaves];
+    __shared__ int ired[kWaves];
+    __shared__ int sqsum[NB];
+    __shared__ float ssc[NB];
+    __shared__ float dtl[NB];
+    __shared__ float r0s;
+    const int D = a.D, E = a.E, N = a.N, P = a.P;
+    const int Kmax = D > E ? D : E;
+    int8_t *sq = reinterpret_cast<int8_t *>(smem);                          // [NB][Kmax]
+    uint32_t *spl = reinterpret_cast<uint32_t *>(smem + NB * Kmax);         // [NB][8][Kmax/32]
+    int *accl = reinterpret_cast<int *>(smem + 2 * NB * Kmax);              // [NB][F2_ROWS]
+    float *tv = reinterpret_cast<float *>(accl + NB * F2_ROWS);             // [NB][64]
+    float *zl = tv + NB * 64;                                               // [NB][P]
+    float *xl = zl + NB * P;                                                // [NB][P]
+    float *Bl = xl + NB * P;                                                // [NB][N]
+    float *Cl = Bl + NB * N;                                                // [NB][N]
+    char *wreg = reinterpret_cast<char *>(Cl + NB * N);                     // sign rows, then LoRA-down rows
+    const int tid = threadIdx.x, wg = blockIdx.x;
+    const int L = a.n_layers, B = a.batch;
+    const dfssm_taps &T = a.taps;
+    const int64_t n_tok = (int64_t)a.n_steps * L;
+    if (wg < a.n1) {
+        // ====================================================================== role 1
+        const int h = wg / a.S, p0 = (wg % a.S) * a.pr, g = h * a.G / a.H;
+        const bool pad_rows = wg == 0 && T.in_acc != nullptr;
+        const int R1t = a.R1 + (pad_rows ? a.npad : 0);
+        const int nbc = 2 * a.G * N;
+        const int CPR1 = D >> 7, NG1 = kBlock / CPR1, c1 = tid % CPR1, rg1 = tid / CPR1;
+        const int TPR1 = kBlock / a.Rin, j1 = tid / TPR1, cl1 = tid % TPR1, C16_1 = D >> 4;
+        const int N4 = N >> 2, nf = a.pr * N4;
+        // the group's B and C rows are tapped by the first item of the group's first head
+        const bool bc_tap = p0 == 0 && h == g * a.H / a.G;
+        // fixed per workgroup: byte offsets (in a layer's in_proj sign matrix) of the 16-byte chunks
+        // this lane copies into LDS, block by block (rotated start), and the rows of the epilogue
+        const int s16 = R1t * CPR1, sblk = (s16 + 63) >> 6, srot = f2_rot(sblk);
+        int soff[F2_SBLK];
+#pragma unroll
+        for (int j = 0; j < F2_SBLK; ++j) {
+            const int k = (tid >> 6) + kWaves * j;
+            soff[j] = 0;
+            if (k < sblk) {
+                int kb = k + srot;
+                if (kb >= sblk) kb -= sblk;
+                const int i = kb * 64 + (tid & 63) < s16 ? kb * 64 + (tid & 63) : 0;
+                const int r = i / CPR1, c = i - r * CPR1;
+                soff[j] = item_row(a, r, h, p0, g).n * (D >> 3) + c * 16;
+            }
+        }
+        ItemRow rmap[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) rmap[k] = item_row(a, min(tid + k * kBlock, F2_ROWS - 1), h, p0, g);
+        char *sgn1 = wreg;
+        char *ldn1 = wreg + f2_round_kb((size_t)R1t * (D >> 3));
+        // ---- per-layer loads that do not depend on the token: issued one layer ahead
+        RowRegs<NB> rw[2];
+        float4 st[F2_FPT][NB];
+        float4 wr[KCH];
+        float dsc1 = 0.f, dtb = 0.f, Ah = 0.f, Dh = 0.f;
+        auto prefetch = [&](int t, int l) {
+            const Entry2 Ly = a.layers[l];
+            const dfssm_proj &pin = Ly.w.in_proj;
+#pragma unroll
+            for (int j = 0; j < F2_SBLK; ++j) {
+                const int k = (tid >> 6) + kWaves * j;
+                if (k < sblk) {
+                    int kb = k + srot;
+                    if (kb >= sblk) kb -= sblk;
+                    __builtin_amdgcn_global_load_lds(pin.sign + soff[j], sgn1 + (size_t)kb * 64 * 16, 16, 0, 0);
+                }
+            }
+            lds_copy_contig(ldn1, reinterpret_cast<const char *>(pin.lora_dn), a.Rin * C16_1);
+            dsc1 = pin.lora_dn_scale[j1];
+            load_norm_w<KCH>(wr, Ly.w.norm_w, D);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int r = tid + k * kBlock;
+                if (r < R1t) {
+                    RowRegs<NB> &R = rw[k];
+                    R.m = rmap[k];
+                    R.sc = half_bits_to_float(pin.row_scale[R.m.n]);
+                    R.us = pin.lora_up_scale[R.m.n];
+                    load_up(R.up, pin.lora_up, a.Rin, R.m.n);
+                    if (R.m.ch >= 0) {
+                        R.cw = *reinterpret_cast<const float4 *>(Ly.w.conv_w + (int64_t)R.m.ch * kConvTaps);
+                        R.cb = Ly.w.conv_b[R.m.ch];
+                        const bool own = R.m.ch < E;
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) {
+                            const float *wsrc = (own || t == 0)
+                                                    ? Ly.st.conv + ((int64_t)b * a.Cd + R.m.ch) * (kConvTaps - 1)
+                                                    : a.bcp + ((((int64_t)wg * L + l) * B + b) * nbc + (R.m.ch - E)) * 3;
+                            R.win[b][0] = wsrc[0];
+                            R.win[b][1] = wsrc[1];
+                            R.win[b][2] = wsrc[2];
+                        }
+                    }
+                }
+            }
+            dtb = Ly.w.dt_bias[h];
+            Ah = -expf(Ly.w.A_log[h]);
+            Dh = Ly.w.D[h];
+#pragma unroll
+            for (int i = 0; i < F2_FPT; ++i) {
+                const int f = tid + kBlock * i;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    st[i][b] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (i < a.fpt && f < nf) {
+                        const int p = f / N4, n4 = f - p * N4;
+                        st[i][b] = reinterpret_cast<const float4 *>(Ly.st.ssm + (((int64_t)b * a.H + h) * P + p0 + p) * N)[n4];
+                    }
+                }
+            }
+        };
+        prefetch(0, 0);
+        for (int64_t it = 0; it < n_tok; ++it) {
+            const int t = (int)(it / L), l = (int)(it - (int64_t)t * L);
+            const Entry2 Ly = a.layers[l];
+            const uint32_t tag = (uint32_t)(it + 1);
+            const int lp = l == 0 ? L - 1 : l - 1;
+            const int64_t rec = it * B;
+            const uint64_t *hx_prev = a.hx + (int64_t)lp * B * D;
+            uint64_t *gxl = a.gx + (int64_t)l * B * E;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's direct-to-LDS copies are in
+            __syncthreads();
+            // ---- residual in, norm, quantizer
+            {
+                const bool fold = l == 0 && t > 0;   // the previous token's stack output through the final RMSNorm
+                f2_prologue<NB, KCH>(a, hx_prev, D, tag - 1, wr, fold ? a.final_w : nullptr,
+                                     fold ? a.y + (int64_t)(t - 1) * B * D : nullptr, sq, spl, sqsum, ssc, red, ired, nullptr,
+                                     wg == 0, fold ? &r0s : nullptr, T.h_in ? T.h_in + rec * D : nullptr,
+                                     T.in_u ? T.in_u + rec * D : nullptr, T.in_q ? T.in_q + rec * D : nullptr,
+                                     T.in_s ? T.in_s + rec : nullptr);
+                if (fold && wg == 0 && tid == 0) st_x(a.rx, tag2(fbits2(r0s), tag));
+            }
+            // LoRA-down t[j] = L_dn[j] . q (sdot4, factors in LDS)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                int part = 0;
+                for (int cc = cl1; cc < C16_1; cc += TPR1)
+                    part = sdot_chunk(*reinterpret_cast<const uint4 *>(ldn1 + (size_t)j1 * D + cc * 16),
+                                      *reinterpret_cast<const int4 *>(sq + b * D + cc * 16), part);
+                part = dpp_group_sum(part, TPR1);
+                if (cl1 == TPR1 - 1) {
+                    tv[b * 64 + j1] = dsc1 * ssc[b] * (float)part;
+                    if (wg == 0 && T.in_t) T.in_t[(rec + b) * a.Rin + j1] = part;
+                }
+            }
+            // packed-sign GEMV of the item's rows (chunk c1 of rows rg1 + NG1 * i), branch-free
+            {
+                const int G32 = D >> 5;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    uint4 pl[8];
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) pl[p] = *reinterpret_cast<const uint4 *>(spl + (b * 8 + p) * G32 + c1 * 4);
+                    int pos[F2_MAXI];
+#pragma unroll
+                    for (int i = 0; i < F2_MAXI; ++i) {
+                        if (NG1 * i >= R1t) break;
+                        const int r = min(rg1 + NG1 * i, R1t - 1);
+                        pos[i] = chunk_pos(*reinterpret_cast<const uint4 *>(sgn1 + (size_t)r * (D >> 3) + c1 * 16), pl);
+                    }
+#pragma unroll
+                    for (int i = 0; i < F2_MAXI; ++i) {
+                        if (NG1 * i >= R1t) break;
+                        pos[i] = dpp_group_sum(pos[i], CPR1);
+                    }
+#pragma unroll
+                    for (int i = 0; i < F2_MAXI; ++i) {
+                        if (NG1 * i >= R1t) break;
+                        const int r = rg1 + NG1 * i;
+                        if (c1 == CPR1 - 1 && r < R1t) accl[b * F2_ROWS + r] = 2 * pos[i] - sqsum[b];
+                    }
+                }
+            }
+            __syncthreads();
+            // epilogue, conv step, z / x / dt / B / C into LDS
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int r = tid + k * kBlock;
+                if (r >= R1t) continue;
+                RowRegs<NB> &R = rw[k];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int acc = accl[b * F2_ROWS + r];
+                    const float yv = ssc[b] * R.sc * (float)acc + R.us * up_dot2(R.up, a.Rin, tv + b * 64);
+                    if (T.in_acc && (r <= 2 * a.pr || bc_tap || r >= a.R1)) T.in_acc[(rec + b) * a.Ninp + R.m.n] = acc;
+                    if (r >= a.R1) continue;   // padding row
+                    const int ch = R.m.ch;
+                    if (ch >= 0) {
+                        const float pre = R.cb + R.cw.x * R.win[b][0] + R.cw.y * R.win[b][1] + R.cw.z * R.win[b][2] + R.cw.w * yv;
+                        const float act = silu_f(pre);
+                        float *wdst = ch < E ? Ly.st.conv + ((int64_t)b * a.Cd + ch) * (kConvTaps - 1)
+                                             : a.bcp + ((((int64_t)wg * L + l) * B + b) * nbc + (ch - E)) * 3;
+                        wdst[0] = R.win[b][1];
+                        wdst[1] = R.win[b][2];
+                        wdst[2] = yv;
+                        if (ch < E) xl[b * P + (r - a.pr)] = act;
+                        else if (r < 2 * a.pr + 1 + N) Bl[b * N + (r - 2 * a.pr - 1)] = act;
+                        else Cl[b * N + (r - 2 * a.pr - 1 - N)] = act;
+                    } else if (r < a.pr) {
+                        zl[b * P + r] = yv;
+                    } else {
+                        dtl[b] = softplus_f(yv + dtb);
+                    }
+                }
+            }
+            __syncthreads();
+            // SSM update + readout, gate, publish g
+#pragma unroll
+            for (int i = 0; i < F2_FPT; ++i) {
+                if (i >= a.fpt) break;
+                const int f = tid + kBlock * i;
+                const bool ok = f < nf;
+                const int p = ok ? f / N4 : 0, n4 = ok ? f - p * N4 : 0;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const float dt = dtl[b];
+                    const float dA = expf(dt * Ah);
+                    const float x = xl[b * P + p];
+                    const float dtx = dt * x;
+                    const float4 Bn = *reinterpret_cast<const float4 *>(Bl + b * N + n4 * 4);
+                    const float4 Cn = *reinterpret_cast<const float4 *>(Cl + b * N + n4 * 4);
+                    float4 v = st[i][b];
+                    v.x = dA * v.x + dtx * Bn.x;
+                    v.y = dA * v.y + dtx * Bn.y;
+                    v.z = dA * v.z + dtx * Bn.z;
+                    v.w = dA * v.w + dtx * Bn.w;
+                    if (ok) reinterpret_cast<float4 *>(Ly.st.ssm + (((int64_t)b * a.H + h) * P + p0 + p) * N)[n4] = v;
+                    float part = ok ? (v.x * Cn.x + v.y * Cn.y) + (v.z * Cn.z + v.w * Cn.w) : 0.f;
+                    part = dpp_group_sum_f(part, N4);
+                    if (ok && n4 == N4 - 1) {
+                        const float gv = (part + Dh * x) * silu_f(zl[b * P + p]);
+                        st_x(gxl + (int64_t)b * E + h * P + p0 + p, tag2(fbits2(gv), tag));
+                    }
+                }
+            }
+            // ---- the next layer's weights and state, while the other role works on this one
+            if (it + 1 < n_tok) {
+                __syncthreads();   // every wave is done with this layer's LDS
+                const int64_t nx = it + 1;
+                const int tn = (int)(nx / L);
+                prefetch(tn, (int)(nx - (int64_t)tn * L));
+            }
+        }
+        // the stack's final RMSNorm of the last token, and the B/C conv windows back to the caller's state
+        if (wg == 0) {
+            const uint32_t tag = (uint32_t)n_tok;
+            const uint64_t *hl = a.hx + (int64_t)(L - 1) * B * D;
+            float *yt = a.y + (int64_t)(a.n_steps - 1) * B * D;
+            float *xs = reinterpret_cast<float *>(wreg);
+            for (int b = 0; b < B; ++b) {
+                float ss = 0.f;
+                for (int e = tid; e < D; e += kBlock) {
+                    uint64_t w = ld_x(hl + (int64_t)b * D + e);
+                    unsigned spins = 0;
+                    while ((uint32_t)(w >> 32) != tag && spins <= kSpin2) {
+                        __builtin_amdgcn_s_sleep(kSleep2);
+                        if (++spins > kSpin2) f2_error(a);
+                        w = ld_x(hl + (int64_t)b * D + e);
+                    }
+                    const float v = bitsf2((uint32_t)w);
+                    xs[e] = v;
+                    ss += v * v;
+                }
+                const float tot = block_sum(ss, red);
+                const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
+                for (int e = tid; e < D; e += kBlock) yt[(int64_t)b * D + e] = (xs[e] * r) * a.final_w[e];
+                __syncthreads();
+            }
+            for (int l = 0; l < L; ++l) {
+                const Entry2 Ly = a.layers[l];
+                for (int k = tid; k < B * nbc; k += kBlock) {
+                    const int b = k / nbc, j = k - b * nbc;
+                    const float *src = a.bcp + ((((int64_t)0 * L + l) * B + b) * nbc + j) * 3;
+                    float *dst = Ly.st.conv + ((int64_t)b * a.Cd + E + j) * (kConvTaps - 1);
+                    dst[0] = src[0];
+                    dst[1] = src[1];
+                    dst[2] = src[2];
+                }
+            }
+        }
+        return;
+    }
+    // ========================================================================== role 2
+    const int w2 = wg - a.n1, n_out0 = w2 * a.R2;
+    const int R2t = max(0, min(a.R2, D - n_out0));
+    const int CPR2 = E >> 7, NG2 = kBlock / CPR2, c2 = tid % CPR2, rg2 = tid / CPR2;
+    const int TPR2 = kBlock / a.Rout, j2 = tid / TPR2, cl2 = tid % TPR2, C16_2 = E >> 4;
+    const bool tap2 = w2 == 0;
+    char *sgn2 = wreg;
+    char *ldn2 = wreg + f2_round_kb((size_t)a.R2 * (E >> 3));
+    const int on = n_out0 + tid;
+    const bool orow = tid < R2t;
+    float dsc2 = 0.f, osc = 0.f, ous = 0.f;
+    int4 oup[F2_UPC];
+    float4 wr[KCH];
+    auto prefetch = [&](int l) {
+        const Entry2 Ly = a.layers[l];
+        const dfssm_proj &pout = Ly.w.out_proj;
+        if (R2t > 0)
+            lds_copy_contig(sgn2, reinterpret_cast<const char *>(pout.sign + (int64_t)n_out0 * (E >> 3)), R2t * CPR2);
+        lds_copy_contig(ldn2, reinterpret_cast<const char *>(pout.lora_dn), a.Rout * C16_2);
+        dsc2 = pout.lora_dn_scale[j2];
+        load_norm_w<KCH>(wr, Ly.w.gnorm_w, E);
+        if (orow) {
+            osc = half_bits_to_float(pout.row_scale[on]);
+            ous = pout.lora_up_scale[on];
+            load_up(oup, pout.lora_up, a.Rout, on);
+        }
+    };
+    // this workgroup's rows of the residual stream (the token input x0 to begin with)
+    float hold[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) hold[b] = orow ? a.x0[(int64_t)b * D + on] : 0.f;
+    const float fw = orow ? a.final_w[on] : 0.f;
+    prefetch(0);
+    for (int64_t it = 0; it < n_tok; ++it) {
+        const int t = (int)(it / L), l = (int)(it - (int64_t)t * L);
+        const uint32_t tag = (uint32_t)(it + 1);
+        const int64_t rec = it * B;
+        const uint64_t *gxl = a.gx + (int64_t)l * B * E;
+        uint64_t *hxl = a.hx + (int64_t)l * B * D;
+        if (l == 0 && t > 0) {
+            // the residual input of layer 0 is the previous token's output through the final RMSNorm,
+            // whose factor role-1 workgroup 0 publishes (the product is the one the prologue forms)
+            uint64_t w = ld_x(a.rx);
+            unsigned spins = 0;
+            while ((uint32_t)(w >> 32) != tag && spins <= kSpin2) {
+                __builtin_amdgcn_s_sleep(kSleep2);
+                if (++spins > kSpin2) f2_error(a);
+                w = ld_x(a.rx);
+            }
+            const float r0 = bitsf2((uint32_t)w);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) hold[b] = (hold[b] * r0) * fw;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's direct-to-LDS copies are in
+        __syncthreads();
+        f2_prologue<NB, KCH>(a, gxl, E, tag, wr, nullptr, nullptr, sq, spl, sqsum, ssc, red, ired, nullptr, tap2, nullptr,
+                             nullptr, T.out_u ? T.out_u + rec * E : nullptr, T.out_q ? T.out_q + rec * E : nullptr,
+                             T.out_s ? T.out_s + rec : nullptr);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            int part = 0;
+            for (int cc = cl2; cc < C16_2; cc += TPR2)
+                part = sdot_chunk(*reinterpret_cast<const uint4 *>(ldn2 + (size_t)j2 * E + cc * 16),
+                                  *reinterpret_cast<const int4 *>(sq + b * E + cc * 16), part);
+            part = dpp_group_sum(part, TPR2);
+            if (cl2 == TPR2 - 1) {
+                tv[b * 64 + j2] = dsc2 * ssc[b] * (float)part;
+                if (tap2 && T.out_t) T.out_t[(rec + b) * a.Rout + j2] = part;
+            }
+        }
+        {
+            const int G32 = E >> 5;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                uint4 pl[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) pl[p] = *reinterpret_cast<const uint4 *>(spl + (b * 8 + p) * G32 + c2 * 4);
+#pragma unroll
+                for (int i = 0; i < F2_MAXO; ++i) {
+                    if (NG2 * i >= a.R2) break;
+                    const int r = rg2 + NG2 * i;
+                    const uint4 bits = *reinterpret_cast<const uint4 *>(sgn2 + (size_t)min(r, max(R2t - 1, 0)) * (E >> 3) + c2 * 16);
+                    int pos = chunk_pos(bits, pl);
+                    pos = dpp_group_sum(pos, CPR2);
+                    if (c2 == CPR2 - 1 && r < R2t) accl[b * F2_ROWS + r] = 2 * pos - sqsum[b];
+                }
+            }
+        }
+        __syncthreads();
+        if (orow) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int acc = accl[b * F2_ROWS + tid];
+                const float yv = ssc[b] * osc * (float)acc + ous * up_dot2(oup, a.Rout, tv + b * 64);
+                if (T.out_acc) T.out_acc[(rec + b) * D + on] = acc;
+                hold[b] = hold[b] + yv;
+                st_x(hxl + (int64_t)b * D + on, tag2(fbits2(hold[b]), tag));
+            }
+        }
+        if (it + 1 < n_tok) {
+            __syncthreads();   // every wave is done with this layer's LDS
+            const int64_t nx = it + 1;
+            prefetch((int)(nx - (nx / L) * L));
+        }
+    }
+}
+
+__global__ void k_store2(Entry2 *dst, Chunk2 c, int n) {
+    if ((int)threadIdx.x < n) dst[threadIdx.x] = c.e[threadIdx.x];
+}
+
+__global__ void k_zero2(uint64_t *p, int64_t n, int *err, uint64_t *rx) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *err = 0;
+        *rx = 0;
+    }
+}
+
+__global__ void k_seed2(uint64_t *hx_last, const float *x0, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        hx_last[i] = (uint64_t)__builtin_bit_cast(uint32_t, x0[i]);
+}
+
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+size_t f2_lds_base(const Shape &s, int nb) {
+    const int kmax = s.D > s.E ? s.D : s.E;
+    return (size_t)2 * nb * kmax + (size_t)nb * F2_ROWS * 4 + (size_t)nb * 64 * 4 + (size_t)nb * 2 * (s.P + s.N) * 4;
+}
+size_t f2_round_kb_host(size_t v) { return (v + 1023) & ~(size_t)1023; }
+// weight region: max over the two phases of (sign rows + LoRA-down factors), each whole KB
+// (also the last token's residual, D floats, for the stack's final RMSNorm)
+size_t f2_wreg_bytes(const Shape &s, int R1max, int R2) {
+    const size_t p1 = f2_round_kb_host((size_t)R1max * (s.D >> 3)) + f2_round_kb_host((size_t)s.Rin * s.D);
+    const size_t p2 = f2_round_kb_host((size_t)R2 * (s.E >> 3)) + f2_round_kb_host((size_t)s.Rout * s.E);
+    const size_t m = p1 > p2 ? p1 : p2;
+    return m > (size_t)s.D * 4 ? m : (size_t)s.D * 4;
+}
+
+// Slices per head (a power of two dividing headdim) for `slots` workgroups, 0 if unsupported.
+int f2_slices(const Shape &s, int slots) {
+    if (slots < s.H) return 0;
+    int S = 1;
+    while (S * 2 <= s.P && s.H * S * 2 <= slots && s.P % (S * 2) == 0) S *= 2;
+    return S;
+}
+
+struct F2Plan {
+    int S, pr, R1, npad, R2, fpt, n1, n2;
+};
+
+bool f2_plan(const Shape &s, int batch, int slots, F2Plan &p) {
+    if (batch != 1) return false;
+    if (!pow2(s.D) || !pow2(s.E) || s.D < 256 || s.E < 256 || s.D > 8192 || s.E > 8192) return false;
+    if (!pow2(s.Rin) || !pow2(s.Rout) || s.Rin < 8 || s.Rout < 8 || s.Rin > 16 * F2_UPC || s.Rout > 16 * F2_UPC) return false;
+    if (s.N % 4 || s.N / 4 > 64 || !pow2(s.N / 4)) return false;
+    // half the resident workgroups (at most) for the SSM items, the rest for out_proj row blocks
+    p.S = f2_slices(s, slots / 2);
+    if (p.S == 0) return false;
+    p.n1 = s.H * p.S;
+    p.pr = s.P / p.S;
+    p.R1 = 2 * p.pr + 1 + 2 * s.N;
+    p.npad = s.Ninp - s.Nin;
+    if (p.R1 + p.npad > F2_ROWS || p.R1 + p.npad > (kBlock / (s.D >> 7)) * F2_MAXI || p.R1 + p.npad > 2 * kBlock)
+        return false;
+    if ((p.R1 + p.npad) * (s.D >> 7) > F2_SBLK * kWaves * 64) return false;
+    const int avail = slots - p.n1;
+    if (avail < 1) return false;
+    p.R2 = (s.D + avail - 1) / avail;
+    p.n2 = (s.D + p.R2 - 1) / p.R2;
+    if (p.R2 > kBlock || p.R2 > (kBlock / (s.E >> 7)) * F2_MAXO) return false;
+    const int nf = p.pr * (s.N / 4);
+    p.fpt = (nf + kBlock - 1) / kBlock;
+    if (p.fpt > F2_FPT) return false;
+    return f2_lds_base(s, batch) + f2_wreg_bytes(s, p.R1 + p.npad, p.R2) <= kF2MaxLds;
+}
+
+template <int NB, int KCH>
+hipError_t f2_launch(F2Args &a, const Shape &s, hipStream_t stream) {
+    const size_t lds = f2_lds_base(s, NB) + f2_wreg_bytes(s, a.R1 + a.npad, a.R2);
+    void *args[] = {&a};
+    // DFSSM_STACK_LAUNCH=plain: the same grid through the ordinary launch API, for profilers that
+    // cannot trace cooperative launches (the grid never exceeds what is resident at once, and every
+    // wait is bounded)
+    const char *mode = getenv("DFSSM_STACK_LAUNCH");
+    if (mode && strcmp(mode, "plain") == 0)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&k_flow2<NB, KCH>), dim3(a.n1 + a.n2), dim3(kBlock), args, lds,
+                               stream);
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_flow2<NB, KCH>), dim3(a.n1 + a.n2), dim3(kBlock),
+                                      args, lds, stream);
+}
+
+template <int NB, int KCH>
+int f2_resident() {
+    static std::atomic<int> memo[kMaxDevices2];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices2) return 0;
+    int v = memo[dev].load(std::memory_order_relaxed);
+    if (v != 0) return v;
+    int ncu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    // with the largest LDS a supported shape may use (registers bound the occupancy to one per CU anyway)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_flow2<NB, KCH>), kBlock,
+                                                     kF2MaxLds) != hipSuccess)
+        return 0;
+    v = per_cu * ncu;
+    memo[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <int NB>
+int f2_resident_nb(int kmax) {
+    if (kmax <= 1024) return f2_resident<NB, 1>();
+    if (kmax <= 2048) return f2_resident<NB, 2>();
+    if (kmax <= 4096) return f2_resident<NB, 4>();
+    return f2_resident<NB, 8>();
+}
+
+int f2_slots(const Shape &s, int batch) {
+    const int kmax = s.D > s.E ? s.D : s.E;
+    return batch == 1 ? f2_resident_nb<1>(kmax) : 0;
+}
+
+template <int NB>
+hipError_t f2_launch_nb(F2Args &a, const Shape &s, hipStream_t stream) {
+    const int kmax = s.D > s.E ? s.D : s.E;
+    if (kmax <= 1024) return f2_launch<NB, 1>(a, s, stream);
+    if (kmax <= 2048) return f2_launch<NB, 2>(a, s, stream);
+    if (kmax <= 4096) return f2_launch<NB, 4>(a, s, stream);
+    return f2_launch<NB, 8>(a, s, stream);
+}
+
+}  // namespace
+
+bool stack2_ok(const Shape &s, int batch) {
+    const char *v = getenv("DFSSM_STACK_V1");
+    if (v && strcmp(v, "1") == 0) return false;
+    F2Plan p{};
+    return f2_plan(s, batch, f2_slots(s, batch), p);
+}
+
+size_t stack2_extra_ws_bytes(const Shape &s, int batch, int n_layers) {
+    F2Plan p{};
+    if (!f2_plan(s, batch, f2_slots(s, batch), p)) return 0;
+    const size_t L = n_layers;
+    return align_up(L * sizeof(Entry2), 256) + 256 + align_up(L * batch * (size_t)(s.D + s.E) * 8, 256) +
+           align_up((size_t)p.n1 * L * batch * 2 * s.G * s.N * 3 * 4, 256);
+}
+
+hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states, int n_layers,
+                         const float *final_w, const float *x0, float *y, int batch, int n_steps, void *extra,
+                         const dfssm_taps *taps, hipStream_t stream) {
+    F2Plan p{};
+    if (!f2_plan(s, batch, f2_slots(s, batch), p)) return hipErrorInvalidConfiguration;
+    char *q = static_cast<char *>(extra);
+    const size_t L = n_layers;
+    Entry2 *table = reinterpret_cast<Entry2 *>(q);
+    q += align_up(L * sizeof(Entry2), 256);
+    int *err = reinterpret_cast<int *>(q);
+    q += 256;
+    uint64_t *words = reinterpret_cast<uint64_t *>(q);
+    const int64_t nwords = (int64_t)L * batch * (s.D + s.E);
+    q += align_up((size_t)nwords * 8, 256);
+    F2Args a{};
+    a.n_layers = n_layers;
+    a.n_steps = n_steps;
+    a.batch = batch;
+    a.D = s.D;
+    a.E = s.E;
+    a.N = s.N;
+    a.P = s.P;
+    a.H = s.H;
+    a.G = s.G;
+    a.Cd = s.Cd;
+    a.Nin = s.Nin;
+    a.Ninp = s.Ninp;
+    a.Rin = s.Rin;
+    a.Rout = s.Rout;
+    a.eps = s.eps;
+    a.S = p.S;
+    a.pr = p.pr;
+    a.R1 = p.R1;
+    a.npad = p.npad;
+    a.R2 = p.R2;
+    a.fpt = p.fpt;
+    a.n1 = p.n1;
+    a.n2 = p.n2;
+    a.layers = table;
+    a.final_w = final_w;
+    a.x0 = x0;
+    a.rx = reinterpret_cast<uint64_t *>(err) + 8;
+    a.y = y;
+    a.hx = words;
+    a.gx = words + L * batch * s.D;
+    a.bcp = reinterpret_cast<float *>(q);
+    a.err = err;
+    if (taps) a.taps = *taps;
+    hipError_t e;
+    for (int l0 = 0; l0 < n_layers; l0 += kTable2) {
+        Chunk2 c{};
+        const int n = min(kTable2, n_layers - l0);
+        for (int i = 0; i < n; ++i) c.e[i] = Entry2{layers[l0 + i], states[l0 + i]};
+        k_store2<<<1, 64, 0, stream>>>(table + l0, c, n);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    k_zero2<<<256, 256, 0, stream>>>(words, nwords, err, a.rx);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_seed2<<<64, 256, 0, stream>>>(a.hx + (int64_t)(L - 1) * batch * s.D, x0, (int64_t)batch * s.D);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return f2_launch_nb<1>(a, s, stream);
+}
+
+}  // namespace dfssm

@@ -76,6 +76,8 @@ struct FlowArgs {
 };
 
 __device__ __forceinline__ uint64_t tagged(uint32_t bits, uint32_t tag) { return ((uint64_t)tag << 32) | bits; }
+// Words per (layer, token) slot, rounded up to even so that every slot starts 16-byte aligned.
+__host__ __device__ __forceinline__ int64_t slot_words(int64_t n) { return (n + 1) & ~(int64_t)1; }
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bitsf(uint32_t b) { return __builtin_bit_cast(float, b); }
 
@@ -132,7 +134,9 @@ __device__ __forceinline__ void publish(uint64_t *f, uint32_t tag) {
     if (threadIdx.x == 0) st_x(f, (uint64_t)tag);
 }
 
-// Prologue input: flagged tagged words of epoch `tag` (all of a thread's words requested first).
+// Prologue input: tagged words of epoch `tag` whose producers have flagged them. A thread owns
+// 4*KCH consecutive inputs (prologue_elem); it loads all of its words at once and reloads them
+// until every epoch matches (bounded).
 template <int KCH>
 struct TaggedSource {
     const FlowArgs *a;
@@ -140,45 +144,28 @@ struct TaggedSource {
     int64_t stride;
     uint32_t tag;
     __device__ __forceinline__ void load(int b, int K, float4 *hv) const {
-        uint64_t w[KCH][4];
-        const uint64_t *xb = X + (int64_t)b * stride;
+        const int e0 = prologue_elem<KCH>(0);
+        if (e0 >= K) return;   // K is a multiple of 4*KCH: a thread has all of its chunks or none
+        const uint64_t *p = X + (int64_t)b * stride + e0;
+        u32x4 r[2 * KCH];
+        unsigned spins = 0;
+        for (;;) {
+            load_words_sc1<KCH>(p, r);
+            bool ok = true;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int e = (i * kBlock + (int)threadIdx.x) * 4;
-            if (e < K) {
-                const ulonglong2 v0 = *reinterpret_cast<const ulonglong2 *>(xb + e);
-                const ulonglong2 v1 = *reinterpret_cast<const ulonglong2 *>(xb + e + 2);
-                w[i][0] = v0.x;
-                w[i][1] = v0.y;
-                w[i][2] = v1.x;
-                w[i][3] = v1.y;
+            for (int j = 0; j < 2 * KCH; ++j) ok = ok && r[j].y == tag && r[j].w == tag;
+            if (ok) break;
+            __builtin_amdgcn_s_sleep(kPollSleep);
+            ++spins;
+            if ((spins & 15) == 0 && ld_x(a->err)) break;
+            if (spins > kSpinLimit) {
+                flag_error(*a);
+                break;
             }
         }
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int e = (i * kBlock + (int)threadIdx.x) * 4;
-            if (e < K) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if ((uint32_t)(w[i][c] >> 32) != tag) w[i][c] = poll_word(*a, xb + e + c, tag);
-                hv[i] = make_float4(bitsf((uint32_t)w[i][0]), bitsf((uint32_t)w[i][1]), bitsf((uint32_t)w[i][2]),
-                                    bitsf((uint32_t)w[i][3]));
-            }
-        }
-    }
-};
-
-// Plain fp32 input (the stack's x0), KCH chunks per thread.
-template <int KCH>
-struct InputSource {
-    const float *X;
-    int64_t stride;
-    __device__ __forceinline__ void load(int b, int K, float4 *hv) const {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int e = (i * kBlock + (int)threadIdx.x) * 4;
-            if (e < K) hv[i] = *reinterpret_cast<const float4 *>(X + (int64_t)b * stride + e);
-        }
+        for (int i = 0; i < KCH; ++i)
+            hv[i] = make_float4(bitsf(r[2 * i].x), bitsf(r[2 * i].z), bitsf(r[2 * i + 1].x), bitsf(r[2 * i + 1].z));
     }
 };
 
@@ -198,6 +185,12 @@ struct TaggedSink {
 
 __global__ void k_store_layers(LayerEntry *dst, LayerChunk c, int n) {
     if ((int)threadIdx.x < n) dst[threadIdx.x] = c.e[threadIdx.x];
+}
+
+// x0 [batch][D] into the last layer's residual slot as epoch-0 words (the flags are all zero).
+__global__ void k_seed_x0(uint64_t *xe_last, const float *x0, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        xe_last[i] = (uint64_t)__builtin_bit_cast(uint32_t, x0[i]);
 }
 
 __global__ void k_zero_words(uint64_t *p, int64_t n, int *err) {
@@ -279,7 +272,7 @@ __device__ void ssm_item(const FlowArgs &a, const LayerEntry &L, int l, int it, 
     const int total = 2 * rpw + 2 * N + 1;
     const int n4 = N >> 2;
     const int nch = rpw * n4;
-    const int64_t sa = a.Ninp + a.Rin + 1;
+    const int64_t sa = slot_words(a.Ninp + a.Rin + 1);
     const uint64_t *xa = a.xa + ((int64_t)l * a.batch + b) * sa;
     // ---- loads that do not depend on this layer's activations
     float4 S[2];
@@ -437,7 +430,7 @@ __global__ __launch_bounds__(kBlock, 3) void k_stack_flow(FlowArgs a) {
     const int nA = a.in_row_items + a.in_lora_items;
     const int nDi = a.out_row_items + a.out_lora_items;
     const int64_t BD = (int64_t)a.batch * a.D;
-    const int64_t sa = a.Ninp + a.Rin + 1, sd = a.D + a.Rout + 1;
+    const int64_t sa = slot_words(a.Ninp + a.Rin + 1), sd = slot_words(a.D + a.Rout + 1);
     const int rpi = a.in_rows_per_item, last = a.in_row_items - 1;
     const dfssm_taps &T = a.taps;
     for (int t = 0; t < a.n_steps; ++t) {
@@ -470,19 +463,17 @@ __global__ __launch_bounds__(kBlock, 3) void k_stack_flow(FlowArgs a) {
                 GemvPre pf{};
                 if (wg < a.in_row_items)
                     gemv_prefetch(pf, q.sign, a.D, wg * rpi, wg == last ? a.Ninp : min((wg + 1) * rpi, a.Nin));
-                if (l == 0 && t == 0) {
-                    const InputSource<KCH> src{a.x0, a.D};
-                    norm_quant_prologue<NB, KCH>(q, src, sq, spl, sqsum, ssc, red, ired, xsave);
-                } else {
-                    if (l == 0) {
-                        q.pre_w = a.final_w;
-                        q.pre_out = a.y + (int64_t)(t - 1) * BD;
-                    }
-                    if (tid < a.res_items) wait_flag(a, a.fe + (int64_t)lp * a.res_items + tid, tag - 1);
-                    __syncthreads();
-                    const TaggedSource<KCH> src{&a, xe_prev, a.D, tag - 1};
-                    norm_quant_prologue<NB, KCH>(q, src, sq, spl, sqsum, ssc, red, ired, l == 0 ? xsave : nullptr);
+                // the token input x0 sits in the last layer's residual slot with epoch 0 (seeded
+                // before the launch); later tokens take the previous token's stack output through the
+                // final RMSNorm, folded in here
+                if (l == 0 && t > 0) {
+                    q.pre_w = a.final_w;
+                    q.pre_out = a.y + (int64_t)(t - 1) * BD;
                 }
+                if (tid < a.res_items) wait_flag(a, a.fe + (int64_t)lp * a.res_items + tid, tag - 1);
+                __syncthreads();
+                const TaggedSource<KCH> src{&a, xe_prev, a.D, tag - 1};
+                norm_quant_prologue<NB, KCH>(q, src, sq, spl, sqsum, ssc, red, ired, l == 0 ? xsave : nullptr);
                 if (wg == 0 && tid < NB) st_x(xa + tid * sa + a.Ninp + a.Rin, tagged(fbits(ssc[tid]), tag));
                 const TaggedSink sink{xa, sa, a.Ninp, tag};
                 for (int it = wg; it < nA; it += nwg) {
@@ -687,7 +678,8 @@ hipError_t launch_flow_nb(FlowArgs &a, const Shape &s, int max_wgs, hipStream_t 
 
 // Upper bounds of the per-layer word and flag counts (item counts at the finest item size).
 size_t words_per_layer(const Shape &s, int batch) {
-    return (size_t)batch * ((size_t)(s.Ninp + s.Rin + 1) + s.E + (s.D + s.Rout + 1) + s.D + 2 * s.G * s.N);
+    return (size_t)batch *
+           ((size_t)slot_words(s.Ninp + s.Rin + 1) + s.E + slot_words(s.D + s.Rout + 1) + s.D + 2 * s.G * s.N);
 }
 size_t flags_per_layer(const Shape &s, int batch) {
     const int in_pass = kWaves * (64 / gemv_lanes_per_row(s.D));
@@ -742,9 +734,9 @@ hipError_t launch_stack_persistent(const Shape &s, const dfssm_layer_weights *la
     a.y = y;
     const int64_t L = n_layers;
     a.xa = words;
-    a.xb = a.xa + L * batch * (s.Ninp + s.Rin + 1);
+    a.xb = a.xa + L * batch * slot_words(s.Ninp + s.Rin + 1);
     a.xd = a.xb + L * batch * s.E;
-    a.xe = a.xd + L * batch * (s.D + s.Rout + 1);
+    a.xe = a.xd + L * batch * slot_words(s.D + s.Rout + 1);
     a.bc = a.xe + L * batch * s.D;
     uint64_t *flags = a.bc + L * batch * 2 * s.G * s.N;
     a.fa = flags;                 // the other flag regions follow once the item counts are planned
@@ -759,6 +751,8 @@ hipError_t launch_stack_persistent(const Shape &s, const dfssm_layer_weights *la
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     k_zero_words<<<256, 256, 0, stream>>>(words, nwords, err);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_seed_x0<<<64, 256, 0, stream>>>(a.xe + (L - 1) * batch * s.D, x0, (int64_t)batch * s.D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (batch) {
         case 1: return launch_flow_nb<1>(a, s, max_wgs, stream);

@@ -193,13 +193,15 @@ def run_stack(dims, layers, x0, states0, n_steps, taps=False, final_w=None):
             None if tp is None else tp.numpy())
 
 
-def test_stack_decode_tiny_forced_and_free_running():
-    nL, T, B = 3, 12, 2
+@pytest.mark.parametrize("B", [1, 2])
+def test_stack_decode_tiny_forced_and_free_running(B):
+    """Batch 1 runs the two-exchange persistent kernel, batch 2 the per-item dataflow kernel."""
+    nL, T = 3, 12
     layers = gen.stack_weights(TINY, nL, seed=1, random_norms=True)
     states0 = [gen.initial_states(TINY, B, l, 1, std=0.1) for l in range(nL)]
     x0 = gen.token_inputs(TINY, (B,), 1, tag=9)
     fw = np.random.default_rng(0).uniform(0.5, 1.5, TINY.d_model).astype(np.float32)
-    say("case: tiny stack decode, 3 layers, 12 steps, batch 2, with taps")
+    say(f"case: tiny stack decode, 3 layers, 12 steps, batch {B}, with taps")
     y, states, taps = run_stack(TINY, layers, x0, states0, T, taps=True, final_w=fw)
     dense = [O.dense_signs(lw) for lw in layers]
     for b in range(B):
@@ -345,3 +347,41 @@ def test_stack_decode_grid_size_invariance():
                 assert (st[l][0] == st_ref[l][0]).all() and (st[l][1] == st_ref[l][1]).all(), (g, l)
     finally:
         os.environ.pop("DFSSM_STACK_MAX_WGS", None)
+
+
+@pytest.mark.parametrize("dims_name", ["tiny", "1p3b"])
+def test_stack_decode_batch1_kernels_agree(dims_name):
+    """The two persistent kernels (two-exchange, the default at batch 1, and the per-item dataflow
+    one, DFSSM_STACK_V1=1) compute the same decode: identical codes except at rounding ties."""
+    import os
+    dims = gen.DIMS[dims_name]
+    nL, T = (3, 8) if dims_name == "tiny" else (4, 4)
+    layers = gen.stack_weights(dims, nL, seed=3, random_norms=True, per_channel_lora=True)
+    states0 = [gen.initial_states(dims, 1, l, 3, std=0.1) for l in range(nL)]
+    x0 = gen.token_inputs(dims, (1,), 3, tag=4)
+    say(f"case: {dims_name} stack, {nL} layers, {T} steps, batch 1, two-exchange kernel")
+    y2, st2, tp2 = run_stack(dims, layers, x0, states0, T, taps=True)
+    try:
+        os.environ["DFSSM_STACK_V1"] = "1"
+        say(f"case: same stack, per-item dataflow kernel")
+        y1, st1, tp1 = run_stack(dims, layers, x0, states0, T, taps=True)
+    finally:
+        os.environ.pop("DFSSM_STACK_V1", None)
+    assert np.isfinite(y2).all()
+    flips = 0
+    for r in range(T * nL):
+        for k in ("in", "out"):
+            f, ok = PY.flips_at_ties(tp1[k + "_u"][r], tp1[k + "_q"][r], tp2[k + "_q"][r])
+            assert ok, (r, k)
+            flips += f
+        if flips:
+            break
+        PY.assert_codes_exact(tp2["in_u"][r], tp2["in_q"][r], tp2["in_s"][r][0], f"record {r} in")
+        PY.assert_codes_exact(tp2["out_u"][r], tp2["out_q"][r], tp2["out_s"][r][0], f"record {r} out")
+    errs = [PY.normwise(y2[t][0], y1[t][0]) for t in range(T)]
+    say(f"{dims_name}: max normwise difference {max(errs):.2e}, code flips {flips}")
+    if flips == 0:
+        assert max(errs) < PY.TOL_LAYER
+        for l in range(nL):
+            assert PY.normwise(st2[l][0], st1[l][0]) < PY.TOL_LAYER
+            assert PY.normwise(st2[l][1], st1[l][1]) < PY.TOL_LAYER
