@@ -4,14 +4,14 @@
 // One cooperative launch runs every step of every layer. The workgroups have two roles:
 //   role 1, item w < n1: head h = w / S, channels [p0, p0 + pr) of that head (pr = P / S):
 //            gather the residual h (all D values), RMSNorm + int8 quantizer, LoRA-down t, the
-//            packed-sign GEMV of exactly the in_proj rows this item consumes (its z and x channels,
-//            its head's dt row, and the group's B and C rows, which every item computes itself
-//            instead of exchanging them), rescale + LoRA-up epilogue, conv step, SSM update +
-//            readout, SiLU(z) gate -> publish this item's gated outputs g
+//            packed-sign GEMV of its share (q rows) of the B and C rows -> rescale + LoRA-up, conv
+//            step, publish them at once; then the rows only it consumes (its z and x channels, its
+//            head's dt row) while those travel; gather its group's B and C, SSM update + readout,
+//            SiLU(z) gate -> publish this item's gated outputs g
 //   role 2, item w >= n1: out_proj rows [(w - n1) * R2, ...): gather g (all E values), gated
 //            RMSNorm + quantizer, LoRA-down, GEMV of its rows, epilogue, residual add -> publish
 //            those rows of h (it keeps them: they are its next residual input)
-// Each exchange is an all-gather of tagged 64-bit words {payload, epoch}, written with
+// Each exchange (h, B/C, g) is an all-gather of tagged 64-bit words {payload, epoch}, written with
 // agent-coherent stores and read with 16-byte agent-coherent loads until every epoch matches;
 // there are no flags and no barriers. Every layer has its own word slots, rewritten one token
 // later; every workgroup reads all of a layer's words before anything of the next token's same
@@ -22,9 +22,6 @@
 // LDS, scales, conv taps and windows, SSM state into registers): that latency hides behind the
 // other role's work. Every wait is bounded: on a timeout the kernel flags the workspace, stops
 // waiting and poisons y with NaN, so every wave still reaches the end.
-//
-// The B and C conv windows are per-workgroup copies in the workspace (each role-1 workgroup
-// computes those channels itself); workgroup 0 writes its copy back to the caller's conv state.
 #include <stdlib.h>
 #include <string.h>
 
@@ -36,8 +33,8 @@ namespace dfssm {
 
 namespace {
 
-constexpr int F2_MAXI = 21;   // in_proj rows per GEMV thread: rows rg + NG * i
-constexpr int F2_SBLK = 21;   // 1 KB blocks of in_proj sign rows each wave copies per layer
+constexpr int F2_MAXI = 12;   // in_proj rows per GEMV thread (after the B/C rows): rows rg + NG * i
+constexpr int F2_SBLK = 8;    // 1 KB blocks of in_proj sign rows each wave copies per layer
 constexpr int F2_UPC = 2;     // LoRA-up chunks (16 B) per row: rank <= 32
 constexpr int F2_MAXO = 4;    // out_proj sign chunks per thread
 constexpr int F2_FPT = 4;     // SSM state float4s per thread and token
@@ -60,13 +57,13 @@ struct F2Args {
     int n_layers, n_steps, batch;
     int D, E, N, P, H, G, Cd, Nin, Ninp, Rin, Rout;
     float eps;
-    int S, pr, R1, npad, R2, fpt, n1, n2;
+    int S, pr, q, R1, npad, R2, fpt, n1, n2;
     const Entry2 *layers;
     const float *final_w, *x0;
     float *y;
     uint64_t *hx, *gx;  // [L][batch][D], [L][batch][E] tagged words
     uint64_t *rx;       // the stack's final RMSNorm factor of the previous token (tagged)
-    float *bcp;         // [nwg][L][batch][2GN][3] private B/C conv windows
+    uint64_t *bcx;      // [L][batch][2GN] tagged words: the conv'd B and C of every group
     int *err;
     dfssm_taps taps;
 };
@@ -103,6 +100,20 @@ __device__ __forceinline__ void f2_gather(const F2Args &a, const uint64_t *p, ui
     }
 }
 
+__device__ __forceinline__ float f2_ss(const float4 &v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
+
+// The stack's final RMSNorm, (h * r) * w, of one gathered vector: the thread layout and the order of
+// the sum of squares are the prologue's, so that the last token's output is bit-identical to what
+// the next token's prologue would form from the same words.
+template <int KCH>
+__device__ __forceinline__ float f2_norm_factor(const F2Args &a, const float4 (&hv)[KCH], int K, float *red) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) ss += f2_ss(hv[i]);
+    const float tot = block_sum(ss, red);
+    return 1.0f / sqrtf(tot / (float)K + a.eps);
+}
+
 // Gather NB vectors of K tagged words, RMSNorm (after the stack's final RMSNorm when pre_w is set),
 // int8 quantizer -> codes sq[b][K], bit-planes spl[b][8][K/32], sum of codes, scale; xs (optional)
 // keeps the normalised input. wr: this thread's norm weights. Taps are written by workgroup 0.
@@ -127,13 +138,9 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
             for (int i = 0; i < KCH; ++i) hv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) ss += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
         if (pre_w) {
-            const float tot0 = block_sum(ss, red);
-            const float r0 = 1.0f / sqrtf(tot0 / (float)K + a.eps);
+            const float r0 = f2_norm_factor<KCH>(a, hv, K, red);
             if (r0_out && tid == 0) *r0_out = r0;
-            ss = 0.f;
             if (mine) {
 #pragma unroll
                 for (int i = 0; i < KCH; ++i) {
@@ -143,11 +150,12 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
                     hv[i].y = (hv[i].y * r0) * w.y;
                     hv[i].z = (hv[i].z * r0) * w.z;
                     hv[i].w = (hv[i].w * r0) * w.w;
-                    ss += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
                     if (tapwg && pre_out) *reinterpret_cast<float4 *>(pre_out + (int64_t)b * K + e) = hv[i];
                 }
             }
         }
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) ss += f2_ss(hv[i]);
         float pm = 0.f;
         if (mine) {
 #pragma unroll
@@ -321,23 +329,24 @@ __device__ __forceinline__ void load_up(int4 (&w)[F2_UPC], const int8_t *lora_up
     }
 }
 
-// Which in_proj row / conv channel the r-th row of an item covers.
+// Which in_proj row / conv channel the r-th row of an item covers: first the item's share of the B
+// and C rows (all groups' B rows, then all groups' C rows, spread over the items), then its z
+// channels, its x channels, its head's dt row, and (workgroup 0, with taps) the padding rows.
 struct ItemRow {
-    int n, ch;  // in_proj row, conv channel (-1: z, dt or padding)
+    int n, ch;  // in_proj row, conv channel (-1: z, dt or padding row; -2: no row)
 };
-__device__ __forceinline__ ItemRow item_row(const F2Args &a, int r, int h, int p0, int g) {
-    const int pr = a.pr, N = a.N, E = a.E;
+__device__ __forceinline__ ItemRow item_row(const F2Args &a, int r, int h, int p0, int bc0) {
+    const int pr = a.pr, q = a.q, E = a.E;
     ItemRow m{0, -1};
-    if (r < pr) {
-        m.n = h * a.P + p0 + r;
-    } else if (r < 2 * pr) {
-        m.ch = h * a.P + p0 + (r - pr);
-    } else if (r == 2 * pr) {
+    if (r < q) {
+        const int bc = bc0 + r;
+        m.ch = bc < 2 * a.G * a.N ? E + bc : -2;
+    } else if (r < q + pr) {
+        m.n = h * a.P + p0 + (r - q);
+    } else if (r < q + 2 * pr) {
+        m.ch = h * a.P + p0 + (r - q - pr);
+    } else if (r == q + 2 * pr) {
         m.n = E + a.Cd + h;
-    } else if (r < 2 * pr + 1 + N) {
-        m.ch = E + g * N + (r - 2 * pr - 1);
-    } else if (r < a.R1) {
-        m.ch = E + a.G * N + g * N + (r - 2 * pr - 1 - N);
     } else {
         m.n = a.Nin + (r - a.R1);   // padding row (computed only for the taps)
     }
@@ -345,17 +354,55 @@ __device__ __forceinline__ ItemRow item_row(const F2Args &a, int r, int h, int p
     return m;
 }
 
-// Per-thread state of one epilogue row (rows tid and tid + 256 of the item).
+// Per-thread parameters of one in_proj row of the item, loaded a layer ahead. The fp16 row scale
+// stays in its bits until used, so that no load has to complete inside the prefetch.
 template <int NB>
 struct RowRegs {
     ItemRow m;
-    float sc, us, cb;
+    uint32_t scb;
+    float us, cb;
     float4 cw;
     int4 up[F2_UPC];
     float win[NB][3];
 };
 
-template <int NB, int KCH>
+template <int NB>
+__device__ __forceinline__ void load_row(RowRegs<NB> &R, const ItemRow &m, const Entry2 &Ly, int rank, int Cd) {
+    const dfssm_proj &pin = Ly.w.in_proj;
+    R.m = m;
+    if (m.ch == -2) return;
+    R.scb = pin.row_scale[m.n];
+    R.us = pin.lora_up_scale[m.n];
+    load_up(R.up, pin.lora_up, rank, m.n);
+    if (m.ch >= 0) {
+        R.cw = *reinterpret_cast<const float4 *>(Ly.w.conv_w + (int64_t)m.ch * kConvTaps);
+        R.cb = Ly.w.conv_b[m.ch];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float *w = Ly.st.conv + ((int64_t)b * Cd + m.ch) * (kConvTaps - 1);
+            R.win[b][0] = w[0];
+            R.win[b][1] = w[1];
+            R.win[b][2] = w[2];
+        }
+    }
+}
+
+// Scaffold + low-rank output of one in_proj row (Eq. 3); for a conv channel also the conv step:
+// the window moves on in the caller's state and the SiLU activation is returned.
+template <int NB>
+__device__ __forceinline__ float finish_row(const RowRegs<NB> &R, int b, int acc, float s, const float *tvb, int rank,
+                                            float *conv_state, int Cd) {
+    const float yv = s * half_bits_to_float((uint16_t)R.scb) * (float)acc + R.us * up_dot2(R.up, rank, tvb);
+    if (R.m.ch < 0) return yv;
+    const float pre = R.cb + R.cw.x * R.win[b][0] + R.cw.y * R.win[b][1] + R.cw.z * R.win[b][2] + R.cw.w * yv;
+    float *w = conv_state + ((int64_t)b * Cd + R.m.ch) * (kConvTaps - 1);
+    w[0] = R.win[b][1];
+    w[1] = R.win[b][2];
+    w[2] = yv;
+    return silu_f(pre);
+}
+
+template <int NB, int KCH1, int KCH2>
 __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     extern __shared__ __align__(16) char smem[];
     __shared__ float red[2 * kWaves];
@@ -379,19 +426,22 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     const int L = a.n_layers, B = a.batch;
     const dfssm_taps &T = a.taps;
     const int64_t n_tok = (int64_t)a.n_steps * L;
+    const int nbc = 2 * a.G * N;
     if (wg < a.n1) {
         // ====================================================================== role 1
         const int h = wg / a.S, p0 = (wg % a.S) * a.pr, g = h * a.G / a.H;
+        const int q = a.q, bc0 = wg * q;
         const bool pad_rows = wg == 0 && T.in_acc != nullptr;
-        const int R1t = a.R1 + (pad_rows ? a.npad : 0);
-        const int nbc = 2 * a.G * N;
+        const int R1t = a.R1 + (pad_rows ? a.npad : 0), nrest = R1t - q;
         const int CPR1 = D >> 7, NG1 = kBlock / CPR1, c1 = tid % CPR1, rg1 = tid / CPR1;
         const int TPR1 = kBlock / a.Rin, j1 = tid / TPR1, cl1 = tid % TPR1, C16_1 = D >> 4;
         const int N4 = N >> 2, nf = a.pr * N4;
-        // the group's B and C rows are tapped by the first item of the group's first head
-        const bool bc_tap = p0 == 0 && h == g * a.H / a.G;
+        // the lane that completes a B/C row's sum also finishes that row; thread r finishes rest row q + r
+        const bool bc_lane = c1 == CPR1 - 1 && rg1 < q;
+        const ItemRow m_bc = item_row(a, min(rg1, q - 1), h, p0, bc0);
+        const ItemRow m_rest = item_row(a, min(q + tid, R1t - 1), h, p0, bc0);
         // fixed per workgroup: byte offsets (in a layer's in_proj sign matrix) of the 16-byte chunks
-        // this lane copies into LDS, block by block (rotated start), and the rows of the epilogue
+        // this lane copies into LDS, block by block (rotated start)
         const int s16 = R1t * CPR1, sblk = (s16 + 63) >> 6, srot = f2_rot(sblk);
         int soff[F2_SBLK];
 #pragma unroll
@@ -403,61 +453,27 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                 if (kb >= sblk) kb -= sblk;
                 const int i = kb * 64 + (tid & 63) < s16 ? kb * 64 + (tid & 63) : 0;
                 const int r = i / CPR1, c = i - r * CPR1;
-                soff[j] = item_row(a, r, h, p0, g).n * (D >> 3) + c * 16;
+                const ItemRow m = item_row(a, r, h, p0, bc0);
+                soff[j] = (m.ch == -2 ? 0 : m.n) * (D >> 3) + c * 16;
             }
         }
-        ItemRow rmap[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) rmap[k] = item_row(a, min(tid + k * kBlock, F2_ROWS - 1), h, p0, g);
         char *sgn1 = wreg;
         char *ldn1 = wreg + f2_round_kb((size_t)R1t * (D >> 3));
         // ---- per-layer loads that do not depend on the token: issued one layer ahead
-        RowRegs<NB> rw[2];
+        RowRegs<NB> rb, rr;
         float4 st[F2_FPT][NB];
-        float4 wr[KCH];
-        float dsc1 = 0.f, dtb = 0.f, Ah = 0.f, Dh = 0.f;
-        auto prefetch = [&](int t, int l) {
+        float4 wr[KCH1];
+        float dsc1 = 0.f, dtb = 0.f, alog = 0.f, Dh = 0.f;
+        auto prefetch = [&](int l) {
             const Entry2 Ly = a.layers[l];
             const dfssm_proj &pin = Ly.w.in_proj;
-#pragma unroll
-            for (int j = 0; j < F2_SBLK; ++j) {
-                const int k = (tid >> 6) + kWaves * j;
-                if (k < sblk) {
-                    int kb = k + srot;
-                    if (kb >= sblk) kb -= sblk;
-                    __builtin_amdgcn_global_load_lds(pin.sign + soff[j], sgn1 + (size_t)kb * 64 * 16, 16, 0, 0);
-                }
-            }
-            lds_copy_contig(ldn1, reinterpret_cast<const char *>(pin.lora_dn), a.Rin * C16_1);
+            // register loads first (their waits come at first use), then the direct-to-LDS copies
+            load_norm_w<KCH1>(wr, Ly.w.norm_w, D);
             dsc1 = pin.lora_dn_scale[j1];
-            load_norm_w<KCH>(wr, Ly.w.norm_w, D);
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int r = tid + k * kBlock;
-                if (r < R1t) {
-                    RowRegs<NB> &R = rw[k];
-                    R.m = rmap[k];
-                    R.sc = half_bits_to_float(pin.row_scale[R.m.n]);
-                    R.us = pin.lora_up_scale[R.m.n];
-                    load_up(R.up, pin.lora_up, a.Rin, R.m.n);
-                    if (R.m.ch >= 0) {
-                        R.cw = *reinterpret_cast<const float4 *>(Ly.w.conv_w + (int64_t)R.m.ch * kConvTaps);
-                        R.cb = Ly.w.conv_b[R.m.ch];
-                        const bool own = R.m.ch < E;
-#pragma unroll
-                        for (int b = 0; b < NB; ++b) {
-                            const float *wsrc = (own || t == 0)
-                                                    ? Ly.st.conv + ((int64_t)b * a.Cd + R.m.ch) * (kConvTaps - 1)
-                                                    : a.bcp + ((((int64_t)wg * L + l) * B + b) * nbc + (R.m.ch - E)) * 3;
-                            R.win[b][0] = wsrc[0];
-                            R.win[b][1] = wsrc[1];
-                            R.win[b][2] = wsrc[2];
-                        }
-                    }
-                }
-            }
+            if (bc_lane) load_row(rb, m_bc, Ly, a.Rin, a.Cd);
+            if (tid < nrest) load_row(rr, m_rest, Ly, a.Rin, a.Cd);
             dtb = Ly.w.dt_bias[h];
-            Ah = -expf(Ly.w.A_log[h]);
+            alog = Ly.w.A_log[h];
             Dh = Ly.w.D[h];
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
@@ -471,8 +487,18 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     }
                 }
             }
+#pragma unroll
+            for (int j = 0; j < F2_SBLK; ++j) {
+                const int k = (tid >> 6) + kWaves * j;
+                if (k < sblk) {
+                    int kb = k + srot;
+                    if (kb >= sblk) kb -= sblk;
+                    __builtin_amdgcn_global_load_lds(pin.sign + soff[j], sgn1 + (size_t)kb * 64 * 16, 16, 0, 0);
+                }
+            }
+            lds_copy_contig(ldn1, reinterpret_cast<const char *>(pin.lora_dn), a.Rin * C16_1);
         };
-        prefetch(0, 0);
+        prefetch(0);
         for (int64_t it = 0; it < n_tok; ++it) {
             const int t = (int)(it / L), l = (int)(it - (int64_t)t * L);
             const Entry2 Ly = a.layers[l];
@@ -481,16 +507,17 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             const int64_t rec = it * B;
             const uint64_t *hx_prev = a.hx + (int64_t)lp * B * D;
             uint64_t *gxl = a.gx + (int64_t)l * B * E;
+            uint64_t *bcxl = a.bcx + (int64_t)l * B * nbc;
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's direct-to-LDS copies are in
             __syncthreads();
             // ---- residual in, norm, quantizer
             {
                 const bool fold = l == 0 && t > 0;   // the previous token's stack output through the final RMSNorm
-                f2_prologue<NB, KCH>(a, hx_prev, D, tag - 1, wr, fold ? a.final_w : nullptr,
-                                     fold ? a.y + (int64_t)(t - 1) * B * D : nullptr, sq, spl, sqsum, ssc, red, ired, nullptr,
-                                     wg == 0, fold ? &r0s : nullptr, T.h_in ? T.h_in + rec * D : nullptr,
-                                     T.in_u ? T.in_u + rec * D : nullptr, T.in_q ? T.in_q + rec * D : nullptr,
-                                     T.in_s ? T.in_s + rec : nullptr);
+                f2_prologue<NB, KCH1>(a, hx_prev, D, tag - 1, wr, fold ? a.final_w : nullptr,
+                                      fold ? a.y + (int64_t)(t - 1) * B * D : nullptr, sq, spl, sqsum, ssc, red, ired,
+                                      nullptr, wg == 0, fold ? &r0s : nullptr, T.h_in ? T.h_in + rec * D : nullptr,
+                                      T.in_u ? T.in_u + rec * D : nullptr, T.in_q ? T.in_q + rec * D : nullptr,
+                                      T.in_s ? T.in_s + rec : nullptr);
                 if (fold && wg == 0 && tid == 0) st_x(a.rx, tag2(fbits2(r0s), tag));
             }
             // LoRA-down t[j] = L_dn[j] . q (sdot4, factors in LDS)
@@ -506,7 +533,9 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     if (wg == 0 && T.in_t) T.in_t[(rec + b) * a.Rin + j1] = part;
                 }
             }
-            // packed-sign GEMV of the item's rows (chunk c1 of rows rg1 + NG1 * i), branch-free
+            __syncthreads();
+            // packed-sign GEMV: first the B/C rows, finished and published at once by the lane that
+            // completes each sum, then the item's other rows (while the B/C words travel)
             {
                 const int G32 = D >> 5;
 #pragma unroll
@@ -514,60 +543,65 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     uint4 pl[8];
 #pragma unroll
                     for (int p = 0; p < 8; ++p) pl[p] = *reinterpret_cast<const uint4 *>(spl + (b * 8 + p) * G32 + c1 * 4);
+                    {
+                        const int r = min(rg1, q - 1);
+                        int pos = chunk_pos(*reinterpret_cast<const uint4 *>(sgn1 + (size_t)r * (D >> 3) + c1 * 16), pl);
+                        pos = dpp_group_sum(pos, CPR1);
+                        if (bc_lane && rb.m.ch != -2) {
+                            const int acc = 2 * pos - sqsum[b];
+                            const float act = finish_row(rb, b, acc, ssc[b], tv + b * 64, a.Rin, Ly.st.conv, a.Cd);
+                            st_x(bcxl + (int64_t)b * nbc + (rb.m.ch - E), tag2(fbits2(act), tag));
+                            if (T.in_acc) T.in_acc[(rec + b) * a.Ninp + rb.m.n] = acc;
+                        }
+                    }
                     int pos[F2_MAXI];
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i) {
-                        if (NG1 * i >= R1t) break;
-                        const int r = min(rg1 + NG1 * i, R1t - 1);
+                        if (NG1 * i >= nrest) break;
+                        const int r = min(q + rg1 + NG1 * i, R1t - 1);
                         pos[i] = chunk_pos(*reinterpret_cast<const uint4 *>(sgn1 + (size_t)r * (D >> 3) + c1 * 16), pl);
                     }
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i) {
-                        if (NG1 * i >= R1t) break;
+                        if (NG1 * i >= nrest) break;
                         pos[i] = dpp_group_sum(pos[i], CPR1);
                     }
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i) {
-                        if (NG1 * i >= R1t) break;
+                        if (NG1 * i >= nrest) break;
                         const int r = rg1 + NG1 * i;
-                        if (c1 == CPR1 - 1 && r < R1t) accl[b * F2_ROWS + r] = 2 * pos[i] - sqsum[b];
+                        if (c1 == CPR1 - 1 && r < nrest) accl[b * F2_ROWS + r] = 2 * pos[i] - sqsum[b];
                     }
                 }
             }
             __syncthreads();
-            // epilogue, conv step, z / x / dt / B / C into LDS
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int r = tid + k * kBlock;
-                if (r >= R1t) continue;
-                RowRegs<NB> &R = rw[k];
+            // the other rows' epilogue (z, conv step of x, dt), then the group's B and C from the exchange
+            if (tid < nrest) {
+                const int r = q + tid;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    const int acc = accl[b * F2_ROWS + r];
-                    const float yv = ssc[b] * R.sc * (float)acc + R.us * up_dot2(R.up, a.Rin, tv + b * 64);
-                    if (T.in_acc && (r <= 2 * a.pr || bc_tap || r >= a.R1)) T.in_acc[(rec + b) * a.Ninp + R.m.n] = acc;
+                    const int acc = accl[b * F2_ROWS + tid];
+                    if (T.in_acc) T.in_acc[(rec + b) * a.Ninp + rr.m.n] = acc;
                     if (r >= a.R1) continue;   // padding row
-                    const int ch = R.m.ch;
-                    if (ch >= 0) {
-                        const float pre = R.cb + R.cw.x * R.win[b][0] + R.cw.y * R.win[b][1] + R.cw.z * R.win[b][2] + R.cw.w * yv;
-                        const float act = silu_f(pre);
-                        float *wdst = ch < E ? Ly.st.conv + ((int64_t)b * a.Cd + ch) * (kConvTaps - 1)
-                                             : a.bcp + ((((int64_t)wg * L + l) * B + b) * nbc + (ch - E)) * 3;
-                        wdst[0] = R.win[b][1];
-                        wdst[1] = R.win[b][2];
-                        wdst[2] = yv;
-                        if (ch < E) xl[b * P + (r - a.pr)] = act;
-                        else if (r < 2 * a.pr + 1 + N) Bl[b * N + (r - 2 * a.pr - 1)] = act;
-                        else Cl[b * N + (r - 2 * a.pr - 1 - N)] = act;
-                    } else if (r < a.pr) {
-                        zl[b * P + r] = yv;
-                    } else {
-                        dtl[b] = softplus_f(yv + dtb);
-                    }
+                    const float v = finish_row(rr, b, acc, ssc[b], tv + b * 64, a.Rin, Ly.st.conv, a.Cd);
+                    if (r < q + a.pr) zl[b * P + (r - q)] = v;
+                    else if (r < q + 2 * a.pr) xl[b * P + (r - q - a.pr)] = v;
+                    else dtl[b] = softplus_f(v + dtb);
+                }
+            }
+            if (tid < (N >> 1)) {
+                const int c = tid < N4 ? 0 : 1, k = (tid - c * N4) * 4;   // B or C, first of 4 words
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    u32x4 w[2];
+                    f2_gather<1>(a, bcxl + (int64_t)b * nbc + c * a.G * N + g * N + k, tag, w);
+                    *reinterpret_cast<float4 *>((c ? Cl : Bl) + b * N + k) =
+                        make_float4(bitsf2(w[0].x), bitsf2(w[0].z), bitsf2(w[1].x), bitsf2(w[1].z));
                 }
             }
             __syncthreads();
             // SSM update + readout, gate, publish g
+            const float Ah = -expf(alog);
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
                 if (i >= a.fpt) break;
@@ -600,44 +634,37 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             if (it + 1 < n_tok) {
                 __syncthreads();   // every wave is done with this layer's LDS
                 const int64_t nx = it + 1;
-                const int tn = (int)(nx / L);
-                prefetch(tn, (int)(nx - (int64_t)tn * L));
+                prefetch((int)(nx - (nx / L) * L));
             }
         }
-        // the stack's final RMSNorm of the last token, and the B/C conv windows back to the caller's state
+        // the stack's final RMSNorm of the last token
         if (wg == 0) {
             const uint32_t tag = (uint32_t)n_tok;
             const uint64_t *hl = a.hx + (int64_t)(L - 1) * B * D;
             float *yt = a.y + (int64_t)(a.n_steps - 1) * B * D;
-            float *xs = reinterpret_cast<float *>(wreg);
+            const int e0 = prologue_elem<KCH1>(0);
+            const bool mine = e0 < D;
             for (int b = 0; b < B; ++b) {
-                float ss = 0.f;
-                for (int e = tid; e < D; e += kBlock) {
-                    uint64_t w = ld_x(hl + (int64_t)b * D + e);
-                    unsigned spins = 0;
-                    while ((uint32_t)(w >> 32) != tag && spins <= kSpin2) {
-                        __builtin_amdgcn_s_sleep(kSleep2);
-                        if (++spins > kSpin2) f2_error(a);
-                        w = ld_x(hl + (int64_t)b * D + e);
-                    }
-                    const float v = bitsf2((uint32_t)w);
-                    xs[e] = v;
-                    ss += v * v;
+                float4 hv[KCH1];
+                if (mine) {
+                    u32x4 r[2 * KCH1];
+                    f2_gather<KCH1>(a, hl + (int64_t)b * D + e0, tag, r);
+#pragma unroll
+                    for (int i = 0; i < KCH1; ++i)
+                        hv[i] = make_float4(bitsf2(r[2 * i].x), bitsf2(r[2 * i].z), bitsf2(r[2 * i + 1].x), bitsf2(r[2 * i + 1].z));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < KCH1; ++i) hv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
                 }
-                const float tot = block_sum(ss, red);
-                const float r = 1.0f / sqrtf(tot / (float)D + a.eps);
-                for (int e = tid; e < D; e += kBlock) yt[(int64_t)b * D + e] = (xs[e] * r) * a.final_w[e];
-                __syncthreads();
-            }
-            for (int l = 0; l < L; ++l) {
-                const Entry2 Ly = a.layers[l];
-                for (int k = tid; k < B * nbc; k += kBlock) {
-                    const int b = k / nbc, j = k - b * nbc;
-                    const float *src = a.bcp + ((((int64_t)0 * L + l) * B + b) * nbc + j) * 3;
-                    float *dst = Ly.st.conv + ((int64_t)b * a.Cd + E + j) * (kConvTaps - 1);
-                    dst[0] = src[0];
-                    dst[1] = src[1];
-                    dst[2] = src[2];
+                const float r0 = f2_norm_factor<KCH1>(a, hv, D, red);
+                if (mine) {
+#pragma unroll
+                    for (int i = 0; i < KCH1; ++i) {
+                        const int e = prologue_elem<KCH1>(i);
+                        const float4 w = *reinterpret_cast<const float4 *>(a.final_w + e);
+                        *reinterpret_cast<float4 *>(yt + (int64_t)b * D + e) =
+                            make_float4((hv[i].x * r0) * w.x, (hv[i].y * r0) * w.y, (hv[i].z * r0) * w.z, (hv[i].w * r0) * w.w);
+                    }
                 }
             }
         }
@@ -653,22 +680,23 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     char *ldn2 = wreg + f2_round_kb((size_t)a.R2 * (E >> 3));
     const int on = n_out0 + tid;
     const bool orow = tid < R2t;
-    float dsc2 = 0.f, osc = 0.f, ous = 0.f;
+    float dsc2 = 0.f, ous = 0.f;
+    uint32_t oscb = 0;
     int4 oup[F2_UPC];
-    float4 wr[KCH];
+    float4 wr[KCH2];
     auto prefetch = [&](int l) {
         const Entry2 Ly = a.layers[l];
         const dfssm_proj &pout = Ly.w.out_proj;
-        if (R2t > 0)
-            lds_copy_contig(sgn2, reinterpret_cast<const char *>(pout.sign + (int64_t)n_out0 * (E >> 3)), R2t * CPR2);
-        lds_copy_contig(ldn2, reinterpret_cast<const char *>(pout.lora_dn), a.Rout * C16_2);
+        load_norm_w<KCH2>(wr, Ly.w.gnorm_w, E);
         dsc2 = pout.lora_dn_scale[j2];
-        load_norm_w<KCH>(wr, Ly.w.gnorm_w, E);
         if (orow) {
-            osc = half_bits_to_float(pout.row_scale[on]);
+            oscb = pout.row_scale[on];
             ous = pout.lora_up_scale[on];
             load_up(oup, pout.lora_up, a.Rout, on);
         }
+        if (R2t > 0)
+            lds_copy_contig(sgn2, reinterpret_cast<const char *>(pout.sign + (int64_t)n_out0 * (E >> 3)), R2t * CPR2);
+        lds_copy_contig(ldn2, reinterpret_cast<const char *>(pout.lora_dn), a.Rout * C16_2);
     };
     // this workgroup's rows of the residual stream (the token input x0 to begin with)
     float hold[NB];
@@ -684,7 +712,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         uint64_t *hxl = a.hx + (int64_t)l * B * D;
         if (l == 0 && t > 0) {
             // the residual input of layer 0 is the previous token's output through the final RMSNorm,
-            // whose factor role-1 workgroup 0 publishes (the product is the one the prologue forms)
+            // whose factor role-1 workgroup 0 publishes (the product is the one its prologue forms)
             uint64_t w = ld_x(a.rx);
             unsigned spins = 0;
             while ((uint32_t)(w >> 32) != tag && spins <= kSpin2) {
@@ -698,9 +726,9 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's direct-to-LDS copies are in
         __syncthreads();
-        f2_prologue<NB, KCH>(a, gxl, E, tag, wr, nullptr, nullptr, sq, spl, sqsum, ssc, red, ired, nullptr, tap2, nullptr,
-                             nullptr, T.out_u ? T.out_u + rec * E : nullptr, T.out_q ? T.out_q + rec * E : nullptr,
-                             T.out_s ? T.out_s + rec : nullptr);
+        f2_prologue<NB, KCH2>(a, gxl, E, tag, wr, nullptr, nullptr, sq, spl, sqsum, ssc, red, ired, nullptr, tap2, nullptr,
+                              nullptr, T.out_u ? T.out_u + rec * E : nullptr, T.out_q ? T.out_q + rec * E : nullptr,
+                              T.out_s ? T.out_s + rec : nullptr);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             int part = 0;
@@ -733,6 +761,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         }
         __syncthreads();
         if (orow) {
+            const float osc = half_bits_to_float((uint16_t)oscb);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int acc = accl[b * F2_ROWS + tid];
@@ -792,12 +821,12 @@ int f2_slices(const Shape &s, int slots) {
 }
 
 struct F2Plan {
-    int S, pr, R1, npad, R2, fpt, n1, n2;
+    int S, pr, q, R1, npad, R2, fpt, n1, n2;
 };
 
 bool f2_plan(const Shape &s, int batch, int slots, F2Plan &p) {
     if (batch != 1) return false;
-    if (!pow2(s.D) || !pow2(s.E) || s.D < 256 || s.E < 256 || s.D > 8192 || s.E > 8192) return false;
+    if (!pow2(s.D) || s.D < 256 || s.D > 4096 || s.E != 2 * s.D) return false;
     if (!pow2(s.Rin) || !pow2(s.Rout) || s.Rin < 8 || s.Rout < 8 || s.Rin > 16 * F2_UPC || s.Rout > 16 * F2_UPC) return false;
     if (s.N % 4 || s.N / 4 > 64 || !pow2(s.N / 4)) return false;
     // half the resident workgroups (at most) for the SSM items, the rest for out_proj row blocks
@@ -805,11 +834,12 @@ bool f2_plan(const Shape &s, int batch, int slots, F2Plan &p) {
     if (p.S == 0) return false;
     p.n1 = s.H * p.S;
     p.pr = s.P / p.S;
-    p.R1 = 2 * p.pr + 1 + 2 * s.N;
+    p.q = (2 * s.G * s.N + p.n1 - 1) / p.n1;
+    p.R1 = p.q + 2 * p.pr + 1;
     p.npad = s.Ninp - s.Nin;
-    if (p.R1 + p.npad > F2_ROWS || p.R1 + p.npad > (kBlock / (s.D >> 7)) * F2_MAXI || p.R1 + p.npad > 2 * kBlock)
-        return false;
-    if ((p.R1 + p.npad) * (s.D >> 7) > F2_SBLK * kWaves * 64) return false;
+    const int CPR1 = s.D >> 7, NG1 = kBlock / CPR1, rest = p.R1 + p.npad - p.q;
+    if (p.q > NG1 || rest > NG1 * F2_MAXI || rest > kBlock || rest > F2_ROWS) return false;
+    if ((p.R1 + p.npad) * CPR1 > F2_SBLK * kWaves * 64) return false;
     const int avail = slots - p.n1;
     if (avail < 1) return false;
     p.R2 = (s.D + avail - 1) / avail;
@@ -821,22 +851,22 @@ bool f2_plan(const Shape &s, int batch, int slots, F2Plan &p) {
     return f2_lds_base(s, batch) + f2_wreg_bytes(s, p.R1 + p.npad, p.R2) <= kF2MaxLds;
 }
 
-template <int NB, int KCH>
+int f2_kch(int K) { return K <= 1024 ? 1 : K / 1024; }
+
+template <int NB, int KCH1, int KCH2>
 hipError_t f2_launch(F2Args &a, const Shape &s, hipStream_t stream) {
     const size_t lds = f2_lds_base(s, NB) + f2_wreg_bytes(s, a.R1 + a.npad, a.R2);
     void *args[] = {&a};
+    const void *fn = reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2>);
     // DFSSM_STACK_LAUNCH=plain: the same grid through the ordinary launch API, for profilers that
     // cannot trace cooperative launches (the grid never exceeds what is resident at once, and every
     // wait is bounded)
     const char *mode = getenv("DFSSM_STACK_LAUNCH");
-    if (mode && strcmp(mode, "plain") == 0)
-        return hipLaunchKernel(reinterpret_cast<const void *>(&k_flow2<NB, KCH>), dim3(a.n1 + a.n2), dim3(kBlock), args, lds,
-                               stream);
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_flow2<NB, KCH>), dim3(a.n1 + a.n2), dim3(kBlock),
-                                      args, lds, stream);
+    if (mode && strcmp(mode, "plain") == 0) return hipLaunchKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
+    return hipLaunchCooperativeKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
 }
 
-template <int NB, int KCH>
+template <int NB, int KCH1, int KCH2>
 int f2_resident() {
     static std::atomic<int> memo[kMaxDevices2];
     int dev = 0;
@@ -846,34 +876,32 @@ int f2_resident() {
     int ncu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     // with the largest LDS a supported shape may use (registers bound the occupancy to one per CU anyway)
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_flow2<NB, KCH>), kBlock,
-                                                     kF2MaxLds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2>),
+                                                     kBlock, kF2MaxLds) != hipSuccess)
         return 0;
     v = per_cu * ncu;
     memo[dev].store(v, std::memory_order_relaxed);
     return v;
 }
 
-template <int NB>
-int f2_resident_nb(int kmax) {
-    if (kmax <= 1024) return f2_resident<NB, 1>();
-    if (kmax <= 2048) return f2_resident<NB, 2>();
-    if (kmax <= 4096) return f2_resident<NB, 4>();
-    return f2_resident<NB, 8>();
-}
-
+// The (D, E = 2D) shapes the kernel is built for: KCH1 = D / 1024, KCH2 = E / 1024 (at least 1).
 int f2_slots(const Shape &s, int batch) {
-    const int kmax = s.D > s.E ? s.D : s.E;
-    return batch == 1 ? f2_resident_nb<1>(kmax) : 0;
+    if (batch != 1 || s.E != 2 * s.D) return 0;
+    switch (f2_kch(s.D)) {
+    case 1: return f2_kch(s.E) == 1 ? f2_resident<1, 1, 1>() : f2_resident<1, 1, 2>();
+    case 2: return f2_resident<1, 2, 4>();
+    case 4: return f2_resident<1, 4, 8>();
+    default: return 0;
+    }
 }
 
-template <int NB>
-hipError_t f2_launch_nb(F2Args &a, const Shape &s, hipStream_t stream) {
-    const int kmax = s.D > s.E ? s.D : s.E;
-    if (kmax <= 1024) return f2_launch<NB, 1>(a, s, stream);
-    if (kmax <= 2048) return f2_launch<NB, 2>(a, s, stream);
-    if (kmax <= 4096) return f2_launch<NB, 4>(a, s, stream);
-    return f2_launch<NB, 8>(a, s, stream);
+hipError_t f2_launch_any(F2Args &a, const Shape &s, hipStream_t stream) {
+    switch (f2_kch(s.D)) {
+    case 1: return f2_kch(s.E) == 1 ? f2_launch<1, 1, 1>(a, s, stream) : f2_launch<1, 1, 2>(a, s, stream);
+    case 2: return f2_launch<1, 2, 4>(a, s, stream);
+    case 4: return f2_launch<1, 4, 8>(a, s, stream);
+    default: return hipErrorInvalidConfiguration;
+    }
 }
 
 }  // namespace
@@ -889,8 +917,7 @@ size_t stack2_extra_ws_bytes(const Shape &s, int batch, int n_layers) {
     F2Plan p{};
     if (!f2_plan(s, batch, f2_slots(s, batch), p)) return 0;
     const size_t L = n_layers;
-    return align_up(L * sizeof(Entry2), 256) + 256 + align_up(L * batch * (size_t)(s.D + s.E) * 8, 256) +
-           align_up((size_t)p.n1 * L * batch * 2 * s.G * s.N * 3 * 4, 256);
+    return align_up(L * sizeof(Entry2), 256) + 256 + align_up(L * batch * (size_t)(s.D + s.E + 2 * s.G * s.N) * 8, 256);
 }
 
 hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states, int n_layers,
@@ -905,7 +932,7 @@ hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, cons
     int *err = reinterpret_cast<int *>(q);
     q += 256;
     uint64_t *words = reinterpret_cast<uint64_t *>(q);
-    const int64_t nwords = (int64_t)L * batch * (s.D + s.E);
+    const int64_t nwords = (int64_t)L * batch * (s.D + s.E + 2 * s.G * s.N);
     q += align_up((size_t)nwords * 8, 256);
     F2Args a{};
     a.n_layers = n_layers;
@@ -925,6 +952,7 @@ hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, cons
     a.eps = s.eps;
     a.S = p.S;
     a.pr = p.pr;
+    a.q = p.q;
     a.R1 = p.R1;
     a.npad = p.npad;
     a.R2 = p.R2;
@@ -938,7 +966,7 @@ hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, cons
     a.y = y;
     a.hx = words;
     a.gx = words + L * batch * s.D;
-    a.bcp = reinterpret_cast<float *>(q);
+    a.bcx = a.gx + L * batch * s.E;
     a.err = err;
     if (taps) a.taps = *taps;
     hipError_t e;
@@ -953,7 +981,7 @@ hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_seed2<<<64, 256, 0, stream>>>(a.hx + (int64_t)(L - 1) * batch * s.D, x0, (int64_t)batch * s.D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return f2_launch_nb<1>(a, s, stream);
+    return f2_launch_any(a, s, stream);
 }
 
 }  // namespace dfssm
