@@ -33,7 +33,7 @@ namespace dfssm {
 
 namespace {
 
-constexpr int F2_MAXI = 12;   // in_proj rows per GEMV thread (after the B/C rows): rows rg + NG * i
+constexpr int F2_MAXI = 8;    // in_proj rows per GEMV thread (after the B/C rows): rows rg + NG * i
 constexpr int F2_SBLK = 8;    // 1 KB blocks of in_proj sign rows each wave copies per layer
 constexpr int F2_UPC = 2;     // LoRA-up chunks (16 B) per row: rank <= 32
 constexpr int F2_MAXO = 4;    // out_proj sign chunks per thread
@@ -68,6 +68,37 @@ struct F2Args {
     dfssm_taps taps;
 };
 
+// Weights and state are reached through pointers read from the layer table, which the compiler
+// cannot place in an address space: accessed as generic (flat) memory, every store would hold up the
+// next LDS wait until it is acknowledged. These helpers state that they are global memory, and the
+// table itself is read through the constant address space (scalar loads: it does not change while
+// the kernel runs). The host pass of the single-source compile has no address spaces for class
+// types and only needs the declarations.
+#define F2_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ T gld(const T *p) {
+#if __HIP_DEVICE_COMPILE__
+    return *(const F2_GLOBAL T *)p;
+#else
+    return *p;
+#endif
+}
+template <typename T>
+__device__ __forceinline__ void gst(T *p, const T &v) {
+#if __HIP_DEVICE_COMPILE__
+    *(F2_GLOBAL T *)p = v;
+#else
+    *p = v;
+#endif
+}
+__device__ __forceinline__ Entry2 f2_entry(const F2Args &a, int l) {
+#if __HIP_DEVICE_COMPILE__
+    return ((const __attribute__((address_space(4))) Entry2 *)a.layers)[l];
+#else
+    return a.layers[l];
+#endif
+}
+
 __device__ __forceinline__ size_t f2_round_kb(size_t v) { return (v + 1023) & ~(size_t)1023; }
 __device__ __forceinline__ uint64_t tag2(uint32_t bits, uint32_t tag) { return ((uint64_t)tag << 32) | bits; }
 __device__ __forceinline__ uint32_t fbits2(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -100,143 +131,6 @@ __device__ __forceinline__ void f2_gather(const F2Args &a, const uint64_t *p, ui
     }
 }
 
-__device__ __forceinline__ float f2_ss(const float4 &v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
-
-// The stack's final RMSNorm, (h * r) * w, of one gathered vector: the thread layout and the order of
-// the sum of squares are the prologue's, so that the last token's output is bit-identical to what
-// the next token's prologue would form from the same words.
-template <int KCH>
-__device__ __forceinline__ float f2_norm_factor(const F2Args &a, const float4 (&hv)[KCH], int K, float *red) {
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) ss += f2_ss(hv[i]);
-    const float tot = block_sum(ss, red);
-    return 1.0f / sqrtf(tot / (float)K + a.eps);
-}
-
-// Gather NB vectors of K tagged words, RMSNorm (after the stack's final RMSNorm when pre_w is set),
-// int8 quantizer -> codes sq[b][K], bit-planes spl[b][8][K/32], sum of codes, scale; xs (optional)
-// keeps the normalised input. wr: this thread's norm weights. Taps are written by workgroup 0.
-template <int NB, int KCH>
-__device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t tag, const float4 (&wr)[KCH],
-                            const float *pre_w, float *pre_out, int8_t *sq, uint32_t *spl, int *sqsum, float *ssc,
-                            float *red, int *ired, float *xs, bool tapwg, float *r0_out, float *tap_h, float *tap_u,
-                            int8_t *tap_q, float *tap_s) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e0 = prologue_elem<KCH>(0);
-    const bool mine = e0 < K;   // K is a multiple of 4*KCH: a thread has all of its chunks or none
-    for (int b = 0; b < NB; ++b) {
-        float4 hv[KCH];
-        if (mine) {
-            u32x4 r[2 * KCH];
-            f2_gather<KCH>(a, X + (int64_t)b * K + e0, tag, r);
-#pragma unroll
-            for (int i = 0; i < KCH; ++i)
-                hv[i] = make_float4(bitsf2(r[2 * i].x), bitsf2(r[2 * i].z), bitsf2(r[2 * i + 1].x), bitsf2(r[2 * i + 1].z));
-        } else {
-#pragma unroll
-            for (int i = 0; i < KCH; ++i) hv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        float ss = 0.f;
-        if (pre_w) {
-            const float r0 = f2_norm_factor<KCH>(a, hv, K, red);
-            if (r0_out && tid == 0) *r0_out = r0;
-            if (mine) {
-#pragma unroll
-                for (int i = 0; i < KCH; ++i) {
-                    const int e = prologue_elem<KCH>(i);
-                    const float4 w = *reinterpret_cast<const float4 *>(pre_w + e);
-                    hv[i].x = (hv[i].x * r0) * w.x;
-                    hv[i].y = (hv[i].y * r0) * w.y;
-                    hv[i].z = (hv[i].z * r0) * w.z;
-                    hv[i].w = (hv[i].w * r0) * w.w;
-                    if (tapwg && pre_out) *reinterpret_cast<float4 *>(pre_out + (int64_t)b * K + e) = hv[i];
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) ss += f2_ss(hv[i]);
-        float pm = 0.f;
-        if (mine) {
-#pragma unroll
-            for (int i = 0; i < KCH; ++i) {
-                const int e = prologue_elem<KCH>(i);
-                if (xs) *reinterpret_cast<float4 *>(xs + b * K + e) = hv[i];
-                if (tapwg && tap_h) *reinterpret_cast<float4 *>(tap_h + (int64_t)b * K + e) = hv[i];
-                const float4 w = wr[i];
-                hv[i].x = hv[i].x * w.x;
-                hv[i].y = hv[i].y * w.y;
-                hv[i].z = hv[i].z * w.z;
-                hv[i].w = hv[i].w * w.w;
-                pm = fmaxf(pm, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)), fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
-            }
-        }
-        // u = fl(fl(h * w) * r): with r > 0 the largest |u| is fl(max|h * w| * r) exactly
-        float tot;
-        block_sum_max(ss, pm, red, tot, pm);
-        const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
-        const float amax = pm * r;
-        const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-        const float s = amax > 0.f ? amax / 127.0f : 0.f;
-        int qs = 0;
-        if (mine) {
-#pragma unroll
-            for (int i = 0; i < KCH; ++i) {
-                const int e = prologue_elem<KCH>(i);
-                hv[i].x = hv[i].x * r;
-                hv[i].y = hv[i].y * r;
-                hv[i].z = hv[i].z * r;
-                hv[i].w = hv[i].w * r;
-                const int q0 = quant1(hv[i].x, inv), q1 = quant1(hv[i].y, inv);
-                const int q2 = quant1(hv[i].z, inv), q3 = quant1(hv[i].w, inv);
-                qs += q0 + q1 + q2 + q3;
-                const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
-                                        ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
-                *reinterpret_cast<uint32_t *>(sq + b * K + e) = packed;
-                if (tapwg) {
-                    if (tap_u) *reinterpret_cast<float4 *>(tap_u + (int64_t)b * K + e) = hv[i];
-                    if (tap_q) *reinterpret_cast<uint32_t *>(tap_q + (int64_t)b * K + e) = packed;
-                }
-            }
-        }
-        qs = block_isum(qs, ired);
-        if (tid == 0) {
-            sqsum[b] = qs;
-            ssc[b] = s;
-            if (tapwg && tap_s) tap_s[b] = s;
-        }
-    }
-    __syncthreads();
-    // bit-planes via wave ballots over 64 consecutive codes
-    const int G32 = K >> 5;
-    for (int b = 0; b < NB; ++b) {
-        for (int c = wave; c < (K >> 6); c += kWaves) {
-            const uint32_t v = (uint8_t)sq[b * K + c * 64 + lane];
-            uint64_t m8 = 0;
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const uint64_t m = __ballot((v >> p) & 1u);
-                if ((lane & 7) == p) m8 = m;
-            }
-            if (lane < 16) spl[(b * 8 + (lane & 7)) * G32 + 2 * c + (lane >> 3)] = lane < 8 ? (uint32_t)m8 : (uint32_t)(m8 >> 32);
-        }
-    }
-    __syncthreads();
-}
-
-// sum_k sgn * q of one 16-byte sign chunk against the bit-planes of the same 128 codes:
-// 2 * (sum over set bits of q) - sum(q) is finished by the caller; this returns sum over set bits.
-__device__ __forceinline__ int chunk_pos(const uint4 &bits, const uint4 (&pl)[8]) {
-    int pos = 0;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int c = __popc(bits.x & pl[p].x) + __popc(bits.y & pl[p].y) + __popc(bits.z & pl[p].z) +
-                      __popc(bits.w & pl[p].w);
-        pos += p < 7 ? (c << p) : -(c << 7);
-    }
-    return pos;
-}
-
 // Sum over groups of w consecutive lanes (w a power of two <= 64) with DPP row operations; the
 // group's total is valid in its last lane (lane % w == w - 1).
 __device__ __forceinline__ int dpp_group_sum(int v, int w) {
@@ -262,6 +156,213 @@ __device__ __forceinline__ float dpp_group_sum_f(float v, int w) {
     return v;
 }
 
+// Whole-wave sum / max by DPP (a few cycles per step, against a full LDS round trip per step for
+// lane shuffles); the fixed order makes every workgroup reducing the same data agree bit for bit.
+template <int CTRL, int RMASK, bool BC>
+__device__ __forceinline__ float dpp_max_f(float v) {
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, RMASK, 0xF, BC)));
+}
+__device__ __forceinline__ float f2_wave_sum(float v) {
+    v = dpp_group_sum_f(v, 64);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float f2_wave_max(float v) {   // v >= 0 (lanes past a row edge read 0)
+    v = dpp_max_f<0xB1, 0xF, true>(v);
+    v = dpp_max_f<0x4E, 0xF, true>(v);
+    v = dpp_max_f<0x114, 0xF, true>(v);
+    v = dpp_max_f<0x118, 0xF, true>(v);
+    v = dpp_max_f<0x142, 0xA, false>(v);
+    v = dpp_max_f<0x143, 0xC, false>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ int f2_wave_isum(int v) { return __builtin_amdgcn_readlane(dpp_group_sum(v, 64), 63); }
+
+// 8x8 bit transpose (delta swaps, Hacker's Delight 7-3): with code j in byte j of x, byte p of the
+// result holds bit p of every code, code j in bit j.
+__device__ __forceinline__ uint64_t transpose8(uint64_t x) {
+    uint64_t t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
+    x ^= t ^ (t << 7);
+    t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
+    x ^= t ^ (t << 14);
+    t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
+    x ^= t ^ (t << 28);
+    return x;
+}
+
+// Bit-plane words of 32 consecutive codes from registers: the thread holds 4*KCH consecutive codes
+// (packed four to a word, lowest code in the low byte); the 32/(4*KCH) threads of one plane word
+// merge their bits with DPP row shifts, and the first of them returns the eight words (bit j of
+// plane p = bit p of code 32w + j).
+template <int KCH>
+__device__ __forceinline__ void code_planes(const uint32_t (&pk)[KCH], uint32_t (&pw)[8]) {
+    constexpr int NP = KCH >= 2 ? KCH / 2 : 1, BL = 4 * KCH;
+    uint64_t y[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+        y[k] = transpose8((uint64_t)pk[2 * k < KCH ? 2 * k : 0] | (2 * k + 1 < KCH ? (uint64_t)pk[2 * k + 1] << 32 : 0ull));
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) v |= (uint32_t)((y[k] >> (8 * p)) & 0xFFu) << (8 * k);
+        if (BL < 32) v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x101, 0xF, 0xF, true) << (BL & 31);        // lane + 1
+        if (BL < 16) v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x102, 0xF, 0xF, true) << ((2 * BL) & 31);  // lane + 2
+        if (BL < 8) v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xF, 0xF, true) << ((4 * BL) & 31);   // lane + 4
+        pw[p] = v;
+    }
+}
+
+__device__ __forceinline__ float f2_ss(const float4 &v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
+
+// The stack's final RMSNorm, (h * r) * w, of one gathered vector: the thread layout and the order of
+// the sum of squares are the prologue's, so that the last token's output is bit-identical to what
+// the next token's prologue would form from the same words.
+// One barrier: the per-wave partials go to slots (kWaves floats) that nothing writes again before
+// the caller's next barrier; the combination order is fixed, so every workgroup reducing the same
+// data gets the same bits.
+template <int KCH>
+__device__ __forceinline__ float f2_norm_factor(const F2Args &a, const float4 (&hv)[KCH], int K, float *slot) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) ss += f2_ss(hv[i]);
+    ss = f2_wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (slot[0] + slot[1]) + (slot[2] + slot[3]);
+    return 1.0f / sqrtf(tot / (float)K + a.eps);
+}
+
+// Gather NB vectors of K tagged words, RMSNorm (after the stack's final RMSNorm when pre_w is set),
+// int8 quantizer -> codes sq[b][K], bit-planes spl[b][8][K/32]; every thread gets the sum of the
+// codes and the scale. wr: this thread's norm weights. Taps are written by workgroup tapwg. red:
+// 3 * kWaves floats, ired: NB * kWaves ints of LDS. Two barriers per vector (three with pre_w).
+template <int NB, int KCH>
+__device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t tag, const float4 (&wr)[KCH],
+                            const float *pre_w, float *pre_out, int8_t *sq, uint32_t *spl, int (&qsum)[NB],
+                            float (&scale)[NB], float *red, int *ired, bool tapwg, float *r0_out, float *tap_h,
+                            float *tap_u, int8_t *tap_q, float *tap_s) {
+    const int tid = threadIdx.x;
+    const int e0 = prologue_elem<KCH>(0);
+    const bool mine = e0 < K;   // K is a multiple of 4*KCH: a thread has all of its chunks or none
+    for (int b = 0; b < NB; ++b) {
+        float4 hv[KCH];
+        if (mine) {
+            u32x4 r[2 * KCH];
+            f2_gather<KCH>(a, X + (int64_t)b * K + e0, tag, r);
+#pragma unroll
+            for (int i = 0; i < KCH; ++i)
+                hv[i] = make_float4(bitsf2(r[2 * i].x), bitsf2(r[2 * i].z), bitsf2(r[2 * i + 1].x), bitsf2(r[2 * i + 1].z));
+        } else {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) hv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float ss = 0.f;
+        if (pre_w) {
+            const float r0 = f2_norm_factor<KCH>(a, hv, K, red + 2 * kWaves);
+            if (r0_out && tid == 0) *r0_out = r0;
+            if (mine) {
+#pragma unroll
+                for (int i = 0; i < KCH; ++i) {
+                    const int e = prologue_elem<KCH>(i);
+                    const float4 w = *reinterpret_cast<const float4 *>(pre_w + e);
+                    hv[i].x = (hv[i].x * r0) * w.x;
+                    hv[i].y = (hv[i].y * r0) * w.y;
+                    hv[i].z = (hv[i].z * r0) * w.z;
+                    hv[i].w = (hv[i].w * r0) * w.w;
+                    if (tapwg && pre_out) *reinterpret_cast<float4 *>(pre_out + (int64_t)b * K + e) = hv[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) ss += f2_ss(hv[i]);
+        float pm = 0.f;
+        if (mine) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const int e = prologue_elem<KCH>(i);
+                if (tapwg && tap_h) *reinterpret_cast<float4 *>(tap_h + (int64_t)b * K + e) = hv[i];
+                const float4 w = wr[i];
+                hv[i].x = hv[i].x * w.x;
+                hv[i].y = hv[i].y * w.y;
+                hv[i].z = hv[i].z * w.z;
+                hv[i].w = hv[i].w * w.w;
+                pm = fmaxf(pm, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)), fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
+            }
+        }
+        // u = fl(fl(h * w) * r): with r > 0 the largest |u| is fl(max|h * w| * r) exactly
+        ss = f2_wave_sum(ss);
+        pm = f2_wave_max(pm);
+        if ((tid & 63) == 0) {
+            red[tid >> 6] = ss;
+            red[kWaves + (tid >> 6)] = pm;
+        }
+        __syncthreads();
+        const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+        pm = fmaxf(fmaxf(red[kWaves], red[kWaves + 1]), fmaxf(red[kWaves + 2], red[kWaves + 3]));
+        const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
+        const float amax = pm * r;
+        const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+        const float s = amax > 0.f ? amax / 127.0f : 0.f;
+        int qs = 0;
+        uint32_t pk[KCH];
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) pk[i] = 0;
+        if (mine) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const int e = prologue_elem<KCH>(i);
+                hv[i].x = hv[i].x * r;
+                hv[i].y = hv[i].y * r;
+                hv[i].z = hv[i].z * r;
+                hv[i].w = hv[i].w * r;
+                const int q0 = quant1(hv[i].x, inv), q1 = quant1(hv[i].y, inv);
+                const int q2 = quant1(hv[i].z, inv), q3 = quant1(hv[i].w, inv);
+                qs += q0 + q1 + q2 + q3;
+                const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
+                                        ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+                *reinterpret_cast<uint32_t *>(sq + b * K + e) = packed;
+                pk[i] = packed;
+                if (tapwg) {
+                    if (tap_u) *reinterpret_cast<float4 *>(tap_u + (int64_t)b * K + e) = hv[i];
+                    if (tap_q) *reinterpret_cast<uint32_t *>(tap_q + (int64_t)b * K + e) = packed;
+                }
+            }
+        }
+        {
+            uint32_t pw[8];
+            code_planes<KCH>(pk, pw);
+            constexpr int NL = KCH >= 8 ? 1 : 8 / KCH;   // threads per plane word
+            if (mine && tid % NL == 0) {
+                const int w = tid * KCH / 8, G32 = K >> 5;
+#pragma unroll
+                for (int p = 0; p < 8; ++p) spl[(b * 8 + p) * G32 + w] = pw[p];
+            }
+        }
+        qs = f2_wave_isum(qs);
+        if ((tid & 63) == 0) ired[b * kWaves + (tid >> 6)] = qs;
+        scale[b] = s;
+        if (tapwg && tap_s && tid == 0) tap_s[b] = s;
+        if (NB > 1) __syncthreads();   // red is reused by the next vector
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        qsum[b] = (ired[b * kWaves] + ired[b * kWaves + 1]) + (ired[b * kWaves + 2] + ired[b * kWaves + 3]);
+}
+
+// sum_k sgn * q of one 16-byte sign chunk against the bit-planes of the same 128 codes:
+// 2 * (sum over set bits of q) - sum(q) is finished by the caller; this returns sum over set bits.
+__device__ __forceinline__ int chunk_pos(const uint4 &bits, const uint4 (&pl)[8]) {
+    int pos = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int c = __popc(bits.x & pl[p].x) + __popc(bits.y & pl[p].y) + __popc(bits.z & pl[p].z) +
+                      __popc(bits.w & pl[p].w);
+        pos += p < 7 ? (c << p) : -(c << 7);
+    }
+    return pos;
+}
+
 __device__ __forceinline__ int sdot_chunk(const uint4 &w, const int4 &q, int acc) {
     acc = __builtin_amdgcn_sdot4((int)w.x, q.x, acc, false);
     acc = __builtin_amdgcn_sdot4((int)w.y, q.y, acc, false);
@@ -270,12 +371,38 @@ __device__ __forceinline__ int sdot_chunk(const uint4 &w, const int4 &q, int acc
     return acc;
 }
 
+// LoRA-down sums t[j] = L_dn[j] . q of a factor held in LDS ([rank][K] int8, rank <= 32) against
+// codes in LDS: the 32 lanes of group jg = tid / 32 take rows jg + 8 * jj (jj < 4), lane cl the
+// 16-byte chunks cl + 32 * m, so each code chunk is read once for four rows and all of a thread's
+// reads are issued before the first is used. The sums end in the group's last lane (cl == 31).
+template <int KCH>
+__device__ __forceinline__ void lora_down_sums(const char *ldn, const int8_t *q, int K, int rank, int (&part)[4]) {
+    const int jg = threadIdx.x >> 5, cl = threadIdx.x & 31, C16 = K >> 4;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) part[jj] = 0;
+    // no branches (they would split the reads into separately waited blocks): chunks past the row
+    // end are read clamped with zero codes, rows past the rank clamped (their sums are not used)
+#pragma unroll
+    for (int m = 0; m < 2 * KCH; ++m) {
+        const bool in = cl + 32 * m < C16;
+        const int cc = in ? cl + 32 * m : C16 - 1;
+        int4 qv = *reinterpret_cast<const int4 *>(q + cc * 16);
+        if (!in) qv = make_int4(0, 0, 0, 0);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            part[jj] = sdot_chunk(*reinterpret_cast<const uint4 *>(ldn + (size_t)min(jg + 8 * jj, rank - 1) * K + cc * 16), qv,
+                                  part[jj]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) part[jj] = dpp_group_sum(part[jj], 32);
+}
+
 template <int KCH>
 __device__ __forceinline__ void load_norm_w(float4 (&wr)[KCH], const float *w, int K) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
         const int e = prologue_elem<KCH>(i);
-        wr[i] = e < K ? *reinterpret_cast<const float4 *>(w + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+        wr[i] = e < K ? gld(reinterpret_cast<const float4 *>(w + e)) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 }
 
@@ -301,13 +428,12 @@ __device__ __forceinline__ float up_dot2(const int4 (&w)[F2_UPC], int rank, cons
     float lr = 0.f;
 #pragma unroll
     for (int i = 0; i < F2_UPC; ++i) {
-        if (i * 16 < rank) {
-            const int ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+        // no rank test: past the rank both the weights (zero-padded) and v (zeroed) are zero
+        const int ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) lr += (float)(int8_t)(ws[q] >> (8 * k)) * v[i * 16 + 4 * q + k];
-        }
+            for (int k = 0; k < 4; ++k) lr += (float)(int8_t)(ws[q] >> (8 * k)) * v[i * 16 + 4 * q + k];
     }
     return lr;
 }
@@ -318,9 +444,9 @@ __device__ __forceinline__ void load_up(int4 (&w)[F2_UPC], const int8_t *lora_up
     for (int i = 0; i < F2_UPC; ++i) {
         if (i * 16 < rank) {
             if (i * 16 + 16 <= rank) {
-                w[i] = reinterpret_cast<const int4 *>(p)[i];
+                w[i] = gld(reinterpret_cast<const int4 *>(p) + i);
             } else {   // rank 8: half a chunk
-                const int2 h = reinterpret_cast<const int2 *>(p)[2 * i];
+                const int2 h = gld(reinterpret_cast<const int2 *>(p) + 2 * i);
                 w[i] = make_int4(h.x, h.y, 0, 0);
             }
         } else {
@@ -371,18 +497,18 @@ __device__ __forceinline__ void load_row(RowRegs<NB> &R, const ItemRow &m, const
     const dfssm_proj &pin = Ly.w.in_proj;
     R.m = m;
     if (m.ch == -2) return;
-    R.scb = pin.row_scale[m.n];
-    R.us = pin.lora_up_scale[m.n];
+    R.scb = gld(pin.row_scale + m.n);
+    R.us = gld(pin.lora_up_scale + m.n);
     load_up(R.up, pin.lora_up, rank, m.n);
     if (m.ch >= 0) {
-        R.cw = *reinterpret_cast<const float4 *>(Ly.w.conv_w + (int64_t)m.ch * kConvTaps);
-        R.cb = Ly.w.conv_b[m.ch];
+        R.cw = gld(reinterpret_cast<const float4 *>(Ly.w.conv_w + (int64_t)m.ch * kConvTaps));
+        R.cb = gld(Ly.w.conv_b + m.ch);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const float *w = Ly.st.conv + ((int64_t)b * Cd + m.ch) * (kConvTaps - 1);
-            R.win[b][0] = w[0];
-            R.win[b][1] = w[1];
-            R.win[b][2] = w[2];
+            R.win[b][0] = gld(w);
+            R.win[b][1] = gld(w + 1);
+            R.win[b][2] = gld(w + 2);
         }
     }
 }
@@ -396,20 +522,20 @@ __device__ __forceinline__ float finish_row(const RowRegs<NB> &R, int b, int acc
     if (R.m.ch < 0) return yv;
     const float pre = R.cb + R.cw.x * R.win[b][0] + R.cw.y * R.win[b][1] + R.cw.z * R.win[b][2] + R.cw.w * yv;
     float *w = conv_state + ((int64_t)b * Cd + R.m.ch) * (kConvTaps - 1);
-    w[0] = R.win[b][1];
-    w[1] = R.win[b][2];
-    w[2] = yv;
+    gst(w, R.win[b][1]);
+    gst(w + 1, R.win[b][2]);
+    gst(w + 2, yv);
     return silu_f(pre);
 }
 
 template <int NB, int KCH1, int KCH2>
 __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     extern __shared__ __align__(16) char smem[];
-    __shared__ float red[2 * kWaves];
-    __shared__ int ired[kWaves];
-    __shared__ int sqsum[NB];
-    __shared__ float ssc[NB];
+    __shared__ float red[3 * kWaves];
+    __shared__ int ired[NB * kWaves];
     __shared__ float dtl[NB];
+    int sqsum[NB];
+    float ssc[NB];
     __shared__ float r0s;
     const int D = a.D, E = a.E, N = a.N, P = a.P;
     const int Kmax = D > E ? D : E;
@@ -427,6 +553,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     const dfssm_taps &T = a.taps;
     const int64_t n_tok = (int64_t)a.n_steps * L;
     const int nbc = 2 * a.G * N;
+    for (int i = tid; i < NB * 64; i += kBlock) tv[i] = 0.f;   // entries past the rank stay zero
     if (wg < a.n1) {
         // ====================================================================== role 1
         const int h = wg / a.S, p0 = (wg % a.S) * a.pr, g = h * a.G / a.H;
@@ -434,7 +561,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         const bool pad_rows = wg == 0 && T.in_acc != nullptr;
         const int R1t = a.R1 + (pad_rows ? a.npad : 0), nrest = R1t - q;
         const int CPR1 = D >> 7, NG1 = kBlock / CPR1, c1 = tid % CPR1, rg1 = tid / CPR1;
-        const int TPR1 = kBlock / a.Rin, j1 = tid / TPR1, cl1 = tid % TPR1, C16_1 = D >> 4;
+        const int C16_1 = D >> 4;
         const int N4 = N >> 2, nf = a.pr * N4;
         // the lane that completes a B/C row's sum also finishes that row; thread r finishes rest row q + r
         const bool bc_lane = c1 == CPR1 - 1 && rg1 < q;
@@ -463,18 +590,19 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         RowRegs<NB> rb, rr;
         float4 st[F2_FPT][NB];
         float4 wr[KCH1];
-        float dsc1 = 0.f, dtb = 0.f, alog = 0.f, Dh = 0.f;
+        float dsc1[4], dtb = 0.f, alog = 0.f, Dh = 0.f;
         auto prefetch = [&](int l) {
-            const Entry2 Ly = a.layers[l];
+            const Entry2 Ly = f2_entry(a, l);
             const dfssm_proj &pin = Ly.w.in_proj;
             // register loads first (their waits come at first use), then the direct-to-LDS copies
             load_norm_w<KCH1>(wr, Ly.w.norm_w, D);
-            dsc1 = pin.lora_dn_scale[j1];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dsc1[jj] = (tid >> 5) + 8 * jj < a.Rin ? gld(pin.lora_dn_scale + (tid >> 5) + 8 * jj) : 0.f;
             if (bc_lane) load_row(rb, m_bc, Ly, a.Rin, a.Cd);
             if (tid < nrest) load_row(rr, m_rest, Ly, a.Rin, a.Cd);
-            dtb = Ly.w.dt_bias[h];
-            alog = Ly.w.A_log[h];
-            Dh = Ly.w.D[h];
+            dtb = gld(Ly.w.dt_bias + h);
+            alog = gld(Ly.w.A_log + h);
+            Dh = gld(Ly.w.D + h);
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
                 const int f = tid + kBlock * i;
@@ -483,7 +611,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     st[i][b] = make_float4(0.f, 0.f, 0.f, 0.f);
                     if (i < a.fpt && f < nf) {
                         const int p = f / N4, n4 = f - p * N4;
-                        st[i][b] = reinterpret_cast<const float4 *>(Ly.st.ssm + (((int64_t)b * a.H + h) * P + p0 + p) * N)[n4];
+                        st[i][b] = gld(reinterpret_cast<const float4 *>(Ly.st.ssm + (((int64_t)b * a.H + h) * P + p0 + p) * N) + n4);
                     }
                 }
             }
@@ -499,9 +627,10 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             lds_copy_contig(ldn1, reinterpret_cast<const char *>(pin.lora_dn), a.Rin * C16_1);
         };
         prefetch(0);
-        for (int64_t it = 0; it < n_tok; ++it) {
-            const int t = (int)(it / L), l = (int)(it - (int64_t)t * L);
-            const Entry2 Ly = a.layers[l];
+        for (int t = 0; t < a.n_steps; ++t)
+        for (int l = 0; l < L; ++l) {
+            const int64_t it = (int64_t)t * L + l;
+            const Entry2 Ly = f2_entry(a, l);
             const uint32_t tag = (uint32_t)(it + 1);
             const int lp = l == 0 ? L - 1 : l - 1;
             const int64_t rec = it * B;
@@ -515,7 +644,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                 const bool fold = l == 0 && t > 0;   // the previous token's stack output through the final RMSNorm
                 f2_prologue<NB, KCH1>(a, hx_prev, D, tag - 1, wr, fold ? a.final_w : nullptr,
                                       fold ? a.y + (int64_t)(t - 1) * B * D : nullptr, sq, spl, sqsum, ssc, red, ired,
-                                      nullptr, wg == 0, fold ? &r0s : nullptr, T.h_in ? T.h_in + rec * D : nullptr,
+                                      wg == 0, fold ? &r0s : nullptr, T.h_in ? T.h_in + rec * D : nullptr,
                                       T.in_u ? T.in_u + rec * D : nullptr, T.in_q ? T.in_q + rec * D : nullptr,
                                       T.in_s ? T.in_s + rec : nullptr);
                 if (fold && wg == 0 && tid == 0) st_x(a.rx, tag2(fbits2(r0s), tag));
@@ -523,14 +652,17 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             // LoRA-down t[j] = L_dn[j] . q (sdot4, factors in LDS)
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                int part = 0;
-                for (int cc = cl1; cc < C16_1; cc += TPR1)
-                    part = sdot_chunk(*reinterpret_cast<const uint4 *>(ldn1 + (size_t)j1 * D + cc * 16),
-                                      *reinterpret_cast<const int4 *>(sq + b * D + cc * 16), part);
-                part = dpp_group_sum(part, TPR1);
-                if (cl1 == TPR1 - 1) {
-                    tv[b * 64 + j1] = dsc1 * ssc[b] * (float)part;
-                    if (wg == 0 && T.in_t) T.in_t[(rec + b) * a.Rin + j1] = part;
+                int part[4];
+                lora_down_sums<KCH1>(ldn1, sq + b * D, D, a.Rin, part);
+                if ((tid & 31) == 31) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int j = (tid >> 5) + 8 * jj;
+                        if (j < a.Rin) {
+                            tv[b * 64 + j] = dsc1[jj] * ssc[b] * (float)part[jj];
+                            if (wg == 0 && T.in_t) T.in_t[(rec + b) * a.Rin + j] = part[jj];
+                        }
+                    }
                 }
             }
             __syncthreads();
@@ -554,23 +686,20 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                             if (T.in_acc) T.in_acc[(rec + b) * a.Ninp + rb.m.n] = acc;
                         }
                     }
+                    // every sign chunk is read before the first is used (the row count is uniform)
+                    uint4 bits[F2_MAXI];
                     int pos[F2_MAXI];
 #pragma unroll
-                    for (int i = 0; i < F2_MAXI; ++i) {
-                        if (NG1 * i >= nrest) break;
-                        const int r = min(q + rg1 + NG1 * i, R1t - 1);
-                        pos[i] = chunk_pos(*reinterpret_cast<const uint4 *>(sgn1 + (size_t)r * (D >> 3) + c1 * 16), pl);
-                    }
+                    for (int i = 0; i < F2_MAXI; ++i)
+                        if (NG1 * i < nrest)
+                            bits[i] = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(q + rg1 + NG1 * i, R1t - 1) * (D >> 3) + c1 * 16);
+#pragma unroll
+                    for (int i = 0; i < F2_MAXI; ++i)
+                        if (NG1 * i < nrest) pos[i] = dpp_group_sum(chunk_pos(bits[i], pl), CPR1);
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i) {
-                        if (NG1 * i >= nrest) break;
-                        pos[i] = dpp_group_sum(pos[i], CPR1);
-                    }
-#pragma unroll
-                    for (int i = 0; i < F2_MAXI; ++i) {
-                        if (NG1 * i >= nrest) break;
                         const int r = rg1 + NG1 * i;
-                        if (c1 == CPR1 - 1 && r < nrest) accl[b * F2_ROWS + r] = 2 * pos[i] - sqsum[b];
+                        if (NG1 * i < nrest && c1 == CPR1 - 1 && r < nrest) accl[b * F2_ROWS + r] = 2 * pos[i] - sqsum[b];
                     }
                 }
             }
@@ -584,7 +713,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     if (T.in_acc) T.in_acc[(rec + b) * a.Ninp + rr.m.n] = acc;
                     if (r >= a.R1) continue;   // padding row
                     const float v = finish_row(rr, b, acc, ssc[b], tv + b * 64, a.Rin, Ly.st.conv, a.Cd);
-                    if (r < q + a.pr) zl[b * P + (r - q)] = v;
+                    if (r < q + a.pr) zl[b * P + (r - q)] = silu_f(v);   // the gate SiLU(z)
                     else if (r < q + 2 * a.pr) xl[b * P + (r - q - a.pr)] = v;
                     else dtl[b] = softplus_f(v + dtb);
                 }
@@ -602,30 +731,52 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             __syncthreads();
             // SSM update + readout, gate, publish g
             const float Ah = -expf(alog);
+            float dtv[NB], dAv[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                dtv[b] = dtl[b];
+                dAv[b] = expf(dtv[b] * Ah);
+            }
+            // every LDS operand first (one wait), then the updates; a thread's n4 is the same for
+            // all of its state rows (kBlock is a multiple of N / 4)
+            const int n4 = tid % N4;
+            float xs[F2_FPT][NB], zs[F2_FPT][NB];
+            float4 Bv[NB], Cv[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                Bv[b] = *reinterpret_cast<const float4 *>(Bl + b * N + n4 * 4);
+                Cv[b] = *reinterpret_cast<const float4 *>(Cl + b * N + n4 * 4);
+#pragma unroll
+                for (int i = 0; i < F2_FPT; ++i) {
+                    const int p = min((tid + kBlock * i) / N4, a.pr - 1);
+                    xs[i][b] = xl[b * P + p];
+                    zs[i][b] = zl[b * P + p];
+                }
+            }
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
                 if (i >= a.fpt) break;
                 const int f = tid + kBlock * i;
                 const bool ok = f < nf;
-                const int p = ok ? f / N4 : 0, n4 = ok ? f - p * N4 : 0;
+                const int p = ok ? f / N4 : 0;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    const float dt = dtl[b];
-                    const float dA = expf(dt * Ah);
-                    const float x = xl[b * P + p];
+                    const float dt = dtv[b];
+                    const float dA = dAv[b];
+                    const float x = xs[i][b];
                     const float dtx = dt * x;
-                    const float4 Bn = *reinterpret_cast<const float4 *>(Bl + b * N + n4 * 4);
-                    const float4 Cn = *reinterpret_cast<const float4 *>(Cl + b * N + n4 * 4);
+                    const float4 Bn = Bv[b];
+                    const float4 Cn = Cv[b];
                     float4 v = st[i][b];
                     v.x = dA * v.x + dtx * Bn.x;
                     v.y = dA * v.y + dtx * Bn.y;
                     v.z = dA * v.z + dtx * Bn.z;
                     v.w = dA * v.w + dtx * Bn.w;
-                    if (ok) reinterpret_cast<float4 *>(Ly.st.ssm + (((int64_t)b * a.H + h) * P + p0 + p) * N)[n4] = v;
+                    if (ok) gst(reinterpret_cast<float4 *>(Ly.st.ssm + (((int64_t)b * a.H + h) * P + p0 + p) * N) + n4, v);
                     float part = ok ? (v.x * Cn.x + v.y * Cn.y) + (v.z * Cn.z + v.w * Cn.w) : 0.f;
                     part = dpp_group_sum_f(part, N4);
                     if (ok && n4 == N4 - 1) {
-                        const float gv = (part + Dh * x) * silu_f(zl[b * P + p]);
+                        const float gv = (part + Dh * x) * zs[i][b];
                         st_x(gxl + (int64_t)b * E + h * P + p0 + p, tag2(fbits2(gv), tag));
                     }
                 }
@@ -633,8 +784,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             // ---- the next layer's weights and state, while the other role works on this one
             if (it + 1 < n_tok) {
                 __syncthreads();   // every wave is done with this layer's LDS
-                const int64_t nx = it + 1;
-                prefetch((int)(nx - (nx / L) * L));
+                prefetch(l + 1 < L ? l + 1 : 0);
             }
         }
         // the stack's final RMSNorm of the last token
@@ -656,7 +806,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
 #pragma unroll
                     for (int i = 0; i < KCH1; ++i) hv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
                 }
-                const float r0 = f2_norm_factor<KCH1>(a, hv, D, red);
+                const float r0 = f2_norm_factor<KCH1>(a, hv, D, red + 2 * kWaves);
                 if (mine) {
 #pragma unroll
                     for (int i = 0; i < KCH1; ++i) {
@@ -666,6 +816,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                             make_float4((hv[i].x * r0) * w.x, (hv[i].y * r0) * w.y, (hv[i].z * r0) * w.z, (hv[i].w * r0) * w.w);
                     }
                 }
+                __syncthreads();   // the reduction slots are reused by the next row
             }
         }
         return;
@@ -674,24 +825,25 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     const int w2 = wg - a.n1, n_out0 = w2 * a.R2;
     const int R2t = max(0, min(a.R2, D - n_out0));
     const int CPR2 = E >> 7, NG2 = kBlock / CPR2, c2 = tid % CPR2, rg2 = tid / CPR2;
-    const int TPR2 = kBlock / a.Rout, j2 = tid / TPR2, cl2 = tid % TPR2, C16_2 = E >> 4;
+    const int C16_2 = E >> 4;
     const bool tap2 = w2 == 0;
     char *sgn2 = wreg;
     char *ldn2 = wreg + f2_round_kb((size_t)a.R2 * (E >> 3));
     const int on = n_out0 + tid;
     const bool orow = tid < R2t;
-    float dsc2 = 0.f, ous = 0.f;
+    float dsc2[4], ous = 0.f;
     uint32_t oscb = 0;
     int4 oup[F2_UPC];
     float4 wr[KCH2];
     auto prefetch = [&](int l) {
-        const Entry2 Ly = a.layers[l];
+        const Entry2 Ly = f2_entry(a, l);
         const dfssm_proj &pout = Ly.w.out_proj;
         load_norm_w<KCH2>(wr, Ly.w.gnorm_w, E);
-        dsc2 = pout.lora_dn_scale[j2];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dsc2[jj] = (tid >> 5) + 8 * jj < a.Rout ? gld(pout.lora_dn_scale + (tid >> 5) + 8 * jj) : 0.f;
         if (orow) {
-            oscb = pout.row_scale[on];
-            ous = pout.lora_up_scale[on];
+            oscb = gld(pout.row_scale + on);
+            ous = gld(pout.lora_up_scale + on);
             load_up(oup, pout.lora_up, a.Rout, on);
         }
         if (R2t > 0)
@@ -704,8 +856,9 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     for (int b = 0; b < NB; ++b) hold[b] = orow ? a.x0[(int64_t)b * D + on] : 0.f;
     const float fw = orow ? a.final_w[on] : 0.f;
     prefetch(0);
-    for (int64_t it = 0; it < n_tok; ++it) {
-        const int t = (int)(it / L), l = (int)(it - (int64_t)t * L);
+    for (int t = 0; t < a.n_steps; ++t)
+    for (int l = 0; l < L; ++l) {
+        const int64_t it = (int64_t)t * L + l;
         const uint32_t tag = (uint32_t)(it + 1);
         const int64_t rec = it * B;
         const uint64_t *gxl = a.gx + (int64_t)l * B * E;
@@ -726,19 +879,22 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's direct-to-LDS copies are in
         __syncthreads();
-        f2_prologue<NB, KCH2>(a, gxl, E, tag, wr, nullptr, nullptr, sq, spl, sqsum, ssc, red, ired, nullptr, tap2, nullptr,
+        f2_prologue<NB, KCH2>(a, gxl, E, tag, wr, nullptr, nullptr, sq, spl, sqsum, ssc, red, ired, tap2, nullptr,
                               nullptr, T.out_u ? T.out_u + rec * E : nullptr, T.out_q ? T.out_q + rec * E : nullptr,
                               T.out_s ? T.out_s + rec : nullptr);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            int part = 0;
-            for (int cc = cl2; cc < C16_2; cc += TPR2)
-                part = sdot_chunk(*reinterpret_cast<const uint4 *>(ldn2 + (size_t)j2 * E + cc * 16),
-                                  *reinterpret_cast<const int4 *>(sq + b * E + cc * 16), part);
-            part = dpp_group_sum(part, TPR2);
-            if (cl2 == TPR2 - 1) {
-                tv[b * 64 + j2] = dsc2 * ssc[b] * (float)part;
-                if (tap2 && T.out_t) T.out_t[(rec + b) * a.Rout + j2] = part;
+            int part[4];
+            lora_down_sums<KCH2>(ldn2, sq + b * E, E, a.Rout, part);
+            if ((tid & 31) == 31) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = (tid >> 5) + 8 * jj;
+                    if (j < a.Rout) {
+                        tv[b * 64 + j] = dsc2[jj] * ssc[b] * (float)part[jj];
+                        if (tap2 && T.out_t) T.out_t[(rec + b) * a.Rout + j] = part[jj];
+                    }
+                }
             }
         }
         {
@@ -748,14 +904,18 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                 uint4 pl[8];
 #pragma unroll
                 for (int p = 0; p < 8; ++p) pl[p] = *reinterpret_cast<const uint4 *>(spl + (b * 8 + p) * G32 + c2 * 4);
+                uint4 bits[F2_MAXO];
+#pragma unroll
+                for (int i = 0; i < F2_MAXO; ++i)
+                    if (NG2 * i < a.R2)
+                        bits[i] = *reinterpret_cast<const uint4 *>(sgn2 + (size_t)min(rg2 + NG2 * i, max(R2t - 1, 0)) * (E >> 3) + c2 * 16);
 #pragma unroll
                 for (int i = 0; i < F2_MAXO; ++i) {
-                    if (NG2 * i >= a.R2) break;
-                    const int r = rg2 + NG2 * i;
-                    const uint4 bits = *reinterpret_cast<const uint4 *>(sgn2 + (size_t)min(r, max(R2t - 1, 0)) * (E >> 3) + c2 * 16);
-                    int pos = chunk_pos(bits, pl);
-                    pos = dpp_group_sum(pos, CPR2);
-                    if (c2 == CPR2 - 1 && r < R2t) accl[b * F2_ROWS + r] = 2 * pos - sqsum[b];
+                    if (NG2 * i < a.R2) {
+                        const int r = rg2 + NG2 * i;
+                        const int pos = dpp_group_sum(chunk_pos(bits[i], pl), CPR2);
+                        if (c2 == CPR2 - 1 && r < R2t) accl[b * F2_ROWS + r] = 2 * pos - sqsum[b];
+                    }
                 }
             }
         }
@@ -773,8 +933,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         }
         if (it + 1 < n_tok) {
             __syncthreads();   // every wave is done with this layer's LDS
-            const int64_t nx = it + 1;
-            prefetch((int)(nx - (nx / L) * L));
+            prefetch(l + 1 < L ? l + 1 : 0);
         }
     }
 }
@@ -783,17 +942,20 @@ __global__ void k_store2(Entry2 *dst, Chunk2 c, int n) {
     if ((int)threadIdx.x < n) dst[threadIdx.x] = c.e[threadIdx.x];
 }
 
+// The exchange words are cleared (and seeded) with the same agent-coherent stores the exchange
+// itself uses, so no earlier run's tagged words can be observed by the polling loads.
 __global__ void k_zero2(uint64_t *p, int64_t n, int *err, uint64_t *rx) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        st_x(p + i, (uint64_t)0);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-        *err = 0;
-        *rx = 0;
+        st_x(err, 0);
+        st_x(rx, (uint64_t)0);
     }
 }
 
 __global__ void k_seed2(uint64_t *hx_last, const float *x0, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        hx_last[i] = (uint64_t)__builtin_bit_cast(uint32_t, x0[i]);
+        st_x(hx_last + i, (uint64_t)__builtin_bit_cast(uint32_t, x0[i]));
 }
 
 bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
