@@ -772,13 +772,24 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     v.y = dA * v.y + dtx * Bn.y;
                     v.z = dA * v.z + dtx * Bn.z;
                     v.w = dA * v.w + dtx * Bn.w;
-                    if (ok) gst(reinterpret_cast<float4 *>(Ly.st.ssm + (((int64_t)b * a.H + h) * P + p0 + p) * N) + n4, v);
+                    st[i][b] = v;
                     float part = ok ? (v.x * Cn.x + v.y * Cn.y) + (v.z * Cn.z + v.w * Cn.w) : 0.f;
                     part = dpp_group_sum_f(part, N4);
                     if (ok && n4 == N4 - 1) {
                         const float gv = (part + Dh * x) * zs[i][b];
                         st_x(gxl + (int64_t)b * E + h * P + p0 + p, tag2(fbits2(gv), tag));
                     }
+                }
+            }
+            // the new state goes out after the gated outputs, so that those are not queued behind it
+#pragma unroll
+            for (int i = 0; i < F2_FPT; ++i) {
+                const int f = tid + kBlock * i;
+                if (i < a.fpt && f < nf) {
+                    const int p = f / N4;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        gst(reinterpret_cast<float4 *>(Ly.st.ssm + (((int64_t)b * a.H + h) * P + p0 + p) * N) + n4, st[i][b]);
                 }
             }
             // ---- the next layer's weights and state, while the other role works on this one
