@@ -58,9 +58,10 @@ def bytes_per_token(d, n_layers: int) -> dict:
     return {"per_layer": per_layer, "layer_total": sum(per_layer.values()), "token_total": total}
 
 
-# the sources the persistent stack kernel is compiled from
-STACK_SOURCES = ("bit_quantized_mamba_packed_amd/csrc/stack.hip", "bit_quantized_mamba_packed_amd/csrc/decode_device.h",
+# the sources the persistent batch-1 stack kernel (k_flow2) is compiled from
+STACK_SOURCES = ("bit_quantized_mamba_packed_amd/csrc/flow2.hip", "bit_quantized_mamba_packed_amd/csrc/decode_device.h",
                  "bit_quantized_mamba_packed_amd/csrc/dfssm_internal.h", "include/dfssm.h")
+STACK_KERNEL = "k_flow2"
 
 
 def kernel_source_hash() -> str:
@@ -96,7 +97,7 @@ def write_counters(fetch_csv: str, write_csv: str, tokens: int) -> dict:
 
     def pick(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        kern = [float(r["Counter_Value"]) for r in rows if "k_stack_flow" in r["Kernel_Name"]]
+        kern = [float(r["Counter_Value"]) for r in rows if STACK_KERNEL in r["Kernel_Name"]]
         copy = [float(r["Counter_Value"]) for r in rows
                 if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 100000]
         if len(kern) != 1 or len(copy) != 1:
@@ -202,7 +203,7 @@ def run_decode_b1(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
                    "rank": dims.rank_in},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
-                     "kernel": "k_stack_flow (persistent, one launch per step)",
+                     "kernel": "k_flow2 (persistent, role-split, one launch per step)",
                      "algorithmic_bytes_per_launch": bpt["token_total"] * T,
                      "avg_launch_ms": round(avg_launch_s * 1e3, 3)},
     }
