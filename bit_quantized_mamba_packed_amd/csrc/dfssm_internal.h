@@ -126,7 +126,7 @@ struct PrefillWs {
     float *s_in, *s_out;
     int32_t *qsum_in, *qsum_out;
     __bf16 *thi_in, *tlo_in, *thi_out, *tlo_out;
-    float *Y, *xbc, *dt, *lam, *lam_end, *cb, *ydiag, *sloc, *gbuf;
+    float *Y, *xbc, *dt, *cb, *lam_end, *sloc, *gbuf;
     void *gemm_scratch;    // split-K scratch shared by the two projections (they run one after the other)
     size_t bytes;
 };

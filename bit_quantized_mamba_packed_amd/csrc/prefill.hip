@@ -7,14 +7,13 @@
 //   2 k_gemm_pm1       in_proj over all tokens (int8 MFMA) with the Eq. (3) epilogue -> Y
 //   3 k_conv_seq       causal conv over the sequence + SiLU (x, B, C); softplus(dt + dt_bias)
 //   4 k_conv_handoff   final conv state = the last d_conv-1 pre-activation inputs
-//   5 SSD, chunk length Q, Lam_t = sum_{tau <= t in chunk} dt_tau A (per head):
-//       k_ssd_lam      Lam within each chunk and its end value
-//       k_ssd_cb       CB[t][s] = C_t . B_s for each chunk and group (shared by the group's heads)
-//       k_ssd_ydiag    Y_diag[t] = sum_{s <= t} exp(Lam_t - Lam_s) CB[t][s] dt_s x_s
-//       k_ssd_sloc     S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s
+//   5 SSD, chunk length Q, Lam_t = sum_{tau <= t in chunk} dt_tau A (per head), fp32 MFMA:
+//       k_ssd_cbm      CB[t][s] = C_t . B_s for each chunk and group (shared by the group's heads)
+//       k_ssd_state    S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s per chunk, and Lam_end
 //       k_ssd_scan     S_in(c) = state entering chunk c; S <- exp(Lam_end) S + S_loc (sequential in c)
-//       k_ssd_yoff     y = Y_diag + exp(Lam_t) C_t . S_in + D x; g = y * SiLU(z)
-//     (exponentials are always taken of differences of Lam)
+//       k_ssd_out      y = sum_{s <= t} exp(Lam_t - Lam_s) CB[t][s] dt_s x_s + exp(Lam_t) C_t . S_in
+//                      + D x; g = y * SiLU(z)
+//     (exponentials only of Lam differences, or of Lam itself: never positive)
 //   6 k_tok_quant      gated RMSNorm + quantizer + LoRA-down of g
 //   7 k_gemm_pm1       out_proj with the residual add -> x_out
 #include "decode_device.h"
@@ -22,8 +21,6 @@
 namespace dfssm {
 
 namespace {
-
-constexpr int TT = 64;  // token / feature tile of the SSD kernels
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
 
@@ -194,191 +191,149 @@ struct SsdArgs {
     const float *A_log, *D;
     const float *Y;        // in_proj output (z at columns [0, E))
     int64_t ldY;
-    float *lam;            // [B][H][L]
-    float *lam_end;        // [B][H][nch]
-    float *cb;             // [B][G][nch][Q][Q]
-    float *ydiag;          // [M][E]
-    float *sloc;           // [B][H][nch][P][N]  (becomes the state entering each chunk)
+    float *cb;             // [B][G][nch][Q][Q]: CB[t][s] = C_t . B_s (s-tiles <= t-tile)
+    float *lam_end;        // [B][H][nch] Lam at each chunk's last token
+    float *sloc;           // [B][H][nch][P][N] chunk states (become the states entering each chunk)
     float *state;          // [B][H][P][N] initial -> final
     float *g;              // [M][E] gated output
 };
 
-// Lam_t = inclusive cumsum of dt_t * A within each chunk: one workgroup per (b, h, c), one token
-// per thread (chunk <= 256), wave scans combined through LDS.
-__global__ __launch_bounds__(kBlock) void k_ssd_lam(SsdArgs a) {
-    __shared__ float wsum[kWaves];
-    const int idx = blockIdx.x;  // (b, h, c)
-    const int c = idx % a.nch, bh = idx / a.nch, h = bh % a.H, b = bh / a.H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t = c * a.Q + tid;
-    const bool ok = tid < a.Q && t < a.L;
-    const float A = -expf(a.A_log[h]);
-    float v = ok ? a.dt[((int64_t)b * a.L + t) * a.H + h] * A : 0.f;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
-    if (lane == 63) wsum[wave] = v;
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) v += wsum[w];
-    if (ok) a.lam[((int64_t)b * a.H + h) * a.L + t] = v;
-    const int last = min(a.Q, a.L - c * a.Q) - 1;
-    if (tid == last) a.lam_end[idx] = v;
-}
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f4v mfma4(float a, float b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
 
-// CB tile (ti, si) of chunk c for group g: 64 x 64 outputs, 4 x 4 per thread, N in tiles of 64.
-__global__ __launch_bounds__(kBlock) void k_ssd_cb(SsdArgs a) {
-    __shared__ __align__(16) float Cs[TT][TT + 4];  // [n][t]
-    __shared__ __align__(16) float Bs[TT][TT + 4];  // [n][s]
-    const int tq = (a.Q + TT - 1) / TT;
-    const int ti = blockIdx.y / tq, si = blockIdx.y % tq;
+// The fp32 MFMA 16x16x4 takes A[i][k] from lane i + 16k, B[k][j] from lane j + 16k and leaves
+// D[4(l/16) + r][l % 16] in lane l, element r. Where both operands are contiguous along the
+// contraction index, lane l reads four consecutive k as one float4 and feeds component j to the
+// j-th of four MFMAs: logical k = l / 16 of MFMA j is physical index 4 (l / 16) + j for A and B
+// alike, so the four MFMAs cover 16 consecutive k exactly once.
+
+// CB[t][s] = C_t . B_s of one 16-token t-tile of chunk c, group g: wave w takes the s-tiles
+// w, w + 4, ... <= the t-tile (only those are read).
+__global__ __launch_bounds__(kBlock) void k_ssd_cbm(SsdArgs a) {
     const int bgc = blockIdx.x, c = bgc % a.nch, g = (bgc / a.nch) % a.G, b = bgc / (a.nch * a.G);
-    if (si > ti) return;
-    const int len = min(a.Q, a.L - c * a.Q);
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    float acc[4][4] = {};
-    const int64_t mbase = (int64_t)b * a.L + c * a.Q;
-    for (int n0 = 0; n0 < a.N; n0 += TT) {
-        for (int k = tid; k < TT * TT; k += kBlock) {
-            const int r = k / TT, n = k % TT;  // r: token row within the tile
-            const int tt = ti * TT + r, ss = si * TT + r;
-            const bool nin = n0 + n < a.N;  // d_state below 64 leaves part of the tile empty
-            Cs[n][r] = nin && tt < len ? a.xbc[(mbase + tt) * a.Cd + a.E + a.G * a.N + g * a.N + n0 + n] : 0.f;
-            Bs[n][r] = nin && ss < len ? a.xbc[(mbase + ss) * a.Cd + a.E + g * a.N + n0 + n] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int n = 0; n < TT; ++n) {
-            const float4 cv = *reinterpret_cast<const float4 *>(&Cs[n][ty * 4]);
-            const float4 bv = *reinterpret_cast<const float4 *>(&Bs[n][tx * 4]);
-            const float cr[4] = {cv.x, cv.y, cv.z, cv.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += cr[i] * br[j];
-        }
-        __syncthreads();
-    }
-    float *out = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * a.Q * a.Q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = ti * TT + ty * 4 + i;
-        if (t >= a.Q) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int s = si * TT + tx * 4 + j;
-            if (s < a.Q) out[(int64_t)t * a.Q + s] = acc[i][j];
-        }
-    }
-}
-
-// Y_diag for token tile ti of chunk c, head h: 64 tokens x P(=64) features, 4 x 4 per thread.
-__global__ __launch_bounds__(kBlock) void k_ssd_ydiag(SsdArgs a) {
-    __shared__ __align__(16) float Ws[TT][TT + 4];  // [s][t]
-    __shared__ __align__(16) float Xs[TT][TT + 4];  // [s][p]
-    __shared__ float lam_t[TT], lam_s[TT], dts[TT];
-    const int tq = (a.Q + TT - 1) / TT;
     const int ti = blockIdx.y;
-    const int bhc = blockIdx.x, c = bhc % a.nch, h = (bhc / a.nch) % a.H, b = bhc / (a.nch * a.H);
-    if (ti >= tq) return;
     const int len = min(a.Q, a.L - c * a.Q);
-    if (ti * TT >= len) return;
-    const int g = h * a.G / a.H;
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    if (ti * 16 >= len) return;   // no barriers in this kernel
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, kq = lane >> 4;
     const int64_t mbase = (int64_t)b * a.L + c * a.Q;
-    const float *lamh = a.lam + ((int64_t)b * a.H + h) * a.L + c * a.Q;
-    const float *cbc = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * a.Q * a.Q;
-    if (tid < TT) lam_t[tid] = ti * TT + tid < len ? lamh[ti * TT + tid] : 0.f;
-    float acc[4][4] = {};
-    for (int si = 0; si <= ti; ++si) {
-        __syncthreads();
-        if (tid < TT) {
-            const int s = si * TT + tid;
-            lam_s[tid] = s < len ? lamh[s] : 0.f;
-            dts[tid] = s < len ? a.dt[(mbase + s) * a.H + h] : 0.f;
+    const float *Crow = a.xbc + (mbase + min(ti * 16 + r, len - 1)) * a.Cd + a.E + a.G * a.N + g * a.N + 4 * kq;
+    float *out = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * a.Q * a.Q;
+    for (int si = wave; si <= ti; si += kWaves) {
+        const float *Brow = a.xbc + (mbase + min(si * 16 + r, len - 1)) * a.Cd + a.E + g * a.N + 4 * kq;
+        f4v acc = {0.f, 0.f, 0.f, 0.f};
+        for (int n0 = 0; n0 < a.N; n0 += 16) {
+            const float4 cv = *reinterpret_cast<const float4 *>(Crow + n0);
+            const float4 bv = *reinterpret_cast<const float4 *>(Brow + n0);
+            acc = mfma4(cv.x, bv.x, acc);
+            acc = mfma4(cv.y, bv.y, acc);
+            acc = mfma4(cv.z, bv.z, acc);
+            acc = mfma4(cv.w, bv.w, acc);
         }
-        __syncthreads();
-        for (int k = tid; k < TT * TT; k += kBlock) {
-            const int r = k / TT, q = k % TT;
-            // W[t=r][s=q] = CB * exp(lam_t - lam_s) * dt_s  for s <= t (both inside the chunk)
-            const int t = ti * TT + r, s = si * TT + q;
-            float wv = 0.f;
-            if (s <= t && t < len) wv = cbc[(int64_t)t * a.Q + s] * expf(lam_t[r] - lam_s[q]) * dts[q];
-            Ws[q][r] = wv;
-            Xs[r][q] = si * TT + r < len ? a.xbc[(mbase + si * TT + r) * a.Cd + h * a.P + q] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int s = 0; s < TT; ++s) {
-            const float4 wv = *reinterpret_cast<const float4 *>(&Ws[s][ty * 4]);
-            const float4 xv = *reinterpret_cast<const float4 *>(&Xs[s][tx * 4]);
-            const float wr[4] = {wv.x, wv.y, wv.z, wv.w}, xr[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += wr[i] * xr[j];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = ti * TT + ty * 4 + i;
-        if (t >= len) continue;
-        *reinterpret_cast<float4 *>(a.ydiag + (mbase + t) * a.E + h * a.P + tx * 4) =
-            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        for (int rr = 0; rr < 4; ++rr) out[(int64_t)(ti * 16 + 4 * kq + rr) * a.Q + si * 16 + r] = acc[rr];
     }
 }
 
-// Chunk-local state S_loc[p][n] = sum_s exp(Lam_end - Lam_s) dt_s x_s[p] B_s[n] for (b, h, c):
-// a (P x chunk) x (chunk x N) product, 64 x 64 outputs per workgroup (4 x 4 per thread), s in tiles of 64.
-__global__ __launch_bounds__(kBlock) void k_ssd_sloc(SsdArgs a) {
-    __shared__ __align__(16) float Xw[TT][TT + 4];  // [s][p], scaled by the decay weight
-    __shared__ __align__(16) float Bs[TT][TT + 4];  // [s][n]
-    __shared__ float wgt[TT];
-    const int bhc = blockIdx.x, c = bhc % a.nch, h = (bhc / a.nch) % a.H, b = bhc / (a.nch * a.H);
-    const int n0 = blockIdx.y * TT;
-    const int len = min(a.Q, a.L - c * a.Q);
-    const int g = h * a.G / a.H;
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    const int64_t mbase = (int64_t)b * a.L + c * a.Q;
-    const float *lamh = a.lam + ((int64_t)b * a.H + h) * a.L + c * a.Q;
-    const float lend = a.lam_end[((int64_t)b * a.H + h) * a.nch + c];
-    float acc[4][4] = {};
-    for (int s0 = 0; s0 < len; s0 += TT) {
-        __syncthreads();
-        if (tid < TT) {
-            const int s = s0 + tid;
-            wgt[tid] = s < len ? expf(lend - lamh[s]) * a.dt[(mbase + s) * a.H + h] : 0.f;
-        }
-        __syncthreads();
-        for (int k = tid; k < TT * TT; k += kBlock) {
-            const int r = k / TT, q = k % TT;  // r: token within the tile, q: feature
-            const int s = s0 + r;
-            const bool sin_ = s < len;
-            Xw[r][q] = sin_ ? a.xbc[(mbase + s) * a.Cd + h * a.P + q] * wgt[r] : 0.f;
-            Bs[r][q] = sin_ && n0 + q < a.N ? a.xbc[(mbase + s) * a.Cd + a.E + g * a.N + n0 + q] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int r = 0; r < TT; ++r) {
-            const float4 xv = *reinterpret_cast<const float4 *>(&Xw[r][ty * 4]);
-            const float4 bv = *reinterpret_cast<const float4 *>(&Bs[r][tx * 4]);
-            const float xr[4] = {xv.x, xv.y, xv.z, xv.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+// Chunked SSD in three passes, each over every (b, h, chunk) at once (Lam_t = inclusive cumsum of
+// dt A within the chunk; exponentials only of Lam differences, or of Lam itself, all <= 0; fp32
+// MFMA 16x16x4; eight waves per workgroup, all P = 64 channels of the head, so every A operand
+// feeds four MFMAs, one per 16-channel tile):
+//   k_ssd_state  S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s of the chunk, and Lam_end
+//   k_ssd_scan   S_in(c) = exp(Lam_end(c-1)) S_in(c-1) + S_loc(c-1), in place (sequential in c)
+//   k_ssd_out    y_t = sum_{s<=t} exp(Lam_t - Lam_s) CB[t][s] dt_s x_s + exp(Lam_t) C_t . S_in + D x_t,
+//                g = y SiLU(z)
+constexpr int kSsdMaxQ = 256, kSsdMaxN = 256, kSsdP = 64, kSsdWaves = 8, kSsdBlock = 64 * kSsdWaves;
+
+// Per-chunk prologue shared by the state and output passes: Lam (in log2 units) and dt of the
+// chunk's tokens, and x of the head transposed to Xt[p][t] (zero past the chunk end). Q <=
+// kSsdBlock / 2; one barrier inside, one at the end.
+__device__ __forceinline__ void ssd_chunk_prologue(const SsdArgs &a, int h, int64_t mbase, int len, float *lam2,
+                                                   float *dts, float (*Xt)[kSsdMaxQ + 4], float *tot) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float A = -expf(a.A_log[h]);
+    const bool in = tid < len;
+    const float dtv = in ? a.dt[(mbase + tid) * a.H + h] : 0.f;
+    float v = dtv * A;
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+    if (lane == 63) tot[wave] = v;
+    // x: thread (t, quarter) loads 16 channels of token t
+    const int t = tid & 255, pq = tid >> 8;   // kSsdBlock = 512: two threads per token, 32 channels each
+    float4 xv[8];
+    if (t < a.Q) {
+        const float *xr = a.xbc + (mbase + min(t, len - 1)) * a.Cd + h * a.P + 32 * pq;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 8; ++j) xv[j] = *reinterpret_cast<const float4 *>(xr + 4 * j);
+    }
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) v += tot[w];
+    if (tid < a.Q) {
+        constexpr float kLog2e = 1.4426950408889634f;
+        lam2[tid] = v * kLog2e;
+        dts[tid] = dtv;
+    }
+    if (t < a.Q) {
+        const bool tin = t < len;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += xr[i] * br[j];
+        for (int j = 0; j < 8; ++j) {
+            if (!tin) xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            Xt[32 * pq + 4 * j][t] = xv[j].x;
+            Xt[32 * pq + 4 * j + 1][t] = xv[j].y;
+            Xt[32 * pq + 4 * j + 2][t] = xv[j].z;
+            Xt[32 * pq + 4 * j + 3][t] = xv[j].w;
         }
     }
-    float *out = a.sloc + (((int64_t)b * a.H + h) * a.nch + c) * a.P * a.N;
+    __syncthreads();
+}
+
+// S_loc of one (b, h, chunk): x is pre-scaled by wend_s = exp(Lam_end - Lam_s) dt_s in LDS. Wave w
+// takes the n-tiles w, w + 8, ... for all four p-tiles, so each B value (read from global in the
+// standard operand layout, 16 tokens at a time) feeds four MFMAs.
+__global__ __launch_bounds__(kSsdBlock) void k_ssd_state(SsdArgs a) {
+    __shared__ float lam2[kSsdMaxQ], dts[kSsdMaxQ], tot[kSsdWaves];
+    __shared__ __align__(16) float Xt[kSsdP][kSsdMaxQ + 4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kq = lane >> 4;
+    const int c = blockIdx.x % a.nch, bh = blockIdx.x / a.nch, h = bh % a.H, b = bh / a.H;
+    const int g = h * a.G / a.H, Q = a.Q, N = a.N, NT = N / 16;
+    const int len = min(Q, a.L - c * Q);
+    const int64_t mbase = (int64_t)b * a.L + c * Q;
+    ssd_chunk_prologue(a, h, mbase, len, lam2, dts, Xt, tot);
+    const float lend2 = lam2[len - 1];
+    for (int i = tid; i < kSsdP * Q; i += kSsdBlock) {   // x_s * wend_s (zero past the chunk end: dts = 0)
+        const int p = i / Q, t = i - p * Q;
+        Xt[p][t] *= __builtin_amdgcn_exp2f(lend2 - lam2[t]) * dts[t];
+    }
+    if (tid == 0) a.lam_end[(int64_t)bh * a.nch + c] = lend2 * 0.6931471805599453f;
+    __syncthreads();
+    const float *Bbase = a.xbc + mbase * a.Cd + a.E + g * N;
+    float *out = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
+    for (int nt = wave; nt < NT; nt += kSsdWaves) {
+        f4v acc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = ty * 4 + i;
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = f4v{0.f, 0.f, 0.f, 0.f};
+        const float *bcol = Bbase + nt * 16 + r;
+        for (int s0 = 0; s0 < Q; s0 += 16) {
+            float bq[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + tx * 4 + j;
-            if (n < a.N) out[(int64_t)p * a.N + n] = acc[i][j];
+            for (int v = 0; v < 4; ++v) bq[v] = bcol[(int64_t)min(s0 + 4 * kq + v, len - 1) * a.Cd];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const float4 xv = *reinterpret_cast<const float4 *>(&Xt[16 * pt + r][s0 + 4 * kq]);
+                acc[pt] = mfma4(xv.x, bq[0], acc[pt]);
+                acc[pt] = mfma4(xv.y, bq[1], acc[pt]);
+                acc[pt] = mfma4(xv.z, bq[2], acc[pt]);
+                acc[pt] = mfma4(xv.w, bq[3], acc[pt]);
+            }
         }
+        // lane l holds S_loc[p = 16 pt + 4 kq + rr][n = 16 nt + r]
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) out[(int64_t)(16 * pt + 4 * kq + rr) * N + nt * 16 + r] = acc[pt][rr];
     }
 }
 
@@ -398,56 +353,119 @@ __global__ __launch_bounds__(kBlock) void k_ssd_scan(SsdArgs a) {
     a.state[(int64_t)bh * PN + e] = S;
 }
 
-// y = Y_diag + exp(Lam_t) C_t . S_in + D x ; g = y * SiLU(z), token tile ti of chunk c, head h.
-__global__ __launch_bounds__(kBlock) void k_ssd_yoff(SsdArgs a) {
-    __shared__ __align__(16) float Cs[TT][TT + 4];  // [n][t]
-    __shared__ __align__(16) float Ss[TT][TT + 4];  // [n][p]
-    const int tq = (a.Q + TT - 1) / TT;
-    const int ti = blockIdx.y;
-    const int bhc = blockIdx.x, c = bhc % a.nch, h = (bhc / a.nch) % a.H, b = bhc / (a.nch * a.H);
-    const int len = min(a.Q, a.L - c * a.Q);
-    if (ti >= tq || ti * TT >= len) return;
-    const int g = h * a.G / a.H;
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    const int64_t mbase = (int64_t)b * a.L + c * a.Q;
-    const float *sin = a.sloc + (((int64_t)b * a.H + h) * a.nch + c) * a.P * a.N;
-    float acc[4][4] = {};
-    for (int n0 = 0; n0 < a.N; n0 += TT) {
-        __syncthreads();
-        for (int k = tid; k < TT * TT; k += kBlock) {
-            const int r = k / TT, n = k % TT;
-            const int t = ti * TT + r;
-            const bool nin = n0 + n < a.N;
-            Cs[n][r] = nin && t < len ? a.xbc[(mbase + t) * a.Cd + a.E + a.G * a.N + g * a.N + n0 + n] : 0.f;
-            Ss[n][r] = nin ? sin[(int64_t)r * a.N + n0 + n] : 0.f;   // r is p here (P == 64)
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int n = 0; n < TT; ++n) {
-            const float4 cv = *reinterpret_cast<const float4 *>(&Cs[n][ty * 4]);
-            const float4 sv = *reinterpret_cast<const float4 *>(&Ss[n][tx * 4]);
-            const float cr[4] = {cv.x, cv.y, cv.z, cv.w}, sr[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += cr[i] * sr[j];
+// Outputs of one (b, h, chunk): wave w owns the t-tiles {w, 15 - w, 16 + w, 31 - w, ...} (balanced
+// causal work) and all four p-tiles of each. Per tile (rows t, first row r0 = 16 ti) three
+// accumulations, each scaled per row at the end:
+//   yo = C_t . S_in                      (x exp(Lam_t))
+//   yc = sum_{s < r0} CB[t][s] x_s u_s,  u_s = dt_s exp(Lam_r0 - Lam_s)   (x exp(Lam_t - Lam_r0))
+//   yd = sum_{r0 <= s <= t} exp(Lam_t - Lam_s) CB[t][s] dt_s x_s          (the diagonal block)
+// Every factor is an exponential of a non-positive number. The state S_in comes through LDS as
+// Sl[p][n]; C and CB rows are read straight from global memory (float4 along the contraction).
+__global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
+    __shared__ float lam2[kSsdMaxQ], dts[kSsdMaxQ], tot[kSsdWaves];
+    __shared__ __align__(16) float Xt[kSsdP][kSsdMaxQ + 4];
+    __shared__ __align__(16) float Sl[kSsdP][kSsdMaxN + 4];   // [p][n] the state entering the chunk
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kq = lane >> 4;
+    const int c = blockIdx.x % a.nch, bh = blockIdx.x / a.nch, h = bh % a.H, b = bh / a.H;
+    const int g = h * a.G / a.H, Q = a.Q, N = a.N, QT = Q / 16, NT = N / 16;
+    const int len = min(Q, a.L - c * Q);
+    const int64_t mbase = (int64_t)b * a.L + c * Q;
+    const float Dh = a.D[h];
+    {
+        const float *sin = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
+        for (int i = tid; i < kSsdP * N / 4; i += kSsdBlock) {
+            const int p = (4 * i) / N, n = (4 * i) % N;
+            *reinterpret_cast<float4 *>(&Sl[p][n]) = *reinterpret_cast<const float4 *>(sin + (int64_t)p * N + n);
         }
     }
-    const float *lamh = a.lam + ((int64_t)b * a.H + h) * a.L + c * a.Q;
-    const float Dh = a.D[h];
+    ssd_chunk_prologue(a, h, mbase, len, lam2, dts, Xt, tot);
+    for (int ti = 0; ti < QT; ++ti) {
+        const int owner = ((ti >> 3) & 1) ? 7 - (ti & 7) : (ti & 7);
+        if (owner != wave || ti * 16 >= len) continue;
+        const int t = min(ti * 16 + r, len - 1);   // the A-operand row this lane supplies
+        const float lt = lam2[t], lr0 = lam2[ti * 16];
+        const float *Crow = a.xbc + (mbase + t) * a.Cd + a.E + a.G * N + g * N + 4 * kq;
+        const float *cbrow = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * Q * Q + (int64_t)t * Q + 4 * kq;
+        f4v yo[4], yc[4], yd[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = ti * TT + ty * 4 + i;
-        if (t >= len) continue;
-        const int64_t m = mbase + t;
-        const float el = expf(lamh[t]);
+        for (int pt = 0; pt < 4; ++pt) yo[pt] = yc[pt] = yd[pt] = f4v{0.f, 0.f, 0.f, 0.f};
+        // C_t . S_in, 64 n at a time (four float4 of C per lane in flight)
+        for (int n0 = 0; n0 < N; n0 += 64) {
+            float4 cv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = tx * 4 + j;
-            const int64_t col = h * a.P + p;
-            const float x = a.xbc[m * a.Cd + col];
-            const float y = a.ydiag[m * a.E + col] + el * acc[i][j] + Dh * x;
-            a.g[m * a.E + col] = y * silu_f(a.Y[m * a.ldY + col]);
+            for (int u = 0; u < 4; ++u) cv[u] = *reinterpret_cast<const float4 *>(Crow + min(n0 + 16 * u, N - 16));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (n0 + 16 * u < N) {
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const float4 sv = *reinterpret_cast<const float4 *>(&Sl[16 * pt + r][n0 + 16 * u + 4 * kq]);
+                        yo[pt] = mfma4(cv[u].x, sv.x, yo[pt]);
+                        yo[pt] = mfma4(cv[u].y, sv.y, yo[pt]);
+                        yo[pt] = mfma4(cv[u].z, sv.z, yo[pt]);
+                        yo[pt] = mfma4(cv[u].w, sv.w, yo[pt]);
+                    }
+                }
+            }
+        }
+        // the blocks below the diagonal, 4 s-tiles (64 tokens) at a time
+        for (int j0 = 0; j0 < ti; j0 += 4) {
+            float4 cbv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cbv[u] = *reinterpret_cast<const float4 *>(cbrow + 16 * min(j0 + u, ti - 1));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (j0 + u < ti) {
+                    const int s0 = (j0 + u) * 16 + 4 * kq;
+                    const float4 ls = *reinterpret_cast<const float4 *>(&lam2[s0]);
+                    const float4 ds = *reinterpret_cast<const float4 *>(&dts[s0]);
+                    const float u0 = ds.x * __builtin_amdgcn_exp2f(lr0 - ls.x), u1 = ds.y * __builtin_amdgcn_exp2f(lr0 - ls.y);
+                    const float u2 = ds.z * __builtin_amdgcn_exp2f(lr0 - ls.z), u3 = ds.w * __builtin_amdgcn_exp2f(lr0 - ls.w);
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const float4 xv = *reinterpret_cast<const float4 *>(&Xt[16 * pt + r][s0]);
+                        yc[pt] = mfma4(cbv[u].x, xv.x * u0, yc[pt]);
+                        yc[pt] = mfma4(cbv[u].y, xv.y * u1, yc[pt]);
+                        yc[pt] = mfma4(cbv[u].z, xv.z * u2, yc[pt]);
+                        yc[pt] = mfma4(cbv[u].w, xv.w * u3, yc[pt]);
+                    }
+                }
+            }
+        }
+        {   // the diagonal block, masked s <= t
+            const int s0 = ti * 16 + 4 * kq;
+            const float4 cbv = *reinterpret_cast<const float4 *>(cbrow + 16 * ti);
+            const float4 ls = *reinterpret_cast<const float4 *>(&lam2[s0]);
+            const float4 ds = *reinterpret_cast<const float4 *>(&dts[s0]);
+            const float w0 = s0 <= t ? cbv.x * __builtin_amdgcn_exp2f(lt - ls.x) * ds.x : 0.f;
+            const float w1 = s0 + 1 <= t ? cbv.y * __builtin_amdgcn_exp2f(lt - ls.y) * ds.y : 0.f;
+            const float w2 = s0 + 2 <= t ? cbv.z * __builtin_amdgcn_exp2f(lt - ls.z) * ds.z : 0.f;
+            const float w3 = s0 + 3 <= t ? cbv.w * __builtin_amdgcn_exp2f(lt - ls.w) * ds.w : 0.f;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const float4 xv = *reinterpret_cast<const float4 *>(&Xt[16 * pt + r][s0]);
+                yd[pt] = mfma4(w0, xv.x, yd[pt]);
+                yd[pt] = mfma4(w1, xv.y, yd[pt]);
+                yd[pt] = mfma4(w2, xv.z, yd[pt]);
+                yd[pt] = mfma4(w3, xv.w, yd[pt]);
+            }
+        }
+        // row scales, + D x, gate, out: lane l holds row t = ti*16 + 4 kq + rr, channel p = 16 pt + r
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int tt = ti * 16 + 4 * kq + rr;
+            if (tt < len) {
+                const float l2 = lam2[tt];
+                const float eo = __builtin_amdgcn_exp2f(l2), ec = __builtin_amdgcn_exp2f(l2 - lr0);
+                const int64_t m = mbase + tt;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const int p = 16 * pt + r;
+                    const int64_t col = (int64_t)h * a.P + p;
+                    const float yv = eo * yo[pt][rr] + ec * yc[pt][rr] + yd[pt][rr] + Dh * Xt[p][tt];
+                    a.g[m * a.E + col] = yv * silu_f(a.Y[m * a.ldY + col]);
+                }
+            }
         }
     }
 }
@@ -623,10 +641,8 @@ PrefillWs carve_prefill_ws(const Shape &s, int batch, int seqlen, int chunk, voi
     w.Y = static_cast<float *>(take(M * s.Ninp * 4));
     w.xbc = static_cast<float *>(take(M * s.Cd * 4));
     w.dt = static_cast<float *>(take(M * s.H * 4));
-    w.lam = static_cast<float *>(take((size_t)batch * s.H * seqlen * 4));
-    w.lam_end = static_cast<float *>(take((size_t)batch * s.H * nch * 4));
     w.cb = static_cast<float *>(take((size_t)batch * s.G * nch * chunk * chunk * 4));
-    w.ydiag = static_cast<float *>(take(M * s.E * 4));
+    w.lam_end = static_cast<float *>(take((size_t)batch * s.H * nch * 4));
     w.sloc = static_cast<float *>(take((size_t)batch * s.H * nch * s.P * s.N * 4));
     w.gbuf = static_cast<float *>(take(M * s.E * 4));
     w.q_out = static_cast<int8_t *>(take(M * s.E));
@@ -723,26 +739,19 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.D = w.D;
         a.Y = ws.Y;
         a.ldY = s.Ninp;
-        a.lam = ws.lam;
-        a.lam_end = ws.lam_end;
         a.cb = ws.cb;
-        a.ydiag = ws.ydiag;
+        a.lam_end = ws.lam_end;
         a.sloc = ws.sloc;
         a.state = st.ssm;
         a.g = ws.gbuf;
-        const int tq = (chunk + TT - 1) / TT;
-        const int nbhc = batch * s.H * nch;
-        k_ssd_lam<<<nbhc, kBlock, 0, stream>>>(a);
+        k_ssd_cbm<<<dim3(batch * s.G * nch, chunk / 16), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ssd_cb<<<dim3(batch * s.G * nch, tq * tq), kBlock, 0, stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ssd_ydiag<<<dim3(nbhc, tq), kBlock, 0, stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ssd_sloc<<<dim3(nbhc, (s.N + TT - 1) / TT), kBlock, 0, stream>>>(a);
+        const int nblk = batch * s.H * nch;
+        k_ssd_state<<<nblk, kSsdBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_ssd_scan<<<dim3((s.P * s.N + kBlock - 1) / kBlock, batch * s.H), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ssd_yoff<<<dim3(nbhc, tq), kBlock, 0, stream>>>(a);
+        k_ssd_out<<<nblk, kSsdBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 6. out: gated RMSNorm + quantizer + LoRA-down of g
