@@ -15,12 +15,16 @@
 // column's bit row for the current K step straight into registers and expands the 16 bits each
 // MFMA needs into 16 bytes with a multiply-and-mask, so LDS carries only A.
 //
-// k_gemm_tile (M > 64): workgroup tile 128 x (64*WNB), 4 waves as 2 x 2, each wave 64 x (32*WNB)
-// = 2 x WNB MFMA blocks; K in steps of 128 through double-buffered LDS, one barrier per step.
+// k_gemm_tile (M > 64): workgroup tile 128 x (64*WNB), 4 waves side by side along N, each wave
+// 128 x (16*WNB) = 4 x WNB/2 MFMA blocks, so every wave expands only its own columns' sign bits
+// (no two waves expand the same bits); K in steps of 128 through double-buffered LDS, one barrier
+// per step.
 // The ragged last column tile is dispatched first so that the short workgroups do not trail.
 // k_gemm_skinny (M <= 64): one workgroup per 32 columns, its 4 waves split K and reduce their
 // int32 partial sums through LDS; A comes straight from global memory (it is 64 x K bytes and
 // stays in L2), B as above.
+#include <algorithm>
+
 #include "decode_device.h"
 
 namespace dfssm {
@@ -45,6 +49,15 @@ __device__ __forceinline__ v4i expand16(uint32_t b16) {
     r.z = (int)nibble_to_bytes((b16 >> 8) & 15u);
     r.w = (int)nibble_to_bytes((b16 >> 12) & 15u);
     return r;
+}
+
+template <typename T>
+__device__ __forceinline__ T *at_bytes(T *base, uint32_t off) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
+}
+template <typename T>
+__device__ __forceinline__ const T *at_bytes(const T *base, uint32_t off) {
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + off);
 }
 
 __device__ __forceinline__ uint32_t u4_get(const uint4 &v, int i) {
@@ -85,18 +98,35 @@ __device__ __forceinline__ v16f lowrank_block(const GemmArgs &a, int mrow, int n
 }
 
 // Epilogue of one 32 x 32 block: lane holds column (lane % 32), rows 8*(r/4) + 4*(lane/32) + r%4.
-__device__ __forceinline__ void store_block(const GemmArgs &a, const v16i &acc, const v16f &lacc, int mb, int n,
-                                            int lane) {
+// Its per-row and per-column operands are loaded (clamped into the matrices) before any store is
+// issued: a load behind stores makes its wait cover the stores as well.
+struct BlockOps {
+    float s[16], res[16];
+    int q[16];
+    float sc, us;
+};
+__device__ __forceinline__ void load_block_ops(const GemmArgs &a, BlockOps &o, int mb, int n, int lane) {
+    const int nc = min(n, a.N - 1);
+    o.sc = half_bits_to_float(a.row_scale[nc]);
+    o.us = a.up_scale[nc];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int mc = min(mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), a.M - 1);
+        o.s[r] = a.s[mc];
+        o.q[r] = a.qsum[mc];
+        o.res[r] = a.res ? a.res[(int64_t)mc * a.ldres + nc] : 0.f;
+    }
+}
+__device__ __forceinline__ void store_block(const GemmArgs &a, const v16i &acc, const v16f &lacc, const BlockOps &o,
+                                            int mb, int n, int lane) {
     if (n >= a.N) return;
-    const float sc = half_bits_to_float(a.row_scale[n]);
-    const float us = a.up_scale[n];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int m = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m >= a.M) continue;
-        const int accv = 2 * acc[r] - a.qsum[m];
-        float v = a.s[m] * sc * (float)accv + us * lacc[r];
-        if (a.res) v += a.res[(int64_t)m * a.ldres + n];
+        const int accv = 2 * acc[r] - o.q[r];
+        float v = o.s[r] * o.sc * (float)accv + o.us * lacc[r];
+        if (a.res) v += o.res[r];
         a.y[(int64_t)m * a.ldy + n] = v;
         if (a.acc_tap) a.acc_tap[(int64_t)m * a.ldacc + n] = accv;
     }
@@ -172,14 +202,14 @@ __device__ __forceinline__ void stage_epilogue(const GemmArgs &a, char *base, in
 }
 
 // two waves per SIMD (<= 256 registers incl. accumulators), so two workgroups share a compute unit
-template <int WNB, bool SPLIT>
+template <int WNB, bool SPLIT, bool RES>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tile(GemmArgs a, int ntm,
                                                                                               int ntn, int splitk) {
-    constexpr int BN = 64 * WNB;
+    constexpr int BN = 64 * WNB, NBW = WNB / 2;   // N blocks of 32 per wave
     __shared__ __align__(16) char smem[kTileSmem];
     __shared__ int last_flag;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wn = wave;
     const int lr = lane & 31, hsel = lane >> 5;
     // tile order: the ragged last column tile of every row first, then row-fastest
     const int bid = blockIdx.x, z = blockIdx.y;
@@ -206,56 +236,71 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int8_t *qrow = a.q + (int64_t)(arow_ok ? m0 + srow : 0) * a.ldq + shalf * 64;
     const bool bcol_ok = tid < BN && n0 + tid < a.N;
     const uint8_t *bsrc = a.sign + (int64_t)(bcol_ok ? n0 + tid : 0) * (K >> 3);
-    int4 ra[4];
-    uint4 rb;
-    auto gload = [&](int k0) {
+    // one register stage: the global loads of step k + 1 are issued while step k computes
+    struct Stage {
+        int4 a[4];
+        uint4 b;
+    };
+    Stage st0;
+    auto gload = [&](Stage &st, int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            ra[i] = arow_ok ? *reinterpret_cast<const int4 *>(qrow + k0 + 16 * i) : make_int4(0, 0, 0, 0);
-        rb = bcol_ok ? *reinterpret_cast<const uint4 *>(bsrc + (k0 >> 3)) : make_uint4(0u, 0u, 0u, 0u);
+            st.a[i] = arow_ok ? *reinterpret_cast<const int4 *>(qrow + k0 + 16 * i) : make_int4(0, 0, 0, 0);
+        st.b = bcol_ok ? *reinterpret_cast<const uint4 *>(bsrc + (k0 >> 3)) : make_uint4(0u, 0u, 0u, 0u);
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](const Stage &st, int buf) {
         int8_t *d = As(buf) + srow * LDS_ROW + shalf * 64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<int4 *>(d + 16 * i) = ra[i];
-        if (tid < BN) *reinterpret_cast<uint4 *>(Bs(buf) + tid * 16) = rb;
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<int4 *>(d + 16 * i) = st.a[i];
+        if (tid < BN) *reinterpret_cast<uint4 *>(Bs(buf) + tid * 16) = st.b;
     };
-    v16i acc[2][WNB];
+    v16i acc[4][NBW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < WNB; ++j)
+        for (int j = 0; j < NBW; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-    gload(kt0 * KT);
+    gload(st0, kt0 * KT);
     const bool early = a.rank <= kEarlyRank;
     char *epi = smem + (early ? kMainLds : 0);
     if (early) stage_epilogue<BN>(a, epi, m0, n0, tid);
-    sstore(0);
+    // per-column scales of the epilogue, loaded now so that no load follows the epilogue's stores
+    float sc[NBW], us[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int n = min(n0 + wn * (32 * NBW) + j * 32 + lr, a.N - 1);
+        sc[j] = half_bits_to_float(a.row_scale[n]);
+        us[j] = a.up_scale[n];
+    }
+    sstore(st0, 0);
     __syncthreads();
+    auto step = [&](int cur) {
+        const int8_t *abase = As(cur) + lr * LDS_ROW + hsel * 16;
+        uint4 bw[NBW];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+            bw[j] = *reinterpret_cast<const uint4 *>(Bs(cur) + (wn * (32 * NBW) + j * 32 + lr) * 16);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v4i af[4], bf[NBW];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i *>(abase + i * 32 * LDS_ROW + s * 32);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) bf[j] = expand16((u4_get(bw[j], s) >> (16 * hsel)) & 0xffffu);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+    };
     for (int kt = kt0; kt < kt1; ++kt) {
         const int cur = (kt - kt0) & 1;
         const bool more = kt + 1 < kt1;
-        if (more) gload((kt + 1) * KT);
-        const int8_t *abase = As(cur) + (wm * 64 + lr) * LDS_ROW + hsel * 16;
-        uint4 bw[WNB];
-#pragma unroll
-        for (int j = 0; j < WNB; ++j)
-            bw[j] = *reinterpret_cast<const uint4 *>(Bs(cur) + (wn * (32 * WNB) + j * 32 + lr) * 16);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            v4i af[2], bf[WNB];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const v4i *>(abase + i * 32 * LDS_ROW + s * 32);
-#pragma unroll
-            for (int j = 0; j < WNB; ++j) bf[j] = expand16((u4_get(bw[j], s) >> (16 * hsel)) & 0xffffu);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < WNB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (more) sstore(cur ^ 1);
+        if (more) gload(st0, (kt + 1) * KT);
+        step(cur);
+        if (more) sstore(st0, cur ^ 1);
         lds_barrier();
     }
     // ---- split K: publish the exact int32 partial sums; the last workgroup of the tile to arrive
@@ -267,11 +312,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         int32_t *part = reinterpret_cast<int32_t *>(static_cast<char *>(a.scratch) + kCntBytes);
         int32_t *mine = part + ((int64_t)tile * splitk + z) * tsz;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < WNB; ++j)
+            for (int j = 0; j < NBW; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) st_x(mine + ((((wave * 2 + i) * WNB + j) * 16 + r) * 64 + lane), acc[i][j][r]);
+                for (int r = 0; r < 16; ++r) st_x(mine + ((((wave * 4 + i) * NBW + j) * 16 + r) * 64 + lane), acc[i][j][r]);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
@@ -284,11 +329,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             if (z2 == z) continue;
             const int32_t *o = part + ((int64_t)tile * splitk + z2) * tsz;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < WNB; ++j)
+                for (int j = 0; j < NBW; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += ld_x(o + ((((wave * 2 + i) * WNB + j) * 16 + r) * 64 + lane));
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += ld_x(o + ((((wave * 4 + i) * NBW + j) * 16 + r) * 64 + lane));
         }
     }
     // ---- epilogue: operands from LDS (staged before the main loop, or now for ranks above 32)
@@ -302,55 +347,61 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const __bf16 *th_l = reinterpret_cast<const __bf16 *>(epi + 1024);
     const __bf16 *tl_l = th_l + BM * RS;
     const int8_t *u_l = reinterpret_cast<const int8_t *>(tl_l + BM * RS);
-    float sc[WNB], us[WNB];
-#pragma unroll
-    for (int j = 0; j < WNB; ++j) {
-        const int n = n0 + wn * (32 * WNB) + j * 32 + lr;
-        sc[j] = n < a.N ? half_bits_to_float(a.row_scale[n]) : 0.f;
-        us[j] = n < a.N ? a.up_scale[n] : 0.f;
-    }
     const int lj = hsel * 8;
+    // Element (local row ml, local column cl) of the tile is at byte ml * ld * 4 + cl * 4 from the
+    // tile's corner: uniform 64-bit corners, 32-bit per-lane offsets.
+    const bool mfull = m0 + BM <= a.M;
+    float *const yt = a.y + (int64_t)m0 * a.ldy + n0;
+    const float *const rt = RES ? a.res + (int64_t)m0 * a.ldres + n0 : nullptr;
+    int32_t *const tt = a.acc_tap ? a.acc_tap + (int64_t)m0 * a.ldacc + n0 : nullptr;
+    constexpr int NIT = 4 * NBW;
+    // Residual of block `it` (clamped into the matrix, so every load is in bounds). The loads of
+    // block it + 1 are issued before the stores of block it: a load behind stores would make its
+    // wait cover the stores as well.
+    float rv[2][16];
+    auto load_res = [&](int it, float (&dst)[16]) {
+        const int clc = min(wn * (32 * NBW) + (it >> 2) * 32 + lr, a.N - 1 - n0);
 #pragma unroll
-    for (int j = 0; j < WNB; ++j) {
-        const int cl = wn * (32 * WNB) + j * 32 + lr;
-        const int n = n0 + cl;
+        for (int r = 0; r < 16; ++r) {
+            const int mlc = min((it & 3) * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3), a.M - 1 - m0);
+            dst[r] = *at_bytes(rt, (uint32_t)(mlc * (int)a.ldres + clc) * 4u);
+        }
+    };
+    if (RES) load_res(0, rv[0]);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int rl = wm * 64 + i * 32;
-            v16f lacc;
+    for (int it = 0; it < NIT; ++it) {
+        const int i = it & 3, j = it >> 2;
+        const int rl = i * 32, cl = wn * (32 * NBW) + j * 32 + lr;
+        v16f lacc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
-            for (int kr = 0; kr < rank; kr += 16) {
-                const bool inr = kr + lj + 8 <= rank;
-                v8bf ahi, alo, bup;
-                uint2 w = make_uint2(0u, 0u);
-                if (inr) {
-                    ahi = *reinterpret_cast<const v8bf *>(th_l + (rl + lr) * RS + kr + lj);
-                    alo = *reinterpret_cast<const v8bf *>(tl_l + (rl + lr) * RS + kr + lj);
-                    w = *reinterpret_cast<const uint2 *>(u_l + cl * RS + kr + lj);
-                } else {
+        for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+        for (int kr = 0; kr < rank; kr += 16) {
+            const bool inr = kr + lj + 8 <= rank;
+            v8bf ahi, alo, bup;
+            uint2 w = make_uint2(0u, 0u);
+            if (inr) {
+                ahi = *reinterpret_cast<const v8bf *>(th_l + (rl + lr) * RS + kr + lj);
+                alo = *reinterpret_cast<const v8bf *>(tl_l + (rl + lr) * RS + kr + lj);
+                w = *reinterpret_cast<const uint2 *>(u_l + cl * RS + kr + lj);
+            } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        ahi[e] = (__bf16)0.f;
-                        alo[e] = (__bf16)0.f;
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    ahi[e] = (__bf16)0.f;
+                    alo[e] = (__bf16)0.f;
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bup[e] = (__bf16)(float)(int8_t)(w.x >> (8 * e));
-                    bup[4 + e] = (__bf16)(float)(int8_t)(w.y >> (8 * e));
-                }
-                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bup, lacc, 0, 0, 0);
-                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bup, lacc, 0, 0, 0);
             }
-            if (n >= a.N) continue;
-            // residual first (y may alias it; each element is read, then written, by this lane only)
-            float rv[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + rl + 8 * (r >> 2) + 4 * hsel + (r & 3);
-                rv[r] = (a.res && m < a.M) ? a.res[(int64_t)m * a.ldres + n] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                bup[e] = (__bf16)(float)(int8_t)(w.x >> (8 * e));
+                bup[4 + e] = (__bf16)(float)(int8_t)(w.y >> (8 * e));
             }
+            lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bup, lacc, 0, 0, 0);
+            lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bup, lacc, 0, 0, 0);
+        }
+        if (RES && it + 1 < NIT) load_res(it + 1, rv[(it + 1) & 1]);
+        if (n0 + cl < a.N) {
+            float v[16];
+            int accv[16];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int ml = rl + 8 * g + 4 * hsel;
@@ -360,13 +411,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 const int qvs[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g + e, m = m0 + ml + e;
-                    if (m >= a.M) continue;
-                    const int accv = 2 * acc[i][j][r] - qvs[e];
-                    float v = svs[e] * sc[j] * (float)accv + us[j] * lacc[r];
-                    if (a.res) v += rv[r];
-                    a.y[(int64_t)m * a.ldy + n] = v;
-                    if (a.acc_tap) a.acc_tap[(int64_t)m * a.ldacc + n] = accv;
+                    const int r = 4 * g + e;
+                    accv[r] = 2 * acc[i][j][r] - qvs[e];
+                    v[r] = svs[e] * sc[j] * (float)accv[r] + us[j] * lacc[r];
+                    if (RES) v[r] += rv[it & 1][r];
+                }
+            }
+            // byte offset = lane part ((4 * hsel) rows, column cl) + uniform part (row rl + 8 g + e)
+            const uint32_t ly = (uint32_t)(4 * hsel * (int)a.ldy + cl) * 4u;
+            const uint32_t lt = (uint32_t)(4 * hsel * (int)a.ldacc + cl) * 4u;
+            if (mfull) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    *at_bytes(yt, ly + (uint32_t)((rl + 8 * (r >> 2) + (r & 3)) * (int)a.ldy) * 4u) = v[r];
+                if (tt) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        *at_bytes(tt, lt + (uint32_t)((rl + 8 * (r >> 2) + (r & 3)) * (int)a.ldacc) * 4u) = accv[r];
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int mr = rl + 8 * (r >> 2) + (r & 3);
+                    if (m0 + mr + 4 * hsel >= a.M) continue;
+                    *at_bytes(yt, ly + (uint32_t)(mr * (int)a.ldy) * 4u) = v[r];
+                    if (tt) *at_bytes(tt, lt + (uint32_t)(mr * (int)a.ldacc) * 4u) = accv[r];
                 }
             }
         }
@@ -430,12 +499,20 @@ __global__ __launch_bounds__(kBlock) void k_gemm_skinny(GemmArgs a) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] += red[0][i][r][lane] + red[1][i][r][lane] + red[2][i][r][lane];
+    // every load of both blocks' epilogues, then the stores
+    const int nb = a.M > 32 ? 2 : 1;
+    v16f lacc[2];
+    BlockOps ops[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        if (i * 32 >= a.M) break;
-        const v16f lacc = lowrank_block(a, i * 32 + lr, n, lane);
-        store_block(a, acc[i], lacc, i * 32, n, lane);
+        if (i < nb) {
+            lacc[i] = lowrank_block(a, i * 32 + lr, n, lane);
+            load_block_ops(a, ops[i], i * 32, n, lane);
+        }
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if (i < nb) store_block(a, acc[i], lacc[i], ops[i], i * 32, n, lane);
 }
 
 }  // namespace
@@ -480,6 +557,9 @@ size_t gemm_scratch_bytes(int M, int N, int K) {
 
 hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
     if (a.K % KT || a.rank % 8 || a.rank > kMaxRank || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
+    // the tile kernel addresses its outputs with 32-bit byte offsets from the tile corner
+    const int64_t ldmax = std::max(a.ldy, std::max(a.res ? a.ldres : 0, a.acc_tap ? a.ldacc : 0));
+    if (ldmax > (int64_t)1 << 22) return hipErrorInvalidValue;
     if (a.M <= 64) {
         k_gemm_skinny<<<(a.N + 31) / 32, kBlock, 0, stream>>>(a);
         return hipGetLastError();
@@ -491,9 +571,17 @@ hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
         k_clear_u32<<<(tiles + kBlock - 1) / kBlock, kBlock, 0, stream>>>(static_cast<uint32_t *>(a.scratch), tiles);
     }
     const dim3 grid(tiles, p.splitk);
-    if (p.wnb == 4) k_gemm_tile<4, false><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
-    else if (p.splitk > 1) k_gemm_tile<2, true><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, p.splitk);
-    else k_gemm_tile<2, false><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
+    const bool res = a.res != nullptr;
+    if (p.wnb == 4) {
+        if (res) k_gemm_tile<4, false, true><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
+        else k_gemm_tile<4, false, false><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
+    } else if (p.splitk > 1) {
+        if (res) k_gemm_tile<2, true, true><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, p.splitk);
+        else k_gemm_tile<2, true, false><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, p.splitk);
+    } else {
+        if (res) k_gemm_tile<2, false, true><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
+        else k_gemm_tile<2, false, false><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
+    }
     return hipGetLastError();
 }
 
