@@ -23,6 +23,52 @@ __device__ __forceinline__ int wave_isum(int v) {
     return v;
 }
 
+// Sum over groups of w consecutive lanes (w a power of two <= 64) with DPP row operations; the
+// group's total is valid in its last lane (lane % w == w - 1).
+__device__ __forceinline__ int dpp_group_sum(int v, int w) {
+    if (w >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    if (w >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+    if (w >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    if (w >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true); // row_shr:8
+    if (w >= 32) v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+    if (w >= 64) v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
+    return v;
+}
+template <int CTRL, int RMASK, bool BC>
+__device__ __forceinline__ float dpp_add_f(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, RMASK, 0xF, BC));
+}
+__device__ __forceinline__ float dpp_group_sum_f(float v, int w) {
+    if (w >= 2) v = dpp_add_f<0xB1, 0xF, true>(v);
+    if (w >= 4) v = dpp_add_f<0x4E, 0xF, true>(v);
+    if (w >= 8) v = dpp_add_f<0x114, 0xF, true>(v);
+    if (w >= 16) v = dpp_add_f<0x118, 0xF, true>(v);
+    if (w >= 32) v = dpp_add_f<0x142, 0xA, false>(v);
+    if (w >= 64) v = dpp_add_f<0x143, 0xC, false>(v);
+    return v;
+}
+
+// Whole-wave sum / max by DPP (a few cycles per step, against a full LDS round trip per step for
+// lane shuffles); the fixed order makes every workgroup reducing the same data agree bit for bit.
+template <int CTRL, int RMASK, bool BC>
+__device__ __forceinline__ float dpp_max_f(float v) {
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, RMASK, 0xF, BC)));
+}
+__device__ __forceinline__ float dpp_wave_sum(float v) {
+    v = dpp_group_sum_f(v, 64);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float dpp_wave_max(float v) {   // v >= 0 (lanes past a row edge read 0)
+    v = dpp_max_f<0xB1, 0xF, true>(v);
+    v = dpp_max_f<0x4E, 0xF, true>(v);
+    v = dpp_max_f<0x114, 0xF, true>(v);
+    v = dpp_max_f<0x118, 0xF, true>(v);
+    v = dpp_max_f<0x142, 0xA, false>(v);
+    v = dpp_max_f<0x143, 0xC, false>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ int dpp_wave_isum(int v) { return __builtin_amdgcn_readlane(dpp_group_sum(v, 64), 63); }
+
 // Block-wide reductions with a fixed combination order, so every workgroup that reduces the
 // same data obtains bit-identical results. `red` is >= kWaves floats of LDS.
 __device__ __forceinline__ float block_sum(float v, float *red) {

@@ -30,91 +30,247 @@ __global__ __launch_bounds__(kBlock) void k_widen_bf16(const uint16_t *x, float 
 }
 
 // ------------------------------------------------------------------ 1/6 per-token quantizer
+// kTqTok tokens per workgroup. Each wave normalises and quantizes two whole tokens (wave-level
+// reductions only, no barrier), leaving their codes in LDS; then the LoRA-down of all of them,
+// t[tok][j] = sum_k q[tok][k] L_dn[j][k], runs on int8 MFMA (32x32x32 blocks, tokens as rows
+// 0..7 of the block, rank rows as its columns, the K blocks split over the waves), so each
+// workgroup reads L_dn once for kTqTok tokens.
+constexpr int kTqTok = 8;
+constexpr int kTqRow = kMaxK + 16;  // LDS bytes per token's codes (the pad spreads rows over the banks)
+typedef int tq_v4i __attribute__((ext_vector_type(4)));
+typedef int tq_v16i __attribute__((ext_vector_type(16)));
+
+template <int KCH>
 __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
-    __shared__ float red[2 * kWaves];
-    __shared__ int ired[kWaves];
-    __shared__ __align__(16) int8_t sq[kMaxK];
+    __shared__ __align__(16) int8_t sq[kTqTok * kTqRow];
+    __shared__ float s_l[kTqTok];
+    __shared__ int tred[kWaves][kMaxRank / 32][4][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int m = blockIdx.x;
+    const int lr = lane & 31, hsel = lane >> 5;
+    const int m0 = blockIdx.x * kTqTok;
     const int K = a.K;
-    constexpr int KCH = kMaxK / 1024;
-    float4 hv[KCH];
-    float ss = 0.f, pm = 0.f;
+    const int nkw = K / 128, nrb = (a.rank + 31) / 32;  // K blocks of 32 per wave; rank blocks of 32
+    // Loads are issued in the order their results are needed (norm weight, the rows, then the
+    // LoRA-down operands), all before any store, with addresses clamped into range and
+    // out-of-range values zeroed after, so that the quantizer of the first row starts while the
+    // rest is still in flight.
+    float dsv[kMaxRank / 32];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-        const int e = (i * kBlock + tid) * 4;
-        if (e < K) {
-            if (a.x_bf16) {
-                const uint2 r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.X) + (int64_t)m * a.ldx + e);
-                hv[i] = make_float4(bf16_bits_to_float(r.x & 0xffffu), bf16_bits_to_float(r.x >> 16),
-                                    bf16_bits_to_float(r.y & 0xffffu), bf16_bits_to_float(r.y >> 16));
-            } else {
-                hv[i] = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.X) + (int64_t)m * a.ldx + e);
+    for (int rb = 0; rb < kMaxRank / 32; ++rb) dsv[rb] = a.dn_scale[min(rb * 32 + (tid & 31), a.rank - 1)];
+    float4 wv[KCH];
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) wv[i] = *reinterpret_cast<const float4 *>(a.W + min((i * 64 + lane) * 4, K - 4));
+    // ---- norm + quantizer: wave w takes tokens w and w + kWaves (both rows in flight at once when
+    // they fit in registers)
+    constexpr int NU = KCH <= 16 ? 2 : 1;
+    // LoRA-down operands (lane: rank row lr, bytes 16 * hsel.. of each 32-wide K block); with one
+    // rank block and exactly PRE K blocks per wave they are loaded with the rows
+    constexpr int PRE = KCH <= 16 ? 2 * KCH : 1;
+    const bool pre = KCH <= 16 && nrb == 1 && nkw == PRE;
+    const int8_t *brow[kMaxRank / 32];
+    bool bok[kMaxRank / 32];
+#pragma unroll
+    for (int rb = 0; rb < kMaxRank / 32; ++rb) {
+        const int j = rb * 32 + lr;
+        bok[rb] = j < a.rank;
+        brow[rb] = a.lora_dn + (int64_t)min(j, a.rank - 1) * K + hsel * 16 + wave * nkw * 32;
+    }
+    tq_v4i bpre[PRE];
+#pragma unroll
+    for (int pass = 0; pass < 2 / NU; ++pass) {
+        float4 hv[NU][KCH];
+        int mrow[NU];
+        bool mok[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int m = m0 + wave + (pass * NU + u) * kWaves;
+            mok[u] = m < a.M;
+            mrow[u] = min(m, a.M - 1);
+        }
+        if (a.x_bf16) {
+            uint2 raw[NU][KCH];
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int i = 0; i < KCH; ++i) {
+                    const int e = min((i * 64 + lane) * 4, K - 4);
+                    raw[u][i] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.X) + (int64_t)mrow[u] * a.ldx + e);
+                }
+            if (pre) {
+#pragma unroll
+                for (int c = 0; c < PRE; ++c) bpre[c] = *reinterpret_cast<const tq_v4i *>(brow[0] + c * 32);
             }
-            if (a.tap_h) *reinterpret_cast<float4 *>(a.tap_h + (int64_t)m * K + e) = hv[i];
-            ss += hv[i].x * hv[i].x + hv[i].y * hv[i].y + hv[i].z * hv[i].z + hv[i].w * hv[i].w;
-            const float4 w = *reinterpret_cast<const float4 *>(a.W + e);
-            hv[i].x *= w.x;
-            hv[i].y *= w.y;
-            hv[i].z *= w.z;
-            hv[i].w *= w.w;
-            pm = fmaxf(pm, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)), fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
-        }
-    }
-    float tot;
-    block_sum_max(ss, pm, red, tot, pm);
-    // u = fl(fl(h * w) * r) so that max|u| = fl(max|h * w| * r) exactly (r > 0)
-    const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
-    const float amax = pm * r;
-    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-    const float s = amax > 0.f ? amax / 127.0f : 0.f;
-    int qs = 0;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-        const int e = (i * kBlock + tid) * 4;
-        if (e < K) {
-            float4 u = hv[i];
-            u.x *= r;
-            u.y *= r;
-            u.z *= r;
-            u.w *= r;
-            const int q0 = quant1(u.x, inv), q1 = quant1(u.y, inv), q2 = quant1(u.z, inv), q3 = quant1(u.w, inv);
-            qs += q0 + q1 + q2 + q3;
-            const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
-                                    ((uint32_t)(q3 & 255) << 24);
-            *reinterpret_cast<uint32_t *>(sq + e) = packed;
-            *reinterpret_cast<uint32_t *>(a.q + (int64_t)m * K + e) = packed;
-            if (a.tap_u) *reinterpret_cast<float4 *>(a.tap_u + (int64_t)m * K + e) = u;
-            if (a.tap_q) *reinterpret_cast<uint32_t *>(a.tap_q + (int64_t)m * K + e) = packed;
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int i = 0; i < KCH; ++i) {
+                    const uint2 r = raw[u][i];
+                    hv[u][i] = make_float4(bf16_bits_to_float(r.x & 0xffffu), bf16_bits_to_float(r.x >> 16),
+                                           bf16_bits_to_float(r.y & 0xffffu), bf16_bits_to_float(r.y >> 16));
+                }
+        } else {
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int i = 0; i < KCH; ++i) {
+                    const int e = min((i * 64 + lane) * 4, K - 4);
+                    hv[u][i] = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.X) + (int64_t)mrow[u] * a.ldx + e);
+                }
+            if (pre) {
+#pragma unroll
+                for (int c = 0; c < PRE; ++c) bpre[c] = *reinterpret_cast<const tq_v4i *>(brow[0] + c * 32);
+            }
         }
-    }
-    qs = block_isum(qs, ired);
-    if (tid == 0) {
-        a.s[m] = s;
-        a.qsum[m] = qs;
-        if (a.tap_s) a.tap_s[m] = s;
+        float ss[NU], pm[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            ss[u] = 0.f;
+            pm[u] = 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const bool ok = (i * 64 + lane) * 4 < K && mok[u];
+                float4 &h = hv[u][i];
+                h.x = ok ? h.x : 0.f;
+                h.y = ok ? h.y : 0.f;
+                h.z = ok ? h.z : 0.f;
+                h.w = ok ? h.w : 0.f;
+                ss[u] += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
+            }
+        }
+        if (a.tap_h) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int i = 0; i < KCH; ++i) {
+                    const int e = (i * 64 + lane) * 4;
+                    if (e < K && mok[u]) *reinterpret_cast<float4 *>(a.tap_h + (int64_t)mrow[u] * K + e) = hv[u][i];
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                float4 &h = hv[u][i];
+                const float4 w = wv[i];
+                h.x *= w.x;
+                h.y *= w.y;
+                h.z *= w.z;
+                h.w *= w.w;
+                pm[u] = fmaxf(pm[u], fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w))));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int tok = wave + (pass * NU + u) * kWaves, m = m0 + tok;
+            const float tot = dpp_wave_sum(ss[u]), mx = dpp_wave_max(pm[u]);
+            // u = fl(fl(h * w) * r) so that max|u| = fl(max|h * w| * r) exactly (r > 0)
+            const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
+            const float amax = mx * r;
+            const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+            const float sv = amax > 0.f ? amax / 127.0f : 0.f;
+            int qs = 0;
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) {
+                const int e = (i * 64 + lane) * 4;
+                if (e < K) {
+                    float4 v = hv[u][i];
+                    v.x *= r;
+                    v.y *= r;
+                    v.z *= r;
+                    v.w *= r;
+                    const int q0 = quant1(v.x, inv), q1 = quant1(v.y, inv), q2 = quant1(v.z, inv), q3 = quant1(v.w, inv);
+                    qs += q0 + q1 + q2 + q3;
+                    const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) |
+                                            ((uint32_t)(q2 & 255) << 16) | ((uint32_t)(q3 & 255) << 24);
+                    *reinterpret_cast<uint32_t *>(sq + tok * kTqRow + e) = packed;
+                    if (m < a.M) {
+                        *reinterpret_cast<uint32_t *>(a.q + (int64_t)m * K + e) = packed;
+                        if (a.tap_u) *reinterpret_cast<float4 *>(a.tap_u + (int64_t)m * K + e) = v;
+                        if (a.tap_q) *reinterpret_cast<uint32_t *>(a.tap_q + (int64_t)m * K + e) = packed;
+                    }
+                }
+            }
+            qs = dpp_wave_isum(qs);
+            if (lane == 0) {
+                s_l[tok] = sv;
+                if (m < a.M) {
+                    a.s[m] = sv;
+                    a.qsum[m] = qs;
+                    if (a.tap_s) a.tap_s[m] = sv;
+                }
+            }
+        }
     }
     __syncthreads();
-    // int8 LoRA-down, one wave per rank row
-    for (int j = wave; j < a.rank; j += kWaves) {
-        const int8_t *row = a.lora_dn + (int64_t)j * K;
-        int acc = 0;
-        for (int off = lane * 16; off < K; off += 1024) {
-            const int4 lw = *reinterpret_cast<const int4 *>(row + off);
-            const int4 qv = *reinterpret_cast<const int4 *>(sq + off);
-            acc = __builtin_amdgcn_sdot4(lw.x, qv.x, acc, false);
-            acc = __builtin_amdgcn_sdot4(lw.y, qv.y, acc, false);
-            acc = __builtin_amdgcn_sdot4(lw.z, qv.z, acc, false);
-            acc = __builtin_amdgcn_sdot4(lw.w, qv.w, acc, false);
+    // ---- LoRA-down on int8 MFMA: lane supplies row (token) lr and column (rank row) lr of the
+    // block; tokens past kTqTok and rank rows past the rank are zero
+    const int8_t *arow = sq + (lr & (kTqTok - 1)) * kTqRow + hsel * 16 + wave * nkw * 32;
+    tq_v16i acc[kMaxRank / 32];
+#pragma unroll
+    for (int rb = 0; rb < kMaxRank / 32; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[rb][r] = 0;
+    const tq_v4i zero4 = {0, 0, 0, 0};
+    if (pre) {
+        tq_v4i av[PRE];
+#pragma unroll
+        for (int c = 0; c < PRE; ++c) {
+            av[c] = *reinterpret_cast<const tq_v4i *>(arow + c * 32);
+            if (lr >= kTqTok) av[c] = zero4;
+            if (!bok[0]) bpre[c] = zero4;
         }
-        acc = wave_isum(acc);
-        if (lane == 0) {
-            const float tp = a.dn_scale[j] * s * (float)acc;
+#pragma unroll
+        for (int c = 0; c < PRE; ++c) acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[c], bpre[c], acc[0], 0, 0, 0);
+    } else {
+        // runs of kTqRun K blocks, a run's loads issued before its MFMAs
+        constexpr int kTqRun = 8;
+        for (int c0 = 0; c0 < nkw; c0 += kTqRun) {
+            tq_v4i av[kTqRun], bv[kTqRun][kMaxRank / 32];
+#pragma unroll
+            for (int c = 0; c < kTqRun; ++c) {
+                const int k = min(c0 + c, nkw - 1) * 32;
+                av[c] = *reinterpret_cast<const tq_v4i *>(arow + k);
+                if (lr >= kTqTok) av[c] = zero4;
+#pragma unroll
+                for (int rb = 0; rb < kMaxRank / 32; ++rb) {
+                    if (rb < nrb) {
+                        bv[c][rb] = *reinterpret_cast<const tq_v4i *>(brow[rb] + k);
+                        if (!bok[rb]) bv[c][rb] = zero4;
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < kTqRun; ++c) {
+                if (c0 + c < nkw) {
+#pragma unroll
+                    for (int rb = 0; rb < kMaxRank / 32; ++rb)
+                        if (rb < nrb) acc[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[c], bv[c][rb], acc[rb], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // rows 0..7 of the block (the tokens) sit in accumulator entries r < 4: token 4 * hsel + r
+#pragma unroll
+    for (int rb = 0; rb < kMaxRank / 32; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tred[wave][rb][r][lane] = acc[rb][r];
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < kMaxRank / 32; ++rb) {
+        if (rb >= nrb) break;
+        const int r = tid >> 6, l = tid & 63;
+        const int tot = ((tred[0][rb][r][l] + tred[1][rb][r][l]) + tred[2][rb][r][l]) + tred[3][rb][r][l];
+        const int tok = 4 * (l >> 5) + r, j = rb * 32 + (l & 31), m = m0 + tok;
+        if (j < a.rank && m < a.M) {
+            const float tp = dsv[rb] * s_l[tok] * (float)tot;
             const __bf16 hi = (__bf16)tp;
             const __bf16 lo = (__bf16)(tp - (float)hi);
             a.thi[(int64_t)m * a.rank + j] = hi;
             a.tlo[(int64_t)m * a.rank + j] = lo;
-            if (a.tap_t) a.tap_t[(int64_t)m * a.rank + j] = acc;
+            if (a.tap_t) a.tap_t[(int64_t)m * a.rank + j] = tot;
         }
     }
 }
@@ -617,8 +773,12 @@ hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w
 }
 
 hipError_t launch_tok_quant(const TokQuantArgs &a, hipStream_t stream) {
-    if (a.K > kMaxK || a.K % 16 || a.rank > kMaxRank) return hipErrorInvalidValue;
-    k_tok_quant<<<a.M, kBlock, 0, stream>>>(a);
+    if (a.K > kMaxK || a.K % 128 || a.rank > kMaxRank || a.rank <= 0 || a.M <= 0) return hipErrorInvalidValue;
+    const int grid = (a.M + kTqTok - 1) / kTqTok;
+    if (a.K <= 1024) k_tok_quant<4><<<grid, kBlock, 0, stream>>>(a);
+    else if (a.K <= 2048) k_tok_quant<8><<<grid, kBlock, 0, stream>>>(a);
+    else if (a.K <= 4096) k_tok_quant<16><<<grid, kBlock, 0, stream>>>(a);
+    else k_tok_quant<32><<<grid, kBlock, 0, stream>>>(a);
     return hipGetLastError();
 }
 
