@@ -7,7 +7,7 @@
 //   2 k_gemm_pm1       in_proj over all tokens (int8 MFMA) with the Eq. (3) epilogue -> Y
 //   3 k_conv_seq       causal conv over the sequence + SiLU (x, B, C); softplus(dt + dt_bias)
 //   4 k_conv_handoff   final conv state = the last d_conv-1 pre-activation inputs
-//   5 SSD, chunk length Q, Lam_t = sum_{tau <= t in chunk} dt_tau A (per head), fp32 MFMA:
+//   5 SSD, chunk length Q, Lam_t = sum_{tau <= t in chunk} dt_tau A (per head), MFMA:
 //       k_ssd_cbm      CB[t][s] = C_t . B_s for each chunk and group (shared by the group's heads)
 //       k_ssd_state    S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s per chunk, and Lam_end
 //       k_ssd_scan     S_in(c) = state entering chunk c; S <- exp(Lam_end) S + S_loc (sequential in c)
@@ -391,24 +391,53 @@ __global__ __launch_bounds__(kBlock) void k_ssd_cbm(SsdArgs a) {
 }
 
 // Chunked SSD in three passes, each over every (b, h, chunk) at once (Lam_t = inclusive cumsum of
-// dt A within the chunk; exponentials only of Lam differences, or of Lam itself, all <= 0; fp32
-// MFMA 16x16x4; eight waves per workgroup, all P = 64 channels of the head, so every A operand
-// feeds four MFMAs, one per 16-channel tile):
+// dt A within the chunk; exponentials only of Lam differences, or of Lam itself, all <= 0):
 //   k_ssd_state  S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s of the chunk, and Lam_end
 //   k_ssd_scan   S_in(c) = exp(Lam_end(c-1)) S_in(c-1) + S_loc(c-1), in place (sequential in c)
 //   k_ssd_out    y_t = sum_{s<=t} exp(Lam_t - Lam_s) CB[t][s] dt_s x_s + exp(Lam_t) C_t . S_in + D x_t,
 //                g = y SiLU(z)
+// The contractions of the state and output passes run on bf16 MFMA 16x16x32 with every fp32
+// operand split as v = hi + lo (hi = bf16(v), lo = bf16(v - hi)) and the product taken as
+// a_hi b_hi + a_hi b_lo + a_lo b_hi: about 16 bits of each operand survive, so each product is
+// within ~2^-16 relative of the fp32 one, at a sixth of the fp32 MFMA cost. Operands used by many
+// products (x, the state) are scaled and split once per chunk into LDS planes; the others (C, CB,
+// B) are split as they are loaded.
 constexpr int kSsdMaxQ = 256, kSsdMaxN = 256, kSsdP = 64, kSsdWaves = 8, kSsdBlock = 64 * kSsdWaves;
+constexpr int kSsdRow = kSsdMaxQ + 8;   // bf16 per LDS plane row (the pad spreads rows over the banks)
+static_assert(kSsdMaxN <= kSsdMaxQ, "state planes share the row length of the x planes");
 
-// Per-chunk prologue shared by the state and output passes: Lam (in log2 units) and dt of the
-// chunk's tokens, and x of the head transposed to Xt[p][t] (zero past the chunk end). Q <=
-// kSsdBlock / 2; one barrier inside, one at the end.
-__device__ __forceinline__ void ssd_chunk_prologue(const SsdArgs &a, int h, int64_t mbase, int len, float *lam2,
-                                                   float *dts, float (*Xt)[kSsdMaxQ + 4], float *tot) {
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+// bf16 MFMA 16x16x32: lane l supplies row (A) / column (B) l % 16 and the 8 contraction indices
+// 8 (l / 16) .. +8, and holds D[4 (l / 16) + r][l % 16] in element r.
+__device__ __forceinline__ f4v mfma_bf(const bf8v &a, const bf8v &b, f4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4v mfma_bf3(const bf8v &ah, const bf8v &al, const bf8v &bh, const bf8v &bl, f4v c) {
+    c = mfma_bf(al, bh, c);
+    c = mfma_bf(ah, bl, c);
+    return mfma_bf(ah, bh, c);
+}
+__device__ __forceinline__ void split8(const float (&v)[8], bf8v &hi, bf8v &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = (__bf16)v[e];
+        lo[e] = (__bf16)(v[e] - (float)hi[e]);
+    }
+}
+__device__ __forceinline__ void split_store2(__bf16 *hi, __bf16 *lo, float v0, float v1) {
+    const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
+    const __bf16 l0 = (__bf16)(v0 - (float)h0), l1 = (__bf16)(v1 - (float)h1);
+    *reinterpret_cast<uint32_t *>(hi) = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    *reinterpret_cast<uint32_t *>(lo) = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+}
+
+// Lam (in log2 units) and dt of the chunk's tokens (DPP block scan; Q <= kSsdBlock / 2); two
+// barriers inside, the results are visible on return.
+__device__ __forceinline__ void ssd_lam(const SsdArgs &a, int h, int64_t mbase, int len, float *lam2, float *dts,
+                                        float *tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float A = -expf(a.A_log[h]);
-    const bool in = tid < len;
-    const float dtv = in ? a.dt[(mbase + tid) * a.H + h] : 0.f;
+    const float dtv = tid < len ? a.dt[(mbase + tid) * a.H + h] : 0.f;
     float v = dtv * A;
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
@@ -417,72 +446,92 @@ __device__ __forceinline__ void ssd_chunk_prologue(const SsdArgs &a, int h, int6
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
     if (lane == 63) tot[wave] = v;
-    // x: thread (t, quarter) loads 16 channels of token t
-    const int t = tid & 255, pq = tid >> 8;   // kSsdBlock = 512: two threads per token, 32 channels each
-    float4 xv[8];
-    if (t < a.Q) {
-        const float *xr = a.xbc + (mbase + min(t, len - 1)) * a.Cd + h * a.P + 32 * pq;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] = *reinterpret_cast<const float4 *>(xr + 4 * j);
-    }
     __syncthreads();
     for (int w = 0; w < wave; ++w) v += tot[w];
-    if (tid < a.Q) {
+    if (tid < kSsdMaxQ) {
         constexpr float kLog2e = 1.4426950408889634f;
         lam2[tid] = v * kLog2e;
         dts[tid] = dtv;
     }
-    if (t < a.Q) {
-        const bool tin = t < len;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (!tin) xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            Xt[32 * pq + 4 * j][t] = xv[j].x;
-            Xt[32 * pq + 4 * j + 1][t] = xv[j].y;
-            Xt[32 * pq + 4 * j + 2][t] = xv[j].z;
-            Xt[32 * pq + 4 * j + 3][t] = xv[j].w;
-        }
-    }
     __syncthreads();
 }
 
-// S_loc of one (b, h, chunk): x is pre-scaled by wend_s = exp(Lam_end - Lam_s) dt_s in LDS. Wave w
-// takes the n-tiles w, w + 8, ... for all four p-tiles, so each B value (read from global in the
-// standard operand layout, 16 tokens at a time) feeds four MFMAs.
+// x of head h for all kSsdMaxQ token slots of the chunk (zero past its end) into planes [p][t]:
+// raw x (hi, lo) when RAW, and x scaled by w_t = dt_t exp(Lam_ref(t) - Lam_t) (hi, lo), with
+// ref(t) = the chunk's last token (END) or the last token of t's 32-token block (!END). Thread:
+// token pair (2 tp, 2 tp + 1), 16 channels. No barrier.
+template <bool END, bool RAW>
+__device__ __forceinline__ void ssd_x_planes(const SsdArgs &a, int h, int64_t mbase, int len, const float *lam2,
+                                             const float *dts, __bf16 *xh, __bf16 *xl, __bf16 *rh, __bf16 *rl) {
+    const int tid = threadIdx.x, tp = tid & 127, cq = tid >> 7;
+    const int t0 = 2 * tp;
+    float4 xv[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float *xr = a.xbc + (mbase + min(t0 + u, len - 1)) * a.Cd + h * a.P + 16 * cq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[u][j] = *reinterpret_cast<const float4 *>(xr + 4 * j);
+    }
+    float w[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = t0 + u;
+        const int ref = END ? len - 1 : min(t | 31, len - 1);
+        w[u] = t < len ? dts[t] * __builtin_amdgcn_exp2f(lam2[ref] - lam2[t]) : 0.f;
+        if (t >= len) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xv[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float x0[4] = {xv[0][j].x, xv[0][j].y, xv[0][j].z, xv[0][j].w};
+        const float x1[4] = {xv[1][j].x, xv[1][j].y, xv[1][j].z, xv[1][j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int o = (16 * cq + 4 * j + e) * kSsdRow + t0;
+            split_store2(xh + o, xl + o, x0[e] * w[0], x1[e] * w[1]);
+            if (RAW) split_store2(rh + o, rl + o, x0[e], x1[e]);
+        }
+    }
+}
+
+// S_loc of one (b, h, chunk) = Xs . B with Xs[p][s] = exp(Lam_end - Lam_s) dt_s x_s (LDS planes)
+// and B[s][n] straight from global memory. Wave w takes the n-tiles w, w + 8, ... for all four
+// p-tiles, so each split B fragment feeds four p-tiles.
 __global__ __launch_bounds__(kSsdBlock) void k_ssd_state(SsdArgs a) {
     __shared__ float lam2[kSsdMaxQ], dts[kSsdMaxQ], tot[kSsdWaves];
-    __shared__ __align__(16) float Xt[kSsdP][kSsdMaxQ + 4];
+    __shared__ __align__(16) __bf16 xh[kSsdP * kSsdRow], xl[kSsdP * kSsdRow];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kq = lane >> 4;
     const int c = blockIdx.x % a.nch, bh = blockIdx.x / a.nch, h = bh % a.H, b = bh / a.H;
     const int g = h * a.G / a.H, Q = a.Q, N = a.N, NT = N / 16;
     const int len = min(Q, a.L - c * Q);
     const int64_t mbase = (int64_t)b * a.L + c * Q;
-    ssd_chunk_prologue(a, h, mbase, len, lam2, dts, Xt, tot);
-    const float lend2 = lam2[len - 1];
-    for (int i = tid; i < kSsdP * Q; i += kSsdBlock) {   // x_s * wend_s (zero past the chunk end: dts = 0)
-        const int p = i / Q, t = i - p * Q;
-        Xt[p][t] *= __builtin_amdgcn_exp2f(lend2 - lam2[t]) * dts[t];
-    }
-    if (tid == 0) a.lam_end[(int64_t)bh * a.nch + c] = lend2 * 0.6931471805599453f;
+    ssd_lam(a, h, mbase, len, lam2, dts, tot);
+    ssd_x_planes<true, false>(a, h, mbase, len, lam2, dts, xh, xl, nullptr, nullptr);
+    if (tid == 0) a.lam_end[(int64_t)bh * a.nch + c] = lam2[len - 1] * 0.6931471805599453f;
     __syncthreads();
     const float *Bbase = a.xbc + mbase * a.Cd + a.E + g * N;
     float *out = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
+    const int nsb = (len + 31) / 32;   // 32-token blocks holding the chunk's tokens
     for (int nt = wave; nt < NT; nt += kSsdWaves) {
         f4v acc[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[pt] = f4v{0.f, 0.f, 0.f, 0.f};
         const float *bcol = Bbase + nt * 16 + r;
-        for (int s0 = 0; s0 < Q; s0 += 16) {
-            float bq[4];
+        for (int sb = 0; sb < nsb; ++sb) {
+            const int s0 = 32 * sb + 8 * kq;
+            float bq[8];   // tokens past the chunk end meet Xs = 0: their (clamped) B values are finite
 #pragma unroll
-            for (int v = 0; v < 4; ++v) bq[v] = bcol[(int64_t)min(s0 + 4 * kq + v, len - 1) * a.Cd];
+            for (int e = 0; e < 8; ++e) bq[e] = bcol[(int64_t)min(s0 + e, len - 1) * a.Cd];
+            bf8v bhv, blv;
+            split8(bq, bhv, blv);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const float4 xv = *reinterpret_cast<const float4 *>(&Xt[16 * pt + r][s0 + 4 * kq]);
-                acc[pt] = mfma4(xv.x, bq[0], acc[pt]);
-                acc[pt] = mfma4(xv.y, bq[1], acc[pt]);
-                acc[pt] = mfma4(xv.z, bq[2], acc[pt]);
-                acc[pt] = mfma4(xv.w, bq[3], acc[pt]);
+                const int o = (16 * pt + r) * kSsdRow + s0;
+                const bf8v ahv = *reinterpret_cast<const bf8v *>(xh + o);
+                const bf8v alv = *reinterpret_cast<const bf8v *>(xl + o);
+                acc[pt] = mfma_bf3(ahv, alv, bhv, blv, acc[pt]);
             }
         }
         // lane l holds S_loc[p = 16 pt + 4 kq + rr][n = 16 nt + r]
@@ -509,117 +558,152 @@ __global__ __launch_bounds__(kBlock) void k_ssd_scan(SsdArgs a) {
     a.state[(int64_t)bh * PN + e] = S;
 }
 
-// Outputs of one (b, h, chunk): wave w owns the t-tiles {w, 15 - w, 16 + w, 31 - w, ...} (balanced
-// causal work) and all four p-tiles of each. Per tile (rows t, first row r0 = 16 ti) three
-// accumulations, each scaled per row at the end:
-//   yo = C_t . S_in                      (x exp(Lam_t))
-//   yc = sum_{s < r0} CB[t][s] x_s u_s,  u_s = dt_s exp(Lam_r0 - Lam_s)   (x exp(Lam_t - Lam_r0))
-//   yd = sum_{r0 <= s <= t} exp(Lam_t - Lam_s) CB[t][s] dt_s x_s          (the diagonal block)
-// Every factor is an exponential of a non-positive number. The state S_in comes through LDS as
-// Sl[p][n]; C and CB rows are read straight from global memory (float4 along the contraction).
+// Outputs of one (b, h, chunk): wave w owns the 16-token t-tiles {w, 15 - w} (balanced causal
+// work) and all four 16-channel p-tiles of each; every term is accumulated already scaled:
+//   phase A  exp(Lam_t) C_t . S_in       A = C_t exp(Lam_t) (split on load), B = S_in (LDS planes)
+//   phase B  off-diagonal 32-token blocks (s <= e = the block's last token < the tile):
+//              sum_s [CB[t][s] exp(Lam_t - Lam_e)] [x_s dt_s exp(Lam_e - Lam_s)]
+//            the diagonal block (the one holding t):
+//              sum_{s <= t} [CB[t][s] exp(Lam_t - Lam_s) dt_s] x_s
+// Every exponential is of a non-positive number. The S_in planes and the x planes share LDS.
 __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
     __shared__ float lam2[kSsdMaxQ], dts[kSsdMaxQ], tot[kSsdWaves];
-    __shared__ __align__(16) float Xt[kSsdP][kSsdMaxQ + 4];
-    __shared__ __align__(16) float Sl[kSsdP][kSsdMaxN + 4];   // [p][n] the state entering the chunk
+    __shared__ __align__(16) __bf16 pl[4][kSsdP * kSsdRow];   // phase A: S_in hi, lo; phase B: xs hi, lo, x hi, lo
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kq = lane >> 4;
     const int c = blockIdx.x % a.nch, bh = blockIdx.x / a.nch, h = bh % a.H, b = bh / a.H;
-    const int g = h * a.G / a.H, Q = a.Q, N = a.N, QT = Q / 16, NT = N / 16;
+    const int g = h * a.G / a.H, Q = a.Q, N = a.N, QT = Q / 16;
     const int len = min(Q, a.L - c * Q);
     const int64_t mbase = (int64_t)b * a.L + c * Q;
     const float Dh = a.D[h];
+    // S_in planes [p][n], zero for n in [N, 32) when N = 16
     {
         const float *sin = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
-        for (int i = tid; i < kSsdP * N / 4; i += kSsdBlock) {
-            const int p = (4 * i) / N, n = (4 * i) % N;
-            *reinterpret_cast<float4 *>(&Sl[p][n]) = *reinterpret_cast<const float4 *>(sin + (int64_t)p * N + n);
+        const int NP = max(N, 32);
+        for (int i = tid; i < kSsdP * NP / 2; i += kSsdBlock) {
+            const int p = (2 * i) / NP, n = (2 * i) % NP;
+            const float2 v = n < N ? *reinterpret_cast<const float2 *>(sin + (int64_t)p * N + n) : make_float2(0.f, 0.f);
+            split_store2(pl[0] + p * kSsdRow + n, pl[1] + p * kSsdRow + n, v.x, v.y);
         }
     }
-    ssd_chunk_prologue(a, h, mbase, len, lam2, dts, Xt, tot);
-    for (int ti = 0; ti < QT; ++ti) {
-        const int owner = ((ti >> 3) & 1) ? 7 - (ti & 7) : (ti & 7);
-        if (owner != wave || ti * 16 >= len) continue;
+    ssd_lam(a, h, mbase, len, lam2, dts, tot);   // its barriers also publish the S_in planes
+    int tiles[2];
+    tiles[0] = wave;
+    tiles[1] = 15 - wave;
+    f4v y[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) y[k][pt] = f4v{0.f, 0.f, 0.f, 0.f};
+    const float *Cbase = a.xbc + mbase * a.Cd + a.E + a.G * N + g * N;
+    // ---- phase A: exp(Lam_t) C_t . S_in
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int ti = tiles[k];
+        if (ti >= QT || ti * 16 >= len) continue;
         const int t = min(ti * 16 + r, len - 1);   // the A-operand row this lane supplies
-        const float lt = lam2[t], lr0 = lam2[ti * 16];
-        const float *Crow = a.xbc + (mbase + t) * a.Cd + a.E + a.G * N + g * N + 4 * kq;
-        const float *cbrow = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * Q * Q + (int64_t)t * Q + 4 * kq;
-        f4v yo[4], yc[4], yd[4];
+        const float et = __builtin_amdgcn_exp2f(lam2[t]);
+        const float *Crow = Cbase + (int64_t)t * a.Cd;
+        for (int n0 = 0; n0 < N; n0 += 32) {
+            const int n = n0 + 8 * kq;
+            float cv[8];
+            if (n < N) {
+                const float4 c0 = *reinterpret_cast<const float4 *>(Crow + n);
+                const float4 c1 = *reinterpret_cast<const float4 *>(Crow + n + 4);
+                cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w;
+                cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
+            } else {
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) yo[pt] = yc[pt] = yd[pt] = f4v{0.f, 0.f, 0.f, 0.f};
-        // C_t . S_in, 64 n at a time (four float4 of C per lane in flight)
-        for (int n0 = 0; n0 < N; n0 += 64) {
-            float4 cv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) cv[u] = *reinterpret_cast<const float4 *>(Crow + min(n0 + 16 * u, N - 16));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (n0 + 16 * u < N) {
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const float4 sv = *reinterpret_cast<const float4 *>(&Sl[16 * pt + r][n0 + 16 * u + 4 * kq]);
-                        yo[pt] = mfma4(cv[u].x, sv.x, yo[pt]);
-                        yo[pt] = mfma4(cv[u].y, sv.y, yo[pt]);
-                        yo[pt] = mfma4(cv[u].z, sv.z, yo[pt]);
-                        yo[pt] = mfma4(cv[u].w, sv.w, yo[pt]);
-                    }
-                }
+                for (int e = 0; e < 8; ++e) cv[e] = 0.f;
             }
-        }
-        // the blocks below the diagonal, 4 s-tiles (64 tokens) at a time
-        for (int j0 = 0; j0 < ti; j0 += 4) {
-            float4 cbv[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) cbv[u] = *reinterpret_cast<const float4 *>(cbrow + 16 * min(j0 + u, ti - 1));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (j0 + u < ti) {
-                    const int s0 = (j0 + u) * 16 + 4 * kq;
-                    const float4 ls = *reinterpret_cast<const float4 *>(&lam2[s0]);
-                    const float4 ds = *reinterpret_cast<const float4 *>(&dts[s0]);
-                    const float u0 = ds.x * __builtin_amdgcn_exp2f(lr0 - ls.x), u1 = ds.y * __builtin_amdgcn_exp2f(lr0 - ls.y);
-                    const float u2 = ds.z * __builtin_amdgcn_exp2f(lr0 - ls.z), u3 = ds.w * __builtin_amdgcn_exp2f(lr0 - ls.w);
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const float4 xv = *reinterpret_cast<const float4 *>(&Xt[16 * pt + r][s0]);
-                        yc[pt] = mfma4(cbv[u].x, xv.x * u0, yc[pt]);
-                        yc[pt] = mfma4(cbv[u].y, xv.y * u1, yc[pt]);
-                        yc[pt] = mfma4(cbv[u].z, xv.z * u2, yc[pt]);
-                        yc[pt] = mfma4(cbv[u].w, xv.w * u3, yc[pt]);
-                    }
-                }
-            }
-        }
-        {   // the diagonal block, masked s <= t
-            const int s0 = ti * 16 + 4 * kq;
-            const float4 cbv = *reinterpret_cast<const float4 *>(cbrow + 16 * ti);
-            const float4 ls = *reinterpret_cast<const float4 *>(&lam2[s0]);
-            const float4 ds = *reinterpret_cast<const float4 *>(&dts[s0]);
-            const float w0 = s0 <= t ? cbv.x * __builtin_amdgcn_exp2f(lt - ls.x) * ds.x : 0.f;
-            const float w1 = s0 + 1 <= t ? cbv.y * __builtin_amdgcn_exp2f(lt - ls.y) * ds.y : 0.f;
-            const float w2 = s0 + 2 <= t ? cbv.z * __builtin_amdgcn_exp2f(lt - ls.z) * ds.z : 0.f;
-            const float w3 = s0 + 3 <= t ? cbv.w * __builtin_amdgcn_exp2f(lt - ls.w) * ds.w : 0.f;
+            for (int e = 0; e < 8; ++e) cv[e] *= et;
+            bf8v ahv, alv;
+            split8(cv, ahv, alv);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const float4 xv = *reinterpret_cast<const float4 *>(&Xt[16 * pt + r][s0]);
-                yd[pt] = mfma4(w0, xv.x, yd[pt]);
-                yd[pt] = mfma4(w1, xv.y, yd[pt]);
-                yd[pt] = mfma4(w2, xv.z, yd[pt]);
-                yd[pt] = mfma4(w3, xv.w, yd[pt]);
+                const int o = (16 * pt + r) * kSsdRow + n;
+                const bf8v bhv = *reinterpret_cast<const bf8v *>(pl[0] + o);
+                const bf8v blv = *reinterpret_cast<const bf8v *>(pl[1] + o);
+                y[k][pt] = mfma_bf3(ahv, alv, bhv, blv, y[k][pt]);
             }
         }
-        // row scales, + D x, gate, out: lane l holds row t = ti*16 + 4 kq + rr, channel p = 16 pt + r
+    }
+    __syncthreads();   // the S_in planes are dead: the x planes take their place
+    ssd_x_planes<false, true>(a, h, mbase, len, lam2, dts, pl[0], pl[1], pl[2], pl[3]);
+    __syncthreads();
+    // ---- phase B: CB-weighted sums over the chunk's earlier tokens
+    const float *cbbase = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * Q * Q;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int ti = tiles[k];
+        if (ti >= QT || ti * 16 >= len) continue;
+        const int t = min(ti * 16 + r, len - 1);
+        const float lt = lam2[t];
+        const float *cbrow = cbbase + (int64_t)t * Q;
+        const int bd = ti >> 1;   // the 32-token block holding the tile
+        for (int sb = 0; sb < bd; ++sb) {
+            const int s0 = 32 * sb + 8 * kq;
+            const float4 c0 = *reinterpret_cast<const float4 *>(cbrow + s0);
+            const float4 c1 = *reinterpret_cast<const float4 *>(cbrow + s0 + 4);
+            const float f = __builtin_amdgcn_exp2f(lt - lam2[32 * sb + 31]);
+            const float cv[8] = {c0.x * f, c0.y * f, c0.z * f, c0.w * f, c1.x * f, c1.y * f, c1.z * f, c1.w * f};
+            bf8v ahv, alv;
+            split8(cv, ahv, alv);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int o = (16 * pt + r) * kSsdRow + s0;
+                const bf8v bhv = *reinterpret_cast<const bf8v *>(pl[0] + o);
+                const bf8v blv = *reinterpret_cast<const bf8v *>(pl[1] + o);
+                y[k][pt] = mfma_bf3(ahv, alv, bhv, blv, y[k][pt]);
+            }
+        }
+        {   // the diagonal block: entries with s > t, or past the chunk, are never read (select, not product)
+            const int s0 = 32 * bd + 8 * kq;
+            float cv[8];
+            if (s0 < Q) {
+                const float4 c0 = *reinterpret_cast<const float4 *>(cbrow + s0);
+                const float4 c1 = *reinterpret_cast<const float4 *>(cbrow + s0 + 4);
+                const float raw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int s = s0 + e;
+                    cv[e] = s <= t ? raw[e] * __builtin_amdgcn_exp2f(lt - lam2[s]) * dts[s] : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cv[e] = 0.f;
+            }
+            bf8v ahv, alv;
+            split8(cv, ahv, alv);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int o = (16 * pt + r) * kSsdRow + s0;
+                const bf8v bhv = *reinterpret_cast<const bf8v *>(pl[2] + o);
+                const bf8v blv = *reinterpret_cast<const bf8v *>(pl[3] + o);
+                y[k][pt] = mfma_bf3(ahv, alv, bhv, blv, y[k][pt]);
+            }
+        }
+        // + D x, gate, out: lane l holds row t = ti*16 + 4 kq + rr, channel p = 16 pt + r
+        float xr[4][4], zr[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t m = mbase + min(ti * 16 + 4 * kq + rr, len - 1);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int64_t col = (int64_t)h * a.P + 16 * pt + r;
+                xr[rr][pt] = a.xbc[m * a.Cd + col];
+                zr[rr][pt] = a.Y[m * a.ldY + col];
+            }
+        }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int tt = ti * 16 + 4 * kq + rr;
             if (tt < len) {
-                const float l2 = lam2[tt];
-                const float eo = __builtin_amdgcn_exp2f(l2), ec = __builtin_amdgcn_exp2f(l2 - lr0);
                 const int64_t m = mbase + tt;
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
-                    const int p = 16 * pt + r;
-                    const int64_t col = (int64_t)h * a.P + p;
-                    const float yv = eo * yo[pt][rr] + ec * yc[pt][rr] + yd[pt][rr] + Dh * Xt[p][tt];
-                    a.g[m * a.E + col] = yv * silu_f(a.Y[m * a.ldY + col]);
+                    const int64_t col = (int64_t)h * a.P + 16 * pt + r;
+                    a.g[m * a.E + col] = (y[k][pt][rr] + Dh * xr[rr][pt]) * silu_f(zr[rr][pt]);
                 }
             }
         }

@@ -175,16 +175,32 @@ def test_prefill_1p3b_2048_tokens_bf16_chunk256():
 
 
 def test_prefill_chunk_lengths_agree():
-    """Every chunk length evaluates the same recurrence: codes agree except at rounding ties and
-    outputs agree within the layer tolerance."""
+    """Every chunk length evaluates the same recurrence. The quantizer rounds half to even, so two
+    correct evaluations that differ by rounding may pick different codes where u * 127 / max|u|
+    sits at a .5 boundary: every code that differs from the chunk-256 run must sit at such a tie,
+    and outputs (and, without a flip, the final states) agree within the layer tolerance up to the
+    first token with a flip."""
     lw = gen.layer_weights(TINY, 9, 15)
     conv0, ssm0 = gen.initial_states(TINY, 1, 9, 15, std=0.2)
-    xs = gen.token_inputs(TINY, (1, 257), 15, tag=6)
+    T = 257
+    xs = gen.token_inputs(TINY, (1, T), 15, tag=6)
     outs = {}
     for c in (16, 32, 64, 128, 256):
-        say(f"case: tiny prefill seqlen 257 chunk {c}")
-        outs[c] = run_prefill(TINY, lw, xs, conv0, ssm0, c, taps=False)
+        say(f"case: tiny prefill seqlen {T} chunk {c}")
+        outs[c] = run_prefill(TINY, lw, xs, conv0, ssm0, c)
+    ref_out, ref_tp, ref_st = outs[256]
     for c in (16, 32, 64, 128):
-        e = max(PY.normwise(outs[c][0][0, t], outs[256][0][0, t]) for t in range(257))
+        out, tp, st = outs[c]
+        first = T
+        for kq, ku in (("in_q", "in_u"), ("out_q", "out_u")):
+            for t in range(T):
+                if (tp[kq][0, t] != ref_tp[kq][0, t]).any():
+                    n, ok = PY.flips_at_ties(ref_tp[ku][0, t], ref_tp[kq][0, t], tp[kq][0, t])
+                    assert ok, f"chunk {c}: {kq} flip away from a rounding tie at token {t}"
+                    first = min(first, t)
+                    break
+        e = max((PY.normwise(out[0, t], ref_out[0, t]) for t in range(first)), default=0.0)
+        say(f"chunk {c}: max normwise difference {e:.2e} over {first} tokens (first code flip: {first < T})")
         assert e < PY.TOL_LAYER, (c, e)
-        assert PY.normwise(outs[c][2][1], outs[256][2][1]) < PY.TOL_LAYER
+        if first == T:
+            assert PY.normwise(st[1], ref_st[1]) < PY.TOL_LAYER
