@@ -94,8 +94,10 @@ struct GemmArgs {
     int32_t *acc_tap;      // optional
     int64_t ldacc;
     void *scratch;         // split-K scratch (gemm_scratch_bytes), 256-byte aligned
+    int counters_zeroed;   // the split-K arrival counters (gemm_counter_words at scratch) are already 0
 };
 size_t gemm_scratch_bytes(int M, int N, int K);
+int gemm_counter_words(int M, int N, int K);   // arrival counters the launch needs zeroed (0: none)
 hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream);
 
 // Per-token RMSNorm + int8 quantizer + int8 LoRA-down for M tokens (prefill / batched decode):
@@ -117,6 +119,8 @@ struct TokQuantArgs {
     float *tap_h, *tap_u, *tap_s;
     int8_t *tap_q;
     int32_t *tap_t;
+    uint32_t *zero_words;  // optional: workgroup 0 sets these nzero words to 0 (the next GEMM's counters)
+    int nzero;
 };
 hipError_t launch_tok_quant(const TokQuantArgs &a, hipStream_t stream);
 

@@ -547,6 +547,12 @@ GemmPlan plan_gemm(int M, int N, int K) {
 
 }  // namespace
 
+int gemm_counter_words(int M, int N, int K) {
+    if (M <= 64) return 0;
+    const GemmPlan p = plan_gemm(M, N, K);
+    return p.splitk > 1 ? p.ntm * p.ntn : 0;
+}
+
 size_t gemm_scratch_bytes(int M, int N, int K) {
     if (M <= 64) return 0;
     const GemmPlan p = plan_gemm(M, N, K);
@@ -568,7 +574,8 @@ hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
     const int tiles = p.ntm * p.ntn;
     if (p.splitk > 1) {
         if (!a.scratch || tiles * 4 > kCntBytes) return hipErrorInvalidValue;
-        k_clear_u32<<<(tiles + kBlock - 1) / kBlock, kBlock, 0, stream>>>(static_cast<uint32_t *>(a.scratch), tiles);
+        if (!a.counters_zeroed)
+            k_clear_u32<<<(tiles + kBlock - 1) / kBlock, kBlock, 0, stream>>>(static_cast<uint32_t *>(a.scratch), tiles);
     }
     const dim3 grid(tiles, p.splitk);
     const bool res = a.res != nullptr;

@@ -6,7 +6,7 @@
 //   1 k_tok_quant      per token: RMSNorm + int8 quantizer, int8 LoRA-down, t' split to bf16
 //   2 k_gemm_pm1       in_proj over all tokens (int8 MFMA) with the Eq. (3) epilogue -> Y
 //   3 k_conv_seq       causal conv over the sequence + SiLU (x, B, C); softplus(dt + dt_bias)
-//   4 k_conv_handoff   final conv state = the last d_conv-1 pre-activation inputs
+//   4 (in k_ssd_cbm)   final conv state = the last d_conv-1 pre-activation inputs
 //   5 SSD, chunk length Q, Lam_t = sum_{tau <= t in chunk} dt_tau A (per head), MFMA:
 //       k_ssd_cbm      CB[t][s] = C_t . B_s for each chunk and group (shared by the group's heads)
 //       k_ssd_state    S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s per chunk, and Lam_end
@@ -49,6 +49,8 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
     const int lr = lane & 31, hsel = lane >> 5;
     const int m0 = blockIdx.x * kTqTok;
     const int K = a.K;
+    if (blockIdx.x == 0)
+        for (int i = tid; i < a.nzero; i += kBlock) a.zero_words[i] = 0u;
     const int nkw = K / 128, nrb = (a.rank + 31) / 32;  // K blocks of 32 per wave; rank blocks of 32
     // Loads are issued in the order their results are needed (norm weight, the rows, then the
     // LoRA-down operands), all before any store, with addresses clamped into range and
@@ -323,22 +325,6 @@ __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
     }
 }
 
-// new state[i] = element L + i of the sequence [old state (3) | inputs (L)]
-__global__ __launch_bounds__(kBlock) void k_conv_handoff(ConvSeqArgs a, float *state, int batch) {
-    const int idx = blockIdx.x * kBlock + threadIdx.x;
-    if (idx >= batch * a.Cd) return;
-    const int b = idx / a.Cd, c = idx - b * a.Cd;
-    float *st = state + (int64_t)idx * (kConvTaps - 1);
-    float nv[kConvTaps - 1];
-#pragma unroll
-    for (int i = 0; i < kConvTaps - 1; ++i) {
-        const int p = a.L + i;  // position in the combined sequence
-        nv[i] = p < kConvTaps - 1 ? st[p] : a.Y[((int64_t)b * a.L + p - (kConvTaps - 1)) * a.ldY + a.E + c];
-    }
-#pragma unroll
-    for (int i = 0; i < kConvTaps - 1; ++i) st[i] = nv[i];
-}
-
 // ------------------------------------------------------------------ 5 SSD
 struct SsdArgs {
     int B, L, H, P, N, G, E, Cd, Q, nch;
@@ -352,6 +338,7 @@ struct SsdArgs {
     float *sloc;           // [B][H][nch][P][N] chunk states (become the states entering each chunk)
     float *state;          // [B][H][P][N] initial -> final
     float *g;              // [M][E] gated output
+    float *conv_state;     // [B][Cd][3]: replaced by the last d_conv-1 pre-activation inputs (k_ssd_cbm)
 };
 
 typedef float f4v __attribute__((ext_vector_type(4)));
@@ -366,6 +353,22 @@ __device__ __forceinline__ f4v mfma4(float a, float b, f4v c) { return __builtin
 // CB[t][s] = C_t . B_s of one 16-token t-tile of chunk c, group g: wave w takes the s-tiles
 // w, w + 4, ... <= the t-tile (only those are read).
 __global__ __launch_bounds__(kBlock) void k_ssd_cbm(SsdArgs a) {
+    {   // conv-state handoff, per (sequence, channel): new state[i] = element L + i of
+        // [old state (3) | the sequence's conv inputs (L)] (the conv pass has read the old state)
+        const int nthr = gridDim.x * gridDim.y * kBlock;
+        for (int idx = (blockIdx.y * gridDim.x + blockIdx.x) * kBlock + threadIdx.x; idx < a.B * a.Cd; idx += nthr) {
+            const int bb = idx / a.Cd, ch = idx - bb * a.Cd;
+            float *st = a.conv_state + (int64_t)idx * (kConvTaps - 1);
+            float nv[kConvTaps - 1];
+#pragma unroll
+            for (int i = 0; i < kConvTaps - 1; ++i) {
+                const int p = a.L + i;
+                nv[i] = p < kConvTaps - 1 ? st[p] : a.Y[((int64_t)bb * a.L + p - (kConvTaps - 1)) * a.ldY + a.E + ch];
+            }
+#pragma unroll
+            for (int i = 0; i < kConvTaps - 1; ++i) st[i] = nv[i];
+        }
+    }
     const int bgc = blockIdx.x, c = bgc % a.nch, g = (bgc / a.nch) % a.G, b = bgc / (a.nch * a.G);
     const int ti = blockIdx.y;
     const int len = min(a.Q, a.L - c * a.Q);
@@ -431,13 +434,16 @@ __device__ __forceinline__ void split_store2(__bf16 *hi, __bf16 *lo, float v0, f
     *reinterpret_cast<uint32_t *>(lo) = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
 }
 
-// Lam (in log2 units) and dt of the chunk's tokens (DPP block scan; Q <= kSsdBlock / 2); two
-// barriers inside, the results are visible on return.
-__device__ __forceinline__ void ssd_lam(const SsdArgs &a, int h, int64_t mbase, int len, float *lam2, float *dts,
-                                        float *tot) {
+// Lam (in log2 units) and dt of the chunk's tokens (DPP block scan over dt_t A, dt_t from
+// ssd_dt_load; Q <= kSsdBlock / 2); two barriers inside, the results are visible on return.
+__device__ __forceinline__ float ssd_dt_load(const SsdArgs &a, int h, int64_t mbase, int len) {
+    const int tid = threadIdx.x;
+    const float v = a.dt[(mbase + min(tid, len - 1)) * a.H + h];
+    return tid < len ? v : 0.f;
+}
+__device__ __forceinline__ void ssd_lam(const SsdArgs &a, int h, float dtv, float *lam2, float *dts, float *tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float A = -expf(a.A_log[h]);
-    const float dtv = tid < len ? a.dt[(mbase + tid) * a.H + h] : 0.f;
     float v = dtv * A;
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
@@ -459,39 +465,44 @@ __device__ __forceinline__ void ssd_lam(const SsdArgs &a, int h, int64_t mbase, 
 // x of head h for all kSsdMaxQ token slots of the chunk (zero past its end) into planes [p][t]:
 // raw x (hi, lo) when RAW, and x scaled by w_t = dt_t exp(Lam_ref(t) - Lam_t) (hi, lo), with
 // ref(t) = the chunk's last token (END) or the last token of t's 32-token block (!END). Thread:
-// token pair (2 tp, 2 tp + 1), 16 channels. No barrier.
-template <bool END, bool RAW>
-__device__ __forceinline__ void ssd_x_planes(const SsdArgs &a, int h, int64_t mbase, int len, const float *lam2,
-                                             const float *dts, __bf16 *xh, __bf16 *xl, __bf16 *rh, __bf16 *rl) {
+// token pair (2 tp, 2 tp + 1), 16 channels. The loads (ssd_x_load) are issued apart from the
+// stores (ssd_x_store) so that they can be in flight during earlier work. No barrier.
+struct SsdXRegs {
+    float4 v[2][4];
+};
+__device__ __forceinline__ void ssd_x_load(const SsdArgs &a, int h, int64_t mbase, int len, SsdXRegs &x) {
     const int tid = threadIdx.x, tp = tid & 127, cq = tid >> 7;
-    const int t0 = 2 * tp;
-    float4 xv[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const float *xr = a.xbc + (mbase + min(t0 + u, len - 1)) * a.Cd + h * a.P + 16 * cq;
+        const float *xr = a.xbc + (mbase + min(2 * tp + u, len - 1)) * a.Cd + h * a.P + 16 * cq;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xv[u][j] = *reinterpret_cast<const float4 *>(xr + 4 * j);
+        for (int j = 0; j < 4; ++j) x.v[u][j] = *reinterpret_cast<const float4 *>(xr + 4 * j);
     }
+}
+template <bool END, bool RAW>
+__device__ __forceinline__ void ssd_x_store(const SsdXRegs &x, int len, const float *lam2, const float *dts, __bf16 *xh,
+                                            __bf16 *xl, __bf16 *rh, __bf16 *rl) {
+    const int tid = threadIdx.x, tp = tid & 127, cq = tid >> 7;
+    const int t0 = 2 * tp;
     float w[2];
+    bool in[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int t = t0 + u;
         const int ref = END ? len - 1 : min(t | 31, len - 1);
-        w[u] = t < len ? dts[t] * __builtin_amdgcn_exp2f(lam2[ref] - lam2[t]) : 0.f;
-        if (t >= len) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xv[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        in[u] = t < len;
+        w[u] = in[u] ? dts[t] * __builtin_amdgcn_exp2f(lam2[ref] - lam2[t]) : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float x0[4] = {xv[0][j].x, xv[0][j].y, xv[0][j].z, xv[0][j].w};
-        const float x1[4] = {xv[1][j].x, xv[1][j].y, xv[1][j].z, xv[1][j].w};
+        const float x0[4] = {x.v[0][j].x, x.v[0][j].y, x.v[0][j].z, x.v[0][j].w};
+        const float x1[4] = {x.v[1][j].x, x.v[1][j].y, x.v[1][j].z, x.v[1][j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int o = (16 * cq + 4 * j + e) * kSsdRow + t0;
-            split_store2(xh + o, xl + o, x0[e] * w[0], x1[e] * w[1]);
-            if (RAW) split_store2(rh + o, rl + o, x0[e], x1[e]);
+            const float r0 = in[0] ? x0[e] : 0.f, r1 = in[1] ? x1[e] : 0.f;
+            split_store2(xh + o, xl + o, r0 * w[0], r1 * w[1]);
+            if (RAW) split_store2(rh + o, rl + o, r0, r1);
         }
     }
 }
@@ -499,7 +510,8 @@ __device__ __forceinline__ void ssd_x_planes(const SsdArgs &a, int h, int64_t mb
 // S_loc of one (b, h, chunk) = Xs . B with Xs[p][s] = exp(Lam_end - Lam_s) dt_s x_s (LDS planes)
 // and B[s][n] straight from global memory. Wave w takes the n-tiles w, w + 8, ... for all four
 // p-tiles, so each split B fragment feeds four p-tiles.
-__global__ __launch_bounds__(kSsdBlock) void k_ssd_state(SsdArgs a) {
+// (two workgroups per compute unit: <= 128 registers)
+__global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_ssd_state(SsdArgs a) {
     __shared__ float lam2[kSsdMaxQ], dts[kSsdMaxQ], tot[kSsdWaves];
     __shared__ __align__(16) __bf16 xh[kSsdP * kSsdRow], xl[kSsdP * kSsdRow];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kq = lane >> 4;
@@ -507,31 +519,51 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_state(SsdArgs a) {
     const int g = h * a.G / a.H, Q = a.Q, N = a.N, NT = N / 16;
     const int len = min(Q, a.L - c * Q);
     const int64_t mbase = (int64_t)b * a.L + c * Q;
-    ssd_lam(a, h, mbase, len, lam2, dts, tot);
-    ssd_x_planes<true, false>(a, h, mbase, len, lam2, dts, xh, xl, nullptr, nullptr);
+    const int nsb = (len + 31) / 32;   // 32-token blocks holding the chunk's tokens
+    const float *Bbase = a.xbc + mbase * a.Cd + a.E + g * N;
+    // B[s][n] of an n-tile, all blocks (rows clamped into the chunk: tokens past its end meet Xs = 0)
+    // B[s][n] of one 32-token block of an n-tile (rows clamped into the chunk: tokens past its end
+    // meet Xs = 0); two blocks in flight: block sb + 1 loads while block sb computes
+    float bq[2][8];
+#define SSD_LOAD_B(nt, sb, dst)                                                                                 \
+    {                                                                                                           \
+        const float *bcol = Bbase + (nt) * 16 + r;                                                              \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e)                                                           \
+            dst[e] = bcol[(int64_t)min(32 * (sb) + 8 * kq + e, len - 1) * a.Cd];                               \
+    }
+    const float dtv = ssd_dt_load(a, h, mbase, len);
+    SsdXRegs xr;
+    ssd_x_load(a, h, mbase, len, xr);
+    SSD_LOAD_B(min(wave, NT - 1), 0, bq[0])   // in flight during the prologue
+    ssd_lam(a, h, dtv, lam2, dts, tot);
+    ssd_x_store<true, false>(xr, len, lam2, dts, xh, xl, nullptr, nullptr);
     if (tid == 0) a.lam_end[(int64_t)bh * a.nch + c] = lam2[len - 1] * 0.6931471805599453f;
     __syncthreads();
-    const float *Bbase = a.xbc + mbase * a.Cd + a.E + g * N;
     float *out = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
-    const int nsb = (len + 31) / 32;   // 32-token blocks holding the chunk's tokens
     for (int nt = wave; nt < NT; nt += kSsdWaves) {
+        if (nt != wave) SSD_LOAD_B(nt, 0, bq[0])
         f4v acc[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[pt] = f4v{0.f, 0.f, 0.f, 0.f};
-        const float *bcol = Bbase + nt * 16 + r;
-        for (int sb = 0; sb < nsb; ++sb) {
+        auto block = [&](int sb, const float (&bv)[8]) {
             const int s0 = 32 * sb + 8 * kq;
-            float bq[8];   // tokens past the chunk end meet Xs = 0: their (clamped) B values are finite
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bq[e] = bcol[(int64_t)min(s0 + e, len - 1) * a.Cd];
             bf8v bhv, blv;
-            split8(bq, bhv, blv);
+            split8(bv, bhv, blv);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 const int o = (16 * pt + r) * kSsdRow + s0;
                 const bf8v ahv = *reinterpret_cast<const bf8v *>(xh + o);
                 const bf8v alv = *reinterpret_cast<const bf8v *>(xl + o);
                 acc[pt] = mfma_bf3(ahv, alv, bhv, blv, acc[pt]);
+            }
+        };
+#pragma unroll 1
+        for (int sb = 0; sb < nsb; sb += 2) {
+            if (sb + 1 < nsb) SSD_LOAD_B(nt, sb + 1, bq[1])
+            block(sb, bq[0]);
+            if (sb + 1 < nsb) {
+                if (sb + 2 < nsb) SSD_LOAD_B(nt, sb + 2, bq[0])
+                block(sb + 1, bq[1]);
             }
         }
         // lane l holds S_loc[p = 16 pt + 4 kq + rr][n = 16 nt + r]
@@ -540,6 +572,7 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_state(SsdArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) out[(int64_t)(16 * pt + 4 * kq + rr) * N + nt * 16 + r] = acc[pt][rr];
     }
+#undef SSD_LOAD_B
 }
 
 // Sequential carry over chunks; sloc[c] is replaced by the state entering chunk c.
@@ -566,85 +599,129 @@ __global__ __launch_bounds__(kBlock) void k_ssd_scan(SsdArgs a) {
 //            the diagonal block (the one holding t):
 //              sum_{s <= t} [CB[t][s] exp(Lam_t - Lam_s) dt_s] x_s
 // Every exponential is of a non-positive number. The S_in planes and the x planes share LDS.
+// NB = 32-wide blocks of d_state (N <= 32 NB). Every global operand of a tile is loaded before the
+// tile's first MFMA (C and the first tile's CB even before the LDS planes are built).
+template <int NB>
 __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
     __shared__ float lam2[kSsdMaxQ], dts[kSsdMaxQ], tot[kSsdWaves];
     __shared__ __align__(16) __bf16 pl[4][kSsdP * kSsdRow];   // phase A: S_in hi, lo; phase B: xs hi, lo, x hi, lo
+    constexpr int kSB = kSsdMaxQ / 32;   // 32-token blocks of a chunk, at most
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kq = lane >> 4;
     const int c = blockIdx.x % a.nch, bh = blockIdx.x / a.nch, h = bh % a.H, b = bh / a.H;
     const int g = h * a.G / a.H, Q = a.Q, N = a.N, QT = Q / 16;
     const int len = min(Q, a.L - c * Q);
     const int64_t mbase = (int64_t)b * a.L + c * Q;
     const float Dh = a.D[h];
-    // S_in planes [p][n], zero for n in [N, 32) when N = 16
-    {
-        const float *sin = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
-        const int NP = max(N, 32);
-        for (int i = tid; i < kSsdP * NP / 2; i += kSsdBlock) {
-            const int p = (2 * i) / NP, n = (2 * i) % NP;
-            const float2 v = n < N ? *reinterpret_cast<const float2 *>(sin + (int64_t)p * N + n) : make_float2(0.f, 0.f);
-            split_store2(pl[0] + p * kSsdRow + n, pl[1] + p * kSsdRow + n, v.x, v.y);
-        }
-    }
-    ssd_lam(a, h, mbase, len, lam2, dts, tot);   // its barriers also publish the S_in planes
     int tiles[2];
+    bool live[2];
     tiles[0] = wave;
     tiles[1] = 15 - wave;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) live[k] = tiles[k] < QT && tiles[k] * 16 < len;
+    // loads in the order their results are needed: dt, S_in, C (phase A), x (phase B planes)
+    const float dtv = ssd_dt_load(a, h, mbase, len);
+    const float *sin = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
+    constexpr int NP = 32 * NB, J = kSsdP * NP / 2 / kSsdBlock;   // S_in planes [p][n], zero for n in [N, NP)
+    float2 sv[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = tid + j * kSsdBlock, p = (2 * i) / NP, n = (2 * i) % NP;
+        sv[j] = *reinterpret_cast<const float2 *>(sin + (int64_t)p * N + min(n, N - 2));
+    }
+    // C rows of both tiles (zero past N)
+    float4 cpre[2][NB][2];
+    const float *Cbase = a.xbc + mbase * a.Cd + a.E + a.G * N + g * N;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (!live[k]) continue;
+        const float *Crow = Cbase + (int64_t)min(tiles[k] * 16 + r, len - 1) * a.Cd;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int n = 32 * nb + 8 * kq;
+            const int nc = min(n, N - 8);
+            cpre[k][nb][0] = *reinterpret_cast<const float4 *>(Crow + nc);
+            cpre[k][nb][1] = *reinterpret_cast<const float4 *>(Crow + nc + 4);
+        }
+    }
+    SsdXRegs xr;
+    ssd_x_load(a, h, mbase, len, xr);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int i = tid + j * kSsdBlock, p = (2 * i) / NP, n = (2 * i) % NP;
+        if (n >= N) sv[j] = make_float2(0.f, 0.f);
+        split_store2(pl[0] + p * kSsdRow + n, pl[1] + p * kSsdRow + n, sv[j].x, sv[j].y);
+    }
+    ssd_lam(a, h, dtv, lam2, dts, tot);   // its barriers also publish the S_in planes
     f4v y[2][4];
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) y[k][pt] = f4v{0.f, 0.f, 0.f, 0.f};
-    const float *Cbase = a.xbc + mbase * a.Cd + a.E + a.G * N + g * N;
     // ---- phase A: exp(Lam_t) C_t . S_in
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const int ti = tiles[k];
-        if (ti >= QT || ti * 16 >= len) continue;
-        const int t = min(ti * 16 + r, len - 1);   // the A-operand row this lane supplies
-        const float et = __builtin_amdgcn_exp2f(lam2[t]);
-        const float *Crow = Cbase + (int64_t)t * a.Cd;
-        for (int n0 = 0; n0 < N; n0 += 32) {
-            const int n = n0 + 8 * kq;
-            float cv[8];
-            if (n < N) {
-                const float4 c0 = *reinterpret_cast<const float4 *>(Crow + n);
-                const float4 c1 = *reinterpret_cast<const float4 *>(Crow + n + 4);
-                cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w;
-                cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
-            } else {
+        if (!live[k]) continue;
+        const float et = __builtin_amdgcn_exp2f(lam2[min(tiles[k] * 16 + r, len - 1)]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) cv[e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cv[e] *= et;
+        for (int nb = 0; nb < NB; ++nb) {
+            const float e = 32 * nb + 8 * kq < N ? et : 0.f;   // d_state columns past N (clamped loads) count 0
+            const float4 c0 = cpre[k][nb][0], c1 = cpre[k][nb][1];
+            const float cv[8] = {c0.x * e, c0.y * e, c0.z * e, c0.w * e, c1.x * e, c1.y * e, c1.z * e, c1.w * e};
             bf8v ahv, alv;
             split8(cv, ahv, alv);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const int o = (16 * pt + r) * kSsdRow + n;
+                const int o = (16 * pt + r) * kSsdRow + 32 * nb + 8 * kq;
                 const bf8v bhv = *reinterpret_cast<const bf8v *>(pl[0] + o);
                 const bf8v blv = *reinterpret_cast<const bf8v *>(pl[1] + o);
                 y[k][pt] = mfma_bf3(ahv, alv, bhv, blv, y[k][pt]);
             }
         }
     }
+    // CB rows of a tile, blocks 0..bd (the diagonal block's columns clamped into the row when Q = 16)
+    const float *cbbase = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * Q * Q;
+    float4 cbp[kSB][2];
+    auto load_cb = [&](int k) {
+        const int ti = tiles[k], bd = ti >> 1;
+        const float *cbrow = cbbase + (int64_t)min(ti * 16 + r, len - 1) * Q;
+#pragma unroll
+        for (int sb = 0; sb < kSB; ++sb) {
+            if (sb > bd) break;
+            const int s0 = min(32 * sb + 8 * kq, Q - 8);
+            cbp[sb][0] = *reinterpret_cast<const float4 *>(cbrow + s0);
+            cbp[sb][1] = *reinterpret_cast<const float4 *>(cbrow + s0 + 4);
+        }
+    };
+    if (live[0]) load_cb(0);
     __syncthreads();   // the S_in planes are dead: the x planes take their place
-    ssd_x_planes<false, true>(a, h, mbase, len, lam2, dts, pl[0], pl[1], pl[2], pl[3]);
+    ssd_x_store<false, true>(xr, len, lam2, dts, pl[0], pl[1], pl[2], pl[3]);
     __syncthreads();
     // ---- phase B: CB-weighted sums over the chunk's earlier tokens
-    const float *cbbase = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * Q * Q;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
+        if (!live[k]) continue;
+        if (k == 1) load_cb(1);
         const int ti = tiles[k];
-        if (ti >= QT || ti * 16 >= len) continue;
+        // + D x and the gate of the tile's outputs: lane l holds row ti*16 + 4 kq + rr, channel 16 pt + r
+        float xr[4][4], zr[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t m = mbase + min(ti * 16 + 4 * kq + rr, len - 1);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int64_t col = (int64_t)h * a.P + 16 * pt + r;
+                xr[rr][pt] = a.xbc[m * a.Cd + col];
+                zr[rr][pt] = a.Y[m * a.ldY + col];
+            }
+        }
         const int t = min(ti * 16 + r, len - 1);
         const float lt = lam2[t];
-        const float *cbrow = cbbase + (int64_t)t * Q;
         const int bd = ti >> 1;   // the 32-token block holding the tile
-        for (int sb = 0; sb < bd; ++sb) {
+#pragma unroll
+        for (int sb = 0; sb < kSB; ++sb) {
+            if (sb >= bd) break;
             const int s0 = 32 * sb + 8 * kq;
-            const float4 c0 = *reinterpret_cast<const float4 *>(cbrow + s0);
-            const float4 c1 = *reinterpret_cast<const float4 *>(cbrow + s0 + 4);
+            const float4 c0 = cbp[sb][0], c1 = cbp[sb][1];
             const float f = __builtin_amdgcn_exp2f(lt - lam2[32 * sb + 31]);
             const float cv[8] = {c0.x * f, c0.y * f, c0.z * f, c0.w * f, c1.x * f, c1.y * f, c1.z * f, c1.w * f};
             bf8v ahv, alv;
@@ -659,19 +736,19 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
         }
         {   // the diagonal block: entries with s > t, or past the chunk, are never read (select, not product)
             const int s0 = 32 * bd + 8 * kq;
-            float cv[8];
-            if (s0 < Q) {
-                const float4 c0 = *reinterpret_cast<const float4 *>(cbrow + s0);
-                const float4 c1 = *reinterpret_cast<const float4 *>(cbrow + s0 + 4);
-                const float raw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int s = s0 + e;
-                    cv[e] = s <= t ? raw[e] * __builtin_amdgcn_exp2f(lt - lam2[s]) * dts[s] : 0.f;
+            for (int sb = 0; sb < kSB; ++sb)
+                if (sb == bd) {
+                    c0 = cbp[sb][0];
+                    c1 = cbp[sb][1];
                 }
-            } else {
+            const float raw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            float cv[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) cv[e] = 0.f;
+            for (int e = 0; e < 8; ++e) {
+                const int s = s0 + e;
+                cv[e] = s <= t ? raw[e] * __builtin_amdgcn_exp2f(lt - lam2[s]) * dts[s] : 0.f;
             }
             bf8v ahv, alv;
             split8(cv, ahv, alv);
@@ -681,18 +758,6 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
                 const bf8v bhv = *reinterpret_cast<const bf8v *>(pl[2] + o);
                 const bf8v blv = *reinterpret_cast<const bf8v *>(pl[3] + o);
                 y[k][pt] = mfma_bf3(ahv, alv, bhv, blv, y[k][pt]);
-            }
-        }
-        // + D x, gate, out: lane l holds row t = ti*16 + 4 kq + rr, channel p = 16 pt + r
-        float xr[4][4], zr[4][4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int64_t m = mbase + min(ti * 16 + 4 * kq + rr, len - 1);
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int64_t col = (int64_t)h * a.P + 16 * pt + r;
-                xr[rr][pt] = a.xbc[m * a.Cd + col];
-                zr[rr][pt] = a.Y[m * a.ldY + col];
             }
         }
 #pragma unroll
@@ -961,8 +1026,6 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         dim3 grid(batch * ((seqlen + kConvRun - 1) / kConvRun), (s.Cd + s.H + kBlock - 1) / kBlock);
         k_conv_seq<<<grid, kBlock, 0, stream>>>(cv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_conv_handoff<<<(batch * s.Cd + kBlock - 1) / kBlock, kBlock, 0, stream>>>(cv, st.conv, batch);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 5. chunked SSD
     {
@@ -988,6 +1051,7 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.sloc = ws.sloc;
         a.state = st.ssm;
         a.g = ws.gbuf;
+        a.conv_state = st.conv;
         k_ssd_cbm<<<dim3(batch * s.G * nch, chunk / 16), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int nblk = batch * s.H * nch;
@@ -995,7 +1059,10 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_ssd_scan<<<dim3((s.P * s.N + kBlock - 1) / kBlock, batch * s.H), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ssd_out<<<nblk, kSsdBlock, 0, stream>>>(a);
+        if (s.N <= 32) k_ssd_out<1><<<nblk, kSsdBlock, 0, stream>>>(a);
+        else if (s.N <= 64) k_ssd_out<2><<<nblk, kSsdBlock, 0, stream>>>(a);
+        else if (s.N <= 128) k_ssd_out<4><<<nblk, kSsdBlock, 0, stream>>>(a);
+        else k_ssd_out<8><<<nblk, kSsdBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 6. out: gated RMSNorm + quantizer + LoRA-down of g
@@ -1020,6 +1087,8 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.tap_q = tp.out_q;
         a.tap_s = tp.out_s;
         a.tap_t = tp.out_t;
+        a.zero_words = static_cast<uint32_t *>(ws.gemm_scratch);   // the out_proj GEMM's split-K counters
+        a.nzero = gemm_counter_words(M, s.D, s.E);
         if ((e = launch_tok_quant(a, stream)) != hipSuccess) return e;
     }
     // 7. out_proj GEMM + residual. The residual is the fp32 (or bf16-widened) layer input.
@@ -1055,6 +1124,7 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.acc_tap = tp.out_acc;
         a.ldacc = s.D;
         a.scratch = ws.gemm_scratch;
+        a.counters_zeroed = 1;
         if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
     }
     return hipSuccess;
