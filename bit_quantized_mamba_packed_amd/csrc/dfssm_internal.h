@@ -95,6 +95,7 @@ struct GemmArgs {
     int64_t ldacc;
     void *scratch;         // split-K scratch (gemm_scratch_bytes), 256-byte aligned
     int counters_zeroed;   // the split-K arrival counters (gemm_counter_words at scratch) are already 0
+                           // (every launch leaves them 0 again: the last arrival of a tile resets its counter)
 };
 size_t gemm_scratch_bytes(int M, int N, int K);
 int gemm_counter_words(int M, int N, int K);   // arrival counters the launch needs zeroed (0: none)

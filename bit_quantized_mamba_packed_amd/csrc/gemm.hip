@@ -138,11 +138,15 @@ __device__ __forceinline__ void store_block(const GemmArgs &a, const v16i &acc, 
 // main loop (their latency hides behind it); larger ranks reuse the main-loop buffers afterwards.
 constexpr int A_BYTES = BM * LDS_ROW;
 constexpr int kCntBytes = 4096;
-constexpr int kMainLds = 2 * A_BYTES + 2 * 256 * 16;
+template <int BN>
+constexpr int main_lds() { return 2 * A_BYTES + 2 * BN * 16; }
 constexpr int kEarlyRank = 32;
-constexpr int epi_lds_bytes(int rank) { return 1024 + 2 * BM * (rank + 8) * 2 + 256 * (rank + 8); }
-constexpr int kTileSmem = kMainLds + epi_lds_bytes(kEarlyRank);
-static_assert(epi_lds_bytes(kMaxRank) <= kTileSmem, "tile LDS");
+template <int BN>
+constexpr int epi_lds_bytes(int rank) { return 1024 + 2 * BM * (rank + 8) * 2 + BN * (rank + 8); }
+template <int BN>
+constexpr int tile_smem() { return main_lds<BN>() + epi_lds_bytes<BN>(kEarlyRank); }
+static_assert(epi_lds_bytes<256>(kMaxRank) <= tile_smem<256>() && epi_lds_bytes<128>(kMaxRank) <= tile_smem<128>(),
+              "tile LDS");
 
 // Workgroup barrier that orders LDS only: outstanding global stores (the epilogue's) are not waited for.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -206,7 +210,8 @@ template <int WNB, bool SPLIT, bool RES>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tile(GemmArgs a, int ntm,
                                                                                               int ntn, int splitk) {
     constexpr int BN = 64 * WNB, NBW = WNB / 2;   // N blocks of 32 per wave
-    __shared__ __align__(16) char smem[kTileSmem];
+    constexpr int BCOL = BN > kBlock ? BN / kBlock : 1;   // sign-bit columns staged per thread
+    __shared__ __align__(16) char smem[tile_smem<BN>()];
     __shared__ int last_flag;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave;
@@ -230,29 +235,39 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int kt0 = z * nk / splitk, kt1 = (z + 1) * nk / splitk;
     auto As = [&](int b) { return reinterpret_cast<int8_t *>(smem) + b * A_BYTES; };
     auto Bs = [&](int b) { return reinterpret_cast<uint8_t *>(smem) + 2 * A_BYTES + b * (BN * 16); };
-    // A staging: thread -> row tid/2, 64-byte half tid%2;  B staging: thread -> column tid (< BN)
+    // A staging: thread -> row tid/2, 64-byte half tid%2;  B staging: thread -> columns tid + kBlock c (< BN)
     const int srow = tid >> 1, shalf = tid & 1;
     const bool arow_ok = m0 + srow < a.M;
     const int8_t *qrow = a.q + (int64_t)(arow_ok ? m0 + srow : 0) * a.ldq + shalf * 64;
-    const bool bcol_ok = tid < BN && n0 + tid < a.N;
-    const uint8_t *bsrc = a.sign + (int64_t)(bcol_ok ? n0 + tid : 0) * (K >> 3);
+    bool bcol_ok[BCOL];
+    const uint8_t *bsrc[BCOL];
+#pragma unroll
+    for (int c = 0; c < BCOL; ++c) {
+        const int col = tid + kBlock * c;
+        bcol_ok[c] = col < BN && n0 + col < a.N;
+        bsrc[c] = a.sign + (int64_t)(bcol_ok[c] ? n0 + col : 0) * (K >> 3);
+    }
     // one register stage: the global loads of step k + 1 are issued while step k computes
     struct Stage {
         int4 a[4];
-        uint4 b;
+        uint4 b[BCOL];
     };
     Stage st0;
     auto gload = [&](Stage &st, int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             st.a[i] = arow_ok ? *reinterpret_cast<const int4 *>(qrow + k0 + 16 * i) : make_int4(0, 0, 0, 0);
-        st.b = bcol_ok ? *reinterpret_cast<const uint4 *>(bsrc + (k0 >> 3)) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int c = 0; c < BCOL; ++c)
+            st.b[c] = bcol_ok[c] ? *reinterpret_cast<const uint4 *>(bsrc[c] + (k0 >> 3)) : make_uint4(0u, 0u, 0u, 0u);
     };
     auto sstore = [&](const Stage &st, int buf) {
         int8_t *d = As(buf) + srow * LDS_ROW + shalf * 64;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<int4 *>(d + 16 * i) = st.a[i];
-        if (tid < BN) *reinterpret_cast<uint4 *>(Bs(buf) + tid * 16) = st.b;
+#pragma unroll
+        for (int c = 0; c < BCOL; ++c)
+            if (tid + kBlock * c < BN) *reinterpret_cast<uint4 *>(Bs(buf) + (tid + kBlock * c) * 16) = st.b[c];
     };
     v16i acc[4][NBW];
 #pragma unroll
@@ -263,7 +278,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
     gload(st0, kt0 * KT);
     const bool early = a.rank <= kEarlyRank;
-    char *epi = smem + (early ? kMainLds : 0);
+    char *epi = smem + (early ? main_lds<BN>() : 0);
     if (early) stage_epilogue<BN>(a, epi, m0, n0, tid);
     // per-column scales of the epilogue, loaded now so that no load follows the epilogue's stores
     float sc[NBW], us[NBW];
@@ -325,6 +340,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         __syncthreads();
         if (!last_flag) return;
+        if (tid == 0) cnt[tile] = 0u;   // every other arrival is in: the counter is free for the next launch
         for (int z2 = 0; z2 < splitk; ++z2) {
             if (z2 == z) continue;
             const int32_t *o = part + ((int64_t)tile * splitk + z2) * tsz;
@@ -541,7 +557,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
     p.ntn = (N + 127) / 128;
     const int64_t tiles = (int64_t)p.ntm * p.ntn;
     p.splitk = 1;
-    while (tiles * p.splitk * 2 <= 512 && p.splitk * 2 <= nk && p.splitk < 8) p.splitk *= 2;
+    while (tiles * p.splitk * 2 <= 512 && p.splitk * 2 <= nk && p.splitk < 4) p.splitk *= 2;
     return p;
 }
 

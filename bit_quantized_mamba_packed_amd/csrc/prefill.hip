@@ -16,6 +16,8 @@
 //     (exponentials only of Lam differences, or of Lam itself: never positive)
 //   6 k_tok_quant      gated RMSNorm + quantizer + LoRA-down of g
 //   7 k_gemm_pm1       out_proj with the residual add -> x_out
+#include <algorithm>
+
 #include "decode_device.h"
 
 namespace dfssm {
@@ -298,6 +300,11 @@ __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
     if (col >= a.Cd + a.H) return;
     const int t1 = min(a.L, t0 + kConvRun);
     const int64_t mb = (int64_t)b * a.L;
+    // every input of the run is loaded before the first store (a load behind a store waits for it)
+    const int64_t ycol = a.E + col;
+    float yv[kConvRun];
+#pragma unroll
+    for (int i = 0; i < kConvRun; ++i) yv[i] = a.Y[(mb + min(t0 + i, t1 - 1)) * a.ldY + ycol];
     if (col < a.Cd) {
         const float4 w = *reinterpret_cast<const float4 *>(a.conv_w + (int64_t)col * kConvTaps);
         const float bias = a.conv_b[col];
@@ -306,13 +313,15 @@ __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
 #pragma unroll
         for (int k = 0; k < kConvTaps - 1; ++k) {
             const int tok = t0 - (kConvTaps - 1) + k;
-            win[k] = tok >= 0 ? a.Y[(mb + tok) * a.ldY + a.E + col]
+            win[k] = tok >= 0 ? a.Y[(mb + tok) * a.ldY + ycol]
                               : a.conv_state[((int64_t)b * a.Cd + col) * (kConvTaps - 1) + (kConvTaps - 1) + tok];
         }
-        for (int t = t0; t < t1; ++t) {
-            const float x = a.Y[(mb + t) * a.ldY + a.E + col];
+#pragma unroll
+        for (int i = 0; i < kConvRun; ++i) {
+            if (t0 + i >= t1) break;
+            const float x = yv[i];
             const float v = bias + w.x * win[0] + w.y * win[1] + w.z * win[2] + w.w * x;
-            a.xbc[(mb + t) * a.Cd + col] = silu_f(v);
+            a.xbc[(mb + t0 + i) * a.Cd + col] = silu_f(v);
             win[0] = win[1];
             win[1] = win[2];
             win[2] = x;
@@ -320,8 +329,11 @@ __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
     } else {
         const int h = col - a.Cd;
         const float db = a.dt_bias[h];
-        for (int t = t0; t < t1; ++t)
-            a.dt[(mb + t) * a.H + h] = softplus_f(a.Y[(mb + t) * a.ldY + a.E + a.Cd + h] + db);
+#pragma unroll
+        for (int i = 0; i < kConvRun; ++i) {
+            if (t0 + i >= t1) break;
+            a.dt[(mb + t0 + i) * a.H + h] = softplus_f(yv[i] + db);
+        }
     }
 }
 
@@ -340,6 +352,8 @@ struct SsdArgs {
     float *g;              // [M][E] gated output
     float *conv_state;     // [B][Cd][3]: replaced by the last d_conv-1 pre-activation inputs (k_ssd_cbm)
 };
+
+constexpr int kSsdMaxQ = 256, kSsdMaxN = 256, kSsdP = 64, kSsdWaves = 8, kSsdBlock = 64 * kSsdWaves;
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f4v mfma4(float a, float b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
@@ -375,21 +389,45 @@ __global__ __launch_bounds__(kBlock) void k_ssd_cbm(SsdArgs a) {
     if (ti * 16 >= len) return;   // no barriers in this kernel
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, kq = lane >> 4;
     const int64_t mbase = (int64_t)b * a.L + c * a.Q;
+    constexpr int NCM = kSsdMaxN / 16;
+    const int NC = a.N / 16;
+    // the t-tile's C fragments once, then the B fragments of each s-tile, the next s-tile's in flight
+    // while the current one computes
     const float *Crow = a.xbc + (mbase + min(ti * 16 + r, len - 1)) * a.Cd + a.E + a.G * a.N + g * a.N + 4 * kq;
-    float *out = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * a.Q * a.Q;
-    for (int si = wave; si <= ti; si += kWaves) {
+    float4 cv[NCM], bv[2][NCM];
+#pragma unroll
+    for (int j = 0; j < NCM; ++j)
+        if (j < NC) cv[j] = *reinterpret_cast<const float4 *>(Crow + 16 * j);
+    auto load_b = [&](int si, float4 (&dst)[NCM]) {
         const float *Brow = a.xbc + (mbase + min(si * 16 + r, len - 1)) * a.Cd + a.E + g * a.N + 4 * kq;
+#pragma unroll
+        for (int j = 0; j < NCM; ++j)
+            if (j < NC) dst[j] = *reinterpret_cast<const float4 *>(Brow + 16 * j);
+    };
+    float *out = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * a.Q * a.Q;
+    auto tile = [&](int si, const float4 (&bt)[NCM]) {
         f4v acc = {0.f, 0.f, 0.f, 0.f};
-        for (int n0 = 0; n0 < a.N; n0 += 16) {
-            const float4 cv = *reinterpret_cast<const float4 *>(Crow + n0);
-            const float4 bv = *reinterpret_cast<const float4 *>(Brow + n0);
-            acc = mfma4(cv.x, bv.x, acc);
-            acc = mfma4(cv.y, bv.y, acc);
-            acc = mfma4(cv.z, bv.z, acc);
-            acc = mfma4(cv.w, bv.w, acc);
+#pragma unroll
+        for (int j = 0; j < NCM; ++j) {
+            if (j < NC) {
+                acc = mfma4(cv[j].x, bt[j].x, acc);
+                acc = mfma4(cv[j].y, bt[j].y, acc);
+                acc = mfma4(cv[j].z, bt[j].z, acc);
+                acc = mfma4(cv[j].w, bt[j].w, acc);
+            }
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) out[(int64_t)(ti * 16 + 4 * kq + rr) * a.Q + si * 16 + r] = acc[rr];
+    };
+    if (wave <= ti) load_b(wave, bv[0]);
+#pragma unroll 1
+    for (int si = wave; si <= ti; si += 2 * kWaves) {
+        if (si + kWaves <= ti) load_b(si + kWaves, bv[1]);
+        tile(si, bv[0]);
+        if (si + kWaves <= ti) {
+            if (si + 2 * kWaves <= ti) load_b(si + 2 * kWaves, bv[0]);
+            tile(si + kWaves, bv[1]);
+        }
     }
 }
 
@@ -405,7 +443,6 @@ __global__ __launch_bounds__(kBlock) void k_ssd_cbm(SsdArgs a) {
 // within ~2^-16 relative of the fp32 one, at a sixth of the fp32 MFMA cost. Operands used by many
 // products (x, the state) are scaled and split once per chunk into LDS planes; the others (C, CB,
 // B) are split as they are loaded.
-constexpr int kSsdMaxQ = 256, kSsdMaxN = 256, kSsdP = 64, kSsdWaves = 8, kSsdBlock = 64 * kSsdWaves;
 constexpr int kSsdRow = kSsdMaxQ + 8;   // bf16 per LDS plane row (the pad spreads rows over the banks)
 static_assert(kSsdMaxN <= kSsdMaxQ, "state planes share the row length of the x planes");
 
@@ -575,18 +612,29 @@ __global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) 
 #undef SSD_LOAD_B
 }
 
-// Sequential carry over chunks; sloc[c] is replaced by the state entering chunk c.
+// Sequential carry over chunks; sloc[c] is replaced by the state entering chunk c. Chunks go in
+// groups of kScanGroup whose loads are all issued before the group's stores.
+constexpr int kScanGroup = 8;
 __global__ __launch_bounds__(kBlock) void k_ssd_scan(SsdArgs a) {
     const int64_t PN = (int64_t)a.P * a.N;
     const int bh = blockIdx.y;
     const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (e >= PN) return;
     float S = a.state[(int64_t)bh * PN + e];
-    for (int c = 0; c < a.nch; ++c) {
-        float *slot = a.sloc + ((int64_t)bh * a.nch + c) * PN + e;
-        const float loc = *slot;
-        *slot = S;
-        S = expf(a.lam_end[(int64_t)bh * a.nch + c]) * S + loc;
+    for (int c0 = 0; c0 < a.nch; c0 += kScanGroup) {
+        float loc[kScanGroup], dec[kScanGroup];
+#pragma unroll
+        for (int i = 0; i < kScanGroup; ++i) {
+            const int c = min(c0 + i, a.nch - 1);
+            loc[i] = a.sloc[((int64_t)bh * a.nch + c) * PN + e];
+            dec[i] = a.lam_end[(int64_t)bh * a.nch + c];
+        }
+#pragma unroll
+        for (int i = 0; i < kScanGroup; ++i) {
+            if (c0 + i >= a.nch) break;
+            a.sloc[((int64_t)bh * a.nch + c0 + i) * PN + e] = S;
+            S = expf(dec[i]) * S + loc[i];
+        }
     }
     a.state[(int64_t)bh * PN + e] = S;
 }
@@ -959,7 +1007,8 @@ PrefillWs carve_prefill_ws(const Shape &s, int batch, int seqlen, int chunk, voi
     w.qsum_out = static_cast<int32_t *>(take(M * 4));
     w.thi_out = static_cast<__bf16 *>(take(M * s.Rout * 2));
     w.tlo_out = static_cast<__bf16 *>(take(M * s.Rout * 2));
-    w.gemm_scratch = take(std::max(gemm_scratch_bytes((int)M, s.Ninp, s.D), gemm_scratch_bytes((int)M, s.D, s.E)));
+    w.gemm_scratch = take(std::max({gemm_scratch_bytes((int)M, s.Ninp, s.D), gemm_scratch_bytes((int)M, 2 * s.E, s.D),
+                                    gemm_scratch_bytes((int)M, s.Ninp - 2 * s.E, s.D), gemm_scratch_bytes((int)M, s.D, s.E)}));
     w.bytes = off;
     return w;
 }
@@ -994,6 +1043,10 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.tap_q = tp.in_q;
         a.tap_s = tp.in_s;
         a.tap_t = tp.in_t;
+        // the split-K counters of this layer's GEMMs (each launch leaves them zero again)
+        a.zero_words = static_cast<uint32_t *>(ws.gemm_scratch);
+        a.nzero = std::max({gemm_counter_words(M, 2 * s.E, s.D), gemm_counter_words(M, s.Ninp - 2 * s.E, s.D),
+                            gemm_counter_words(M, s.D, s.E)});
         if ((e = launch_tok_quant(a, stream)) != hipSuccess) return e;
     }
     // 2. in_proj GEMM
@@ -1003,22 +1056,30 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.ldq = s.D;
         a.qsum = ws.qsum_in;
         a.s = ws.s_in;
-        a.sign = w.in_proj.sign;
         a.M = M;
-        a.N = s.Ninp;
         a.K = s.D;
-        a.row_scale = w.in_proj.row_scale;
-        a.up_scale = w.in_proj.lora_up_scale;
-        a.lora_up = w.in_proj.lora_up;
         a.rank = s.Rin;
         a.thi = ws.thi_in;
         a.tlo = ws.tlo_in;
-        a.y = ws.Y;
         a.ldy = s.Ninp;
-        a.acc_tap = tp.in_acc;
         a.ldacc = s.Ninp;
         a.scratch = ws.gemm_scratch;
-        if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
+        // two launches: the z | x rows (wide tiles, a whole number of them), then the B | C | dt rows
+        // (few columns: narrow tiles with the K range split), so that neither leaves a short tail
+        // of whole tiles behind
+        const int cuts[3] = {0, 2 * s.E, s.Ninp};
+        for (int part = 0; part < 2; ++part) {
+            const int n0 = cuts[part];
+            a.N = cuts[part + 1] - n0;
+            a.sign = w.in_proj.sign + (int64_t)n0 * (s.D / 8);
+            a.row_scale = w.in_proj.row_scale + n0;
+            a.up_scale = w.in_proj.lora_up_scale + n0;
+            a.lora_up = w.in_proj.lora_up + (int64_t)n0 * s.Rin;
+            a.y = ws.Y + n0;
+            a.acc_tap = tp.in_acc ? tp.in_acc + n0 : nullptr;
+            a.counters_zeroed = 1;
+            if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
+        }
     }
     // 3/4. conv over the sequence, dt, conv-state handoff
     ConvSeqArgs cv{ws.Y, s.Ninp, s.E, s.Cd, s.H, seqlen, M, w.conv_w, w.conv_b, w.dt_bias, st.conv, ws.xbc, ws.dt};
@@ -1087,8 +1148,6 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.tap_q = tp.out_q;
         a.tap_s = tp.out_s;
         a.tap_t = tp.out_t;
-        a.zero_words = static_cast<uint32_t *>(ws.gemm_scratch);   // the out_proj GEMM's split-K counters
-        a.nzero = gemm_counter_words(M, s.D, s.E);
         if ((e = launch_tok_quant(a, stream)) != hipSuccess) return e;
     }
     // 7. out_proj GEMM + residual. The residual is the fp32 (or bf16-widened) layer input.
