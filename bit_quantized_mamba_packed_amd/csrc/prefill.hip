@@ -643,17 +643,16 @@ __global__ __launch_bounds__(kBlock) void k_ssd_scan(SsdArgs a) {
 // work) and all four 16-channel p-tiles of each; every term is accumulated already scaled:
 //   phase A  exp(Lam_t) C_t . S_in       A = C_t exp(Lam_t) (split on load), B = S_in (LDS planes)
 //   phase B  off-diagonal 32-token blocks (s <= e = the block's last token < the tile):
-//              sum_s [CB[t][s] exp(Lam_t - Lam_e)] [x_s dt_s exp(Lam_e - Lam_s)]
+//              sum_s [CB[t][s] exp(Lam_t - Lam_e)] [x_s dt_s exp(Lam_e - Lam_s)]   (B: LDS planes)
 //            the diagonal block (the one holding t):
-//              sum_{s <= t} [CB[t][s] exp(Lam_t - Lam_s) dt_s] x_s
-// Every exponential is of a non-positive number. The S_in planes and the x planes share LDS.
-// NB = 32-wide blocks of d_state (N <= 32 NB). Every global operand of a tile is loaded before the
-// tile's first MFMA (C and the first tile's CB even before the LDS planes are built).
+//              sum_{s <= t} [CB[t][s] exp(Lam_t - Lam_s) dt_s] x_s                 (B: x from memory)
+// Every exponential is of a non-positive number. The S_in planes and the x planes share 67.5 KB of
+// LDS and the kernel keeps to 128 registers, so two workgroups share a compute unit and one
+// workgroup's loads overlap the other's MFMA work. NB = 32-wide blocks of d_state (N <= 32 NB).
 template <int NB>
-__global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
+__global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_ssd_out(SsdArgs a) {
     __shared__ float lam2[kSsdMaxQ], dts[kSsdMaxQ], tot[kSsdWaves];
-    __shared__ __align__(16) __bf16 pl[4][kSsdP * kSsdRow];   // phase A: S_in hi, lo; phase B: xs hi, lo, x hi, lo
-    constexpr int kSB = kSsdMaxQ / 32;   // 32-token blocks of a chunk, at most
+    __shared__ __align__(16) __bf16 pl[2][kSsdP * kSsdRow];   // phase A: S_in hi, lo; phase B: xs hi, lo
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kq = lane >> 4;
     const int c = blockIdx.x % a.nch, bh = blockIdx.x / a.nch, h = bh % a.H, b = bh / a.H;
     const int g = h * a.G / a.H, Q = a.Q, N = a.N, QT = Q / 16;
@@ -666,38 +665,22 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
     tiles[1] = 15 - wave;
 #pragma unroll
     for (int k = 0; k < 2; ++k) live[k] = tiles[k] < QT && tiles[k] * 16 < len;
-    // loads in the order their results are needed: dt, S_in, C (phase A), x (phase B planes)
     const float dtv = ssd_dt_load(a, h, mbase, len);
-    const float *sin = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
-    constexpr int NP = 32 * NB, J = kSsdP * NP / 2 / kSsdBlock;   // S_in planes [p][n], zero for n in [N, NP)
-    float2 sv[J];
+    {   // S_in planes [p][n], zero for n in [N, 32 NB)
+        const float *sin = a.sloc + ((int64_t)bh * a.nch + c) * kSsdP * N;
+        constexpr int NP = 32 * NB, J = kSsdP * NP / 2 / kSsdBlock;
+        float2 sv[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int i = tid + j * kSsdBlock, p = (2 * i) / NP, n = (2 * i) % NP;
-        sv[j] = *reinterpret_cast<const float2 *>(sin + (int64_t)p * N + min(n, N - 2));
-    }
-    // C rows of both tiles (zero past N)
-    float4 cpre[2][NB][2];
-    const float *Cbase = a.xbc + mbase * a.Cd + a.E + a.G * N + g * N;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (!live[k]) continue;
-        const float *Crow = Cbase + (int64_t)min(tiles[k] * 16 + r, len - 1) * a.Cd;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int n = 32 * nb + 8 * kq;
-            const int nc = min(n, N - 8);
-            cpre[k][nb][0] = *reinterpret_cast<const float4 *>(Crow + nc);
-            cpre[k][nb][1] = *reinterpret_cast<const float4 *>(Crow + nc + 4);
+        for (int j = 0; j < J; ++j) {
+            const int i = tid + j * kSsdBlock, p = (2 * i) / NP, n = (2 * i) % NP;
+            sv[j] = *reinterpret_cast<const float2 *>(sin + (int64_t)p * N + min(n, N - 2));
         }
-    }
-    SsdXRegs xr;
-    ssd_x_load(a, h, mbase, len, xr);
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int i = tid + j * kSsdBlock, p = (2 * i) / NP, n = (2 * i) % NP;
-        if (n >= N) sv[j] = make_float2(0.f, 0.f);
-        split_store2(pl[0] + p * kSsdRow + n, pl[1] + p * kSsdRow + n, sv[j].x, sv[j].y);
+        for (int j = 0; j < J; ++j) {
+            const int i = tid + j * kSsdBlock, p = (2 * i) / NP, n = (2 * i) % NP;
+            if (n >= N) sv[j] = make_float2(0.f, 0.f);
+            split_store2(pl[0] + p * kSsdRow + n, pl[1] + p * kSsdRow + n, sv[j].x, sv[j].y);
+        }
     }
     ssd_lam(a, h, dtv, lam2, dts, tot);   // its barriers also publish the S_in planes
     f4v y[2][4];
@@ -706,14 +689,24 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) y[k][pt] = f4v{0.f, 0.f, 0.f, 0.f};
     // ---- phase A: exp(Lam_t) C_t . S_in
+    const float *Cbase = a.xbc + mbase * a.Cd + a.E + a.G * N + g * N;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         if (!live[k]) continue;
-        const float et = __builtin_amdgcn_exp2f(lam2[min(tiles[k] * 16 + r, len - 1)]);
+        const int t = min(tiles[k] * 16 + r, len - 1);
+        const float *Crow = Cbase + (int64_t)t * a.Cd;
+        float4 cl[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int nc = min(32 * nb + 8 * kq, N - 8);
+            cl[nb][0] = *reinterpret_cast<const float4 *>(Crow + nc);
+            cl[nb][1] = *reinterpret_cast<const float4 *>(Crow + nc + 4);
+        }
+        const float et = __builtin_amdgcn_exp2f(lam2[t]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const float e = 32 * nb + 8 * kq < N ? et : 0.f;   // d_state columns past N (clamped loads) count 0
-            const float4 c0 = cpre[k][nb][0], c1 = cpre[k][nb][1];
+            const float4 c0 = cl[nb][0], c1 = cl[nb][1];
             const float cv[8] = {c0.x * e, c0.y * e, c0.z * e, c0.w * e, c1.x * e, c1.y * e, c1.z * e, c1.w * e};
             bf8v ahv, alv;
             split8(cv, ahv, alv);
@@ -726,50 +719,39 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
             }
         }
     }
-    // CB rows of a tile, blocks 0..bd (the diagonal block's columns clamped into the row when Q = 16)
-    const float *cbbase = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * Q * Q;
-    float4 cbp[kSB][2];
-    auto load_cb = [&](int k) {
-        const int ti = tiles[k], bd = ti >> 1;
-        const float *cbrow = cbbase + (int64_t)min(ti * 16 + r, len - 1) * Q;
-#pragma unroll
-        for (int sb = 0; sb < kSB; ++sb) {
-            if (sb > bd) break;
-            const int s0 = min(32 * sb + 8 * kq, Q - 8);
-            cbp[sb][0] = *reinterpret_cast<const float4 *>(cbrow + s0);
-            cbp[sb][1] = *reinterpret_cast<const float4 *>(cbrow + s0 + 4);
-        }
-    };
-    if (live[0]) load_cb(0);
-    __syncthreads();   // the S_in planes are dead: the x planes take their place
-    ssd_x_store<false, true>(xr, len, lam2, dts, pl[0], pl[1], pl[2], pl[3]);
+    __syncthreads();   // the S_in planes are dead: the scaled x planes take their place
+    {
+        SsdXRegs xr;
+        ssd_x_load(a, h, mbase, len, xr);
+        ssd_x_store<false, false>(xr, len, lam2, dts, pl[0], pl[1], nullptr, nullptr);
+    }
     __syncthreads();
     // ---- phase B: CB-weighted sums over the chunk's earlier tokens
+    const float *cbbase = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * Q * Q;
+    const float *xbase = a.xbc + mbase * a.Cd + (int64_t)h * a.P;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         if (!live[k]) continue;
-        if (k == 1) load_cb(1);
         const int ti = tiles[k];
-        // + D x and the gate of the tile's outputs: lane l holds row ti*16 + 4 kq + rr, channel 16 pt + r
-        float xr[4][4], zr[4][4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int64_t m = mbase + min(ti * 16 + 4 * kq + rr, len - 1);
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int64_t col = (int64_t)h * a.P + 16 * pt + r;
-                xr[rr][pt] = a.xbc[m * a.Cd + col];
-                zr[rr][pt] = a.Y[m * a.ldY + col];
-            }
-        }
         const int t = min(ti * 16 + r, len - 1);
         const float lt = lam2[t];
+        const float *cbrow = cbbase + (int64_t)t * Q;
         const int bd = ti >> 1;   // the 32-token block holding the tile
-#pragma unroll
-        for (int sb = 0; sb < kSB; ++sb) {
-            if (sb >= bd) break;
+        // off-diagonal blocks, the next block's CB in flight while one computes
+        float4 cn[2];
+        {
+            const int s0 = min(8 * kq, Q - 8);
+            cn[0] = *reinterpret_cast<const float4 *>(cbrow + s0);
+            cn[1] = *reinterpret_cast<const float4 *>(cbrow + s0 + 4);
+        }
+        for (int sb = 0; sb < bd; ++sb) {
+            const float4 c0 = cn[0], c1 = cn[1];
+            {
+                const int s1 = min(32 * (sb + 1) + 8 * kq, Q - 8);
+                cn[0] = *reinterpret_cast<const float4 *>(cbrow + s1);
+                cn[1] = *reinterpret_cast<const float4 *>(cbrow + s1 + 4);
+            }
             const int s0 = 32 * sb + 8 * kq;
-            const float4 c0 = cbp[sb][0], c1 = cbp[sb][1];
             const float f = __builtin_amdgcn_exp2f(lt - lam2[32 * sb + 31]);
             const float cv[8] = {c0.x * f, c0.y * f, c0.z * f, c0.w * f, c1.x * f, c1.y * f, c1.z * f, c1.w * f};
             bf8v ahv, alv;
@@ -782,16 +764,17 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
                 y[k][pt] = mfma_bf3(ahv, alv, bhv, blv, y[k][pt]);
             }
         }
-        {   // the diagonal block: entries with s > t, or past the chunk, are never read (select, not product)
+        {   // the diagonal block (cn holds its CB): entries with s > t, or past the chunk, are never
+            // read (select, not product); B = x of the block's tokens (rows clamped into the chunk)
             const int s0 = 32 * bd + 8 * kq;
-            float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0;
+            const float raw[8] = {cn[0].x, cn[0].y, cn[0].z, cn[0].w, cn[1].x, cn[1].y, cn[1].z, cn[1].w};
+            float xd[4][8];
 #pragma unroll
-            for (int sb = 0; sb < kSB; ++sb)
-                if (sb == bd) {
-                    c0 = cbp[sb][0];
-                    c1 = cbp[sb][1];
-                }
-            const float raw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            for (int e = 0; e < 8; ++e) {
+                const float *xrow = xbase + (int64_t)min(s0 + e, len - 1) * a.Cd + r;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) xd[pt][e] = xrow[16 * pt];
+            }
             float cv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -802,10 +785,21 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_out(SsdArgs a) {
             split8(cv, ahv, alv);
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const int o = (16 * pt + r) * kSsdRow + s0;
-                const bf8v bhv = *reinterpret_cast<const bf8v *>(pl[2] + o);
-                const bf8v blv = *reinterpret_cast<const bf8v *>(pl[3] + o);
+                bf8v bhv, blv;
+                split8(xd[pt], bhv, blv);
                 y[k][pt] = mfma_bf3(ahv, alv, bhv, blv, y[k][pt]);
+            }
+        }
+        // + D x, gate, out: lane l holds row ti*16 + 4 kq + rr, channel 16 pt + r
+        float xr[4][4], zr[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t m = mbase + min(ti * 16 + 4 * kq + rr, len - 1);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int64_t col = (int64_t)h * a.P + 16 * pt + r;
+                xr[rr][pt] = a.xbc[m * a.Cd + col];
+                zr[rr][pt] = a.Y[m * a.ldY + col];
             }
         }
 #pragma unroll
