@@ -290,24 +290,35 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
     sstore(st0, 0);
     __syncthreads();
+    // one K step: the A fragments of sub-step s + 1 are read from LDS while sub-step s multiplies
     auto step = [&](int cur) {
         const int8_t *abase = As(cur) + lr * LDS_ROW + hsel * 16;
         uint4 bw[NBW];
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
             bw[j] = *reinterpret_cast<const uint4 *>(Bs(cur) + (wn * (32 * NBW) + j * 32 + lr) * 16);
+        v4i af[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[0][i] = *reinterpret_cast<const v4i *>(abase + i * 32 * LDS_ROW);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            v4i af[4], bf[NBW];
+            if (s < 3) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i *>(abase + i * 32 * LDS_ROW + s * 32);
+                for (int i = 0; i < 4; ++i)
+                    af[(s + 1) & 1][i] = *reinterpret_cast<const v4i *>(abase + i * 32 * LDS_ROW + (s + 1) * 32);
+            }
+            // keep the next sub-step's reads ahead of this sub-step's MFMAs (the scheduler would
+            // otherwise sink each read to just before its use)
+            __builtin_amdgcn_sched_barrier(0);
+            v4i bf[NBW];
 #pragma unroll
             for (int j = 0; j < NBW; ++j) bf[j] = expand16((u4_get(bw[j], s) >> (16 * hsel)) & 0xffffu);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < NBW; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][i], bf[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     for (int kt = kt0; kt < kt1; ++kt) {
