@@ -20,7 +20,7 @@
 // (no two waves expand the same bits); K in steps of 128 through double-buffered LDS, one barrier
 // per step.
 // The ragged last column tile is dispatched first so that the short workgroups do not trail.
-// k_gemm_skinny (M <= 64): one workgroup per 32 columns, its 4 waves split K and reduce their
+// k_gemm_skinny (M <= 64): one workgroup per 32 columns, its 8 waves split K and reduce their
 // int32 partial sums through LDS; A comes straight from global memory (it is 64 x K bytes and
 // stays in L2), B as above.
 #include <algorithm>
@@ -474,16 +474,20 @@ __global__ void k_clear_u32(uint32_t *p, int n) {
     if (i < n) p[i] = 0u;
 }
 
-// M <= 64: one workgroup per 32 output columns; wave w takes K steps [w*nk/4, (w+1)*nk/4).
-__global__ __launch_bounds__(kBlock) void k_gemm_skinny(GemmArgs a) {
-    __shared__ int red[kWaves - 1][2][16][64];
+// M <= 64: one workgroup of kSkWaves waves per 32 output columns; wave w takes the K steps
+// [w nk / kSkWaves, (w + 1) nk / kSkWaves), all of its loads issued (kSkRun steps at a time) before
+// its first MFMA. The int32 partial sums meet in LDS; waves 0 and 1 each finish one 32-row block,
+// with their epilogue operands loaded before the reduction barrier.
+constexpr int kSkWaves = 8, kSkBlock = 64 * kSkWaves, kSkRun = 4;
+__global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a) {
+    __shared__ int red[kSkWaves][2][16][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, hsel = lane >> 5;
     const int n0 = blockIdx.x * 32;
     const int n = n0 + lr;
     const bool nok = n < a.N;
     const int K = a.K, nkt = K / KT;
-    const int kb = (wave * nkt / kWaves) * KT, ke = ((wave + 1) * nkt / kWaves) * KT;  // may be empty
+    const int kb = wave * nkt / kSkWaves, ke = (wave + 1) * nkt / kSkWaves;   // may be empty
     const uint8_t *brow = a.sign + (int64_t)(nok ? n : 0) * (K >> 3);
     const int8_t *arow[2];
     bool aok[2];
@@ -498,48 +502,54 @@ __global__ __launch_bounds__(kBlock) void k_gemm_skinny(GemmArgs a) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] = 0;
-    for (int k0 = kb; k0 < ke; k0 += KT) {
-        const uint4 bw = nok ? *reinterpret_cast<const uint4 *>(brow + (k0 >> 3)) : make_uint4(0u, 0u, 0u, 0u);
-        v4i af[2][4];
+    for (int k0 = kb; k0 < ke; k0 += kSkRun) {
+        uint4 bw[kSkRun];
+        v4i af[kSkRun][2][4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int c = 0; c < kSkRun; ++c) {
+            const int kt = min(k0 + c, ke - 1) * KT;
+            bw[c] = nok ? *reinterpret_cast<const uint4 *>(brow + (kt >> 3)) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                af[i][s] = aok[i] ? *reinterpret_cast<const v4i *>(arow[i] + k0 + 32 * s) : v4i{0, 0, 0, 0};
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const v4i bf = expand16((u4_get(bw, s) >> (16 * hsel)) & 0xffffu);
+                for (int s = 0; s < 4; ++s)
+                    af[c][i][s] = aok[i] ? *reinterpret_cast<const v4i *>(arow[i] + kt + 32 * s) : v4i{0, 0, 0, 0};
+        }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][s], bf, acc[i], 0, 0, 0);
+        for (int c = 0; c < kSkRun; ++c) {
+            if (k0 + c >= ke) break;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const v4i bf = expand16((u4_get(bw[c], s) >> (16 * hsel)) & 0xffffu);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[c][i][s], bf, acc[i], 0, 0, 0);
+            }
         }
     }
-    // integer partial sums of waves 1..3 -> wave 0 (exact, fixed order)
-    if (wave > 0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) red[wave - 1][i][r][lane] = acc[i][r];
+        for (int r = 0; r < 16; ++r) red[wave][i][r][lane] = acc[i][r];
+    // waves 0 and 1: the epilogue operands of row block `wave` while the partial sums land
+    const int nb = a.M > 32 ? 2 : 1;
+    const bool fin = wave < nb;
+    v16f lacc;
+    BlockOps ops;
+    if (fin) {
+        lacc = lowrank_block(a, wave * 32 + lr, n, lane);
+        load_block_ops(a, ops, wave * 32, n, lane);
     }
     __syncthreads();
-    if (wave != 0) return;
+    if (!fin) return;
+    v16i tot;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < 16; ++r) {
+        int t = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] += red[0][i][r][lane] + red[1][i][r][lane] + red[2][i][r][lane];
-    // every load of both blocks' epilogues, then the stores
-    const int nb = a.M > 32 ? 2 : 1;
-    v16f lacc[2];
-    BlockOps ops[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        if (i < nb) {
-            lacc[i] = lowrank_block(a, i * 32 + lr, n, lane);
-            load_block_ops(a, ops[i], i * 32, n, lane);
-        }
+        for (int w = 0; w < kSkWaves; ++w) t += red[w][wave][r][lane];   // exact, fixed order
+        tot[r] = t;
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        if (i < nb) store_block(a, acc[i], lacc[i], ops[i], i * 32, n, lane);
+    store_block(a, tot, lacc, ops, wave * 32, n, lane);
 }
 
 }  // namespace
@@ -594,7 +604,7 @@ hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
     const int64_t ldmax = std::max(a.ldy, std::max(a.res ? a.ldres : 0, a.acc_tap ? a.ldacc : 0));
     if (ldmax > (int64_t)1 << 22) return hipErrorInvalidValue;
     if (a.M <= 64) {
-        k_gemm_skinny<<<(a.N + 31) / 32, kBlock, 0, stream>>>(a);
+        k_gemm_skinny<<<(a.N + 31) / 32, kSkBlock, 0, stream>>>(a);
         return hipGetLastError();
     }
     const GemmPlan p = plan_gemm(a.M, a.N, a.K);

@@ -38,6 +38,7 @@ __global__ __launch_bounds__(kBlock) void k_widen_bf16(const uint16_t *x, float 
 // 0..7 of the block, rank rows as its columns, the K blocks split over the waves), so each
 // workgroup reads L_dn once for kTqTok tokens.
 constexpr int kTqTok = 8;
+constexpr int kTq1MaxM = 256;   // up to this many tokens: k_tok_quant1 (one token per workgroup)
 constexpr int kTqRow = kMaxK + 16;  // LDS bytes per token's codes (the pad spreads rows over the banks)
 typedef int tq_v4i __attribute__((ext_vector_type(4)));
 typedef int tq_v16i __attribute__((ext_vector_type(16)));
@@ -275,6 +276,180 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
             a.thi[(int64_t)m * a.rank + j] = hi;
             a.tlo[(int64_t)m * a.rank + j] = lo;
             if (a.tap_t) a.tap_t[(int64_t)m * a.rank + j] = tot;
+        }
+    }
+}
+
+// The same for few tokens (batched decode): one token per workgroup, its row split over the four
+// waves (KC chunks of 4 per thread, block reductions in a fixed order), LoRA-down on int8 MFMA with
+// the token as row 0 of the block and the K blocks split over the waves.
+template <int KC>
+__global__ __launch_bounds__(kBlock) void k_tok_quant1(TokQuantArgs a) {
+    __shared__ __align__(16) int8_t sq[kMaxK];
+    __shared__ float red[2 * kWaves];
+    __shared__ int ired[kWaves];
+    __shared__ int tred[kWaves][kMaxRank / 32][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, hsel = lane >> 5;
+    const int m = blockIdx.x, K = a.K;
+    const int nkw = K / 128, nrb = (a.rank + 31) / 32;
+    if (m == 0)
+        for (int i = tid; i < a.nzero; i += kBlock) a.zero_words[i] = 0u;
+    float dsv[kMaxRank / 32];
+#pragma unroll
+    for (int rb = 0; rb < kMaxRank / 32; ++rb) dsv[rb] = a.dn_scale[min(rb * 32 + lr, a.rank - 1)];
+    // loads first: norm weight, the row, then the LoRA-down operands (rank rows lr, bytes 16 hsel..)
+    float4 wv[KC], hv[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) wv[i] = *reinterpret_cast<const float4 *>(a.W + min((i * kBlock + tid) * 4, K - 4));
+    if (a.x_bf16) {
+        uint2 raw[KC];
+#pragma unroll
+        for (int i = 0; i < KC; ++i)
+            raw[i] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(a.X) + (int64_t)m * a.ldx +
+                                                      min((i * kBlock + tid) * 4, K - 4));
+#pragma unroll
+        for (int i = 0; i < KC; ++i)
+            hv[i] = make_float4(bf16_bits_to_float(raw[i].x & 0xffffu), bf16_bits_to_float(raw[i].x >> 16),
+                                bf16_bits_to_float(raw[i].y & 0xffffu), bf16_bits_to_float(raw[i].y >> 16));
+    } else {
+#pragma unroll
+        for (int i = 0; i < KC; ++i)
+            hv[i] = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.X) + (int64_t)m * a.ldx +
+                                                      min((i * kBlock + tid) * 4, K - 4));
+    }
+    const int8_t *brow[kMaxRank / 32];
+    bool bok[kMaxRank / 32];
+#pragma unroll
+    for (int rb = 0; rb < kMaxRank / 32; ++rb) {
+        const int j = rb * 32 + lr;
+        bok[rb] = j < a.rank;
+        brow[rb] = a.lora_dn + (int64_t)min(j, a.rank - 1) * K + hsel * 16 + wave * nkw * 32;
+    }
+    constexpr int PRE = 2 * KC * 4;   // K blocks of 32 per wave when K = 1024 KC
+    const bool pre = nrb == 1 && nkw == PRE;
+    tq_v4i bpre[PRE];
+    if (pre) {
+#pragma unroll
+        for (int c = 0; c < PRE; ++c) bpre[c] = *reinterpret_cast<const tq_v4i *>(brow[0] + c * 32);
+    }
+    // ---- RMSNorm statistics and the quantizer
+    float ss = 0.f, pm = 0.f;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const bool ok = (i * kBlock + tid) * 4 < K;
+        float4 &h = hv[i];
+        h.x = ok ? h.x : 0.f;
+        h.y = ok ? h.y : 0.f;
+        h.z = ok ? h.z : 0.f;
+        h.w = ok ? h.w : 0.f;
+        ss += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
+    }
+    if (a.tap_h) {
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const int e = (i * kBlock + tid) * 4;
+            if (e < K) *reinterpret_cast<float4 *>(a.tap_h + (int64_t)m * K + e) = hv[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        float4 &h = hv[i];
+        h.x *= wv[i].x;
+        h.y *= wv[i].y;
+        h.z *= wv[i].z;
+        h.w *= wv[i].w;
+        pm = fmaxf(pm, fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w))));
+    }
+    ss = dpp_wave_sum(ss);
+    pm = dpp_wave_max(pm);
+    if (lane == 0) {
+        red[wave] = ss;
+        red[kWaves + wave] = pm;
+    }
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float mx = fmaxf(fmaxf(red[kWaves], red[kWaves + 1]), fmaxf(red[kWaves + 2], red[kWaves + 3]));
+    // u = fl(fl(h * w) * r) so that max|u| = fl(max|h * w| * r) exactly (r > 0)
+    const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
+    const float amax = mx * r;
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    const float sv = amax > 0.f ? amax / 127.0f : 0.f;
+    int qs = 0;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int e = (i * kBlock + tid) * 4;
+        if (e < K) {
+            float4 v = hv[i];
+            v.x *= r;
+            v.y *= r;
+            v.z *= r;
+            v.w *= r;
+            const int q0 = quant1(v.x, inv), q1 = quant1(v.y, inv), q2 = quant1(v.z, inv), q3 = quant1(v.w, inv);
+            qs += q0 + q1 + q2 + q3;
+            const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
+                                    ((uint32_t)(q3 & 255) << 24);
+            *reinterpret_cast<uint32_t *>(sq + e) = packed;
+            *reinterpret_cast<uint32_t *>(a.q + (int64_t)m * K + e) = packed;
+            if (a.tap_u) *reinterpret_cast<float4 *>(a.tap_u + (int64_t)m * K + e) = v;
+            if (a.tap_q) *reinterpret_cast<uint32_t *>(a.tap_q + (int64_t)m * K + e) = packed;
+        }
+    }
+    qs = dpp_wave_isum(qs);
+    if (lane == 0) ired[wave] = qs;
+    __syncthreads();
+    if (tid == 0) {
+        a.s[m] = sv;
+        a.qsum[m] = (ired[0] + ired[1]) + (ired[2] + ired[3]);
+        if (a.tap_s) a.tap_s[m] = sv;
+    }
+    // ---- LoRA-down: the token is row 0 of the 32 x 32 block (the other rows are zero)
+    const int8_t *arow = sq + hsel * 16 + wave * nkw * 32;
+    tq_v16i acc[kMaxRank / 32];
+#pragma unroll
+    for (int rb = 0; rb < kMaxRank / 32; ++rb)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[rb][q] = 0;
+    const tq_v4i zero4 = {0, 0, 0, 0};
+    if (pre) {
+#pragma unroll
+        for (int c = 0; c < PRE; ++c) {
+            tq_v4i av = *reinterpret_cast<const tq_v4i *>(arow + c * 32);
+            if (lr != 0) av = zero4;
+            if (!bok[0]) bpre[c] = zero4;
+            acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bpre[c], acc[0], 0, 0, 0);
+        }
+    } else {
+        for (int c = 0; c < nkw; ++c) {
+            tq_v4i av = *reinterpret_cast<const tq_v4i *>(arow + c * 32);
+            if (lr != 0) av = zero4;
+#pragma unroll
+            for (int rb = 0; rb < kMaxRank / 32; ++rb) {
+                if (rb < nrb) {
+                    tq_v4i bv = *reinterpret_cast<const tq_v4i *>(brow[rb] + c * 32);
+                    if (!bok[rb]) bv = zero4;
+                    acc[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc[rb], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // row 0 of the block sits in accumulator entry 0 of lanes 0..31 (column lr)
+#pragma unroll
+    for (int rb = 0; rb < kMaxRank / 32; ++rb) tred[wave][rb][lane] = acc[rb][0];
+    __syncthreads();
+    if (tid < 64) {
+#pragma unroll
+        for (int rb = 0; rb < kMaxRank / 32; ++rb) {
+            const int j = rb * 32 + lane;
+            if (rb < nrb && lane < 32 && j < a.rank) {
+                const int t = ((tred[0][rb][lane] + tred[1][rb][lane]) + tred[2][rb][lane]) + tred[3][rb][lane];
+                const float tp = dsv[rb] * sv * (float)t;
+                const __bf16 hi = (__bf16)tp;
+                const __bf16 lo = (__bf16)(tp - (float)hi);
+                a.thi[(int64_t)m * a.rank + j] = hi;
+                a.tlo[(int64_t)m * a.rank + j] = lo;
+                if (a.tap_t) a.tap_t[(int64_t)m * a.rank + j] = t;
+            }
         }
     }
 }
@@ -965,6 +1140,13 @@ hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w
 
 hipError_t launch_tok_quant(const TokQuantArgs &a, hipStream_t stream) {
     if (a.K > kMaxK || a.K % 128 || a.rank > kMaxRank || a.rank <= 0 || a.M <= 0) return hipErrorInvalidValue;
+    if (a.M <= kTq1MaxM) {   // few tokens: one per workgroup
+        if (a.K <= 1024) k_tok_quant1<1><<<a.M, kBlock, 0, stream>>>(a);
+        else if (a.K <= 2048) k_tok_quant1<2><<<a.M, kBlock, 0, stream>>>(a);
+        else if (a.K <= 4096) k_tok_quant1<4><<<a.M, kBlock, 0, stream>>>(a);
+        else k_tok_quant1<8><<<a.M, kBlock, 0, stream>>>(a);
+        return hipGetLastError();
+    }
     const int grid = (a.M + kTqTok - 1) / kTqTok;
     if (a.K <= 1024) k_tok_quant<4><<<grid, kBlock, 0, stream>>>(a);
     else if (a.K <= 2048) k_tok_quant<8><<<grid, kBlock, 0, stream>>>(a);
