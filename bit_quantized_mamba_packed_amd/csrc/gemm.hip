@@ -66,70 +66,47 @@ __device__ __forceinline__ uint32_t u4_get(const uint4 &v, int i) {
 
 // Low-rank term of one 32 x 32 block (rows m0.., columns n0..) on bf16 MFMA from global memory:
 // lacc[r] = sum_j t'[m][j] * lora_up[n][j] for this lane's 16 outputs (used by the skinny kernel).
+// Every operand load is issued before the first MFMA (addresses clamped, operands past the rank or
+// the matrix zeroed after the load).
 __device__ __forceinline__ v16f lowrank_block(const GemmArgs &a, int mrow, int ncol, int lane) {
+    constexpr int KR = kMaxRank / 16;
+    const int lj = (lane >> 5) * 8;
+    const int mc = min(mrow, a.M - 1), nc = min(ncol, a.N - 1);
+    uint4 hraw[KR], lraw[KR];
+    uint2 w[KR];
+#pragma unroll
+    for (int q = 0; q < KR; ++q) {
+        const int kr = min(16 * q + lj, a.rank - 8);
+        hraw[q] = *reinterpret_cast<const uint4 *>(a.thi + (int64_t)mc * a.rank + kr);
+        lraw[q] = *reinterpret_cast<const uint4 *>(a.tlo + (int64_t)mc * a.rank + kr);
+        w[q] = *reinterpret_cast<const uint2 *>(a.lora_up + (int64_t)nc * a.rank + kr);
+    }
     v16f lacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
-    const int lj = (lane >> 5) * 8;
-    for (int kr = 0; kr < a.rank; kr += 16) {
-        const bool inr = kr + lj + 8 <= a.rank;
-        v8bf ahi, alo, bup;
-        if (inr && mrow < a.M) {
-            ahi = *reinterpret_cast<const v8bf *>(a.thi + (int64_t)mrow * a.rank + kr + lj);
-            alo = *reinterpret_cast<const v8bf *>(a.tlo + (int64_t)mrow * a.rank + kr + lj);
-        } else {
+    const bool rok = mrow < a.M, cok = ncol < a.N;
+#pragma unroll
+    for (int q = 0; q < KR; ++q) {
+        if (16 * q >= a.rank) break;
+        const bool inr = 16 * q + lj + 8 <= a.rank;
+        v8bf ahi = __builtin_bit_cast(v8bf, hraw[q]), alo = __builtin_bit_cast(v8bf, lraw[q]), bup;
+        if (!(inr && rok)) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 ahi[e] = (__bf16)0.f;
                 alo[e] = (__bf16)0.f;
             }
         }
-        uint2 w = make_uint2(0u, 0u);
-        if (inr && ncol < a.N) w = *reinterpret_cast<const uint2 *>(a.lora_up + (int64_t)ncol * a.rank + kr + lj);
+        const uint2 wq = inr && cok ? w[q] : make_uint2(0u, 0u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            bup[e] = (__bf16)(float)(int8_t)(w.x >> (8 * e));
-            bup[4 + e] = (__bf16)(float)(int8_t)(w.y >> (8 * e));
+            bup[e] = (__bf16)(float)(int8_t)(wq.x >> (8 * e));
+            bup[4 + e] = (__bf16)(float)(int8_t)(wq.y >> (8 * e));
         }
         lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bup, lacc, 0, 0, 0);
         lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bup, lacc, 0, 0, 0);
     }
     return lacc;
-}
-
-// Epilogue of one 32 x 32 block: lane holds column (lane % 32), rows 8*(r/4) + 4*(lane/32) + r%4.
-// Its per-row and per-column operands are loaded (clamped into the matrices) before any store is
-// issued: a load behind stores makes its wait cover the stores as well.
-struct BlockOps {
-    float s[16], res[16];
-    int q[16];
-    float sc, us;
-};
-__device__ __forceinline__ void load_block_ops(const GemmArgs &a, BlockOps &o, int mb, int n, int lane) {
-    const int nc = min(n, a.N - 1);
-    o.sc = half_bits_to_float(a.row_scale[nc]);
-    o.us = a.up_scale[nc];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int mc = min(mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), a.M - 1);
-        o.s[r] = a.s[mc];
-        o.q[r] = a.qsum[mc];
-        o.res[r] = a.res ? a.res[(int64_t)mc * a.ldres + nc] : 0.f;
-    }
-}
-__device__ __forceinline__ void store_block(const GemmArgs &a, const v16i &acc, const v16f &lacc, const BlockOps &o,
-                                            int mb, int n, int lane) {
-    if (n >= a.N) return;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int m = mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m >= a.M) continue;
-        const int accv = 2 * acc[r] - o.q[r];
-        float v = o.s[r] * o.sc * (float)accv + o.us * lacc[r];
-        if (a.res) v += o.res[r];
-        a.y[(int64_t)m * a.ldy + n] = v;
-        if (a.acc_tap) a.acc_tap[(int64_t)m * a.ldacc + n] = accv;
-    }
 }
 
 // LDS of the tile kernel. Main loop: A[2][BM][A_ROW] int8 codes, B[2][BN][16] sign bytes (kMainLds).
@@ -478,8 +455,8 @@ __global__ void k_clear_u32(uint32_t *p, int n) {
 // [w nk / kSkWaves, (w + 1) nk / kSkWaves), all of its loads issued (kSkRun steps at a time) before
 // its first MFMA. The int32 partial sums meet in LDS; waves 0 and 1 each finish one 32-row block,
 // with their epilogue operands loaded before the reduction barrier.
-constexpr int kSkWaves = 8, kSkBlock = 64 * kSkWaves, kSkRun = 4;
-__global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a) {
+constexpr int kSkWaves = 8, kSkBlock = 64 * kSkWaves, kSkRun = 1;
+__global__ __launch_bounds__(kSkBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_skinny(GemmArgs a) {
     __shared__ int red[kSkWaves][2][16][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, hsel = lane >> 5;
@@ -530,26 +507,43 @@ __global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) red[wave][i][r][lane] = acc[i][r];
-    // waves 0 and 1: the epilogue operands of row block `wave` while the partial sums land
+    // every wave finishes a quarter of one 32-row block: row block ib = wave % 2, accumulator entries
+    // r in [4 rq, 4 rq + 4) (rows 8 rq + 4 (lane / 32) + 0..3), its epilogue operands loaded while the
+    // partial sums land
     const int nb = a.M > 32 ? 2 : 1;
-    const bool fin = wave < nb;
+    const int ib = wave & 1, rq = wave >> 1;
+    const bool fin = ib < nb;
     v16f lacc;
-    BlockOps ops;
+    float sv[4], rv[4], sc = 0.f, us = 0.f;
+    int qv[4];
     if (fin) {
-        lacc = lowrank_block(a, wave * 32 + lr, n, lane);
-        load_block_ops(a, ops, wave * 32, n, lane);
+        lacc = lowrank_block(a, ib * 32 + lr, n, lane);
+        const int nc = min(n, a.N - 1);
+        sc = half_bits_to_float(a.row_scale[nc]);
+        us = a.up_scale[nc];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int mc = min(ib * 32 + 8 * rq + 4 * hsel + e, a.M - 1);
+            sv[e] = a.s[mc];
+            qv[e] = a.qsum[mc];
+            rv[e] = a.res ? a.res[(int64_t)mc * a.ldres + nc] : 0.f;
+        }
     }
     __syncthreads();
-    if (!fin) return;
-    v16i tot;
+    if (!fin || !nok) return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rq + e, m = ib * 32 + 8 * rq + 4 * hsel + e;
+        if (m >= a.M) continue;
         int t = 0;
 #pragma unroll
-        for (int w = 0; w < kSkWaves; ++w) t += red[w][wave][r][lane];   // exact, fixed order
-        tot[r] = t;
+        for (int w = 0; w < kSkWaves; ++w) t += red[w][ib][r][lane];   // exact, fixed order
+        const int accv = 2 * t - qv[e];
+        float v = sv[e] * sc * (float)accv + us * lacc[r];
+        if (a.res) v += rv[e];
+        a.y[(int64_t)m * a.ldy + n] = v;
+        if (a.acc_tap) a.acc_tap[(int64_t)m * a.ldacc + n] = accv;
     }
-    store_block(a, tot, lacc, ops, wave * 32, n, lane);
 }
 
 }  // namespace
@@ -599,7 +593,7 @@ size_t gemm_scratch_bytes(int M, int N, int K) {
 }
 
 hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
-    if (a.K % KT || a.rank % 8 || a.rank > kMaxRank || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
+    if (a.K % KT || a.rank % 8 || a.rank <= 0 || a.rank > kMaxRank || a.M <= 0 || a.N <= 0) return hipErrorInvalidValue;
     // the tile kernel addresses its outputs with 32-bit byte offsets from the tile corner
     const int64_t ldmax = std::max(a.ldy, std::max(a.res ? a.ldres : 0, a.acc_tap ? a.ldacc : 0));
     if (ldmax > (int64_t)1 << 22) return hipErrorInvalidValue;
