@@ -103,6 +103,10 @@ struct SsmArgs {
     int rows_per_wg;     // rows_per_wg * N is a multiple of 1024 (or covers the head)
 };
 
+// Thread: up to kSsmIt chunks of 4 state entries (rows p0.., chunk c4 of N / 4); every load is issued
+// before the first store, and the C . S row sums use DPP over the row's N / 4 lanes (the total lands
+// in the row's last lane, which writes the gated output).
+constexpr int kSsmIt = 2;   // rows_per_wg * N / 4 <= kSsmIt * kBlock
 __global__ __launch_bounds__(kBlock) void k_ssm(SsmArgs a) {
     const int b = blockIdx.y;
     const int wg_per_head = a.P / a.rows_per_wg;
@@ -117,26 +121,36 @@ __global__ __launch_bounds__(kBlock) void k_ssm(SsmArgs a) {
     const float *Cv = xrow + a.E + a.G * a.N + g * a.N;
     const int n4 = a.N >> 2;
     const int nchunks = a.rows_per_wg * n4;
-    for (int ci = threadIdx.x; ci < nchunks; ci += kBlock) {
-        const int pr = ci / n4, c4 = ci - pr * n4;
-        const int p = p0 + pr;
-        const float x = xrow[h * a.P + p];
-        const float dtx = dt * x;
-        float4 *sp = reinterpret_cast<float4 *>(a.ssm + (((int64_t)b * a.H + h) * a.P + p) * a.N) + c4;
-        float4 S = *sp;
-        const float4 Bn = reinterpret_cast<const float4 *>(Bv)[c4];
-        const float4 Cn = reinterpret_cast<const float4 *>(Cv)[c4];
-        S.x = dA * S.x + dtx * Bn.x;
-        S.y = dA * S.y + dtx * Bn.y;
-        S.z = dA * S.z + dtx * Bn.z;
-        S.w = dA * S.w + dtx * Bn.w;
-        *sp = S;
-        float part = (S.x * Cn.x + S.y * Cn.y) + (S.z * Cn.z + S.w * Cn.w);
-        for (int m = n4 >> 1; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-        if (c4 == 0) {
-            const float y = part + Dh * x;
-            const float z = a.zbuf[(int64_t)b * a.E + h * a.P + p];
-            a.gbuf[(int64_t)b * a.E + h * a.P + p] = y * silu_f(z);
+    float4 S[kSsmIt], Bn[kSsmIt], Cn[kSsmIt];
+    float x[kSsmIt], z[kSsmIt];
+    float4 *sp[kSsmIt];
+#pragma unroll
+    for (int it = 0; it < kSsmIt; ++it) {
+        const int ci = min((int)threadIdx.x + it * kBlock, nchunks - 1);
+        const int pr = ci / n4, c4 = ci - pr * n4, p = p0 + pr;
+        sp[it] = reinterpret_cast<float4 *>(a.ssm + (((int64_t)b * a.H + h) * a.P + p) * a.N) + c4;
+        S[it] = *sp[it];
+        Bn[it] = reinterpret_cast<const float4 *>(Bv)[c4];
+        Cn[it] = reinterpret_cast<const float4 *>(Cv)[c4];
+        x[it] = xrow[h * a.P + p];
+        z[it] = a.zbuf[(int64_t)b * a.E + h * a.P + p];
+    }
+#pragma unroll
+    for (int it = 0; it < kSsmIt; ++it) {
+        const int ci = threadIdx.x + it * kBlock;
+        if (it * kBlock >= nchunks) break;   // uniform: no later chunk exists
+        const int pr = ci / n4, c4 = ci - pr * n4, p = p0 + pr;
+        const float dtx = dt * x[it];
+        float4 s4 = S[it];
+        s4.x = dA * s4.x + dtx * Bn[it].x;
+        s4.y = dA * s4.y + dtx * Bn[it].y;
+        s4.z = dA * s4.z + dtx * Bn[it].z;
+        s4.w = dA * s4.w + dtx * Bn[it].w;
+        float part = (s4.x * Cn[it].x + s4.y * Cn[it].y) + (s4.z * Cn[it].z + s4.w * Cn[it].w);
+        part = dpp_group_sum_f(part, n4);
+        if (ci < nchunks) {
+            *sp[it] = s4;
+            if (c4 == n4 - 1) a.gbuf[(int64_t)b * a.E + h * a.P + p] = (part + Dh * x[it]) * silu_f(z[it]);
         }
     }
 }
