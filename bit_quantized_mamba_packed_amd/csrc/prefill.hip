@@ -465,8 +465,19 @@ struct ConvSeqArgs {
     float *dt;             // [M][H]
 };
 
-// One thread per channel and run of kConvRun consecutive tokens of one sequence: the window of
-// the last d_conv-1 inputs slides in registers, so every Y element is read about once.
+// SiLU and softplus for the sequence conv pass, on the hardware exp2 and reciprocal (a few ulp; the
+// layer tolerance is 1e-3)
+__device__ __forceinline__ float silu_fast(float v) {
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v));
+}
+__device__ __forceinline__ float softplus_fast(float v) {
+    return v > 20.0f ? v : log1pf(__builtin_amdgcn_exp2f(1.4426950408889634f * v));
+}
+
+// One thread per channel (or dt column) and run of kConvRun consecutive tokens of one sequence: the
+// window of the last d_conv-1 inputs slides in registers, every input is read once, all of a run's
+// loads before its first store (a load behind a store waits for it). (Four channels per thread with
+// 16-byte accesses measured slower: fewer threads in flight.)
 constexpr int kConvRun = 32;
 __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
     const int runs = (a.L + kConvRun - 1) / kConvRun;
@@ -475,11 +486,10 @@ __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
     if (col >= a.Cd + a.H) return;
     const int t1 = min(a.L, t0 + kConvRun);
     const int64_t mb = (int64_t)b * a.L;
-    // every input of the run is loaded before the first store (a load behind a store waits for it)
-    const int64_t ycol = a.E + col;
+    const float *yc = a.Y + a.E + col;
     float yv[kConvRun];
 #pragma unroll
-    for (int i = 0; i < kConvRun; ++i) yv[i] = a.Y[(mb + min(t0 + i, t1 - 1)) * a.ldY + ycol];
+    for (int i = 0; i < kConvRun; ++i) yv[i] = yc[(mb + min(t0 + i, t1 - 1)) * a.ldY];
     if (col < a.Cd) {
         const float4 w = *reinterpret_cast<const float4 *>(a.conv_w + (int64_t)col * kConvTaps);
         const float bias = a.conv_b[col];
@@ -488,7 +498,7 @@ __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
 #pragma unroll
         for (int k = 0; k < kConvTaps - 1; ++k) {
             const int tok = t0 - (kConvTaps - 1) + k;
-            win[k] = tok >= 0 ? a.Y[(mb + tok) * a.ldY + ycol]
+            win[k] = tok >= 0 ? yc[(mb + tok) * a.ldY]
                               : a.conv_state[((int64_t)b * a.Cd + col) * (kConvTaps - 1) + (kConvTaps - 1) + tok];
         }
 #pragma unroll
@@ -496,7 +506,7 @@ __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
             if (t0 + i >= t1) break;
             const float x = yv[i];
             const float v = bias + w.x * win[0] + w.y * win[1] + w.z * win[2] + w.w * x;
-            a.xbc[(mb + t0 + i) * a.Cd + col] = silu_f(v);
+            a.xbc[(mb + t0 + i) * a.Cd + col] = silu_fast(v);
             win[0] = win[1];
             win[1] = win[2];
             win[2] = x;
@@ -507,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
 #pragma unroll
         for (int i = 0; i < kConvRun; ++i) {
             if (t0 + i >= t1) break;
-            a.dt[(mb + t0 + i) * a.H + h] = softplus_f(yv[i] + db);
+            a.dt[(mb + t0 + i) * a.H + h] = softplus_fast(yv[i] + db);
         }
     }
 }
