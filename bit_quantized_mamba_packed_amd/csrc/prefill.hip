@@ -32,25 +32,26 @@ __global__ __launch_bounds__(kBlock) void k_widen_bf16(const uint16_t *x, float 
 }
 
 // ------------------------------------------------------------------ 1/6 per-token quantizer
-// kTqTok tokens per workgroup. Each wave normalises and quantizes two whole tokens (wave-level
+// TOK (8 or 4) tokens per workgroup. Each wave normalises and quantizes TOK / 4 whole tokens (wave-level
 // reductions only, no barrier), leaving their codes in LDS; then the LoRA-down of all of them,
 // t[tok][j] = sum_k q[tok][k] L_dn[j][k], runs on int8 MFMA (32x32x32 blocks, tokens as rows
 // 0..7 of the block, rank rows as its columns, the K blocks split over the waves), so each
-// workgroup reads L_dn once for kTqTok tokens.
-constexpr int kTqTok = 8;
+// workgroup reads L_dn once for TOK tokens (with TOK = 4, L_dn streams in runs instead of being
+// loaded with the rows).
+constexpr int kTqTok = 8;   // tokens per workgroup of k_tok_quant (4 measured slower: L_dn streamed)
 constexpr int kTq1MaxM = 256;   // up to this many tokens: k_tok_quant1 (one token per workgroup)
 constexpr int kTqRow = kMaxK + 16;  // LDS bytes per token's codes (the pad spreads rows over the banks)
 typedef int tq_v4i __attribute__((ext_vector_type(4)));
 typedef int tq_v16i __attribute__((ext_vector_type(16)));
 
-template <int KCH>
+template <int KCH, int TOK>
 __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
-    __shared__ __align__(16) int8_t sq[kTqTok * kTqRow];
-    __shared__ float s_l[kTqTok];
+    __shared__ __align__(16) int8_t sq[TOK * kTqRow];
+    __shared__ float s_l[TOK];
     __shared__ int tred[kWaves][kMaxRank / 32][4][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, hsel = lane >> 5;
-    const int m0 = blockIdx.x * kTqTok;
+    const int m0 = blockIdx.x * TOK;
     const int K = a.K;
     if (blockIdx.x == 0)
         for (int i = tid; i < a.nzero; i += kBlock) a.zero_words[i] = 0u;
@@ -67,11 +68,12 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
     for (int i = 0; i < KCH; ++i) wv[i] = *reinterpret_cast<const float4 *>(a.W + min((i * 64 + lane) * 4, K - 4));
     // ---- norm + quantizer: wave w takes tokens w and w + kWaves (both rows in flight at once when
     // they fit in registers)
-    constexpr int NU = KCH <= 16 ? 2 : 1;
+    constexpr int TPW = TOK / kWaves;   // tokens per wave
+    constexpr int NU = KCH <= 16 ? TPW : 1;
     // LoRA-down operands (lane: rank row lr, bytes 16 * hsel.. of each 32-wide K block); with one
     // rank block and exactly PRE K blocks per wave they are loaded with the rows
-    constexpr int PRE = KCH <= 16 ? 2 * KCH : 1;
-    const bool pre = KCH <= 16 && nrb == 1 && nkw == PRE;
+    constexpr int PRE = KCH <= 16 && TOK == 8 ? 2 * KCH : 1;
+    const bool pre = KCH <= 16 && TOK == 8 && nrb == 1 && nkw == PRE;
     const int8_t *brow[kMaxRank / 32];
     bool bok[kMaxRank / 32];
 #pragma unroll
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
     }
     tq_v4i bpre[PRE];
 #pragma unroll
-    for (int pass = 0; pass < 2 / NU; ++pass) {
+    for (int pass = 0; pass < TPW / NU; ++pass) {
         float4 hv[NU][KCH];
         int mrow[NU];
         bool mok[NU];
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
     __syncthreads();
     // ---- LoRA-down on int8 MFMA: lane supplies row (token) lr and column (rank row) lr of the
     // block; tokens past kTqTok and rank rows past the rank are zero
-    const int8_t *arow = sq + (lr & (kTqTok - 1)) * kTqRow + hsel * 16 + wave * nkw * 32;
+    const int8_t *arow = sq + (lr & (TOK - 1)) * kTqRow + hsel * 16 + wave * nkw * 32;
     tq_v16i acc[kMaxRank / 32];
 #pragma unroll
     for (int rb = 0; rb < kMaxRank / 32; ++rb)
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
 #pragma unroll
         for (int c = 0; c < PRE; ++c) {
             av[c] = *reinterpret_cast<const tq_v4i *>(arow + c * 32);
-            if (lr >= kTqTok) av[c] = zero4;
+            if (lr >= TOK) av[c] = zero4;
             if (!bok[0]) bpre[c] = zero4;
         }
 #pragma unroll
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
             for (int c = 0; c < kTqRun; ++c) {
                 const int k = min(c0 + c, nkw - 1) * 32;
                 av[c] = *reinterpret_cast<const tq_v4i *>(arow + k);
-                if (lr >= kTqTok) av[c] = zero4;
+                if (lr >= TOK) av[c] = zero4;
 #pragma unroll
                 for (int rb = 0; rb < kMaxRank / 32; ++rb) {
                     if (rb < nrb) {
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
         const int r = tid >> 6, l = tid & 63;
         const int tot = ((tred[0][rb][r][l] + tred[1][rb][r][l]) + tred[2][rb][r][l]) + tred[3][rb][r][l];
         const int tok = 4 * (l >> 5) + r, j = rb * 32 + (l & 31), m = m0 + tok;
-        if (j < a.rank && m < a.M) {
+        if (tok < TOK && j < a.rank && m < a.M) {
             const float tp = dsv[rb] * s_l[tok] * (float)tot;
             const __bf16 hi = (__bf16)tp;
             const __bf16 lo = (__bf16)(tp - (float)hi);
@@ -1158,10 +1160,10 @@ hipError_t launch_tok_quant(const TokQuantArgs &a, hipStream_t stream) {
         return hipGetLastError();
     }
     const int grid = (a.M + kTqTok - 1) / kTqTok;
-    if (a.K <= 1024) k_tok_quant<4><<<grid, kBlock, 0, stream>>>(a);
-    else if (a.K <= 2048) k_tok_quant<8><<<grid, kBlock, 0, stream>>>(a);
-    else if (a.K <= 4096) k_tok_quant<16><<<grid, kBlock, 0, stream>>>(a);
-    else k_tok_quant<32><<<grid, kBlock, 0, stream>>>(a);
+    if (a.K <= 1024) k_tok_quant<4, kTqTok><<<grid, kBlock, 0, stream>>>(a);
+    else if (a.K <= 2048) k_tok_quant<8, kTqTok><<<grid, kBlock, 0, stream>>>(a);
+    else if (a.K <= 4096) k_tok_quant<16, kTqTok><<<grid, kBlock, 0, stream>>>(a);
+    else k_tok_quant<32, kTqTok><<<grid, kBlock, 0, stream>>>(a);
     return hipGetLastError();
 }
 
