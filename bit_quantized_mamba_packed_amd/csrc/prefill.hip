@@ -543,81 +543,6 @@ struct SsdArgs {
 constexpr int kSsdMaxQ = 256, kSsdMaxN = 256, kSsdP = 64, kSsdWaves = 8, kSsdBlock = 64 * kSsdWaves;
 
 typedef float f4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f4v mfma4(float a, float b, f4v c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
-
-// The fp32 MFMA 16x16x4 takes A[i][k] from lane i + 16k, B[k][j] from lane j + 16k and leaves
-// D[4(l/16) + r][l % 16] in lane l, element r. Where both operands are contiguous along the
-// contraction index, lane l reads four consecutive k as one float4 and feeds component j to the
-// j-th of four MFMAs: logical k = l / 16 of MFMA j is physical index 4 (l / 16) + j for A and B
-// alike, so the four MFMAs cover 16 consecutive k exactly once.
-
-// CB[t][s] = C_t . B_s of one 16-token t-tile of chunk c, group g: wave w takes the s-tiles
-// w, w + 4, ... <= the t-tile (only those are read).
-__global__ __launch_bounds__(kBlock) void k_ssd_cbm(SsdArgs a) {
-    {   // conv-state handoff, per (sequence, channel): new state[i] = element L + i of
-        // [old state (3) | the sequence's conv inputs (L)] (the conv pass has read the old state)
-        const int nthr = gridDim.x * gridDim.y * kBlock;
-        for (int idx = (blockIdx.y * gridDim.x + blockIdx.x) * kBlock + threadIdx.x; idx < a.B * a.Cd; idx += nthr) {
-            const int bb = idx / a.Cd, ch = idx - bb * a.Cd;
-            float *st = a.conv_state + (int64_t)idx * (kConvTaps - 1);
-            float nv[kConvTaps - 1];
-#pragma unroll
-            for (int i = 0; i < kConvTaps - 1; ++i) {
-                const int p = a.L + i;
-                nv[i] = p < kConvTaps - 1 ? st[p] : a.Y[((int64_t)bb * a.L + p - (kConvTaps - 1)) * a.ldY + a.E + ch];
-            }
-#pragma unroll
-            for (int i = 0; i < kConvTaps - 1; ++i) st[i] = nv[i];
-        }
-    }
-    const int bgc = blockIdx.x, c = bgc % a.nch, g = (bgc / a.nch) % a.G, b = bgc / (a.nch * a.G);
-    const int ti = blockIdx.y;
-    const int len = min(a.Q, a.L - c * a.Q);
-    if (ti * 16 >= len) return;   // no barriers in this kernel
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, kq = lane >> 4;
-    const int64_t mbase = (int64_t)b * a.L + c * a.Q;
-    constexpr int NCM = kSsdMaxN / 16;
-    const int NC = a.N / 16;
-    // the t-tile's C fragments once, then the B fragments of each s-tile, the next s-tile's in flight
-    // while the current one computes
-    const float *Crow = a.xbc + (mbase + min(ti * 16 + r, len - 1)) * a.Cd + a.E + a.G * a.N + g * a.N + 4 * kq;
-    float4 cv[NCM], bv[2][NCM];
-#pragma unroll
-    for (int j = 0; j < NCM; ++j)
-        if (j < NC) cv[j] = *reinterpret_cast<const float4 *>(Crow + 16 * j);
-    auto load_b = [&](int si, float4 (&dst)[NCM]) {
-        const float *Brow = a.xbc + (mbase + min(si * 16 + r, len - 1)) * a.Cd + a.E + g * a.N + 4 * kq;
-#pragma unroll
-        for (int j = 0; j < NCM; ++j)
-            if (j < NC) dst[j] = *reinterpret_cast<const float4 *>(Brow + 16 * j);
-    };
-    float *out = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * a.Q * a.Q;
-    auto tile = [&](int si, const float4 (&bt)[NCM]) {
-        f4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < NCM; ++j) {
-            if (j < NC) {
-                acc = mfma4(cv[j].x, bt[j].x, acc);
-                acc = mfma4(cv[j].y, bt[j].y, acc);
-                acc = mfma4(cv[j].z, bt[j].z, acc);
-                acc = mfma4(cv[j].w, bt[j].w, acc);
-            }
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) out[(int64_t)(ti * 16 + 4 * kq + rr) * a.Q + si * 16 + r] = acc[rr];
-    };
-    if (wave <= ti) load_b(wave, bv[0]);
-#pragma unroll 1
-    for (int si = wave; si <= ti; si += 2 * kWaves) {
-        if (si + kWaves <= ti) load_b(si + kWaves, bv[1]);
-        tile(si, bv[0]);
-        if (si + kWaves <= ti) {
-            if (si + 2 * kWaves <= ti) load_b(si + 2 * kWaves, bv[0]);
-            tile(si + kWaves, bv[1]);
-        }
-    }
-}
-
 // Chunked SSD in three passes, each over every (b, h, chunk) at once (Lam_t = inclusive cumsum of
 // dt A within the chunk; exponentials only of Lam differences, or of Lam itself, all <= 0):
 //   k_ssd_state  S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s of the chunk, and Lam_end
@@ -728,6 +653,75 @@ __device__ __forceinline__ void ssd_x_store(const SsdXRegs &x, int len, const fl
             split_store2(xh + o, xl + o, r0 * w[0], r1 * w[1]);
             if (RAW) split_store2(rh + o, rl + o, r0, r1);
         }
+    }
+}
+
+// CB[t][s] = C_t . B_s of one 16-token t-tile of chunk c, group g, on bf16 MFMA with both operands
+// split hi/lo: 8 waves, wave w takes the s-tiles w, w + 8, ... <= the t-tile (only those are read);
+// the t-tile's C fragments are split once, each s-tile's B fragments as they load (the next
+// s-tile's loads in flight while one computes). Also the conv-state hand-off.
+__global__ __launch_bounds__(kSsdBlock) void k_ssd_cbm(SsdArgs a) {
+    {   // conv-state handoff, per (sequence, channel): new state[i] = element L + i of
+        // [old state (3) | the sequence's conv inputs (L)] (the conv pass has read the old state)
+        const int nthr = gridDim.x * gridDim.y * kSsdBlock;
+        for (int idx = (blockIdx.y * gridDim.x + blockIdx.x) * kSsdBlock + threadIdx.x; idx < a.B * a.Cd; idx += nthr) {
+            const int bb = idx / a.Cd, ch = idx - bb * a.Cd;
+            float *st = a.conv_state + (int64_t)idx * (kConvTaps - 1);
+            float nv[kConvTaps - 1];
+#pragma unroll
+            for (int i = 0; i < kConvTaps - 1; ++i) {
+                const int p = a.L + i;
+                nv[i] = p < kConvTaps - 1 ? st[p] : a.Y[((int64_t)bb * a.L + p - (kConvTaps - 1)) * a.ldY + a.E + ch];
+            }
+#pragma unroll
+            for (int i = 0; i < kConvTaps - 1; ++i) st[i] = nv[i];
+        }
+    }
+    const int bgc = blockIdx.x, c = bgc % a.nch, g = (bgc / a.nch) % a.G, b = bgc / (a.nch * a.G);
+    const int ti = blockIdx.y;
+    const int len = min(a.Q, a.L - c * a.Q);
+    if (ti * 16 >= len) return;   // no barriers in this kernel
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, kq = lane >> 4;
+    const int64_t mbase = (int64_t)b * a.L + c * a.Q;
+    constexpr int NBM = kSsdMaxN / 32;
+    const int N = a.N, NB = (N + 31) / 32;
+    // lane: row (C) / column (B) r of its tile, d_state indices 32 nb + 8 kq .. +8 (zero past N)
+    auto load8 = [&](const float *row, int nb, float (&v)[8]) {
+        const int n = 32 * nb + 8 * kq, nc = min(n, N - 8);
+        const float4 v0 = *reinterpret_cast<const float4 *>(row + nc), v1 = *reinterpret_cast<const float4 *>(row + nc + 4);
+        const bool ok = n < N;
+        v[0] = ok ? v0.x : 0.f; v[1] = ok ? v0.y : 0.f; v[2] = ok ? v0.z : 0.f; v[3] = ok ? v0.w : 0.f;
+        v[4] = ok ? v1.x : 0.f; v[5] = ok ? v1.y : 0.f; v[6] = ok ? v1.z : 0.f; v[7] = ok ? v1.w : 0.f;
+    };
+    const float *Crow = a.xbc + (mbase + min(ti * 16 + r, len - 1)) * a.Cd + a.E + a.G * N + g * N;
+    bf8v ch[NBM], cl[NBM];
+#pragma unroll
+    for (int nb = 0; nb < NBM; ++nb) {
+        if (nb < NB) {
+            float v[8];
+            load8(Crow, nb, v);
+            split8(v, ch[nb], cl[nb]);
+        }
+    }
+    float *out = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * a.Q * a.Q;
+    for (int si = wave; si <= ti; si += kSsdWaves) {
+        const float *Brow = a.xbc + (mbase + min(si * 16 + r, len - 1)) * a.Cd + a.E + g * N;
+        float bv[NBM][8];
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb)
+            if (nb < NB) load8(Brow, nb, bv[nb]);
+        f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            if (nb < NB) {
+                bf8v bh, bl;
+                split8(bv[nb], bh, bl);
+                acc = mfma_bf3(ch[nb], cl[nb], bh, bl, acc);
+            }
+        }
+        // lane l holds CB[t = 16 ti + 4 kq + rr][s = 16 si + r]
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) out[(int64_t)(ti * 16 + 4 * kq + rr) * a.Q + si * 16 + r] = acc[rr];
     }
 }
 
@@ -1301,7 +1295,7 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.state = st.ssm;
         a.g = ws.gbuf;
         a.conv_state = st.conv;
-        k_ssd_cbm<<<dim3(batch * s.G * nch, chunk / 16), kBlock, 0, stream>>>(a);
+        k_ssd_cbm<<<dim3(batch * s.G * nch, chunk / 16), kSsdBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const int nblk = batch * s.H * nch;
         k_ssd_state<<<nblk, kSsdBlock, 0, stream>>>(a);
