@@ -918,6 +918,14 @@ __global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) 
         const float lt = lam2[t];
         const float *cbrow = cbbase + (int64_t)t * Q;
         const int bd = ti >> 1;   // the 32-token block holding the tile
+        // z of the tile's outputs (lane l: rows ti*16 + 4 kq + rr, channels 16 pt + r), in flight during the tile
+        float zr[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int64_t m = mbase + min(ti * 16 + 4 * kq + rr, len - 1);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) zr[rr][pt] = a.Y[m * a.ldY + (int64_t)h * a.P + 16 * pt + r];
+        }
         // off-diagonal blocks, the next block's CB in flight while one computes
         float4 cn[2];
         {
@@ -956,11 +964,12 @@ __global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) xd[pt][e] = xrow[16 * pt];
             }
+            // the skip term D x_t rides on the diagonal entry: A[t][t] = CB[t][t] dt_t + D
             float cv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int s = s0 + e;
-                cv[e] = s <= t ? raw[e] * __builtin_amdgcn_exp2f(lt - lam2[s]) * dts[s] : 0.f;
+                cv[e] = s <= t ? raw[e] * __builtin_amdgcn_exp2f(lt - lam2[s]) * dts[s] + (s == t ? Dh : 0.f) : 0.f;
             }
             bf8v ahv, alv;
             split8(cv, ahv, alv);
@@ -971,18 +980,7 @@ __global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) 
                 y[k][pt] = mfma_bf3(ahv, alv, bhv, blv, y[k][pt]);
             }
         }
-        // + D x, gate, out: lane l holds row ti*16 + 4 kq + rr, channel 16 pt + r
-        float xr[4][4], zr[4][4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int64_t m = mbase + min(ti * 16 + 4 * kq + rr, len - 1);
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                const int64_t col = (int64_t)h * a.P + 16 * pt + r;
-                xr[rr][pt] = a.xbc[m * a.Cd + col];
-                zr[rr][pt] = a.Y[m * a.ldY + col];
-            }
-        }
+        // gate, out: lane l holds row ti*16 + 4 kq + rr, channel 16 pt + r
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int tt = ti * 16 + 4 * kq + rr;
@@ -991,7 +989,7 @@ __global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
                 for (int pt = 0; pt < 4; ++pt) {
                     const int64_t col = (int64_t)h * a.P + 16 * pt + r;
-                    a.g[m * a.E + col] = (y[k][pt][rr] + Dh * xr[rr][pt]) * silu_f(zr[rr][pt]);
+                    a.g[m * a.E + col] = y[k][pt][rr] * silu_fast(zr[rr][pt]);
                 }
             }
         }
