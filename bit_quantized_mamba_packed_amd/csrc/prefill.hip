@@ -32,30 +32,29 @@ __global__ __launch_bounds__(kBlock) void k_widen_bf16(const uint16_t *x, float 
 }
 
 // ------------------------------------------------------------------ 1/6 per-token quantizer
-// TOK (8 or 4) tokens per workgroup. Each wave normalises and quantizes TOK / 4 whole tokens (wave-level
-// reductions only, no barrier), leaving their codes in LDS; then the LoRA-down of all of them,
-// t[tok][j] = sum_k q[tok][k] L_dn[j][k], runs on int8 MFMA (32x32x32 blocks, tokens as rows
-// 0..7 of the block, rank rows as its columns, the K blocks split over the waves), so each
-// workgroup reads L_dn once for TOK tokens (with TOK = 4, L_dn streams in runs instead of being
-// loaded with the rows).
-constexpr int kTqTok = 8;   // tokens per workgroup of k_tok_quant (4 measured slower: L_dn streamed)
+// TOK tokens per workgroup of NW waves (one or two tokens per wave). Each wave normalises and
+// quantizes whole tokens (wave-level reductions only, no barrier), leaving the codes in LDS; then the LoRA-down of
+// all of them, t[tok][j] = sum_k q[tok][k] L_dn[j][k], runs on int8 MFMA (32x32x32 blocks, tokens
+// as rows 0..7 of the block, rank rows as its columns, the K blocks split over the waves), so each
+// workgroup reads L_dn once for TOK tokens (loaded with the rows when TOK = 8 and K <= 4096).
+constexpr int kTqTok = 8;   // tokens per workgroup of k_tok_quant
 constexpr int kTq1MaxM = 256;   // up to this many tokens: k_tok_quant1 (one token per workgroup)
 constexpr int kTqRow = kMaxK + 16;  // LDS bytes per token's codes (the pad spreads rows over the banks)
 typedef int tq_v4i __attribute__((ext_vector_type(4)));
 typedef int tq_v16i __attribute__((ext_vector_type(16)));
 
-template <int KCH, int TOK>
-__global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
+template <int KCH, int TOK, int NW>
+__global__ __launch_bounds__(64 * NW) void k_tok_quant(TokQuantArgs a) {
     __shared__ __align__(16) int8_t sq[TOK * kTqRow];
     __shared__ float s_l[TOK];
-    __shared__ int tred[kWaves][kMaxRank / 32][4][64];
+    __shared__ int tred[NW][kMaxRank / 32][4][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, hsel = lane >> 5;
     const int m0 = blockIdx.x * TOK;
     const int K = a.K;
     if (blockIdx.x == 0)
-        for (int i = tid; i < a.nzero; i += kBlock) a.zero_words[i] = 0u;
-    const int nkw = K / 128, nrb = (a.rank + 31) / 32;  // K blocks of 32 per wave; rank blocks of 32
+        for (int i = tid; i < a.nzero; i += 64 * NW) a.zero_words[i] = 0u;
+    const int nkw = K / (32 * NW), nrb = (a.rank + 31) / 32;  // K blocks of 32 per wave; rank blocks of 32
     // Loads are issued in the order their results are needed (norm weight, the rows, then the
     // LoRA-down operands), all before any store, with addresses clamped into range and
     // out-of-range values zeroed after, so that the quantizer of the first row starts while the
@@ -66,13 +65,13 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
     float4 wv[KCH];
 #pragma unroll
     for (int i = 0; i < KCH; ++i) wv[i] = *reinterpret_cast<const float4 *>(a.W + min((i * 64 + lane) * 4, K - 4));
-    // ---- norm + quantizer: wave w takes tokens w and w + kWaves (both rows in flight at once when
+    // ---- norm + quantizer: wave w takes tokens w, w + NW, ... (all of them in flight at once when
     // they fit in registers)
-    constexpr int TPW = TOK / kWaves;   // tokens per wave
+    constexpr int TPW = TOK / NW;   // tokens per wave
     constexpr int NU = KCH <= 16 ? TPW : 1;
     // LoRA-down operands (lane: rank row lr, bytes 16 * hsel.. of each 32-wide K block); with one
     // rank block and exactly PRE K blocks per wave they are loaded with the rows
-    constexpr int PRE = KCH <= 16 && TOK == 8 ? 2 * KCH : 1;
+    constexpr int PRE = KCH <= 16 && TOK == 8 ? 8 * KCH / NW : 1;
     const bool pre = KCH <= 16 && TOK == 8 && nrb == 1 && nkw == PRE;
     const int8_t *brow[kMaxRank / 32];
     bool bok[kMaxRank / 32];
@@ -90,7 +89,7 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
         bool mok[NU];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int m = m0 + wave + (pass * NU + u) * kWaves;
+            const int m = m0 + wave + (pass * NU + u) * NW;
             mok[u] = m < a.M;
             mrow[u] = min(m, a.M - 1);
         }
@@ -171,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int tok = wave + (pass * NU + u) * kWaves, m = m0 + tok;
+            const int tok = wave + (pass * NU + u) * NW, m = m0 + tok;
             const float tot = dpp_wave_sum(ss[u]), mx = dpp_wave_max(pm[u]);
             // u = fl(fl(h * w) * r) so that max|u| = fl(max|h * w| * r) exactly (r > 0)
             const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
@@ -267,9 +266,11 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant(TokQuantArgs a) {
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < kMaxRank / 32; ++rb) {
-        if (rb >= nrb) break;
+        if (rb >= nrb || tid >= 256) break;
         const int r = tid >> 6, l = tid & 63;
-        const int tot = ((tred[0][rb][r][l] + tred[1][rb][r][l]) + tred[2][rb][r][l]) + tred[3][rb][r][l];
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) tot += tred[w][rb][r][l];   // exact, fixed order
         const int tok = 4 * (l >> 5) + r, j = rb * 32 + (l & 31), m = m0 + tok;
         if (tok < TOK && j < a.rank && m < a.M) {
             const float tp = dsv[rb] * s_l[tok] * (float)tot;
@@ -1151,11 +1152,12 @@ hipError_t launch_tok_quant(const TokQuantArgs &a, hipStream_t stream) {
         else k_tok_quant1<8><<<a.M, kBlock, 0, stream>>>(a);
         return hipGetLastError();
     }
+    // one wave per token while the rows fit the registers of 2 waves per SIMD, else two tokens per wave
     const int grid = (a.M + kTqTok - 1) / kTqTok;
-    if (a.K <= 1024) k_tok_quant<4, kTqTok><<<grid, kBlock, 0, stream>>>(a);
-    else if (a.K <= 2048) k_tok_quant<8, kTqTok><<<grid, kBlock, 0, stream>>>(a);
-    else if (a.K <= 4096) k_tok_quant<16, kTqTok><<<grid, kBlock, 0, stream>>>(a);
-    else k_tok_quant<32, kTqTok><<<grid, kBlock, 0, stream>>>(a);
+    if (a.K <= 1024) k_tok_quant<4, kTqTok, 8><<<grid, 512, 0, stream>>>(a);
+    else if (a.K <= 2048) k_tok_quant<8, kTqTok, 8><<<grid, 512, 0, stream>>>(a);
+    else if (a.K <= 4096) k_tok_quant<16, kTqTok, 4><<<grid, 256, 0, stream>>>(a);
+    else k_tok_quant<32, kTqTok, 4><<<grid, 256, 0, stream>>>(a);
     return hipGetLastError();
 }
 
