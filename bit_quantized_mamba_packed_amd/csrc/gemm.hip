@@ -37,7 +37,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int BM = 128, KT = 128;
-constexpr int LDS_ROW = KT + 16;  // bytes per LDS row of A (the pad staggers the banks of the fragment reads)
 
 __device__ __forceinline__ uint32_t nibble_to_bytes(uint32_t nib) { return (nib * 0x00204081u) & 0x01010101u; }
 
@@ -109,14 +108,18 @@ __device__ __forceinline__ v16f lowrank_block(const GemmArgs &a, int mrow, int n
     return lacc;
 }
 
-// LDS of the tile kernel. Main loop: A[2][BM][A_ROW] int8 codes, B[2][BN][16] sign bytes (kMainLds).
+// LDS of the tile kernel. Main loop: A[2][BM][KT] int8 codes (16-byte columns of row r stored at
+// column ^ (r & 7), so the fragment reads of 8 consecutive rows hit 8 different bank groups),
+// B[2][max(BN, 256)][16] sign bytes; both are written by direct global->LDS loads.
 // Epilogue operands: s[BM] f32, qsum[BM] i32, thi/tlo [BM][rank+8] bf16, lora_up [BN][rank+8] int8.
 // For rank <= 32 they get their own region behind the main-loop buffers and are loaded before the
 // main loop (their latency hides behind it); larger ranks reuse the main-loop buffers afterwards.
-constexpr int A_BYTES = BM * LDS_ROW;
+constexpr int A_BYTES = BM * KT;
+template <int BN>
+constexpr int b_bytes() { return (BN > 256 ? BN : 256) * 16; }
 constexpr int kCntBytes = 4096;
 template <int BN>
-constexpr int main_lds() { return 2 * A_BYTES + 2 * BN * 16; }
+constexpr int main_lds() { return 2 * A_BYTES + 2 * b_bytes<BN>(); }
 constexpr int kEarlyRank = 32;
 template <int BN>
 constexpr int epi_lds_bytes(int rank) { return 1024 + 2 * BM * (rank + 8) * 2 + BN * (rank + 8); }
@@ -125,8 +128,20 @@ constexpr int tile_smem() { return main_lds<BN>() + epi_lds_bytes<BN>(kEarlyRank
 static_assert(epi_lds_bytes<256>(kMaxRank) <= tile_smem<256>() && epi_lds_bytes<128>(kMaxRank) <= tile_smem<128>(),
               "tile LDS");
 
-// Workgroup barrier that orders LDS only: outstanding global stores (the epilogue's) are not waited for.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Direct global->LDS load of 16 bytes per lane: the wave's 64 lanes fill 1 KB of LDS from `lds`
+// (wave-uniform) in lane order. Written as inline asm so that the compiler does not make every
+// later LDS read wait for it (it cannot tell which LDS bytes the load writes); the waits are
+// explicit: dma_barrier before any read of what it wrote, and before it overwrites anything read.
+__device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(base) : "memory");
+}
+
+// Workgroup barrier after direct global->LDS loads: those count as vector-memory loads, so every
+// wave waits for its own to land (vmcnt) and its LDS reads to finish before the barrier.
+__device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Stage the epilogue operands of tile (m0, n0) into LDS at `base`.
 template <int BN>
@@ -187,7 +202,7 @@ template <int WNB, bool SPLIT, bool RES>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tile(GemmArgs a, int ntm,
                                                                                               int ntn, int splitk) {
     constexpr int BN = 64 * WNB, NBW = WNB / 2;   // N blocks of 32 per wave
-    constexpr int BCOL = BN > kBlock ? BN / kBlock : 1;   // sign-bit columns staged per thread
+    constexpr int BDMA = b_bytes<BN>() / 4096;   // 1 KB sign-bit loads per wave and K step
     __shared__ __align__(16) char smem[tile_smem<BN>()];
     __shared__ int last_flag;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -211,40 +226,28 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int K = a.K, nk = K / KT;
     const int kt0 = z * nk / splitk, kt1 = (z + 1) * nk / splitk;
     auto As = [&](int b) { return reinterpret_cast<int8_t *>(smem) + b * A_BYTES; };
-    auto Bs = [&](int b) { return reinterpret_cast<uint8_t *>(smem) + 2 * A_BYTES + b * (BN * 16); };
-    // A staging: thread -> row tid/2, 64-byte half tid%2;  B staging: thread -> columns tid + kBlock c (< BN)
-    const int srow = tid >> 1, shalf = tid & 1;
-    const bool arow_ok = m0 + srow < a.M;
-    const int8_t *qrow = a.q + (int64_t)(arow_ok ? m0 + srow : 0) * a.ldq + shalf * 64;
-    bool bcol_ok[BCOL];
-    const uint8_t *bsrc[BCOL];
+    auto Bs = [&](int b) { return reinterpret_cast<uint8_t *>(smem) + 2 * A_BYTES + b * b_bytes<BN>(); };
+    // Direct global->LDS loads (16 bytes per lane, 1 KB per wave and instruction, written to LDS in
+    // lane order). A: wave w, load i covers rows 8 (4 w + i) .. + 8; lane l fills LDS column l & 7
+    // of row l >> 3 with the code bytes of column (l & 7) ^ (l >> 3) (the swizzle). B: wave w, load
+    // c covers bit rows 64 (4 c + w) + l. Rows and columns past the matrix are clamped into it:
+    // they only feed outputs that are never stored.
+    const int8_t *asrc[4];
 #pragma unroll
-    for (int c = 0; c < BCOL; ++c) {
-        const int col = tid + kBlock * c;
-        bcol_ok[c] = col < BN && n0 + col < a.N;
-        bsrc[c] = a.sign + (int64_t)(bcol_ok[c] ? n0 + col : 0) * (K >> 3);
+    for (int i = 0; i < 4; ++i) {
+        const int row = 8 * (4 * wave + i) + (lane >> 3);
+        asrc[i] = a.q + (int64_t)min(m0 + row, a.M - 1) * a.ldq + (((lane & 7) ^ (lane >> 3)) << 4);
     }
-    // one register stage: the global loads of step k + 1 are issued while step k computes
-    struct Stage {
-        int4 a[4];
-        uint4 b[BCOL];
-    };
-    Stage st0;
-    auto gload = [&](Stage &st, int k0) {
+    const uint8_t *bsrc[BDMA];
+#pragma unroll
+    for (int c = 0; c < BDMA; ++c) bsrc[c] = a.sign + (int64_t)min(n0 + 64 * (4 * c + wave) + lane, a.N - 1) * (K >> 3);
+    auto dma = [&](int buf, int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            st.a[i] = arow_ok ? *reinterpret_cast<const int4 *>(qrow + k0 + 16 * i) : make_int4(0, 0, 0, 0);
+            lds_dma16(asrc[i] + k0, As(buf) + 1024 * (4 * wave + i));
 #pragma unroll
-        for (int c = 0; c < BCOL; ++c)
-            st.b[c] = bcol_ok[c] ? *reinterpret_cast<const uint4 *>(bsrc[c] + (k0 >> 3)) : make_uint4(0u, 0u, 0u, 0u);
-    };
-    auto sstore = [&](const Stage &st, int buf) {
-        int8_t *d = As(buf) + srow * LDS_ROW + shalf * 64;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<int4 *>(d + 16 * i) = st.a[i];
-#pragma unroll
-        for (int c = 0; c < BCOL; ++c)
-            if (tid + kBlock * c < BN) *reinterpret_cast<uint4 *>(Bs(buf) + (tid + kBlock * c) * 16) = st.b[c];
+        for (int c = 0; c < BDMA; ++c)
+            lds_dma16(bsrc[c] + (k0 >> 3), Bs(buf) + 1024 * (4 * c + wave));
     };
     v16i acc[4][NBW];
 #pragma unroll
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-    gload(st0, kt0 * KT);
+    dma(0, kt0 * KT);
     const bool early = a.rank <= kEarlyRank;
     char *epi = smem + (early ? main_lds<BN>() : 0);
     if (early) stage_epilogue<BN>(a, epi, m0, n0, tid);
@@ -265,24 +268,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         sc[j] = half_bits_to_float(a.row_scale[n]);
         us[j] = a.up_scale[n];
     }
-    sstore(st0, 0);
-    __syncthreads();
+    dma_barrier();
     // one K step: the A fragments of sub-step s + 1 are read from LDS while sub-step s multiplies
     auto step = [&](int cur) {
-        const int8_t *abase = As(cur) + lr * LDS_ROW + hsel * 16;
+        // row i * 32 + lr, 16-byte column 2 s + hsel, stored at column (2 s + hsel) ^ (lr & 7)
+        const int8_t *abase = As(cur) + lr * KT + ((hsel ^ (lr & 1)) << 4);
+        const int sx = (lr >> 1) & 3;
         uint4 bw[NBW];
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
             bw[j] = *reinterpret_cast<const uint4 *>(Bs(cur) + (wn * (32 * NBW) + j * 32 + lr) * 16);
         v4i af[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) af[0][i] = *reinterpret_cast<const v4i *>(abase + i * 32 * LDS_ROW);
+        for (int i = 0; i < 4; ++i) af[0][i] = *reinterpret_cast<const v4i *>(abase + i * 32 * KT + (sx << 5));
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if (s < 3) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    af[(s + 1) & 1][i] = *reinterpret_cast<const v4i *>(abase + i * 32 * LDS_ROW + (s + 1) * 32);
+                    af[(s + 1) & 1][i] = *reinterpret_cast<const v4i *>(abase + i * 32 * KT + (((s + 1) ^ sx) << 5));
             }
             // keep the next sub-step's reads ahead of this sub-step's MFMAs (the scheduler would
             // otherwise sink each read to just before its use)
@@ -301,10 +305,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int kt = kt0; kt < kt1; ++kt) {
         const int cur = (kt - kt0) & 1;
         const bool more = kt + 1 < kt1;
-        if (more) gload(st0, (kt + 1) * KT);
+        if (more) dma(cur ^ 1, (kt + 1) * KT);
         step(cur);
-        if (more) sstore(st0, cur ^ 1);
-        lds_barrier();
+        dma_barrier();
     }
     // ---- split K: publish the exact int32 partial sums; the last workgroup of the tile to arrive
     // adds the others' and runs the epilogue (no workgroup ever waits for another)
