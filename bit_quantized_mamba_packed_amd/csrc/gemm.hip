@@ -20,9 +20,10 @@
 // (no two waves expand the same bits); K in steps of 128 through double-buffered LDS, one barrier
 // per step.
 // The ragged last column tile is dispatched first so that the short workgroups do not trail.
-// k_gemm_skinny (M <= 64): one workgroup per 32 columns, its 8 waves split K and reduce their
-// int32 partial sums through LDS; A comes straight from global memory (it is 64 x K bytes and
-// stays in L2), B as above.
+// k_gemm_skinny (M <= 64): one workgroup of 16 waves per 32 columns (per 64 when that would leave
+// more workgroups than compute units), the waves split K, each issuing the loads of its share at
+// once, and add their int32 partial sums with LDS atomics (exact, so in any order); A comes straight
+// from global memory (it is 64 x K bytes and stays in L2), B as above.
 #include <algorithm>
 
 #include "decode_device.h"
@@ -65,30 +66,41 @@ __device__ __forceinline__ uint32_t u4_get(const uint4 &v, int i) {
 
 // Low-rank term of one 32 x 32 block (rows m0.., columns n0..) on bf16 MFMA from global memory:
 // lacc[r] = sum_j t'[m][j] * lora_up[n][j] for this lane's 16 outputs (used by the skinny kernel).
-// Every operand load is issued before the first MFMA (addresses clamped, operands past the rank or
-// the matrix zeroed after the load).
-__device__ __forceinline__ v16f lowrank_block(const GemmArgs &a, int mrow, int ncol, int lane) {
-    constexpr int KR = kMaxRank / 16;
+// The operands are loaded first (addresses clamped) and multiplied later (operands past the rank or
+// the matrix zeroed), so that their latency can hide behind other work.
+// Q = rank / 16 rounded up (at most kMaxRank / 16).
+constexpr int kLrQ = kMaxRank / 16;
+template <int Q>
+struct LowrankOps {
+    uint4 h[Q], l[Q];
+    uint2 w[Q];
+};
+template <int Q>
+__device__ __forceinline__ LowrankOps<Q> lowrank_load(const GemmArgs &a, int mrow, int ncol, int lane) {
     const int lj = (lane >> 5) * 8;
     const int mc = min(mrow, a.M - 1), nc = min(ncol, a.N - 1);
-    uint4 hraw[KR], lraw[KR];
-    uint2 w[KR];
+    LowrankOps<Q> o;
 #pragma unroll
-    for (int q = 0; q < KR; ++q) {
+    for (int q = 0; q < Q; ++q) {
         const int kr = min(16 * q + lj, a.rank - 8);
-        hraw[q] = *reinterpret_cast<const uint4 *>(a.thi + (int64_t)mc * a.rank + kr);
-        lraw[q] = *reinterpret_cast<const uint4 *>(a.tlo + (int64_t)mc * a.rank + kr);
-        w[q] = *reinterpret_cast<const uint2 *>(a.lora_up + (int64_t)nc * a.rank + kr);
+        o.h[q] = *reinterpret_cast<const uint4 *>(a.thi + (int64_t)mc * a.rank + kr);
+        o.l[q] = *reinterpret_cast<const uint4 *>(a.tlo + (int64_t)mc * a.rank + kr);
+        o.w[q] = *reinterpret_cast<const uint2 *>(a.lora_up + (int64_t)nc * a.rank + kr);
     }
+    return o;
+}
+template <int Q>
+__device__ __forceinline__ v16f lowrank_mma(const GemmArgs &a, const LowrankOps<Q> &o, int mrow, int ncol, int lane) {
+    const int lj = (lane >> 5) * 8;
     v16f lacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
     const bool rok = mrow < a.M, cok = ncol < a.N;
 #pragma unroll
-    for (int q = 0; q < KR; ++q) {
+    for (int q = 0; q < Q; ++q) {
         if (16 * q >= a.rank) break;
         const bool inr = 16 * q + lj + 8 <= a.rank;
-        v8bf ahi = __builtin_bit_cast(v8bf, hraw[q]), alo = __builtin_bit_cast(v8bf, lraw[q]), bup;
+        v8bf ahi = __builtin_bit_cast(v8bf, o.h[q]), alo = __builtin_bit_cast(v8bf, o.l[q]), bup;
         if (!(inr && rok)) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -96,7 +108,7 @@ __device__ __forceinline__ v16f lowrank_block(const GemmArgs &a, int mrow, int n
                 alo[e] = (__bf16)0.f;
             }
         }
-        const uint2 wq = inr && cok ? w[q] : make_uint2(0u, 0u);
+        const uint2 wq = inr && cok ? o.w[q] : make_uint2(0u, 0u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             bup[e] = (__bf16)(float)(int8_t)(wq.x >> (8 * e));
@@ -138,6 +150,9 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
     const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds);
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(base) : "memory");
 }
+
+// Workgroup barrier that orders LDS only: outstanding global loads are not waited for.
+__device__ __forceinline__ void sk_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Workgroup barrier after direct global->LDS loads: those count as vector-memory loads, so every
 // wave waits for its own to land (vmcnt) and its LDS reads to finish before the barrier.
@@ -458,90 +473,133 @@ __global__ void k_clear_u32(uint32_t *p, int n) {
 // [w nk / kSkWaves, (w + 1) nk / kSkWaves), all of its loads issued (kSkRun steps at a time) before
 // its first MFMA. The int32 partial sums meet in LDS; waves 0 and 1 each finish one 32-row block,
 // with their epilogue operands loaded before the reduction barrier.
-constexpr int kSkWaves = 8, kSkBlock = 64 * kSkWaves, kSkRun = 1;
-__global__ __launch_bounds__(kSkBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_skinny(GemmArgs a) {
-    __shared__ int red[kSkWaves][2][16][64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+constexpr int kSkWaves = 16, kSkBlock = 64 * kSkWaves;
+constexpr int kSkChunk = 1024;   // K bytes of A per LDS chunk (8 K steps of 128)
+template <int CB>
+constexpr int sk_lds_bytes() { return 2 * (64 * kSkChunk + CB * 32 * (kSkChunk / 8)); }
+
+// M <= 64 rows, CB blocks of 32 columns per workgroup. K runs in chunks of 1024 through two LDS
+// buffers: A[64][1024] (row r's 16-byte column c stored at c ^ (r & 7)) and the sign bits
+// B[CB * 32][128] (column n's 16-byte piece p stored at p ^ (n & 7)), both written by direct
+// global->LDS loads that read whole rows (coalesced), chunk c + 1 in flight while chunk c is
+// multiplied. Wave w computes output block w % (2 CB) (row block bit 0, column block bit 1..) over
+// the K steps kg, kg + KG, ... of every chunk (kg = w / (2 CB), KG = 8 / CB), so the partial sums
+// of only KG waves meet per output, in LDS after the last chunk.
+template <int CB>
+__global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a) {
+    constexpr int NBLK = 2 * CB, KG = kSkWaves / NBLK, A_BUF = 64 * kSkChunk, B_BUF = CB * 32 * (kSkChunk / 8);
+    __shared__ __align__(16) char smem[sk_lds_bytes<CB>()];
+    // the wave index is uniform: in a scalar register, so are the row pointers and block indices
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, hsel = lane >> 5;
-    const int n0 = blockIdx.x * 32;
-    const int n = n0 + lr;
-    const bool nok = n < a.N;
-    const int K = a.K, nkt = K / KT;
-    const int kb = wave * nkt / kSkWaves, ke = (wave + 1) * nkt / kSkWaves;   // may be empty
-    const uint8_t *brow = a.sign + (int64_t)(nok ? n : 0) * (K >> 3);
-    const int8_t *arow[2];
-    bool aok[2];
+    const int n0 = blockIdx.x * 32 * CB;
+    const int K = a.K, nkt = K / KT, nch = (K + kSkChunk - 1) / kSkChunk;
+    auto As = [&](int b) { return reinterpret_cast<int8_t *>(smem) + b * A_BUF; };
+    auto Bs = [&](int b) { return reinterpret_cast<uint8_t *>(smem) + 2 * A_BUF + b * B_BUF; };
+    // loads of chunk c: A rows wave + 16 i (i < 4), lane l -> 16-byte column l ^ (row & 7); B: wave
+    // w < 4 CB loads columns 8 w + l / 8, lane l -> piece (l & 7) ^ (column & 7). Rows past M and
+    // columns past N read row / column clamped into the matrix (outputs never stored); bytes past K
+    // in a short last chunk read clamped addresses (K steps never used).
+    const int8_t *arow[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int m = i * 32 + lr;
-        aok[i] = m < a.M;
-        arow[i] = a.q + (int64_t)(aok[i] ? m : 0) * a.ldq + hsel * 16;
-    }
-    v16i acc[2];
+    for (int i = 0; i < 4; ++i) arow[i] = a.q + (int64_t)min(wave + 16 * i, a.M - 1) * a.ldq;
+    const int asw = 16 * (lane ^ (wave & 7));   // row & 7 == wave & 7 for every row of this wave
+    const int bcol = 8 * wave + (lane >> 3);
+    const uint8_t *brow = a.sign + (int64_t)min(n0 + bcol, a.N - 1) * (K >> 3);
+    const int bsw = 16 * ((lane & 7) ^ (bcol & 7));
+    auto dma = [&](int c) {
+        const int b = c & 1, k0 = c * kSkChunk;
+        const int aoff = min(k0 + asw, K - 16), boff = min((k0 >> 3) + bsw, (K >> 3) - 16);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0;
-    for (int k0 = kb; k0 < ke; k0 += kSkRun) {
-        uint4 bw[kSkRun];
-        v4i af[kSkRun][2][4];
-#pragma unroll
-        for (int c = 0; c < kSkRun; ++c) {
-            const int kt = min(k0 + c, ke - 1) * KT;
-            bw[c] = nok ? *reinterpret_cast<const uint4 *>(brow + (kt >> 3)) : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    af[c][i][s] = aok[i] ? *reinterpret_cast<const v4i *>(arow[i] + kt + 32 * s) : v4i{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int c = 0; c < kSkRun; ++c) {
-            if (k0 + c >= ke) break;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const v4i bf = expand16((u4_get(bw[c], s) >> (16 * hsel)) & 0xffffu);
-#pragma unroll
-                for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[c][i][s], bf, acc[i], 0, 0, 0);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[wave][i][r][lane] = acc[i][r];
-    // every wave finishes a quarter of one 32-row block: row block ib = wave % 2, accumulator entries
-    // r in [4 rq, 4 rq + 4) (rows 8 rq + 4 (lane / 32) + 0..3), its epilogue operands loaded while the
-    // partial sums land
+        for (int i = 0; i < 4; ++i) lds_dma16(arow[i] + aoff, As(b) + (wave + 16 * i) * kSkChunk);
+        if (wave < 4 * CB) lds_dma16(brow + boff, Bs(b) + wave * 1024);
+    };
+    // epilogue operands of this wave's quarter of a block, loaded before the chunks (so that waiting
+    // for them never waits for a chunk) and used after the last one: block fb = wave / 4 (row block
+    // fb & 1, column block fb >> 1), accumulator entries r in [4 rq, 4 rq + 4), rows
+    // 8 rq + 4 (lane / 32) + 0..3
     const int nb = a.M > 32 ? 2 : 1;
-    const int ib = wave & 1, rq = wave >> 1;
-    const bool fin = ib < nb;
-    v16f lacc;
-    float sv[4], rv[4], sc = 0.f, us = 0.f;
+    const int fb = wave >> 2, fib = fb & 1, fcb = fb >> 1, rq = wave & 3;
+    const bool fin = fb < NBLK && fib < nb;
+    const int n = n0 + fcb * 32 + lr;
+    float sv[4], rv[4], us = 0.f;
     int qv[4];
+    uint16_t scb = 0;   // fp16 bits of the row scale, widened after the chunks (no wait before their loads)
+    // the low-rank operands too when the rank is at most 32 (registers), else after the last chunk
+    const bool lr_pre = a.rank <= 32;
+    LowrankOps<2> lops;
     if (fin) {
-        lacc = lowrank_block(a, ib * 32 + lr, n, lane);
         const int nc = min(n, a.N - 1);
-        sc = half_bits_to_float(a.row_scale[nc]);
+        scb = a.row_scale[nc];
         us = a.up_scale[nc];
+        const float *rrow = a.res ? a.res : a.s;   // a valid address either way; the value is dropped without res
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int mc = min(ib * 32 + 8 * rq + 4 * hsel + e, a.M - 1);
+            const int mc = min(fib * 32 + 8 * rq + 4 * hsel + e, a.M - 1);
             sv[e] = a.s[mc];
             qv[e] = a.qsum[mc];
-            rv[e] = a.res ? a.res[(int64_t)mc * a.ldres + nc] : 0.f;
+            rv[e] = rrow[a.res ? (int64_t)mc * a.ldres + nc : 0];
+        }
+        if (lr_pre) lops = lowrank_load<2>(a, fib * 32 + lr, n, lane);
+    }
+    dma(0);
+    if (nch > 1) dma(1);
+    constexpr int TPC = 8 / KG;   // K steps per wave and chunk
+    const int blk = wave % NBLK, kg = wave / NBLK, rb = blk & 1, cb = blk >> 1;
+    v16i acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0;
+    for (int c = 0; c < nch; ++c) {
+        if (c == 0 && nch > 1) {
+            // chunk 0 has landed once only this wave's loads of chunk 1 (the youngest) are pending
+            if (wave < 4 * CB) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        } else {
+            dma_barrier();   // chunk c has landed; every wave is done with the buffer chunk c + 1 goes to
+            if (c >= 1 && c + 1 < nch) dma(c + 1);
+        }
+        const int b = c & 1, ntc = min(8, nkt - 8 * c);
+        const int8_t *abase = As(b) + (rb * 32 + lr) * kSkChunk;
+        const uint8_t *bbase = Bs(b) + (cb * 32 + lr) * (kSkChunk / 8);
+        uint4 bw[TPC];
+        v4i af[TPC][4];
+#pragma unroll
+        for (int j = 0; j < TPC; ++j) {
+            const int t = min(kg + KG * j, ntc - 1);   // a K step past a short chunk is read clamped, then dropped
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[j][s] = *reinterpret_cast<const v4i *>(abase + 16 * (8 * t + ((2 * s + hsel) ^ (lr & 7))));
+            bw[j] = *reinterpret_cast<const uint4 *>(bbase + 16 * (t ^ (lr & 7)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < TPC; ++j) {
+            if (kg + KG * j >= ntc) bw[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[j][s], expand16((u4_get(bw[j], s) >> (16 * hsel)) & 0xffffu), acc, 0, 0, 0);
         }
     }
+    // the KG partial sums of every output meet in LDS (over the A buffers, once every wave is done)
     __syncthreads();
-    if (!fin || !nok) return;
+    int *red = reinterpret_cast<int *>(smem);   // [wave][16][64]
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+    v16f lacc;
+    if (fin) {
+        if (lr_pre) lacc = lowrank_mma<2>(a, lops, fib * 32 + lr, n, lane);
+        else lacc = lowrank_mma<kLrQ>(a, lowrank_load<kLrQ>(a, fib * 32 + lr, n, lane), fib * 32 + lr, n, lane);
+    }
+    __syncthreads();
+    if (!fin || n >= a.N) return;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int r = 4 * rq + e, m = ib * 32 + 8 * rq + 4 * hsel + e;
+        const int r = 4 * rq + e, m = fib * 32 + 8 * rq + 4 * hsel + e;
         if (m >= a.M) continue;
         int t = 0;
 #pragma unroll
-        for (int w = 0; w < kSkWaves; ++w) t += red[w][ib][r][lane];   // exact, fixed order
+        for (int g = 0; g < KG; ++g) t += red[((g * NBLK + fb) * 16 + r) * 64 + lane];
         const int accv = 2 * t - qv[e];
+        const float sc = half_bits_to_float(scb);
         float v = sv[e] * sc * (float)accv + us * lacc[r];
         if (a.res) v += rv[e];
         a.y[(int64_t)m * a.ldy + n] = v;
@@ -601,7 +659,10 @@ hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
     const int64_t ldmax = std::max(a.ldy, std::max(a.res ? a.ldres : 0, a.acc_tap ? a.ldacc : 0));
     if (ldmax > (int64_t)1 << 22) return hipErrorInvalidValue;
     if (a.M <= 64) {
-        k_gemm_skinny<<<(a.N + 31) / 32, kSkBlock, 0, stream>>>(a);
+        // two column blocks per workgroup when one each would not fit one workgroup per compute unit
+        const int ncb = (a.N + 31) / 32;
+        if (ncb > 256) k_gemm_skinny<2><<<(ncb + 1) / 2, kSkBlock, 0, stream>>>(a);
+        else k_gemm_skinny<1><<<ncb, kSkBlock, 0, stream>>>(a);
         return hipGetLastError();
     }
     const GemmPlan p = plan_gemm(a.M, a.N, a.K);
