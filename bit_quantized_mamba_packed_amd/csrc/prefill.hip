@@ -283,25 +283,24 @@ __global__ __launch_bounds__(64 * NW) void k_tok_quant(TokQuantArgs a) {
     }
 }
 
-// The same for few tokens (batched decode): one token per workgroup, its row split over the four
-// waves (KC chunks of 4 per thread, block reductions in a fixed order), LoRA-down on int8 MFMA with
-// the token as row 0 of the block and the K blocks split over the waves.
+// The same for few tokens (batched decode): one token per workgroup row, its LoRA-down rows split
+// in slices of kTq1Rows over blockIdx.y (so that a few tokens still fill the chip and no workgroup
+// reads more than its slice of L_dn). Every slice normalises and quantizes the whole token (the
+// same code path, so the same codes); slice 0 writes the codes, scale and code sum. The thread's
+// 4 KC codes (4 consecutive per chunk, chunks 1 KB apart) meet the same bytes of each L_dn row in
+// sdot4 products, summed over the workgroup in a fixed order (exact integers).
+constexpr int kTq1Rows = 8;
 template <int KC>
 __global__ __launch_bounds__(kBlock) void k_tok_quant1(TokQuantArgs a) {
-    __shared__ __align__(16) int8_t sq[kMaxK];
     __shared__ float red[2 * kWaves];
     __shared__ int ired[kWaves];
-    __shared__ int tred[kWaves][kMaxRank / 32][64];
+    __shared__ int tred[kWaves][kTq1Rows];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 31, hsel = lane >> 5;
-    const int m = blockIdx.x, K = a.K;
-    const int nkw = K / 128, nrb = (a.rank + 31) / 32;
-    if (m == 0)
+    const int m = blockIdx.x, slice = blockIdx.y, j0 = slice * kTq1Rows, K = a.K;
+    if (m == 0 && slice == 0)
         for (int i = tid; i < a.nzero; i += kBlock) a.zero_words[i] = 0u;
-    float dsv[kMaxRank / 32];
-#pragma unroll
-    for (int rb = 0; rb < kMaxRank / 32; ++rb) dsv[rb] = a.dn_scale[min(rb * 32 + lr, a.rank - 1)];
-    // loads first: norm weight, the row, then the LoRA-down operands (rank rows lr, bytes 16 hsel..)
+    // loads first: norm weight, the row, the slice's L_dn bytes at the thread's positions (clamped;
+    // positions past K and rows past the rank are dropped later)
     float4 wv[KC], hv[KC];
 #pragma unroll
     for (int i = 0; i < KC; ++i) wv[i] = *reinterpret_cast<const float4 *>(a.W + min((i * kBlock + tid) * 4, K - 4));
@@ -321,20 +320,12 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant1(TokQuantArgs a) {
             hv[i] = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.X) + (int64_t)m * a.ldx +
                                                       min((i * kBlock + tid) * 4, K - 4));
     }
-    const int8_t *brow[kMaxRank / 32];
-    bool bok[kMaxRank / 32];
+    int ld[kTq1Rows][KC];
 #pragma unroll
-    for (int rb = 0; rb < kMaxRank / 32; ++rb) {
-        const int j = rb * 32 + lr;
-        bok[rb] = j < a.rank;
-        brow[rb] = a.lora_dn + (int64_t)min(j, a.rank - 1) * K + hsel * 16 + wave * nkw * 32;
-    }
-    constexpr int PRE = 2 * KC * 4;   // K blocks of 32 per wave when K = 1024 KC
-    const bool pre = nrb == 1 && nkw == PRE;
-    tq_v4i bpre[PRE];
-    if (pre) {
+    for (int jj = 0; jj < kTq1Rows; ++jj) {
+        const int8_t *lrow = a.lora_dn + (int64_t)min(j0 + jj, a.rank - 1) * K;
 #pragma unroll
-        for (int c = 0; c < PRE; ++c) bpre[c] = *reinterpret_cast<const tq_v4i *>(brow[0] + c * 32);
+        for (int i = 0; i < KC; ++i) ld[jj][i] = *reinterpret_cast<const int *>(lrow + min((i * kBlock + tid) * 4, K - 4));
     }
     // ---- RMSNorm statistics and the quantizer
     float ss = 0.f, pm = 0.f;
@@ -348,7 +339,8 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant1(TokQuantArgs a) {
         h.w = ok ? h.w : 0.f;
         ss += h.x * h.x + h.y * h.y + h.z * h.z + h.w * h.w;
     }
-    if (a.tap_h) {
+    const bool writer = slice == 0;
+    if (a.tap_h && writer) {
 #pragma unroll
         for (int i = 0; i < KC; ++i) {
             const int e = (i * kBlock + tid) * 4;
@@ -379,6 +371,9 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant1(TokQuantArgs a) {
     const float inv = amax > 0.f ? 127.0f / amax : 0.f;
     const float sv = amax > 0.f ? amax / 127.0f : 0.f;
     int qs = 0;
+    int dacc[kTq1Rows];
+#pragma unroll
+    for (int jj = 0; jj < kTq1Rows; ++jj) dacc[jj] = 0;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
         const int e = (i * kBlock + tid) * 4;
@@ -392,68 +387,38 @@ __global__ __launch_bounds__(kBlock) void k_tok_quant1(TokQuantArgs a) {
             qs += q0 + q1 + q2 + q3;
             const uint32_t packed = (uint32_t)(q0 & 255) | ((uint32_t)(q1 & 255) << 8) | ((uint32_t)(q2 & 255) << 16) |
                                     ((uint32_t)(q3 & 255) << 24);
-            *reinterpret_cast<uint32_t *>(sq + e) = packed;
-            *reinterpret_cast<uint32_t *>(a.q + (int64_t)m * K + e) = packed;
-            if (a.tap_u) *reinterpret_cast<float4 *>(a.tap_u + (int64_t)m * K + e) = v;
-            if (a.tap_q) *reinterpret_cast<uint32_t *>(a.tap_q + (int64_t)m * K + e) = packed;
+#pragma unroll
+            for (int jj = 0; jj < kTq1Rows; ++jj) dacc[jj] = __builtin_amdgcn_sdot4((int)packed, ld[jj][i], dacc[jj], false);
+            if (writer) {
+                *reinterpret_cast<uint32_t *>(a.q + (int64_t)m * K + e) = packed;
+                if (a.tap_u) *reinterpret_cast<float4 *>(a.tap_u + (int64_t)m * K + e) = v;
+                if (a.tap_q) *reinterpret_cast<uint32_t *>(a.tap_q + (int64_t)m * K + e) = packed;
+            }
         }
     }
     qs = dpp_wave_isum(qs);
-    if (lane == 0) ired[wave] = qs;
+#pragma unroll
+    for (int jj = 0; jj < kTq1Rows; ++jj) dacc[jj] = dpp_wave_isum(dacc[jj]);
+    if (lane == 0) {
+        ired[wave] = qs;
+#pragma unroll
+        for (int jj = 0; jj < kTq1Rows; ++jj) tred[wave][jj] = dacc[jj];
+    }
     __syncthreads();
-    if (tid == 0) {
+    if (writer && tid == 0) {
         a.s[m] = sv;
         a.qsum[m] = (ired[0] + ired[1]) + (ired[2] + ired[3]);
         if (a.tap_s) a.tap_s[m] = sv;
     }
-    // ---- LoRA-down: the token is row 0 of the 32 x 32 block (the other rows are zero)
-    const int8_t *arow = sq + hsel * 16 + wave * nkw * 32;
-    tq_v16i acc[kMaxRank / 32];
-#pragma unroll
-    for (int rb = 0; rb < kMaxRank / 32; ++rb)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[rb][q] = 0;
-    const tq_v4i zero4 = {0, 0, 0, 0};
-    if (pre) {
-#pragma unroll
-        for (int c = 0; c < PRE; ++c) {
-            tq_v4i av = *reinterpret_cast<const tq_v4i *>(arow + c * 32);
-            if (lr != 0) av = zero4;
-            if (!bok[0]) bpre[c] = zero4;
-            acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bpre[c], acc[0], 0, 0, 0);
-        }
-    } else {
-        for (int c = 0; c < nkw; ++c) {
-            tq_v4i av = *reinterpret_cast<const tq_v4i *>(arow + c * 32);
-            if (lr != 0) av = zero4;
-#pragma unroll
-            for (int rb = 0; rb < kMaxRank / 32; ++rb) {
-                if (rb < nrb) {
-                    tq_v4i bv = *reinterpret_cast<const tq_v4i *>(brow[rb] + c * 32);
-                    if (!bok[rb]) bv = zero4;
-                    acc[rb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc[rb], 0, 0, 0);
-                }
-            }
-        }
-    }
-    // row 0 of the block sits in accumulator entry 0 of lanes 0..31 (column lr)
-#pragma unroll
-    for (int rb = 0; rb < kMaxRank / 32; ++rb) tred[wave][rb][lane] = acc[rb][0];
-    __syncthreads();
-    if (tid < 64) {
-#pragma unroll
-        for (int rb = 0; rb < kMaxRank / 32; ++rb) {
-            const int j = rb * 32 + lane;
-            if (rb < nrb && lane < 32 && j < a.rank) {
-                const int t = ((tred[0][rb][lane] + tred[1][rb][lane]) + tred[2][rb][lane]) + tred[3][rb][lane];
-                const float tp = dsv[rb] * sv * (float)t;
-                const __bf16 hi = (__bf16)tp;
-                const __bf16 lo = (__bf16)(tp - (float)hi);
-                a.thi[(int64_t)m * a.rank + j] = hi;
-                a.tlo[(int64_t)m * a.rank + j] = lo;
-                if (a.tap_t) a.tap_t[(int64_t)m * a.rank + j] = t;
-            }
-        }
+    if (tid < kTq1Rows && j0 + tid < a.rank) {
+        const int j = j0 + tid;
+        const int t = ((tred[0][tid] + tred[1][tid]) + tred[2][tid]) + tred[3][tid];
+        const float tp = a.dn_scale[j] * sv * (float)t;
+        const __bf16 hi = (__bf16)tp;
+        const __bf16 lo = (__bf16)(tp - (float)hi);
+        a.thi[(int64_t)m * a.rank + j] = hi;
+        a.tlo[(int64_t)m * a.rank + j] = lo;
+        if (a.tap_t) a.tap_t[(int64_t)m * a.rank + j] = t;
     }
 }
 
@@ -1146,10 +1111,11 @@ hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w
 hipError_t launch_tok_quant(const TokQuantArgs &a, hipStream_t stream) {
     if (a.K > kMaxK || a.K % 128 || a.rank > kMaxRank || a.rank <= 0 || a.M <= 0) return hipErrorInvalidValue;
     if (a.M <= kTq1MaxM) {   // few tokens: one per workgroup
-        if (a.K <= 1024) k_tok_quant1<1><<<a.M, kBlock, 0, stream>>>(a);
-        else if (a.K <= 2048) k_tok_quant1<2><<<a.M, kBlock, 0, stream>>>(a);
-        else if (a.K <= 4096) k_tok_quant1<4><<<a.M, kBlock, 0, stream>>>(a);
-        else k_tok_quant1<8><<<a.M, kBlock, 0, stream>>>(a);
+        const dim3 grid(a.M, (a.rank + kTq1Rows - 1) / kTq1Rows);
+        if (a.K <= 1024) k_tok_quant1<1><<<grid, kBlock, 0, stream>>>(a);
+        else if (a.K <= 2048) k_tok_quant1<2><<<grid, kBlock, 0, stream>>>(a);
+        else if (a.K <= 4096) k_tok_quant1<4><<<grid, kBlock, 0, stream>>>(a);
+        else k_tok_quant1<8><<<grid, kBlock, 0, stream>>>(a);
         return hipGetLastError();
     }
     // one wave per token while the rows fit the registers of 2 waves per SIMD, else two tokens per wave
