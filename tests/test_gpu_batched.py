@@ -45,9 +45,10 @@ def test_layer_decode_tiny_batch64_mfma():
         say(f"row {b}: forced max err {worst:.2e} conv {ec:.2e} ssm {es:.2e}")
 
 
-@pytest.mark.parametrize("B", [5, 17, 130])
+@pytest.mark.parametrize("B", [5, 17, 33, 50, 130])
 def test_layer_decode_tiny_ragged_batches_mfma(B):
-    """Batches that leave a ragged 128-row GEMM tile."""
+    """Batches that leave a ragged 32-row block of the skinny GEMM (5, 17: one block; 33, 50: a
+    partial second block) or a ragged 128-row tile of the tile GEMM (130)."""
     lw = gen.layer_weights(TINY, 11, 21)
     conv0, ssm0 = gen.initial_states(TINY, B, 11, 21, std=0.2)
     xs = gen.token_inputs(TINY, (2, B), 21, tag=2)
@@ -56,6 +57,25 @@ def test_layer_decode_tiny_ragged_batches_mfma(B):
     dense = O.dense_signs(lw)
     p1_all_rows(lw, tps, dense)
     for b in sorted({0, B // 2, B - 1}):
+        forced_chain(lw, xs, conv0, ssm0, outs, tps, final, b=b, dense=dense)
+
+
+# a tiny layer whose in_proj has 8200 rows (8 past a multiple of 64, 257 blocks of 32): the skinny
+# GEMM takes two column blocks per workgroup and its last workgroup holds a partial first block
+WIDE = gen.Dims(d_model=256, d_inner=512, d_state=16, headdim=64, ngroups=1, d_conv=4,
+                n_in_proj=8200, rank_in=8, rank_out=8)
+
+
+@pytest.mark.parametrize("B", [7, 64])
+def test_layer_decode_wide_in_proj_two_column_blocks(B):
+    lw = gen.layer_weights(WIDE, 13, 23)
+    conv0, ssm0 = gen.initial_states(WIDE, B, 13, 23, std=0.2)
+    xs = gen.token_inputs(WIDE, (2, B), 23, tag=3)
+    say(f"case: tiny layer with 8200 in_proj rows, batch {B}, 2 steps (MFMA projections)")
+    outs, tps, final, _ = run_layer(WIDE, lw, xs, conv0, ssm0)
+    dense = O.dense_signs(lw)
+    p1_all_rows(lw, tps, dense)
+    for b in sorted({0, B - 1}):
         forced_chain(lw, xs, conv0, ssm0, outs, tps, final, b=b, dense=dense)
 
 
