@@ -151,9 +151,6 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *lds) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(base) : "memory");
 }
 
-// Workgroup barrier that orders LDS only: outstanding global loads are not waited for.
-__device__ __forceinline__ void sk_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Workgroup barrier after direct global->LDS loads: those count as vector-memory loads, so every
 // wave waits for its own to land (vmcnt) and its LDS reads to finish before the barrier.
 __device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
