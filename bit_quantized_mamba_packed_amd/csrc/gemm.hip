@@ -27,6 +27,7 @@
 #include <algorithm>
 
 #include "decode_device.h"
+#include "gemm_conv.h"
 
 namespace dfssm {
 
@@ -482,8 +483,8 @@ constexpr int sk_lds_bytes() { return 2 * (64 * kSkChunk + CB * 32 * (kSkChunk /
 // multiplied. Wave w computes output block w % (2 CB) (row block bit 0, column block bit 1..) over
 // the K steps kg, kg + KG, ... of every chunk (kg = w / (2 CB), KG = 8 / CB), so the partial sums
 // of only KG waves meet per output, in LDS after the last chunk.
-template <int CB>
-__global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a) {
+template <int CB, bool CONV>
+__global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a, ConvEpi cv) {
     constexpr int NBLK = 2 * CB, KG = kSkWaves / NBLK, A_BUF = 64 * kSkChunk, B_BUF = CB * 32 * (kSkChunk / 8);
     __shared__ __align__(16) char smem[sk_lds_bytes<CB>()];
     // the wave index is uniform: in a scalar register, so are the row pointers and block indices
@@ -539,6 +540,16 @@ __global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a) {
         }
         if (lr_pre) lops = lowrank_load<2>(a, fib * 32 + lr, n, lane);
     }
+    // conv step operands of this lane's column (kind 0: z, 1: conv, 2: dt, 3: past them)
+    int kind = 3;
+    float4 cw = make_float4(0.f, 0.f, 0.f, 0.f);
+    float cbias = 0.f;
+    if (CONV && fin) {
+        kind = n < cv.E ? 0 : n < cv.E + cv.Cd ? 1 : n < cv.E + cv.Cd + cv.H ? 2 : 3;
+        const int ch = min(max(n - cv.E, 0), cv.Cd - 1), hh = min(max(n - cv.E - cv.Cd, 0), cv.H - 1);
+        cw = *reinterpret_cast<const float4 *>(cv.conv_w + (int64_t)ch * kConvTaps);
+        cbias = kind == 2 ? cv.dt_bias[hh] : cv.conv_b[ch];
+    }
     dma(0);
     if (nch > 1) dma(1);
     constexpr int TPC = 8 / KG;   // K steps per wave and chunk
@@ -576,6 +587,18 @@ __global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a) {
                 acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[j][s], expand16((u4_get(bw[j], s) >> (16 * hsel)) & 0xffffu), acc, 0, 0, 0);
         }
     }
+    // the conv state of this lane's outputs, loaded while the partial sums meet
+    float cst[4][3];
+    if (CONV && fin) {
+        const int ch = min(max(n - cv.E, 0), cv.Cd - 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int mc = min(fib * 32 + 8 * rq + 4 * hsel + e, a.M - 1);
+            const float *sp = cv.conv_state + ((int64_t)mc * cv.Cd + ch) * (kConvTaps - 1);
+#pragma unroll
+            for (int k = 0; k < kConvTaps - 1; ++k) cst[e][k] = sp[k];
+        }
+    }
     // the KG partial sums of every output meet in LDS (over the A buffers, once every wave is done)
     __syncthreads();
     int *red = reinterpret_cast<int *>(smem);   // [wave][16][64]
@@ -599,8 +622,22 @@ __global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a) {
         const float sc = half_bits_to_float(scb);
         float v = sv[e] * sc * (float)accv + us * lacc[r];
         if (a.res) v += rv[e];
-        a.y[(int64_t)m * a.ldy + n] = v;
         if (a.acc_tap) a.acc_tap[(int64_t)m * a.ldacc + n] = accv;
+        if (!CONV) {
+            a.y[(int64_t)m * a.ldy + n] = v;
+        } else if (kind == 0) {
+            cv.zbuf[(int64_t)m * cv.E + n] = v;
+        } else if (kind == 1) {
+            const int ch = n - cv.E;
+            const float pre = cbias + cw.x * cst[e][0] + cw.y * cst[e][1] + cw.z * cst[e][2] + cw.w * v;
+            float *sp = cv.conv_state + ((int64_t)m * cv.Cd + ch) * (kConvTaps - 1);
+            sp[0] = cst[e][1];
+            sp[1] = cst[e][2];
+            sp[2] = v;
+            cv.xbc[(int64_t)m * cv.Cd + ch] = silu_f(pre);
+        } else if (kind == 2) {
+            cv.dtbuf[(int64_t)m * cv.H + (n - cv.E - cv.Cd)] = softplus_f(v + cbias);
+        }
     }
 }
 
@@ -658,8 +695,8 @@ hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
     if (a.M <= 64) {
         // two column blocks per workgroup when one each would not fit one workgroup per compute unit
         const int ncb = (a.N + 31) / 32;
-        if (ncb > 256) k_gemm_skinny<2><<<(ncb + 1) / 2, kSkBlock, 0, stream>>>(a);
-        else k_gemm_skinny<1><<<ncb, kSkBlock, 0, stream>>>(a);
+        if (ncb > 256) k_gemm_skinny<2, false><<<(ncb + 1) / 2, kSkBlock, 0, stream>>>(a, ConvEpi{});
+        else k_gemm_skinny<1, false><<<ncb, kSkBlock, 0, stream>>>(a, ConvEpi{});
         return hipGetLastError();
     }
     const GemmPlan p = plan_gemm(a.M, a.N, a.K);
@@ -681,6 +718,16 @@ hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
         if (res) k_gemm_tile<2, false, true><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
         else k_gemm_tile<2, false, false><<<grid, kBlock, 0, stream>>>(a, p.ntm, p.ntn, 1);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_pm1_conv(const GemmArgs &a, const ConvEpi &c, hipStream_t stream) {
+    if (a.K % KT || a.rank % 8 || a.rank <= 0 || a.rank > kMaxRank || a.M <= 0 || a.M > 64 || a.N <= 0)
+        return hipErrorInvalidValue;
+    if (c.E <= 0 || c.Cd <= 0 || c.H <= 0 || c.E + c.Cd + c.H > a.N) return hipErrorInvalidValue;
+    const int ncb = (a.N + 31) / 32;
+    if (ncb > 256) k_gemm_skinny<2, true><<<(ncb + 1) / 2, kSkBlock, 0, stream>>>(a, c);
+    else k_gemm_skinny<1, true><<<ncb, kSkBlock, 0, stream>>>(a, c);
     return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@
 #include <algorithm>
 
 #include "decode_device.h"
+#include "gemm_conv.h"
 
 namespace dfssm {
 
@@ -1050,12 +1051,15 @@ hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w
         a.acc_tap = tp.in_acc;
         a.ldacc = s.Ninp;
         a.scratch = pws.gemm_scratch;
-        if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
-    }
-    {
-        ConvStepArgs a{pws.Y, s.Ninp, s.E, s.Cd, s.H, w.conv_w, w.conv_b, w.dt_bias, st.conv, dws.zbuf, dws.xbc, dws.dtbuf};
-        k_conv_step_y<<<dim3((s.Nin + kBlock - 1) / kBlock, batch), kBlock, 0, stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (batch <= 64) {   // the skinny GEMM runs the conv step in its epilogue
+            const ConvEpi c{s.E, s.Cd, s.H, w.conv_w, w.conv_b, w.dt_bias, st.conv, dws.zbuf, dws.xbc, dws.dtbuf};
+            if ((e = launch_gemm_pm1_conv(a, c, stream)) != hipSuccess) return e;
+        } else {
+            if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
+            ConvStepArgs cs{pws.Y, s.Ninp, s.E, s.Cd, s.H, w.conv_w, w.conv_b, w.dt_bias, st.conv, dws.zbuf, dws.xbc, dws.dtbuf};
+            k_conv_step_y<<<dim3((s.Nin + kBlock - 1) / kBlock, batch), kBlock, 0, stream>>>(cs);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     if ((e = launch_ssm_step(s, w, st, dws, batch, stream)) != hipSuccess) return e;
     {
