@@ -444,10 +444,12 @@ __device__ __forceinline__ float softplus_fast(float v) {
 }
 
 // One thread per channel (or dt column) and run of kConvRun consecutive tokens of one sequence: the
-// window of the last d_conv-1 inputs slides in registers, every input is read once, all of a run's
-// loads before its first store (a load behind a store waits for it). (Four channels per thread with
-// 16-byte accesses measured slower: fewer threads in flight.)
-constexpr int kConvRun = 32;
+// window of the last d_conv-1 inputs slides in registers (the run re-reads the d_conv-1 inputs
+// before it), all of a run's loads before its first store (a load behind a store waits for it).
+// Short runs measured fastest (8 tokens: 16.4 us per 2048 x 4416 pass, 32 tokens: 20.8): more
+// threads in flight outweigh the re-read window. (Two or four channels per thread with 8- or
+// 16-byte accesses measured slower.)
+constexpr int kConvRun = 8;
 __global__ __launch_bounds__(kBlock) void k_conv_seq(ConvSeqArgs a) {
     const int runs = (a.L + kConvRun - 1) / kConvRun;
     const int b = blockIdx.x / runs, t0 = (blockIdx.x - b * runs) * kConvRun;
