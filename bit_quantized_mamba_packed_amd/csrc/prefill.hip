@@ -766,27 +766,30 @@ __global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) 
 // groups of kScanGroup whose loads are all issued before the group's stores.
 constexpr int kScanGroup = 8;
 __global__ __launch_bounds__(kBlock) void k_ssd_scan(SsdArgs a) {
-    const int64_t PN = (int64_t)a.P * a.N;
+    const int64_t PN = (int64_t)a.P * a.N;   // even (P = 64)
     const int bh = blockIdx.y;
-    const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t e = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 2;   // two state entries per thread
     if (e >= PN) return;
-    float S = a.state[(int64_t)bh * PN + e];
+    float2 S = *reinterpret_cast<const float2 *>(a.state + (int64_t)bh * PN + e);
     for (int c0 = 0; c0 < a.nch; c0 += kScanGroup) {
-        float loc[kScanGroup], dec[kScanGroup];
+        float2 loc[kScanGroup];
+        float dec[kScanGroup];
 #pragma unroll
         for (int i = 0; i < kScanGroup; ++i) {
             const int c = min(c0 + i, a.nch - 1);
-            loc[i] = a.sloc[((int64_t)bh * a.nch + c) * PN + e];
+            loc[i] = *reinterpret_cast<const float2 *>(a.sloc + ((int64_t)bh * a.nch + c) * PN + e);
             dec[i] = a.lam_end[(int64_t)bh * a.nch + c];
         }
 #pragma unroll
         for (int i = 0; i < kScanGroup; ++i) {
             if (c0 + i >= a.nch) break;
-            a.sloc[((int64_t)bh * a.nch + c0 + i) * PN + e] = S;
-            S = expf(dec[i]) * S + loc[i];
+            *reinterpret_cast<float2 *>(a.sloc + ((int64_t)bh * a.nch + c0 + i) * PN + e) = S;
+            const float f = expf(dec[i]);
+            S.x = f * S.x + loc[i].x;
+            S.y = f * S.y + loc[i].y;
         }
     }
-    a.state[(int64_t)bh * PN + e] = S;
+    *reinterpret_cast<float2 *>(a.state + (int64_t)bh * PN + e) = S;
 }
 
 // Outputs of one (b, h, chunk): wave w owns the 16-token t-tiles {w, 15 - w} (balanced causal
@@ -1272,7 +1275,7 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         const int nblk = batch * s.H * nch;
         k_ssd_state<<<nblk, kSsdBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ssd_scan<<<dim3((s.P * s.N + kBlock - 1) / kBlock, batch * s.H), kBlock, 0, stream>>>(a);
+        k_ssd_scan<<<dim3((s.P * s.N / 2 + kBlock - 1) / kBlock, batch * s.H), kBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (s.N <= 32) k_ssd_out<1><<<nblk, kSsdBlock, 0, stream>>>(a);
         else if (s.N <= 64) k_ssd_out<2><<<nblk, kSsdBlock, 0, stream>>>(a);
