@@ -107,6 +107,10 @@ struct SsmArgs {
 // before the first store, and the C . S row sums use DPP over the row's N / 4 lanes (the total lands
 // in the row's last lane, which writes the gated output).
 constexpr int kSsmIt = 2;   // rows_per_wg * N / 4 <= kSsmIt * kBlock
+// The state is read and written once per step and not again before the next token's pass over
+// every layer, so its accesses are non-temporal (they would only evict what the caches can reuse):
+// batch-64 48-layer decode 17.3 -> 17.9 K tokens/s.
+typedef float ssm_f4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kBlock) void k_ssm(SsmArgs a) {
     const int b = blockIdx.y;
     const int wg_per_head = a.P / a.rows_per_wg;
@@ -129,7 +133,8 @@ __global__ __launch_bounds__(kBlock) void k_ssm(SsmArgs a) {
         const int ci = min((int)threadIdx.x + it * kBlock, nchunks - 1);
         const int pr = ci / n4, c4 = ci - pr * n4, p = p0 + pr;
         sp[it] = reinterpret_cast<float4 *>(a.ssm + (((int64_t)b * a.H + h) * a.P + p) * a.N) + c4;
-        S[it] = *sp[it];
+        const ssm_f4 v = __builtin_nontemporal_load(reinterpret_cast<const ssm_f4 *>(sp[it]));
+        S[it] = make_float4(v.x, v.y, v.z, v.w);
         Bn[it] = reinterpret_cast<const float4 *>(Bv)[c4];
         Cn[it] = reinterpret_cast<const float4 *>(Cv)[c4];
         x[it] = xrow[h * a.P + p];
@@ -149,7 +154,8 @@ __global__ __launch_bounds__(kBlock) void k_ssm(SsmArgs a) {
         float part = (s4.x * Cn[it].x + s4.y * Cn[it].y) + (s4.z * Cn[it].z + s4.w * Cn[it].w);
         part = dpp_group_sum_f(part, n4);
         if (ci < nchunks) {
-            *sp[it] = s4;
+            const ssm_f4 v = {s4.x, s4.y, s4.z, s4.w};
+            __builtin_nontemporal_store(v, reinterpret_cast<ssm_f4 *>(sp[it]));
             if (c4 == n4 - 1) a.gbuf[(int64_t)b * a.E + h * a.P + p] = (part + Dh * x[it]) * silu_f(z[it]);
         }
     }
