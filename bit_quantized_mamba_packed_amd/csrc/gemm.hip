@@ -211,18 +211,16 @@ __device__ __forceinline__ void stage_epilogue(const GemmArgs &a, char *base, in
 }
 
 // two waves per SIMD (<= 256 registers incl. accumulators), so two workgroups share a compute unit
+// One workgroup's tile: tile index bid, K slice z of splitk; smem holds tile_smem<64 WNB>() bytes.
 template <int WNB, bool SPLIT, bool RES>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tile(GemmArgs a, int ntm,
-                                                                                              int ntn, int splitk) {
+__device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int ntn, int splitk, int bid, int z,
+                                               char *smem, int &last_flag) {
     constexpr int BN = 64 * WNB, NBW = WNB / 2;   // N blocks of 32 per wave
     constexpr int BDMA = b_bytes<BN>() / 4096;   // 1 KB sign-bit loads per wave and K step
-    __shared__ __align__(16) char smem[tile_smem<BN>()];
-    __shared__ int last_flag;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave;
     const int lr = lane & 31, hsel = lane >> 5;
     // tile order: the ragged last column tile of every row first, then row-fastest
-    const int bid = blockIdx.x, z = blockIdx.y;
     int tm, tn;
     {
         const bool ragged = (a.N % BN) != 0;
@@ -460,6 +458,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
         }
     }
+}
+
+template <int WNB, bool SPLIT, bool RES>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tile(GemmArgs a, int ntm,
+                                                                                              int ntn, int splitk) {
+    __shared__ __align__(16) char smem[tile_smem<64 * WNB>()];
+    __shared__ int last_flag;
+    gemm_tile_body<WNB, SPLIT, RES>(a, ntm, ntn, splitk, blockIdx.x, blockIdx.y, smem, last_flag);
+}
+
+// Two independent GEMMs of one input in one launch: the nsmall K-split units of the narrow one
+// (128 x 128 tiles) first, then the wide one's 128 x 256 tiles, so that the short units end early
+// and their slots take the wide tiles that did not fit the first round (instead of a second launch
+// whose few workgroups leave most compute units idle).
+constexpr int kPairLds = tile_smem<256>() > tile_smem<128>() ? tile_smem<256>() : tile_smem<128>();
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tile_pair(
+    GemmArgs wide, int ntm_w, int ntn_w, GemmArgs narrow, int ntm_n, int ntn_n, int splitk_n) {
+    __shared__ __align__(16) char smem[kPairLds];
+    __shared__ int last_flag;
+    const int tiles_n = ntm_n * ntn_n, nsmall = tiles_n * splitk_n;
+    const int bid = blockIdx.x;
+    if (bid < nsmall) gemm_tile_body<2, true, false>(narrow, ntm_n, ntn_n, splitk_n, bid % tiles_n, bid / tiles_n, smem, last_flag);
+    else gemm_tile_body<4, false, false>(wide, ntm_w, ntn_w, 1, bid - nsmall, 0, smem, last_flag);
 }
 
 __global__ void k_clear_u32(uint32_t *p, int n) {
@@ -728,6 +749,27 @@ hipError_t launch_gemm_pm1_conv(const GemmArgs &a, const ConvEpi &c, hipStream_t
     const int ncb = (a.N + 31) / 32;
     if (ncb > 256) k_gemm_skinny<2, true><<<(ncb + 1) / 2, kSkBlock, 0, stream>>>(a, c);
     else k_gemm_skinny<1, true><<<ncb, kSkBlock, 0, stream>>>(a, c);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_pm1_pair(const GemmArgs &wide, const GemmArgs &narrow, hipStream_t stream) {
+    for (const GemmArgs *a : {&wide, &narrow}) {
+        if (a->K % KT || a->rank % 8 || a->rank <= 0 || a->rank > kMaxRank || a->M <= 64 || a->N <= 0 || a->res)
+            return hipErrorInvalidValue;
+        const int64_t ldmax = std::max(a->ldy, a->acc_tap ? a->ldacc : (int64_t)0);
+        if (ldmax > (int64_t)1 << 22) return hipErrorInvalidValue;
+    }
+    const GemmPlan pw = plan_gemm(wide.M, wide.N, wide.K), pn = plan_gemm(narrow.M, narrow.N, narrow.K);
+    if (pw.wnb != 4 || pw.splitk != 1 || pn.wnb != 2 || pn.splitk < 2) {   // not the shapes the pair serves
+        hipError_t e = launch_gemm_pm1(wide, stream);
+        return e != hipSuccess ? e : launch_gemm_pm1(narrow, stream);
+    }
+    const int tiles_n = pn.ntm * pn.ntn;
+    if (!narrow.scratch || tiles_n * 4 > kCntBytes) return hipErrorInvalidValue;
+    if (!narrow.counters_zeroed)
+        k_clear_u32<<<(tiles_n + kBlock - 1) / kBlock, kBlock, 0, stream>>>(static_cast<uint32_t *>(narrow.scratch), tiles_n);
+    const int grid = tiles_n * pn.splitk + pw.ntm * pw.ntn;
+    k_gemm_tile_pair<<<grid, kBlock, 0, stream>>>(wide, pw.ntm, pw.ntn, narrow, pn.ntm, pn.ntn, pn.splitk);
     return hipGetLastError();
 }
 

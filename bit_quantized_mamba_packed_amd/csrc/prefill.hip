@@ -1224,21 +1224,29 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.ldy = s.Ninp;
         a.ldacc = s.Ninp;
         a.scratch = ws.gemm_scratch;
-        // two launches: the z | x rows (wide tiles, a whole number of them), then the B | C | dt rows
-        // (few columns: narrow tiles with the K range split), so that neither leaves a short tail
-        // of whole tiles behind
+        // two GEMMs over the same codes: the z | x rows (wide tiles, a whole number of them) and the
+        // B | C | dt rows (few columns: narrow tiles with the K range split), in one launch with the
+        // narrow units first, so that neither leaves a short tail of whole tiles behind
         const int cuts[3] = {0, 2 * s.E, s.Ninp};
-        for (int part = 0; part < 2; ++part) {
-            const int n0 = cuts[part];
-            a.N = cuts[part + 1] - n0;
-            a.sign = w.in_proj.sign + (int64_t)n0 * (s.D / 8);
-            a.row_scale = w.in_proj.row_scale + n0;
-            a.up_scale = w.in_proj.lora_up_scale + n0;
-            a.lora_up = w.in_proj.lora_up + (int64_t)n0 * s.Rin;
-            a.y = ws.Y + n0;
-            a.acc_tap = tp.in_acc ? tp.in_acc + n0 : nullptr;
-            a.counters_zeroed = 1;
-            if ((e = launch_gemm_pm1(a, stream)) != hipSuccess) return e;
+        GemmArgs part[2];
+        for (int k = 0; k < 2; ++k) {
+            GemmArgs &g = part[k];
+            g = a;
+            const int n0 = cuts[k];
+            g.N = cuts[k + 1] - n0;
+            g.sign = w.in_proj.sign + (int64_t)n0 * (s.D / 8);
+            g.row_scale = w.in_proj.row_scale + n0;
+            g.up_scale = w.in_proj.lora_up_scale + n0;
+            g.lora_up = w.in_proj.lora_up + (int64_t)n0 * s.Rin;
+            g.y = ws.Y + n0;
+            g.acc_tap = tp.in_acc ? tp.in_acc + n0 : nullptr;
+            g.counters_zeroed = 1;
+        }
+        if (M > 64) {
+            if ((e = launch_gemm_pm1_pair(part[0], part[1], stream)) != hipSuccess) return e;
+        } else {
+            for (int k = 0; k < 2; ++k)
+                if ((e = launch_gemm_pm1(part[k], stream)) != hipSuccess) return e;
         }
     }
     // 3/4. conv over the sequence, dt, conv-state handoff
