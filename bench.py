@@ -215,17 +215,18 @@ def run_decode_b1(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
 def run_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     """48 layer prefills of 2048 bf16 tokens (chunk 256) from zero states; one step = the stack."""
     nL, S, Q = args.layers, 2048, 256
-    states = [Dv.DeviceState(np.zeros((1, dims.conv_dim, dims.d_conv - 1), np.float32),
-                             np.zeros((1, dims.nheads, dims.headdim, dims.d_state), np.float32)) for _ in range(nL)]
+    # every layer's state in one allocation, reset by one fill per step
+    conv_all = torch.zeros((nL, 1, dims.conv_dim, dims.d_conv - 1), dtype=torch.float32, device="cuda")
+    ssm_all = torch.zeros((nL, 1, dims.nheads, dims.headdim, dims.d_state), dtype=torch.float32, device="cuda")
+    states = [Dv.DeviceState.from_tensors(conv_all[l], ssm_all[l]) for l in range(nL)]
     x_np = gen.token_inputs(dims, (1, S), 0, tag=11, bf16=True)
     xb = torch.from_numpy(x_np).cuda().to(torch.bfloat16)
     h = [torch.empty((1, S, dims.d_model), dtype=torch.float32, device="cuda") for _ in range(2)]
     ws = Dv.workspace(dims, L.DFSSM_OP_LAYER_PREFILL, 1, S)
 
     def step():
-        for st in states:
-            st.conv.zero_()
-            st.ssm.zero_()
+        conv_all.zero_()
+        ssm_all.zero_()
         for l in range(nL):
             src = xb if l == 0 else h[(l - 1) % 2]
             Dv.layer_prefill(dims, layers[l], states[l], src, h[l % 2], Q, ws)

@@ -67,6 +67,17 @@ class DeviceState:
         self.conv.copy_(torch.from_numpy(np.asarray(conv, np.float32)))
         self.ssm.copy_(torch.from_numpy(np.asarray(ssm, np.float32)))
 
+    @classmethod
+    def from_tensors(cls, conv: torch.Tensor, ssm: torch.Tensor) -> "DeviceState":
+        """A state over existing contiguous fp32 device tensors (e.g. views of one allocation that
+        holds a whole stack's states, so that they can be reset with one fill)."""
+        if not (conv.is_contiguous() and ssm.is_contiguous()) or conv.dtype != torch.float32 or ssm.dtype != torch.float32:
+            raise ValueError("DeviceState.from_tensors: contiguous fp32 tensors required")
+        st = cls.__new__(cls)
+        st.conv, st.ssm = conv, ssm
+        st.struct = L.dfssm_layer_state(conv.data_ptr(), ssm.data_ptr())
+        return st
+
 
 class Taps:
     """Tap buffers for `records` token records (layout [record][...] as include/dfssm.h states)."""
