@@ -10,9 +10,10 @@ library launches on (the persistent stack kernel is the only long-running kernel
 which gives the kernel's average launch duration for the roofline.
 
 Secondary workloads (reported under "secondary", or alone with --workload):
-  prefill2048  48 dfssm_layer_prefill calls over 2048 bf16 tokens (chunk 256) from zero states,
-               then 16 stack-decode steps from the handed-off states (checked, not timed);
-               roofline: int8 MFMA ops of the scaffold GEMMs / time.
+  prefill2048  one dfssm_stack_prefill of 2048 bf16 tokens (chunk 256) through the 48 layers from
+               zero states, then 16 stack-decode steps from the handed-off states and the last
+               position's output (checked, not timed); roofline: int8 MFMA ops of the scaffold
+               GEMMs / step time, and / the GEMM kernels' own time from the committed trace.
   decode_b64   48-layer stack decode at batch 64 (states ~ N(0, 0.1)), 128 tokens per sequence
                per step; roofline: algorithmic HBM bytes (weights once per token step, every
                sequence's conv/SSM state read and written) / time.
@@ -170,8 +171,8 @@ def run_decode_b1(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
     wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws), args.steps,
                             args.warmup, torch)
-    if not torch.isfinite(y).all():
-        raise SystemExit("non-finite decode output")
+    if Dv.stack_status(ws) != L.DFSSM_STATUS_OK or not torch.isfinite(y).all():
+        raise SystemExit("batch-1 stack decode failed (wait timeout or non-finite output)")
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -213,38 +214,35 @@ def run_decode_b1(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
 
 
 def run_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
-    """48 layer prefills of 2048 bf16 tokens (chunk 256) from zero states; one step = the stack."""
+    """One dfssm_stack_prefill of 2048 bf16 tokens (chunk 256) through the 48 layers from zero
+    states; one step = the whole stack prefill including its final RMSNorm."""
     nL, S, Q = args.layers, 2048, 256
     # every layer's state in one allocation, reset by one fill per step
     conv_all = torch.zeros((nL, 1, dims.conv_dim, dims.d_conv - 1), dtype=torch.float32, device="cuda")
     ssm_all = torch.zeros((nL, 1, dims.nheads, dims.headdim, dims.d_state), dtype=torch.float32, device="cuda")
-    states = [Dv.DeviceState.from_tensors(conv_all[l], ssm_all[l]) for l in range(nL)]
+    states = [Dv.DeviceState.from_tensors(conv_all[l], ssm_all[l], dims, 1) for l in range(nL)]
     x_np = gen.token_inputs(dims, (1, S), 0, tag=11, bf16=True)
     xb = torch.from_numpy(x_np).cuda().to(torch.bfloat16)
-    h = [torch.empty((1, S, dims.d_model), dtype=torch.float32, device="cuda") for _ in range(2)]
-    ws = Dv.workspace(dims, L.DFSSM_OP_LAYER_PREFILL, 1, S)
+    fw = torch.ones(dims.d_model, dtype=torch.float32, device="cuda")
+    y = torch.empty((1, S, dims.d_model), dtype=torch.float32, device="cuda")
+    ws = Dv.workspace(dims, L.DFSSM_OP_STACK_PREFILL, 1, S, nL)
 
     def step():
         conv_all.zero_()
         ssm_all.zero_()
-        for l in range(nL):
-            src = xb if l == 0 else h[(l - 1) % 2]
-            Dv.layer_prefill(dims, layers[l], states[l], src, h[l % 2], Q, ws)
+        Dv.stack_prefill(dims, layers, states, fw, xb, y, Q, ws)
 
     wall, launch_ms = timed(step, args.steps, args.warmup, torch)
-    out_last = h[(nL - 1) % 2]
-    if not torch.isfinite(out_last).all():
-        raise SystemExit("non-finite prefill output")
-    # hand the final states to 16 decode steps (not timed), fed the RMSNorm of the last position
-    fw = torch.ones(dims.d_model, dtype=torch.float32, device="cuda")
-    x_last = out_last[:, -1, :].contiguous()
-    x0 = x_last * torch.rsqrt(x_last.pow(2).mean(-1, keepdim=True) + dims.eps)
-    y = torch.empty((16, 1, dims.d_model), dtype=torch.float32, device="cuda")
-    wsd = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
-    Dv.stack_decode(dims, layers, states, fw, x0, y, 16, wsd)
-    torch.cuda.synchronize()
     if not torch.isfinite(y).all():
-        raise SystemExit("non-finite decode after prefill")
+        raise SystemExit("non-finite prefill output")
+    # the final states go on to 16 decode steps (not timed) from the last position's output
+    x0 = y[:, -1, :].contiguous()
+    yd = torch.empty((16, 1, dims.d_model), dtype=torch.float32, device="cuda")
+    wsd = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
+    Dv.stack_decode(dims, layers, states, fw, x0, yd, 16, wsd)
+    torch.cuda.synchronize()
+    if Dv.stack_status(wsd) != L.DFSSM_STATUS_OK or not torch.isfinite(yd).all():
+        raise SystemExit("decode after prefill failed")
     ops = int8_ops_per_token(dims) * S * nL
     avg_s = sum(launch_ms) / len(launch_ms) / 1e3
     achieved = ops / avg_s / 1e12
@@ -260,6 +258,9 @@ def run_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
                      "kernel": "whole prefill step (all kernels of 48 layers); scaffold int8 ops only",
                      "algorithmic_ops_per_launch": ops, "avg_launch_ms": round(avg_s * 1e3, 3)},
     }
+    gemm = prefill_gemm_profile(dims, nL, S)
+    if gemm is not None:
+        out["roofline_scaffold_gemms"] = gemm
     if not args.no_cpu_baseline:
         from oracle import dfssm_oracle as O
         nl_cpu = 2
@@ -276,6 +277,41 @@ def run_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     return out
 
 
+PREFILL_GEMM_PROFILE = os.path.join(ROOT, "profiles", "prefill2048_gemm_kernels.json")
+PREFILL_GEMM_SOURCES = ("bit_quantized_mamba_packed_amd/csrc/gemm.hip", "bit_quantized_mamba_packed_amd/csrc/gemm_conv.h",
+                        "bit_quantized_mamba_packed_amd/csrc/dfssm_internal.h")
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def prefill_gemm_profile(d, n_layers: int, S: int):
+    """The scaffold GEMM kernels' share of the int8 MFMA roofline, from the committed rocprofv3
+    kernel trace of this workload (per-launch average durations of the in_proj and out_proj GEMM
+    kernels); None when the GEMM sources changed since the trace was taken."""
+    if not os.path.exists(PREFILL_GEMM_PROFILE):
+        return None
+    p = json.load(open(PREFILL_GEMM_PROFILE))
+    if p.get("source_hash") != source_hash(PREFILL_GEMM_SOURCES):
+        return None
+    ops_in = 2 * d.n_in_proj * d.d_model * S
+    ops_out = 2 * d.d_model * d.d_inner * S
+    t_in, t_out = p["in_proj_avg_ns"] * 1e-9, p["out_proj_avg_ns"] * 1e-9
+    tot = n_layers * (t_in + t_out)
+    ach = n_layers * (ops_in + ops_out) / tot / 1e12
+    return {"bound": "mfma", "peak": 5000.0, "unit": "TFLOP/s", "achieved": round(ach, 2),
+            "frac": round(ach / 5000.0, 5), "gemm_ms_per_prefill": round(tot * 1e3, 3),
+            "in_proj": {"kernel": p["in_proj_kernel"], "avg_us": round(t_in * 1e6, 2),
+                        "frac": round(ops_in / t_in / 1e12 / 5000.0, 5)},
+            "out_proj": {"kernel": p["out_proj_kernel"], "avg_us": round(t_out * 1e6, 2),
+                         "frac": round(ops_out / t_out / 1e12 / 5000.0, 5)},
+            "source": "profiles/prefill2048_gemm_kernels.json (rocprofv3 kernel trace of this workload)"}
+
+
 def run_decode_b64(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     nL, B, T = args.layers, 64, 128
     states = []
@@ -289,8 +325,8 @@ def run_decode_b64(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict
     steps = max(1, min(args.steps, 2))
     wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws), steps,
                             min(args.warmup, 1), torch)
-    if not torch.isfinite(y).all():
-        raise SystemExit("non-finite batched decode output")
+    if Dv.stack_status(ws) != L.DFSSM_STATUS_OK or not torch.isfinite(y).all():
+        raise SystemExit("batched stack decode failed")
     per_step = decode_b64_bytes_per_step(dims, nL, B)
     avg_s = sum(launch_ms) / len(launch_ms) / 1e3
     achieved = per_step * T / avg_s / 1e9

@@ -18,13 +18,22 @@ DFSSM_EHIP = -4
 DFSSM_OP_LAYER_DECODE = 0
 DFSSM_OP_LAYER_PREFILL = 1
 DFSSM_OP_STACK_DECODE = 2
+DFSSM_OP_STACK_PREFILL = 3
+
+DFSSM_STACK_STATUS_OFFSET = 0
+DFSSM_STATUS_OK = 0
+DFSSM_STATUS_TIMEOUT = 1
+
+DFSSM_PATH_AUTO = 0
+DFSSM_PATH_FLOW = 1
+DFSSM_PATH_PER_LAYER = 2
 
 DFSSM_F32 = 0
 DFSSM_BF16 = 1
 
 # every symbol include/dfssm.h declares
 EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_prefill",
-           "dfssm_stack_decode", "dfssm_strerror")
+           "dfssm_stack_decode", "dfssm_stack_decode_ex", "dfssm_stack_prefill", "dfssm_strerror")
 
 
 class dfssm_dims(C.Structure):
@@ -58,6 +67,10 @@ class dfssm_taps(C.Structure):
                 ("out_acc", C.c_void_p), ("out_t", C.c_void_p)]
 
 
+class dfssm_stack_opts(C.Structure):
+    _fields_ = [("path", C.c_int32), ("reserved", C.c_int32)]
+
+
 _lib = None
 
 
@@ -84,6 +97,15 @@ def load() -> C.CDLL:
                                        C.POINTER(dfssm_layer_state), C.c_int32, P, P, P, C.c_int32,
                                        C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
     lib.dfssm_stack_decode.restype = C.c_int
+    lib.dfssm_stack_decode_ex.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
+                                          C.POINTER(dfssm_layer_state), C.c_int32, P, P, P, C.c_int32,
+                                          C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps),
+                                          C.POINTER(dfssm_stack_opts), P]
+    lib.dfssm_stack_decode_ex.restype = C.c_int
+    lib.dfssm_stack_prefill.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
+                                        C.POINTER(dfssm_layer_state), C.c_int32, P, P, C.c_int32, P,
+                                        C.c_int32, C.c_int32, C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
+    lib.dfssm_stack_prefill.restype = C.c_int
     lib.dfssm_strerror.argtypes = [C.c_int]
     lib.dfssm_strerror.restype = C.c_char_p
     _lib = lib
@@ -114,6 +136,18 @@ def dfssm_stack_decode(dims, layers, states, n_layers, final_norm_w, x0, y, batc
     """layers / states: ctypes arrays (dfssm_layer_weights * n) / (dfssm_layer_state * n)."""
     return int(load().dfssm_stack_decode(C.byref(dims), layers, states, n_layers, final_norm_w, x0, y, batch,
                                          n_steps, ws, ws_bytes, _ref(taps), stream))
+
+
+def dfssm_stack_decode_ex(dims, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, ws, ws_bytes,
+                          taps=None, opts=None, stream=None) -> int:
+    return int(load().dfssm_stack_decode_ex(C.byref(dims), layers, states, n_layers, final_norm_w, x0, y, batch,
+                                            n_steps, ws, ws_bytes, _ref(taps), _ref(opts), stream))
+
+
+def dfssm_stack_prefill(dims, layers, states, n_layers, final_norm_w, x_in, x_dtype, y, batch, seqlen, chunk, ws,
+                        ws_bytes, taps=None, stream=None) -> int:
+    return int(load().dfssm_stack_prefill(C.byref(dims), layers, states, n_layers, final_norm_w, x_in, x_dtype, y,
+                                          batch, seqlen, chunk, ws, ws_bytes, _ref(taps), stream))
 
 
 def dfssm_strerror(status: int) -> str:

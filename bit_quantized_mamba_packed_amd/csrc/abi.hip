@@ -1,7 +1,5 @@
 // C ABI of the DF-SSM hot path: argument validation, workspace carving and launch sequencing.
 // Every check happens before the first enqueue, so a rejected call has no side effect.
-#include <stdlib.h>
-
 #include <algorithm>
 
 #include "dfssm_internal.h"
@@ -83,11 +81,12 @@ int check_taps(const dfssm_taps *t) {
     return DFSSM_OK;
 }
 
+// A stack decode's workspace starts with its status word (kAlign bytes), then the decode carve.
 size_t decode_ws_bytes(const Shape &s, int batch, bool stack, int n_layers = 0) {
     DecodeWs w = carve_decode_ws(s, batch, nullptr, stack);
-    size_t extra = 0;
-    if (stack && stack_persistent_ok(s, batch))
-        extra = std::max(stack_extra_ws_bytes(s, batch, n_layers), stack2_extra_ws_bytes(s, batch, n_layers));
+    size_t extra = stack ? kAlign : 0;
+    if (stack && stack2_ok(s, batch))
+        extra += stack2_extra_ws_bytes(s, batch, n_layers);
     else if (decode_uses_mfma(s, batch)) extra = carve_prefill_ws(s, batch, 1, 1, nullptr).bytes;
     return w.bytes + extra;
 }
@@ -96,6 +95,42 @@ bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64 || c
 
 size_t prefill_ws_bytes(const Shape &s, int batch, int seqlen, int chunk) {
     return carve_prefill_ws(s, batch, seqlen, chunk, nullptr).bytes;
+}
+
+bool prefill_size_ok(const Shape &s, int batch, int seqlen) {
+    return seqlen > 0 && seqlen <= 65536 && batch > 0 && batch <= 64 && (int64_t)batch * seqlen <= (1 << 20) &&
+           s.Rin % 8 == 0 && s.Rout % 8 == 0;
+}
+
+// Largest prefill carve over the supported chunk lengths.
+size_t prefill_ws_any_chunk(const Shape &s, int batch, int seqlen) {
+    size_t mx = 0;
+    for (int c = 16; c <= 256; c *= 2) mx = std::max(mx, prefill_ws_bytes(s, batch, seqlen, c));
+    return mx;
+}
+
+// A stack prefill: one residual buffer [batch][seqlen][D] fp32, then one layer's prefill carve.
+size_t stack_prefill_hbuf_bytes(const Shape &s, int batch, int seqlen) {
+    return align_up((size_t)batch * seqlen * s.D * 4, kAlign);
+}
+
+// Tap pointers of one layer's records inside [n_layers][records_per_layer][...] buffers.
+dfssm_taps taps_for_layer(const dfssm_taps *t, const Shape &s, int64_t rec) {
+    dfssm_taps o{};
+    if (!t) return o;
+    const TapPtrs p = tap_offset(t, s, rec);
+    o.h_in = p.h_in;
+    o.in_u = p.in_u;
+    o.in_q = p.in_q;
+    o.in_s = p.in_s;
+    o.in_acc = p.in_acc;
+    o.in_t = p.in_t;
+    o.out_u = p.out_u;
+    o.out_q = p.out_q;
+    o.out_s = p.out_s;
+    o.out_acc = p.out_acc;
+    o.out_t = p.out_t;
+    return o;
 }
 
 // One decode step of one layer through whichever projection path suits the batch.
@@ -107,11 +142,6 @@ hipError_t decode_step(const Shape &s, const dfssm_layer_weights &w, const dfssm
         return launch_layer_decode_mfma(s, w, st, x_in, x_out, batch, d, p, tp, stream);
     }
     return launch_layer_decode(s, w, st, x_in, x_out, batch, d, tp, stream);
-}
-
-int env_int(const char *name, int dflt) {
-    const char *v = getenv(name);
-    return v ? atoi(v) : dflt;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DFSSM_OK : DFSSM_EHIP; }
@@ -179,14 +209,11 @@ size_t dfssm_workspace_bytes(const dfssm_dims *dims, int32_t op, int32_t batch, 
             if (n_layers <= 0) return 0;
             return decode_ws_bytes(s, batch, true, n_layers);
         case DFSSM_OP_LAYER_PREFILL:
-            if (seqlen <= 0 || seqlen > 65536 || batch > 64 || (int64_t)batch * seqlen > (1 << 20) || s.Rin % 8 ||
-                s.Rout % 8)
-                return 0;
-            {   // enough for every supported chunk length
-                size_t mx = 0;
-                for (int c = 16; c <= 256; c *= 2) mx = std::max(mx, prefill_ws_bytes(s, batch, seqlen, c));
-                return mx;
-            }
+            if (!prefill_size_ok(s, batch, seqlen)) return 0;
+            return prefill_ws_any_chunk(s, batch, seqlen);
+        case DFSSM_OP_STACK_PREFILL:
+            if (n_layers <= 0 || !prefill_size_ok(s, batch, seqlen)) return 0;
+            return stack_prefill_hbuf_bytes(s, batch, seqlen) + prefill_ws_any_chunk(s, batch, seqlen);
         default: return 0;
     }
 }
@@ -216,9 +243,8 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w, co
     if (x_dtype != DFSSM_F32 && x_dtype != DFSSM_BF16) return DFSSM_EINVAL;
     if (x_in == static_cast<const void *>(x_out)) return DFSSM_EINVAL;
     if (!chunk_ok(chunk)) return DFSSM_EUNSUPPORTED;
-    if (seqlen > 65536 || batch > 64 || (int64_t)batch * seqlen > (1 << 20)) return DFSSM_EUNSUPPORTED;
     const Shape s = shape_of(*dims);
-    if (s.Rin % 8 || s.Rout % 8) return DFSSM_EUNSUPPORTED;
+    if (!prefill_size_ok(s, batch, seqlen)) return DFSSM_EUNSUPPORTED;
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
     if (ws_bytes < prefill_ws_bytes(s, batch, seqlen, chunk)) return DFSSM_EWORKSPACE;
     const PrefillWs p = carve_prefill_ws(s, batch, seqlen, chunk, ws);
@@ -229,6 +255,14 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w, co
 int dfssm_stack_decode(const dfssm_dims *dims, const dfssm_layer_weights *layers, const dfssm_layer_state *states,
                        int32_t n_layers, const float *final_norm_w, const float *x0, float *y, int32_t batch,
                        int32_t n_steps, void *ws, size_t ws_bytes, const dfssm_taps *taps, void *stream) {
+    return dfssm_stack_decode_ex(dims, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, ws, ws_bytes,
+                                 taps, nullptr, stream);
+}
+
+int dfssm_stack_decode_ex(const dfssm_dims *dims, const dfssm_layer_weights *layers, const dfssm_layer_state *states,
+                          int32_t n_layers, const float *final_norm_w, const float *x0, float *y, int32_t batch,
+                          int32_t n_steps, void *ws, size_t ws_bytes, const dfssm_taps *taps,
+                          const dfssm_stack_opts *opts, void *stream) {
     int r;
     if ((r = check_dims(dims))) return r;
     if (!layers || !states || n_layers <= 0 || n_steps <= 0 || batch <= 0) return DFSSM_EINVAL;
@@ -238,32 +272,75 @@ int dfssm_stack_decode(const dfssm_dims *dims, const dfssm_layer_weights *layers
     if ((r = check_taps(taps))) return r;
     if (bad_ptr(final_norm_w) || bad_ptr(x0) || bad_ptr(y)) return DFSSM_EINVAL;
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
+    const dfssm_stack_opts o = opts ? *opts : dfssm_stack_opts{};
+    if (o.path < DFSSM_PATH_AUTO || o.path > DFSSM_PATH_PER_LAYER || o.reserved != 0) return DFSSM_EINVAL;
     const Shape s = shape_of(*dims);
     if (ws_bytes < decode_ws_bytes(s, batch, true, n_layers)) return DFSSM_EWORKSPACE;
-    const DecodeWs wsp = carve_decode_ws(s, batch, ws, true);
+    const bool flow = stack2_ok(s, batch);
+    int path = o.path;
+    if (path == DFSSM_PATH_AUTO) path = flow ? DFSSM_PATH_FLOW : DFSSM_PATH_PER_LAYER;
+    if (path == DFSSM_PATH_FLOW && !flow) return DFSSM_EUNSUPPORTED;
+    int32_t *status = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + DFSSM_STACK_STATUS_OFFSET);
+    char *wsd = static_cast<char *>(ws) + kAlign;
+    const DecodeWs wsp = carve_decode_ws(s, batch, wsd, true);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t ny = (int64_t)n_steps * batch * s.D;
+    int *err = nullptr;
     hipError_t e;
-    if (stack_persistent_ok(s, batch) && stack2_ok(s, batch))
-        return hip_status(launch_stack2(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps,
-                                        static_cast<char *>(ws) + wsp.bytes, taps, st));
-    if (stack_persistent_ok(s, batch)) {
-        // DFSSM_STACK_MAX_WGS caps the resident grid (a tuning knob; 0 = as many as useful)
-        e = launch_stack_persistent(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, wsp,
-                                    static_cast<char *>(ws) + wsp.bytes, taps, env_int("DFSSM_STACK_MAX_WGS", 0), st);
-        return hip_status(e);
+    if (path == DFSSM_PATH_FLOW) {
+        e = launch_stack2(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, wsd + wsp.bytes, taps, &err, st);
+        if (e != hipSuccess) return DFSSM_EHIP;
+        return hip_status(launch_stack_finish(err, status, y, ny, st));
     }
     const int64_t rowsz = (int64_t)batch * s.D;
     for (int t = 0; t < n_steps; ++t) {
         const float *xin = t == 0 ? x0 : y + (t - 1) * rowsz;
         for (int l = 0; l < n_layers; ++l) {
             const TapPtrs tp = tap_offset(taps, s, ((int64_t)t * n_layers + l) * batch);
-            e = decode_step(s, layers[l], states[l], l == 0 ? xin : wsp.hbuf, wsp.hbuf, batch, ws, true, tp, st);
+            e = decode_step(s, layers[l], states[l], l == 0 ? xin : wsp.hbuf, wsp.hbuf, batch, wsd, true, tp, st);
             if (e != hipSuccess) return DFSSM_EHIP;
         }
         e = launch_final_norm(wsp.hbuf, final_norm_w, y + t * rowsz, nullptr, s.D, s.eps, batch, st);
         if (e != hipSuccess) return DFSSM_EHIP;
     }
-    return DFSSM_OK;
+    return hip_status(launch_stack_finish(nullptr, status, y, ny, st));
+}
+
+int dfssm_stack_prefill(const dfssm_dims *dims, const dfssm_layer_weights *layers, const dfssm_layer_state *states,
+                        int32_t n_layers, const float *final_norm_w, const void *x_in, int32_t x_dtype, float *y,
+                        int32_t batch, int32_t seqlen, int32_t chunk, void *ws, size_t ws_bytes,
+                        const dfssm_taps *taps, void *stream) {
+    int r;
+    if ((r = check_dims(dims))) return r;
+    if (!layers || !states || n_layers <= 0 || batch <= 0 || seqlen <= 0) return DFSSM_EINVAL;
+    if (n_layers > 1024) return DFSSM_EUNSUPPORTED;
+    for (int l = 0; l < n_layers; ++l)
+        if ((r = check_weights(&layers[l])) || (r = check_state(&states[l]))) return r;
+    if ((r = check_taps(taps))) return r;
+    if (bad_ptr(final_norm_w) || bad_ptr(x_in) || bad_ptr(y)) return DFSSM_EINVAL;
+    if (x_dtype != DFSSM_F32 && x_dtype != DFSSM_BF16) return DFSSM_EINVAL;
+    if (x_in == static_cast<const void *>(y)) return DFSSM_EINVAL;
+    if (!chunk_ok(chunk)) return DFSSM_EUNSUPPORTED;
+    const Shape s = shape_of(*dims);
+    if (!prefill_size_ok(s, batch, seqlen)) return DFSSM_EUNSUPPORTED;
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
+    const size_t hb = stack_prefill_hbuf_bytes(s, batch, seqlen);
+    if (ws_bytes < hb + prefill_ws_bytes(s, batch, seqlen, chunk)) return DFSSM_EWORKSPACE;
+    float *hbuf = static_cast<float *>(ws);
+    const PrefillWs p = carve_prefill_ws(s, batch, seqlen, chunk, static_cast<char *>(ws) + hb);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t per_layer = (int64_t)batch * seqlen;
+    // layer outputs alternate between y and the workspace buffer so that the last one lands in y,
+    // which the stack's final RMSNorm then rewrites in place (row by row, each row read first)
+    for (int l = 0; l < n_layers; ++l) {
+        const void *src = l == 0 ? x_in : ((n_layers - l) % 2 == 0 ? static_cast<const void *>(y) : hbuf);
+        float *dst = (n_layers - 1 - l) % 2 == 0 ? y : hbuf;
+        const dfssm_taps tl = taps_for_layer(taps, s, l * per_layer);
+        hipError_t e = launch_layer_prefill(s, layers[l], states[l], src, l == 0 && x_dtype == DFSSM_BF16, dst, batch,
+                                            seqlen, chunk, p, taps ? &tl : nullptr, st);
+        if (e != hipSuccess) return DFSSM_EHIP;
+    }
+    return hip_status(launch_final_norm(y, final_norm_w, y, nullptr, s.D, s.eps, (int)per_layer, st));
 }
 
 const char *dfssm_strerror(int status) {

@@ -310,6 +310,26 @@ hipError_t launch_layer_decode(const Shape &s, const dfssm_layer_weights &w, con
     return hipSuccess;
 }
 
+// Status and poison after a stack decode (one small launch; reads the flag the persistent
+// kernels set when a wait timed out).
+__global__ void k_stack_finish(const int *err, int32_t *status, float *y, int64_t n) {
+    const int bad = err ? __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        status[0] = bad ? DFSSM_STATUS_TIMEOUT : 0;
+        status[1] = bad;   // the kernel's own record of the wait that timed out (diagnostic only)
+    }
+    if (!bad) return;
+    const float nan = __builtin_nanf("");
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        y[i] = nan;
+}
+
+hipError_t launch_stack_finish(const int *err, int32_t *status, float *y, int64_t n, hipStream_t stream) {
+    const int64_t want = (n + kBlock - 1) / kBlock;
+    k_stack_finish<<<(unsigned)(want < 1024 ? (want > 0 ? want : 1) : 1024), kBlock, 0, stream>>>(err, status, y, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_final_norm(const float *h, const float *w, float *y, float *y2, int D, float eps, int batch,
                              hipStream_t stream) {
     k_final_norm<<<batch, kBlock, 0, stream>>>(h, w, y, y2, D, eps);

@@ -52,22 +52,16 @@ hipError_t launch_layer_decode(const Shape &s, const dfssm_layer_weights &w,
                                int batch, const DecodeWs &ws, const TapPtrs &taps,
                                hipStream_t stream);
 
-// Extra workspace of the persistent stack kernel (layer table, barrier counter, error flag,
-// raw B/C values) and its launcher; batch <= kGemvMaxBatch.
-size_t stack_extra_ws_bytes(const Shape &s, int batch, int n_layers);
-hipError_t launch_stack_persistent(const Shape &s, const dfssm_layer_weights *layers,
-                                   const dfssm_layer_state *states, int n_layers, const float *final_w,
-                                   const float *x0, float *y, int batch, int n_steps, const DecodeWs &ws,
-                                   void *extra, const dfssm_taps *taps, int max_wgs, hipStream_t stream);
-bool stack_persistent_ok(const Shape &s, int batch);
-
-// Two-exchange persistent stack decode (flow2.hip), used when the shape and batch fit it and
-// DFSSM_STACK_V1=1 is not set.
+// Two-exchange persistent stack decode (flow2.hip), used at batch 1 when the shape fits it.
 bool stack2_ok(const Shape &s, int batch);
 size_t stack2_extra_ws_bytes(const Shape &s, int batch, int n_layers);
 hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states, int n_layers,
                          const float *final_w, const float *x0, float *y, int batch, int n_steps, void *extra,
-                         const dfssm_taps *taps, hipStream_t stream);
+                         const dfssm_taps *taps, int **err_flag, hipStream_t stream);
+
+// After a stack decode: status[0] = *err (0 when err is null), and when *err is set every one of
+// the n floats of y becomes NaN, so that a timed-out exchange can never pass as a result.
+hipError_t launch_stack_finish(const int *err, int32_t *status, float *y, int64_t n, hipStream_t stream);
 
 // int8-code x (+-1 scaffold) GEMM with the projection epilogue (gemm.hip):
 //   y[m][n] = s[m]*row_scale[n]*acc[m][n] + up_scale[n] * sum_j t'[m][j]*lora_up[n][j] (+ res[m][n])

@@ -20,10 +20,9 @@
 // A workgroup works on one phase per layer, so right after publishing it loads what its next
 // layer needs that does not depend on the token (sign rows and LoRA-down factors straight into
 // LDS, scales, conv taps and windows, SSM state into registers): that latency hides behind the
-// other role's work. Every wait is bounded: on a timeout the kernel flags the workspace, stops
-// waiting and poisons y with NaN, so every wave still reaches the end.
-#include <stdlib.h>
-#include <string.h>
+// other role's work. Every wait is bounded: on a timeout the kernel sets the workspace's error
+// flag and every later wait gives up at once, so every wave still reaches the end; the launch that
+// follows the kernel (launch_stack_finish) reports the flag and fills y with NaN.
 
 #include <atomic>
 
@@ -104,12 +103,7 @@ __device__ __forceinline__ uint64_t tag2(uint32_t bits, uint32_t tag) { return (
 __device__ __forceinline__ uint32_t fbits2(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bitsf2(uint32_t b) { return __builtin_bit_cast(float, b); }
 
-__device__ void f2_error(const F2Args &a) {
-    __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float nan = __builtin_nanf("");
-    a.y[0] = nan;
-    a.y[(int64_t)(a.n_steps - 1) * a.batch * a.D] = nan;
-}
+__device__ void f2_error(const F2Args &a) { __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
 // This thread's 4*KCH consecutive words at p, reloaded until every epoch equals `tag` (bounded).
 template <int KCH>
@@ -985,11 +979,6 @@ hipError_t f2_launch(F2Args &a, const Shape &s, hipStream_t stream) {
     const size_t lds = f2_lds_base(s, NB) + f2_wreg_bytes(s, a.R1 + a.npad, a.R2);
     void *args[] = {&a};
     const void *fn = reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2>);
-    // DFSSM_STACK_LAUNCH=plain: the same grid through the ordinary launch API, for profilers that
-    // cannot trace cooperative launches (the grid never exceeds what is resident at once, and every
-    // wait is bounded)
-    const char *mode = getenv("DFSSM_STACK_LAUNCH");
-    if (mode && strcmp(mode, "plain") == 0) return hipLaunchKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
     return hipLaunchCooperativeKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
 }
 
@@ -1034,8 +1023,6 @@ hipError_t f2_launch_any(F2Args &a, const Shape &s, hipStream_t stream) {
 }  // namespace
 
 bool stack2_ok(const Shape &s, int batch) {
-    const char *v = getenv("DFSSM_STACK_V1");
-    if (v && strcmp(v, "1") == 0) return false;
     F2Plan p{};
     return f2_plan(s, batch, f2_slots(s, batch), p);
 }
@@ -1049,7 +1036,7 @@ size_t stack2_extra_ws_bytes(const Shape &s, int batch, int n_layers) {
 
 hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states, int n_layers,
                          const float *final_w, const float *x0, float *y, int batch, int n_steps, void *extra,
-                         const dfssm_taps *taps, hipStream_t stream) {
+                         const dfssm_taps *taps, int **err_flag, hipStream_t stream) {
     F2Plan p{};
     if (!f2_plan(s, batch, f2_slots(s, batch), p)) return hipErrorInvalidConfiguration;
     char *q = static_cast<char *>(extra);
@@ -1095,6 +1082,7 @@ hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, cons
     a.gx = words + L * batch * s.D;
     a.bcx = a.gx + L * batch * s.E;
     a.err = err;
+    *err_flag = err;
     if (taps) a.taps = *taps;
     hipError_t e;
     for (int l0 = 0; l0 < n_layers; l0 += kTable2) {

@@ -68,11 +68,18 @@ class DeviceState:
         self.ssm.copy_(torch.from_numpy(np.asarray(ssm, np.float32)))
 
     @classmethod
-    def from_tensors(cls, conv: torch.Tensor, ssm: torch.Tensor) -> "DeviceState":
+    def from_tensors(cls, conv: torch.Tensor, ssm: torch.Tensor, d, batch: int) -> "DeviceState":
         """A state over existing contiguous fp32 device tensors (e.g. views of one allocation that
-        holds a whole stack's states, so that they can be reset with one fill)."""
-        if not (conv.is_contiguous() and ssm.is_contiguous()) or conv.dtype != torch.float32 or ssm.dtype != torch.float32:
-            raise ValueError("DeviceState.from_tensors: contiguous fp32 tensors required")
+        holds a whole stack's states, so that they can be reset with one fill). The tensors must hold
+        exactly batch x conv_dim x (d_conv - 1) and batch x nheads x headdim x d_state values."""
+        for name, t, n in (("conv", conv, batch * d.conv_dim * (d.d_conv - 1)),
+                           ("ssm", ssm, batch * d.nheads * d.headdim * d.d_state)):
+            if not t.is_cuda:
+                raise ValueError(f"DeviceState.from_tensors: {name} is not a device tensor")
+            if not t.is_contiguous() or t.dtype != torch.float32:
+                raise ValueError(f"DeviceState.from_tensors: {name} must be contiguous fp32")
+            if t.numel() != n:
+                raise ValueError(f"DeviceState.from_tensors: {name} holds {t.numel()} values, expected {n}")
         st = cls.__new__(cls)
         st.conv, st.ssm = conv, ssm
         st.struct = L.dfssm_layer_state(conv.data_ptr(), ssm.data_ptr())
@@ -123,15 +130,38 @@ def layer_decode(d, layer: DeviceLayer, state: DeviceState, x_in: torch.Tensor, 
     L.check(st, "dfssm_layer_decode")
 
 
-def stack_decode(d, layers: list, states: list, final_w: torch.Tensor, x0: torch.Tensor, y: torch.Tensor,
-                 n_steps: int, ws: torch.Tensor, taps: Taps = None) -> None:
+def _arrays(layers: list, states: list):
     n = len(layers)
-    arr_w = (L.dfssm_layer_weights * n)(*[l.struct for l in layers])
-    arr_s = (L.dfssm_layer_state * n)(*[s.struct for s in states])
-    st = L.dfssm_stack_decode(dims_struct(d), arr_w, arr_s, n, final_w.data_ptr(), x0.data_ptr(), y.data_ptr(),
-                              x0.shape[0], n_steps, ws.data_ptr(), ws.numel(),
-                              None if taps is None else taps.struct, stream_handle())
-    L.check(st, "dfssm_stack_decode")
+    return (L.dfssm_layer_weights * n)(*[l.struct for l in layers]), (L.dfssm_layer_state * n)(*[s.struct for s in states])
+
+
+def stack_decode(d, layers: list, states: list, final_w: torch.Tensor, x0: torch.Tensor, y: torch.Tensor,
+                 n_steps: int, ws: torch.Tensor, taps: Taps = None, path: int = L.DFSSM_PATH_AUTO) -> None:
+    """dfssm_stack_decode_ex; the call's status word stays in ws (stack_status reads it)."""
+    arr_w, arr_s = _arrays(layers, states)
+    opts = L.dfssm_stack_opts(path, 0)
+    st = L.dfssm_stack_decode_ex(dims_struct(d), arr_w, arr_s, len(layers), final_w.data_ptr(), x0.data_ptr(),
+                                 y.data_ptr(), x0.shape[0], n_steps, ws.data_ptr(), ws.numel(),
+                                 None if taps is None else taps.struct, opts, stream_handle())
+    L.check(st, "dfssm_stack_decode_ex")
+
+
+def stack_status(ws: torch.Tensor) -> int:
+    """The status word a stack decode left in its workspace (synchronises with the device)."""
+    o = L.DFSSM_STACK_STATUS_OFFSET
+    return int(ws[o:o + 4].view(torch.int32).item())
+
+
+def stack_prefill(d, layers: list, states: list, final_w: torch.Tensor, x_in: torch.Tensor, y: torch.Tensor,
+                  chunk: int, ws: torch.Tensor, taps: Taps = None) -> None:
+    """x_in [batch][seqlen][d_model] fp32 or bf16 -> y = RMSNorm(stack(x_in)) * final_w, fp32."""
+    arr_w, arr_s = _arrays(layers, states)
+    batch, seqlen = x_in.shape[0], x_in.shape[1]
+    dtype = L.DFSSM_BF16 if x_in.dtype == torch.bfloat16 else L.DFSSM_F32
+    st = L.dfssm_stack_prefill(dims_struct(d), arr_w, arr_s, len(layers), final_w.data_ptr(), x_in.data_ptr(),
+                               dtype, y.data_ptr(), batch, seqlen, chunk, ws.data_ptr(), ws.numel(),
+                               None if taps is None else taps.struct, stream_handle())
+    L.check(st, "dfssm_stack_prefill")
 
 
 def layer_prefill(d, layer: DeviceLayer, state: DeviceState, x_in: torch.Tensor, x_out: torch.Tensor, chunk: int,

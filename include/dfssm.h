@@ -57,6 +57,20 @@ extern "C" {
 #define DFSSM_OP_LAYER_DECODE  0
 #define DFSSM_OP_LAYER_PREFILL 1
 #define DFSSM_OP_STACK_DECODE  2
+#define DFSSM_OP_STACK_PREFILL 3
+
+/* Status word of a stack decode: the int32 at byte offset DFSSM_STACK_STATUS_OFFSET of the
+ * workspace holds, once the call's work has completed on the stream, DFSSM_STATUS_OK or
+ * DFSSM_STATUS_TIMEOUT (a wait between the workgroups of a persistent launch ran past its bound,
+ * e.g. because the device could not keep the whole grid running; every value of y is then NaN). */
+#define DFSSM_STACK_STATUS_OFFSET 0   /* the int32 after it is an internal diagnostic code */
+#define DFSSM_STATUS_OK      0
+#define DFSSM_STATUS_TIMEOUT 1
+
+/* dfssm_stack_opts.path */
+#define DFSSM_PATH_AUTO      0   /* the fastest path that supports the shape and batch            */
+#define DFSSM_PATH_FLOW      1   /* batch 1: one persistent launch, two exchanges per layer        */
+#define DFSSM_PATH_PER_LAYER 2   /* a launch sequence per layer and token (any batch)              */
 
 /* token input dtypes of dfssm_layer_prefill */
 #define DFSSM_F32  0
@@ -135,9 +149,10 @@ typedef struct dfssm_taps {
 
 /*
  * Bytes of device workspace `op` needs for this shape, batch, sequence length and layer count
- * (seqlen is ignored by the decode ops, n_layers by the single-layer ops; for the prefill op the
+ * (seqlen is ignored by the decode ops, n_layers by the single-layer ops; for the prefill ops the
  * size covers every supported chunk length). Returns 0 for an invalid or unsupported shape.
- * The workspace needs no initialisation and holds nothing between calls.
+ * The workspace needs no initialisation and carries nothing from one call to the next (a stack
+ * decode leaves its status word, DFSSM_STACK_STATUS_OFFSET, for the caller to read).
  */
 size_t dfssm_workspace_bytes(const dfssm_dims *dims, int32_t op, int32_t batch, int32_t seqlen,
                              int32_t n_layers);
@@ -174,6 +189,17 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w,
                         void *ws, size_t ws_bytes, const dfssm_taps *taps, void *stream);
 
 /*
+ * Kernel selection for dfssm_stack_decode_ex (every path computes the same decode; zero-initialise
+ * the struct for the defaults).
+ *   path      DFSSM_PATH_*; a path that cannot run the shape and batch is DFSSM_EUNSUPPORTED.
+ *   reserved  must be 0.
+ */
+typedef struct dfssm_stack_opts {
+    int32_t path;
+    int32_t reserved;
+} dfssm_stack_opts;
+
+/*
  * Autoregressive-style decode through a stack of n_layers layers for n_steps tokens:
  *   x(0) = x0;  for t: h = x(t); h = layer_l(h) for l = 0..n_layers-1;
  *   y[t] = RMSNorm(h) * final_norm_w;  x(t+1) = y[t].
@@ -181,7 +207,8 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w,
  * pass in a graph to remove per-kernel launch cost; here the layers hand their partial results to
  * each other through tagged words in the workspace instead of kernel boundaries). When the device
  * cannot keep the needed workgroups resident at once, the call falls back to per-layer kernels
- * with the same results.
+ * with the same results. The call's status word (DFSSM_STACK_STATUS_OFFSET) is written in the
+ * workspace once its work completes.
  *   layers, states: HOST arrays [n_layers] of the structs above; final_norm_w [d_model] fp32;
  *   x0 [batch][d_model] fp32; y [n_steps][batch][d_model] fp32 (must not alias x0);
  *   taps: NULL or records laid out [n_steps][n_layers][batch][...].
@@ -192,6 +219,30 @@ int dfssm_stack_decode(const dfssm_dims *dims, const dfssm_layer_weights *layers
                        const float *final_norm_w, const float *x0, float *y,
                        int32_t batch, int32_t n_steps, void *ws, size_t ws_bytes,
                        const dfssm_taps *taps, void *stream);
+
+/* dfssm_stack_decode with an explicit kernel path (opts: HOST pointer, NULL = defaults). */
+int dfssm_stack_decode_ex(const dfssm_dims *dims, const dfssm_layer_weights *layers,
+                          const dfssm_layer_state *states, int32_t n_layers,
+                          const float *final_norm_w, const float *x0, float *y,
+                          int32_t batch, int32_t n_steps, void *ws, size_t ws_bytes,
+                          const dfssm_taps *taps, const dfssm_stack_opts *opts, void *stream);
+
+/*
+ * Prefill of `seqlen` tokens per sequence through a stack of n_layers layers (the pages' §4.1
+ * forward over a prompt, batch rows independent), leaving every layer's final conv/SSM state in
+ * `states` for the decode that continues from it:
+ *   h = x_in;  h = layer_l(h) for l = 0..n_layers-1 (each as dfssm_layer_prefill);
+ *   y[b][t] = RMSNorm(h[b][t]) * final_norm_w
+ * so y[b][seqlen-1] is the x0 of a dfssm_stack_decode that continues the sequences.
+ *   layers, states: HOST arrays [n_layers]; x_in [batch][seqlen][d_model] fp32 or bf16 bit patterns;
+ *   y [batch][seqlen][d_model] fp32 (must not alias x_in); taps: NULL or records laid out
+ *   [n_layers][batch][seqlen][...]. Limits as for dfssm_layer_prefill; 1 <= n_layers <= 1024.
+ */
+int dfssm_stack_prefill(const dfssm_dims *dims, const dfssm_layer_weights *layers,
+                        const dfssm_layer_state *states, int32_t n_layers,
+                        const float *final_norm_w, const void *x_in, int32_t x_dtype, float *y,
+                        int32_t batch, int32_t seqlen, int32_t chunk, void *ws, size_t ws_bytes,
+                        const dfssm_taps *taps, void *stream);
 
 /* Static, human-readable text of a status code. */
 const char *dfssm_strerror(int status);

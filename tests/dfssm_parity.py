@@ -10,7 +10,20 @@ Protocol
       two sides cannot masquerade as an arithmetic error), layer outputs and conv/SSM states must
       agree to 1e-3 normwise relative error per token; free-running runs are compared too, and
       any code flip between them must sit at a rounding tie.
-  P3  48-layer stack: 1e-2 normwise on every output token.
+  P3  48-layer stack: 1e-2 on every output token.
+
+Every float comparison takes the larger of two errors: the normwise relative error of the whole
+vector, and the worst element's error relative to its own magnitude plus the vector's RMS,
+max_i |a_i - b_i| / (|b_i| + rms(b)). The second bound catches a few wrong elements (a stale
+state row, an off-by-one at a ragged tail) that a normwise figure over thousands of values would
+average away.
+
+Code flips and the tie window: two correct fp32 evaluations of u differ by a few ulps, so the
+codes u * 127 / max|u| they give can differ only where that product sits within a few ulps of a
+.5 boundary (~1e-5 at 127). The window `tie_tol` = 2e-3 is wider because the prefill SSD passes
+form products from a three-term bf16 split of their fp32 operands (about 2^-16 relative per
+product): their outputs, and hence the next quantizer inputs, can differ from the sequential fp32
+evaluation by ~1e-5 relative, which moves u * 127 / max|u| (at most 127) by up to ~1e-3.
 """
 from __future__ import annotations
 
@@ -27,6 +40,22 @@ def normwise(a, b) -> float:
     b = np.asarray(b, np.float64)
     den = np.linalg.norm(b)
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def elementwise(a, b) -> float:
+    """max_i |a_i - b_i| / (|b_i| + rms(b))."""
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    if b.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(b * b)))
+    den = np.abs(b) + (rms if rms > 0 else 1.0)
+    return float(np.max(np.abs(a - b) / den))
+
+
+def err(a, b) -> float:
+    """The error every float comparison is held to: the larger of normwise and elementwise."""
+    return max(normwise(a, b), elementwise(a, b))
 
 
 def assert_codes_exact(u, q, s, what=""):
@@ -59,8 +88,8 @@ def check_layer_step(W, h_in, conv_prev, ssm_prev, tap, out_gpu, conv_gpu, ssm_g
                           None if dense is None else dense["out"], what + " out")
     force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
     h_o, cs_o, ss_o, tp_o = O.layer_decode(h_in, W, conv_prev, ssm_prev, force=force, dense=dense)
-    errs = dict(in_u=normwise(tap["in_u"], tp_o.in_u), out_u=normwise(tap["out_u"], tp_o.out_u),
-                out=normwise(out_gpu, h_o), conv=normwise(conv_gpu, cs_o), ssm=normwise(ssm_gpu, ss_o))
+    errs = dict(in_u=err(tap["in_u"], tp_o.in_u), out_u=err(tap["out_u"], tp_o.out_u),
+                out=err(out_gpu, h_o), conv=err(conv_gpu, cs_o), ssm=err(ssm_gpu, ss_o))
     assert errs["in_u"] < 1e-5, f"{what}: {errs}"
     for k in ("out_u", "out", "conv", "ssm"):
         assert errs[k] < tol, f"{what}: {k} {errs}"

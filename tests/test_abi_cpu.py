@@ -182,3 +182,54 @@ def test_batched_decode_workspace_covers_the_mfma_path():
     # beyond 4 tokens the projections run as GEMMs over per-token codes held in the workspace
     assert w5 > w4 * 5 // 4 + 5 * d.d_model
     assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_DECODE, 64, 0, 48) > 0
+
+
+def test_stack_decode_ex_rejects_bad_options():
+    d = _dims()
+    n = 2
+    ws_need = L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_DECODE, 1, 0, n)
+    arr_w = (L.dfssm_layer_weights * n)(*[_fake_weights() for _ in range(n)])
+    arr_s = (L.dfssm_layer_state * n)(*[L.dfssm_layer_state(FAKE, FAKE) for _ in range(n)])
+
+    def call(**kw):
+        return L.dfssm_stack_decode_ex(d, arr_w, arr_s, n, FAKE, FAKE, FAKE, 1, 4, FAKE, ws_need,
+                                       None, L.dfssm_stack_opts(**kw))
+
+    assert call(path=7) == L.DFSSM_EINVAL
+    assert call(path=-1) == L.DFSSM_EINVAL
+    assert call(reserved=1) == L.DFSSM_EINVAL
+    # batch 5 has no persistent kernel: asking for one is unsupported, not silently rerouted
+    ws5 = L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_DECODE, 5, 0, n)
+    st = L.dfssm_stack_decode_ex(d, arr_w, arr_s, n, FAKE, FAKE, FAKE, 5, 4, FAKE, ws5, None,
+                                 L.dfssm_stack_opts(path=L.DFSSM_PATH_FLOW))
+    assert st == L.DFSSM_EUNSUPPORTED
+
+
+def test_stack_prefill_workspace_and_rejects_bad_arguments():
+    d = _dims()
+    n = 3
+    one = L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_PREFILL, 2, 100)
+    need = L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_PREFILL, 2, 100, n)
+    # one layer's prefill workspace plus one residual buffer of batch x seqlen x d_model floats
+    assert need >= one + 2 * 100 * d.d_model * 4
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_PREFILL, 2, 100, 0) == 0
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_PREFILL, 65, 100, n) == 0
+    arr_w = (L.dfssm_layer_weights * n)(*[_fake_weights() for _ in range(n)])
+    arr_s = (L.dfssm_layer_state * n)(*[L.dfssm_layer_state(FAKE, FAKE) for _ in range(n)])
+    Y = FAKE + 0x100000
+    ok = dict(nl=n, x=FAKE, dt=L.DFSSM_F32, y=Y, batch=2, seqlen=100, chunk=64, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.dfssm_stack_prefill(d, arr_w, arr_s, a["nl"], FAKE, a["x"], a["dt"], a["y"], a["batch"],
+                                     a["seqlen"], a["chunk"], a["ws"], a["wsb"])
+
+    assert call(nl=0) == L.DFSSM_EINVAL
+    assert call(y=FAKE) == L.DFSSM_EINVAL            # aliases x_in
+    assert call(dt=3) == L.DFSSM_EINVAL
+    assert call(chunk=100) == L.DFSSM_EUNSUPPORTED
+    assert call(batch=65) == L.DFSSM_EUNSUPPORTED
+    assert call(wsb=2 * 100 * d.d_model * 4) == L.DFSSM_EWORKSPACE     # the residual buffer alone
+    arr_s[1].conv = None
+    assert call() == L.DFSSM_EINVAL

@@ -94,10 +94,10 @@ def test_layer_decode_mfma_and_gemv_paths_agree():
             for half in (0, 4):
                 f, ok = PY.flips_at_ties(t4[t]["in_u"][b], t4[t]["in_q"][b], t8[t]["in_q"][b + half])
                 assert ok, (t, b)
-                assert PY.normwise(o8[t][b + half], o4[t][b]) < PY.TOL_LAYER
+                assert PY.err(o8[t][b + half], o4[t][b]) < PY.TOL_LAYER
             # rows that saw the same inputs in the same launch are bit-identical
             assert (o8[t][b] == o8[t][b + 4]).all()
-    assert PY.normwise(f8[1][:4], f4[1]) < PY.TOL_LAYER
+    assert PY.err(f8[1][:4], f4[1]) < PY.TOL_LAYER
 
 
 def test_layer_decode_1p3b_batch64():
@@ -140,12 +140,12 @@ def test_stack_decode_tiny_batch64_forced():
                 h, cs[l], ss[l], _ = O.layer_decode(tap["h_in"], layers[l], cs[l], ss[l], force=force,
                                                     dense=dense[l])
                 if l + 1 < nL:
-                    assert PY.normwise(PY.tap_record(taps, (t * nL + l + 1) * B + b)["h_in"], h) < PY.TOL_LAYER
+                    assert PY.err(PY.tap_record(taps, (t * nL + l + 1) * B + b)["h_in"], h) < PY.TOL_LAYER
                 else:
-                    assert PY.normwise(y[t][b], O.rmsnorm(h, fw, TINY.eps)) < PY.TOL_LAYER
+                    assert PY.err(y[t][b], O.rmsnorm(h, fw, TINY.eps)) < PY.TOL_LAYER
         for l in range(nL):
-            assert PY.normwise(states[l][0][b], cs[l]) < PY.TOL_LAYER
-            assert PY.normwise(states[l][1][b], ss[l]) < PY.TOL_LAYER
+            assert PY.err(states[l][0][b], cs[l]) < PY.TOL_LAYER
+            assert PY.err(states[l][1][b], ss[l]) < PY.TOL_LAYER
 
 
 def test_stack_decode_1p3b_48_layers_batch64_sampled():
@@ -176,11 +176,11 @@ def test_stack_decode_1p3b_48_layers_batch64_sampled():
             PY.assert_products_exact(lw.in_proj, tap["in_q"], tap["in_acc"], tap["in_t"], dense["in"])
             PY.assert_products_exact(lw.out_proj, tap["out_q"], tap["out_acc"], tap["out_t"], dense["out"])
             h, cs, ss, _ = O.layer_decode(tap["h_in"], lw, st_a[l][0][b], st_a[l][1][b], force=force, dense=dense)
-            errs = dict(conv=PY.normwise(st_b[l][0][b], cs), ssm=PY.normwise(st_b[l][1][b], ss))
+            errs = dict(conv=PY.err(st_b[l][0][b], cs), ssm=PY.err(st_b[l][1][b], ss))
             if out_gpu is not None:
-                errs["out"] = PY.normwise(out_gpu, h)
+                errs["out"] = PY.err(out_gpu, h)
             else:
-                errs["out"] = PY.normwise(y_b[0][b], O.rmsnorm(h, np.ones(BIG.d_model), BIG.eps))
+                errs["out"] = PY.err(y_b[0][b], O.rmsnorm(h, np.ones(BIG.d_model), BIG.eps))
             for k, v in errs.items():
                 assert v < PY.TOL_LAYER, (l, b, errs)
                 worst[k] = max(worst.get(k, 0.0), v)

@@ -62,11 +62,11 @@ def forced_chain(lw, xs, conv0, ssm0, outs, tps, final, b=0, dense=None):
                                  None if dense is None else dense["out"], f"t={t} out")
         force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
         h, cs, ss, tpo = O.layer_decode(xs[t][b], lw, cs, ss, force=force, dense=dense)
-        e = PY.normwise(outs[t][b], h)
+        e = PY.err(outs[t][b], h)
         assert e < PY.TOL_LAYER, f"step {t} row {b}: output err {e}"
-        assert PY.normwise(tap["in_u"], tpo.in_u) < 1e-5
+        assert PY.err(tap["in_u"], tpo.in_u) < 1e-5
         worst = max(worst, e)
-    ec, es = PY.normwise(final[0][b], cs), PY.normwise(final[1][b], ss)
+    ec, es = PY.err(final[0][b], cs), PY.err(final[1][b], ss)
     assert ec < PY.TOL_LAYER and es < PY.TOL_LAYER, (ec, es)
     return worst, ec, es
 
@@ -83,7 +83,7 @@ def free_running(lw, xs, conv0, ssm0, outs, tps, b=0, n=None):
             assert (ok1 if f1 else ok2), f"step {t}: a code flip away from a rounding tie"
             flips = f1 + f2
             break
-        errs.append(PY.normwise(outs[t][b], o_out[t]))
+        errs.append(PY.err(outs[t][b], o_out[t]))
     if errs:
         assert max(errs) < PY.TOL_LAYER, errs
     return (max(errs) if errs else 0.0), flips
@@ -177,7 +177,7 @@ def test_layer_decode_degenerate_cases():
     forced_chain(lw, xs, conv0, ssm0, outs, tps, final)
 
 
-def run_stack(dims, layers, x0, states0, n_steps, taps=False, final_w=None):
+def run_stack(dims, layers, x0, states0, n_steps, taps=False, final_w=None, path=0):
     L, Dv = _lib()
     B = x0.shape[0]
     devs = [Dv.DeviceLayer(lw) for lw in layers]
@@ -187,15 +187,16 @@ def run_stack(dims, layers, x0, states0, n_steps, taps=False, final_w=None):
     y = torch.empty((n_steps, B, dims.d_model), dtype=torch.float32, device="cuda")
     ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, B, 0, len(layers))
     tp = Dv.Taps(dims, n_steps * len(layers) * B) if taps else None
-    Dv.stack_decode(dims, devs, sts, fw, xt, y, n_steps, ws, tp)
+    Dv.stack_decode(dims, devs, sts, fw, xt, y, n_steps, ws, tp, path=path)
     torch.cuda.synchronize()
+    assert Dv.stack_status(ws) == L.DFSSM_STATUS_OK, "a persistent-kernel wait timed out"
     return (y.cpu().numpy(), [(s.conv.cpu().numpy(), s.ssm.cpu().numpy()) for s in sts],
             None if tp is None else tp.numpy())
 
 
 @pytest.mark.parametrize("B", [1, 2])
 def test_stack_decode_tiny_forced_and_free_running(B):
-    """Batch 1 runs the two-exchange persistent kernel, batch 2 the per-item dataflow kernel."""
+    """Batch 1 runs the two-exchange persistent kernel, batch 2 per-layer launches."""
     nL, T = 3, 12
     layers = gen.stack_weights(TINY, nL, seed=1, random_norms=True)
     states0 = [gen.initial_states(TINY, B, l, 1, std=0.1) for l in range(nL)]
@@ -225,17 +226,17 @@ def test_stack_decode_tiny_forced_and_free_running(B):
                 h, cs[l], ss[l], _ = O.layer_decode(h_in, layers[l], cs[l], ss[l], force=force, dense=dense[l])
                 if l + 1 < nL:
                     nxt = PY.tap_record(taps, (t * nL + l + 1) * B + b)["h_in"]
-                    assert PY.normwise(nxt, h) < PY.TOL_LAYER
+                    assert PY.err(nxt, h) < PY.TOL_LAYER
                 else:
-                    assert PY.normwise(y[t][b], O.rmsnorm(h, fw, TINY.eps)) < PY.TOL_LAYER
+                    assert PY.err(y[t][b], O.rmsnorm(h, fw, TINY.eps)) < PY.TOL_LAYER
         for l in range(nL):
-            assert PY.normwise(states[l][0][b], cs[l]) < PY.TOL_LAYER
-            assert PY.normwise(states[l][1][b], ss[l]) < PY.TOL_LAYER
+            assert PY.err(states[l][0][b], cs[l]) < PY.TOL_LAYER
+            assert PY.err(states[l][1][b], ss[l]) < PY.TOL_LAYER
     # free-running P3
     for b in range(B):
         yo, _, _ = O.stack_decode(x0[b], layers, [s[0][b] for s in states0], [s[1][b] for s in states0],
                                   T, fw, TINY.eps)
-        errs = [PY.normwise(y[t][b], yo[t]) for t in range(T)]
+        errs = [PY.err(y[t][b], yo[t]) for t in range(T)]
         say(f"tiny stack free-running row {b}: max err {max(errs):.2e}")
         assert max(errs) < PY.TOL_STACK
 
@@ -274,12 +275,12 @@ def test_stack_decode_1p3b_48_layers_512_steps_sampled():
         PY.assert_products_exact(lw.in_proj, tap["in_q"], tap["in_acc"], tap["in_t"], dense["in"], f"layer {l}")
         PY.assert_products_exact(lw.out_proj, tap["out_q"], tap["out_acc"], tap["out_t"], dense["out"], f"layer {l}")
         h, cs, ss, _ = O.layer_decode(tap["h_in"], lw, st_a[l][0][0], st_a[l][1][0], force=force, dense=dense)
-        errs_tap["conv"] = PY.normwise(st_b[l][0][0], cs)
-        errs_tap["ssm"] = PY.normwise(st_b[l][1][0], ss)
+        errs_tap["conv"] = PY.err(st_b[l][0][0], cs)
+        errs_tap["ssm"] = PY.err(st_b[l][1][0], ss)
         if out_gpu is not None:
-            errs_tap["out"] = PY.normwise(out_gpu, h)
+            errs_tap["out"] = PY.err(out_gpu, h)
         else:
-            errs_tap["out"] = PY.normwise(y_b[0][0], O.rmsnorm(h, np.ones(BIG.d_model), BIG.eps))
+            errs_tap["out"] = PY.err(y_b[0][0], O.rmsnorm(h, np.ones(BIG.d_model), BIG.eps))
         for k, v in errs_tap.items():
             assert v < PY.TOL_LAYER, (l, errs_tap)
             worst[k] = max(worst.get(k, 0.0), v)
@@ -304,9 +305,34 @@ def test_stack_decode_1p3b_48_layers_512_steps_sampled():
             force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
             h, cs[l], ss[l], _ = O.layer_decode(h, layers[l], cs[l], ss[l], force=force, dense=dense_all[l])
         yo = O.rmsnorm(h, np.ones(BIG.d_model), BIG.eps)
-        errs.append(PY.normwise(y4[t][0], yo))
+        errs.append(PY.err(y4[t][0], yo))
         x = yo
     say(f"1p3b stack code-forced {T2} steps: {errs}")
+    assert max(errs) < PY.TOL_STACK
+    # the same P3 window in the middle of the run: 4 tapped steps continuing from the GPU's own
+    # states after step 255 (they must reproduce steps 256-259 of the full run bit for bit)
+    M = 256
+    say(f"case: same stack, {M} steps then {T2} tapped steps")
+    y_m, st_m, _ = run_stack(BIG, layers, x0, states0, M)
+    assert (y_m == y_full[:M]).all()
+    y_w, _, taps_w = run_stack(BIG, layers, y_m[-1], st_m, T2, taps=True)
+    assert (y_w == y_full[M:M + T2]).all()
+    cs = [s[0][0].astype(np.float64) for s in st_m]
+    ss = [s[1][0].astype(np.float64) for s in st_m]
+    x = y_m[-1][0].astype(np.float64)
+    errs = []
+    for t in range(T2):
+        h = x
+        for l in range(nL):
+            tap = PY.tap_record(taps_w, t * nL + l)
+            PY.assert_codes_exact(tap["in_u"], tap["in_q"], tap["in_s"][0], f"mid t{t} l{l} in")
+            PY.assert_codes_exact(tap["out_u"], tap["out_q"], tap["out_s"][0], f"mid t{t} l{l} out")
+            force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
+            h, cs[l], ss[l], _ = O.layer_decode(h, layers[l], cs[l], ss[l], force=force, dense=dense_all[l])
+        yo = O.rmsnorm(h, np.ones(BIG.d_model), BIG.eps)
+        errs.append(PY.err(y_w[t][0], yo))
+        x = yo
+    say(f"1p3b stack code-forced steps {M}-{M + T2 - 1}: {errs}")
     assert max(errs) < PY.TOL_STACK
     # free-running first step, layer by layer, up to the first code flip (which must sit at a tie)
     h = x0[0].astype(np.float64)
@@ -323,50 +349,25 @@ def test_stack_decode_1p3b_48_layers_512_steps_sampled():
             break
         nxt = PY.tap_record(taps4, l + 1)["h_in"] if l + 1 < nL else None
         if nxt is not None:
-            assert PY.normwise(nxt, ho) < PY.TOL_LAYER
+            assert PY.err(nxt, ho) < PY.TOL_LAYER
         h = ho
 
 
-def test_stack_decode_grid_size_invariance():
-    """The persistent kernel gives bit-identical results whatever the resident grid size, so every
-    work item is computed exactly once and the barriers order the phases."""
-    import os
-    nL, T, B = 3, 5, 2
-    layers = gen.stack_weights(TINY, nL, seed=4, random_norms=True, per_channel_lora=True)
-    states0 = [gen.initial_states(TINY, B, l, 4, std=0.2) for l in range(nL)]
-    x0 = gen.token_inputs(TINY, (B,), 4, tag=2)
-    say("case: tiny stack decode, default grid")
-    y_ref, st_ref, _ = run_stack(TINY, layers, x0, states0, T)
-    try:
-        for g in (1, 7, 64):
-            os.environ["DFSSM_STACK_MAX_WGS"] = str(g)
-            say(f"case: tiny stack decode, grid capped at {g} workgroups")
-            y, st, _ = run_stack(TINY, layers, x0, states0, T)
-            assert (y == y_ref).all(), g
-            for l in range(nL):
-                assert (st[l][0] == st_ref[l][0]).all() and (st[l][1] == st_ref[l][1]).all(), (g, l)
-    finally:
-        os.environ.pop("DFSSM_STACK_MAX_WGS", None)
-
-
 @pytest.mark.parametrize("dims_name", ["tiny", "1p3b"])
-def test_stack_decode_batch1_kernels_agree(dims_name):
-    """The two persistent kernels (two-exchange, the default at batch 1, and the per-item dataflow
-    one, DFSSM_STACK_V1=1) compute the same decode: identical codes except at rounding ties."""
-    import os
+def test_stack_decode_batch1_paths_agree(dims_name):
+    """The two batch-1 paths (the two-exchange persistent kernel, the default, and per-layer
+    launches) compute the same decode: identical codes except at rounding ties."""
+    L, _ = _lib()
+    other, path = "per-layer", L.DFSSM_PATH_PER_LAYER
     dims = gen.DIMS[dims_name]
     nL, T = (3, 8) if dims_name == "tiny" else (4, 4)
     layers = gen.stack_weights(dims, nL, seed=3, random_norms=True, per_channel_lora=True)
     states0 = [gen.initial_states(dims, 1, l, 3, std=0.1) for l in range(nL)]
     x0 = gen.token_inputs(dims, (1,), 3, tag=4)
     say(f"case: {dims_name} stack, {nL} layers, {T} steps, batch 1, two-exchange kernel")
-    y2, st2, tp2 = run_stack(dims, layers, x0, states0, T, taps=True)
-    try:
-        os.environ["DFSSM_STACK_V1"] = "1"
-        say(f"case: same stack, per-item dataflow kernel")
-        y1, st1, tp1 = run_stack(dims, layers, x0, states0, T, taps=True)
-    finally:
-        os.environ.pop("DFSSM_STACK_V1", None)
+    y2, st2, tp2 = run_stack(dims, layers, x0, states0, T, taps=True, path=L.DFSSM_PATH_FLOW)
+    say(f"case: same stack, {other} path")
+    y1, st1, tp1 = run_stack(dims, layers, x0, states0, T, taps=True, path=path)
     assert np.isfinite(y2).all()
     flips = 0
     for r in range(T * nL):
@@ -378,10 +379,10 @@ def test_stack_decode_batch1_kernels_agree(dims_name):
             break
         PY.assert_codes_exact(tp2["in_u"][r], tp2["in_q"][r], tp2["in_s"][r][0], f"record {r} in")
         PY.assert_codes_exact(tp2["out_u"][r], tp2["out_q"][r], tp2["out_s"][r][0], f"record {r} out")
-    errs = [PY.normwise(y2[t][0], y1[t][0]) for t in range(T)]
+    errs = [PY.err(y2[t][0], y1[t][0]) for t in range(T)]
     say(f"{dims_name}: max normwise difference {max(errs):.2e}, code flips {flips}")
     if flips == 0:
         assert max(errs) < PY.TOL_LAYER
         for l in range(nL):
-            assert PY.normwise(st2[l][0], st1[l][0]) < PY.TOL_LAYER
-            assert PY.normwise(st2[l][1], st1[l][1]) < PY.TOL_LAYER
+            assert PY.err(st2[l][0], st1[l][0]) < PY.TOL_LAYER
+            assert PY.err(st2[l][1], st1[l][1]) < PY.TOL_LAYER

@@ -41,8 +41,9 @@ def run_prefill(dims, lw, xs, conv0, ssm0, chunk, bf16=False, taps=True):
     return y.cpu().numpy(), tps, (st.conv.cpu().numpy(), st.ssm.cpu().numpy())
 
 
-def check_sequence(lw, xs, conv0, ssm0, out, tps, final, dense=None, tol=PY.TOL_LAYER, what=""):
-    """P1 + P2 over one sequence (batch row): xs [T][D], tps dict of [T][...]."""
+def check_sequence(lw, xs, conv0, ssm0, out, tps, final, dense=None, tol=PY.TOL_LAYER, what="", final_w=None):
+    """P1 + P2 over one sequence (batch row): xs [T][D], tps dict of [T][...]. With final_w, `out`
+    is the stack's output RMSNorm(h) * final_w of this (last) layer's residual h."""
     T = xs.shape[0]
     assert (tps["h_in"] == xs).all(), f"{what}: h_in tap is not the layer input"
     for t in range(T):
@@ -55,10 +56,12 @@ def check_sequence(lw, xs, conv0, ssm0, out, tps, final, dense=None, tol=PY.TOL_
     assert (tps["in_t"].astype(np.int64) == otp["in_t"]).all(), f"{what}: in t"
     assert (tps["out_acc"].astype(np.int64) == otp["out_acc"]).all(), f"{what}: out acc"
     assert (tps["out_t"].astype(np.int64) == otp["out_t"]).all(), f"{what}: out t"
-    e_in = max(PY.normwise(tps["in_u"][t], otp["in_u"][t]) for t in range(T))
-    e_ou = max(PY.normwise(tps["out_u"][t], otp["out_u"][t]) for t in range(T))
-    e_o = max(PY.normwise(out[t], o[t]) for t in range(T))
-    e_c, e_s = PY.normwise(final[0], cs), PY.normwise(final[1], ss)
+    e_in = max(PY.err(tps["in_u"][t], otp["in_u"][t]) for t in range(T))
+    e_ou = max(PY.err(tps["out_u"][t], otp["out_u"][t]) for t in range(T))
+    if final_w is not None:
+        o = O.rmsnorm(o, final_w, lw.dims.eps)
+    e_o = max(PY.err(out[t], o[t]) for t in range(T))
+    e_c, e_s = PY.err(final[0], cs), PY.err(final[1], ss)
     errs = dict(in_u=e_in, out_u=e_ou, out=e_o, conv=e_c, ssm=e_s)
     assert e_in < 1e-5, f"{what}: {errs}"
     for k in ("out_u", "out", "conv", "ssm"):
@@ -83,7 +86,7 @@ def free_running_sequence(lw, xs, conv0, ssm0, out, tps, dense=None, what=""):
         if f:
             assert ok, f"{what} t={t}: an out-code flip away from a rounding tie"
             continue
-        errs.append(PY.normwise(out[t], o[t]))
+        errs.append(PY.err(out[t], o[t]))
     if errs:
         assert max(errs) < PY.TOL_LAYER, f"{what}: {max(errs)}"
     return (max(errs) if errs else 0.0), first
@@ -199,8 +202,127 @@ def test_prefill_chunk_lengths_agree():
                     assert ok, f"chunk {c}: {kq} flip away from a rounding tie at token {t}"
                     first = min(first, t)
                     break
-        e = max((PY.normwise(out[0, t], ref_out[0, t]) for t in range(first)), default=0.0)
+        e = max((PY.err(out[0, t], ref_out[0, t]) for t in range(first)), default=0.0)
         say(f"chunk {c}: max normwise difference {e:.2e} over {first} tokens (first code flip: {first < T})")
         assert e < PY.TOL_LAYER, (c, e)
         if first == T:
-            assert PY.normwise(st[1], ref_st[1]) < PY.TOL_LAYER
+            assert PY.err(st[1], ref_st[1]) < PY.TOL_LAYER
+
+
+def run_stack_prefill(dims, layers, xs, states0, chunk, final_w, bf16=False, taps=True):
+    """dfssm_stack_prefill over xs [B][T][D]; returns (y, taps numpy per layer [L][B][T][...] as a
+    function of the layer, final states, the device taps object)."""
+    L, Dv = _lib()
+    B, T = xs.shape[:2]
+    nL = len(layers)
+    devs = [Dv.DeviceLayer(lw) for lw in layers]
+    sts = [Dv.DeviceState(c, s_) for c, s_ in states0]
+    x = torch.from_numpy(np.ascontiguousarray(xs)).cuda()
+    if bf16:
+        x = x.to(torch.bfloat16)
+    fw = torch.from_numpy(final_w).cuda()
+    y = torch.empty((B, T, dims.d_model), dtype=torch.float32, device="cuda")
+    ws = Dv.workspace(dims, L.DFSSM_OP_STACK_PREFILL, B, T, nL)
+    tp = Dv.Taps(dims, nL * B * T) if taps else None
+    Dv.stack_prefill(dims, devs, sts, fw, x, y, chunk, ws, tp)
+    torch.cuda.synchronize()
+
+    def layer_taps(l):
+        return {k: v[l * B * T:(l + 1) * B * T].cpu().numpy().reshape(B, T, -1) for k, v in tp.t.items()}
+
+    return (y.cpu().numpy(), layer_taps if taps else None,
+            [(s_.conv.cpu().numpy(), s_.ssm.cpu().numpy()) for s_ in sts], devs, sts)
+
+
+def test_stack_prefill_tiny_per_layer_and_composition():
+    """A 3-layer stack prefill (batch 2, 300 tokens, chunk 64, nonzero states, random final norm
+    weight): every layer checked from its own GPU input (P1 + P2 per token, final states), the
+    output against the oracle's final RMSNorm, and the whole against three dfssm_layer_prefill calls
+    and the library's final norm (the same kernels: bit-identical)."""
+    nL, B, T, Q = 3, 2, 300, 64
+    layers = gen.stack_weights(TINY, nL, seed=16, random_norms=True, per_channel_lora=True)
+    states0 = [gen.initial_states(TINY, B, l, 16, std=0.2) for l in range(nL)]
+    xs = gen.token_inputs(TINY, (B, T), 16, tag=7)
+    fw = np.random.default_rng(16).uniform(0.5, 1.5, TINY.d_model).astype(np.float32)
+    say(f"case: tiny stack prefill, {nL} layers, batch {B}, seqlen {T}, chunk {Q}")
+    y, lt, finals, _, _ = run_stack_prefill(TINY, layers, xs, states0, Q, fw)
+    for l in range(nL):
+        tl = lt(l)
+        dense = O.dense_signs(layers[l])
+        for b in range(B):
+            tb = {k: v[b] for k, v in tl.items()}
+            out = lt(l + 1)["h_in"][b] if l + 1 < nL else y[b]
+            errs = check_sequence(layers[l], tb["h_in"], states0[l][0][b], states0[l][1][b], out, tb,
+                                  (finals[l][0][b], finals[l][1][b]), dense, what=f"layer {l} row {b}",
+                                  final_w=None if l + 1 < nL else fw)
+            say(f"layer {l} row {b}: {errs}")
+    # composition of single-layer prefills gives the same bits
+    say("case: same stack as three dfssm_layer_prefill calls")
+    h = xs
+    st = [list(s_) for s_ in states0]
+    for l in range(nL):
+        h, _, fin = run_prefill(TINY, layers[l], h, st[l][0], st[l][1], Q, taps=False)
+        assert (fin[0] == finals[l][0]).all() and (fin[1] == finals[l][1]).all(), l
+    assert (O.rmsnorm(h, fw, TINY.eps) - y).__abs__().max() < 1e-5
+
+
+def test_stack_prefill_1p3b_48_layers_2048_then_decode():
+    """The prefill workload (48 layers, 2048 bf16 tokens, chunk 256, zero states) with its final
+    states handed to 16 stack-decode steps fed the last position's output. Sampled layers are
+    checked over every token from their own GPU input (codes and integer sums exact, floats and the
+    final states against the oracle's sequential recurrence); the 16 decode steps are checked
+    through all 48 layers with the GPU's codes forced into the oracle, which starts from the
+    handed-off states and keeps its own float trajectory (P3)."""
+    L, Dv = _lib()
+    nL, T, Q, T2 = 48, 2048, 256, 16
+    layers = gen.stack_weights(BIG, nL, seed=0)
+    states0 = [gen.initial_states(BIG, 1, l) for l in range(nL)]
+    xs = gen.token_inputs(BIG, (1, T), 0, tag=11, bf16=True)
+    fw = np.ones(BIG.d_model, np.float32)
+    say(f"case: 1.3B stack prefill, {nL} layers, seqlen {T}, chunk {Q}, bf16 input, with taps")
+    y, lt, finals, devs, sts = run_stack_prefill(BIG, layers, xs, states0, Q, fw, bf16=True)
+    assert np.isfinite(y).all()
+    for l in (0, 1, 24, 47):
+        tl = {k: v[0] for k, v in lt(l).items()}
+        out = lt(l + 1)["h_in"][0] if l + 1 < nL else y[0]
+        if l == 0:
+            assert (tl["h_in"] == xs[0]).all()
+        errs = check_sequence(layers[l], tl["h_in"], states0[l][0][0], states0[l][1][0], out, tl,
+                              (finals[l][0][0], finals[l][1][0]), O.dense_signs(layers[l]), what=f"layer {l}",
+                              final_w=None if l + 1 < nL else fw)
+        say(f"prefill layer {l}: {errs}")
+    # hand-off: decode 16 tokens from the prefill's final states, x0 = the last position's output
+    say(f"case: {T2} stack-decode steps from the handed-off states")
+    x0 = torch.from_numpy(np.ascontiguousarray(y[:, -1])).cuda()
+    yd = torch.empty((T2, 1, BIG.d_model), dtype=torch.float32, device="cuda")
+    wsd = Dv.workspace(BIG, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
+    tpd = Dv.Taps(BIG, T2 * nL)
+    Dv.stack_decode(BIG, devs, sts, torch.from_numpy(fw).cuda(), x0, yd, T2, wsd, tpd)
+    torch.cuda.synchronize()
+    assert Dv.stack_status(wsd) == L.DFSSM_STATUS_OK
+    yd = yd.cpu().numpy()
+    taps = tpd.numpy()
+    dense_all = [O.dense_signs(lw) for lw in layers]
+    cs = [f[0][0].astype(np.float64) for f in finals]
+    ss = [f[1][0].astype(np.float64) for f in finals]
+    x = y[0, -1].astype(np.float64)
+    errs = []
+    for t in range(T2):
+        h = x
+        for l in range(nL):
+            tap = PY.tap_record(taps, t * nL + l)
+            PY.assert_codes_exact(tap["in_u"], tap["in_q"], tap["in_s"][0], f"decode t{t} l{l} in")
+            PY.assert_codes_exact(tap["out_u"], tap["out_q"], tap["out_s"][0], f"decode t{t} l{l} out")
+            PY.assert_products_exact(layers[l].in_proj, tap["in_q"], tap["in_acc"], tap["in_t"], dense_all[l]["in"])
+            PY.assert_products_exact(layers[l].out_proj, tap["out_q"], tap["out_acc"], tap["out_t"],
+                                     dense_all[l]["out"])
+            force = dict(in_q=tap["in_q"], in_s=tap["in_s"][0], out_q=tap["out_q"], out_s=tap["out_s"][0])
+            h, cs[l], ss[l], _ = O.layer_decode(h, layers[l], cs[l], ss[l], force=force, dense=dense_all[l])
+        yo = O.rmsnorm(h, fw, BIG.eps)
+        errs.append(PY.err(yd[t][0], yo))
+        x = yo
+    say(f"hand-off decode, code-forced through 48 layers: max err {max(errs):.2e}")
+    assert max(errs) < PY.TOL_STACK
+    for l in range(nL):
+        assert PY.err(sts[l].conv.cpu().numpy()[0], cs[l]) < PY.TOL_STACK, l
+        assert PY.err(sts[l].ssm.cpu().numpy()[0], ss[l]) < PY.TOL_STACK, l

@@ -376,3 +376,60 @@ def test_layer_tokens_equals_sequential_decode():
     f = dict(in_q=tp2["in_q"], in_s=tp2["in_s"], out_q=tp2["out_q"], out_s=tp2["out_s"])
     o3, _, _, _ = O.layer_tokens(xs, lw, conv0[0], ssm0[0], force=f)
     np.testing.assert_array_equal(o3, o2)
+
+
+# ------------------------------------------------------------------ elementwise functions
+def test_softplus_closed_forms_and_library():
+    """softplus(v) = log(1 + e^v): ln 2 at 0, softplus(v) - softplus(-v) = v, numpy's logaddexp(0, v)
+    (the same function by another route) everywhere, continuous across the v > 20 branch, e^v in
+    the far-negative tail."""
+    assert O.softplus(0.0) == pytest.approx(np.log(2.0), rel=1e-15)
+    # above 20 the oracle returns v itself (the usual Mamba threshold): it drops log1p(e^-v) <= 2.1e-9
+    v = np.linspace(-30.0, 30.0, 601)
+    np.testing.assert_allclose(O.softplus(v) - O.softplus(-v), v, rtol=0, atol=2.1e-9)
+    inner = np.abs(v) <= 20.0
+    np.testing.assert_allclose(O.softplus(v[inner]) - O.softplus(-v[inner]), v[inner], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.softplus(v[inner]), np.logaddexp(0.0, v[inner]), rtol=1e-14, atol=1e-300)
+    np.testing.assert_allclose(O.softplus(v), np.logaddexp(0.0, v), rtol=1e-10, atol=0)
+    lo, hi = O.softplus(np.nextafter(20.0, 0.0)), O.softplus(np.nextafter(20.0, 40.0))
+    assert abs(float(hi) - float(lo)) < 1e-8
+    np.testing.assert_allclose(O.softplus(np.array([-40.0, -60.0])), np.exp([-40.0, -60.0]), rtol=1e-12)
+    assert (O.softplus(v) >= np.maximum(v, 0.0)).all()
+
+
+def test_silu_closed_forms_and_library():
+    """silu(v) = v * sigmoid(v): 0 at 0, silu(v) - silu(-v) = v, scipy's expit gives the sigmoid by
+    another route, slope 1/2 at 0, -> v for large v and -> 0 for very negative v."""
+    from scipy.special import expit
+    assert O.silu(0.0) == 0.0
+    v = np.linspace(-30.0, 30.0, 601)
+    np.testing.assert_allclose(O.silu(v) - O.silu(-v), v, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.silu(v), v * expit(v), rtol=1e-14, atol=1e-300)
+    h = 1e-6
+    assert (O.silu(h) - O.silu(-h)) / (2 * h) == pytest.approx(0.5, rel=1e-9)
+    assert O.silu(1.0) == pytest.approx(1.0 / (1.0 + np.exp(-1.0)), rel=1e-15)
+    assert O.silu(40.0) == pytest.approx(40.0, rel=1e-15) and abs(O.silu(-40.0)) < 1e-15
+
+
+def test_stack_identity_layers_closed_form():
+    """With every layer the identity (z rows zeroed, so the gate and the out-projection codes are 0),
+    the stack's step t outputs RMSNorm applied t + 1 times with the final weight w: y[t] points along
+    x0 * w^(t+1) and y[t] / w has mean square m / (m + eps), m the mean square of the step's input.
+    Feeding back the un-normalised residual, or dropping w, breaks the direction or the scale."""
+    dm = _tiny_dims()
+    layers = [_zero_z_rows(gen.layer_weights(dm, l, 26, random_norms=True)) for l in range(2)]
+    states = [gen.initial_states(dm, 1, l) for l in range(2)]
+    x0 = gen.token_inputs(dm, (1,), 26)[0].astype(np.float64) * 3.0
+    w = np.random.default_rng(26).uniform(0.5, 1.5, dm.d_model)
+    T = 4
+    ys, _, _ = O.stack_decode(x0, layers, [s[0][0] for s in states], [s[1][0] for s in states], T, w, dm.eps)
+    x = x0
+    for t in range(T):
+        direction = x0 * w ** (t + 1)
+        ratio = ys[t] / direction
+        np.testing.assert_allclose(ratio, ratio[0], rtol=1e-12)          # parallel, same sign
+        assert ratio[0] > 0
+        m = sum(float(v) * float(v) for v in x) / x.size                  # mean square of the input
+        got = sum(float(v) * float(v) for v in ys[t] / w) / x.size
+        assert got == pytest.approx(m / (m + dm.eps), rel=1e-12)
+        x = ys[t]
