@@ -16,6 +16,7 @@ DFSSM_EWORKSPACE = -3
 DFSSM_EHIP = -4
 
 DFSSM_OP_LAYER_DECODE = 0
+DFSSM_NOALLOC_SCRATCH_BYTES = 16 << 20
 DFSSM_OP_LAYER_PREFILL = 1
 DFSSM_OP_STACK_DECODE = 2
 DFSSM_OP_STACK_PREFILL = 3
@@ -32,7 +33,7 @@ DFSSM_F32 = 0
 DFSSM_BF16 = 1
 
 # every symbol include/dfssm.h declares
-EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_prefill",
+EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_decode_noalloc", "dfssm_layer_prefill",
            "dfssm_stack_decode", "dfssm_stack_decode_ex", "dfssm_stack_prefill", "dfssm_strerror")
 
 
@@ -89,6 +90,10 @@ def load() -> C.CDLL:
                                        C.POINTER(dfssm_layer_state), P, P, C.c_int32, P, C.c_size_t,
                                        C.POINTER(dfssm_taps), P]
     lib.dfssm_layer_decode.restype = C.c_int
+    lib.dfssm_layer_decode_noalloc.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
+                                               C.POINTER(dfssm_layer_state), P, P, C.c_int32,
+                                               C.POINTER(dfssm_taps), P]
+    lib.dfssm_layer_decode_noalloc.restype = C.c_int
     lib.dfssm_layer_prefill.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
                                         C.POINTER(dfssm_layer_state), P, C.c_int32, P, C.c_int32,
                                         C.c_int32, C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
@@ -123,6 +128,11 @@ def dfssm_workspace_bytes(dims: dfssm_dims, op: int, batch: int, seqlen: int = 0
 def dfssm_layer_decode(dims, w, state, x_in, x_out, batch, ws, ws_bytes, taps=None, stream=None) -> int:
     return int(load().dfssm_layer_decode(C.byref(dims), C.byref(w), C.byref(state), x_in, x_out, batch,
                                          ws, ws_bytes, _ref(taps), stream))
+
+
+def dfssm_layer_decode_noalloc(dims, w, state, x_in, x_out, batch, taps=None, stream=None) -> int:
+    return int(load().dfssm_layer_decode_noalloc(C.byref(dims), C.byref(w), C.byref(state), x_in, x_out, batch,
+                                                 _ref(taps), stream))
 
 
 def dfssm_layer_prefill(dims, w, state, x_in, x_dtype, x_out, batch, seqlen, chunk, ws, ws_bytes,

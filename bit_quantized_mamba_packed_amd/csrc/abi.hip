@@ -1,6 +1,8 @@
 // C ABI of the DF-SSM hot path: argument validation, workspace carving and launch sequencing.
 // Every check happens before the first enqueue, so a rejected call has no side effect.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "dfssm_internal.h"
 
@@ -24,9 +26,39 @@ Shape shape_of(const dfssm_dims &d) {
     return s;
 }
 
+// Fixed device scratch of dfssm_layer_decode_noalloc: every GPU the library runs on holds its own
+// copy until the process ends. In host code `scratch` names a host-side stand-in, never the device
+// array: its device address comes from hipGetSymbolAddress, once per device (scratch_on_device).
+constexpr size_t kNoAllocScratchBytes = DFSSM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, looked up on the first call on that device.
+hipError_t scratch_on_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 int check_dims(const dfssm_dims *d) {
     if (!d) return DFSSM_EINVAL;
@@ -229,6 +261,22 @@ int dfssm_layer_decode(const dfssm_dims *dims, const dfssm_layer_weights *w, con
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
     const Shape s = shape_of(*dims);
     if (ws_bytes < decode_ws_bytes(s, batch, false)) return DFSSM_EWORKSPACE;
+    const TapPtrs tp = tap_offset(taps, s, 0);
+    return hip_status(decode_step(s, *w, *state, x_in, x_out, batch, ws, false, tp, static_cast<hipStream_t>(stream)));
+}
+
+int dfssm_layer_decode_noalloc(const dfssm_dims *dims, const dfssm_layer_weights *w,
+                               const dfssm_layer_state *state, const float *x_in, float *x_out, int32_t batch,
+                               const dfssm_taps *taps, void *stream) {
+    int r;
+    if ((r = check_dims(dims))) return r;
+    if ((r = check_weights(w)) || (r = check_state(state)) || (r = check_taps(taps))) return r;
+    if (bad_ptr(x_in) || bad_ptr(x_out) || batch <= 0) return DFSSM_EINVAL;
+    if (batch > 4096) return DFSSM_EUNSUPPORTED;
+    const Shape s = shape_of(*dims);
+    if (decode_ws_bytes(s, batch, false) > kNoAllocScratchBytes) return DFSSM_EWORKSPACE;
+    void *ws = nullptr;
+    if (scratch_on_device(&ws) != hipSuccess) return DFSSM_EHIP;
     const TapPtrs tp = tap_offset(taps, s, 0);
     return hip_status(decode_step(s, *w, *state, x_in, x_out, batch, ws, false, tp, static_cast<hipStream_t>(stream)));
 }

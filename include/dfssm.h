@@ -173,6 +173,22 @@ int dfssm_layer_decode(const dfssm_dims *dims, const dfssm_layer_weights *w,
                        void *stream);
 
 /*
+ * dfssm_layer_decode without a workspace argument, for callers that cannot allocate device memory
+ * around the call: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. The intermediates live in a fixed device array of DFSSM_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends (its address is looked up on
+ * the first call on each device, so make one call before capturing a graph). The call allocates
+ * nothing; a shape and batch whose dfssm_workspace_bytes(DFSSM_OP_LAYER_DECODE) exceeds the array
+ * returns DFSSM_EWORKSPACE (e.g. the Mamba-2 1.3B layer runs up to batch 4). Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams, or host threads)
+ * race and must be ordered by the caller. Arguments and results as dfssm_layer_decode.
+ */
+#define DFSSM_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dfssm_layer_decode_noalloc(const dfssm_dims *dims, const dfssm_layer_weights *w,
+                               const dfssm_layer_state *state, const float *x_in, float *x_out,
+                               int32_t batch, const dfssm_taps *taps, void *stream);
+
+/*
  * Prefill of `seqlen` tokens per sequence through one layer, starting from `state` and leaving
  * the final conv/SSM state in it. The result equals seqlen successive dfssm_layer_decode steps
  * (quantization is per token); the SSM part is evaluated as a chunked scan with chunk length
