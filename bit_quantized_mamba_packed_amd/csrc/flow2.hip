@@ -1001,12 +1001,12 @@ int f2_resident() {
 }
 
 // The (D, E = 2D) shapes the kernel is built for: KCH1 = D / 1024, KCH2 = E / 1024 (at least 1).
+// D = 4096 would mean 128 heads, whose items hold more rows than the GEMV loop takes (f2_plan).
 int f2_slots(const Shape &s, int batch) {
     if (batch != 1 || s.E != 2 * s.D) return 0;
     switch (f2_kch(s.D)) {
     case 1: return f2_kch(s.E) == 1 ? f2_resident<1, 1, 1>() : f2_resident<1, 1, 2>();
     case 2: return f2_resident<1, 2, 4>();
-    case 4: return f2_resident<1, 4, 8>();
     default: return 0;
     }
 }
@@ -1015,7 +1015,6 @@ hipError_t f2_launch_any(F2Args &a, const Shape &s, hipStream_t stream) {
     switch (f2_kch(s.D)) {
     case 1: return f2_kch(s.E) == 1 ? f2_launch<1, 1, 1>(a, s, stream) : f2_launch<1, 1, 2>(a, s, stream);
     case 2: return f2_launch<1, 2, 4>(a, s, stream);
-    case 4: return f2_launch<1, 4, 8>(a, s, stream);
     default: return hipErrorInvalidConfiguration;
     }
 }
