@@ -17,6 +17,7 @@ Secondary workloads (reported under "secondary", or alone with --workload):
   decode_b64   48-layer stack decode at batch 64 (states ~ N(0, 0.1)), 128 tokens per sequence
                per step; roofline: algorithmic HBM bytes (weights once per token step, every
                sequence's conv/SSM state read and written) / time.
+  decode_sweep the same at batch 8, 32, 128 and 512 (zero states), one point per batch.
 
 Prints ONE JSON line. `roofline.achieved` = algorithmic bytes (ops) of one launch / that launch's
 duration. `roofline.traffic` = HBM bytes per launch from the committed rocprofv3 FETCH_SIZE +
@@ -344,7 +345,41 @@ def run_decode_b64(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict
     }
 
 
-WORKLOADS = {"decode_b1": run_decode_b1, "prefill2048": run_prefill, "decode_b64": run_decode_b64}
+def run_decode_sweep(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
+    """48-layer stack decode at the batch sizes of the pages' batched throughput table (8, 32, 128,
+    512; zero states, seeded inputs): tokens/s and algorithmic HBM bytes (weights once per token
+    step, every sequence's conv/SSM state read and written) per second."""
+    nL = args.layers
+    out = {"metric": "decode tokens/s by batch, 48-layer 1.3B shape; achieved HBM GB/s vs peak",
+           "unit": "tokens/s", "points": []}
+    for B in (8, 32, 128, 512):
+        T = max(16, 1024 // B)
+        conv = torch.zeros((nL, B, dims.conv_dim, dims.d_conv - 1), dtype=torch.float32, device="cuda")
+        ssm = torch.zeros((nL, B, dims.nheads, dims.headdim, dims.d_state), dtype=torch.float32, device="cuda")
+        states = [Dv.DeviceState.from_tensors(conv[l], ssm[l], dims, B) for l in range(nL)]
+        fw = torch.ones(dims.d_model, dtype=torch.float32, device="cuda")
+        x0 = torch.from_numpy(gen.token_inputs(dims, (B,), 0, tag=12)).cuda()
+        y = torch.empty((T, B, dims.d_model), dtype=torch.float32, device="cuda")
+        ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, B, 0, nL)
+        steps = max(1, min(args.steps, 2))
+        wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws), steps,
+                                min(args.warmup, 1), torch)
+        if Dv.stack_status(ws) != L.DFSSM_STATUS_OK or not torch.isfinite(y).all():
+            raise SystemExit(f"batch-{B} stack decode failed")
+        per_step = decode_b64_bytes_per_step(dims, nL, B)
+        avg_s = sum(launch_ms) / len(launch_ms) / 1e3
+        ach = per_step * T / avg_s / 1e9
+        out["points"].append({"batch": B, "tokens_per_step": T, "value": round(steps * T * B / wall, 2),
+                              "ms_per_step": round(wall / steps * 1e3, 3),
+                              "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
+                                           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 5)}})
+        del conv, ssm, states, y, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+WORKLOADS = {"decode_b1": run_decode_b1, "prefill2048": run_prefill, "decode_b64": run_decode_b64,
+             "decode_sweep": run_decode_sweep}
 
 
 def main() -> int:
@@ -393,11 +428,11 @@ def main() -> int:
     out = run_decode_b1(*common)
     if not args.no_secondary:
         sec = {}
-        for name in ("prefill2048", "decode_b64"):
+        for name in ("prefill2048", "decode_b64", "decode_sweep"):
             r = WORKLOADS[name](*common)
             torch.cuda.empty_cache()
             sec[name] = {k: r[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",
-                                           "cpu_baseline") if k in r}
+                                           "roofline_scaffold_gemms", "points", "cpu_baseline") if k in r}
         out["secondary"] = sec
     print(json.dumps(out), flush=True)
     return 0

@@ -119,7 +119,7 @@ size_t decode_ws_bytes(const Shape &s, int batch, bool stack, int n_layers = 0) 
     size_t extra = stack ? kAlign : 0;
     if (stack && stack2_ok(s, batch))
         extra += stack2_extra_ws_bytes(s, batch, n_layers);
-    else if (decode_uses_mfma(s, batch)) extra = carve_prefill_ws(s, batch, 1, 1, nullptr).bytes;
+    else if (decode_uses_mfma(s, batch)) extra += carve_prefill_ws(s, batch, 1, 0, nullptr).bytes;
     return w.bytes + extra;
 }
 
@@ -170,7 +170,7 @@ hipError_t decode_step(const Shape &s, const dfssm_layer_weights &w, const dfssm
                        float *x_out, int batch, void *ws, bool stack, const TapPtrs &tp, hipStream_t stream) {
     const DecodeWs d = carve_decode_ws(s, batch, ws, stack);
     if (decode_uses_mfma(s, batch)) {
-        const PrefillWs p = carve_prefill_ws(s, batch, 1, 1, static_cast<char *>(ws) + d.bytes);
+        const PrefillWs p = carve_prefill_ws(s, batch, 1, 0, static_cast<char *>(ws) + d.bytes);
         return launch_layer_decode_mfma(s, w, st, x_in, x_out, batch, d, p, tp, stream);
     }
     return launch_layer_decode(s, w, st, x_in, x_out, batch, d, tp, stream);

@@ -119,7 +119,8 @@ struct TokQuantArgs {
 };
 hipError_t launch_tok_quant(const TokQuantArgs &a, hipStream_t stream);
 
-// Prefill workspace carve-up (tokens M = batch * seqlen, chunk Q).
+// Prefill workspace carve-up (tokens M = batch * seqlen, chunk Q; Q = 0 for a decode step, which
+// runs no chunked scan and so carves none of its buffers).
 struct PrefillWs {
     int8_t *q_in, *q_out;
     float *s_in, *s_out;
@@ -140,7 +141,7 @@ hipError_t launch_ssm_step(const Shape &s, const dfssm_layer_weights &w, const d
                            const DecodeWs &ws, int batch, hipStream_t stream);
 
 // One decode step of one layer for many tokens through the int8-MFMA projections (prefill.hip);
-// pws is a prefill workspace carved for (batch, seqlen 1, chunk 1).
+// pws is a prefill workspace carved for (batch, seqlen 1, chunk 0).
 hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
                                     const float *x_in, float *x_out, int batch, const DecodeWs &dws,
                                     const PrefillWs &pws, const TapPtrs &taps, hipStream_t stream);

@@ -1149,7 +1149,7 @@ PrefillWs carve_prefill_ws(const Shape &s, int batch, int seqlen, int chunk, voi
         return p;
     };
     const size_t M = (size_t)batch * seqlen;
-    const int nch = (seqlen + chunk - 1) / chunk;
+    const int nch = chunk > 0 ? (seqlen + chunk - 1) / chunk : 0;   // chunk 0: decode, no scan buffers
     w.q_in = static_cast<int8_t *>(take(M * s.D));
     w.s_in = static_cast<float *>(take(M * 4));
     w.qsum_in = static_cast<int32_t *>(take(M * 4));

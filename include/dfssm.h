@@ -179,7 +179,7 @@ int dfssm_layer_decode(const dfssm_dims *dims, const dfssm_layer_weights *w,
  * the library holds on every GPU it runs on until the process ends (its address is looked up on
  * the first call on each device, so make one call before capturing a graph). The call allocates
  * nothing; a shape and batch whose dfssm_workspace_bytes(DFSSM_OP_LAYER_DECODE) exceeds the array
- * returns DFSSM_EWORKSPACE (e.g. the Mamba-2 1.3B layer runs up to batch 4). Every call on a GPU
+ * returns DFSSM_EWORKSPACE (the Mamba-2 1.3B layer fits up to batch 64). Every call on a GPU
  * shares that GPU's array: calls that overlap on one GPU (different streams, or host threads)
  * race and must be ordered by the caller. Arguments and results as dfssm_layer_decode.
  */

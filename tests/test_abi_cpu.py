@@ -233,3 +233,13 @@ def test_stack_prefill_workspace_and_rejects_bad_arguments():
     assert call(wsb=2 * 100 * d.d_model * 4) == L.DFSSM_EWORKSPACE     # the residual buffer alone
     arr_s[1].conv = None
     assert call() == L.DFSSM_EINVAL
+
+
+def test_stack_workspace_covers_status_word_and_every_layer_step():
+    """A stack decode's workspace holds its status word (256 bytes) ahead of what one layer step of
+    the same batch needs, for the packed-sign GEMV batches and the MFMA GEMM batches alike."""
+    for d in (_dims(), _dims(d_model=2048, d_inner=4096, d_state=128, n_in_proj=8512, rank_in=32, rank_out=32)):
+        for B in (1, 2, 4, 5, 8, 64, 65, 512):
+            layer = L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_DECODE, B)
+            stack = L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_DECODE, B, 0, 3)
+            assert stack >= layer + 256 + 2 * B * d.d_model * 4, (B, layer, stack)

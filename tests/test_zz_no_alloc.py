@@ -61,7 +61,10 @@ def _same(out, states, what):
 def test_noalloc_matches_layer_decode_two_calls_second_smaller():
     L, Dv = _lib()
     big = gen.DIMS["1p3b"]
-    print("case: no-alloc layer decode, 1.3B layer, batch 4, 3 steps", flush=True)
+    print("case: no-alloc layer decode, 1.3B layer, batch 48 (skinny MFMA GEMMs), 2 steps", flush=True)
+    out, st = _pair(big, 0, 30, 48, 2, 0.1)
+    _same(out, st, "1.3B batch 48")
+    print("case: no-alloc layer decode, 1.3B layer, batch 4 (packed-sign GEMV), 3 steps", flush=True)
     out, st = _pair(big, 0, 31, 4, 3, 0.1)
     _same(out, st, "1.3B batch 4")
     print("case: no-alloc layer decode, tiny layer, batch 2, 2 steps (smaller, after the larger)", flush=True)
@@ -76,11 +79,14 @@ def test_noalloc_rejects_what_exceeds_the_scratch():
     L, Dv = _lib()
     big = gen.DIMS["1p3b"]
     d = Dv.dims_struct(big)
-    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_DECODE, 64) > L.DFSSM_NOALLOC_SCRATCH_BYTES
+    B = 512
+    assert L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_DECODE, B) > L.DFSSM_NOALLOC_SCRATCH_BYTES
     lw = Dv.DeviceLayer(gen.layer_weights(big, 0, 0))
-    st = Dv.DeviceState(*gen.initial_states(big, 64))
-    x = torch.zeros((64, big.d_model), device="cuda")
+    conv = torch.zeros((B, big.conv_dim, big.d_conv - 1), device="cuda")
+    ssm = torch.zeros((B, big.nheads, big.headdim, big.d_state), device="cuda")
+    st = Dv.DeviceState.from_tensors(conv, ssm, big, B)
+    x = torch.zeros((B, big.d_model), device="cuda")
     y = torch.empty_like(x)
-    r = L.dfssm_layer_decode_noalloc(d, lw.struct, st.struct, x.data_ptr(), y.data_ptr(), 64, None,
+    r = L.dfssm_layer_decode_noalloc(d, lw.struct, st.struct, x.data_ptr(), y.data_ptr(), B, None,
                                      Dv.stream_handle())
     assert r == L.DFSSM_EWORKSPACE, L.dfssm_strerror(r)
