@@ -37,6 +37,11 @@ What each function follows and what pins it (the pins live in tests/test_oracle_
   layer_tokens      the same steps run stage by stage over the sequence (batched projections).
                     pinned by: equals layer_decode_steps (codes, integer sums and floats)
   table1_bytes      [DF-SSM] §3.3 Table 1.  pinned by the table's printed sizes
+  embed             [DF-SSM] §3.3 (int8 embedding, per-row scale), Table 1 (103 MB, tied).
+                    pinned by: Table 1's embedding size; rows by explicit indexing
+  lm_head           the tied head over the same int8 rows (Table 1 "Embedding + LM head (tied)")
+                    with the per-token quantizer (R18).  pinned by: brute force with Python ints;
+                    the dequantised dense product; planted maxima for the argmax
 
 Readings where the page is silent (also listed in the design doc):
   R1 scaffold values are +-1 times a per-output-row fp16 scale (the page's 1-bit storage; 1 bit
@@ -51,7 +56,11 @@ Readings where the page is silent (also listed in the design doc):
   R14 discretisation dA = exp(dt*A), dB x = dt * x * B (App. B Table 12), no ZOH factor;
   R15 dt = softplus(dt_raw + dt_bias);  A = -exp(A_log);
   R17 conv applies to x, B and C; SiLU after the conv on all three; the conv state keeps the last
-      d_conv-1 pre-activation inputs, oldest first.
+      d_conv-1 pre-activation inputs, oldest first;
+  R18 the tied LM head reads the stack's normalised output y through the same per-token int8
+      quantizer as the projections: logits[v] = s * row_scale[v] * sum_k codes[v,k] q[k] (an
+      integer contraction like the scaffold's); the argmax takes the smallest index among equal
+      maxima.
 """
 from __future__ import annotations
 
@@ -411,3 +420,33 @@ def table1_bytes(d_model: int, d_inner: int, n_in_proj: int, n_layers: int, rank
     if vocab is not None:
         out["embedding"] = vocab * d_model
     return out
+
+
+# ----------------------------------------------------------------------------- embedding + LM head
+def embed(tokens, codes, row_scale):
+    """[DF-SSM] §3.3: the int8 embedding with a per-row scale. tokens [B] -> x [B][d_model] fp64,
+    x[b] = row_scale[tokens[b]] * codes[tokens[b]]."""
+    tok = np.asarray(tokens, np.int64)
+    return np.asarray(row_scale, F64)[tok][:, None] * np.asarray(codes, F64)[tok]
+
+
+def lm_head(y, codes, row_scale, chunk_rows: int = 4096):
+    """The tied head over the embedding rows (Table 1) for one token y [d_model] (R18).
+
+    Returns (logits fp64 [vocab], acc int64 [vocab], q int8 [d_model], s fp32):
+      (q, s) = quantize_token(y);  acc[v] = sum_k codes[v,k] q[k] (exact);  logits = s*row_scale*acc.
+    The rows are taken in blocks only to bound memory; every block product is exact in fp64."""
+    q, s = quantize_token(y)
+    qf = np.asarray(q, F64)
+    V = codes.shape[0]
+    acc = np.empty(V, np.int64)
+    for r0 in range(0, V, chunk_rows):
+        acc[r0:r0 + chunk_rows] = (np.asarray(codes[r0:r0 + chunk_rows], F64) @ qf).astype(np.int64)
+    logits = F64(s) * np.asarray(row_scale, F64) * acc.astype(F64)
+    return logits, acc, q, s
+
+
+def argmax_first(v) -> int:
+    """Index of the largest value, the smallest such index when several are equal (R18)."""
+    v = np.asarray(v)
+    return int(np.flatnonzero(v == v.max())[0])

@@ -17,7 +17,9 @@ whose weights are not available):
 * dt_bias is chosen so that softplus(dt_bias) is log-uniform in [1e-3, 1e-1];
 * depthwise conv taps and bias ~ U[-0.5, 0.5];
 * norm weights 1, or U[0.5, 1.5] when ``random_norms`` is set;
-* token inputs ~ N(0, 1) fp32 (optionally rounded to bf16); initial states zero or N(0, std).
+* token inputs ~ N(0, 1) fp32 (optionally rounded to bf16); initial states zero or N(0, std);
+* int8 embedding (tied LM head): 50,280 rows (Table 1's 103 MB at d_model 2048), codes uniform in
+  [-127, 127], per-row scales U[2e-4, 1e-3]; token ids uniform.
 
 No function here computes any part of the layer: no norm, quantizer, projection, convolution,
 gate or recurrence.
@@ -182,6 +184,38 @@ def layer_weights(dims: Dims, layer: int = 0, seed: int = 0, *, random_norms: bo
 
 def stack_weights(dims: Dims, n_layers: int, seed: int = 0, **kw) -> list:
     return [layer_weights(dims, l, seed, **kw) for l in range(n_layers)]
+
+
+# tensor ids of the embedding (a "layer" slot of its own)
+_EMBED_LAYER_KEY = 200000
+VOCAB_1P3B = 50280   # rows of the int8 embedding: 50,280 x 2,048 B = 103 MB (Table 1)
+
+
+@dataclass
+class Embedding:
+    """int8 embedding with a per-row fp32 scale, tied to the LM head.
+
+    codes     int8 [vocab][d_model]
+    row_scale fp32 [vocab]    (weight[v][k] = codes[v][k] * row_scale[v])
+    """
+    codes: np.ndarray
+    row_scale: np.ndarray
+
+    @property
+    def vocab(self) -> int:
+        return self.codes.shape[0]
+
+
+def embedding(dims: Dims, vocab: int = VOCAB_1P3B, seed: int = 0) -> Embedding:
+    """Seeded int8 embedding: codes uniform in [-127, 127], per-row scales U[2e-4, 1e-3]."""
+    codes = _rng(seed, _EMBED_LAYER_KEY, 0).integers(-127, 128, size=(vocab, dims.d_model)).astype(np.int8)
+    scale = _rng(seed, _EMBED_LAYER_KEY, 1).uniform(2e-4, 1e-3, size=vocab).astype(np.float32)
+    return Embedding(codes, scale)
+
+
+def token_ids(batch: int, vocab: int, seed: int = 0, tag: int = 0) -> np.ndarray:
+    """Uniform token ids in [0, vocab), int32 [batch]."""
+    return _rng(seed, _INPUT_LAYER_KEY, 1000 + tag).integers(0, vocab, size=batch).astype(np.int32)
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:

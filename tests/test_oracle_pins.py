@@ -433,3 +433,50 @@ def test_stack_identity_layers_closed_form():
         got = sum(float(v) * float(v) for v in ys[t] / w) / x.size
         assert got == pytest.approx(m / (m + dm.eps), rel=1e-12)
         x = ys[t]
+
+
+# ------------------------------------------------------------------ embedding + LM head
+def test_embedding_size_matches_table1():
+    fx = _golden("table1_model_size.json")
+    d = gen.DIMS["1p3b"]
+    b = O.table1_bytes(d.d_model, d.d_inner, d.n_in_proj, fx["n_layers"], fx["lora_rank"], vocab=gen.VOCAB_1P3B)
+    # one byte per weight of the tied embedding/LM head reproduces the printed 103 MB
+    assert round(b["embedding"] / 1e6) == fx["embedding_MB"]
+    assert round(2 * b["embedding"] / 1e6) != fx["embedding_MB"]          # not fp16, not untied
+
+
+def test_embed_rows_by_explicit_indexing():
+    rng = np.random.default_rng(50)
+    codes = rng.integers(-127, 128, size=(11, 6)).astype(np.int8)
+    scale = rng.uniform(1e-4, 1e-3, 11).astype(np.float32)
+    toks = np.array([3, 0, 10, 3], np.int32)
+    x = O.embed(toks, codes, scale)
+    for i, t in enumerate(toks):
+        for k in range(6):
+            assert x[i, k] == float(scale[t]) * int(codes[t, k])
+
+
+def test_lm_head_brute_force_dense_and_argmax():
+    rng = np.random.default_rng(51)
+    V, D = 37, 24
+    codes = rng.integers(-127, 128, size=(V, D)).astype(np.int8)
+    scale = rng.uniform(1e-4, 1e-3, V).astype(np.float32)
+    y = rng.standard_normal(D).astype(np.float32)
+    logits, acc, q, s = O.lm_head(y, codes, scale, chunk_rows=5)
+    qo, so = O.quantize_token(y)
+    assert (q == qo).all() and s == so
+    for v in range(V):
+        assert acc[v] == sum(int(codes[v, k]) * int(q[k]) for k in range(D))
+    # the same logits from the dequantised matrices by another route
+    dense = (codes.astype(np.float64) * scale.astype(np.float64)[:, None]) @ (q.astype(np.float64) * float(s))
+    np.testing.assert_allclose(logits, dense, rtol=1e-12, atol=1e-15)
+    # a planted maximum wins; equal maxima resolve to the smallest index
+    c2 = codes.copy()
+    c2[17] = np.where(q >= 0, 127, -127)
+    s2 = scale.copy()
+    s2[17] = 2e-3
+    l2, _, _, _ = O.lm_head(y, c2, s2)
+    assert O.argmax_first(l2) == 17
+    c2[30], s2[30] = c2[17], s2[17]
+    l3, _, _, _ = O.lm_head(y, c2, s2)
+    assert O.argmax_first(l3) == 17
