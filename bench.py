@@ -18,6 +18,8 @@ Secondary workloads (reported under "secondary", or alone with --workload):
                per step; roofline: algorithmic HBM bytes (weights once per token step, every
                sequence's conv/SSM state read and written) / time.
   decode_sweep the same at batch 8, 32, 128 and 512 (zero states), one point per batch.
+  lm_head      the tied int8 LM head alone (batch 1, HBM roofline), and a greedy decode of the whole
+               model (embedding -> 48 layers -> head -> next token), 64 tokens.
 
 Prints ONE JSON line. `roofline.achieved` = algorithmic bytes (ops) of one launch / that launch's
 duration. `roofline.traffic` = HBM bytes per launch from the committed rocprofv3 FETCH_SIZE +
@@ -378,8 +380,67 @@ def run_decode_sweep(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> di
     return out
 
 
+def run_lm_head(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
+    """The tied int8 LM head alone (batch 1, 50,280 x 2,048 int8 rows, greedy token only), and a
+    greedy full-model decode: token -> int8 embedding -> the 48-layer stack (one dfssm_stack_decode
+    step) -> LM head -> next token, 64 tokens from zero states."""
+    emb_np = gen.embedding(dims, seed=0)
+    emb = Dv.DeviceEmbedding(emb_np)
+    V, D = emb_np.vocab, dims.d_model
+    y = torch.from_numpy(gen.token_inputs(dims, (1,), 0, tag=30)).cuda()   # any fp32 row: the head quantizes it per token
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = Dv.workspace(dims, L.DFSSM_OP_LM_HEAD, 1)
+    calls = 200
+    wall, launch_ms = timed(lambda: [Dv.lm_head(dims, emb, y, None, nxt, ws) for _ in range(calls)],
+                            max(1, min(args.steps, 3)), 1, torch)
+    avg_s = sum(launch_ms) / len(launch_ms) / 1e3 / calls
+    head_bytes = V * D + 4 * V + 4 * D + 4
+    ach = head_bytes / avg_s / 1e9
+    out = {"metric": "LM head (tied int8, 50,280 x 2,048) batch 1: achieved HBM GB/s vs peak",
+           "value": round(ach, 2), "unit": "GB/s", "us_per_call": round(avg_s * 1e6, 3),
+           "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBS, 5), "traffic": None,
+                        "kernel": "k_lm_head + k_argmax (one call)", "algorithmic_bytes_per_launch": head_bytes,
+                        "avg_launch_us": round(avg_s * 1e6, 3)}}
+    # greedy decode of the whole model
+    nL, T = args.layers, 64
+    conv = torch.zeros((nL, 1, dims.conv_dim, dims.d_conv - 1), dtype=torch.float32, device="cuda")
+    ssm = torch.zeros((nL, 1, dims.nheads, dims.headdim, dims.d_state), dtype=torch.float32, device="cuda")
+    states = [Dv.DeviceState.from_tensors(conv[l], ssm[l], dims, 1) for l in range(nL)]
+    fw = torch.ones(D, dtype=torch.float32, device="cuda")
+    tok = torch.from_numpy(gen.token_ids(1, V, seed=0, tag=31)).cuda()
+    toks = torch.empty((T, 4), dtype=torch.int32, device="cuda")   # one 16-byte slot per token
+    x = torch.empty((1, D), dtype=torch.float32, device="cuda")
+    yd = torch.empty((1, 1, D), dtype=torch.float32, device="cuda")
+    wsd = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
+
+    def greedy():
+        conv.zero_()
+        ssm.zero_()
+        t = tok
+        for i in range(T):
+            Dv.embed(emb, t, x)
+            Dv.stack_decode(dims, layers, states, fw, x, yd, 1, wsd)
+            Dv.lm_head(dims, emb, yd[0], None, toks[i], ws)
+            t = toks[i, :1]
+
+    gw, g_ms = timed(greedy, max(1, min(args.steps, 2)), 1, torch)
+    if Dv.stack_status(wsd) != L.DFSSM_STATUS_OK:
+        raise SystemExit("greedy decode: stack status")
+    per_tok = bytes_per_token(dims, nL)["token_total"] + head_bytes + 4 * D
+    g_avg = sum(g_ms) / len(g_ms) / 1e3
+    out["greedy_full_model"] = {"metric": "greedy decode tokens/s batch=1, embedding + 48 layers + tied LM head",
+                                "value": round(T / g_avg, 2), "unit": "tokens/s", "tokens_per_step": T,
+                                "bytes_per_token": per_tok,
+                                "roofline": {"bound": "hbm", "achieved": round(per_tok * T / g_avg / 1e9, 2),
+                                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                             "frac": round(per_tok * T / g_avg / 1e9 / HBM_PEAK_GBS, 5)},
+                                "note": "one stack-decode launch per token (host loop), no host sync inside the step"}
+    return out
+
+
 WORKLOADS = {"decode_b1": run_decode_b1, "prefill2048": run_prefill, "decode_b64": run_decode_b64,
-             "decode_sweep": run_decode_sweep}
+             "decode_sweep": run_decode_sweep, "lm_head": run_lm_head}
 
 
 def main() -> int:
@@ -428,11 +489,12 @@ def main() -> int:
     out = run_decode_b1(*common)
     if not args.no_secondary:
         sec = {}
-        for name in ("prefill2048", "decode_b64", "decode_sweep"):
+        for name in ("prefill2048", "decode_b64", "decode_sweep", "lm_head"):
             r = WORKLOADS[name](*common)
             torch.cuda.empty_cache()
             sec[name] = {k: r[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",
-                                           "roofline_scaffold_gemms", "points", "cpu_baseline") if k in r}
+                                           "roofline_scaffold_gemms", "points", "us_per_call",
+                                           "greedy_full_model", "cpu_baseline") if k in r}
         out["secondary"] = sec
     print(json.dumps(out), flush=True)
     return 0

@@ -20,6 +20,7 @@ DFSSM_NOALLOC_SCRATCH_BYTES = 16 << 20
 DFSSM_OP_LAYER_PREFILL = 1
 DFSSM_OP_STACK_DECODE = 2
 DFSSM_OP_STACK_PREFILL = 3
+DFSSM_OP_LM_HEAD = 4
 
 DFSSM_STACK_STATUS_OFFSET = 0
 DFSSM_STATUS_OK = 0
@@ -34,7 +35,8 @@ DFSSM_BF16 = 1
 
 # every symbol include/dfssm.h declares
 EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_decode_noalloc", "dfssm_layer_prefill",
-           "dfssm_stack_decode", "dfssm_stack_decode_ex", "dfssm_stack_prefill", "dfssm_strerror")
+           "dfssm_stack_decode", "dfssm_stack_decode_ex", "dfssm_stack_prefill", "dfssm_embed", "dfssm_lm_head",
+           "dfssm_strerror")
 
 
 class dfssm_dims(C.Structure):
@@ -70,6 +72,14 @@ class dfssm_taps(C.Structure):
 
 class dfssm_stack_opts(C.Structure):
     _fields_ = [("path", C.c_int32), ("reserved", C.c_int32)]
+
+
+class dfssm_embedding(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("row_scale", C.c_void_p), ("vocab", C.c_int32), ("d_model", C.c_int32)]
+
+
+class dfssm_head_taps(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("s", C.c_void_p), ("acc", C.c_void_p)]
 
 
 _lib = None
@@ -111,6 +121,11 @@ def load() -> C.CDLL:
                                         C.POINTER(dfssm_layer_state), C.c_int32, P, P, C.c_int32, P,
                                         C.c_int32, C.c_int32, C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
     lib.dfssm_stack_prefill.restype = C.c_int
+    lib.dfssm_embed.argtypes = [C.POINTER(dfssm_embedding), P, C.c_int32, P, P]
+    lib.dfssm_embed.restype = C.c_int
+    lib.dfssm_lm_head.argtypes = [C.POINTER(dfssm_embedding), P, C.c_int32, P, P, P, C.c_size_t,
+                                  C.POINTER(dfssm_head_taps), P]
+    lib.dfssm_lm_head.restype = C.c_int
     lib.dfssm_strerror.argtypes = [C.c_int]
     lib.dfssm_strerror.restype = C.c_char_p
     _lib = lib
@@ -158,6 +173,14 @@ def dfssm_stack_prefill(dims, layers, states, n_layers, final_norm_w, x_in, x_dt
                         ws_bytes, taps=None, stream=None) -> int:
     return int(load().dfssm_stack_prefill(C.byref(dims), layers, states, n_layers, final_norm_w, x_in, x_dtype, y,
                                           batch, seqlen, chunk, ws, ws_bytes, _ref(taps), stream))
+
+
+def dfssm_embed(emb, tokens, batch, x, stream=None) -> int:
+    return int(load().dfssm_embed(C.byref(emb), tokens, batch, x, stream))
+
+
+def dfssm_lm_head(emb, y, batch, logits, next_tokens, ws, ws_bytes, taps=None, stream=None) -> int:
+    return int(load().dfssm_lm_head(C.byref(emb), y, batch, logits, next_tokens, ws, ws_bytes, _ref(taps), stream))
 
 
 def dfssm_strerror(status: int) -> str:

@@ -243,6 +243,9 @@ size_t dfssm_workspace_bytes(const dfssm_dims *dims, int32_t op, int32_t batch, 
         case DFSSM_OP_LAYER_PREFILL:
             if (!prefill_size_ok(s, batch, seqlen)) return 0;
             return prefill_ws_any_chunk(s, batch, seqlen);
+        case DFSSM_OP_LM_HEAD:
+            if (batch > 4096) return 0;
+            return head_ws_bytes(batch);
         case DFSSM_OP_STACK_PREFILL:
             if (n_layers <= 0 || !prefill_size_ok(s, batch, seqlen)) return 0;
             return stack_prefill_hbuf_bytes(s, batch, seqlen) + prefill_ws_any_chunk(s, batch, seqlen);
@@ -389,6 +392,36 @@ int dfssm_stack_prefill(const dfssm_dims *dims, const dfssm_layer_weights *layer
         if (e != hipSuccess) return DFSSM_EHIP;
     }
     return hip_status(launch_final_norm(y, final_norm_w, y, nullptr, s.D, s.eps, (int)per_layer, st));
+}
+
+static int check_embedding(const dfssm_embedding *e) {
+    if (!e || bad_ptr(e->codes) || bad_ptr(e->row_scale) || e->vocab <= 0 || e->d_model <= 0) return DFSSM_EINVAL;
+    if (e->d_model % 128 || e->d_model > kMaxK || e->vocab > (1 << 24)) return DFSSM_EUNSUPPORTED;
+    return DFSSM_OK;
+}
+
+int dfssm_embed(const dfssm_embedding *emb, const int32_t *tokens, int32_t batch, float *x, void *stream) {
+    int r;
+    if ((r = check_embedding(emb))) return r;
+    if (bad_ptr(tokens) || bad_ptr(x) || batch <= 0) return DFSSM_EINVAL;
+    if (batch > 4096) return DFSSM_EUNSUPPORTED;
+    return hip_status(launch_embed(emb->codes, emb->row_scale, emb->vocab, emb->d_model, tokens, batch, x,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int dfssm_lm_head(const dfssm_embedding *emb, const float *y, int32_t batch, float *logits, int32_t *next_tokens,
+                  void *ws, size_t ws_bytes, const dfssm_head_taps *taps, void *stream) {
+    int r;
+    if ((r = check_embedding(emb))) return r;
+    if (bad_ptr(y) || batch <= 0 || bad_opt_ptr(logits) || bad_opt_ptr(next_tokens)) return DFSSM_EINVAL;
+    if (!logits && !next_tokens) return DFSSM_EINVAL;
+    if (taps && (bad_opt_ptr(taps->q) || bad_opt_ptr(taps->s) || bad_opt_ptr(taps->acc))) return DFSSM_EINVAL;
+    if (batch > 4096) return DFSSM_EUNSUPPORTED;
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255)) return DFSSM_EINVAL;
+    if (ws_bytes < head_ws_bytes(batch)) return DFSSM_EWORKSPACE;
+    const HeadTaps t{taps ? taps->q : nullptr, taps ? taps->s : nullptr, taps ? taps->acc : nullptr};
+    return hip_status(launch_lm_head(emb->codes, emb->row_scale, emb->vocab, emb->d_model, y, batch, logits,
+                                     next_tokens, ws, t, static_cast<hipStream_t>(stream)));
 }
 
 const char *dfssm_strerror(int status) {

@@ -147,6 +147,18 @@ hipError_t launch_layer_decode_mfma(const Shape &s, const dfssm_layer_weights &w
                                     const PrefillWs &pws, const TapPtrs &taps, hipStream_t stream);
 bool decode_uses_mfma(const Shape &s, int batch);
 
+// Tied int8 embedding and LM head (head.hip).
+struct HeadTaps {
+    int8_t *q;      // [batch][D] the head's int8 codes of y
+    float *s;       // [batch] their scale
+    int32_t *acc;   // [batch][V] integer row sums
+};
+size_t head_ws_bytes(int batch);
+hipError_t launch_lm_head(const int8_t *codes, const float *row_scale, int V, int D, const float *y, int batch,
+                          float *logits, int32_t *next_tokens, void *ws, const HeadTaps &taps, hipStream_t stream);
+hipError_t launch_embed(const int8_t *codes, const float *row_scale, int V, int D, const int32_t *tokens, int batch,
+                        float *x, hipStream_t stream);
+
 // Enqueue y = RMSNorm(h) * w for `batch` rows of length D, also copying y to `y2` when non-null.
 hipError_t launch_final_norm(const float *h, const float *w, float *y, float *y2, int D, float eps,
                              int batch, hipStream_t stream);

@@ -173,3 +173,34 @@ def layer_prefill(d, layer: DeviceLayer, state: DeviceState, x_in: torch.Tensor,
                                batch, seqlen, chunk, ws.data_ptr(), ws.numel(),
                                None if taps is None else taps.struct, stream_handle())
     L.check(st, "dfssm_layer_prefill")
+
+
+class DeviceEmbedding:
+    """Device copy of the tied int8 embedding (keeps the tensors alive) and its C struct."""
+
+    def __init__(self, emb, device="cuda"):
+        self.codes = _dev(emb.codes, device)
+        self.row_scale = _dev(np.asarray(emb.row_scale, np.float32), device)
+        self.vocab, self.d_model = emb.codes.shape
+        self.struct = L.dfssm_embedding(self.codes.data_ptr(), self.row_scale.data_ptr(), self.vocab, self.d_model)
+
+
+def embed(emb: DeviceEmbedding, tokens: torch.Tensor, x: torch.Tensor) -> None:
+    """x [batch][d_model] fp32 = the embedding rows of tokens (int32 device tensor)."""
+    L.check(L.dfssm_embed(emb.struct, tokens.data_ptr(), tokens.numel(), x.data_ptr(), stream_handle()), "dfssm_embed")
+
+
+def lm_head(d, emb: DeviceEmbedding, y: torch.Tensor, logits: torch.Tensor = None, next_tokens: torch.Tensor = None,
+            ws: torch.Tensor = None, taps: dict = None) -> torch.Tensor:
+    """Logits and/or greedy next tokens of y [batch][d_model]; returns the workspace it used."""
+    batch = y.shape[0]
+    if ws is None:
+        ws = workspace(d, L.DFSSM_OP_LM_HEAD, batch)
+    t = None
+    if taps is not None:
+        t = L.dfssm_head_taps(*[taps[k].data_ptr() if k in taps else None for k in ("q", "s", "acc")])
+    st = L.dfssm_lm_head(emb.struct, y.data_ptr(), batch, None if logits is None else logits.data_ptr(),
+                         None if next_tokens is None else next_tokens.data_ptr(), ws.data_ptr(), ws.numel(), t,
+                         stream_handle())
+    L.check(st, "dfssm_lm_head")
+    return ws

@@ -260,6 +260,46 @@ int dfssm_stack_prefill(const dfssm_dims *dims, const dfssm_layer_weights *layer
                         int32_t batch, int32_t seqlen, int32_t chunk, void *ws, size_t ws_bytes,
                         const dfssm_taps *taps, void *stream);
 
+/*
+ * The tied int8 embedding / LM head ([DF-SSM] §3.3: the embedding is quantized to int8 per row;
+ * Table 1: "Embedding + LM head (tied)", 103 MB for the 1.3B model):
+ *   weight[v][k] = codes[v][k] * row_scale[v]
+ *   codes [vocab][d_model] int8 row-major; row_scale [vocab] fp32.
+ * Supported: d_model a multiple of 128 up to 8192; 1 <= vocab <= 1<<24.
+ */
+typedef struct dfssm_embedding {
+    const int8_t *codes;
+    const float  *row_scale;
+    int32_t vocab, d_model;
+} dfssm_embedding;
+
+/* Optional taps of dfssm_lm_head (any member may be NULL): q [batch][d_model] int8 and s [batch]
+ * fp32, the head's codes of y; acc [batch][vocab] int32, the integer row sums. */
+typedef struct dfssm_head_taps {
+    int8_t  *q;
+    float   *s;
+    int32_t *acc;
+} dfssm_head_taps;
+
+/* x[b] = weight[tokens[b]] (fp32 [batch][d_model]); tokens [batch] int32 on the device (ids outside
+ * [0, vocab) are clamped into it). 1 <= batch <= 4096. No workspace. */
+int dfssm_embed(const dfssm_embedding *emb, const int32_t *tokens, int32_t batch, float *x, void *stream);
+
+/*
+ * The tied LM head over y [batch][d_model] fp32 (the stack's normalised output, dfssm_stack_decode's
+ * y[t]): per token the same int8 quantizer as the projections, (q, s) = Qz(y[b]), then
+ *   acc[v] = sum_k codes[v][k] q[k] (int32),  logits[b][v] = s * row_scale[v] * acc[v]
+ * and next_tokens[b] = the v of the largest logit (the smallest v among equal logits).
+ *   logits [batch][vocab] fp32 and next_tokens [batch] int32 may each be NULL (not both);
+ *   ws: dfssm_workspace_bytes(dims, DFSSM_OP_LM_HEAD, batch, 0, 0) bytes (dims.d_model == d_model).
+ * Every byte of the embedding is read once per call of up to 8 tokens (an HBM-bound GEMV).
+ * 1 <= batch <= 4096.
+ */
+#define DFSSM_OP_LM_HEAD 4
+int dfssm_lm_head(const dfssm_embedding *emb, const float *y, int32_t batch, float *logits,
+                  int32_t *next_tokens, void *ws, size_t ws_bytes, const dfssm_head_taps *taps,
+                  void *stream);
+
 /* Static, human-readable text of a status code. */
 const char *dfssm_strerror(int status);
 
