@@ -32,10 +32,13 @@ namespace dfssm {
 
 namespace {
 
-constexpr int F2_MAXI = 8;    // in_proj rows per GEMV thread (after the B/C rows): rows rg + NG * i
+// in_proj rows per GEMV thread after the B/C rows (rows rg + NG * i): with CPR lanes per row
+// (CPR = d_model / 128) the items of the supported shapes hold at most 80, 48 or 32 such rows
+constexpr int f2_maxi(int cpr) { return cpr >= 16 ? 5 : cpr >= 8 ? 2 : 1; }
 constexpr int F2_SBLK = 8;    // 1 KB blocks of in_proj sign rows each wave copies per layer
 constexpr int F2_UPC = 2;     // LoRA-up chunks (16 B) per row: rank <= 32
-constexpr int F2_MAXO = 4;    // out_proj sign chunks per thread
+// out_proj rows per GEMV thread: a role-2 workgroup holds d_model / 128 rows
+constexpr int f2_maxo(int cpr) { return cpr >= 32 ? 2 : 1; }
 constexpr int F2_FPT = 4;     // SSM state float4s per thread and token
 constexpr int F2_ROWS = 512;  // item rows (incl. padding rows) per workgroup, at most
 constexpr unsigned kSpin2 = 1u << 21;
@@ -476,8 +479,10 @@ __device__ __forceinline__ float finish_row(const RowRegs<NB> &R, int b, int acc
     return silu_f(pre);
 }
 
-template <int NB, int KCH1, int KCH2>
+template <int NB, int KCH1, int KCH2, int CPR1, int CPR2>
 __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
+    constexpr int F2_MAXI = f2_maxi(CPR1), F2_MAXO = f2_maxo(CPR2);
+    constexpr int NG1 = kBlock / CPR1, NG2 = kBlock / CPR2;
     extern __shared__ __align__(16) char smem[];
     __shared__ float red[3 * kWaves];
     __shared__ int ired[NB * kWaves];
@@ -508,7 +513,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         const int q = a.q, bc0 = wg * q;
         const bool pad_rows = wg == 0 && T.in_acc != nullptr;
         const int R1t = a.R1 + (pad_rows ? a.npad : 0), nrest = R1t - q;
-        const int CPR1 = D >> 7, NG1 = kBlock / CPR1, c1 = tid % CPR1, rg1 = tid / CPR1;
+        const int c1 = tid % CPR1, rg1 = tid / CPR1;
         const int C16_1 = D >> 4;
         const int N4 = N >> 2, nf = a.pr * N4;
         // the lane that completes a B/C row's sum also finishes that row; thread r finishes rest row q + r
@@ -783,7 +788,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     // ========================================================================== role 2
     const int w2 = wg - a.n1, n_out0 = w2 * a.R2;
     const int R2t = max(0, min(a.R2, D - n_out0));
-    const int CPR2 = E >> 7, NG2 = kBlock / CPR2, c2 = tid % CPR2, rg2 = tid / CPR2;
+    const int c2 = tid % CPR2, rg2 = tid / CPR2;
     const int C16_2 = E >> 4;
     const bool tap2 = w2 == 0;
     char *sgn2 = wreg;
@@ -959,30 +964,29 @@ bool f2_plan(const Shape &s, int batch, int slots, F2Plan &p) {
     p.R1 = p.q + 2 * p.pr + 1;
     p.npad = s.Ninp - s.Nin;
     const int CPR1 = s.D >> 7, NG1 = kBlock / CPR1, rest = p.R1 + p.npad - p.q;
-    if (p.q > NG1 || rest > NG1 * F2_MAXI || rest > kBlock || rest > F2_ROWS) return false;
+    if (p.q > NG1 || rest > NG1 * f2_maxi(CPR1) || rest > kBlock || rest > F2_ROWS) return false;
     if ((p.R1 + p.npad) * CPR1 > F2_SBLK * kWaves * 64) return false;
     const int avail = slots - p.n1;
     if (avail < 1) return false;
     p.R2 = (s.D + avail - 1) / avail;
     p.n2 = (s.D + p.R2 - 1) / p.R2;
-    if (p.R2 > kBlock || p.R2 > (kBlock / (s.E >> 7)) * F2_MAXO) return false;
+    if (p.R2 > kBlock || p.R2 > (kBlock / (s.E >> 7)) * f2_maxo(s.E >> 7)) return false;
     const int nf = p.pr * (s.N / 4);
     p.fpt = (nf + kBlock - 1) / kBlock;
     if (p.fpt > F2_FPT) return false;
     return f2_lds_base(s, batch) + f2_wreg_bytes(s, p.R1 + p.npad, p.R2) <= kF2MaxLds;
 }
 
-int f2_kch(int K) { return K <= 1024 ? 1 : K / 1024; }
 
-template <int NB, int KCH1, int KCH2>
+template <int NB, int KCH1, int KCH2, int CPR1, int CPR2>
 hipError_t f2_launch(F2Args &a, const Shape &s, hipStream_t stream) {
     const size_t lds = f2_lds_base(s, NB) + f2_wreg_bytes(s, a.R1 + a.npad, a.R2);
     void *args[] = {&a};
-    const void *fn = reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2>);
+    const void *fn = reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2, CPR1, CPR2>);
     return hipLaunchCooperativeKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
 }
 
-template <int NB, int KCH1, int KCH2>
+template <int NB, int KCH1, int KCH2, int CPR1, int CPR2>
 int f2_resident() {
     static std::atomic<int> memo[kMaxDevices2];
     int dev = 0;
@@ -992,7 +996,7 @@ int f2_resident() {
     int ncu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     // with the largest LDS a supported shape may use (registers bound the occupancy to one per CU anyway)
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2, CPR1, CPR2>),
                                                      kBlock, kF2MaxLds) != hipSuccess)
         return 0;
     v = per_cu * ncu;
@@ -1000,21 +1004,26 @@ int f2_resident() {
     return v;
 }
 
-// The (D, E = 2D) shapes the kernel is built for: KCH1 = D / 1024, KCH2 = E / 1024 (at least 1).
-// D = 4096 would mean 128 heads, whose items hold more rows than the GEMV loop takes (f2_plan).
+// The (D, E = 2D) shapes the kernel is built for: KCH1 = D / 1024, KCH2 = E / 1024 (at least 1),
+// CPR = lanes per sign row (D / 128, E / 128). D = 4096 would mean 128 heads, whose items hold more
+// rows than the GEMV loop takes (f2_plan).
 int f2_slots(const Shape &s, int batch) {
     if (batch != 1 || s.E != 2 * s.D) return 0;
-    switch (f2_kch(s.D)) {
-    case 1: return f2_kch(s.E) == 1 ? f2_resident<1, 1, 1>() : f2_resident<1, 1, 2>();
-    case 2: return f2_resident<1, 2, 4>();
+    switch (s.D) {
+    case 256: return f2_resident<1, 1, 1, 2, 4>();
+    case 512: return f2_resident<1, 1, 1, 4, 8>();
+    case 1024: return f2_resident<1, 1, 2, 8, 16>();
+    case 2048: return f2_resident<1, 2, 4, 16, 32>();
     default: return 0;
     }
 }
 
 hipError_t f2_launch_any(F2Args &a, const Shape &s, hipStream_t stream) {
-    switch (f2_kch(s.D)) {
-    case 1: return f2_kch(s.E) == 1 ? f2_launch<1, 1, 1>(a, s, stream) : f2_launch<1, 1, 2>(a, s, stream);
-    case 2: return f2_launch<1, 2, 4>(a, s, stream);
+    switch (s.D) {
+    case 256: return f2_launch<1, 1, 1, 2, 4>(a, s, stream);
+    case 512: return f2_launch<1, 1, 1, 4, 8>(a, s, stream);
+    case 1024: return f2_launch<1, 1, 2, 8, 16>(a, s, stream);
+    case 2048: return f2_launch<1, 2, 4, 16, 32>(a, s, stream);
     default: return hipErrorInvalidConfiguration;
     }
 }
