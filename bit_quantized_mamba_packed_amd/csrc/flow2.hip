@@ -375,16 +375,25 @@ __device__ __forceinline__ void lds_copy_contig(char *dst, const char *src, int 
     }
 }
 
+// sum_j L_up[n][j] * v[j] over the (at most 32) low-rank terms; v (16-byte aligned LDS) is read as
+// eight 16-byte vectors before the first product, so the reads are in flight together.
 __device__ __forceinline__ float up_dot2(const int4 (&w)[F2_UPC], int rank, const float *v) {
+    float4 vv[4 * F2_UPC];
+#pragma unroll
+    for (int i = 0; i < 4 * F2_UPC; ++i) vv[i] = reinterpret_cast<const float4 *>(v)[i];
     float lr = 0.f;
 #pragma unroll
     for (int i = 0; i < F2_UPC; ++i) {
         // no rank test: past the rank both the weights (zero-padded) and v (zeroed) are zero
         const int ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) lr += (float)(int8_t)(ws[q] >> (8 * k)) * v[i * 16 + 4 * q + k];
+        for (int q = 0; q < 4; ++q) {
+            const float4 x = vv[4 * i + q];
+            lr += (float)(int8_t)(ws[q]) * x.x;
+            lr += (float)(int8_t)(ws[q] >> 8) * x.y;
+            lr += (float)(int8_t)(ws[q] >> 16) * x.z;
+            lr += (float)(int8_t)(ws[q] >> 24) * x.w;
+        }
     }
     return lr;
 }
@@ -628,10 +637,16 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     uint4 pl[8];
 #pragma unroll
                     for (int p = 0; p < 8; ++p) pl[p] = *reinterpret_cast<const uint4 *>(spl + (b * 8 + p) * G32 + c1 * 4);
+                    // every sign chunk is read before the first is used: the B/C row's and the item's
+                    // other rows' (rows past the item's end are read clamped and their sums dropped)
+                    const uint4 bcbits = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(rg1, q - 1) * (D >> 3) + c1 * 16);
+                    uint4 bits[F2_MAXI];
+                    int pos[F2_MAXI];
+#pragma unroll
+                    for (int i = 0; i < F2_MAXI; ++i)
+                        bits[i] = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(q + rg1 + NG1 * i, R1t - 1) * (D >> 3) + c1 * 16);
                     {
-                        const int r = min(rg1, q - 1);
-                        int pos = chunk_pos(*reinterpret_cast<const uint4 *>(sgn1 + (size_t)r * (D >> 3) + c1 * 16), pl);
-                        pos = dpp_group_sum(pos, CPR1);
+                        const int pos = dpp_group_sum(chunk_pos(bcbits, pl), CPR1);
                         if (bc_lane && rb.m.ch != -2) {
                             const int acc = 2 * pos - sqsum[b];
                             const float act = finish_row(rb, b, acc, ssc[b], tv + b * 64, a.Rin, Ly.st.conv, a.Cd);
@@ -639,16 +654,8 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                             if (T.in_acc) T.in_acc[(rec + b) * a.Ninp + rb.m.n] = acc;
                         }
                     }
-                    // every sign chunk is read before the first is used (the row count is uniform)
-                    uint4 bits[F2_MAXI];
-                    int pos[F2_MAXI];
 #pragma unroll
-                    for (int i = 0; i < F2_MAXI; ++i)
-                        if (NG1 * i < nrest)
-                            bits[i] = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(q + rg1 + NG1 * i, R1t - 1) * (D >> 3) + c1 * 16);
-#pragma unroll
-                    for (int i = 0; i < F2_MAXI; ++i)
-                        if (NG1 * i < nrest) pos[i] = dpp_group_sum(chunk_pos(bits[i], pl), CPR1);
+                    for (int i = 0; i < F2_MAXI; ++i) pos[i] = dpp_group_sum(chunk_pos(bits[i], pl), CPR1);
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i) {
                         const int r = rg1 + NG1 * i;
@@ -871,15 +878,12 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                 uint4 bits[F2_MAXO];
 #pragma unroll
                 for (int i = 0; i < F2_MAXO; ++i)
-                    if (NG2 * i < a.R2)
-                        bits[i] = *reinterpret_cast<const uint4 *>(sgn2 + (size_t)min(rg2 + NG2 * i, max(R2t - 1, 0)) * (E >> 3) + c2 * 16);
+                    bits[i] = *reinterpret_cast<const uint4 *>(sgn2 + (size_t)min(rg2 + NG2 * i, max(R2t - 1, 0)) * (E >> 3) + c2 * 16);
 #pragma unroll
                 for (int i = 0; i < F2_MAXO; ++i) {
-                    if (NG2 * i < a.R2) {
-                        const int r = rg2 + NG2 * i;
-                        const int pos = dpp_group_sum(chunk_pos(bits[i], pl), CPR2);
-                        if (c2 == CPR2 - 1 && r < R2t) accl[b * F2_ROWS + r] = 2 * pos - sqsum[b];
-                    }
+                    const int r = rg2 + NG2 * i;
+                    const int pos = dpp_group_sum(chunk_pos(bits[i], pl), CPR2);
+                    if (c2 == CPR2 - 1 && r < R2t) accl[b * F2_ROWS + r] = 2 * pos - sqsum[b];
                 }
             }
         }
