@@ -163,6 +163,24 @@ __device__ __forceinline__ void code_planes(const uint32_t (&pk)[KCH], uint32_t 
     }
 }
 
+// Sum over groups of w consecutive lanes (w a power of two <= 64, uniform across the wave but not
+// known at compile time), total in the group's last lane: every DPP step runs and the steps past w
+// add zero, so the reduction has no branches.
+template <int CTRL, int RMASK, bool BC>
+__device__ __forceinline__ float f2_dpp_step(float v, int keep) {
+    const int d = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, RMASK, 0xF, BC);
+    return v + __builtin_bit_cast(float, d & keep);
+}
+__device__ __forceinline__ float f2_group_sum(float v, int w) {
+    v = f2_dpp_step<0xB1, 0xF, true>(v, -(w >= 2));
+    v = f2_dpp_step<0x4E, 0xF, true>(v, -(w >= 4));
+    v = f2_dpp_step<0x114, 0xF, true>(v, -(w >= 8));
+    v = f2_dpp_step<0x118, 0xF, true>(v, -(w >= 16));
+    v = f2_dpp_step<0x142, 0xA, false>(v, -(w >= 32));
+    v = f2_dpp_step<0x143, 0xC, false>(v, -(w >= 64));
+    return v;
+}
+
 __device__ __forceinline__ float f2_ss(const float4 &v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
 
 // The stack's final RMSNorm, (h * r) * w, of one gathered vector: the thread layout and the order of
@@ -715,9 +733,8 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             }
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
-                if (i >= a.fpt) break;
                 const int f = tid + kBlock * i;
-                const bool ok = f < nf;
+                const bool ok = i < a.fpt && f < nf;
                 const int p = ok ? f / N4 : 0;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
@@ -734,7 +751,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     v.w = dA * v.w + dtx * Bn.w;
                     st[i][b] = v;
                     float part = ok ? (v.x * Cn.x + v.y * Cn.y) + (v.z * Cn.z + v.w * Cn.w) : 0.f;
-                    part = dpp_group_sum_f(part, N4);
+                    part = f2_group_sum(part, N4);
                     if (ok && n4 == N4 - 1) {
                         const float gv = (part + Dh * x) * zs[i][b];
                         st_x(gxl + (int64_t)b * E + h * P + p0 + p, tag2(fbits2(gv), tag));
