@@ -108,10 +108,35 @@ __device__ __forceinline__ float bitsf2(uint32_t b) { return __builtin_bit_cast(
 
 __device__ void f2_error(const F2Args &a) { __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
+// One coherent (sc1) 16-byte load of two tagged words, waited for inside the same asm block.
+__device__ __forceinline__ u32x4 f2_load_chunk(const uint64_t *p) {
+    u32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=&v"(r) : "v"(p) : "memory");
+    return r;
+}
+
 // This thread's 4*KCH consecutive words at p, reloaded until every epoch equals `tag` (bounded).
+// With `light`, the thread first polls only its first two words (its words come from one producer,
+// which stores them together) and reads all of them once those carry the epoch: for a wait that
+// starts long before the data exists, this keeps the polling of every waiting workgroup from
+// loading the fabric that the producers' own traffic and the final reads need.
 template <int KCH>
-__device__ __forceinline__ void f2_gather(const F2Args &a, const uint64_t *p, uint32_t tag, u32x4 (&r)[2 * KCH]) {
+__device__ __forceinline__ void f2_gather(const F2Args &a, const uint64_t *p, uint32_t tag, u32x4 (&r)[2 * KCH],
+                                          bool light = false) {
     unsigned spins = 0;
+    if (KCH > 1 && light) {
+        for (;;) {
+            const u32x4 c = f2_load_chunk(p);
+            if (c.y == tag && c.w == tag) break;
+            __builtin_amdgcn_s_sleep(kSleep2);
+            ++spins;
+            if ((spins & 63) == 0 && ld_x(a.err)) return;
+            if (spins > kSpin2) {
+                f2_error(a);
+                return;
+            }
+        }
+    }
     for (;;) {
         load_words_sc1<KCH>(p, r);
         bool ok = true;
@@ -209,7 +234,7 @@ template <int NB, int KCH>
 __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t tag, const float4 (&wr)[KCH],
                             const float *pre_w, float *pre_out, int8_t *sq, uint32_t *spl, int (&qsum)[NB],
                             float (&scale)[NB], float *red, int *ired, bool tapwg, float *r0_out, float *tap_h,
-                            float *tap_u, int8_t *tap_q, float *tap_s) {
+                            float *tap_u, int8_t *tap_q, float *tap_s, bool light = false) {
     const int tid = threadIdx.x;
     const int e0 = prologue_elem<KCH>(0);
     const bool mine = e0 < K;   // K is a multiple of 4*KCH: a thread has all of its chunks or none
@@ -217,7 +242,7 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
         float4 hv[KCH];
         if (mine) {
             u32x4 r[2 * KCH];
-            f2_gather<KCH>(a, X + (int64_t)b * K + e0, tag, r);
+            f2_gather<KCH>(a, X + (int64_t)b * K + e0, tag, r, light);
 #pragma unroll
             for (int i = 0; i < KCH; ++i)
                 hv[i] = make_float4(bitsf2(r[2 * i].x), bitsf2(r[2 * i].z), bitsf2(r[2 * i + 1].x), bitsf2(r[2 * i + 1].z));
@@ -514,6 +539,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     __shared__ float red[3 * kWaves];
     __shared__ int ired[NB * kWaves];
     __shared__ float dtl[NB];
+    __shared__ float gsh[NB][64];   // the item's gated outputs, published by one coalesced store
     int sqsum[NB];
     float ssc[NB];
     __shared__ float r0s;
@@ -752,13 +778,16 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     st[i][b] = v;
                     float part = ok ? (v.x * Cn.x + v.y * Cn.y) + (v.z * Cn.z + v.w * Cn.w) : 0.f;
                     part = f2_group_sum(part, N4);
-                    if (ok && n4 == N4 - 1) {
-                        const float gv = (part + Dh * x) * zs[i][b];
-                        st_x(gxl + (int64_t)b * E + h * P + p0 + p, tag2(fbits2(gv), tag));
-                    }
+                    if (ok && n4 == N4 - 1) gsh[b][p] = (part + Dh * x) * zs[i][b];
                 }
             }
-            // the new state goes out after the gated outputs, so that those are not queued behind it
+            // the gated outputs go out as one store of pr consecutive words (whole cache lines: the
+            // item's slot starts on a 256-byte boundary), then the new state
+            __syncthreads();
+            if (tid < a.pr) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) st_x(gxl + (int64_t)b * E + h * P + p0 + tid, tag2(fbits2(gsh[b][tid]), tag));
+            }
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
                 const int f = tid + kBlock * i;
@@ -869,7 +898,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         __syncthreads();
         f2_prologue<NB, KCH2>(a, gxl, E, tag, wr, nullptr, nullptr, sq, spl, sqsum, ssc, red, ired, tap2, nullptr,
                               nullptr, T.out_u ? T.out_u + rec * E : nullptr, T.out_q ? T.out_q + rec * E : nullptr,
-                              T.out_s ? T.out_s + rec : nullptr);
+                              T.out_s ? T.out_s + rec : nullptr, true);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             int part[4];
