@@ -13,7 +13,9 @@
 //            those rows of h (it keeps them: they are its next residual input)
 // Each exchange (h, B/C, g) is an all-gather of tagged 64-bit words {payload, epoch}, written with
 // agent-coherent stores and read with 16-byte agent-coherent loads until every epoch matches;
-// there are no flags and no barriers. Every layer has its own word slots, rewritten one token
+// there are no flags and no barriers. The h and g producers write their words as whole 128-byte
+// lines in one store instruction (a role-2 workgroup's 16 rows of h; an item's gated outputs,
+// staged in LDS first): coherent stores of partial lines take microseconds longer to be visible. Every layer has its own word slots, rewritten one token
 // later; every workgroup reads all of a layer's words before anything of the next token's same
 // layer can be produced, so a slot is never rewritten while a reader still needs it.
 //
