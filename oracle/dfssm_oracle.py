@@ -37,6 +37,13 @@ What each function follows and what pins it (the pins live in tests/test_oracle_
   layer_tokens      the same steps run stage by stage over the sequence (batched projections).
                     pinned by: equals layer_decode_steps (codes, integer sums and floats)
   table1_bytes      [DF-SSM] §3.3 Table 1.  pinned by the table's printed sizes
+  state_codec_*     [DF-SSM] §3.4 (density field state: mean +- 3 sigma normalisation, first-order
+                    sigma-delta with an 8-bit accumulator, threshold 0.5, popcount readout) and App. D
+                    (K = 23 for d_state 128, K^2 ~ 4 d_state), reading R19.  pinned by: constant rows
+                    read back exactly; the sigma-delta density within one cell of each value; the
+                    accumulator bounds; the field sizes App. D prints
+  ssd_chunked       with codec=True: the carried state passes through the codec at every chunk
+                    boundary (DF-SSD, §3.4 / App. D).  pinned by: codec off equals the plain scan
   embed             [DF-SSM] §3.3 (int8 embedding, per-row scale), Table 1 (103 MB, tied).
                     pinned by: Table 1's embedding size; rows by explicit indexing
   lm_head           the tied head over the same int8 rows (Table 1 "Embedding + LM head (tied)")
@@ -60,7 +67,15 @@ Readings where the page is silent (also listed in the design doc):
   R18 the tied LM head reads the stack's normalised output y through the same per-token int8
       quantizer as the projections: logits[v] = s * row_scale[v] * sum_k codes[v,k] q[k] (an
       integer contraction like the scaffold's); the argmax takes the smallest index among equal
-      maxima.
+      maxima;
+  R19 the density field of §3.4 covers one state row (the d_state values of one (head, channel)):
+      K = round(sqrt(4 d_state)) (23 for 128, App. D), value i owns cells floor(i K^2/N) up to
+      floor((i+1) K^2/N) of the K x K field in raster order; mu and sigma are the row's mean and
+      population standard deviation (fp32, summed in element order); x = clamp((s - (mu - 3 sigma))
+      / (6 sigma), 0, 1) is taken to 8 bits, t = rint(255 x); the first-order sigma-delta runs over
+      the cells in raster order with an int8 error e: v = e + t, bit = (v >= 128), e = v - 255 bit;
+      the readout is mu - 3 sigma + 6 sigma * popcount(value's cells) / cells. A row with sigma = 0
+      reads back as mu.
 """
 from __future__ import annotations
 
@@ -352,7 +367,7 @@ def ssm_scan_sequential(xs, dts, A, Bs, Cs, D, S0, ngroups: int):
     return ys, S
 
 
-def ssd_chunked(xs, dts, A, Bs, Cs, D, S0, ngroups: int, chunk: int):
+def ssd_chunked(xs, dts, A, Bs, Cs, D, S0, ngroups: int, chunk: int, codec: bool = False):
     """Chunked evaluation of the same recurrence ([SSD] state-space-duality block form).
 
     Within a chunk, with Lam_t = sum_{tau <= t in chunk} dt_tau A (per head):
@@ -360,7 +375,9 @@ def ssd_chunked(xs, dts, A, Bs, Cs, D, S0, ngroups: int, chunk: int):
           + exp(Lam_t) C_t . S_prev                                      (carried state)
           + D x_t
       S_end = exp(Lam_end) S_prev + sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s
-    Exponentials are always of differences of Lam (never ratios of exponentials)."""
+    Exponentials are always of differences of Lam (never ratios of exponentials).
+    With codec, the state carried into every chunk after the first passes through the density
+    field codec first (DF-SSD: the codec at chunk boundaries, [DF-SSM] §3.4, App. D)."""
     xs = np.asarray(xs, F64)
     dts = np.asarray(dts, F64)
     A = np.asarray(A, F64)
@@ -372,6 +389,8 @@ def ssd_chunked(xs, dts, A, Bs, Cs, D, S0, ngroups: int, chunk: int):
     ys = np.empty((T, H, P))
     for c0 in range(0, T, chunk):
         c1 = min(T, c0 + chunk)
+        if codec and c0 > 0:
+            S = state_codec_roundtrip(S.astype(F32))
         a = dts[c0:c1] * A[None, :]                      # [Q][H]
         lam = np.cumsum(a, axis=0)                       # inclusive
         Q = c1 - c0
@@ -450,3 +469,78 @@ def argmax_first(v) -> int:
     """Index of the largest value, the smallest such index when several are equal (R18)."""
     v = np.asarray(v)
     return int(np.flatnonzero(v == v.max())[0])
+
+
+# ----------------------------------------------------------------------------- density field state codec
+def codec_field_side(d_state: int) -> int:
+    """K of the K x K field: K^2 ~ 4 d_state ([DF-SSM] App. D), K = round(sqrt(4 d_state))."""
+    return int(round((4 * d_state) ** 0.5))
+
+
+def codec_cells(d_state: int) -> np.ndarray:
+    """cells[i] .. cells[i+1]: the cells of value i in raster order (R19)."""
+    K2 = codec_field_side(d_state) ** 2
+    return np.array([(i * K2) // d_state for i in range(d_state + 1)], np.int64)
+
+
+def state_codec_stats(row) -> tuple:
+    """(mu, sigma) of one state row in fp32, summed in element order (R19)."""
+    r = np.asarray(row, F32)
+    acc = F32(0)
+    for v in r:
+        acc = F32(acc + v)
+    mu = F32(acc / F32(r.size))
+    acc2 = F32(0)
+    for v in r:
+        d = F32(v - mu)
+        acc2 = F32(acc2 + F32(d * d))
+    sigma = F32(np.sqrt(F32(acc2 / F32(r.size))))
+    return mu, sigma
+
+
+def state_codec_encode_row(row, mu=None, sigma=None) -> tuple:
+    """Density field of one state row ([DF-SSM] §3.4 steps 1-3, R19): returns (bits uint8 [K*K], mu,
+    sigma). mu/sigma may be given (e.g. decided elsewhere in the same fp32 arithmetic)."""
+    r = np.asarray(row, F32)
+    N = r.size
+    if mu is None:
+        mu, sigma = state_codec_stats(r)
+    mu, sigma = F32(mu), F32(sigma)
+    cells = codec_cells(N)
+    bits = np.zeros(cells[-1], np.uint8)
+    if sigma == F32(0):
+        return bits, mu, sigma
+    lo = F32(mu - F32(F32(3) * sigma))
+    span = F32(F32(6) * sigma)
+    x = np.clip(((r - lo).astype(F32) / span).astype(F32), F32(0), F32(1))   # step 1: mu +- 3 sigma -> [0, 1]
+    t = np.rint((x * F32(255)).astype(F32)).astype(np.int64)                   # 8-bit target per value
+    e = 0                                                                       # 8-bit error accumulator
+    for i in range(N):
+        for c in range(cells[i], cells[i + 1]):                                # step 2: first-order sigma-delta
+            v = e + int(t[i])
+            b = 1 if v >= 128 else 0                                            # step 3: threshold at 0.5
+            e = v - 255 * b
+            bits[c] = b
+    return bits, mu, sigma
+
+
+def state_codec_decode_row(bits, mu, sigma, d_state: int) -> np.ndarray:
+    """Readout ([DF-SSM] §3.4 step 4): popcount density of each value's cells, back through the
+    normalisation. Returns fp64 [d_state]."""
+    cells = codec_cells(d_state)
+    mu, sigma = F64(F32(mu)), F64(F32(sigma))
+    if sigma == 0:
+        return np.full(d_state, mu)
+    dens = np.array([np.sum(bits[cells[i]:cells[i + 1]]) / (cells[i + 1] - cells[i]) for i in range(d_state)])
+    return (mu - 3 * sigma) + 6 * sigma * dens
+
+
+def state_codec_roundtrip(S) -> np.ndarray:
+    """Encode then decode every row of a state [..., d_state] (fp64 out)."""
+    S = np.asarray(S, F32)
+    flat = S.reshape(-1, S.shape[-1])
+    out = np.empty(flat.shape)
+    for k in range(flat.shape[0]):
+        bits, mu, sigma = state_codec_encode_row(flat[k])
+        out[k] = state_codec_decode_row(bits, mu, sigma, flat.shape[1])
+    return out.reshape(S.shape)

@@ -480,3 +480,91 @@ def test_lm_head_brute_force_dense_and_argmax():
     c2[30], s2[30] = c2[17], s2[17]
     l3, _, _, _ = O.lm_head(y, c2, s2)
     assert O.argmax_first(l3) == 17
+
+
+# ------------------------------------------------------------------ density field state codec
+def test_codec_field_sizes_from_appendix_d():
+    # App. D: K = 23 (a 529-cell field) for d_state 128, and K^2 ~ 4 d_state in general
+    assert O.codec_field_side(128) == 23 and O.codec_field_side(128) ** 2 == 529
+    for n in (16, 32, 64, 128, 256):
+        K = O.codec_field_side(n)
+        assert abs(K * K - 4 * n) <= 2 * K + 1
+        cells = O.codec_cells(n)
+        assert cells[0] == 0 and cells[-1] == K * K and (np.diff(cells) >= 3).all()
+        assert np.diff(cells).max() - np.diff(cells).min() <= 1          # cells spread evenly
+
+
+def test_codec_constant_and_flat_rows():
+    for n in (16, 128):
+        # a constant row whose fp32 mean is exact: sigma = 0, read back exactly
+        row = np.full(n, 0.375, np.float32)
+        bits, mu, sigma = O.state_codec_encode_row(row)
+        assert sigma == 0 and not bits.any()
+        np.testing.assert_array_equal(O.state_codec_decode_row(bits, mu, sigma, n), np.float32(0.375))
+        # any constant row reads back to within the rounding of its fp32 mean
+        row = np.full(n, 0.37, np.float32)
+        bits, mu, sigma = O.state_codec_encode_row(row)
+        np.testing.assert_allclose(O.state_codec_decode_row(bits, mu, sigma, n), 0.37, rtol=2e-6)
+
+
+def test_codec_sigma_delta_density_and_accumulator():
+    """Every value's cell density is within one cell of its 8-bit target (the first-order error
+    feedback carries the rest), the error accumulator fits 8 bits, and the density summed over the
+    whole field is within one cell of the summed targets (no drift)."""
+    rng = np.random.default_rng(60)
+    n = 128
+    cells = O.codec_cells(n)
+    for trial in range(5):
+        row = (rng.standard_normal(n) * rng.uniform(0.01, 3)).astype(np.float32)
+        bits, mu, sigma = O.state_codec_encode_row(row)
+        lo, span = np.float32(mu - np.float32(3) * sigma), np.float32(np.float32(6) * sigma)
+        x = np.clip(((row - lo) / span).astype(np.float32), 0, 1)
+        t = np.rint(x * np.float32(255)).astype(np.int64)
+        # brute-force the accumulator path independently of the encoder's loop structure
+        e, emin, emax, k = 0, 0, 0, 0
+        for i in range(n):
+            for _ in range(cells[i + 1] - cells[i]):
+                v = e + t[i]
+                assert bits[k] == (1 if v >= 128 else 0)
+                e = v - 255 * bits[k]
+                emin, emax = min(emin, e), max(emax, e)
+                k += 1
+        assert -128 <= emin and emax <= 127
+        ncell = np.diff(cells)
+        for i in range(n):
+            dens = bits[cells[i]:cells[i + 1]].sum()
+            assert abs(dens - t[i] * ncell[i] / 255) <= 1.0 + 1e-9 + 1, (i, dens, t[i])
+        assert abs(bits.sum() - (t * ncell).sum() / 255) <= 1.0 + 1e-9
+        # the readout lands within one cell's share of the [mu - 3 sigma, mu + 3 sigma] range, and
+        # inside it, for values that were inside it
+        dec = O.state_codec_decode_row(bits, mu, sigma, n)
+        inside = (row >= lo) & (row <= lo + span)
+        assert (dec >= lo - 1e-6).all() and (dec <= lo + span + 1e-6).all()
+        assert np.mean(np.abs(dec - row)[inside]) < float(span) / 4
+
+
+def test_codec_stats_are_the_row_mean_and_std():
+    rng = np.random.default_rng(61)
+    row = rng.standard_normal(128).astype(np.float32)
+    mu, sigma = O.state_codec_stats(row)
+    assert abs(float(mu) - float(np.mean(row.astype(np.float64)))) < 1e-6
+    assert abs(float(sigma) - float(np.std(row.astype(np.float64)))) < 1e-6
+
+
+def test_dfssd_codec_off_is_the_plain_scan_and_on_stays_close():
+    rng = np.random.default_rng(62)
+    T, H, P, N, G = 80, 2, 3, 16, 1
+    xs = rng.standard_normal((T, H, P))
+    dts = rng.uniform(1e-3, 0.2, (T, H))
+    A = -rng.uniform(1, 16, H)
+    Bs, Cs = rng.standard_normal((T, G, N)), rng.standard_normal((T, G, N))
+    D = rng.standard_normal(H)
+    S0 = rng.standard_normal((H, P, N)) * 0.5
+    y0, S_0 = O.ssd_chunked(xs, dts, A, Bs, Cs, D, S0, G, 16)
+    y1, S_1 = O.ssd_chunked(xs, dts, A, Bs, Cs, D, S0, G, 16, codec=False)
+    np.testing.assert_array_equal(y0, y1)
+    yc, S_c = O.ssd_chunked(xs, dts, A, Bs, Cs, D, S0, G, 16, codec=True)
+    # the first chunk never sees the codec
+    np.testing.assert_array_equal(yc[:16], y0[:16])
+    assert not np.array_equal(yc[16:], y0[16:])
+    assert np.linalg.norm(yc - y0) / np.linalg.norm(y0) < 0.5
