@@ -439,8 +439,39 @@ def run_lm_head(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     return out
 
 
+def run_state_codec(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
+    """Density field codec of one 1.3B layer's SSM state at batch 64 (262,144 rows of 128 fp32 ->
+    23 x 23 bit fields + mu, sigma): encode and decode timed apart, each against HBM."""
+    B = 64
+    _, S = gen.initial_states(dims, B, seed=0, std=0.1)
+    ssm = torch.from_numpy(S).cuda()
+    back = torch.empty_like(ssm)
+    fields, stats = Dv.state_encode(dims, ssm, B)
+    rows = B * dims.nheads * dims.headdim
+    W = L.dfssm_state_field_words(dims.d_state)
+    state_b, code_b = rows * dims.d_state * 4, rows * (4 * W + 8)
+    calls = 20
+    res = {}
+    for name, fn in (("encode", lambda: Dv.state_encode(dims, ssm, B)),
+                     ("decode", lambda: Dv.state_decode(dims, fields, stats, B, back))):
+        wall, ms = timed(lambda: [fn() for _ in range(calls)], max(1, min(args.steps, 3)), 1, torch)
+        avg_s = sum(ms) / len(ms) / 1e3 / calls
+        ach = (state_b + code_b) / avg_s / 1e9
+        res[name] = {"us_per_call": round(avg_s * 1e6, 3), "achieved": round(ach, 2),
+                     "frac": round(ach / HBM_PEAK_GBS, 5)}
+    enc = res["encode"]
+    return {"metric": "density field state codec, 1.3B layer state at batch 64: encode HBM GB/s",
+            "value": enc["achieved"], "unit": "GB/s", "us_per_call": enc["us_per_call"],
+            "config": {"workload": "state_codec_1p3b_b64", "rows": rows, "d_state": dims.d_state,
+                       "field_words": W, "state_bytes": state_b, "code_bytes": code_b},
+            "roofline": {"bound": "hbm", "achieved": enc["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": enc["frac"], "traffic": None, "kernel": "k_state_encode",
+                         "algorithmic_bytes_per_launch": state_b + code_b, "avg_launch_us": enc["us_per_call"]},
+            "decode": res["decode"]}
+
+
 WORKLOADS = {"decode_b1": run_decode_b1, "prefill2048": run_prefill, "decode_b64": run_decode_b64,
-             "decode_sweep": run_decode_sweep, "lm_head": run_lm_head}
+             "decode_sweep": run_decode_sweep, "lm_head": run_lm_head, "state_codec": run_state_codec}
 
 
 def main() -> int:
@@ -489,12 +520,12 @@ def main() -> int:
     out = run_decode_b1(*common)
     if not args.no_secondary:
         sec = {}
-        for name in ("prefill2048", "decode_b64", "decode_sweep", "lm_head"):
+        for name in ("prefill2048", "decode_b64", "decode_sweep", "lm_head", "state_codec"):
             r = WORKLOADS[name](*common)
             torch.cuda.empty_cache()
             sec[name] = {k: r[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",
                                            "roofline_scaffold_gemms", "points", "us_per_call",
-                                           "greedy_full_model", "cpu_baseline") if k in r}
+                                           "greedy_full_model", "cpu_baseline", "decode") if k in r}
         out["secondary"] = sec
     print(json.dumps(out), flush=True)
     return 0

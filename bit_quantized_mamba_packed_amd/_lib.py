@@ -36,7 +36,7 @@ DFSSM_BF16 = 1
 # every symbol include/dfssm.h declares
 EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_decode_noalloc", "dfssm_layer_prefill",
            "dfssm_stack_decode", "dfssm_stack_decode_ex", "dfssm_stack_prefill", "dfssm_embed", "dfssm_lm_head",
-           "dfssm_strerror")
+           "dfssm_state_field_words", "dfssm_state_encode", "dfssm_state_decode", "dfssm_strerror")
 
 
 class dfssm_dims(C.Structure):
@@ -126,6 +126,12 @@ def load() -> C.CDLL:
     lib.dfssm_lm_head.argtypes = [C.POINTER(dfssm_embedding), P, C.c_int32, P, P, P, C.c_size_t,
                                   C.POINTER(dfssm_head_taps), P]
     lib.dfssm_lm_head.restype = C.c_int
+    lib.dfssm_state_field_words.argtypes = [C.c_int32]
+    lib.dfssm_state_field_words.restype = C.c_int32
+    lib.dfssm_state_encode.argtypes = [C.POINTER(dfssm_dims), P, C.c_int32, P, P, P]
+    lib.dfssm_state_encode.restype = C.c_int
+    lib.dfssm_state_decode.argtypes = [C.POINTER(dfssm_dims), P, P, C.c_int32, P, P]
+    lib.dfssm_state_decode.restype = C.c_int
     lib.dfssm_strerror.argtypes = [C.c_int]
     lib.dfssm_strerror.restype = C.c_char_p
     _lib = lib
@@ -181,6 +187,18 @@ def dfssm_embed(emb, tokens, batch, x, stream=None) -> int:
 
 def dfssm_lm_head(emb, y, batch, logits, next_tokens, ws, ws_bytes, taps=None, stream=None) -> int:
     return int(load().dfssm_lm_head(C.byref(emb), y, batch, logits, next_tokens, ws, ws_bytes, _ref(taps), stream))
+
+
+def dfssm_state_field_words(d_state: int) -> int:
+    return int(load().dfssm_state_field_words(d_state))
+
+
+def dfssm_state_encode(dims, ssm, batch, fields, stats, stream=None) -> int:
+    return int(load().dfssm_state_encode(C.byref(dims), ssm, batch, fields, stats, stream))
+
+
+def dfssm_state_decode(dims, fields, stats, batch, ssm, stream=None) -> int:
+    return int(load().dfssm_state_decode(C.byref(dims), fields, stats, batch, ssm, stream))
 
 
 def dfssm_strerror(status: int) -> str:

@@ -424,6 +424,32 @@ int dfssm_lm_head(const dfssm_embedding *emb, const float *y, int32_t batch, flo
                                      next_tokens, ws, t, static_cast<hipStream_t>(stream)));
 }
 
+int32_t dfssm_state_field_words(int32_t d_state) { return codec_field_words(d_state); }
+
+int dfssm_state_encode(const dfssm_dims *dims, const float *ssm, int32_t batch, uint32_t *fields, float *stats,
+                       void *stream) {
+    int r;
+    if ((r = check_dims(dims))) return r;
+    if (bad_ptr(ssm) || bad_ptr(fields) || bad_ptr(stats) || batch <= 0) return DFSSM_EINVAL;
+    if (batch > 4096) return DFSSM_EUNSUPPORTED;
+    const Shape s = shape_of(*dims);
+    if (codec_field_words(s.N) == 0) return DFSSM_EUNSUPPORTED;
+    return hip_status(launch_state_encode(ssm, (int64_t)batch * s.H * s.P, s.N, fields, stats,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int dfssm_state_decode(const dfssm_dims *dims, const uint32_t *fields, const float *stats, int32_t batch, float *ssm,
+                       void *stream) {
+    int r;
+    if ((r = check_dims(dims))) return r;
+    if (bad_ptr(ssm) || bad_ptr(fields) || bad_ptr(stats) || batch <= 0) return DFSSM_EINVAL;
+    if (batch > 4096) return DFSSM_EUNSUPPORTED;
+    const Shape s = shape_of(*dims);
+    if (codec_field_words(s.N) == 0) return DFSSM_EUNSUPPORTED;
+    return hip_status(launch_state_decode(fields, stats, (int64_t)batch * s.H * s.P, s.N, ssm,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 const char *dfssm_strerror(int status) {
     switch (status) {
         case DFSSM_OK: return "success";

@@ -1,0 +1,256 @@
+// Density field codec of the SSM state ([DF-SSM] §3.4 "Density Field State Representation", App. D
+// "Density Field Configuration"): each state row (the d_state values of one head channel) becomes
+// a K x K bit field with K^2 ~ 4 d_state (K = 23 for d_state 128) plus its mean and standard
+// deviation:
+//   1. normalisation: x = clamp((s - (mu - 3 sigma)) / (6 sigma), 0, 1), taken to 8 bits t = rint(255 x)
+//   2. first-order sigma-delta over the cells in raster order, value i owning cells
+//      floor(i K^2 / N) .. floor((i+1) K^2 / N): v = e + t_i, bit = (v >= 128), e = v - 255 bit,
+//      e an 8-bit accumulator (it stays in [-128, 127])
+//   3. threshold at 0.5 (128 of 256)
+//   4. readout: s' = mu - 3 sigma + 6 sigma * popcount(value's cells) / cells (a row with sigma = 0
+//      reads back as mu)
+// The sigma-delta pass is sequential along a row, so one lane owns one row and holds it in
+// registers; the kernels are templated on d_state so that every value-to-cell boundary is a
+// compile-time constant and the whole row is straight-line code (no indexed register arrays).
+// Global traffic goes through a small LDS tile per wave so that each load or store instruction
+// covers whole 128-byte lines: state rows move 32 columns at a time (a [64][33] float tile, odd
+// stride so that the 64 lanes walking their rows hit distinct banks) and the fields of the wave's
+// 64 consecutive rows, which are contiguous in memory, move as one coalesced block.
+#include "decode_device.h"
+
+namespace dfssm {
+
+namespace {
+
+constexpr int kCodecRows = 64;   // rows per workgroup (one wave, one row per lane)
+
+constexpr int codec_side(int n) {
+    // K = round(sqrt(4 n)) for the supported n (16, 32, 64, 128, 256): 8, 11, 16, 23, 32
+    return n == 16 ? 8 : n == 32 ? 11 : n == 64 ? 16 : n == 128 ? 23 : n == 256 ? 32 : 0;
+}
+constexpr int codec_words(int n) { return (codec_side(n) * codec_side(n) + 31) / 32; }
+
+// First cell of value i (value i owns cells cell_begin(i) .. cell_begin(i + 1) - 1).
+template <int N>
+constexpr int cell_begin(int i) {
+    return (i * codec_side(N) * codec_side(N)) / N;
+}
+
+// Staging geometry: state columns move kT at a time through a [64][kT + 1] float tile (odd
+// stride: the 64 lanes walking their own rows hit distinct banks); the wave's fields sit in LDS as
+// [64][WS] words, WS the odd one of W, W + 1.
+template <int N>
+struct Tile {
+    static constexpr int kT = N < 32 ? N : 32;             // columns per pass
+    static constexpr int kStride = kT + 1;
+    static constexpr int kLpr = kT / 4;                     // lanes per row (one float4 each)
+    static constexpr int kRpp = kCodecRows / kLpr;          // rows per pass
+    static constexpr int W = codec_words(N);
+    static constexpr int WS = W | 1;
+    static constexpr int kFloats = kCodecRows * (kStride > WS ? kStride : WS);
+};
+
+// Rows [r0, r0 + nr) of N floats, columns [c0, c0 + kT): global -> tile[row][col]. Each pass
+// covers kRpp rows x kT * 4 contiguous bytes.
+template <int N>
+__device__ __forceinline__ void tile_load(const float *src, int64_t r0, int nr, int c0, float *tile) {
+    using T = Tile<N>;
+#pragma unroll
+    for (int p = 0; p < kCodecRows / T::kRpp; ++p) {
+        const int rr = p * T::kRpp + (int)threadIdx.x / T::kLpr, cc = ((int)threadIdx.x % T::kLpr) * 4;
+        if (rr < nr) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + (r0 + rr) * N + c0 + cc);
+            float *d = tile + rr * T::kStride + cc;
+            d[0] = v.x;
+            d[1] = v.y;
+            d[2] = v.z;
+            d[3] = v.w;
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void tile_store(float *dst, int64_t r0, int nr, int c0, const float *tile) {
+    using T = Tile<N>;
+#pragma unroll
+    for (int p = 0; p < kCodecRows / T::kRpp; ++p) {
+        const int rr = p * T::kRpp + (int)threadIdx.x / T::kLpr, cc = ((int)threadIdx.x % T::kLpr) * 4;
+        if (rr < nr) {
+            const float *s = tile + rr * T::kStride + cc;
+            *reinterpret_cast<float4 *>(dst + (r0 + rr) * N + c0 + cc) = make_float4(s[0], s[1], s[2], s[3]);
+        }
+    }
+}
+
+template <int N>
+__global__ __launch_bounds__(kCodecRows) void k_state_encode(const float *__restrict__ ssm, int64_t rows,
+                                                            uint32_t *__restrict__ fields, float *__restrict__ stats) {
+#pragma clang fp contract(off)
+    using T = Tile<N>;
+    constexpr int K2 = codec_side(N) * codec_side(N), W = T::W;
+    __shared__ float lds[T::kFloats];
+    const int64_t r0 = (int64_t)blockIdx.x * kCodecRows;
+    const int nr = (int)min((int64_t)kCodecRows, rows - r0);
+    const int lane = threadIdx.x;
+
+    float v[N];
+#pragma unroll
+    for (int c0 = 0; c0 < N; c0 += T::kT) {
+        tile_load<N>(ssm, r0, nr, c0, lds);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < T::kT; ++j) v[c0 + j] = lds[lane * T::kStride + j];
+        __syncthreads();
+    }
+
+    // mean and population standard deviation, summed in element order
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc = acc + v[i];
+    const float mu = acc / (float)N;
+    float acc2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float d = v[i] - mu;
+        acc2 = acc2 + d * d;
+    }
+    const float sigma = sqrtf(acc2 / (float)N);
+    const float lo = mu - 3.0f * sigma, span = 6.0f * sigma;
+
+    // 8-bit codes, kept as t - 128 so that a cell's decision is the sign of e + (t - 128)
+    int tm[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float x = fminf(fmaxf((v[i] - lo) / span, 0.f), 1.f);
+        tm[i] = (int)rintf(x * 255.0f) - 128;
+    }
+
+    // sigma-delta over the cells; bits collected inverted (a set bit of `inv` is a 0 cell)
+    uint32_t word[W];
+    int e = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) word[w] = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+#pragma unroll
+        for (int c = cell_begin<N>(i); c < cell_begin<N>(i + 1); ++c) {
+            const int u = e + tm[i];            // v - 128
+            const int neg = u >> 31;            // -1 where v < 128 (bit 0), else 0
+            e = u - 127 + (neg & 255);          // v - 255 * bit
+            word[c >> 5] |= (uint32_t)neg & (1u << (c & 31));
+        }
+    }
+    const bool flat = !(sigma != 0.f);   // sigma == 0: all-zero field, readout mu
+    constexpr uint32_t kTailMask = (K2 & 31) ? ((1u << (K2 & 31)) - 1u) : 0xffffffffu;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const uint32_t valid = (w == W - 1) ? kTailMask : 0xffffffffu;
+        lds[lane * T::WS + w] = __builtin_bit_cast(float, flat ? 0u : (~word[w] & valid));
+    }
+    if (lane < nr) *reinterpret_cast<float2 *>(stats + 2 * (r0 + lane)) = make_float2(mu, sigma);
+    __syncthreads();
+    // the wave's nr rows of fields are nr * W contiguous words
+    uint32_t *dst = fields + r0 * W;
+    for (int k = lane; k < nr * W; k += kCodecRows) {
+        const int rr = k / W, w = k - rr * W;
+        dst[k] = __builtin_bit_cast(uint32_t, lds[rr * T::WS + w]);
+    }
+}
+
+template <int N>
+__global__ __launch_bounds__(kCodecRows) void k_state_decode(const uint32_t *__restrict__ fields,
+                                                            const float *__restrict__ stats, int64_t rows,
+                                                            float *__restrict__ ssm) {
+    using T = Tile<N>;
+    constexpr int W = T::W;
+    __shared__ float lds[T::kFloats];
+    const int64_t r0 = (int64_t)blockIdx.x * kCodecRows;
+    const int nr = (int)min((int64_t)kCodecRows, rows - r0);
+    const int lane = threadIdx.x;
+
+    const uint32_t *srcw = fields + r0 * W;
+    for (int k = lane; k < nr * W; k += kCodecRows) {
+        const int rr = k / W, w = k - rr * W;
+        lds[rr * T::WS + w] = __builtin_bit_cast(float, srcw[k]);
+    }
+    float2 ms = make_float2(0.f, 0.f);
+    if (lane < nr) ms = *reinterpret_cast<const float2 *>(stats + 2 * (r0 + lane));
+    __syncthreads();
+    uint32_t word[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) word[w] = __builtin_bit_cast(uint32_t, lds[lane * T::WS + w]);
+    __syncthreads();
+
+    const float mu = ms.x, sigma = ms.y;
+    const float lo = mu - 3.0f * sigma, span = 6.0f * sigma;
+    const bool flat = !(sigma != 0.f);
+    float out[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int c0 = cell_begin<N>(i), c1 = cell_begin<N>(i + 1);
+        // cells c0 .. c1 - 1 span at most two words (a value owns fewer than 32 cells)
+        const int w0 = c0 >> 5, w1 = (c1 - 1) >> 5, b0 = c0 & 31;
+        int ones;
+        if (w0 == w1) {
+            const uint32_t m = (c1 - c0 == 32) ? 0xffffffffu : ((1u << (c1 - c0)) - 1u);
+            ones = __builtin_popcount((word[w0] >> b0) & m);
+        } else {
+            const int n1 = c1 - (w1 << 5);
+            ones = __builtin_popcount(word[w0] >> b0) + __builtin_popcount(word[w1] & ((1u << n1) - 1u));
+        }
+        const float dens = (float)ones * (1.0f / (float)(c1 - c0));
+        out[i] = flat ? mu : lo + span * dens;
+    }
+#pragma unroll
+    for (int c0 = 0; c0 < N; c0 += T::kT) {
+#pragma unroll
+        for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = out[c0 + j];
+        __syncthreads();
+        tile_store<N>(ssm, r0, nr, c0, lds);
+        __syncthreads();
+    }
+}
+
+template <int N>
+hipError_t encode_n(const float *ssm, int64_t rows, uint32_t *fields, float *stats, hipStream_t stream) {
+    const int64_t grid = (rows + kCodecRows - 1) / kCodecRows;
+    k_state_encode<N><<<(unsigned)grid, kCodecRows, 0, stream>>>(ssm, rows, fields, stats);
+    return hipGetLastError();
+}
+
+template <int N>
+hipError_t decode_n(const uint32_t *fields, const float *stats, int64_t rows, float *ssm, hipStream_t stream) {
+    const int64_t grid = (rows + kCodecRows - 1) / kCodecRows;
+    k_state_decode<N><<<(unsigned)grid, kCodecRows, 0, stream>>>(fields, stats, rows, ssm);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int codec_field_words(int d_state) { return codec_side(d_state) ? codec_words(d_state) : 0; }
+
+hipError_t launch_state_encode(const float *ssm, int64_t rows, int N, uint32_t *fields, float *stats,
+                               hipStream_t stream) {
+    switch (N) {
+    case 16: return encode_n<16>(ssm, rows, fields, stats, stream);
+    case 32: return encode_n<32>(ssm, rows, fields, stats, stream);
+    case 64: return encode_n<64>(ssm, rows, fields, stats, stream);
+    case 128: return encode_n<128>(ssm, rows, fields, stats, stream);
+    case 256: return encode_n<256>(ssm, rows, fields, stats, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_state_decode(const uint32_t *fields, const float *stats, int64_t rows, int N, float *ssm,
+                               hipStream_t stream) {
+    switch (N) {
+    case 16: return decode_n<16>(fields, stats, rows, ssm, stream);
+    case 32: return decode_n<32>(fields, stats, rows, ssm, stream);
+    case 64: return decode_n<64>(fields, stats, rows, ssm, stream);
+    case 128: return decode_n<128>(fields, stats, rows, ssm, stream);
+    case 256: return decode_n<256>(fields, stats, rows, ssm, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dfssm

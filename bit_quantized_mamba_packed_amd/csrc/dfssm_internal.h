@@ -159,6 +159,13 @@ hipError_t launch_lm_head(const int8_t *codes, const float *row_scale, int V, in
 hipError_t launch_embed(const int8_t *codes, const float *row_scale, int V, int D, const int32_t *tokens, int batch,
                         float *x, hipStream_t stream);
 
+// Density field codec of SSM state rows (codec.hip): rows of N = d_state floats.
+int codec_field_words(int d_state);   // 32-bit words of one row's K x K field (0: unsupported N)
+hipError_t launch_state_encode(const float *ssm, int64_t rows, int N, uint32_t *fields, float *stats,
+                               hipStream_t stream);
+hipError_t launch_state_decode(const uint32_t *fields, const float *stats, int64_t rows, int N, float *ssm,
+                               hipStream_t stream);
+
 // Enqueue y = RMSNorm(h) * w for `batch` rows of length D, also copying y to `y2` when non-null.
 hipError_t launch_final_norm(const float *h, const float *w, float *y, float *y2, int D, float eps,
                              int batch, hipStream_t stream);

@@ -204,3 +204,19 @@ def lm_head(d, emb: DeviceEmbedding, y: torch.Tensor, logits: torch.Tensor = Non
                          stream_handle())
     L.check(st, "dfssm_lm_head")
     return ws
+
+
+def state_encode(d, ssm: torch.Tensor, batch: int):
+    """Density field codec of an SSM state [batch][H][P][N] -> (fields uint32 [rows][W], stats [rows][2])."""
+    rows = batch * d.nheads * d.headdim
+    W = L.dfssm_state_field_words(d.d_state)
+    fields = torch.empty((rows, W), dtype=torch.int32, device=ssm.device)
+    stats = torch.empty((rows, 2), dtype=torch.float32, device=ssm.device)
+    L.check(L.dfssm_state_encode(dims_struct(d), ssm.data_ptr(), batch, fields.data_ptr(), stats.data_ptr(),
+                                 stream_handle()), "dfssm_state_encode")
+    return fields, stats
+
+
+def state_decode(d, fields: torch.Tensor, stats: torch.Tensor, batch: int, ssm: torch.Tensor) -> None:
+    L.check(L.dfssm_state_decode(dims_struct(d), fields.data_ptr(), stats.data_ptr(), batch, ssm.data_ptr(),
+                                 stream_handle()), "dfssm_state_decode")

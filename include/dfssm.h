@@ -300,6 +300,28 @@ int dfssm_lm_head(const dfssm_embedding *emb, const float *y, int32_t batch, flo
                   int32_t *next_tokens, void *ws, size_t ws_bytes, const dfssm_head_taps *taps,
                   void *stream);
 
+/*
+ * Density field codec of the SSM state ([DF-SSM] §3.4 "Density Field State Representation", App. D).
+ * Each state row (the d_state values of one head channel; batch*nheads*headdim rows, in the layout
+ * of dfssm_layer_state.ssm) is stored as a K x K bit field, K = round(sqrt(4*d_state)) (23 for
+ * d_state 128: 529 bits), plus its fp32 mean and population standard deviation:
+ *   x_i = clamp((s_i - (mu - 3 sigma)) / (6 sigma), 0, 1),  t_i = rint(255 x_i)  (8 bits)
+ *   value i owns cells floor(i K^2 / d_state) .. floor((i+1) K^2 / d_state) - 1 in raster order;
+ *   first-order sigma-delta over the cells with an 8-bit error e (starting at 0):
+ *     v = e + t_i;  bit = (v >= 128);  e = v - 255 * bit
+ *   readout: s'_i = mu - 3 sigma + 6 sigma * (ones among value i's cells) / (its cells);
+ *   a row with sigma = 0 has an all-zero field and reads back as mu.
+ *   fields [rows][dfssm_state_field_words(d_state)] uint32: cell c is bit c % 32 of word c / 32;
+ *   stats  [rows][2] fp32: mu, sigma.
+ * The state of the 1.3B layer (2 MiB per sequence) encodes to 4096 x (68 + 8) bytes = 304 KiB.
+ * Supported d_state: 16, 32, 64, 128, 256. 1 <= batch <= 4096. No workspace.
+ */
+int32_t dfssm_state_field_words(int32_t d_state);
+int dfssm_state_encode(const dfssm_dims *dims, const float *ssm, int32_t batch, uint32_t *fields,
+                       float *stats, void *stream);
+int dfssm_state_decode(const dfssm_dims *dims, const uint32_t *fields, const float *stats,
+                       int32_t batch, float *ssm, void *stream);
+
 /* Static, human-readable text of a status code. */
 const char *dfssm_strerror(int status);
 

@@ -243,3 +243,20 @@ def test_stack_workspace_covers_status_word_and_every_layer_step():
             layer = L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_DECODE, B)
             stack = L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_DECODE, B, 0, 3)
             assert stack >= layer + 256 + 2 * B * d.d_model * 4, (B, layer, stack)
+
+
+def test_state_codec_field_size_and_rejects_bad_arguments():
+    # K = round(sqrt(4 d_state)): 8, 11, 16, 23, 32 -> ceil(K^2 / 32) words
+    assert [L.dfssm_state_field_words(n) for n in (16, 32, 64, 128, 256)] == [2, 4, 8, 17, 32]
+    assert L.dfssm_state_field_words(100) == 0
+    d = _dims()
+    for fn in (lambda **k: L.dfssm_state_encode(k.get("dims", d), k.get("a", FAKE), k.get("batch", 1),
+                                                k.get("b", FAKE), k.get("c", FAKE)),
+               lambda **k: L.dfssm_state_decode(k.get("dims", d), k.get("b", FAKE), k.get("c", FAKE),
+                                                k.get("batch", 1), k.get("a", FAKE))):
+        assert fn(a=None) == L.DFSSM_EINVAL
+        assert fn(b=FAKE + 4) == L.DFSSM_EINVAL
+        assert fn(c=None) == L.DFSSM_EINVAL
+        assert fn(batch=0) == L.DFSSM_EINVAL
+        assert fn(batch=4097) == L.DFSSM_EUNSUPPORTED
+        assert fn(dims=_dims(d_state=100)) == L.DFSSM_EUNSUPPORTED
