@@ -49,6 +49,13 @@ What each function follows and what pins it (the pins live in tests/test_oracle_
   lm_head           the tied head over the same int8 rows (Table 1 "Embedding + LM head (tied)")
                     with the per-token quantizer (R18).  pinned by: brute force with Python ints;
                     the dequantised dense product; planted maxima for the argmax
+  dfw_quantize      [DF-SSM] §3.1 Eq. (1) (17 levels, K_w = 16), R20.  pinned by: the level set
+                    Eq. (3) prints; end points, zero and clamping; ties to even; idempotence,
+                    monotonicity and the half-step error bound
+  dfw_unpack_planes the 5-bit level index in five 1-bit planes (R20).  pinned by: pure-Python
+                    bit extraction
+  project_dfw       Eq. (3) with the 17-level scaffold (R20).  pinned by: brute force with
+                    Fractions; with only the end levels it equals the 1-bit project()
 
 Readings where the page is silent (also listed in the design doc):
   R1 scaffold values are +-1 times a per-output-row fp16 scale (the page's 1-bit storage; 1 bit
@@ -76,6 +83,12 @@ Readings where the page is silent (also listed in the design doc):
       the cells in raster order with an int8 error e: v = e + t, bit = (v >= 128), e = v - 255 bit;
       the readout is mu - 3 sigma + 6 sigma * popcount(value's cells) / cells. A row with sigma = 0
       reads back as mu.
+  R20 the 17-level scaffold (the pre-binarisation grid of §3.1 Eq. (1), K_w = 16) is stored as the
+      level index k = round(clamp((w + 1)/2, 0, 1) * 16) in [0, 16] (round half to even, as
+      torch.round), weight value (k - 8)/8 = 2k/16 - 1 times the row's fp16 scale (as in R1); the
+      5-bit index sits in five bit planes, plane b holding bit b of k in the 1-bit layout of R2;
+      the scaffold sum acc = sum_k (k - 8) q_k is an exact integer and y = s*sc*acc/8 + the
+      low-rank term of R5.
 """
 from __future__ import annotations
 
@@ -544,3 +557,46 @@ def state_codec_roundtrip(S) -> np.ndarray:
         bits, mu, sigma = state_codec_encode_row(flat[k])
         out[k] = state_codec_decode_row(bits, mu, sigma, flat.shape[1])
     return out.reshape(S.shape)
+
+
+# ----------------------------------------------------------------------------- 17-level DFW scaffold
+DFW_KW = 16                 # Eq. (1): K_w = 16 -> 17 levels
+DFW_PLANES = 5              # bits of the level index 0..16
+
+
+def dfw_quantize(w, K_w: int = DFW_KW) -> tuple:
+    """[DF-SSM] §3.1 Eq. (1): w_q = round(clamp((w + 1)/2, 0, 1) K_w) / K_w * 2 - 1 (R20).
+    Returns (w_q fp64, level index k int64 in [0, K_w]); round is half to even, in fp64."""
+    w = np.asarray(w, F64)
+    k = np.rint(np.clip((w + 1.0) / 2.0, 0.0, 1.0) * K_w)
+    return k / K_w * 2.0 - 1.0, k.astype(np.int64)
+
+
+def dfw_unpack_planes(planes: np.ndarray, n_in: int) -> np.ndarray:
+    """[5][n_out][n_in/8] uint8 bit planes -> level index k int64 [n_out][n_in] (R20, layout R2)."""
+    planes = np.asarray(planes, np.uint8)
+    k = np.zeros((planes.shape[1], n_in), np.int64)
+    for b in range(planes.shape[0]):
+        bits = np.unpackbits(planes[b], axis=1, bitorder="little")[:, :n_in].astype(np.int64)
+        k += bits << b
+    return k
+
+
+def project_dfw(q: np.ndarray, s, P, k: Optional[np.ndarray] = None) -> tuple:
+    """One projection of one token with the 17-level scaffold ([DF-SSM] §3.2 Eq. (3), R20, R5).
+
+    q int8 [n_in], s fp32; P has planes [5][n_out][n_in/8], row_scale, lora_dn, dn_scale, lora_up,
+    up_scale. Returns (y fp64 [n_out], acc int64 [n_out], t int64 [rank]):
+      acc[n] = sum_k (k[n,i] - 8) q[i]      (exact integer; weight value (k - 8)/8)
+      t[j]   = sum_i L_dn[j,i] q[i]
+      y[n]   = s*sc[n]*acc[n]/8 + us[n] * sum_j L_up[n,j] * ds[j] * s * t[j]
+    """
+    lev = dfw_unpack_planes(P.planes, P.n_in) if k is None else np.asarray(k, np.int64)
+    qf = np.asarray(q, F64)
+    acc = (lev - 8).astype(F64) @ qf          # integers below 2^53: exact
+    t = np.asarray(P.lora_dn, F64) @ qf
+    s64 = F64(F32(s))
+    sc = np.asarray(P.row_scale, np.float16).astype(F64)
+    v = np.asarray(P.dn_scale, F64) * s64 * t
+    y = s64 * sc * acc / 8.0 + np.asarray(P.up_scale, F64) * (np.asarray(P.lora_up, F64) @ v)
+    return y, acc.astype(np.int64), t.astype(np.int64)

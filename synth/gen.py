@@ -28,6 +28,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 import math
+from typing import Optional
 
 import numpy as np
 
@@ -244,3 +245,61 @@ def initial_states(dims: Dims, batch: int, layer: int = 0, seed: int = 0, std: f
     conv = (_rng(seed, layer, _STATE_TENSOR_BASE).standard_normal(cshape) * std).astype(np.float32)
     ssm = (_rng(seed, layer, _STATE_TENSOR_BASE + 1).standard_normal(sshape) * std).astype(np.float32)
     return conv, ssm
+
+
+@dataclass
+class DfwProjWeights:
+    """A projection with the 17-level scaffold: 5-bit level index in five bit planes.
+
+    planes    uint8 [5][n_out][n_in/8]  plane b holds bit b of the level index (0..16), each in the
+                                        1-bit layout (bit k % 8 of byte k/8)
+    row_scale, lora_dn, dn_scale, lora_up, up_scale as in ProjWeights
+    """
+    planes: np.ndarray
+    row_scale: np.ndarray
+    lora_dn: np.ndarray
+    dn_scale: np.ndarray
+    lora_up: np.ndarray
+    up_scale: np.ndarray
+
+    @property
+    def n_out(self) -> int:
+        return self.planes.shape[1]
+
+    @property
+    def n_in(self) -> int:
+        return self.planes.shape[2] * 8
+
+    @property
+    def rank(self) -> int:
+        return self.lora_dn.shape[0]
+
+
+_DFW_LAYER_KEY = 300000
+
+
+def pack_level_planes(levels: np.ndarray) -> np.ndarray:
+    """Level indices int [n_out][n_in] in [0, 16] -> uint8 [5][n_out][n_in/8] bit planes."""
+    lv = np.asarray(levels, np.int64)
+    return np.stack([np.packbits(((lv >> b) & 1).astype(np.uint8), axis=1, bitorder="little")
+                     for b in range(5)])
+
+
+def dfw_levels(n_out: int, n_in: int, seed: int = 0, tag: int = 0) -> np.ndarray:
+    """Seeded level indices, int64 [n_out][n_in]: Binomial(16, 1/2) (the middle levels most) mixed
+    with 1/8 uniform over 0..16, so that every one of the 17 levels, the end levels included,
+    occurs in any block of a few hundred weights."""
+    rng = _rng(seed, _DFW_LAYER_KEY, tag)
+    lv = rng.binomial(16, 0.5, size=(n_out, n_in))
+    uni = rng.integers(0, 17, size=(n_out, n_in))
+    return np.where(rng.random((n_out, n_in)) < 0.125, uni, lv).astype(np.int64)
+
+
+def dfw_proj(n_out: int, n_in: int, rank: int, seed: int = 0, levels: Optional[np.ndarray] = None) -> DfwProjWeights:
+    """Seeded 17-level projection (row scales, LoRA factors and scales drawn as for ProjWeights)."""
+    if levels is None:
+        levels = dfw_levels(n_out, n_in, seed)
+    base = _proj(lambda name: _rng(seed, _DFW_LAYER_KEY + 1, _T.get(name, 0) + 1000),
+                 "in", n_out, n_in, rank, per_channel=True)
+    return DfwProjWeights(pack_level_planes(levels), base.row_scale, base.lora_dn, base.dn_scale,
+                          base.lora_up, base.up_scale)

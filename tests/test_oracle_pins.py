@@ -568,3 +568,96 @@ def test_dfssd_codec_off_is_the_plain_scan_and_on_stays_close():
     np.testing.assert_array_equal(yc[:16], y0[:16])
     assert not np.array_equal(yc[16:], y0[16:])
     assert np.linalg.norm(yc - y0) / np.linalg.norm(y0) < 0.5
+
+
+# ------------------------------------------------------------------ 17-level DFW scaffold
+def test_dfw_levels_are_the_set_eq3_prints():
+    # Eq. (3): W_scaffold in {-1, -14/16, ..., 0, ..., 14/16, 1}: 17 values, step 2/16
+    w = np.linspace(-1.5, 1.5, 100001)
+    wq, k = O.dfw_quantize(w)
+    vals = sorted({Fraction(float(v)).limit_denominator(16) for v in wq})
+    assert vals == [Fraction(2 * i, 16) - 1 for i in range(17)]
+    assert set(k.tolist()) == set(range(17))
+    # value and index agree: w_q = 2k/16 - 1 = (k - 8)/8
+    assert np.array_equal(wq, (k - 8) / 8.0)
+
+
+def test_dfw_end_points_zero_clamp_and_ties():
+    wq, k = O.dfw_quantize([-1.0, 1.0, 0.0, -7.0, 3.5, 1.0 + 1e-9, -1.0 - 1e-9])
+    assert wq.tolist() == [-1.0, 1.0, 0.0, -1.0, 1.0, 1.0, -1.0]
+    assert k.tolist() == [0, 16, 8, 0, 16, 16, 0]
+    # (w + 1)/2 * 16 = j + 1/2 exactly at w = (2j + 1)/16 - 1: round half to even picks the even j
+    j = np.arange(16)
+    wt = (2 * j + 1) / 16.0 - 1.0
+    _, kt = O.dfw_quantize(wt)
+    assert kt.tolist() == [int(x) + (int(x) % 2) for x in j]
+    # just off the tie the nearer level wins
+    _, kp = O.dfw_quantize(wt + 1e-9)
+    assert kp.tolist() == (j + 1).tolist()
+
+
+def test_dfw_idempotent_monotone_and_half_step_error():
+    rng = np.random.default_rng(21)
+    w = np.sort(rng.uniform(-1.2, 1.2, 20000))
+    wq, _ = O.dfw_quantize(w)
+    assert np.array_equal(O.dfw_quantize(wq)[0], wq)
+    assert (np.diff(wq) >= 0).all()
+    inside = np.abs(w) <= 1
+    assert np.abs(wq - w)[inside].max() <= 1 / 16 + 1e-15
+
+
+def test_dfw_planes_match_pure_python_bit_extraction():
+    lv = gen.dfw_levels(3, 24, seed=2)
+    assert lv.min() >= 0 and lv.max() <= 16
+    planes = gen.pack_level_planes(lv)
+    assert planes.shape == (5, 3, 3)
+    k = O.dfw_unpack_planes(planes, 24)
+    for n in range(3):
+        for i in range(24):
+            v = sum(((int(planes[b, n, i // 8]) >> (i % 8)) & 1) << b for b in range(5))
+            assert k[n, i] == v == lv[n, i]
+
+
+def test_dfw_levels_generator_covers_all_17():
+    lv = gen.dfw_levels(64, 2048, seed=0)
+    assert set(np.unique(lv).tolist()) == set(range(17))
+
+
+def test_project_dfw_brute_force_exact():
+    P = gen.dfw_proj(5, 24, 3, seed=4)
+    rng = np.random.default_rng(6)
+    q = rng.integers(-127, 128, 24).astype(np.int8)
+    s = np.float32(0.0293)
+    y, acc, t = O.project_dfw(q, s, P)
+    S = Fraction(float(s))
+    for n in range(5):
+        a = Fraction(0)
+        for i in range(24):
+            k = sum(((int(P.planes[b, n, i // 8]) >> (i % 8)) & 1) << b for b in range(5))
+            a += (Fraction(2 * k, 16) - 1) * int(q[i])          # Eq. (1)'s level value times the code
+        assert acc[n] == 8 * a
+        exact = S * Fraction(float(P.row_scale[n])) * a
+        for j in range(3):
+            tj = sum(int(P.lora_dn[j, i]) * int(q[i]) for i in range(24))
+            assert t[j] == tj
+            exact += Fraction(float(P.up_scale[n])) * int(P.lora_up[n, j]) * Fraction(float(P.dn_scale[j])) * S * tj
+        assert abs(float(exact) - y[n]) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def test_project_dfw_end_levels_equal_the_one_bit_projection():
+    # a 17-level scaffold that only uses levels 0 and 16 (-1 and +1) is the 1-bit scaffold
+    P1 = _proj(12, 64, 4, seed=10)
+    bits = np.unpackbits(P1.sign, axis=1, bitorder="little")[:, :64].astype(np.int64)
+    Pd = gen.DfwProjWeights(gen.pack_level_planes(16 * bits), P1.row_scale, P1.lora_dn, P1.dn_scale,
+                            P1.lora_up, P1.up_scale)
+    rng = np.random.default_rng(11)
+    q = rng.integers(-127, 128, 64).astype(np.int8)
+    y1, acc1, t1 = O.project(q, np.float32(0.017), P1)
+    yd, accd, td = O.project_dfw(q, np.float32(0.017), Pd)
+    assert np.array_equal(accd, 8 * acc1) and np.array_equal(td, t1)
+    np.testing.assert_allclose(yd, y1, rtol=1e-13, atol=1e-15)
+    # and the middle level contributes nothing
+    P0 = gen.DfwProjWeights(gen.pack_level_planes(np.full((12, 64), 8)), P1.row_scale, P1.lora_dn,
+                            P1.dn_scale, P1.lora_up, P1.up_scale)
+    y0, acc0, _ = O.project_dfw(q, np.float32(0.017), P0)
+    assert (acc0 == 0).all()
