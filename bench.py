@@ -470,8 +470,42 @@ def run_state_codec(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dic
             "decode": res["decode"]}
 
 
+def run_dfw_proj(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
+    """The 17-level scaffold projection at batch 1 (decode) on the 1.3B in_proj (8,512 x 2,048) and
+    out_proj (2,048 x 4,096) shapes, rank 32: quantizer + five-plane GEMV + LoRA epilogue per call."""
+    res = {}
+    for name, n_out, n_in in (("in_proj", dims.n_in_proj, dims.d_model), ("out_proj", dims.d_model, dims.d_inner)):
+        P = gen.dfw_proj(n_out, n_in, dims.rank_in, seed=0)
+        dp = Dv.DeviceDfwProj(P)
+        pts = {}
+        for B in (1, 4):
+            x = torch.from_numpy(gen.token_inputs(gen.Dims(d_model=n_in, d_inner=n_in, d_state=16, headdim=64,
+                                                           ngroups=1, d_conv=4, n_in_proj=n_in, rank_in=8,
+                                                           rank_out=8), (B,), 0, tag=40)).cuda()
+            y = torch.empty((B, n_out), device="cuda")
+            ws = torch.empty(L.dfssm_dfw_workspace_bytes(n_in, P.rank, B), dtype=torch.uint8, device="cuda")
+            calls = 200
+            _, ms = timed(lambda: [Dv.dfw_project(dp, x, y, ws) for _ in range(calls)], max(1, min(args.steps, 3)), 1, torch)
+            avg_s = sum(ms) / len(ms) / 1e3 / calls
+            nbytes = (n_out * n_in * 5 // 8 + P.rank * n_in + n_out * P.rank + n_out * (2 + 4) + P.rank * 4
+                      + B * 4 * (n_in + n_out))
+            ach = nbytes / avg_s / 1e9
+            pts[f"B{B}"] = {"us_per_call": round(avg_s * 1e6, 3), "algorithmic_bytes": nbytes,
+                            "achieved_GBs": round(ach, 2), "frac": round(ach / HBM_PEAK_GBS, 5)}
+        res[name] = pts
+    top = res["in_proj"]["B1"]
+    return {"metric": "17-level scaffold projection, 1.3B in_proj at batch 1: achieved HBM GB/s",
+            "value": top["achieved_GBs"], "unit": "GB/s", "us_per_call": top["us_per_call"],
+            "config": {"workload": "dfw_proj_1p3b", "rank": dims.rank_in, "planes": 5},
+            "roofline": {"bound": "hbm", "achieved": top["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": top["frac"], "traffic": None, "kernel": "k_dfw_quant + k_dfw_gemv<1> (one call)",
+                         "algorithmic_bytes_per_launch": top["algorithmic_bytes"], "avg_launch_us": top["us_per_call"]},
+            "points": res}
+
+
 WORKLOADS = {"decode_b1": run_decode_b1, "prefill2048": run_prefill, "decode_b64": run_decode_b64,
-             "decode_sweep": run_decode_sweep, "lm_head": run_lm_head, "state_codec": run_state_codec}
+             "decode_sweep": run_decode_sweep, "lm_head": run_lm_head, "state_codec": run_state_codec,
+             "dfw_proj": run_dfw_proj}
 
 
 def main() -> int:
@@ -520,7 +554,7 @@ def main() -> int:
     out = run_decode_b1(*common)
     if not args.no_secondary:
         sec = {}
-        for name in ("prefill2048", "decode_b64", "decode_sweep", "lm_head", "state_codec"):
+        for name in ("prefill2048", "decode_b64", "decode_sweep", "lm_head", "state_codec", "dfw_proj"):
             r = WORKLOADS[name](*common)
             torch.cuda.empty_cache()
             sec[name] = {k: r[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",

@@ -36,7 +36,8 @@ DFSSM_BF16 = 1
 # every symbol include/dfssm.h declares
 EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_decode_noalloc", "dfssm_layer_prefill",
            "dfssm_stack_decode", "dfssm_stack_decode_ex", "dfssm_stack_prefill", "dfssm_embed", "dfssm_lm_head",
-           "dfssm_state_field_words", "dfssm_state_encode", "dfssm_state_decode", "dfssm_strerror")
+           "dfssm_state_field_words", "dfssm_state_encode", "dfssm_state_decode", "dfssm_dfw_workspace_bytes",
+           "dfssm_dfw_project", "dfssm_strerror")
 
 
 class dfssm_dims(C.Structure):
@@ -80,6 +81,15 @@ class dfssm_embedding(C.Structure):
 
 class dfssm_head_taps(C.Structure):
     _fields_ = [("q", C.c_void_p), ("s", C.c_void_p), ("acc", C.c_void_p)]
+
+
+class dfssm_dfw_proj(C.Structure):
+    _fields_ = [("planes", C.c_void_p), ("row_scale", C.c_void_p), ("lora_dn", C.c_void_p),
+                ("lora_dn_scale", C.c_void_p), ("lora_up", C.c_void_p), ("lora_up_scale", C.c_void_p)]
+
+
+class dfssm_dfw_taps(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("s", C.c_void_p), ("acc", C.c_void_p), ("t", C.c_void_p)]
 
 
 _lib = None
@@ -126,6 +136,11 @@ def load() -> C.CDLL:
     lib.dfssm_lm_head.argtypes = [C.POINTER(dfssm_embedding), P, C.c_int32, P, P, P, C.c_size_t,
                                   C.POINTER(dfssm_head_taps), P]
     lib.dfssm_lm_head.restype = C.c_int
+    lib.dfssm_dfw_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int32]
+    lib.dfssm_dfw_workspace_bytes.restype = C.c_size_t
+    lib.dfssm_dfw_project.argtypes = [C.POINTER(dfssm_dfw_proj), C.c_int32, C.c_int32, C.c_int32, P, P, C.c_int32,
+                                      P, C.c_size_t, C.POINTER(dfssm_dfw_taps), P]
+    lib.dfssm_dfw_project.restype = C.c_int
     lib.dfssm_state_field_words.argtypes = [C.c_int32]
     lib.dfssm_state_field_words.restype = C.c_int32
     lib.dfssm_state_encode.argtypes = [C.POINTER(dfssm_dims), P, C.c_int32, P, P, P]
@@ -187,6 +202,15 @@ def dfssm_embed(emb, tokens, batch, x, stream=None) -> int:
 
 def dfssm_lm_head(emb, y, batch, logits, next_tokens, ws, ws_bytes, taps=None, stream=None) -> int:
     return int(load().dfssm_lm_head(C.byref(emb), y, batch, logits, next_tokens, ws, ws_bytes, _ref(taps), stream))
+
+
+def dfssm_dfw_workspace_bytes(n_in: int, rank: int, batch: int) -> int:
+    return int(load().dfssm_dfw_workspace_bytes(n_in, rank, batch))
+
+
+def dfssm_dfw_project(w, n_out, n_in, rank, x, y, batch, ws, ws_bytes, taps=None, stream=None) -> int:
+    return int(load().dfssm_dfw_project(C.byref(w), n_out, n_in, rank, x, y, batch, ws, ws_bytes, _ref(taps),
+                                        stream))
 
 
 def dfssm_state_field_words(d_state: int) -> int:

@@ -424,6 +424,34 @@ int dfssm_lm_head(const dfssm_embedding *emb, const float *y, int32_t batch, flo
                                      next_tokens, ws, t, static_cast<hipStream_t>(stream)));
 }
 
+static bool dfw_shape_ok(int32_t n_out, int32_t n_in, int32_t rank, int32_t batch) {
+    return n_in >= 128 && n_in <= 8192 && n_in % 128 == 0 && n_out >= 1 && n_out <= (1 << 20) && rank >= 1 &&
+           rank <= 64 && batch >= 1 && batch <= 256;
+}
+
+size_t dfssm_dfw_workspace_bytes(int32_t n_in, int32_t rank, int32_t batch) {
+    if (!dfw_shape_ok(1, n_in, rank, batch)) return 0;
+    return dfw_ws_bytes(n_in, rank, batch);
+}
+
+int dfssm_dfw_project(const dfssm_dfw_proj *w, int32_t n_out, int32_t n_in, int32_t rank, const float *x, float *y,
+                      int32_t batch, void *ws, size_t ws_bytes, const dfssm_dfw_taps *taps, void *stream) {
+    if (!w || bad_ptr(x) || bad_ptr(y) || bad_ptr(ws)) return DFSSM_EINVAL;
+    if (bad_ptr(w->planes) || bad_ptr(w->row_scale) || bad_ptr(w->lora_dn) || bad_ptr(w->lora_dn_scale) ||
+        bad_ptr(w->lora_up) || bad_ptr(w->lora_up_scale))
+        return DFSSM_EINVAL;
+    if (n_out <= 0 || n_in <= 0 || rank <= 0 || batch <= 0) return DFSSM_EINVAL;
+    if (!dfw_shape_ok(n_out, n_in, rank, batch)) return DFSSM_EUNSUPPORTED;
+    if (taps && (bad_opt_ptr(taps->q) || bad_opt_ptr(taps->s) || bad_opt_ptr(taps->acc) || bad_opt_ptr(taps->t)))
+        return DFSSM_EINVAL;
+    if (ws_bytes < dfw_ws_bytes(n_in, rank, batch)) return DFSSM_EWORKSPACE;
+    const DfwWeights dw{w->planes, w->row_scale, w->lora_dn, w->lora_dn_scale, w->lora_up, w->lora_up_scale};
+    DfwTaps tp{};
+    if (taps) tp = DfwTaps{taps->q, taps->s, taps->acc, taps->t};
+    return hip_status(launch_dfw_project(dw, n_out, n_in, rank, x, y, batch, ws, tp,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int32_t dfssm_state_field_words(int32_t d_state) { return codec_field_words(d_state); }
 
 int dfssm_state_encode(const dfssm_dims *dims, const float *ssm, int32_t batch, uint32_t *fields, float *stats,

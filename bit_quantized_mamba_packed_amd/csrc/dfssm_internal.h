@@ -159,6 +159,25 @@ hipError_t launch_lm_head(const int8_t *codes, const float *row_scale, int V, in
 hipError_t launch_embed(const int8_t *codes, const float *row_scale, int V, int D, const int32_t *tokens, int batch,
                         float *x, hipStream_t stream);
 
+// Projection with the 17-level scaffold (dfw.hip).
+struct DfwWeights {
+    const uint8_t *planes;        // [5][n_out][K/8]
+    const uint16_t *row_scale;    // [n_out] fp16
+    const int8_t *lora_dn;        // [rank][K]
+    const float *lora_dn_scale;   // [rank]
+    const int8_t *lora_up;        // [n_out][rank]
+    const float *lora_up_scale;   // [n_out]
+};
+struct DfwTaps {
+    int8_t *q;      // [batch][K]
+    float *s;       // [batch]
+    int32_t *acc;   // [batch][n_out]
+    int32_t *t;     // [batch][rank]
+};
+size_t dfw_ws_bytes(int K, int rank, int batch);
+hipError_t launch_dfw_project(const DfwWeights &w, int n_out, int K, int rank, const float *x, float *y, int batch,
+                              void *ws, const DfwTaps &taps, hipStream_t stream);
+
 // Density field codec of SSM state rows (codec.hip): rows of N = d_state floats.
 int codec_field_words(int d_state);   // 32-bit words of one row's K x K field (0: unsupported N)
 hipError_t launch_state_encode(const float *ssm, int64_t rows, int N, uint32_t *fields, float *stats,

@@ -220,3 +220,31 @@ def state_encode(d, ssm: torch.Tensor, batch: int):
 def state_decode(d, fields: torch.Tensor, stats: torch.Tensor, batch: int, ssm: torch.Tensor) -> None:
     L.check(L.dfssm_state_decode(dims_struct(d), fields.data_ptr(), stats.data_ptr(), batch, ssm.data_ptr(),
                                  stream_handle()), "dfssm_state_decode")
+
+
+class DeviceDfwProj:
+    """A 17-level projection's tensors on the device (planes [5][n_out][n_in/8] uint8, ...)."""
+
+    def __init__(self, w, device="cuda"):
+        self.n_out, self.n_in, self.rank = int(w.n_out), int(w.n_in), int(w.rank)
+        self.planes = _dev(np.ascontiguousarray(w.planes, np.uint8), device)
+        self.row_scale = _dev(np.asarray(w.row_scale, np.float16).view(np.uint16), device)
+        self.lora_dn = _dev(np.ascontiguousarray(w.lora_dn, np.int8), device)
+        self.dn_scale = _dev(np.ascontiguousarray(w.dn_scale, np.float32), device)
+        self.lora_up = _dev(np.ascontiguousarray(w.lora_up, np.int8), device)
+        self.up_scale = _dev(np.ascontiguousarray(w.up_scale, np.float32), device)
+        self.struct = L.dfssm_dfw_proj(self.planes.data_ptr(), self.row_scale.data_ptr(), self.lora_dn.data_ptr(),
+                                       self.dn_scale.data_ptr(), self.lora_up.data_ptr(), self.up_scale.data_ptr())
+
+
+def dfw_project(p: DeviceDfwProj, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor = None, taps: dict = None) -> None:
+    """y [batch][n_out] = the 17-level projection of x [batch][n_in] (both fp32 on the device)."""
+    batch = int(x.shape[0])
+    need = L.dfssm_dfw_workspace_bytes(p.n_in, p.rank, batch)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    t = None
+    if taps:
+        t = L.dfssm_dfw_taps(*[taps[k].data_ptr() if taps.get(k) is not None else None for k in ("q", "s", "acc", "t")])
+    L.check(L.dfssm_dfw_project(p.struct, p.n_out, p.n_in, p.rank, x.data_ptr(), y.data_ptr(), batch,
+                                ws.data_ptr(), ws.numel(), t, stream_handle()), "dfssm_dfw_project")

@@ -301,6 +301,43 @@ int dfssm_lm_head(const dfssm_embedding *emb, const float *y, int32_t batch, flo
                   void *stream);
 
 /*
+ * Projection with the 17-level scaffold ([DF-SSM] §3.1 Eq. (1): K_w = 16, 17 levels from -1 to +1;
+ * §3.2 Eq. (3): y = W_scaffold x + W_A (W_B x)), the scaffold before binarisation.
+ * The weight of row n, input i is (k - 8)/8 * row_scale[n], k = the level index 0..16 of Eq. (1)
+ * (round(clamp((w+1)/2, 0, 1) * 16)), stored as five bit planes: planes[b][n][i/8] bit i % 8 holds
+ * bit b of k (the 1-bit scaffold layout, once per plane; 5/8 byte per weight). Per token b:
+ *   (q, s) = the per-token int8 quantizer of x[b] (as in the layer projections, without a norm)
+ *   acc[n] = sum_i (k[n][i] - 8) q[i]            (exact int32)
+ *   t[j]   = sum_i lora_dn[j][i] q[i]            (exact int32)
+ *   y[b][n] = s * row_scale[n] * acc[n] / 8 + lora_up_scale[n] * sum_j lora_up[n][j] * lora_dn_scale[j] * s * t[j]
+ * x [batch][n_in] fp32 and y [batch][n_out] fp32 are device buffers.
+ * Supported: n_in a multiple of 128, 128..8192; 1 <= n_out <= 1<<20; 1 <= rank <= 64; 1 <= batch <= 256.
+ * The five planes are read once per group of up to four tokens. Workspace:
+ * dfssm_dfw_workspace_bytes(n_in, rank, batch) bytes. Taps (each member may be NULL): q [batch][n_in],
+ * s [batch], acc [batch][n_out], t [batch][rank].
+ */
+typedef struct dfssm_dfw_proj {
+    const uint8_t  *planes;          /* [5][n_out][n_in/8] */
+    const uint16_t *row_scale;       /* [n_out] IEEE fp16 */
+    const int8_t   *lora_dn;         /* [rank][n_in] */
+    const float    *lora_dn_scale;   /* [rank] */
+    const int8_t   *lora_up;         /* [n_out][rank] */
+    const float    *lora_up_scale;   /* [n_out] */
+} dfssm_dfw_proj;
+
+typedef struct dfssm_dfw_taps {
+    int8_t  *q;
+    float   *s;
+    int32_t *acc;
+    int32_t *t;
+} dfssm_dfw_taps;
+
+size_t dfssm_dfw_workspace_bytes(int32_t n_in, int32_t rank, int32_t batch);
+int dfssm_dfw_project(const dfssm_dfw_proj *w, int32_t n_out, int32_t n_in, int32_t rank, const float *x,
+                      float *y, int32_t batch, void *ws, size_t ws_bytes, const dfssm_dfw_taps *taps,
+                      void *stream);
+
+/*
  * Density field codec of the SSM state ([DF-SSM] §3.4 "Density Field State Representation", App. D).
  * Each state row (the d_state values of one head channel; batch*nheads*headdim rows, in the layout
  * of dfssm_layer_state.ssm) is stored as a K x K bit field, K = round(sqrt(4*d_state)) (23 for

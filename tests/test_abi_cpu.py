@@ -260,3 +260,37 @@ def test_state_codec_field_size_and_rejects_bad_arguments():
         assert fn(batch=0) == L.DFSSM_EINVAL
         assert fn(batch=4097) == L.DFSSM_EUNSUPPORTED
         assert fn(dims=_dims(d_state=100)) == L.DFSSM_EUNSUPPORTED
+
+
+def test_dfw_project_workspace_and_rejects_bad_arguments():
+    assert L.dfssm_dfw_workspace_bytes(2048, 32, 4) > 0
+    assert L.dfssm_dfw_workspace_bytes(100, 32, 4) == 0
+    assert L.dfssm_dfw_workspace_bytes(2048, 65, 4) == 0
+    assert L.dfssm_dfw_workspace_bytes(2048, 32, 257) == 0
+    w = L.dfssm_dfw_proj(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = L.dfssm_dfw_workspace_bytes(2048, 32, 2)
+
+    def call(**kw):
+        a = dict(w=w, n_out=512, n_in=2048, rank=32, x=FAKE, y=FAKE, batch=2, ws=FAKE, ws_bytes=need, taps=None)
+        a.update(kw)
+        return L.dfssm_dfw_project(a["w"], a["n_out"], a["n_in"], a["rank"], a["x"], a["y"], a["batch"],
+                                   a["ws"], a["ws_bytes"], a["taps"])
+
+    assert call(x=None) == L.DFSSM_EINVAL
+    assert call(y=FAKE + 8) == L.DFSSM_EINVAL
+    assert call(w=L.dfssm_dfw_proj(None, FAKE, FAKE, FAKE, FAKE, FAKE)) == L.DFSSM_EINVAL
+    assert call(batch=0) == L.DFSSM_EINVAL
+    assert call(n_in=2000) == L.DFSSM_EUNSUPPORTED
+    assert call(n_in=16384) == L.DFSSM_EUNSUPPORTED
+    assert call(rank=65) == L.DFSSM_EUNSUPPORTED
+    assert call(batch=257) == L.DFSSM_EUNSUPPORTED
+    assert call(ws_bytes=need - 1) == L.DFSSM_EWORKSPACE
+    assert call(taps=L.dfssm_dfw_taps(FAKE + 1, None, None, None)) == L.DFSSM_EINVAL
+
+
+def test_dfw_workspace_holds_every_region():
+    # codes [B][K] i8 + their eight bit planes (K bytes per token) + s + sum(q) + t [B][rank] i32,
+    # each region rounded to 256 bytes
+    r = lambda v: (v + 255) // 256 * 256
+    for K, rank, B in ((256, 8, 3), (2048, 32, 4), (8192, 64, 256), (384, 5, 5)):
+        assert L.dfssm_dfw_workspace_bytes(K, rank, B) == r(B * K) + r(B * K) + r(4 * B) + r(4 * B) + r(4 * B * rank)
