@@ -172,7 +172,7 @@ def run_decode_b1(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     x0 = torch.from_numpy(x0_np).cuda()
     y = torch.empty((T, 1, dims.d_model), dtype=torch.float32, device="cuda")
     ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
-    wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws), args.steps,
+    wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws, launch=LAUNCH[0]), args.steps,
                             args.warmup, torch)
     if Dv.stack_status(ws) != L.DFSSM_STATUS_OK or not torch.isfinite(y).all():
         raise SystemExit("batch-1 stack decode failed (wait timeout or non-finite output)")
@@ -242,7 +242,7 @@ def run_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     x0 = y[:, -1, :].contiguous()
     yd = torch.empty((16, 1, dims.d_model), dtype=torch.float32, device="cuda")
     wsd = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, 1, 0, nL)
-    Dv.stack_decode(dims, layers, states, fw, x0, yd, 16, wsd)
+    Dv.stack_decode(dims, layers, states, fw, x0, yd, 16, wsd, launch=LAUNCH[0])
     torch.cuda.synchronize()
     if Dv.stack_status(wsd) != L.DFSSM_STATUS_OK or not torch.isfinite(yd).all():
         raise SystemExit("decode after prefill failed")
@@ -280,6 +280,10 @@ def run_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     return out
 
 
+# how the batch-1 persistent kernel is launched (--ordinary-launch: for kernel tracers that cannot
+# follow a cooperative launch)
+LAUNCH = [0]
+
 PREFILL_GEMM_PROFILE = os.path.join(ROOT, "profiles", "prefill2048_gemm_kernels.json")
 PREFILL_GEMM_SOURCES = ("bit_quantized_mamba_packed_amd/csrc/gemm.hip", "bit_quantized_mamba_packed_amd/csrc/gemm_conv.h",
                         "bit_quantized_mamba_packed_amd/csrc/dfssm_internal.h")
@@ -315,6 +319,29 @@ def prefill_gemm_profile(d, n_layers: int, S: int):
             "source": "profiles/prefill2048_gemm_kernels.json (rocprofv3 kernel trace of this workload)"}
 
 
+def write_gemm_profile(trace_csv: str) -> dict:
+    """Summarise the rocprofv3 kernel trace of `bench.py --workload prefill2048 --steps 1` into
+    PREFILL_GEMM_PROFILE: the average duration of the in_proj GEMM launch (k_gemm_tile_pair, both
+    of its GEMMs) and of the out_proj GEMM launch (k_gemm_tile) over the traced prefills."""
+    import csv
+    rows = list(csv.DictReader(open(trace_csv)))
+
+    def avg(tag):
+        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows if tag in r["Kernel_Name"]]
+        if not d:
+            raise SystemExit(f"{trace_csv}: no {tag} dispatch")
+        return sum(d) / len(d), len(d), next(r["Kernel_Name"] for r in rows if tag in r["Kernel_Name"])
+
+    t_in, n_in, k_in = avg("k_gemm_tile_pair")
+    t_out, n_out, k_out = avg("k_gemm_tile<")
+    out = {"source_hash": source_hash(PREFILL_GEMM_SOURCES), "in_proj_avg_ns": t_in, "in_proj_dispatches": n_in,
+           "in_proj_kernel": k_in.split("(")[0], "out_proj_avg_ns": t_out, "out_proj_dispatches": n_out,
+           "out_proj_kernel": k_out.split("(")[0]}
+    with open(PREFILL_GEMM_PROFILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def run_decode_b64(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     nL, B, T = args.layers, 64, 128
     states = []
@@ -326,7 +353,7 @@ def run_decode_b64(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict
     y = torch.empty((T, B, dims.d_model), dtype=torch.float32, device="cuda")
     ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, B, 0, nL)
     steps = max(1, min(args.steps, 2))
-    wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws), steps,
+    wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws, launch=LAUNCH[0]), steps,
                             min(args.warmup, 1), torch)
     if Dv.stack_status(ws) != L.DFSSM_STATUS_OK or not torch.isfinite(y).all():
         raise SystemExit("batched stack decode failed")
@@ -364,7 +391,7 @@ def run_decode_sweep(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> di
         y = torch.empty((T, B, dims.d_model), dtype=torch.float32, device="cuda")
         ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, B, 0, nL)
         steps = max(1, min(args.steps, 2))
-        wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws), steps,
+        wall, launch_ms = timed(lambda: Dv.stack_decode(dims, layers, states, fw, x0, y, T, ws, launch=LAUNCH[0]), steps,
                                 min(args.warmup, 1), torch)
         if Dv.stack_status(ws) != L.DFSSM_STATUS_OK or not torch.isfinite(y).all():
             raise SystemExit(f"batch-{B} stack decode failed")
@@ -420,7 +447,7 @@ def run_lm_head(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
         t = tok
         for i in range(T):
             Dv.embed(emb, t, x)
-            Dv.stack_decode(dims, layers, states, fw, x, yd, 1, wsd)
+            Dv.stack_decode(dims, layers, states, fw, x, yd, 1, wsd, launch=LAUNCH[0])
             Dv.lm_head(dims, emb, yd[0], None, toks[i], ws)
             t = toks[i, :1]
 
@@ -523,7 +550,15 @@ def main() -> int:
                     help="after the timed region, copy 512 MiB once (calibrates rocprofv3 byte counters)")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter CSVs into profiles/ and exit (no GPU)")
+    ap.add_argument("--ordinary-launch", action="store_true",
+                    help="launch the batch-1 persistent kernel with the ordinary launch API (same grid; for "
+                         "kernel tracers that cannot follow cooperative launches)")
+    ap.add_argument("--write-gemm-profile", metavar="TRACE_CSV",
+                    help="summarise a rocprofv3 kernel trace of the prefill workload into profiles/ and exit (no GPU)")
     args = ap.parse_args()
+    if args.write_gemm_profile:
+        print(json.dumps(write_gemm_profile(args.write_gemm_profile), indent=1))
+        return 0
     if args.write_counters:
         print(json.dumps(write_counters(*args.write_counters, args.tokens), indent=1))
         return 0
@@ -541,6 +576,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 1
+    if args.ordinary_launch:
+        LAUNCH[0] = L.DFSSM_LAUNCH_ORDINARY
     L.load()
     dims = gen.DIMS["1p3b"]
     layers_np = gen.stack_weights(dims, args.layers, seed=0)

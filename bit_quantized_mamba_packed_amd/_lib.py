@@ -29,6 +29,8 @@ DFSSM_STATUS_TIMEOUT = 1
 DFSSM_PATH_AUTO = 0
 DFSSM_PATH_FLOW = 1
 DFSSM_PATH_PER_LAYER = 2
+DFSSM_LAUNCH_COOPERATIVE = 0
+DFSSM_LAUNCH_ORDINARY = 1
 
 DFSSM_F32 = 0
 DFSSM_BF16 = 1
@@ -72,7 +74,7 @@ class dfssm_taps(C.Structure):
 
 
 class dfssm_stack_opts(C.Structure):
-    _fields_ = [("path", C.c_int32), ("reserved", C.c_int32)]
+    _fields_ = [("path", C.c_int32), ("launch", C.c_int32)]
 
 
 class dfssm_embedding(C.Structure):

@@ -324,7 +324,8 @@ int dfssm_stack_decode_ex(const dfssm_dims *dims, const dfssm_layer_weights *lay
     if (bad_ptr(final_norm_w) || bad_ptr(x0) || bad_ptr(y)) return DFSSM_EINVAL;
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
     const dfssm_stack_opts o = opts ? *opts : dfssm_stack_opts{};
-    if (o.path < DFSSM_PATH_AUTO || o.path > DFSSM_PATH_PER_LAYER || o.reserved != 0) return DFSSM_EINVAL;
+    if (o.path < DFSSM_PATH_AUTO || o.path > DFSSM_PATH_PER_LAYER) return DFSSM_EINVAL;
+    if (o.launch != DFSSM_LAUNCH_COOPERATIVE && o.launch != DFSSM_LAUNCH_ORDINARY) return DFSSM_EINVAL;
     const Shape s = shape_of(*dims);
     if (ws_bytes < decode_ws_bytes(s, batch, true, n_layers)) return DFSSM_EWORKSPACE;
     const bool flow = stack2_ok(s, batch);
@@ -339,7 +340,8 @@ int dfssm_stack_decode_ex(const dfssm_dims *dims, const dfssm_layer_weights *lay
     int *err = nullptr;
     hipError_t e;
     if (path == DFSSM_PATH_FLOW) {
-        e = launch_stack2(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, wsd + wsp.bytes, taps, &err, st);
+        e = launch_stack2(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, wsd + wsp.bytes, taps,
+                          o.launch == DFSSM_LAUNCH_COOPERATIVE, &err, st);
         if (e != hipSuccess) return DFSSM_EHIP;
         return hip_status(launch_stack_finish(err, status, y, ny, st));
     }

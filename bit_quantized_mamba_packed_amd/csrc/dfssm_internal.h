@@ -57,7 +57,7 @@ bool stack2_ok(const Shape &s, int batch);
 size_t stack2_extra_ws_bytes(const Shape &s, int batch, int n_layers);
 hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states, int n_layers,
                          const float *final_w, const float *x0, float *y, int batch, int n_steps, void *extra,
-                         const dfssm_taps *taps, int **err_flag, hipStream_t stream);
+                         const dfssm_taps *taps, bool cooperative, int **err_flag, hipStream_t stream);
 
 // After a stack decode: status[0] = *err (0 when err is null), and when *err is set every one of
 // the n floats of y becomes NaN, so that a timed-out exchange can never pass as a result.

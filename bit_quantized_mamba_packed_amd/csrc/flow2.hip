@@ -1030,12 +1030,17 @@ bool f2_plan(const Shape &s, int batch, int slots, F2Plan &p) {
 }
 
 
+// The grid (one workgroup per slot the plan counted as resident) is the same either way; the
+// cooperative API also verifies that the device keeps all of it resident. The ordinary launch is
+// for tools that cannot follow cooperative launches: should part of the grid not be resident, the
+// bounded waits time out and the call reports DFSSM_STATUS_TIMEOUT.
 template <int NB, int KCH1, int KCH2, int CPR1, int CPR2>
-hipError_t f2_launch(F2Args &a, const Shape &s, hipStream_t stream) {
+hipError_t f2_launch(F2Args &a, const Shape &s, bool cooperative, hipStream_t stream) {
     const size_t lds = f2_lds_base(s, NB) + f2_wreg_bytes(s, a.R1 + a.npad, a.R2);
     void *args[] = {&a};
     const void *fn = reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2, CPR1, CPR2>);
-    return hipLaunchCooperativeKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
+    if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
+    return hipLaunchKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
 }
 
 template <int NB, int KCH1, int KCH2, int CPR1, int CPR2>
@@ -1070,12 +1075,12 @@ int f2_slots(const Shape &s, int batch) {
     }
 }
 
-hipError_t f2_launch_any(F2Args &a, const Shape &s, hipStream_t stream) {
+hipError_t f2_launch_any(F2Args &a, const Shape &s, bool coop, hipStream_t stream) {
     switch (s.D) {
-    case 256: return f2_launch<1, 1, 1, 2, 4>(a, s, stream);
-    case 512: return f2_launch<1, 1, 1, 4, 8>(a, s, stream);
-    case 1024: return f2_launch<1, 1, 2, 8, 16>(a, s, stream);
-    case 2048: return f2_launch<1, 2, 4, 16, 32>(a, s, stream);
+    case 256: return f2_launch<1, 1, 1, 2, 4>(a, s, coop, stream);
+    case 512: return f2_launch<1, 1, 1, 4, 8>(a, s, coop, stream);
+    case 1024: return f2_launch<1, 1, 2, 8, 16>(a, s, coop, stream);
+    case 2048: return f2_launch<1, 2, 4, 16, 32>(a, s, coop, stream);
     default: return hipErrorInvalidConfiguration;
     }
 }
@@ -1096,7 +1101,7 @@ size_t stack2_extra_ws_bytes(const Shape &s, int batch, int n_layers) {
 
 hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states, int n_layers,
                          const float *final_w, const float *x0, float *y, int batch, int n_steps, void *extra,
-                         const dfssm_taps *taps, int **err_flag, hipStream_t stream) {
+                         const dfssm_taps *taps, bool cooperative, int **err_flag, hipStream_t stream) {
     F2Plan p{};
     if (!f2_plan(s, batch, f2_slots(s, batch), p)) return hipErrorInvalidConfiguration;
     char *q = static_cast<char *>(extra);
@@ -1156,7 +1161,7 @@ hipError_t launch_stack2(const Shape &s, const dfssm_layer_weights *layers, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_seed2<<<64, 256, 0, stream>>>(a.hx + (int64_t)(L - 1) * batch * s.D, x0, (int64_t)batch * s.D);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return f2_launch_any(a, s, stream);
+    return f2_launch_any(a, s, cooperative, stream);
 }
 
 }  // namespace dfssm

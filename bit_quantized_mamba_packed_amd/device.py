@@ -136,10 +136,11 @@ def _arrays(layers: list, states: list):
 
 
 def stack_decode(d, layers: list, states: list, final_w: torch.Tensor, x0: torch.Tensor, y: torch.Tensor,
-                 n_steps: int, ws: torch.Tensor, taps: Taps = None, path: int = L.DFSSM_PATH_AUTO) -> None:
+                 n_steps: int, ws: torch.Tensor, taps: Taps = None, path: int = L.DFSSM_PATH_AUTO,
+                 launch: int = L.DFSSM_LAUNCH_COOPERATIVE) -> None:
     """dfssm_stack_decode_ex; the call's status word stays in ws (stack_status reads it)."""
     arr_w, arr_s = _arrays(layers, states)
-    opts = L.dfssm_stack_opts(path, 0)
+    opts = L.dfssm_stack_opts(path, launch)
     st = L.dfssm_stack_decode_ex(dims_struct(d), arr_w, arr_s, len(layers), final_w.data_ptr(), x0.data_ptr(),
                                  y.data_ptr(), x0.shape[0], n_steps, ws.data_ptr(), ws.numel(),
                                  None if taps is None else taps.struct, opts, stream_handle())

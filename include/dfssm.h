@@ -208,11 +208,18 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w,
  * Kernel selection for dfssm_stack_decode_ex (every path computes the same decode; zero-initialise
  * the struct for the defaults).
  *   path      DFSSM_PATH_*; a path that cannot run the shape and batch is DFSSM_EUNSUPPORTED.
- *   reserved  must be 0.
+ *   launch    DFSSM_LAUNCH_*: how DFSSM_PATH_FLOW's persistent kernel is launched. Its grid (one
+ *             workgroup per compute unit) must be resident all at once; the cooperative launch
+ *             (default) has the runtime verify that, the ordinary launch does not (for tools that
+ *             cannot follow cooperative launches, e.g. kernel tracers): if the device then leaves
+ *             part of the grid waiting, the bounded waits expire and the call's status word reads
+ *             DFSSM_STATUS_TIMEOUT. Ignored by the other paths.
  */
+#define DFSSM_LAUNCH_COOPERATIVE 0
+#define DFSSM_LAUNCH_ORDINARY    1
 typedef struct dfssm_stack_opts {
     int32_t path;
-    int32_t reserved;
+    int32_t launch;
 } dfssm_stack_opts;
 
 /*

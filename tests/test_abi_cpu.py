@@ -197,7 +197,8 @@ def test_stack_decode_ex_rejects_bad_options():
 
     assert call(path=7) == L.DFSSM_EINVAL
     assert call(path=-1) == L.DFSSM_EINVAL
-    assert call(reserved=1) == L.DFSSM_EINVAL
+    assert call(launch=2) == L.DFSSM_EINVAL
+    assert call(launch=-1) == L.DFSSM_EINVAL
     # batch 5 has no persistent kernel: asking for one is unsupported, not silently rerouted
     ws5 = L.dfssm_workspace_bytes(d, L.DFSSM_OP_STACK_DECODE, 5, 0, n)
     st = L.dfssm_stack_decode_ex(d, arr_w, arr_s, n, FAKE, FAKE, FAKE, 5, 4, FAKE, ws5, None,

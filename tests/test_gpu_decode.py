@@ -177,7 +177,7 @@ def test_layer_decode_degenerate_cases():
     forced_chain(lw, xs, conv0, ssm0, outs, tps, final)
 
 
-def run_stack(dims, layers, x0, states0, n_steps, taps=False, final_w=None, path=0):
+def run_stack(dims, layers, x0, states0, n_steps, taps=False, final_w=None, path=0, launch=0):
     L, Dv = _lib()
     B = x0.shape[0]
     devs = [Dv.DeviceLayer(lw) for lw in layers]
@@ -187,7 +187,7 @@ def run_stack(dims, layers, x0, states0, n_steps, taps=False, final_w=None, path
     y = torch.empty((n_steps, B, dims.d_model), dtype=torch.float32, device="cuda")
     ws = Dv.workspace(dims, L.DFSSM_OP_STACK_DECODE, B, 0, len(layers))
     tp = Dv.Taps(dims, n_steps * len(layers) * B) if taps else None
-    Dv.stack_decode(dims, devs, sts, fw, xt, y, n_steps, ws, tp, path=path)
+    Dv.stack_decode(dims, devs, sts, fw, xt, y, n_steps, ws, tp, path=path, launch=launch)
     torch.cuda.synchronize()
     assert Dv.stack_status(ws) == L.DFSSM_STATUS_OK, "a persistent-kernel wait timed out"
     return (y.cpu().numpy(), [(s.conv.cpu().numpy(), s.ssm.cpu().numpy()) for s in sts],
@@ -386,3 +386,20 @@ def test_stack_decode_batch1_paths_agree(dims_name):
         for l in range(nL):
             assert PY.err(st2[l][0], st1[l][0]) < PY.TOL_LAYER
             assert PY.err(st2[l][1], st1[l][1]) < PY.TOL_LAYER
+
+
+def test_stack_decode_batch1_ordinary_launch_is_bit_identical():
+    """The persistent kernel launched with the ordinary API (for kernel tracers) computes exactly what
+    the cooperative launch computes: same grid, same code."""
+    L, _ = _lib()
+    dims = gen.DIMS["1p3b"]
+    nL, T = 3, 4
+    layers = gen.stack_weights(dims, nL, seed=5)
+    states0 = [gen.initial_states(dims, 1, l, 5, std=0.1) for l in range(nL)]
+    x0 = gen.token_inputs(dims, (1,), 5, tag=6)
+    say("case: 1.3B stack, 3 layers, 4 steps, batch 1, cooperative then ordinary launch")
+    y1, st1, _ = run_stack(dims, layers, x0, states0, T, path=L.DFSSM_PATH_FLOW)
+    y2, st2, _ = run_stack(dims, layers, x0, states0, T, path=L.DFSSM_PATH_FLOW, launch=L.DFSSM_LAUNCH_ORDINARY)
+    assert np.array_equal(y1, y2)
+    for a, b in zip(st1, st2):
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
