@@ -44,6 +44,9 @@ What each function follows and what pins it (the pins live in tests/test_oracle_
                     accumulator bounds; the field sizes App. D prints
   ssd_chunked       with codec=True: the carried state passes through the codec at every chunk
                     boundary (DF-SSD, §3.4 / App. D).  pinned by: codec off equals the plain scan
+  layer_tokens      with codec_chunk: the same DF-SSD inside the layer.  pinned by: its SSM part equals
+                    ssd_chunked(codec=True) on the layer's own x, dt, B, C; one chunk covering the
+                    sequence equals the plain layer
   embed             [DF-SSM] §3.3 (int8 embedding, per-row scale), Table 1 (103 MB, tied).
                     pinned by: Table 1's embedding size; rows by explicit indexing
   lm_head           the tied head over the same int8 rows (Table 1 "Embedding + LM head (tied)")
@@ -300,13 +303,20 @@ def layer_prefill(xs, W, conv_state, ssm_state):
     return layer_decode_steps(xs, W, conv_state, ssm_state)
 
 
-def layer_tokens(xs, W, conv_state, ssm_state, force: Optional[dict] = None, dense: Optional[dict] = None):
+def layer_tokens(xs, W, conv_state, ssm_state, force: Optional[dict] = None, dense: Optional[dict] = None,
+                 codec_chunk: Optional[int] = None):
     """layer_decode_steps evaluated stage by stage over a sequence xs [T][d_model].
 
     Stage k of token t needs only stage k-1 of tokens <= t, so running each stage over all T
     tokens before the next (projections as one matrix product, conv and recurrence as loops over
     t) gives the sequential-decode result. ``force`` may hold per-token arrays 'in_q' [T][D],
     'in_s' [T], 'out_q' [T][E], 'out_s' [T] (see layer_decode).
+    With ``codec_chunk`` = Q (DF-SSD, [DF-SSM] §3.4 / App. D), the SSM state entering every chunk
+    of Q tokens after the first passes through the density field codec, as in
+    ssd_chunked(codec=True); ``force['state_in']`` [n_chunks][H][P][N] may then replace the coded
+    state entering chunk c >= 1 (code forcing of the codec's decisions). The taps then also hold
+    'state_pre' and 'state_in' [n_chunks][H][P][N] (chunk 0: the initial state) and the SSM
+    inputs 'x' [T][E], 'dt' [T][H], 'B', 'C' [T][G][N].
     Returns (outs [T][d_model], conv_state, ssm_state, taps dict of arrays [T][...])."""
     dm = W.dims
     E, H, N, G = dm.d_inner, dm.nheads, dm.d_state, dm.ngroups
@@ -327,10 +337,21 @@ def layer_tokens(xs, W, conv_state, ssm_state, force: Optional[dict] = None, den
     A = -np.exp(np.asarray(W.A_log, F64))
     cs, ss = np.asarray(conv_state, F64), np.asarray(ssm_state, F64)
     y = np.empty((T, E))
+    pre, ent, xs_in, Bs, Cs = [], [], np.empty((T, E)), np.empty((T, G, N)), np.empty((T, G, N))
     for t in range(T):
+        if codec_chunk is not None and t % codec_chunk == 0:
+            c = t // codec_chunk
+            pre.append(ss.copy())
+            if c > 0:
+                if force is not None and "state_in" in force:
+                    ss = np.asarray(force["state_in"][c], F64)
+                else:
+                    ss = state_codec_roundtrip(ss.astype(F32))
+            ent.append(ss.copy())
         xbc_act, cs = conv_step(cs, Y[t, E:E + Cd], W.conv_w, W.conv_b)
         Bm = xbc_act[E:E + G * N].reshape(G, N)
         Cm = xbc_act[E + G * N:E + 2 * G * N].reshape(G, N)
+        xs_in[t], Bs[t], Cs[t] = xbc_act[:E], Bm, Cm
         y[t], ss = ssm_step(ss, xbc_act[:E], Bm, Cm, dt[t], A, W.D, G)
     u2 = gated_rmsnorm(y, z, W.gnorm_w, dm.eps)[0].astype(F32)
     q2 = np.empty((T, E), np.int8)
@@ -341,6 +362,8 @@ def layer_tokens(xs, W, conv_state, ssm_state, force: Optional[dict] = None, den
         q2, s2 = np.asarray(force["out_q"], np.int8), np.asarray(force["out_s"], F32)
     o, acc2, t2 = project_tokens(q2, s2, W.out_proj, dense["out"])
     taps = dict(in_u=u, in_q=q, in_s=s, in_acc=acc, in_t=tt, out_u=u2, out_q=q2, out_s=s2, out_acc=acc2, out_t=t2)
+    if codec_chunk is not None:
+        taps.update(state_pre=np.stack(pre), state_in=np.stack(ent), x=xs_in, dt=dt, B=Bs, C=Cs)
     return xs + o, cs, ss, taps
 
 

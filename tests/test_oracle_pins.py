@@ -661,3 +661,27 @@ def test_project_dfw_end_levels_equal_the_one_bit_projection():
                             P1.dn_scale, P1.lora_up, P1.up_scale)
     y0, acc0, _ = O.project_dfw(q, np.float32(0.017), P0)
     assert (acc0 == 0).all()
+
+
+def test_layer_dfssd_matches_chunked_codec_scan_and_reduces_to_plain():
+    dm = _tiny_dims()
+    W = gen.layer_weights(dm, 0, seed=12)
+    rng = np.random.default_rng(13)
+    T, Q = 11, 4
+    xs = rng.standard_normal((T, dm.d_model))
+    conv0 = rng.standard_normal((dm.conv_dim, dm.d_conv - 1)) * 0.1
+    ssm0 = rng.standard_normal((dm.nheads, dm.headdim, dm.d_state)) * 0.1
+    o, cs, ss, tp = O.layer_tokens(xs, W, conv0, ssm0, codec_chunk=Q)
+    A = -np.exp(np.asarray(W.A_log, np.float64))
+    ys, S = O.ssd_chunked(tp["x"].reshape(T, dm.nheads, dm.headdim), tp["dt"], A, tp["B"], tp["C"], W.D, ssm0,
+                          dm.ngroups, Q, codec=True)
+    np.testing.assert_allclose(ss, S, rtol=1e-9, atol=1e-12)
+    assert tp["state_in"].shape[0] == tp["state_pre"].shape[0] == 3
+    assert np.array_equal(tp["state_in"][0], ssm0) and not np.allclose(tp["state_in"][1], tp["state_pre"][1])
+    # forcing the coded states with the oracle's own gives the same run
+    o2, _, ss2, _ = O.layer_tokens(xs, W, conv0, ssm0, force={"state_in": tp["state_in"]}, codec_chunk=Q)
+    assert np.array_equal(o2, o) and np.array_equal(ss2, ss)
+    # one chunk over the whole sequence: no boundary, the plain layer
+    o3, _, ss3, _ = O.layer_tokens(xs, W, conv0, ssm0, codec_chunk=T)
+    o4, _, ss4, _ = O.layer_tokens(xs, W, conv0, ssm0)
+    assert np.array_equal(o3, o4) and np.array_equal(ss3, ss4)
