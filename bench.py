@@ -497,6 +497,37 @@ def run_state_codec(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dic
             "decode": res["decode"]}
 
 
+def run_dfssd_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
+    """One 1.3B layer over 2048 bf16 tokens (chunk 256) with the density field codec on the state at
+    the 7 chunk boundaries (DF-SSD), against the same prefill without it. The codec carry runs one
+    wave per head sequentially over the chunks: bound by its per-row sigma-delta chain, not HBM."""
+    S, Q = 2048, 256
+    lay = layers[0]
+    conv = torch.zeros((1, dims.conv_dim, dims.d_conv - 1), dtype=torch.float32, device="cuda")
+    ssm = torch.zeros((1, dims.nheads, dims.headdim, dims.d_state), dtype=torch.float32, device="cuda")
+    st = Dv.DeviceState.from_tensors(conv, ssm, dims, 1)
+    xb = torch.from_numpy(gen.token_inputs(dims, (1, S), 0, tag=12, bf16=True)).cuda().to(torch.bfloat16)
+    y = torch.empty((1, S, dims.d_model), dtype=torch.float32, device="cuda")
+    ws = Dv.workspace(dims, L.DFSSM_OP_LAYER_PREFILL, 1, S)
+    res = {}
+    for name, codec in (("plain", False), ("dfssd", True)):
+        def step():
+            conv.zero_()
+            ssm.zero_()
+            Dv.layer_prefill(dims, lay, st, xb, y, Q, ws, state_codec=codec)
+        _, ms = timed(step, max(3, args.steps), 1, torch)
+        if not torch.isfinite(y).all():
+            raise SystemExit("non-finite DF-SSD prefill output")
+        res[name] = round(sum(ms) / len(ms), 4)
+    extra = res["dfssd"] - res["plain"]
+    return {"metric": "DF-SSD layer prefill, 1.3B layer, 2048 bf16 tokens, chunk 256: ms per layer",
+            "value": res["dfssd"], "unit": "ms", "higher_is_better": False,
+            "config": {"workload": "dfssd_prefill_1p3b_layer2048", "chunk": Q, "boundaries": S // Q - 1},
+            "plain_ms": res["plain"], "codec_carry_ms": round(extra, 4),
+            "note": "codec carry = DF-SSD minus plain (the scan with 4096 state rows encoded and read back at "
+                    "each of 7 boundaries, one lane per row)"}
+
+
 def run_dfw_proj(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
     """The 17-level scaffold projection at batch 1 (decode) on the 1.3B in_proj (8,512 x 2,048) and
     out_proj (2,048 x 4,096) shapes, rank 32: quantizer + five-plane GEMV + LoRA epilogue per call."""
@@ -532,7 +563,7 @@ def run_dfw_proj(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:
 
 WORKLOADS = {"decode_b1": run_decode_b1, "prefill2048": run_prefill, "decode_b64": run_decode_b64,
              "decode_sweep": run_decode_sweep, "lm_head": run_lm_head, "state_codec": run_state_codec,
-             "dfw_proj": run_dfw_proj}
+             "dfw_proj": run_dfw_proj, "dfssd_prefill": run_dfssd_prefill}
 
 
 def main() -> int:
@@ -591,12 +622,14 @@ def main() -> int:
     out = run_decode_b1(*common)
     if not args.no_secondary:
         sec = {}
-        for name in ("prefill2048", "decode_b64", "decode_sweep", "lm_head", "state_codec", "dfw_proj"):
+        for name in ("prefill2048", "decode_b64", "decode_sweep", "lm_head", "state_codec", "dfw_proj",
+                     "dfssd_prefill"):
             r = WORKLOADS[name](*common)
             torch.cuda.empty_cache()
             sec[name] = {k: r[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",
                                            "roofline_scaffold_gemms", "points", "us_per_call",
-                                           "greedy_full_model", "cpu_baseline", "decode") if k in r}
+                                           "greedy_full_model", "cpu_baseline", "decode", "plain_ms",
+                                           "codec_carry_ms") if k in r}
         out["secondary"] = sec
     print(json.dumps(out), flush=True)
     return 0

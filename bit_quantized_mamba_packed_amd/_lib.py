@@ -37,6 +37,7 @@ DFSSM_BF16 = 1
 
 # every symbol include/dfssm.h declares
 EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_decode_noalloc", "dfssm_layer_prefill",
+           "dfssm_layer_prefill_ex",
            "dfssm_stack_decode", "dfssm_stack_decode_ex", "dfssm_stack_prefill", "dfssm_embed", "dfssm_lm_head",
            "dfssm_state_field_words", "dfssm_state_encode", "dfssm_state_decode", "dfssm_dfw_workspace_bytes",
            "dfssm_dfw_project", "dfssm_strerror")
@@ -85,6 +86,11 @@ class dfssm_head_taps(C.Structure):
     _fields_ = [("q", C.c_void_p), ("s", C.c_void_p), ("acc", C.c_void_p)]
 
 
+class dfssm_prefill_opts(C.Structure):
+    _fields_ = [("state_codec", C.c_int32), ("reserved", C.c_int32), ("chunk_state_pre", C.c_void_p),
+                ("chunk_state_in", C.c_void_p)]
+
+
 class dfssm_dfw_proj(C.Structure):
     _fields_ = [("planes", C.c_void_p), ("row_scale", C.c_void_p), ("lora_dn", C.c_void_p),
                 ("lora_dn_scale", C.c_void_p), ("lora_up", C.c_void_p), ("lora_up_scale", C.c_void_p)]
@@ -120,6 +126,11 @@ def load() -> C.CDLL:
                                         C.POINTER(dfssm_layer_state), P, C.c_int32, P, C.c_int32,
                                         C.c_int32, C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
     lib.dfssm_layer_prefill.restype = C.c_int
+    lib.dfssm_layer_prefill_ex.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
+                                           C.POINTER(dfssm_layer_state), P, C.c_int32, P, C.c_int32,
+                                           C.c_int32, C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps),
+                                           C.POINTER(dfssm_prefill_opts), P]
+    lib.dfssm_layer_prefill_ex.restype = C.c_int
     lib.dfssm_stack_decode.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
                                        C.POINTER(dfssm_layer_state), C.c_int32, P, P, P, C.c_int32,
                                        C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
@@ -171,6 +182,12 @@ def dfssm_layer_decode(dims, w, state, x_in, x_out, batch, ws, ws_bytes, taps=No
 def dfssm_layer_decode_noalloc(dims, w, state, x_in, x_out, batch, taps=None, stream=None) -> int:
     return int(load().dfssm_layer_decode_noalloc(C.byref(dims), C.byref(w), C.byref(state), x_in, x_out, batch,
                                                  _ref(taps), stream))
+
+
+def dfssm_layer_prefill_ex(dims, w, state, x_in, x_dtype, x_out, batch, seqlen, chunk, ws, ws_bytes,
+                           taps=None, opts=None, stream=None) -> int:
+    return int(load().dfssm_layer_prefill_ex(C.byref(dims), C.byref(w), C.byref(state), x_in, x_dtype, x_out,
+                                             batch, seqlen, chunk, ws, ws_bytes, _ref(taps), _ref(opts), stream))
 
 
 def dfssm_layer_prefill(dims, w, state, x_in, x_dtype, x_out, batch, seqlen, chunk, ws, ws_bytes,

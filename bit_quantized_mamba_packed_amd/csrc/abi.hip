@@ -287,7 +287,19 @@ int dfssm_layer_decode_noalloc(const dfssm_dims *dims, const dfssm_layer_weights
 int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w, const dfssm_layer_state *state,
                         const void *x_in, int32_t x_dtype, float *x_out, int32_t batch, int32_t seqlen,
                         int32_t chunk, void *ws, size_t ws_bytes, const dfssm_taps *taps, void *stream) {
+    return dfssm_layer_prefill_ex(dims, w, state, x_in, x_dtype, x_out, batch, seqlen, chunk, ws, ws_bytes, taps,
+                                  nullptr, stream);
+}
+
+int dfssm_layer_prefill_ex(const dfssm_dims *dims, const dfssm_layer_weights *w, const dfssm_layer_state *state,
+                           const void *x_in, int32_t x_dtype, float *x_out, int32_t batch, int32_t seqlen,
+                           int32_t chunk, void *ws, size_t ws_bytes, const dfssm_taps *taps,
+                           const dfssm_prefill_opts *opts, void *stream) {
     int r;
+    const dfssm_prefill_opts o = opts ? *opts : dfssm_prefill_opts{};
+    if ((o.state_codec != 0 && o.state_codec != 1) || o.reserved != 0) return DFSSM_EINVAL;
+    if (bad_opt_ptr(o.chunk_state_pre) || bad_opt_ptr(o.chunk_state_in)) return DFSSM_EINVAL;
+    if (!o.state_codec && (o.chunk_state_pre || o.chunk_state_in)) return DFSSM_EINVAL;
     if ((r = check_dims(dims))) return r;
     if ((r = check_weights(w)) || (r = check_state(state)) || (r = check_taps(taps))) return r;
     if (bad_ptr(x_in) || bad_ptr(x_out) || batch <= 0 || seqlen <= 0) return DFSSM_EINVAL;
@@ -299,8 +311,9 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w, co
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return DFSSM_EINVAL;
     if (ws_bytes < prefill_ws_bytes(s, batch, seqlen, chunk)) return DFSSM_EWORKSPACE;
     const PrefillWs p = carve_prefill_ws(s, batch, seqlen, chunk, ws);
+    const PrefillCodec pc{o.state_codec == 1, o.chunk_state_pre, o.chunk_state_in};
     return hip_status(launch_layer_prefill(s, *w, *state, x_in, x_dtype == DFSSM_BF16, x_out, batch, seqlen, chunk, p,
-                                           taps, static_cast<hipStream_t>(stream)));
+                                           taps, static_cast<hipStream_t>(stream), &pc));
 }
 
 int dfssm_stack_decode(const dfssm_dims *dims, const dfssm_layer_weights *layers, const dfssm_layer_state *states,

@@ -82,6 +82,30 @@ __device__ __forceinline__ void tile_store(float *dst, int64_t r0, int nr, int c
     }
 }
 
+// Readout of one row's field: lo + span * (ones among the value's cells) / cells.
+template <int N>
+__device__ __forceinline__ void row_decode(const uint32_t (&word)[codec_words(N)], float mu, float sigma,
+                                           float (&out)[N]) {
+    const float lo = mu - 3.0f * sigma, span = 6.0f * sigma;
+    const bool flat = !(sigma != 0.f);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int c0 = cell_begin<N>(i), c1 = cell_begin<N>(i + 1);
+        // cells c0 .. c1 - 1 span at most two words (a value owns fewer than 32 cells)
+        const int w0 = c0 >> 5, w1 = (c1 - 1) >> 5, b0 = c0 & 31;
+        int ones;
+        if (w0 == w1) {
+            const uint32_t m = (c1 - c0 == 32) ? 0xffffffffu : ((1u << (c1 - c0)) - 1u);
+            ones = __builtin_popcount((word[w0] >> b0) & m);
+        } else {
+            const int n1 = c1 - (w1 << 5);
+            ones = __builtin_popcount(word[w0] >> b0) + __builtin_popcount(word[w1] & ((1u << n1) - 1u));
+        }
+        const float dens = (float)ones * (1.0f / (float)(c1 - c0));
+        out[i] = flat ? mu : lo + span * dens;
+    }
+}
+
 template <int N>
 __global__ __launch_bounds__(kCodecRows) void k_state_encode(const float *__restrict__ ssm, int64_t rows,
                                                             uint32_t *__restrict__ fields, float *__restrict__ stats) {
@@ -181,26 +205,8 @@ __global__ __launch_bounds__(kCodecRows) void k_state_decode(const uint32_t *__r
     for (int w = 0; w < W; ++w) word[w] = __builtin_bit_cast(uint32_t, lds[lane * T::WS + w]);
     __syncthreads();
 
-    const float mu = ms.x, sigma = ms.y;
-    const float lo = mu - 3.0f * sigma, span = 6.0f * sigma;
-    const bool flat = !(sigma != 0.f);
     float out[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const int c0 = cell_begin<N>(i), c1 = cell_begin<N>(i + 1);
-        // cells c0 .. c1 - 1 span at most two words (a value owns fewer than 32 cells)
-        const int w0 = c0 >> 5, w1 = (c1 - 1) >> 5, b0 = c0 & 31;
-        int ones;
-        if (w0 == w1) {
-            const uint32_t m = (c1 - c0 == 32) ? 0xffffffffu : ((1u << (c1 - c0)) - 1u);
-            ones = __builtin_popcount((word[w0] >> b0) & m);
-        } else {
-            const int n1 = c1 - (w1 << 5);
-            ones = __builtin_popcount(word[w0] >> b0) + __builtin_popcount(word[w1] & ((1u << n1) - 1u));
-        }
-        const float dens = (float)ones * (1.0f / (float)(c1 - c0));
-        out[i] = flat ? mu : lo + span * dens;
-    }
+    row_decode<N>(word, ms.x, ms.y, out);
 #pragma unroll
     for (int c0 = 0; c0 < N; c0 += T::kT) {
 #pragma unroll
@@ -209,6 +215,127 @@ __global__ __launch_bounds__(kCodecRows) void k_state_decode(const uint32_t *__r
         tile_store<N>(ssm, r0, nr, c0, lds);
         __syncthreads();
     }
+}
+
+// DF-SSD carry ([DF-SSM] §3.4, App. D: the codec at chunk boundaries of the chunked scan). One wave
+// per (sequence, head), one lane per state row (the head's 64 channels): S starts as the layer's
+// state; for every chunk c the state entering it is S itself for c = 0 and codec(S) after that,
+// and it is written over sloc[c] (which held the chunk's own contribution S_loc, read first), then
+// S = exp(Lam_end(c)) * entering + S_loc(c); the state after the last chunk is the layer's new state.
+// Optional taps: the state entering each chunk before and after the codec.
+struct ScanCodecArgs {
+    float *state;            // [BH][64][N] initial -> final
+    float *sloc;             // [BH][nch][64][N] chunk contributions -> entering states
+    const float *lam_end;    // [BH][nch]
+    int BH, nch;
+    float *tap_pre, *tap_in; // [nch][BH][64][N] or null
+};
+
+template <int N>
+__global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) {
+#pragma clang fp contract(off)
+    using T = Tile<N>;
+    constexpr int K2 = codec_side(N) * codec_side(N), W = T::W;
+    __shared__ float lds[T::kFloats];
+    const int bh = blockIdx.x, lane = threadIdx.x;
+    constexpr int64_t PN = (int64_t)kCodecRows * N;
+    float S[N];
+#pragma unroll
+    for (int c0 = 0; c0 < N; c0 += T::kT) {
+        tile_load<N>(a.state + bh * PN, 0, kCodecRows, c0, lds);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < T::kT; ++j) S[c0 + j] = lds[lane * T::kStride + j];
+        __syncthreads();
+    }
+    for (int c = 0; c < a.nch; ++c) {
+        const int64_t slot = ((int64_t)c * a.BH + bh) * PN;
+        if (a.tap_pre) {
+#pragma unroll
+            for (int c0 = 0; c0 < N; c0 += T::kT) {
+#pragma unroll
+                for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
+                __syncthreads();
+                tile_store<N>(a.tap_pre + slot, 0, kCodecRows, c0, lds);
+                __syncthreads();
+            }
+        }
+        if (c > 0) {
+            // ---- encode (mean and population standard deviation in element order, 8-bit codes,
+            // sigma-delta), then read back in place
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc = acc + S[i];
+            const float mu = acc / (float)N;
+            float acc2 = 0.f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const float d = S[i] - mu;
+                acc2 = acc2 + d * d;
+            }
+            const float sigma = sqrtf(acc2 / (float)N);
+            const float lo = mu - 3.0f * sigma, span = 6.0f * sigma;
+            int tm[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const float x = fminf(fmaxf((S[i] - lo) / span, 0.f), 1.f);
+                tm[i] = (int)rintf(x * 255.0f) - 128;
+            }
+            uint32_t word[W];
+            int e = 0;
+#pragma unroll
+            for (int w = 0; w < W; ++w) word[w] = 0u;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+#pragma unroll
+                for (int cc = cell_begin<N>(i); cc < cell_begin<N>(i + 1); ++cc) {
+                    const int u = e + tm[i];
+                    const int neg = u >> 31;
+                    e = u - 127 + (neg & 255);
+                    word[cc >> 5] |= (uint32_t)neg & (1u << (cc & 31));
+                }
+            }
+            constexpr uint32_t kTailMask = (K2 & 31) ? ((1u << (K2 & 31)) - 1u) : 0xffffffffu;
+            const bool flat = !(sigma != 0.f);
+#pragma unroll
+            for (int w = 0; w < W; ++w) word[w] = flat ? 0u : (~word[w] & ((w == W - 1) ? kTailMask : 0xffffffffu));
+            row_decode<N>(word, mu, sigma, S);
+        }
+        // S_loc of this chunk (read before its slot is overwritten), the entering state out, the carry
+        const float f = expf(a.lam_end[(int64_t)bh * a.nch + c]);
+        float *sl = a.sloc + ((int64_t)bh * a.nch + c) * PN;
+#pragma unroll
+        for (int c0 = 0; c0 < N; c0 += T::kT) {
+            tile_load<N>(sl, 0, kCodecRows, c0, lds);
+            __syncthreads();
+            float loc[T::kT];
+#pragma unroll
+            for (int j = 0; j < T::kT; ++j) loc[j] = lds[lane * T::kStride + j];
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
+            __syncthreads();
+            tile_store<N>(sl, 0, kCodecRows, c0, lds);
+            if (a.tap_in) tile_store<N>(a.tap_in + slot, 0, kCodecRows, c0, lds);
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < T::kT; ++j) S[c0 + j] = f * S[c0 + j] + loc[j];
+        }
+    }
+#pragma unroll
+    for (int c0 = 0; c0 < N; c0 += T::kT) {
+#pragma unroll
+        for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
+        __syncthreads();
+        tile_store<N>(a.state + bh * PN, 0, kCodecRows, c0, lds);
+        __syncthreads();
+    }
+}
+
+template <int N>
+hipError_t scan_codec_n(const ScanCodecArgs &a, hipStream_t stream) {
+    k_ssd_scan_codec<N><<<(unsigned)a.BH, kCodecRows, 0, stream>>>(a);
+    return hipGetLastError();
 }
 
 template <int N>
@@ -237,6 +364,20 @@ hipError_t launch_state_encode(const float *ssm, int64_t rows, int N, uint32_t *
     case 64: return encode_n<64>(ssm, rows, fields, stats, stream);
     case 128: return encode_n<128>(ssm, rows, fields, stats, stream);
     case 256: return encode_n<256>(ssm, rows, fields, stats, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_ssd_scan_codec(float *state, float *sloc, const float *lam_end, int BH, int nch, int N, int P,
+                                 float *tap_pre, float *tap_in, hipStream_t stream) {
+    if (P != kCodecRows) return hipErrorInvalidValue;
+    const ScanCodecArgs a{state, sloc, lam_end, BH, nch, tap_pre, tap_in};
+    switch (N) {
+    case 16: return scan_codec_n<16>(a, stream);
+    case 32: return scan_codec_n<32>(a, stream);
+    case 64: return scan_codec_n<64>(a, stream);
+    case 128: return scan_codec_n<128>(a, stream);
+    case 256: return scan_codec_n<256>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

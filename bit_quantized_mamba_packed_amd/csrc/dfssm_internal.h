@@ -132,9 +132,15 @@ struct PrefillWs {
 };
 PrefillWs carve_prefill_ws(const Shape &s, int batch, int seqlen, int chunk, void *base);
 
+// DF-SSD: the codec on the state entering every chunk after the first (taps optional)
+struct PrefillCodec {
+    bool on;
+    float *tap_pre, *tap_in;   // [nch][batch][H][P][N]
+};
 hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
                                 const void *x_in, int x_bf16, float *x_out, int batch, int seqlen, int chunk,
-                                const PrefillWs &ws, const dfssm_taps *taps, hipStream_t stream);
+                                const PrefillWs &ws, const dfssm_taps *taps, hipStream_t stream,
+                                const PrefillCodec *codec = nullptr);
 
 // Per-layer SSM step + gate for `batch` tokens from ws.xbc/zbuf/dtbuf into ws.gbuf (decode.hip).
 hipError_t launch_ssm_step(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
@@ -184,6 +190,11 @@ hipError_t launch_state_encode(const float *ssm, int64_t rows, int N, uint32_t *
                                hipStream_t stream);
 hipError_t launch_state_decode(const uint32_t *fields, const float *stats, int64_t rows, int N, float *ssm,
                                hipStream_t stream);
+// The chunked scan's carry with the codec on the state entering every chunk after the first
+// (replaces k_ssd_scan): state [BH][P][N] initial -> final, sloc [BH][nch][P][N] chunk contributions
+// -> entering states, lam_end [BH][nch]; taps [nch][BH][P][N] or null. P must be 64.
+hipError_t launch_ssd_scan_codec(float *state, float *sloc, const float *lam_end, int BH, int nch, int N, int P,
+                                 float *tap_pre, float *tap_in, hipStream_t stream);
 
 // Enqueue y = RMSNorm(h) * w for `batch` rows of length D, also copying y to `y2` when non-null.
 hipError_t launch_final_norm(const float *h, const float *w, float *y, float *y2, int D, float eps,

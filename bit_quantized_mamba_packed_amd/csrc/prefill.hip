@@ -1175,7 +1175,8 @@ PrefillWs carve_prefill_ws(const Shape &s, int batch, int seqlen, int chunk, voi
 
 hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, const dfssm_layer_state &st,
                                 const void *x_in, int x_bf16, float *x_out, int batch, int seqlen, int chunk,
-                                const PrefillWs &ws, const dfssm_taps *taps, hipStream_t stream) {
+                                const PrefillWs &ws, const dfssm_taps *taps, hipStream_t stream,
+                                const PrefillCodec *codec) {
     const int M = batch * seqlen;
     const int nch = (seqlen + chunk - 1) / chunk;
     const TapPtrs tp = tap_offset(taps, s, 0);
@@ -1286,8 +1287,14 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         const int nblk = batch * s.H * nch;
         k_ssd_state<<<nblk, kSsdBlock, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ssd_scan<<<dim3((s.P * s.N / 2 + kBlock - 1) / kBlock, batch * s.H), kBlock, 0, stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (codec && codec->on) {
+            e = launch_ssd_scan_codec(st.ssm, ws.sloc, ws.lam_end, batch * s.H, nch, s.N, s.P, codec->tap_pre,
+                                      codec->tap_in, stream);
+        } else {
+            k_ssd_scan<<<dim3((s.P * s.N / 2 + kBlock - 1) / kBlock, batch * s.H), kBlock, 0, stream>>>(a);
+            e = hipGetLastError();
+        }
+        if (e != hipSuccess) return e;
         if (s.N <= 32) k_ssd_out<1><<<nblk, kSsdBlock, 0, stream>>>(a);
         else if (s.N <= 64) k_ssd_out<2><<<nblk, kSsdBlock, 0, stream>>>(a);
         else if (s.N <= 128) k_ssd_out<4><<<nblk, kSsdBlock, 0, stream>>>(a);

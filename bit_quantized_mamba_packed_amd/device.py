@@ -166,14 +166,20 @@ def stack_prefill(d, layers: list, states: list, final_w: torch.Tensor, x_in: to
 
 
 def layer_prefill(d, layer: DeviceLayer, state: DeviceState, x_in: torch.Tensor, x_out: torch.Tensor, chunk: int,
-                  ws: torch.Tensor, taps: Taps = None) -> None:
-    """x_in [batch][seqlen][d_model] fp32 or bf16 (torch.bfloat16 is passed as its bit patterns)."""
+                  ws: torch.Tensor, taps: Taps = None, state_codec: bool = False, chunk_state_pre: torch.Tensor = None,
+                  chunk_state_in: torch.Tensor = None) -> None:
+    """x_in [batch][seqlen][d_model] fp32 or bf16 (torch.bfloat16 is passed as its bit patterns).
+    state_codec: DF-SSD (dfssm_layer_prefill_ex), with optional taps of the chunk-entering states."""
     batch, seqlen = x_in.shape[0], x_in.shape[1]
     dtype = L.DFSSM_BF16 if x_in.dtype == torch.bfloat16 else L.DFSSM_F32
-    st = L.dfssm_layer_prefill(dims_struct(d), layer.struct, state.struct, x_in.data_ptr(), dtype, x_out.data_ptr(),
-                               batch, seqlen, chunk, ws.data_ptr(), ws.numel(),
-                               None if taps is None else taps.struct, stream_handle())
-    L.check(st, "dfssm_layer_prefill")
+    opts = None
+    if state_codec:
+        opts = L.dfssm_prefill_opts(1, 0, None if chunk_state_pre is None else chunk_state_pre.data_ptr(),
+                                    None if chunk_state_in is None else chunk_state_in.data_ptr())
+    st = L.dfssm_layer_prefill_ex(dims_struct(d), layer.struct, state.struct, x_in.data_ptr(), dtype, x_out.data_ptr(),
+                                  batch, seqlen, chunk, ws.data_ptr(), ws.numel(),
+                                  None if taps is None else taps.struct, opts, stream_handle())
+    L.check(st, "dfssm_layer_prefill_ex")
 
 
 class DeviceEmbedding:

@@ -205,6 +205,33 @@ int dfssm_layer_prefill(const dfssm_dims *dims, const dfssm_layer_weights *w,
                         void *ws, size_t ws_bytes, const dfssm_taps *taps, void *stream);
 
 /*
+ * dfssm_layer_prefill with options (opts: HOST pointer, NULL = defaults, which is dfssm_layer_prefill).
+ *   state_codec       1: DF-SSD ([DF-SSM] §3.4 "Density Field State Representation", App. D): the SSM
+ *                     state entering every chunk after the first passes through the density field
+ *                     codec of dfssm_state_encode / dfssm_state_decode (encoded and read back, per
+ *                     state row) before the chunk uses it; the state after the last chunk, written
+ *                     back to state->ssm, is not coded. 0: off.
+ *   reserved          must be 0.
+ *   chunk_state_pre   optional (state_codec only), device [n_chunks][batch][nheads][headdim][d_state]
+ *                     fp32, n_chunks = ceil(seqlen / chunk): the state entering each chunk before the
+ *                     codec (chunk 0: the initial state).
+ *   chunk_state_in    optional, the same shape: the state each chunk uses (after the codec).
+ * The codec carry runs one wave per (sequence, head), sequentially over the chunks.
+ */
+typedef struct dfssm_prefill_opts {
+    int32_t state_codec;
+    int32_t reserved;
+    float  *chunk_state_pre;
+    float  *chunk_state_in;
+} dfssm_prefill_opts;
+
+int dfssm_layer_prefill_ex(const dfssm_dims *dims, const dfssm_layer_weights *w,
+                           const dfssm_layer_state *state, const void *x_in, int32_t x_dtype,
+                           float *x_out, int32_t batch, int32_t seqlen, int32_t chunk,
+                           void *ws, size_t ws_bytes, const dfssm_taps *taps,
+                           const dfssm_prefill_opts *opts, void *stream);
+
+/*
  * Kernel selection for dfssm_stack_decode_ex (every path computes the same decode; zero-initialise
  * the struct for the defaults).
  *   path      DFSSM_PATH_*; a path that cannot run the shape and batch is DFSSM_EUNSUPPORTED.

@@ -295,3 +295,18 @@ def test_dfw_workspace_holds_every_region():
     r = lambda v: (v + 255) // 256 * 256
     for K, rank, B in ((256, 8, 3), (2048, 32, 4), (8192, 64, 256), (384, 5, 5)):
         assert L.dfssm_dfw_workspace_bytes(K, rank, B) == r(B * K) + r(B * K) + r(4 * B) + r(4 * B) + r(4 * B * rank)
+
+
+def test_layer_prefill_ex_rejects_bad_options():
+    d = _dims()
+    w = _fake_weights()
+    st = L.dfssm_layer_state(FAKE, FAKE)
+    need = L.dfssm_workspace_bytes(d, L.DFSSM_OP_LAYER_PREFILL, 1, 64)
+
+    def call(opts):
+        return L.dfssm_layer_prefill_ex(d, w, st, FAKE, L.DFSSM_F32, FAKE + 4096, 1, 64, 16, FAKE, need, None, opts)
+
+    assert call(L.dfssm_prefill_opts(2, 0, None, None)) == L.DFSSM_EINVAL
+    assert call(L.dfssm_prefill_opts(1, 1, None, None)) == L.DFSSM_EINVAL
+    assert call(L.dfssm_prefill_opts(1, 0, FAKE + 4, None)) == L.DFSSM_EINVAL
+    assert call(L.dfssm_prefill_opts(0, 0, FAKE, None)) == L.DFSSM_EINVAL      # taps without the codec
