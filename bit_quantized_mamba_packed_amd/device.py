@@ -124,6 +124,8 @@ def workspace(d, op: int, batch: int, seqlen: int = 0, n_layers: int = 0, device
 def layer_decode(d, layer: DeviceLayer, state: DeviceState, x_in: torch.Tensor, x_out: torch.Tensor,
                  ws: torch.Tensor, taps: Taps = None) -> None:
     batch = x_in.shape[0]
+    _need("x_in", x_in, torch.float32, batch * d.d_model)
+    _need("x_out", x_out, torch.float32, batch * d.d_model)
     st = L.dfssm_layer_decode(dims_struct(d), layer.struct, state.struct, x_in.data_ptr(), x_out.data_ptr(),
                               batch, ws.data_ptr(), ws.numel(), None if taps is None else taps.struct,
                               stream_handle())
@@ -139,6 +141,10 @@ def stack_decode(d, layers: list, states: list, final_w: torch.Tensor, x0: torch
                  n_steps: int, ws: torch.Tensor, taps: Taps = None, path: int = L.DFSSM_PATH_AUTO,
                  launch: int = L.DFSSM_LAUNCH_COOPERATIVE) -> None:
     """dfssm_stack_decode_ex; the call's status word stays in ws (stack_status reads it)."""
+    batch = x0.shape[0]
+    _need("x0", x0, torch.float32, batch * d.d_model)
+    _need("y", y, torch.float32, n_steps * batch * d.d_model)
+    _need("final_w", final_w, torch.float32, d.d_model)
     arr_w, arr_s = _arrays(layers, states)
     opts = L.dfssm_stack_opts(path, launch)
     st = L.dfssm_stack_decode_ex(dims_struct(d), arr_w, arr_s, len(layers), final_w.data_ptr(), x0.data_ptr(),
@@ -159,6 +165,9 @@ def stack_prefill(d, layers: list, states: list, final_w: torch.Tensor, x_in: to
     arr_w, arr_s = _arrays(layers, states)
     batch, seqlen = x_in.shape[0], x_in.shape[1]
     dtype = L.DFSSM_BF16 if x_in.dtype == torch.bfloat16 else L.DFSSM_F32
+    _need("x_in", x_in, torch.bfloat16 if dtype == L.DFSSM_BF16 else torch.float32, batch * seqlen * d.d_model)
+    _need("y", y, torch.float32, batch * seqlen * d.d_model)
+    _need("final_w", final_w, torch.float32, d.d_model)
     st = L.dfssm_stack_prefill(dims_struct(d), arr_w, arr_s, len(layers), final_w.data_ptr(), x_in.data_ptr(),
                                dtype, y.data_ptr(), batch, seqlen, chunk, ws.data_ptr(), ws.numel(),
                                None if taps is None else taps.struct, stream_handle())
@@ -172,7 +181,13 @@ def layer_prefill(d, layer: DeviceLayer, state: DeviceState, x_in: torch.Tensor,
     state_codec: DF-SSD (dfssm_layer_prefill_ex), with optional taps of the chunk-entering states."""
     batch, seqlen = x_in.shape[0], x_in.shape[1]
     dtype = L.DFSSM_BF16 if x_in.dtype == torch.bfloat16 else L.DFSSM_F32
+    _need("x_in", x_in, torch.bfloat16 if dtype == L.DFSSM_BF16 else torch.float32, batch * seqlen * d.d_model)
+    _need("x_out", x_out, torch.float32, batch * seqlen * d.d_model)
     opts = None
+    nch = (seqlen + chunk - 1) // chunk if chunk > 0 else 0
+    for name, t in (("chunk_state_pre", chunk_state_pre), ("chunk_state_in", chunk_state_in)):
+        if t is not None:
+            _need(name, t, torch.float32, nch * batch * d.nheads * d.headdim * d.d_state)
     if state_codec:
         opts = L.dfssm_prefill_opts(1, 0, None if chunk_state_pre is None else chunk_state_pre.data_ptr(),
                                     None if chunk_state_in is None else chunk_state_in.data_ptr())
@@ -192,8 +207,28 @@ class DeviceEmbedding:
         self.struct = L.dfssm_embedding(self.codes.data_ptr(), self.row_scale.data_ptr(), self.vocab, self.d_model)
 
 
+def _need(name: str, t: torch.Tensor, dtype, numel: int) -> None:
+    """A device tensor the library will read or write: on the GPU, contiguous, of the given dtype
+    (or element size) and with at least `numel` elements; ValueError otherwise, before any launch."""
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: not a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+    if isinstance(dtype, int):
+        if t.element_size() != dtype:
+            raise ValueError(f"{name}: expected {dtype}-byte elements, got {t.dtype}")
+    elif t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: holds {t.numel()} elements, needs {numel}")
+
+
 def embed(emb: DeviceEmbedding, tokens: torch.Tensor, x: torch.Tensor) -> None:
     """x [batch][d_model] fp32 = the embedding rows of tokens (int32 device tensor)."""
+    _need("tokens", tokens, torch.int32, 1)
+    _need("x", x, torch.float32, tokens.numel() * emb.d_model)
     L.check(L.dfssm_embed(emb.struct, tokens.data_ptr(), tokens.numel(), x.data_ptr(), stream_handle()), "dfssm_embed")
 
 
@@ -201,6 +236,11 @@ def lm_head(d, emb: DeviceEmbedding, y: torch.Tensor, logits: torch.Tensor = Non
             ws: torch.Tensor = None, taps: dict = None) -> torch.Tensor:
     """Logits and/or greedy next tokens of y [batch][d_model]; returns the workspace it used."""
     batch = y.shape[0]
+    _need("y", y, torch.float32, batch * emb.d_model)
+    if logits is not None:
+        _need("logits", logits, torch.float32, batch * emb.vocab)
+    if next_tokens is not None:
+        _need("next_tokens", next_tokens, torch.int32, batch)
     if ws is None:
         ws = workspace(d, L.DFSSM_OP_LM_HEAD, batch)
     t = None
@@ -217,6 +257,7 @@ def state_encode(d, ssm: torch.Tensor, batch: int):
     """Density field codec of an SSM state [batch][H][P][N] -> (fields uint32 [rows][W], stats [rows][2])."""
     rows = batch * d.nheads * d.headdim
     W = L.dfssm_state_field_words(d.d_state)
+    _need("ssm", ssm, torch.float32, rows * d.d_state)
     fields = torch.empty((rows, W), dtype=torch.int32, device=ssm.device)
     stats = torch.empty((rows, 2), dtype=torch.float32, device=ssm.device)
     L.check(L.dfssm_state_encode(dims_struct(d), ssm.data_ptr(), batch, fields.data_ptr(), stats.data_ptr(),
@@ -225,6 +266,11 @@ def state_encode(d, ssm: torch.Tensor, batch: int):
 
 
 def state_decode(d, fields: torch.Tensor, stats: torch.Tensor, batch: int, ssm: torch.Tensor) -> None:
+    """SSM state [batch][H][P][N] read back from fields [rows][W] and stats [rows][2]."""
+    rows = batch * d.nheads * d.headdim
+    _need("fields", fields, 4, rows * L.dfssm_state_field_words(d.d_state))
+    _need("stats", stats, torch.float32, rows * 2)
+    _need("ssm", ssm, torch.float32, rows * d.d_state)
     L.check(L.dfssm_state_decode(dims_struct(d), fields.data_ptr(), stats.data_ptr(), batch, ssm.data_ptr(),
                                  stream_handle()), "dfssm_state_decode")
 
@@ -247,6 +293,13 @@ class DeviceDfwProj:
 def dfw_project(p: DeviceDfwProj, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor = None, taps: dict = None) -> None:
     """y [batch][n_out] = the 17-level projection of x [batch][n_in] (both fp32 on the device)."""
     batch = int(x.shape[0])
+    _need("x", x, torch.float32, batch * p.n_in)
+    _need("y", y, torch.float32, batch * p.n_out)
+    if taps:
+        for k, dt, n in (("q", torch.int8, batch * p.n_in), ("s", torch.float32, batch),
+                         ("acc", torch.int32, batch * p.n_out), ("t", torch.int32, batch * p.rank)):
+            if taps.get(k) is not None:
+                _need(f"taps[{k}]", taps[k], dt, n)
     need = L.dfssm_dfw_workspace_bytes(p.n_in, p.rank, batch)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)

@@ -310,3 +310,12 @@ def test_layer_prefill_ex_rejects_bad_options():
     assert call(L.dfssm_prefill_opts(1, 1, None, None)) == L.DFSSM_EINVAL
     assert call(L.dfssm_prefill_opts(1, 0, FAKE + 4, None)) == L.DFSSM_EINVAL
     assert call(L.dfssm_prefill_opts(0, 0, FAKE, None)) == L.DFSSM_EINVAL      # taps without the codec
+
+
+def test_device_wrappers_reject_host_and_short_tensors():
+    import torch
+    from bit_quantized_mamba_packed_amd import device as Dv
+    with pytest.raises(ValueError, match="not a device tensor"):
+        Dv._need("x", torch.zeros(4), torch.float32, 4)
+    with pytest.raises(ValueError):
+        Dv._need("x", None, torch.float32, 4)
