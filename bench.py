@@ -600,7 +600,7 @@ def main() -> int:
         print(json.dumps(write_counters(*args.write_counters, args.tokens), indent=1))
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
               "the batch-1 decode does not shard usefully (its per-layer all-reduces would cost more than the layer), "
               "and batched decode and prefill would shard by sequence, which this single-GPU build does not run.", file=sys.stderr)
         return 2
