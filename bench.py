@@ -602,7 +602,7 @@ def main() -> int:
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
               "the batch-1 decode does not shard usefully (its per-layer all-reduces would cost more than the layer), "
-              "and batched decode and prefill would shard by sequence, which this single-GPU build does not run.", file=sys.stderr)
+              "and batched decode and prefill would shard by sequence, which the library does not run across GPUs.", file=sys.stderr)
         return 2
 
     import numpy as np
