@@ -82,6 +82,39 @@ __device__ __forceinline__ void tile_store(float *dst, int64_t r0, int nr, int c
     }
 }
 
+// a / b rounded to nearest (the IEEE quotient) from y = RN(1 / b): q0 = RN(a y) is within two ulps;
+// one fma correction makes it faithful, and the second is Markstein's step, which then yields the
+// correctly rounded quotient (for normal b and quotients that neither overflow nor underflow; the
+// codes only depend on quotients in [0, 1], smaller ones clamp to 0). Five operations instead of
+// the ten of a full division, for the 8-bit codes of a row that share one divisor.
+__device__ __forceinline__ float div_by_recip(float a, float b, float y) {
+    const float q0 = a * y;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, b, a), y, q0);
+    return __builtin_fmaf(__builtin_fmaf(-q1, b, a), y, q1);
+}
+
+// 2^m as a float, -126 <= m <= 127.
+__device__ __forceinline__ float pow2f(int m) { return __builtin_bit_cast(float, (uint32_t)(m + 127) << 23); }
+
+// The divisor of a row's codes brought to [1, 2) by an exact power-of-two scale s1 * s2 (applied to
+// every dividend as well, so each quotient is unchanged), which keeps RN(1 / divisor) normal for any
+// span > 0. A span of 0 (a constant row, whose field is all zero) keeps scale 1.
+struct RowDivisor {
+    float s1, s2, b, y;
+};
+__device__ __forceinline__ RowDivisor row_divisor(float span) {
+    const int k = span > 0.f ? -ilogbf(span) : 0;
+    RowDivisor d;
+    d.s1 = pow2f(k >> 1);
+    d.s2 = pow2f(k - (k >> 1));
+    d.b = (span * d.s1) * d.s2;
+    d.y = 1.0f / d.b;
+    return d;
+}
+__device__ __forceinline__ float row_quotient(float a, const RowDivisor &d) {
+    return div_by_recip((a * d.s1) * d.s2, d.b, d.y);
+}
+
 // Readout of one row's field: lo + span * (ones among the value's cells) / cells.
 template <int N>
 __device__ __forceinline__ void row_decode(const uint32_t (&word)[codec_words(N)], float mu, float sigma,
@@ -143,9 +176,10 @@ __global__ __launch_bounds__(kCodecRows) void k_state_encode(const float *__rest
 
     // 8-bit codes, kept as t - 128 so that a cell's decision is the sign of e + (t - 128)
     int tm[N];
+    const RowDivisor dv = row_divisor(span);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const float x = fminf(fmaxf((v[i] - lo) / span, 0.f), 1.f);
+        const float x = fminf(fmaxf(row_quotient(v[i] - lo, dv), 0.f), 1.f);
         tm[i] = (int)rintf(x * 255.0f) - 128;
     }
 
@@ -276,9 +310,10 @@ __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) 
             const float sigma = sqrtf(acc2 / (float)N);
             const float lo = mu - 3.0f * sigma, span = 6.0f * sigma;
             int tm[N];
+            const RowDivisor dv = row_divisor(span);
 #pragma unroll
             for (int i = 0; i < N; ++i) {
-                const float x = fminf(fmaxf((S[i] - lo) / span, 0.f), 1.f);
+                const float x = fminf(fmaxf(row_quotient(S[i] - lo, dv), 0.f), 1.f);
                 tm[i] = (int)rintf(x * 255.0f) - 128;
             }
             uint32_t word[W];
