@@ -526,10 +526,28 @@ def run_dfssd_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> d
             raise SystemExit("non-finite DF-SSD prefill output")
         res[name] = round(sum(ms) / len(ms), 4)
     extra = res["dfssd"] - res["plain"]
+    # the whole stack with DF-SSD in every layer (dfssm_stack_prefill_ex)
+    nL = args.layers
+    conv_all = torch.zeros((nL, 1, dims.conv_dim, dims.d_conv - 1), dtype=torch.float32, device="cuda")
+    ssm_all = torch.zeros((nL, 1, dims.nheads, dims.headdim, dims.d_state), dtype=torch.float32, device="cuda")
+    states = [Dv.DeviceState.from_tensors(conv_all[l], ssm_all[l], dims, 1) for l in range(nL)]
+    fw = torch.ones(dims.d_model, dtype=torch.float32, device="cuda")
+    wss = Dv.workspace(dims, L.DFSSM_OP_STACK_PREFILL, 1, S, nL)
+
+    def stack_step():
+        conv_all.zero_()
+        ssm_all.zero_()
+        Dv.stack_prefill(dims, layers, states, fw, xb, y, Q, wss, state_codec=True)
+
+    _, sms = timed(stack_step, max(1, min(args.steps, 3)), 1, torch)
+    if not torch.isfinite(y).all():
+        raise SystemExit("non-finite DF-SSD stack prefill output")
+    stack_ms = sum(sms) / len(sms)
     return {"metric": "DF-SSD layer prefill, 1.3B layer, 2048 bf16 tokens, chunk 256: ms per layer",
             "value": res["dfssd"], "unit": "ms", "higher_is_better": False,
             "config": {"workload": "dfssd_prefill_1p3b_layer2048", "chunk": Q, "boundaries": S // Q - 1},
             "plain_ms": res["plain"], "codec_carry_ms": round(extra, 4),
+            "stack": {"layers": nL, "ms_per_prefill": round(stack_ms, 3), "tokens_per_s": round(S / stack_ms * 1e3, 1)},
             "note": "codec carry = DF-SSD minus plain (the scan with 4096 state rows encoded and read back at "
                     "each of 7 boundaries, one lane per row)"}
 
@@ -635,7 +653,7 @@ def main() -> int:
             sec[name] = {k: r[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline",
                                            "roofline_scaffold_gemms", "points", "us_per_call",
                                            "greedy_full_model", "cpu_baseline", "decode", "plain_ms",
-                                           "codec_carry_ms") if k in r}
+                                           "codec_carry_ms", "stack") if k in r}
         out["secondary"] = sec
     print(json.dumps(out), flush=True)
     return 0

@@ -37,7 +37,7 @@ DFSSM_BF16 = 1
 
 # every symbol include/dfssm.h declares
 EXPORTS = ("dfssm_workspace_bytes", "dfssm_layer_decode", "dfssm_layer_decode_noalloc", "dfssm_layer_prefill",
-           "dfssm_layer_prefill_ex",
+           "dfssm_layer_prefill_ex", "dfssm_stack_prefill_ex",
            "dfssm_stack_decode", "dfssm_stack_decode_ex", "dfssm_stack_prefill", "dfssm_embed", "dfssm_lm_head",
            "dfssm_state_field_words", "dfssm_state_encode", "dfssm_state_decode", "dfssm_dfw_workspace_bytes",
            "dfssm_dfw_project", "dfssm_strerror")
@@ -144,6 +144,11 @@ def load() -> C.CDLL:
                                         C.POINTER(dfssm_layer_state), C.c_int32, P, P, C.c_int32, P,
                                         C.c_int32, C.c_int32, C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps), P]
     lib.dfssm_stack_prefill.restype = C.c_int
+    lib.dfssm_stack_prefill_ex.argtypes = [C.POINTER(dfssm_dims), C.POINTER(dfssm_layer_weights),
+                                           C.POINTER(dfssm_layer_state), C.c_int32, P, P, C.c_int32, P,
+                                           C.c_int32, C.c_int32, C.c_int32, P, C.c_size_t, C.POINTER(dfssm_taps),
+                                           C.POINTER(dfssm_prefill_opts), P]
+    lib.dfssm_stack_prefill_ex.restype = C.c_int
     lib.dfssm_embed.argtypes = [C.POINTER(dfssm_embedding), P, C.c_int32, P, P]
     lib.dfssm_embed.restype = C.c_int
     lib.dfssm_lm_head.argtypes = [C.POINTER(dfssm_embedding), P, C.c_int32, P, P, P, C.c_size_t,
@@ -207,6 +212,12 @@ def dfssm_stack_decode_ex(dims, layers, states, n_layers, final_norm_w, x0, y, b
                           taps=None, opts=None, stream=None) -> int:
     return int(load().dfssm_stack_decode_ex(C.byref(dims), layers, states, n_layers, final_norm_w, x0, y, batch,
                                             n_steps, ws, ws_bytes, _ref(taps), _ref(opts), stream))
+
+
+def dfssm_stack_prefill_ex(dims, layers, states, n_layers, final_norm_w, x_in, x_dtype, y, batch, seqlen, chunk, ws,
+                           ws_bytes, taps=None, opts=None, stream=None) -> int:
+    return int(load().dfssm_stack_prefill_ex(C.byref(dims), layers, states, n_layers, final_norm_w, x_in, x_dtype, y,
+                                             batch, seqlen, chunk, ws, ws_bytes, _ref(taps), _ref(opts), stream))
 
 
 def dfssm_stack_prefill(dims, layers, states, n_layers, final_norm_w, x_in, x_dtype, y, batch, seqlen, chunk, ws,

@@ -376,7 +376,18 @@ int dfssm_stack_prefill(const dfssm_dims *dims, const dfssm_layer_weights *layer
                         int32_t n_layers, const float *final_norm_w, const void *x_in, int32_t x_dtype, float *y,
                         int32_t batch, int32_t seqlen, int32_t chunk, void *ws, size_t ws_bytes,
                         const dfssm_taps *taps, void *stream) {
+    return dfssm_stack_prefill_ex(dims, layers, states, n_layers, final_norm_w, x_in, x_dtype, y, batch, seqlen, chunk,
+                                  ws, ws_bytes, taps, nullptr, stream);
+}
+
+int dfssm_stack_prefill_ex(const dfssm_dims *dims, const dfssm_layer_weights *layers, const dfssm_layer_state *states,
+                           int32_t n_layers, const float *final_norm_w, const void *x_in, int32_t x_dtype, float *y,
+                           int32_t batch, int32_t seqlen, int32_t chunk, void *ws, size_t ws_bytes,
+                           const dfssm_taps *taps, const dfssm_prefill_opts *opts, void *stream) {
     int r;
+    const dfssm_prefill_opts o = opts ? *opts : dfssm_prefill_opts{};
+    if ((o.state_codec != 0 && o.state_codec != 1) || o.reserved != 0) return DFSSM_EINVAL;
+    if (o.chunk_state_pre || o.chunk_state_in) return DFSSM_EINVAL;   // per-layer taps: the layer call
     if ((r = check_dims(dims))) return r;
     if (!layers || !states || n_layers <= 0 || batch <= 0 || seqlen <= 0) return DFSSM_EINVAL;
     if (n_layers > 1024) return DFSSM_EUNSUPPORTED;
@@ -402,8 +413,9 @@ int dfssm_stack_prefill(const dfssm_dims *dims, const dfssm_layer_weights *layer
         const void *src = l == 0 ? x_in : ((n_layers - l) % 2 == 0 ? static_cast<const void *>(y) : hbuf);
         float *dst = (n_layers - 1 - l) % 2 == 0 ? y : hbuf;
         const dfssm_taps tl = taps_for_layer(taps, s, l * per_layer);
+        const PrefillCodec pc{o.state_codec == 1, nullptr, nullptr};
         hipError_t e = launch_layer_prefill(s, layers[l], states[l], src, l == 0 && x_dtype == DFSSM_BF16, dst, batch,
-                                            seqlen, chunk, p, taps ? &tl : nullptr, st);
+                                            seqlen, chunk, p, taps ? &tl : nullptr, st, &pc);
         if (e != hipSuccess) return DFSSM_EHIP;
     }
     return hip_status(launch_final_norm(y, final_norm_w, y, nullptr, s.D, s.eps, (int)per_layer, st));

@@ -160,18 +160,20 @@ def stack_status(ws: torch.Tensor) -> int:
 
 
 def stack_prefill(d, layers: list, states: list, final_w: torch.Tensor, x_in: torch.Tensor, y: torch.Tensor,
-                  chunk: int, ws: torch.Tensor, taps: Taps = None) -> None:
-    """x_in [batch][seqlen][d_model] fp32 or bf16 -> y = RMSNorm(stack(x_in)) * final_w, fp32."""
+                  chunk: int, ws: torch.Tensor, taps: Taps = None, state_codec: bool = False) -> None:
+    """x_in [batch][seqlen][d_model] fp32 or bf16 -> y = RMSNorm(stack(x_in)) * final_w, fp32.
+    state_codec: DF-SSD in every layer (dfssm_stack_prefill_ex)."""
     arr_w, arr_s = _arrays(layers, states)
     batch, seqlen = x_in.shape[0], x_in.shape[1]
     dtype = L.DFSSM_BF16 if x_in.dtype == torch.bfloat16 else L.DFSSM_F32
     _need("x_in", x_in, torch.bfloat16 if dtype == L.DFSSM_BF16 else torch.float32, batch * seqlen * d.d_model)
     _need("y", y, torch.float32, batch * seqlen * d.d_model)
     _need("final_w", final_w, torch.float32, d.d_model)
-    st = L.dfssm_stack_prefill(dims_struct(d), arr_w, arr_s, len(layers), final_w.data_ptr(), x_in.data_ptr(),
-                               dtype, y.data_ptr(), batch, seqlen, chunk, ws.data_ptr(), ws.numel(),
-                               None if taps is None else taps.struct, stream_handle())
-    L.check(st, "dfssm_stack_prefill")
+    opts = L.dfssm_prefill_opts(1 if state_codec else 0, 0, None, None)
+    st = L.dfssm_stack_prefill_ex(dims_struct(d), arr_w, arr_s, len(layers), final_w.data_ptr(), x_in.data_ptr(),
+                                  dtype, y.data_ptr(), batch, seqlen, chunk, ws.data_ptr(), ws.numel(),
+                                  None if taps is None else taps.struct, opts, stream_handle())
+    L.check(st, "dfssm_stack_prefill_ex")
 
 
 def layer_prefill(d, layer: DeviceLayer, state: DeviceState, x_in: torch.Tensor, x_out: torch.Tensor, chunk: int,

@@ -294,6 +294,15 @@ int dfssm_stack_prefill(const dfssm_dims *dims, const dfssm_layer_weights *layer
                         int32_t batch, int32_t seqlen, int32_t chunk, void *ws, size_t ws_bytes,
                         const dfssm_taps *taps, void *stream);
 
+/* dfssm_stack_prefill with options (opts: HOST pointer, NULL = defaults): state_codec applies DF-SSD
+ * (see dfssm_prefill_opts) in every layer; the chunk-state taps must be NULL here (take them from
+ * dfssm_layer_prefill_ex). */
+int dfssm_stack_prefill_ex(const dfssm_dims *dims, const dfssm_layer_weights *layers,
+                           const dfssm_layer_state *states, int32_t n_layers,
+                           const float *final_norm_w, const void *x_in, int32_t x_dtype, float *y,
+                           int32_t batch, int32_t seqlen, int32_t chunk, void *ws, size_t ws_bytes,
+                           const dfssm_taps *taps, const dfssm_prefill_opts *opts, void *stream);
+
 /*
  * The tied int8 embedding / LM head ([DF-SSM] §3.3: the embedding is quantized to int8 per row;
  * Table 1: "Embedding + LM head (tied)", 103 MB for the 1.3B model):

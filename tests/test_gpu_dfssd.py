@@ -119,3 +119,33 @@ def test_dfssd_1p3b_layer_2048_tokens_bf16():
     check_codec_boundaries(pre, ent, ssm0, rows_per_boundary=48, seed=1)
     check_forced(lw, xs[0], conv0[0], ssm0[0], out[0], {k: v[0] for k, v in tps.items()}, (final[0][0], final[1][0]),
                  pre[:, 0], ent[:, 0], 256, "1p3b")
+
+
+def test_dfssd_stack_prefill_equals_the_layer_calls():
+    """dfssm_stack_prefill_ex with state_codec: the same bits as DF-SSD layer prefills one after the
+    other plus the library's final norm (the same kernels), and every layer's coded boundaries hold
+    the codec's decisions (checked through the layer calls' taps)."""
+    L, Dv = _lib()
+    dims = gen.DIMS["tiny"]
+    nL, B, T, Q = 3, 2, 130, 32
+    layers = gen.stack_weights(dims, nL, seed=23)
+    states0 = [gen.initial_states(dims, B, l, 23, std=0.1) for l in range(nL)]
+    xs = gen.token_inputs(dims, (B, T), 23, tag=6)
+    fw = np.random.default_rng(23).uniform(0.5, 1.5, dims.d_model).astype(np.float32)
+    say(f"case: DF-SSD tiny stack prefill, {nL} layers, batch {B}, {T} tokens, chunk {Q}")
+    devs = [Dv.DeviceLayer(w) for w in layers]
+    sts = [Dv.DeviceState(c, s) for c, s in states0]
+    x = torch.from_numpy(xs).cuda()
+    y = torch.empty((B, T, dims.d_model), device="cuda")
+    ws = Dv.workspace(dims, L.DFSSM_OP_STACK_PREFILL, B, T, nL)
+    Dv.stack_prefill(dims, devs, sts, torch.from_numpy(fw).cuda(), x, y, Q, ws, state_codec=True)
+    torch.cuda.synchronize()
+    ys = y.cpu().numpy()
+    finals = [(s.ssm.cpu().numpy(), s.conv.cpu().numpy()) for s in sts]
+    h = xs
+    for l in range(nL):
+        out, _, final, pre, ent = run_dfssd(dims, layers[l], h, states0[l][0], states0[l][1], Q)
+        check_codec_boundaries(pre, ent, states0[l][1])
+        assert np.array_equal(final[1], finals[l][0]) and np.array_equal(final[0], finals[l][1]), l
+        h = out
+    assert np.abs(O.rmsnorm(h, fw, dims.eps) - ys).max() < 1e-5
