@@ -23,6 +23,12 @@
  * conv_dim = d_inner + 2*ngroups*d_state; nheads = d_inner / headdim; head h reads B and C of
  * group h*ngroups/nheads.
  *
+ * Around the layer: the tied int8 embedding and LM head (dfssm_embed, dfssm_lm_head; paper §3.3,
+ * Table 1), the projection with the 17-level scaffold the 1-bit one is binarised from
+ * (dfssm_dfw_project; §3.1 Eq. (1)), and the density field codec of the SSM state, standalone
+ * (dfssm_state_encode / dfssm_state_decode) and at the chunk boundaries of the prefill scan
+ * (dfssm_layer_prefill_ex / dfssm_stack_prefill_ex; §3.4, App. D).
+ *
  * Conventions
  *  - Every pointer is a DEVICE pointer (hipMalloc'd or equivalent) unless marked HOST.
  *  - The caller owns all memory. Weights are read-only; states are updated in place; no pointer
