@@ -34,14 +34,18 @@ namespace dfssm {
 
 namespace {
 
-// in_proj rows per GEMV thread after the B/C rows (rows rg + NG * i): with CPR lanes per row
-// (CPR = d_model / 128) the items of the supported shapes hold at most 80, 48 or 32 such rows
-constexpr int f2_maxi(int cpr) { return cpr >= 16 ? 5 : cpr >= 8 ? 2 : 1; }
-constexpr int F2_SBLK = 8;    // 1 KB blocks of in_proj sign rows each wave copies per layer
+// Threads per workgroup: eight waves, two on each SIMD, so that one wave's LDS, DPP and memory
+// latencies are covered by the other's work (with one wave per SIMD every one of them is exposed).
+constexpr int F2_T = 512;
+constexpr int F2_W = F2_T / 64;
+// in_proj rows per GEMV thread (rows rg + NG * i, the B/C rows first): with CPR lanes per row
+// (CPR = d_model / 128, NG = F2_T / CPR row groups) an item may hold up to 96, 64 or 128 rows
+constexpr int f2_maxi(int cpr) { return cpr >= 16 ? 3 : 1; }
+constexpr int F2_SBLK = 4;    // 1 KB blocks of in_proj sign rows each wave copies per layer
 constexpr int F2_UPC = 2;     // LoRA-up chunks (16 B) per row: rank <= 32
 // out_proj rows per GEMV thread: a role-2 workgroup holds d_model / 128 rows
-constexpr int f2_maxo(int cpr) { return cpr >= 32 ? 2 : 1; }
-constexpr int F2_FPT = 4;     // SSM state float4s per thread and token
+constexpr int f2_maxo(int cpr) { return cpr >= 64 ? 2 : 1; }
+constexpr int F2_FPT = 2;     // SSM state float4s per thread and token
 constexpr int F2_ROWS = 512;  // item rows (incl. padding rows) per workgroup, at most
 constexpr unsigned kSpin2 = 1u << 21;
 constexpr int kSleep2 = 1;
@@ -210,10 +214,22 @@ __device__ __forceinline__ float f2_group_sum(float v, int w) {
 
 __device__ __forceinline__ float f2_ss(const float4 &v) { return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w; }
 
+// The F2_W per-wave partials in a fixed pairwise order (every workgroup gets the same bits).
+__device__ __forceinline__ float f2_sum8(const float *v) {
+    return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+__device__ __forceinline__ float f2_max8(const float *v) {
+    return fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+}
+__device__ __forceinline__ int f2_isum8(const int *v) {
+    return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+static_assert(F2_W == 8, "the partial combinations take eight waves");
+
 // The stack's final RMSNorm, (h * r) * w, of one gathered vector: the thread layout and the order of
 // the sum of squares are the prologue's, so that the last token's output is bit-identical to what
 // the next token's prologue would form from the same words.
-// One barrier: the per-wave partials go to slots (kWaves floats) that nothing writes again before
+// One barrier: the per-wave partials go to slots (F2_W floats) that nothing writes again before
 // the caller's next barrier; the combination order is fixed, so every workgroup reducing the same
 // data gets the same bits.
 template <int KCH>
@@ -224,14 +240,14 @@ __device__ __forceinline__ float f2_norm_factor(const F2Args &a, const float4 (&
     ss = dpp_wave_sum(ss);
     if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float tot = (slot[0] + slot[1]) + (slot[2] + slot[3]);
+    const float tot = f2_sum8(slot);
     return 1.0f / sqrtf(tot / (float)K + a.eps);
 }
 
 // Gather NB vectors of K tagged words, RMSNorm (after the stack's final RMSNorm when pre_w is set),
 // int8 quantizer -> codes sq[b][K], bit-planes spl[b][8][K/32]; every thread gets the sum of the
 // codes and the scale. wr: this thread's norm weights. Taps are written by workgroup tapwg. red:
-// 3 * kWaves floats, ired: NB * kWaves ints of LDS. Two barriers per vector (three with pre_w).
+// 3 * F2_W floats, ired: NB * F2_W ints of LDS. Two barriers per vector (three with pre_w).
 template <int NB, int KCH>
 __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t tag, const float4 (&wr)[KCH],
                             const float *pre_w, float *pre_out, int8_t *sq, uint32_t *spl, int (&qsum)[NB],
@@ -254,7 +270,7 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
         }
         float ss = 0.f;
         if (pre_w) {
-            const float r0 = f2_norm_factor<KCH>(a, hv, K, red + 2 * kWaves);
+            const float r0 = f2_norm_factor<KCH>(a, hv, K, red + 2 * F2_W);
             if (r0_out && tid == 0) *r0_out = r0;
             if (mine) {
 #pragma unroll
@@ -290,11 +306,11 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
         pm = dpp_wave_max(pm);
         if ((tid & 63) == 0) {
             red[tid >> 6] = ss;
-            red[kWaves + (tid >> 6)] = pm;
+            red[F2_W + (tid >> 6)] = pm;
         }
         __syncthreads();
-        const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-        pm = fmaxf(fmaxf(red[kWaves], red[kWaves + 1]), fmaxf(red[kWaves + 2], red[kWaves + 3]));
+        const float tot = f2_sum8(red);
+        pm = f2_max8(red + F2_W);
         const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
         const float amax = pm * r;
         const float inv = amax > 0.f ? 127.0f / amax : 0.f;
@@ -335,7 +351,7 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
             }
         }
         qs = dpp_wave_isum(qs);
-        if ((tid & 63) == 0) ired[b * kWaves + (tid >> 6)] = qs;
+        if ((tid & 63) == 0) ired[b * F2_W + (tid >> 6)] = qs;
         scale[b] = s;
         if (tapwg && tap_s && tid == 0) tap_s[b] = s;
         if (NB > 1) __syncthreads();   // red is reused by the next vector
@@ -343,7 +359,7 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-        qsum[b] = (ired[b * kWaves] + ired[b * kWaves + 1]) + (ired[b * kWaves + 2] + ired[b * kWaves + 3]);
+        qsum[b] = f2_isum8(ired + b * F2_W);
 }
 
 // sum_k sgn * q of one 16-byte sign chunk against the bit-planes of the same 128 codes:
@@ -368,20 +384,20 @@ __device__ __forceinline__ int sdot_chunk(const uint4 &w, const int4 &q, int acc
 }
 
 // LoRA-down sums t[j] = L_dn[j] . q of a factor held in LDS ([rank][K] int8, rank <= 32) against
-// codes in LDS: the 32 lanes of group jg = tid / 32 take rows jg + 8 * jj (jj < 4), lane cl the
-// 16-byte chunks cl + 32 * m, so each code chunk is read once for four rows and all of a thread's
-// reads are issued before the first is used. The sums end in the group's last lane (cl == 31).
+// codes in LDS: wave jg takes rows jg + 8 * jj (jj < 4), lane cl the 16-byte chunks cl + 64 * m
+// (K = 4 * KCH * F2_T, so 2 * KCH chunks per lane), so each code chunk is read once for four rows
+// and all of a thread's reads are issued before the first is used. The sums end in lane 63.
 template <int KCH>
 __device__ __forceinline__ void lora_down_sums(const char *ldn, const int8_t *q, int K, int rank, int (&part)[4]) {
-    const int jg = threadIdx.x >> 5, cl = threadIdx.x & 31, C16 = K >> 4;
+    const int jg = threadIdx.x >> 6, cl = threadIdx.x & 63, C16 = K >> 4;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) part[jj] = 0;
     // no branches (they would split the reads into separately waited blocks): chunks past the row
     // end are read clamped with zero codes, rows past the rank clamped (their sums are not used)
 #pragma unroll
     for (int m = 0; m < 2 * KCH; ++m) {
-        const bool in = cl + 32 * m < C16;
-        const int cc = in ? cl + 32 * m : C16 - 1;
+        const bool in = cl + 64 * m < C16;
+        const int cc = in ? cl + 64 * m : C16 - 1;
         int4 qv = *reinterpret_cast<const int4 *>(q + cc * 16);
         if (!in) qv = make_int4(0, 0, 0, 0);
 #pragma unroll
@@ -390,7 +406,7 @@ __device__ __forceinline__ void lora_down_sums(const char *ldn, const int8_t *q,
                                   part[jj]);
     }
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) part[jj] = dpp_group_sum(part[jj], 32);
+    for (int jj = 0; jj < 4; ++jj) part[jj] = dpp_group_sum(part[jj], 64);
 }
 
 template <int KCH>
@@ -412,7 +428,7 @@ __device__ __forceinline__ int f2_rot(int nblk) { return nblk > 0 ? (int)((block
 __device__ __forceinline__ void lds_copy_contig(char *dst, const char *src, int n16) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nblk = (n16 + 63) >> 6, rot = f2_rot(nblk);
-    for (int k = wave; k < nblk; k += kWaves) {
+    for (int k = wave; k < nblk; k += F2_W) {
         int kb = k + rot;
         if (kb >= nblk) kb -= nblk;
         const int base = kb * 64, i = base + lane;
@@ -533,13 +549,15 @@ __device__ __forceinline__ float finish_row(const RowRegs<NB> &R, int b, int acc
     return silu_f(pre);
 }
 
-template <int NB, int KCH1, int KCH2, int CPR1, int CPR2>
-__global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
+// TAPS: whether any debug tap is set; without them the tap code (and the registers holding its
+// pointers) is compiled out of the launch that carries no taps.
+template <int NB, int KCH1, int KCH2, int CPR1, int CPR2, bool TAPS>
+__global__ __launch_bounds__(F2_T, 1) void k_flow2(F2Args a) {
     constexpr int F2_MAXI = f2_maxi(CPR1), F2_MAXO = f2_maxo(CPR2);
-    constexpr int NG1 = kBlock / CPR1, NG2 = kBlock / CPR2;
+    constexpr int NG1 = F2_T / CPR1, NG2 = F2_T / CPR2;
     extern __shared__ __align__(16) char smem[];
-    __shared__ float red[3 * kWaves];
-    __shared__ int ired[NB * kWaves];
+    __shared__ float red[3 * F2_W];
+    __shared__ int ired[NB * F2_W];
     __shared__ float dtl[NB];
     __shared__ float gsh[NB][64];   // the item's gated outputs, published by one coalesced store
     int sqsum[NB];
@@ -558,10 +576,10 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
     char *wreg = reinterpret_cast<char *>(Cl + NB * N);                     // sign rows, then LoRA-down rows
     const int tid = threadIdx.x, wg = blockIdx.x;
     const int L = a.n_layers, B = a.batch;
-    const dfssm_taps &T = a.taps;
+    const dfssm_taps T = TAPS ? a.taps : dfssm_taps{};
     const int64_t n_tok = (int64_t)a.n_steps * L;
     const int nbc = 2 * a.G * N;
-    for (int i = tid; i < NB * 64; i += kBlock) tv[i] = 0.f;   // entries past the rank stay zero
+    for (int i = tid; i < NB * 64; i += F2_T) tv[i] = 0.f;   // entries past the rank stay zero
     if (wg < a.n1) {
         // ====================================================================== role 1
         const int h = wg / a.S, p0 = (wg % a.S) * a.pr, g = h * a.G / a.H;
@@ -581,7 +599,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         int soff[F2_SBLK];
 #pragma unroll
         for (int j = 0; j < F2_SBLK; ++j) {
-            const int k = (tid >> 6) + kWaves * j;
+            const int k = (tid >> 6) + F2_W * j;
             soff[j] = 0;
             if (k < sblk) {
                 int kb = k + srot;
@@ -605,7 +623,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             // register loads first (their waits come at first use), then the direct-to-LDS copies
             load_norm_w<KCH1>(wr, Ly.w.norm_w, D);
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) dsc1[jj] = (tid >> 5) + 8 * jj < a.Rin ? gld(pin.lora_dn_scale + (tid >> 5) + 8 * jj) : 0.f;
+            for (int jj = 0; jj < 4; ++jj) dsc1[jj] = (tid >> 6) + 8 * jj < a.Rin ? gld(pin.lora_dn_scale + (tid >> 6) + 8 * jj) : 0.f;
             if (bc_lane) load_row(rb, m_bc, Ly, a.Rin, a.Cd);
             if (tid < nrest) load_row(rr, m_rest, Ly, a.Rin, a.Cd);
             dtb = gld(Ly.w.dt_bias + h);
@@ -613,7 +631,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             Dh = gld(Ly.w.D + h);
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
-                const int f = tid + kBlock * i;
+                const int f = tid + F2_T * i;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     st[i][b] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -625,7 +643,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             }
 #pragma unroll
             for (int j = 0; j < F2_SBLK; ++j) {
-                const int k = (tid >> 6) + kWaves * j;
+                const int k = (tid >> 6) + F2_W * j;
                 if (k < sblk) {
                     int kb = k + srot;
                     if (kb >= sblk) kb -= sblk;
@@ -662,10 +680,10 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             for (int b = 0; b < NB; ++b) {
                 int part[4];
                 lora_down_sums<KCH1>(ldn1, sq + b * D, D, a.Rin, part);
-                if ((tid & 31) == 31) {
+                if ((tid & 63) == 63) {
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const int j = (tid >> 5) + 8 * jj;
+                        const int j = (tid >> 6) + 8 * jj;
                         if (j < a.Rin) {
                             tv[b * 64 + j] = dsc1[jj] * ssc[b] * (float)part[jj];
                             if (wg == 0 && T.in_t) T.in_t[(rec + b) * a.Rin + j] = part[jj];
@@ -674,8 +692,9 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                 }
             }
             __syncthreads();
-            // packed-sign GEMV: first the B/C rows, finished and published at once by the lane that
-            // completes each sum, then the item's other rows (while the B/C words travel)
+            // packed-sign GEMV over the item's rows r = rg1 + NG1 * i (the B/C rows are r < q, all in
+            // the first pass): the lane that completes a B/C row's sum finishes and publishes it at
+            // once, then the other passes run while the B/C words travel
             {
                 const int G32 = D >> 5;
 #pragma unroll
@@ -683,29 +702,26 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                     uint4 pl[8];
 #pragma unroll
                     for (int p = 0; p < 8; ++p) pl[p] = *reinterpret_cast<const uint4 *>(spl + (b * 8 + p) * G32 + c1 * 4);
-                    // every sign chunk is read before the first is used: the B/C row's and the item's
-                    // other rows' (rows past the item's end are read clamped and their sums dropped)
-                    const uint4 bcbits = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(rg1, q - 1) * (D >> 3) + c1 * 16);
+                    // every sign chunk is read before the first is used (rows past the item's end are
+                    // read clamped and their sums dropped)
                     uint4 bits[F2_MAXI];
                     int pos[F2_MAXI];
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i)
-                        bits[i] = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(q + rg1 + NG1 * i, R1t - 1) * (D >> 3) + c1 * 16);
-                    {
-                        const int pos = dpp_group_sum(chunk_pos(bcbits, pl), CPR1);
-                        if (bc_lane && rb.m.ch != -2) {
-                            const int acc = 2 * pos - sqsum[b];
-                            const float act = finish_row(rb, b, acc, ssc[b], tv + b * 64, a.Rin, Ly.st.conv, a.Cd);
-                            st_x(bcxl + (int64_t)b * nbc + (rb.m.ch - E), tag2(fbits2(act), tag));
-                            if (T.in_acc) T.in_acc[(rec + b) * a.Ninp + rb.m.n] = acc;
-                        }
+                        bits[i] = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(rg1 + NG1 * i, R1t - 1) * (D >> 3) + c1 * 16);
+                    pos[0] = dpp_group_sum(chunk_pos(bits[0], pl), CPR1);
+                    if (bc_lane && rb.m.ch != -2) {
+                        const int acc = 2 * pos[0] - sqsum[b];
+                        const float act = finish_row(rb, b, acc, ssc[b], tv + b * 64, a.Rin, Ly.st.conv, a.Cd);
+                        st_x(bcxl + (int64_t)b * nbc + (rb.m.ch - E), tag2(fbits2(act), tag));
+                        if (T.in_acc) T.in_acc[(rec + b) * a.Ninp + rb.m.n] = acc;
                     }
 #pragma unroll
-                    for (int i = 0; i < F2_MAXI; ++i) pos[i] = dpp_group_sum(chunk_pos(bits[i], pl), CPR1);
+                    for (int i = 1; i < F2_MAXI; ++i) pos[i] = dpp_group_sum(chunk_pos(bits[i], pl), CPR1);
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i) {
                         const int r = rg1 + NG1 * i;
-                        if (NG1 * i < nrest && c1 == CPR1 - 1 && r < nrest) accl[b * F2_ROWS + r] = 2 * pos[i] - sqsum[b];
+                        if (NG1 * i < R1t && c1 == CPR1 - 1 && r >= q && r < R1t) accl[b * F2_ROWS + r - q] = 2 * pos[i] - sqsum[b];
                     }
                 }
             }
@@ -744,7 +760,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                 dAv[b] = expf(dtv[b] * Ah);
             }
             // every LDS operand first (one wait), then the updates; a thread's n4 is the same for
-            // all of its state rows (kBlock is a multiple of N / 4)
+            // all of its state rows (F2_T is a multiple of N / 4)
             const int n4 = tid % N4;
             float xs[F2_FPT][NB], zs[F2_FPT][NB];
             float4 Bv[NB], Cv[NB];
@@ -754,14 +770,14 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
                 Cv[b] = *reinterpret_cast<const float4 *>(Cl + b * N + n4 * 4);
 #pragma unroll
                 for (int i = 0; i < F2_FPT; ++i) {
-                    const int p = min((tid + kBlock * i) / N4, a.pr - 1);
+                    const int p = min((tid + F2_T * i) / N4, a.pr - 1);
                     xs[i][b] = xl[b * P + p];
                     zs[i][b] = zl[b * P + p];
                 }
             }
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
-                const int f = tid + kBlock * i;
+                const int f = tid + F2_T * i;
                 const bool ok = i < a.fpt && f < nf;
                 const int p = ok ? f / N4 : 0;
 #pragma unroll
@@ -792,7 +808,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
             }
 #pragma unroll
             for (int i = 0; i < F2_FPT; ++i) {
-                const int f = tid + kBlock * i;
+                const int f = tid + F2_T * i;
                 if (i < a.fpt && f < nf) {
                     const int p = f / N4;
 #pragma unroll
@@ -825,7 +841,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
 #pragma unroll
                     for (int i = 0; i < KCH1; ++i) hv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
                 }
-                const float r0 = f2_norm_factor<KCH1>(a, hv, D, red + 2 * kWaves);
+                const float r0 = f2_norm_factor<KCH1>(a, hv, D, red + 2 * F2_W);
                 if (mine) {
 #pragma unroll
                     for (int i = 0; i < KCH1; ++i) {
@@ -859,7 +875,7 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         const dfssm_proj &pout = Ly.w.out_proj;
         load_norm_w<KCH2>(wr, Ly.w.gnorm_w, E);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) dsc2[jj] = (tid >> 5) + 8 * jj < a.Rout ? gld(pout.lora_dn_scale + (tid >> 5) + 8 * jj) : 0.f;
+        for (int jj = 0; jj < 4; ++jj) dsc2[jj] = (tid >> 6) + 8 * jj < a.Rout ? gld(pout.lora_dn_scale + (tid >> 6) + 8 * jj) : 0.f;
         if (orow) {
             oscb = gld(pout.row_scale + on);
             ous = gld(pout.lora_up_scale + on);
@@ -905,10 +921,10 @@ __global__ __launch_bounds__(kBlock, 1) void k_flow2(F2Args a) {
         for (int b = 0; b < NB; ++b) {
             int part[4];
             lora_down_sums<KCH2>(ldn2, sq + b * E, E, a.Rout, part);
-            if ((tid & 31) == 31) {
+            if ((tid & 63) == 63) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const int j = (tid >> 5) + 8 * jj;
+                    const int j = (tid >> 6) + 8 * jj;
                     if (j < a.Rout) {
                         tv[b * 64 + j] = dsc2[jj] * ssc[b] * (float)part[jj];
                         if (tap2 && T.out_t) T.out_t[(rec + b) * a.Rout + j] = part[jj];
@@ -1015,16 +1031,16 @@ bool f2_plan(const Shape &s, int batch, int slots, F2Plan &p) {
     p.q = (2 * s.G * s.N + p.n1 - 1) / p.n1;
     p.R1 = p.q + 2 * p.pr + 1;
     p.npad = s.Ninp - s.Nin;
-    const int CPR1 = s.D >> 7, NG1 = kBlock / CPR1, rest = p.R1 + p.npad - p.q;
-    if (p.q > NG1 || rest > NG1 * f2_maxi(CPR1) || rest > kBlock || rest > F2_ROWS) return false;
-    if ((p.R1 + p.npad) * CPR1 > F2_SBLK * kWaves * 64) return false;
+    const int CPR1 = s.D >> 7, NG1 = F2_T / CPR1, rest = p.R1 + p.npad - p.q;
+    if (p.q > NG1 || p.R1 + p.npad > NG1 * f2_maxi(CPR1) || rest > F2_T || rest > F2_ROWS) return false;
+    if ((p.R1 + p.npad) * CPR1 > F2_SBLK * F2_W * 64) return false;
     const int avail = slots - p.n1;
     if (avail < 1) return false;
     p.R2 = (s.D + avail - 1) / avail;
     p.n2 = (s.D + p.R2 - 1) / p.R2;
-    if (p.R2 > kBlock || p.R2 > (kBlock / (s.E >> 7)) * f2_maxo(s.E >> 7)) return false;
+    if (p.R2 > F2_T || p.R2 > (F2_T / (s.E >> 7)) * f2_maxo(s.E >> 7)) return false;
     const int nf = p.pr * (s.N / 4);
-    p.fpt = (nf + kBlock - 1) / kBlock;
+    p.fpt = (nf + F2_T - 1) / F2_T;
     if (p.fpt > F2_FPT) return false;
     return f2_lds_base(s, batch) + f2_wreg_bytes(s, p.R1 + p.npad, p.R2) <= kF2MaxLds;
 }
@@ -1034,13 +1050,19 @@ bool f2_plan(const Shape &s, int batch, int slots, F2Plan &p) {
 // cooperative API also verifies that the device keeps all of it resident. The ordinary launch is
 // for tools that cannot follow cooperative launches: should part of the grid not be resident, the
 // bounded waits time out and the call reports DFSSM_STATUS_TIMEOUT.
+bool f2_any_tap(const dfssm_taps &t) {
+    return t.in_u || t.in_q || t.in_s || t.in_acc || t.in_t || t.out_u || t.out_q || t.out_s || t.out_acc || t.out_t ||
+           t.h_in;
+}
+
 template <int NB, int KCH1, int KCH2, int CPR1, int CPR2>
 hipError_t f2_launch(F2Args &a, const Shape &s, bool cooperative, hipStream_t stream) {
     const size_t lds = f2_lds_base(s, NB) + f2_wreg_bytes(s, a.R1 + a.npad, a.R2);
     void *args[] = {&a};
-    const void *fn = reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2, CPR1, CPR2>);
-    if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
-    return hipLaunchKernel(fn, dim3(a.n1 + a.n2), dim3(kBlock), args, lds, stream);
+    const void *fn = f2_any_tap(a.taps) ? reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2, CPR1, CPR2, true>)
+                                        : reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2, CPR1, CPR2, false>);
+    if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(a.n1 + a.n2), dim3(F2_T), args, lds, stream);
+    return hipLaunchKernel(fn, dim3(a.n1 + a.n2), dim3(F2_T), args, lds, stream);
 }
 
 template <int NB, int KCH1, int KCH2, int CPR1, int CPR2>
@@ -1053,15 +1075,15 @@ int f2_resident() {
     int ncu = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     // with the largest LDS a supported shape may use (registers bound the occupancy to one per CU anyway)
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2, CPR1, CPR2>),
-                                                     kBlock, kF2MaxLds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&k_flow2<NB, KCH1, KCH2, CPR1, CPR2, true>),
+                                                     F2_T, kF2MaxLds) != hipSuccess)
         return 0;
     v = per_cu * ncu;
     memo[dev].store(v, std::memory_order_relaxed);
     return v;
 }
 
-// The (D, E = 2D) shapes the kernel is built for: KCH1 = D / 1024, KCH2 = E / 1024 (at least 1),
+// The (D, E = 2D) shapes the kernel is built for: KCH1 = D / 2048, KCH2 = E / 2048 (at least 1),
 // CPR = lanes per sign row (D / 128, E / 128). D = 4096 would mean 128 heads, whose items hold more
 // rows than the GEMV loop takes (f2_plan).
 int f2_slots(const Shape &s, int batch) {
@@ -1069,8 +1091,8 @@ int f2_slots(const Shape &s, int batch) {
     switch (s.D) {
     case 256: return f2_resident<1, 1, 1, 2, 4>();
     case 512: return f2_resident<1, 1, 1, 4, 8>();
-    case 1024: return f2_resident<1, 1, 2, 8, 16>();
-    case 2048: return f2_resident<1, 2, 4, 16, 32>();
+    case 1024: return f2_resident<1, 1, 1, 8, 16>();
+    case 2048: return f2_resident<1, 1, 2, 16, 32>();
     default: return 0;
     }
 }
@@ -1079,8 +1101,8 @@ hipError_t f2_launch_any(F2Args &a, const Shape &s, bool coop, hipStream_t strea
     switch (s.D) {
     case 256: return f2_launch<1, 1, 1, 2, 4>(a, s, coop, stream);
     case 512: return f2_launch<1, 1, 1, 4, 8>(a, s, coop, stream);
-    case 1024: return f2_launch<1, 1, 2, 8, 16>(a, s, coop, stream);
-    case 2048: return f2_launch<1, 2, 4, 16, 32>(a, s, coop, stream);
+    case 1024: return f2_launch<1, 1, 1, 8, 16>(a, s, coop, stream);
+    case 2048: return f2_launch<1, 1, 2, 16, 32>(a, s, coop, stream);
     default: return hipErrorInvalidConfiguration;
     }
 }
