@@ -46,6 +46,7 @@ constexpr int F2_UPC = 2;     // LoRA-up chunks (16 B) per row: rank <= 32
 // out_proj rows per GEMV thread: a role-2 workgroup holds d_model / 128 rows
 constexpr int f2_maxo(int cpr) { return cpr >= 64 ? 2 : 1; }
 constexpr int F2_FPT = 2;     // SSM state float4s per thread and token
+constexpr int F2_BCW = 2;     // first wave of the B/C gather (rows past 128 would share a wave with it)
 constexpr int F2_ROWS = 512;  // item rows (incl. padding rows) per workgroup, at most
 constexpr unsigned kSpin2 = 1u << 21;
 constexpr int kSleep2 = 1;
@@ -114,35 +115,10 @@ __device__ __forceinline__ float bitsf2(uint32_t b) { return __builtin_bit_cast(
 
 __device__ void f2_error(const F2Args &a) { __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
-// One coherent (sc1) 16-byte load of two tagged words, waited for inside the same asm block.
-__device__ __forceinline__ u32x4 f2_load_chunk(const uint64_t *p) {
-    u32x4 r;
-    asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=&v"(r) : "v"(p) : "memory");
-    return r;
-}
-
 // This thread's 4*KCH consecutive words at p, reloaded until every epoch equals `tag` (bounded).
-// With `light`, the thread first polls only its first two words (its words come from one producer,
-// which stores them together) and reads all of them once those carry the epoch: for a wait that
-// starts long before the data exists, this keeps the polling of every waiting workgroup from
-// loading the fabric that the producers' own traffic and the final reads need.
 template <int KCH>
-__device__ __forceinline__ void f2_gather(const F2Args &a, const uint64_t *p, uint32_t tag, u32x4 (&r)[2 * KCH],
-                                          bool light = false) {
+__device__ __forceinline__ void f2_gather(const F2Args &a, const uint64_t *p, uint32_t tag, u32x4 (&r)[2 * KCH]) {
     unsigned spins = 0;
-    if (KCH > 1 && light) {
-        for (;;) {
-            const u32x4 c = f2_load_chunk(p);
-            if (c.y == tag && c.w == tag) break;
-            __builtin_amdgcn_s_sleep(kSleep2);
-            ++spins;
-            if ((spins & 63) == 0 && ld_x(a.err)) return;
-            if (spins > kSpin2) {
-                f2_error(a);
-                return;
-            }
-        }
-    }
     for (;;) {
         load_words_sc1<KCH>(p, r);
         bool ok = true;
@@ -226,6 +202,13 @@ __device__ __forceinline__ int f2_isum8(const int *v) {
 }
 static_assert(F2_W == 8, "the partial combinations take eight waves");
 
+// RMSNorm factor (mean of squares + eps)^-1/2 by the hardware reciprocal square root (about one
+// ulp): the factor needs no correctly rounded value, since the quantizer's decisions are taken on
+// the u this workgroup forms with it, and the last token's final RMSNorm uses the same expression.
+__device__ __forceinline__ float f2_rnorm(float sumsq, int K, float eps) {
+    return __builtin_amdgcn_rsqf(sumsq / (float)K + eps);
+}
+
 // The stack's final RMSNorm, (h * r) * w, of one gathered vector: the thread layout and the order of
 // the sum of squares are the prologue's, so that the last token's output is bit-identical to what
 // the next token's prologue would form from the same words.
@@ -241,7 +224,7 @@ __device__ __forceinline__ float f2_norm_factor(const F2Args &a, const float4 (&
     if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float tot = f2_sum8(slot);
-    return 1.0f / sqrtf(tot / (float)K + a.eps);
+    return f2_rnorm(tot, K, a.eps);
 }
 
 // Gather NB vectors of K tagged words, RMSNorm (after the stack's final RMSNorm when pre_w is set),
@@ -252,7 +235,7 @@ template <int NB, int KCH>
 __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t tag, const float4 (&wr)[KCH],
                             const float *pre_w, float *pre_out, int8_t *sq, uint32_t *spl, int (&qsum)[NB],
                             float (&scale)[NB], float *red, int *ired, bool tapwg, float *r0_out, float *tap_h,
-                            float *tap_u, int8_t *tap_q, float *tap_s, bool light = false) {
+                            float *tap_u, int8_t *tap_q, float *tap_s) {
     const int tid = threadIdx.x;
     const int e0 = prologue_elem<KCH>(0);
     const bool mine = e0 < K;   // K is a multiple of 4*KCH: a thread has all of its chunks or none
@@ -260,7 +243,7 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
         float4 hv[KCH];
         if (mine) {
             u32x4 r[2 * KCH];
-            f2_gather<KCH>(a, X + (int64_t)b * K + e0, tag, r, light);
+            f2_gather<KCH>(a, X + (int64_t)b * K + e0, tag, r);
 #pragma unroll
             for (int i = 0; i < KCH; ++i)
                 hv[i] = make_float4(bitsf2(r[2 * i].x), bitsf2(r[2 * i].z), bitsf2(r[2 * i + 1].x), bitsf2(r[2 * i + 1].z));
@@ -311,7 +294,7 @@ __device__ void f2_prologue(const F2Args &a, const uint64_t *X, int K, uint32_t 
         __syncthreads();
         const float tot = f2_sum8(red);
         pm = f2_max8(red + F2_W);
-        const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
+        const float r = f2_rnorm(tot, K, a.eps);
         const float amax = pm * r;
         const float inv = amax > 0.f ? 127.0f / amax : 0.f;
         const float s = amax > 0.f ? amax / 127.0f : 0.f;
@@ -740,8 +723,11 @@ __global__ __launch_bounds__(F2_T, 1) void k_flow2(F2Args a) {
                     else dtl[b] = softplus_f(v + dtb);
                 }
             }
-            if (tid < (N >> 1)) {
-                const int c = tid < N4 ? 0 : 1, k = (tid - c * N4) * 4;   // B or C, first of 4 words
+            // the group's B and C: gathered by the waves past the epilogue rows (the words were published
+            // during the GEMV), while the first waves finish their rows
+            const int tbc = tid - F2_BCW * 64;
+            if (tbc >= 0 && tbc < (N >> 1)) {
+                const int c = tbc < N4 ? 0 : 1, k = (tbc - c * N4) * 4;   // B or C, first of 4 words
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     u32x4 w[2];
@@ -916,7 +902,7 @@ __global__ __launch_bounds__(F2_T, 1) void k_flow2(F2Args a) {
         __syncthreads();
         f2_prologue<NB, KCH2>(a, gxl, E, tag, wr, nullptr, nullptr, sq, spl, sqsum, ssc, red, ired, tap2, nullptr,
                               nullptr, T.out_u ? T.out_u + rec * E : nullptr, T.out_q ? T.out_q + rec * E : nullptr,
-                              T.out_s ? T.out_s + rec : nullptr, true);
+                              T.out_s ? T.out_s + rec : nullptr);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             int part[4];
