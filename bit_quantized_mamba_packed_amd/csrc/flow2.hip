@@ -459,6 +459,9 @@ __device__ __forceinline__ void load_up(int4 (&w)[F2_UPC], const int8_t *lora_up
     }
 }
 
+// Row of row group g (of ng) in GEMV pass i: passes 0 and 1 in group order, later ones reversed.
+__device__ __forceinline__ int f2_pass_row(int g, int i, int ng) { return ng * i + (i >= 2 ? ng - 1 - g : g); }
+
 // Which in_proj row / conv channel the r-th row of an item covers: first the item's share of the B
 // and C rows (all groups' B rows, then all groups' C rows, spread over the items), then its z
 // channels, its x channels, its head's dt row, and (workgroup 0, with taps) the padding rows.
@@ -675,9 +678,12 @@ __global__ __launch_bounds__(F2_T, 1) void k_flow2(F2Args a) {
                 }
             }
             __syncthreads();
-            // packed-sign GEMV over the item's rows r = rg1 + NG1 * i (the B/C rows are r < q, all in
-            // the first pass): the lane that completes a B/C row's sum finishes and publishes it at
-            // once, then the other passes run while the B/C words travel
+            // packed-sign GEMV over the item's rows, pass i taking rows [NG1 * i, NG1 * (i + 1)) (the
+            // B/C rows are r < q, all in the first pass of wave 0): the lane that completes a B/C row's
+            // sum finishes and publishes it at once, then the other passes run while the B/C words
+            // travel. Passes after the second run in reverse group order, so that the few rows of a
+            // last, partial pass fall to the last waves rather than to the one finishing the B/C rows,
+            // and a wave skips a pass in which none of its groups has a row.
             {
                 const int G32 = D >> 5;
 #pragma unroll
@@ -691,7 +697,7 @@ __global__ __launch_bounds__(F2_T, 1) void k_flow2(F2Args a) {
                     int pos[F2_MAXI];
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i)
-                        bits[i] = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(rg1 + NG1 * i, R1t - 1) * (D >> 3) + c1 * 16);
+                        bits[i] = *reinterpret_cast<const uint4 *>(sgn1 + (size_t)min(f2_pass_row(rg1, i, NG1), R1t - 1) * (D >> 3) + c1 * 16);
                     pos[0] = dpp_group_sum(chunk_pos(bits[0], pl), CPR1);
                     if (bc_lane && rb.m.ch != -2) {
                         const int acc = 2 * pos[0] - sqsum[b];
@@ -700,10 +706,13 @@ __global__ __launch_bounds__(F2_T, 1) void k_flow2(F2Args a) {
                         if (T.in_acc) T.in_acc[(rec + b) * a.Ninp + rb.m.n] = acc;
                     }
 #pragma unroll
-                    for (int i = 1; i < F2_MAXI; ++i) pos[i] = dpp_group_sum(chunk_pos(bits[i], pl), CPR1);
+                    for (int i = 1; i < F2_MAXI; ++i) {
+                        pos[i] = 0;
+                        if (__any(f2_pass_row(rg1, i, NG1) < R1t)) pos[i] = dpp_group_sum(chunk_pos(bits[i], pl), CPR1);
+                    }
 #pragma unroll
                     for (int i = 0; i < F2_MAXI; ++i) {
-                        const int r = rg1 + NG1 * i;
+                        const int r = f2_pass_row(rg1, i, NG1);
                         if (NG1 * i < R1t && c1 == CPR1 - 1 && r >= q && r < R1t) accl[b * F2_ROWS + r - q] = 2 * pos[i] - sqsum[b];
                     }
                 }
