@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "dfssm_internal.h"
 
@@ -113,14 +114,28 @@ int check_taps(const dfssm_taps *t) {
     return DFSSM_OK;
 }
 
-// A stack decode's workspace starts with its status word (kAlign bytes), then the decode carve.
+// A batched stack decode of at least kHalvesMinBatch sequences runs as two batch halves on two
+// streams (stack_decode_halves).
+constexpr int kHalvesMinBatch = 32;
+
+// Bytes one decode_step of `batch` sequences carves from its workspace.
+size_t step_ws_bytes(const Shape &s, int batch, bool stack) {
+    size_t b = carve_decode_ws(s, batch, nullptr, stack).bytes;
+    if (decode_uses_mfma(s, batch)) b += carve_prefill_ws(s, batch, 1, 0, nullptr).bytes;
+    return b;
+}
+
+// One half's share of a halved stack decode's workspace (the larger half: the second).
+size_t half_ws_bytes(const Shape &s, int batch) { return align_up(step_ws_bytes(s, batch - batch / 2, true), kAlign); }
+
+// A stack decode's workspace starts with its status word (kAlign bytes), then the decode carve (the
+// persistent kernel's tables and exchange words at batch 1, two half carves at kHalvesMinBatch and up).
 size_t decode_ws_bytes(const Shape &s, int batch, bool stack, int n_layers = 0) {
-    DecodeWs w = carve_decode_ws(s, batch, nullptr, stack);
-    size_t extra = stack ? kAlign : 0;
-    if (stack && stack2_ok(s, batch))
-        extra += stack2_extra_ws_bytes(s, batch, n_layers);
-    else if (decode_uses_mfma(s, batch)) extra += carve_prefill_ws(s, batch, 1, 0, nullptr).bytes;
-    return w.bytes + extra;
+    if (!stack) return step_ws_bytes(s, batch, false);
+    size_t b = step_ws_bytes(s, batch, true);
+    if (stack2_ok(s, batch)) b += stack2_extra_ws_bytes(s, batch, n_layers);
+    if (batch >= kHalvesMinBatch) b = std::max(b, 2 * half_ws_bytes(s, batch));
+    return kAlign + b;
 }
 
 bool chunk_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128 || chunk == 256; }
@@ -177,6 +192,73 @@ hipError_t decode_step(const Shape &s, const dfssm_layer_weights &w, const dfssm
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DFSSM_OK : DFSSM_EHIP; }
+
+// The second stream of halved stack decodes, one per device (default priority, created on first
+// use, kept until the process ends), and the two events that fork it from the caller's stream and
+// join it back. Every call re-records the events, so an enqueue holds g_halves_mu throughout.
+constexpr int kMaxHalvesDevices = 64;
+struct HalvesStream {
+    hipStream_t s;
+    hipEvent_t fork, join;
+};
+HalvesStream g_halves[kMaxHalvesDevices];
+std::mutex g_halves_mu;
+
+// A per-layer stack decode as two batch halves [0, b0) and [b0, batch), b0 = batch / 2: the first on
+// the caller's stream, the second on the device's halves stream, their launches interleaved layer by
+// layer. A half's sequences, states, outputs and tap records are contiguous slices of the caller's,
+// and the halves share nothing but the (read-only) weights, so the results are those of the single
+// stream; while one half's SSM step streams its state the other's projections and quantizers, which
+// do not fill the GPU, run beside it.
+hipError_t stack_decode_halves(const Shape &s, const dfssm_layer_weights *layers, const dfssm_layer_state *states,
+                               int n_layers, const float *final_norm_w, const float *x0, float *y, int batch,
+                               int n_steps, char *wsd, const dfssm_taps *taps, hipStream_t st) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxHalvesDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_halves_mu);
+    HalvesStream &hs = g_halves[dev];
+    if (!hs.s) {
+        if ((e = hipEventCreateWithFlags(&hs.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&hs.join, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipStreamCreateWithFlags(&hs.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    }
+    const int b0 = batch / 2, nb[2] = {b0, batch - b0};
+    const hipStream_t xs[2] = {st, hs.s};
+    const size_t hb = half_ws_bytes(s, batch);
+    std::vector<dfssm_layer_state> hst(2 * (size_t)n_layers);
+    DecodeWs dws[2];
+    for (int i = 0; i < 2; ++i) {
+        const int64_t first = i ? b0 : 0;
+        dws[i] = carve_decode_ws(s, nb[i], wsd + i * hb, true);
+        for (int l = 0; l < n_layers; ++l) {
+            hst[i * n_layers + l].conv = states[l].conv + first * s.Cd * (kConvTaps - 1);
+            hst[i * n_layers + l].ssm = states[l].ssm + first * s.H * s.P * s.N;
+        }
+    }
+    if ((e = hipEventRecord(hs.fork, st)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(hs.s, hs.fork, 0)) != hipSuccess) return e;
+    const int64_t rowsz = (int64_t)batch * s.D;
+    for (int t = 0; t < n_steps; ++t) {
+        for (int l = 0; l < n_layers; ++l)
+            for (int i = 0; i < 2; ++i) {
+                const int64_t first = i ? b0 : 0;
+                const float *xin = (t == 0 ? x0 : y + (t - 1) * rowsz) + first * s.D;
+                const TapPtrs tp = tap_offset(taps, s, ((int64_t)t * n_layers + l) * batch + first);
+                e = decode_step(s, layers[l], hst[i * n_layers + l], l == 0 ? xin : dws[i].hbuf, dws[i].hbuf, nb[i],
+                                wsd + i * hb, true, tp, xs[i]);
+                if (e != hipSuccess) return e;
+            }
+        for (int i = 0; i < 2; ++i) {
+            e = launch_final_norm(dws[i].hbuf, final_norm_w, y + t * rowsz + (i ? b0 : 0) * s.D, nullptr, s.D, s.eps,
+                                  nb[i], xs[i]);
+            if (e != hipSuccess) return e;
+        }
+    }
+    if ((e = hipEventRecord(hs.join, hs.s)) != hipSuccess) return e;
+    return hipStreamWaitEvent(st, hs.join, 0);
+}
 
 }  // namespace
 
@@ -357,6 +439,11 @@ int dfssm_stack_decode_ex(const dfssm_dims *dims, const dfssm_layer_weights *lay
                           o.launch == DFSSM_LAUNCH_COOPERATIVE, &err, st);
         if (e != hipSuccess) return DFSSM_EHIP;
         return hip_status(launch_stack_finish(err, status, y, ny, st));
+    }
+    if (batch >= kHalvesMinBatch) {
+        e = stack_decode_halves(s, layers, states, n_layers, final_norm_w, x0, y, batch, n_steps, wsd, taps, st);
+        if (e != hipSuccess) return DFSSM_EHIP;
+        return hip_status(launch_stack_finish(nullptr, status, y, ny, st));
     }
     const int64_t rowsz = (int64_t)batch * s.D;
     for (int t = 0; t < n_steps; ++t) {

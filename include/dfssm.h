@@ -259,12 +259,15 @@ typedef struct dfssm_stack_opts {
  * Autoregressive-style decode through a stack of n_layers layers for n_steps tokens:
  *   x(0) = x0;  for t: h = x(t); h = layer_l(h) for l = 0..n_layers-1;
  *   y[t] = RMSNorm(h) * final_norm_w;  x(t+1) = y[t].
- * The whole token loop runs as ONE persistent kernel launch (the paper's §4.1 captures the forward
- * pass in a graph to remove per-kernel launch cost; here the layers hand their partial results to
- * each other through tagged words in the workspace instead of kernel boundaries). When the device
- * cannot keep the needed workgroups resident at once, the call falls back to per-layer kernels
- * with the same results. The call's status word (DFSSM_STACK_STATUS_OFFSET) is written in the
- * workspace once its work completes.
+ * At batch 1 the whole token loop runs as ONE persistent kernel launch (the paper's §4.1 captures
+ * the forward pass in a graph to remove per-kernel launch cost; here the layers hand their partial
+ * results to each other through tagged words in the workspace instead of kernel boundaries). When
+ * the device cannot keep the needed workgroups resident at once, and at batch > 1, the call runs
+ * per-layer kernels with the same results. From batch 32 up the batch runs as two halves: the first
+ * on `stream`, the second on a stream the library creates once per device (default priority,
+ * forked from `stream` by an event at the start of the call and joined back into it at the end),
+ * so all of the call's work is still ordered on `stream`. The call's status word
+ * (DFSSM_STACK_STATUS_OFFSET) is written in the workspace once its work completes.
  *   layers, states: HOST arrays [n_layers] of the structs above; final_norm_w [d_model] fp32;
  *   x0 [batch][d_model] fp32; y [n_steps][batch][d_model] fp32 (must not alias x0);
  *   taps: NULL or records laid out [n_steps][n_layers][batch][...].

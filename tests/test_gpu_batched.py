@@ -185,3 +185,28 @@ def test_stack_decode_1p3b_48_layers_batch64_sampled():
                 assert v < PY.TOL_LAYER, (l, b, errs)
                 worst[k] = max(worst.get(k, 0.0), v)
     say(f"1p3b batch-64 stack last step per-layer worst errors: {worst}")
+
+
+def test_stack_decode_halves_match_single_stream():
+    """From 32 sequences up a stack decode runs as two batch halves on two streams. At batch 41
+    (halves of 20 and 21) the outputs, final states and every tap record equal, bit for bit, those of
+    two separate decodes of the same 20 and 21 sequences, which run below the threshold on one stream."""
+    nL, T, B, b0 = 3, 3, 41, 20
+    layers = gen.stack_weights(TINY, nL, seed=7, random_norms=True, per_channel_lora=True)
+    states0 = [gen.initial_states(TINY, B, l, 7, std=0.1) for l in range(nL)]
+    x0 = gen.token_inputs(TINY, (B,), 7, tag=6)
+    fw = np.random.default_rng(7).uniform(0.5, 1.5, TINY.d_model).astype(np.float32)
+    say(f"case: tiny stack decode, {nL} layers, {T} steps, batch {B} (two halves) against {b0} + {B - b0}")
+    y, states, taps = run_stack(TINY, layers, x0, states0, T, taps=True, final_w=fw)
+    for lo, hi in ((0, b0), (b0, B)):
+        part = [(c[lo:hi].copy(), s[lo:hi].copy()) for c, s in states0]
+        yp, sp, tp = run_stack(TINY, layers, x0[lo:hi].copy(), part, T, taps=True, final_w=fw)
+        assert (y[:, lo:hi] == yp).all(), (lo, hi)
+        for l in range(nL):
+            assert (states[l][0][lo:hi] == sp[l][0]).all() and (states[l][1][lo:hi] == sp[l][1]).all(), (lo, l)
+        n = hi - lo
+        for t in range(T):
+            for l in range(nL):
+                for k, v in taps.items():
+                    full = v[(t * nL + l) * B + lo:(t * nL + l) * B + hi]
+                    assert (full == tp[k][(t * nL + l) * n:(t * nL + l + 1) * n]).all(), (k, t, l, lo)
