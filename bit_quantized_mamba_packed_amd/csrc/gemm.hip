@@ -20,10 +20,10 @@
 // (no two waves expand the same bits); K in steps of 128 through double-buffered LDS, one barrier
 // per step.
 // The ragged last column tile is dispatched first so that the short workgroups do not trail.
-// k_gemm_skinny (M <= 64): one workgroup of 16 waves per 32 columns (per 64 when that would leave
-// more workgroups than compute units), the waves split K, each issuing the loads of its share at
-// once, and add their int32 partial sums with LDS atomics (exact, so in any order); A comes straight
-// from global memory (it is 64 x K bytes and stays in L2), B as above.
+// k_gemm_skinny (M <= 64): one workgroup of 16 waves (8 when M <= 32: one 32-row block) per 32
+// columns (per 64 when that would leave more workgroups than compute units); A and the sign bits go
+// through LDS in K chunks of 1024 by direct loads, the waves split the K steps of every chunk, and
+// their int32 partial sums meet in LDS (exact, so in any order).
 #include <algorithm>
 
 #include "decode_device.h"
@@ -488,26 +488,30 @@ __global__ void k_clear_u32(uint32_t *p, int n) {
     if (i < n) p[i] = 0u;
 }
 
-// M <= 64: one workgroup of kSkWaves waves per 32 output columns; wave w takes the K steps
-// [w nk / kSkWaves, (w + 1) nk / kSkWaves), all of its loads issued (kSkRun steps at a time) before
+// M <= 64: one workgroup of NW waves per 32 output columns; wave w takes the K steps
+// [w nk / NW, (w + 1) nk / NW), all of its loads issued (kSkRun steps at a time) before
 // its first MFMA. The int32 partial sums meet in LDS; waves 0 and 1 each finish one 32-row block,
 // with their epilogue operands loaded before the reduction barrier.
-constexpr int kSkWaves = 16, kSkBlock = 64 * kSkWaves;
+// NW = 16 waves for M <= 64 (two 32-row blocks), 8 for M <= 32 (one: half the code bytes and MFMAs)
+template <int NW>
+constexpr int sk_block() { return 64 * NW; }
 constexpr int kSkChunk = 1024;   // K bytes of A per LDS chunk (8 K steps of 128)
 template <int CB>
-constexpr int sk_lds_bytes() { return 2 * (64 * kSkChunk + CB * 32 * (kSkChunk / 8)); }
+constexpr int sk_lds_bytes(int NW) { return 2 * (4 * NW * kSkChunk + CB * 32 * (kSkChunk / 8)); }
 
-// M <= 64 rows, CB blocks of 32 columns per workgroup. K runs in chunks of 1024 through two LDS
-// buffers: A[64][1024] (row r's 16-byte column c stored at c ^ (r & 7)) and the sign bits
-// B[CB * 32][128] (column n's 16-byte piece p stored at p ^ (n & 7)), both written by direct
-// global->LDS loads that read whole rows (coalesced), chunk c + 1 in flight while chunk c is
-// multiplied. Wave w computes output block w % (2 CB) (row block bit 0, column block bit 1..) over
-// the K steps kg, kg + KG, ... of every chunk (kg = w / (2 CB), KG = 8 / CB), so the partial sums
-// of only KG waves meet per output, in LDS after the last chunk.
-template <int CB, bool CONV>
-__global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a, ConvEpi cv) {
-    constexpr int NBLK = 2 * CB, KG = kSkWaves / NBLK, A_BUF = 64 * kSkChunk, B_BUF = CB * 32 * (kSkChunk / 8);
-    __shared__ __align__(16) char smem[sk_lds_bytes<CB>()];
+// M <= 64 rows (NW = 16 waves, NRB = 2 row blocks of 32) or M <= 32 (NW = 8, NRB = 1), CB blocks
+// of 32 columns per workgroup. K runs in chunks of 1024 through two LDS buffers: A[32 NRB][1024]
+// (row r's 16-byte column c stored at c ^ (r & 7)) and the sign bits B[CB * 32][128] (column n's
+// 16-byte piece p stored at p ^ (n & 7)), both written by direct global->LDS loads that read whole
+// rows (coalesced), chunk c + 1 in flight while chunk c is multiplied. Wave w computes output block
+// w % (NRB CB) (row block w % NRB, column block (w % (NRB CB)) / NRB) over the K steps kg, kg + KG,
+// ... of every chunk (kg = w / (NRB CB), KG = 8 / CB), so the partial sums of only KG waves meet
+// per output, in LDS after the last chunk.
+template <int CB, bool CONV, int NW>
+__global__ __launch_bounds__(sk_block<NW>()) void k_gemm_skinny(GemmArgs a, ConvEpi cv) {
+    constexpr int NRB = NW / 8, NBLK = NRB * CB, KG = NW / NBLK, A_BUF = 4 * NW * kSkChunk, B_BUF = CB * 32 * (kSkChunk / 8);
+    static_assert(NW == 8 || NW == 16, "8 waves (one row block) or 16 (two)");
+    __shared__ __align__(16) char smem[sk_lds_bytes<CB>(NW)];
     // the wave index is uniform: in a scalar register, so are the row pointers and block indices
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, hsel = lane >> 5;
@@ -515,13 +519,13 @@ __global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a, ConvEpi cv
     const int K = a.K, nkt = K / KT, nch = (K + kSkChunk - 1) / kSkChunk;
     auto As = [&](int b) { return reinterpret_cast<int8_t *>(smem) + b * A_BUF; };
     auto Bs = [&](int b) { return reinterpret_cast<uint8_t *>(smem) + 2 * A_BUF + b * B_BUF; };
-    // loads of chunk c: A rows wave + 16 i (i < 4), lane l -> 16-byte column l ^ (row & 7); B: wave
+    // loads of chunk c: A rows wave + NW i (i < 4), lane l -> 16-byte column l ^ (row & 7); B: wave
     // w < 4 CB loads columns 8 w + l / 8, lane l -> piece (l & 7) ^ (column & 7). Rows past M and
     // columns past N read row / column clamped into the matrix (outputs never stored); bytes past K
     // in a short last chunk read clamped addresses (K steps never used).
     const int8_t *arow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = a.q + (int64_t)min(wave + 16 * i, a.M - 1) * a.ldq;
+    for (int i = 0; i < 4; ++i) arow[i] = a.q + (int64_t)min(wave + NW * i, a.M - 1) * a.ldq;
     const int asw = 16 * (lane ^ (wave & 7));   // row & 7 == wave & 7 for every row of this wave
     const int bcol = 8 * wave + (lane >> 3);
     const uint8_t *brow = a.sign + (int64_t)min(n0 + bcol, a.N - 1) * (K >> 3);
@@ -530,15 +534,15 @@ __global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a, ConvEpi cv
         const int b = c & 1, k0 = c * kSkChunk;
         const int aoff = min(k0 + asw, K - 16), boff = min((k0 >> 3) + bsw, (K >> 3) - 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(arow[i] + aoff, As(b) + (wave + 16 * i) * kSkChunk);
+        for (int i = 0; i < 4; ++i) lds_dma16(arow[i] + aoff, As(b) + (wave + NW * i) * kSkChunk);
         if (wave < 4 * CB) lds_dma16(brow + boff, Bs(b) + wave * 1024);
     };
     // epilogue operands of this wave's quarter of a block, loaded before the chunks (so that waiting
     // for them never waits for a chunk) and used after the last one: block fb = wave / 4 (row block
-    // fb & 1, column block fb >> 1), accumulator entries r in [4 rq, 4 rq + 4), rows
+    // fb % NRB, column block fb / NRB), accumulator entries r in [4 rq, 4 rq + 4), rows
     // 8 rq + 4 (lane / 32) + 0..3
     const int nb = a.M > 32 ? 2 : 1;
-    const int fb = wave >> 2, fib = fb & 1, fcb = fb >> 1, rq = wave & 3;
+    const int fb = wave >> 2, fib = fb % NRB, fcb = fb / NRB, rq = wave & 3;
     const bool fin = fb < NBLK && fib < nb;
     const int n = n0 + fcb * 32 + lr;
     float sv[4], rv[4], us = 0.f;
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(kSkBlock) void k_gemm_skinny(GemmArgs a, ConvEpi cv
     dma(0);
     if (nch > 1) dma(1);
     constexpr int TPC = 8 / KG;   // K steps per wave and chunk
-    const int blk = wave % NBLK, kg = wave / NBLK, rb = blk & 1, cb = blk >> 1;
+    const int blk = wave % NBLK, kg = wave / NBLK, rb = blk % NRB, cb = blk / NRB;
     v16i acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0;
@@ -716,8 +720,13 @@ hipError_t launch_gemm_pm1(const GemmArgs &a, hipStream_t stream) {
     if (a.M <= 64) {
         // two column blocks per workgroup when one each would not fit one workgroup per compute unit
         const int ncb = (a.N + 31) / 32;
-        if (ncb > 256) k_gemm_skinny<2, false><<<(ncb + 1) / 2, kSkBlock, 0, stream>>>(a, ConvEpi{});
-        else k_gemm_skinny<1, false><<<ncb, kSkBlock, 0, stream>>>(a, ConvEpi{});
+        if (a.M <= 32) {
+            if (ncb > 256) k_gemm_skinny<2, false, 8><<<(ncb + 1) / 2, sk_block<8>(), 0, stream>>>(a, ConvEpi{});
+            else k_gemm_skinny<1, false, 8><<<ncb, sk_block<8>(), 0, stream>>>(a, ConvEpi{});
+        } else {
+            if (ncb > 256) k_gemm_skinny<2, false, 16><<<(ncb + 1) / 2, sk_block<16>(), 0, stream>>>(a, ConvEpi{});
+            else k_gemm_skinny<1, false, 16><<<ncb, sk_block<16>(), 0, stream>>>(a, ConvEpi{});
+        }
         return hipGetLastError();
     }
     const GemmPlan p = plan_gemm(a.M, a.N, a.K);
@@ -747,8 +756,13 @@ hipError_t launch_gemm_pm1_conv(const GemmArgs &a, const ConvEpi &c, hipStream_t
         return hipErrorInvalidValue;
     if (c.E <= 0 || c.Cd <= 0 || c.H <= 0 || c.E + c.Cd + c.H > a.N) return hipErrorInvalidValue;
     const int ncb = (a.N + 31) / 32;
-    if (ncb > 256) k_gemm_skinny<2, true><<<(ncb + 1) / 2, kSkBlock, 0, stream>>>(a, c);
-    else k_gemm_skinny<1, true><<<ncb, kSkBlock, 0, stream>>>(a, c);
+    if (a.M <= 32) {
+        if (ncb > 256) k_gemm_skinny<2, true, 8><<<(ncb + 1) / 2, sk_block<8>(), 0, stream>>>(a, c);
+        else k_gemm_skinny<1, true, 8><<<ncb, sk_block<8>(), 0, stream>>>(a, c);
+    } else {
+        if (ncb > 256) k_gemm_skinny<2, true, 16><<<(ncb + 1) / 2, sk_block<16>(), 0, stream>>>(a, c);
+        else k_gemm_skinny<1, true, 16><<<ncb, sk_block<16>(), 0, stream>>>(a, c);
+    }
     return hipGetLastError();
 }
 
