@@ -321,18 +321,19 @@ def prefill_gemm_profile(d, n_layers: int, S: int):
 
 def write_gemm_profile(trace_csv: str) -> dict:
     """Summarise the rocprofv3 kernel trace of `bench.py --workload prefill2048 --steps 1` into
-    PREFILL_GEMM_PROFILE: the average duration of the in_proj GEMM launch (k_gemm_tile_pair, both
+    PREFILL_GEMM_PROFILE: the average duration of the in_proj GEMM launch (k_gemm_tile_ext, both
     of its GEMMs) and of the out_proj GEMM launch (k_gemm_tile) over the traced prefills."""
     import csv
     rows = list(csv.DictReader(open(trace_csv)))
 
-    def avg(tag):
-        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows if tag in r["Kernel_Name"]]
-        if not d:
-            raise SystemExit(f"{trace_csv}: no {tag} dispatch")
-        return sum(d) / len(d), len(d), next(r["Kernel_Name"] for r in rows if tag in r["Kernel_Name"])
+    def avg(*tags):
+        sel = [r for r in rows if any(t in r["Kernel_Name"] for t in tags)]
+        if not sel:
+            raise SystemExit(f"{trace_csv}: no {' / '.join(tags)} dispatch")
+        d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel]
+        return sum(d) / len(d), len(d), sel[0]["Kernel_Name"]
 
-    t_in, n_in, k_in = avg("k_gemm_tile_pair")
+    t_in, n_in, k_in = avg("k_gemm_tile_ext", "k_gemm_tile_pair")
     t_out, n_out, k_out = avg("k_gemm_tile<")
     import re
 

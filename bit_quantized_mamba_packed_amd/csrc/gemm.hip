@@ -20,6 +20,11 @@
 // (no two waves expand the same bits); K in steps of 128 through double-buffered LDS, one barrier
 // per step.
 // The ragged last column tile is dispatched first so that the short workgroups do not trail.
+// k_gemm_tile_ext (prefill in_proj): the z|x GEMM's 128 x 256 tiles fill exactly one round of
+// two workgroups per compute unit at 2,048 tokens; the B|C|dt GEMM (a few 32-column blocks) rides
+// along, each block with the first column tiles (one 32 x 32 block per wave, over the whole K), so
+// its work needs neither a second round of tiles nor a split K range (k_gemm_tile_pair, which runs
+// the narrow GEMM as K-split units ahead of the wide tiles, remains for other shapes).
 // k_gemm_skinny (M <= 64): one workgroup of 16 waves (8 when M <= 32: one 32-row block) per 32
 // columns (per 64 when that would leave more workgroups than compute units); A and the sign bits go
 // through LDS in K chunks of 1024 by direct loads, the waves split the K steps of every chunk, and
@@ -212,9 +217,14 @@ __device__ __forceinline__ void stage_epilogue(const GemmArgs &a, char *base, in
 
 // two waves per SIMD (<= 256 registers incl. accumulators), so two workgroups share a compute unit
 // One workgroup's tile: tile index bid, K slice z of splitk; smem holds tile_smem<64 WNB>() bytes.
-template <int WNB, bool SPLIT, bool RES>
+// EXT: the tiles of column tiles tn < next also compute the 32 columns [32 tn, 32 tn + 32) of a second
+// GEMM `nar` over the same codes (one 32 x 32 block per wave: rows 32 w .. 32 w + 31), so that a
+// narrow GEMM rides along the wide one's single round of tiles; its sign bits take a 1 KB LDS slot
+// per K buffer after the tile's own LDS (kExtLds).
+template <int WNB, bool SPLIT, bool RES, bool EXT = false>
 __device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int ntn, int splitk, int bid, int z,
-                                               char *smem, int &last_flag) {
+                                               char *smem, int &last_flag, const GemmArgs *nar = nullptr,
+                                               int next = 0) {
     constexpr int BN = 64 * WNB, NBW = WNB / 2;   // N blocks of 32 per wave
     constexpr int BDMA = b_bytes<BN>() / 4096;   // 1 KB sign-bit loads per wave and K step
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,6 +245,11 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int n
     }
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = a.K, nk = K / KT;
+    const bool ext = EXT && tn < next;   // uniform over the workgroup
+    const int wvu = __builtin_amdgcn_readfirstlane(wave);
+    uint8_t *const bx0 = reinterpret_cast<uint8_t *>(smem) + tile_smem<BN>();
+    const uint8_t *xsrc = nullptr;
+    if (EXT) xsrc = nar->sign + (int64_t)min(32 * tn + lr, nar->N - 1) * (K >> 3);
     const int kt0 = z * nk / splitk, kt1 = (z + 1) * nk / splitk;
     auto As = [&](int b) { return reinterpret_cast<int8_t *>(smem) + b * A_BYTES; };
     auto Bs = [&](int b) { return reinterpret_cast<uint8_t *>(smem) + 2 * A_BYTES + b * b_bytes<BN>(); };
@@ -259,6 +274,8 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int n
 #pragma unroll
         for (int c = 0; c < BDMA; ++c)
             lds_dma16(bsrc[c] + (k0 >> 3), Bs(buf) + 1024 * (4 * c + wave));
+        // ext: lane l writes the 16 bytes of column l & 31 (lanes 32..63 repeat 0..31)
+        if (EXT && ext && wvu == 0) lds_dma16(xsrc + (k0 >> 3), bx0 + 1024 * buf);
     };
     v16i acc[4][NBW];
 #pragma unroll
@@ -267,6 +284,9 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int n
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    v16i accx;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accx[r] = 0;
     dma(0, kt0 * KT);
     const bool early = a.rank <= kEarlyRank;
     char *epi = smem + (early ? main_lds<BN>() : 0);
@@ -289,6 +309,8 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int n
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
             bw[j] = *reinterpret_cast<const uint4 *>(Bs(cur) + (wn * (32 * NBW) + j * 32 + lr) * 16);
+        uint4 bwx = make_uint4(0u, 0u, 0u, 0u);
+        if (EXT && ext) bwx = *reinterpret_cast<const uint4 *>(bx0 + 1024 * cur + lr * 16);
         v4i af[2][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) af[0][i] = *reinterpret_cast<const v4i *>(abase + i * 32 * KT + (sx << 5));
@@ -310,6 +332,15 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int n
 #pragma unroll
                 for (int j = 0; j < NBW; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][i], bf[j], acc[i][j], 0, 0, 0);
+            if (EXT && ext) {   // the wave's rows 32 w .. 32 w + 31 are A fragment w
+                const v4i bfx = expand16((u4_get(bwx, s) >> (16 * hsel)) & 0xffffu);
+                switch (wvu) {
+                    case 0: accx = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][0], bfx, accx, 0, 0, 0); break;
+                    case 1: accx = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][1], bfx, accx, 0, 0, 0); break;
+                    case 2: accx = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][2], bfx, accx, 0, 0, 0); break;
+                    default: accx = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][3], bfx, accx, 0, 0, 0); break;
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -386,6 +417,15 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int n
         }
     };
     if (RES) load_res(0, rv[0]);
+    // ext block operands, loaded now so that their latency hides behind the main epilogue
+    LowrankOps<kLrQ> xops;
+    float scx = 0.f, usx = 0.f;
+    if (EXT && ext) {
+        const int nc = min(32 * tn + lr, nar->N - 1);
+        xops = lowrank_load<kLrQ>(*nar, m0 + 32 * wvu + lr, 32 * tn + lr, lane);
+        scx = half_bits_to_float(nar->row_scale[nc]);
+        usx = nar->up_scale[nc];
+    }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int i = it & 3, j = it >> 2;
@@ -458,6 +498,23 @@ __device__ __forceinline__ void gemm_tile_body(const GemmArgs &a, int ntm, int n
             }
         }
     }
+    if (EXT && ext) {
+        // the wave's ext block: rows m0 + 32 w + 8 (r >> 2) + 4 hsel + (r & 3), column 32 tn + lr of nar
+        const GemmArgs &b = *nar;
+        const int rl = 32 * wvu, n = 32 * tn + lr;
+        const v16f lacc = lowrank_mma<kLrQ>(b, xops, m0 + rl + lr, n, lane);
+        if (n < b.N) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ml = rl + 8 * (r >> 2) + 4 * hsel + (r & 3), m = m0 + ml;
+                if (m < b.M) {
+                    const int accv = 2 * accx[r] - q_l[ml];
+                    b.y[(int64_t)m * b.ldy + n] = s_l[ml] * scx * (float)accv + usx * lacc[r];
+                    if (b.acc_tap) b.acc_tap[(int64_t)m * b.ldacc + n] = accv;
+                }
+            }
+        }
+    }
 }
 
 template <int WNB, bool SPLIT, bool RES>
@@ -481,6 +538,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int bid = blockIdx.x;
     if (bid < nsmall) gemm_tile_body<2, true, false>(narrow, ntm_n, ntn_n, splitk_n, bid % tiles_n, bid / tiles_n, smem, last_flag);
     else gemm_tile_body<4, false, false>(wide, ntm_w, ntn_w, 1, bid - nsmall, 0, smem, last_flag);
+}
+
+// The same pair as one round of wide tiles: the narrow GEMM's 32-column blocks ride along the first
+// `next` column tiles (EXT), so no tile waits for a second round and no K range is split.
+constexpr int kExtLds = 2048;
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_tile_ext(
+    GemmArgs wide, int ntm_w, int ntn_w, GemmArgs narrow, int next) {
+    __shared__ __align__(16) char smem[tile_smem<256>() + kExtLds];
+    __shared__ int last_flag;
+    // the tiles that carry a narrow block (column tiles 0 .. next - 1) come first: tile order is
+    // row-fastest
+    gemm_tile_body<4, false, false, true>(wide, ntm_w, ntn_w, 1, blockIdx.x, 0, smem, last_flag, &narrow, next);
 }
 
 __global__ void k_clear_u32(uint32_t *p, int n) {
@@ -777,6 +846,11 @@ hipError_t launch_gemm_pm1_pair(const GemmArgs &wide, const GemmArgs &narrow, hi
     if (pw.wnb != 4 || pw.splitk != 1 || pn.wnb != 2 || pn.splitk < 2) {   // not the shapes the pair serves
         hipError_t e = launch_gemm_pm1(wide, stream);
         return e != hipSuccess ? e : launch_gemm_pm1(narrow, stream);
+    }
+    const int next = (narrow.N + 31) / 32;
+    if (narrow.M == wide.M && narrow.K == wide.K && narrow.rank == wide.rank && wide.N % 256 == 0 && next <= pw.ntn) {
+        k_gemm_tile_ext<<<pw.ntm * pw.ntn, kBlock, 0, stream>>>(wide, pw.ntm, pw.ntn, narrow, next);
+        return hipGetLastError();
     }
     const int tiles_n = pn.ntm * pn.ntn;
     if (!narrow.scratch || tiles_n * 4 > kCntBytes) return hipErrorInvalidValue;
