@@ -6,10 +6,11 @@
 //   1 k_tok_quant      per token: RMSNorm + int8 quantizer, int8 LoRA-down, t' split to bf16
 //   2 k_gemm_pm1       in_proj over all tokens (int8 MFMA) with the Eq. (3) epilogue -> Y
 //   3 k_conv_seq       causal conv over the sequence + SiLU (x, B, C); softplus(dt + dt_bias)
-//   4 (in k_ssd_cbm)   final conv state = the last d_conv-1 pre-activation inputs
+//   4 (C.B^T pass)     final conv state = the last d_conv-1 pre-activation inputs
 //   5 SSD, chunk length Q, Lam_t = sum_{tau <= t in chunk} dt_tau A (per head), MFMA:
-//       k_ssd_cbm      CB[t][s] = C_t . B_s for each chunk and group (shared by the group's heads)
-//       k_ssd_state    S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s per chunk, and Lam_end
+//     k_ssd_cbm_state, one launch of two independent passes:
+//       C.B^T          CB[t][s] = C_t . B_s for each chunk and group (shared by the group's heads)
+//       chunk state    S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s per chunk, and Lam_end
 //       k_ssd_scan     S_in(c) = state entering chunk c; S <- exp(Lam_end) S + S_loc (sequential in c)
 //       k_ssd_out      y = sum_{s <= t} exp(Lam_t - Lam_s) CB[t][s] dt_s x_s + exp(Lam_t) C_t . S_in
 //                      + D x; g = y * SiLU(z)
@@ -506,7 +507,7 @@ struct SsdArgs {
     float *sloc;           // [B][H][nch][P][N] chunk states (become the states entering each chunk)
     float *state;          // [B][H][P][N] initial -> final
     float *g;              // [M][E] gated output
-    float *conv_state;     // [B][Cd][3]: replaced by the last d_conv-1 pre-activation inputs (k_ssd_cbm)
+    float *conv_state;     // [B][Cd][3]: replaced by the last d_conv-1 pre-activation inputs (C.B^T pass)
 };
 
 constexpr int kSsdMaxQ = 256, kSsdMaxN = 256, kSsdP = 64, kSsdWaves = 8, kSsdBlock = 64 * kSsdWaves;
@@ -514,7 +515,8 @@ constexpr int kSsdMaxQ = 256, kSsdMaxN = 256, kSsdP = 64, kSsdWaves = 8, kSsdBlo
 typedef float f4v __attribute__((ext_vector_type(4)));
 // Chunked SSD in three passes, each over every (b, h, chunk) at once (Lam_t = inclusive cumsum of
 // dt A within the chunk; exponentials only of Lam differences, or of Lam itself, all <= 0):
-//   k_ssd_state  S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s of the chunk, and Lam_end
+//   k_ssd_cbm_state  S_loc = sum_s exp(Lam_end - Lam_s) dt_s x_s (x) B_s of the chunk, and Lam_end
+//                (beside the C.B^T pass, in the same launch)
 //   k_ssd_scan   S_in(c) = exp(Lam_end(c-1)) S_in(c-1) + S_loc(c-1), in place (sequential in c)
 //   k_ssd_out    y_t = sum_{s<=t} exp(Lam_t - Lam_s) CB[t][s] dt_s x_s + exp(Lam_t) C_t . S_in + D x_t,
 //                g = y SiLU(z)
@@ -630,12 +632,16 @@ __device__ __forceinline__ void ssd_x_store(const SsdXRegs &x, int len, const fl
 // the t-tile's C fragments are split once, each s-tile's B fragments as they load (the next
 // s-tile's loads in flight while one computes). Also the conv-state hand-off.
 constexpr int kCbmSplit = 2;   // workgroups per (chunk, t-tile): 9.0 -> 6.7 us (4: 9.3)
-__global__ __launch_bounds__(kSsdBlock) void k_ssd_cbm(SsdArgs a) {
+// Workgroup wg of the ncbm = (B G nch) x (Q / 16) x kCbmSplit of this pass (bgc fastest, then the
+// t-tile, then the split). NBM: 32-wide blocks of d_state held (N <= 32 NBM).
+template <int NBM>
+__device__ __forceinline__ void ssd_cbm_body(const SsdArgs &a, int wg, int ncbm) {
+    const int nbgc = a.B * a.G * a.nch, ntt = a.Q / 16;
+    const int bgc = wg % nbgc, ti = (wg / nbgc) % ntt, zsp = wg / (nbgc * ntt);
     {   // conv-state handoff, per (sequence, channel): new state[i] = element L + i of
         // [old state (3) | the sequence's conv inputs (L)] (the conv pass has read the old state)
-        const int nthr = gridDim.x * gridDim.y * gridDim.z * kSsdBlock;
-        for (int idx = ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * kSsdBlock + threadIdx.x;
-             idx < a.B * a.Cd; idx += nthr) {
+        const int nthr = ncbm * kSsdBlock;
+        for (int idx = wg * kSsdBlock + threadIdx.x; idx < a.B * a.Cd; idx += nthr) {
             const int bb = idx / a.Cd, ch = idx - bb * a.Cd;
             float *st = a.conv_state + (int64_t)idx * (kConvTaps - 1);
             float nv[kConvTaps - 1];
@@ -648,13 +654,11 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_cbm(SsdArgs a) {
             for (int i = 0; i < kConvTaps - 1; ++i) st[i] = nv[i];
         }
     }
-    const int bgc = blockIdx.x, c = bgc % a.nch, g = (bgc / a.nch) % a.G, b = bgc / (a.nch * a.G);
-    const int ti = blockIdx.y;
+    const int c = bgc % a.nch, g = (bgc / a.nch) % a.G, b = bgc / (a.nch * a.G);
     const int len = min(a.Q, a.L - c * a.Q);
-    if (ti * 16 >= len) return;   // no barriers in this kernel
+    if (ti * 16 >= len) return;   // no barriers in this pass
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, kq = lane >> 4;
     const int64_t mbase = (int64_t)b * a.L + c * a.Q;
-    constexpr int NBM = kSsdMaxN / 32;
     const int N = a.N, NB = (N + 31) / 32;
     // lane: row (C) / column (B) r of its tile, d_state indices 32 nb + 8 kq .. +8 (zero past N)
     auto load8 = [&](const float *row, int nb, float (&v)[8]) {
@@ -675,8 +679,8 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_cbm(SsdArgs a) {
         }
     }
     float *out = a.cb + (((int64_t)b * a.G + g) * a.nch + c) * a.Q * a.Q;
-    // the t-tile's s-tiles are spread over the gridDim.z workgroups of (chunk, t-tile) and their waves
-    for (int si = blockIdx.z * kSsdWaves + wave; si <= ti; si += kSsdWaves * gridDim.z) {
+    // the t-tile's s-tiles are spread over the kCbmSplit workgroups of (chunk, t-tile) and their waves
+    for (int si = zsp * kSsdWaves + wave; si <= ti; si += kSsdWaves * kCbmSplit) {
         const float *Brow = a.xbc + (mbase + min(si * 16 + r, len - 1)) * a.Cd + a.E + g * N;
         float bv[NBM][8];
 #pragma unroll
@@ -700,12 +704,12 @@ __global__ __launch_bounds__(kSsdBlock) void k_ssd_cbm(SsdArgs a) {
 // S_loc of one (b, h, chunk) = Xs . B with Xs[p][s] = exp(Lam_end - Lam_s) dt_s x_s (LDS planes)
 // and B[s][n] straight from global memory. Wave w takes the n-tiles w, w + 8, ... for all four
 // p-tiles, so each split B fragment feeds four p-tiles.
-// (two workgroups per compute unit: <= 128 registers)
-__global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_ssd_state(SsdArgs a) {
+// Workgroup blk of B H nch.
+__device__ __forceinline__ void ssd_state_body(const SsdArgs &a, int blk) {
     __shared__ float lam2[kSsdMaxQ], dts[kSsdMaxQ], tot[kSsdWaves];
     __shared__ __align__(16) __bf16 xh[kSsdP * kSsdRow], xl[kSsdP * kSsdRow];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, kq = lane >> 4;
-    const int c = blockIdx.x % a.nch, bh = blockIdx.x / a.nch, h = bh % a.H, b = bh / a.H;
+    const int c = blk % a.nch, bh = blk / a.nch, h = bh % a.H, b = bh / a.H;
     const int g = h * a.G / a.H, Q = a.Q, N = a.N, NT = N / 16;
     const int len = min(Q, a.L - c * Q);
     const int64_t mbase = (int64_t)b * a.L + c * Q;
@@ -763,6 +767,17 @@ __global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(4))) 
             for (int rr = 0; rr < 4; ++rr) out[(int64_t)(16 * pt + 4 * kq + rr) * N + nt * 16 + r] = acc[pt][rr];
     }
 #undef SSD_LOAD_B
+}
+
+// The two passes that need only the conv outputs, in one launch: the ncbm C.B^T workgroups first
+// (short), then the B H nch chunk-state workgroups, which take the slots the short ones free (one
+// launch of 6.8 + 19.7 us became one of about 20). Two workgroups per compute unit (<= 128 registers)
+// up to d_state 128; d_state 256 holds twice the C.B^T operands and runs one (no spills).
+template <int NBM>
+__global__ __launch_bounds__(kSsdBlock) __attribute__((amdgpu_waves_per_eu(NBM <= 4 ? 4 : 2))) void k_ssd_cbm_state(SsdArgs a, int ncbm) {
+    const int wg = blockIdx.x;
+    if (wg < ncbm) ssd_cbm_body<NBM>(a, wg, ncbm);
+    else ssd_state_body(a, wg - ncbm);
 }
 
 // Sequential carry over chunks; sloc[c] is replaced by the state entering chunk c. Chunks go in
@@ -1282,10 +1297,11 @@ hipError_t launch_layer_prefill(const Shape &s, const dfssm_layer_weights &w, co
         a.state = st.ssm;
         a.g = ws.gbuf;
         a.conv_state = st.conv;
-        k_ssd_cbm<<<dim3(batch * s.G * nch, chunk / 16, kCbmSplit), kSsdBlock, 0, stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int nblk = batch * s.H * nch;
-        k_ssd_state<<<nblk, kSsdBlock, 0, stream>>>(a);
+        const int nblk = batch * s.H * nch, ncbm = batch * s.G * nch * (chunk / 16) * kCbmSplit;
+        if (s.N <= 32) k_ssd_cbm_state<1><<<ncbm + nblk, kSsdBlock, 0, stream>>>(a, ncbm);
+        else if (s.N <= 64) k_ssd_cbm_state<2><<<ncbm + nblk, kSsdBlock, 0, stream>>>(a, ncbm);
+        else if (s.N <= 128) k_ssd_cbm_state<4><<<ncbm + nblk, kSsdBlock, 0, stream>>>(a, ncbm);
+        else k_ssd_cbm_state<8><<<ncbm + nblk, kSsdBlock, 0, stream>>>(a, ncbm);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (codec && codec->on) {
             e = launch_ssd_scan_codec(st.ssm, ws.sloc, ws.lam_end, batch * s.H, nch, s.N, s.P, codec->tap_pre,
