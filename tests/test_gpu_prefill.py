@@ -177,6 +177,24 @@ def test_prefill_1p3b_2048_tokens_bf16_chunk256():
     say(f"1p3b prefill: forced {errs}; free-running {fr:.2e} up to token {first}")
 
 
+def test_prefill_1p3b_two_ragged_sequences_nonzero_state():
+    """Two 1.3B-shaped sequences of 1,100 tokens (2,200 rows: the one-round in_proj GEMM with the
+    B|C|dt blocks riding along; the second sequence starts inside a 128-row tile) with nonzero initial
+    conv and SSM states, chunk 256, fp32 input: every token of both sequences and both final states."""
+    B, T = 2, 1100
+    lw = gen.layer_weights(BIG, 3, 7)
+    conv0, ssm0 = gen.initial_states(BIG, B, 3, 7, std=0.3)
+    xs = gen.token_inputs(BIG, (B, T), 7, tag=6)
+    say(f"case: 1.3B-shaped layer prefill, batch {B}, seqlen {T}, chunk 256, nonzero state, fp32 input")
+    out, tps, final = run_prefill(BIG, lw, xs, conv0, ssm0, 256)
+    dense = O.dense_signs(lw)
+    for b in range(B):
+        tb = {k: v[b] for k, v in tps.items()}
+        errs = check_sequence(lw, xs[b], conv0[b], ssm0[b], out[b], tb, (final[0][b], final[1][b]), dense,
+                              what=f"1p3b two sequences, row {b}")
+        say(f"1p3b two sequences row {b}: forced {errs}")
+
+
 def test_prefill_chunk_lengths_agree():
     """Every chunk length evaluates the same recurrence. The quantizer rounds half to even, so two
     correct evaluations that differ by rounding may pick different codes where u * 127 / max|u|
