@@ -265,14 +265,55 @@ struct ScanCodecArgs {
     float *tap_pre, *tap_in; // [nch][BH][64][N] or null
 };
 
+// A whole [64][N] block (one chunk's S_loc of a head) in flight at once: the loads of every tile
+// pass land in registers (rows kRpp apart, kT columns per pass), and later go to a [64][N + 1] LDS
+// array (odd stride: each lane then reads its own row without bank conflicts).
+template <int N>
+struct BlockRegs {
+    static constexpr int kLoads = (N / Tile<N>::kT) * (kCodecRows / Tile<N>::kRpp);
+    float4 v[kLoads];
+};
+template <int N>
+__device__ __forceinline__ void block_issue(const float *src, BlockRegs<N> &b) {
+    using T = Tile<N>;
+    const int rr0 = (int)threadIdx.x / T::kLpr, cc = ((int)threadIdx.x % T::kLpr) * 4;
+#pragma unroll
+    for (int c0 = 0; c0 < N / T::kT; ++c0)
+#pragma unroll
+        for (int p = 0; p < kCodecRows / T::kRpp; ++p)
+            b.v[c0 * (kCodecRows / T::kRpp) + p] =
+                *reinterpret_cast<const float4 *>(src + (int64_t)(p * T::kRpp + rr0) * N + c0 * T::kT + cc);
+}
+template <int N>
+__device__ __forceinline__ void block_to_lds(const BlockRegs<N> &b, float *full) {
+    using T = Tile<N>;
+    const int rr0 = (int)threadIdx.x / T::kLpr, cc = ((int)threadIdx.x % T::kLpr) * 4;
+#pragma unroll
+    for (int c0 = 0; c0 < N / T::kT; ++c0)
+#pragma unroll
+        for (int p = 0; p < kCodecRows / T::kRpp; ++p) {
+            const float4 v = b.v[c0 * (kCodecRows / T::kRpp) + p];
+            float *d = full + (p * T::kRpp + rr0) * (N + 1) + c0 * T::kT + cc;
+            d[0] = v.x;
+            d[1] = v.y;
+            d[2] = v.z;
+            d[3] = v.w;
+        }
+}
+
 template <int N>
 __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) {
 #pragma clang fp contract(off)
     using T = Tile<N>;
-    constexpr int K2 = codec_side(N) * codec_side(N), W = T::W;
     __shared__ float lds[T::kFloats];
+    // up to d_state 128 the next chunk's S_loc is in flight while the current chunk's state is
+    // coded (a whole block in registers: 128 more per lane); d_state 256 loads it pass by pass
+    constexpr bool kAhead = N <= 128;
+    __shared__ float full[kAhead ? kCodecRows * (N + 1) : 1];
     const int bh = blockIdx.x, lane = threadIdx.x;
     constexpr int64_t PN = (int64_t)kCodecRows * N;
+    BlockRegs<kAhead ? N : 16> nxt;
+    if constexpr (kAhead) block_issue<N>(a.sloc + (int64_t)bh * a.nch * PN, nxt);
     float S[N];
 #pragma unroll
     for (int c0 = 0; c0 < N; c0 += T::kT) {
@@ -316,45 +357,63 @@ __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) 
                 const float x = fminf(fmaxf(row_quotient(S[i] - lo, dv), 0.f), 1.f);
                 tm[i] = (int)rintf(x * 255.0f) - 128;
             }
-            uint32_t word[W];
-            int e = 0;
-#pragma unroll
-            for (int w = 0; w < W; ++w) word[w] = 0u;
+            // The field is only read back here, so the sigma-delta runs one step per value: with
+            // U = e + 127 in [0, 254] at a value's first cell, each of its c cells adds t (0..255)
+            // to U and emits a 1 exactly when U reaches 255 (then U -= 255), so the value's cells
+            // hold (U + c t) div 255 ones and leave U' = (U + c t) mod 255 -- the same bits' count
+            // as the cell-by-cell pass, without the 529-step chain.
+            const bool flat = !(sigma != 0.f);
+            uint32_t U = 127u;
 #pragma unroll
             for (int i = 0; i < N; ++i) {
-#pragma unroll
-                for (int cc = cell_begin<N>(i); cc < cell_begin<N>(i + 1); ++cc) {
-                    const int u = e + tm[i];
-                    const int neg = u >> 31;
-                    e = u - 127 + (neg & 255);
-                    word[cc >> 5] |= (uint32_t)neg & (1u << (cc & 31));
-                }
+                const uint32_t cells = (uint32_t)(cell_begin<N>(i + 1) - cell_begin<N>(i));
+                const uint32_t sum = U + cells * (uint32_t)(tm[i] + 128);
+                const uint32_t ones = sum / 255u;
+                U = sum - 255u * ones;
+                const float dens = (float)ones * (1.0f / (float)cells);
+                S[i] = flat ? mu : lo + span * dens;
             }
-            constexpr uint32_t kTailMask = (K2 & 31) ? ((1u << (K2 & 31)) - 1u) : 0xffffffffu;
-            const bool flat = !(sigma != 0.f);
-#pragma unroll
-            for (int w = 0; w < W; ++w) word[w] = flat ? 0u : (~word[w] & ((w == W - 1) ? kTailMask : 0xffffffffu));
-            row_decode<N>(word, mu, sigma, S);
         }
-        // S_loc of this chunk (read before its slot is overwritten), the entering state out, the carry
+        // S_loc of this chunk (loaded ahead; read before its slot is overwritten), the entering state
+        // out, the carry
         const float f = expf(a.lam_end[(int64_t)bh * a.nch + c]);
         float *sl = a.sloc + ((int64_t)bh * a.nch + c) * PN;
-#pragma unroll
-        for (int c0 = 0; c0 < N; c0 += T::kT) {
-            tile_load<N>(sl, 0, kCodecRows, c0, lds);
+        if constexpr (kAhead) {
+            block_to_lds<N>(nxt, full);
             __syncthreads();
-            float loc[T::kT];
+            float loc[N];
 #pragma unroll
-            for (int j = 0; j < T::kT; ++j) loc[j] = lds[lane * T::kStride + j];
-            __syncthreads();
+            for (int j = 0; j < N; ++j) loc[j] = full[lane * (N + 1) + j];
+            if (c + 1 < a.nch) block_issue<N>(sl + PN, nxt);
 #pragma unroll
-            for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
-            __syncthreads();
-            tile_store<N>(sl, 0, kCodecRows, c0, lds);
-            if (a.tap_in) tile_store<N>(a.tap_in + slot, 0, kCodecRows, c0, lds);
-            __syncthreads();
+            for (int c0 = 0; c0 < N; c0 += T::kT) {
 #pragma unroll
-            for (int j = 0; j < T::kT; ++j) S[c0 + j] = f * S[c0 + j] + loc[j];
+                for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
+                __syncthreads();
+                tile_store<N>(sl, 0, kCodecRows, c0, lds);
+                if (a.tap_in) tile_store<N>(a.tap_in + slot, 0, kCodecRows, c0, lds);
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < T::kT; ++j) S[c0 + j] = f * S[c0 + j] + loc[c0 + j];
+            }
+        } else {
+#pragma unroll
+            for (int c0 = 0; c0 < N; c0 += T::kT) {
+                tile_load<N>(sl, 0, kCodecRows, c0, lds);
+                __syncthreads();
+                float loc[T::kT];
+#pragma unroll
+                for (int j = 0; j < T::kT; ++j) loc[j] = lds[lane * T::kStride + j];
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
+                __syncthreads();
+                tile_store<N>(sl, 0, kCodecRows, c0, lds);
+                if (a.tap_in) tile_store<N>(a.tap_in + slot, 0, kCodecRows, c0, lds);
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < T::kT; ++j) S[c0 + j] = f * S[c0 + j] + loc[j];
+            }
         }
     }
 #pragma unroll
