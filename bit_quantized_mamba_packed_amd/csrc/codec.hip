@@ -252,7 +252,8 @@ __global__ __launch_bounds__(kCodecRows) void k_state_decode(const uint32_t *__r
 }
 
 // DF-SSD carry ([DF-SSM] §3.4, App. D: the codec at chunk boundaries of the chunked scan). One wave
-// per (sequence, head), one lane per state row (the head's 64 channels): S starts as the layer's
+// per R rows of a (sequence, head) -- every state row is coded on its own -- and one lane per state
+// row (the head's 64 channels): S starts as the layer's
 // state; for every chunk c the state entering it is S itself for c = 0 and codec(S) after that,
 // and it is written over sloc[c] (which held the chunk's own contribution S_loc, read first), then
 // S = exp(Lam_end(c)) * entering + S_loc(c); the state after the last chunk is the layer's new state.
@@ -265,34 +266,35 @@ struct ScanCodecArgs {
     float *tap_pre, *tap_in; // [nch][BH][64][N] or null
 };
 
-// A whole [64][N] block (one chunk's S_loc of a head) in flight at once: the loads of every tile
-// pass land in registers (rows kRpp apart, kT columns per pass), and later go to a [64][N + 1] LDS
-// array (odd stride: each lane then reads its own row without bank conflicts).
-template <int N>
+// A whole [R][N] block (R rows of one chunk's S_loc of a head) in flight at once: the loads of every
+// tile pass land in registers (rows kRpp apart, kT columns per pass), and later go to an [R][N + 1]
+// LDS array (odd stride: each lane then reads its own row without bank conflicts). R is a multiple
+// of kRpp; src points at the block's first row.
+template <int N, int R>
 struct BlockRegs {
-    static constexpr int kLoads = (N / Tile<N>::kT) * (kCodecRows / Tile<N>::kRpp);
+    static constexpr int kLoads = (N / Tile<N>::kT) * (R / Tile<N>::kRpp);
     float4 v[kLoads];
 };
-template <int N>
-__device__ __forceinline__ void block_issue(const float *src, BlockRegs<N> &b) {
+template <int N, int R>
+__device__ __forceinline__ void block_issue(const float *src, BlockRegs<N, R> &b) {
     using T = Tile<N>;
     const int rr0 = (int)threadIdx.x / T::kLpr, cc = ((int)threadIdx.x % T::kLpr) * 4;
 #pragma unroll
     for (int c0 = 0; c0 < N / T::kT; ++c0)
 #pragma unroll
-        for (int p = 0; p < kCodecRows / T::kRpp; ++p)
-            b.v[c0 * (kCodecRows / T::kRpp) + p] =
+        for (int p = 0; p < R / T::kRpp; ++p)
+            b.v[c0 * (R / T::kRpp) + p] =
                 *reinterpret_cast<const float4 *>(src + (int64_t)(p * T::kRpp + rr0) * N + c0 * T::kT + cc);
 }
-template <int N>
-__device__ __forceinline__ void block_to_lds(const BlockRegs<N> &b, float *full) {
+template <int N, int R>
+__device__ __forceinline__ void block_to_lds(const BlockRegs<N, R> &b, float *full) {
     using T = Tile<N>;
     const int rr0 = (int)threadIdx.x / T::kLpr, cc = ((int)threadIdx.x % T::kLpr) * 4;
 #pragma unroll
     for (int c0 = 0; c0 < N / T::kT; ++c0)
 #pragma unroll
-        for (int p = 0; p < kCodecRows / T::kRpp; ++p) {
-            const float4 v = b.v[c0 * (kCodecRows / T::kRpp) + p];
+        for (int p = 0; p < R / T::kRpp; ++p) {
+            const float4 v = b.v[c0 * (R / T::kRpp) + p];
             float *d = full + (p * T::kRpp + rr0) * (N + 1) + c0 * T::kT + cc;
             d[0] = v.x;
             d[1] = v.y;
@@ -301,7 +303,7 @@ __device__ __forceinline__ void block_to_lds(const BlockRegs<N> &b, float *full)
         }
 }
 
-template <int N>
+template <int N, int R>
 __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) {
 #pragma clang fp contract(off)
     using T = Tile<N>;
@@ -309,18 +311,21 @@ __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) 
     // up to d_state 128 the next chunk's S_loc is in flight while the current chunk's state is
     // coded (a whole block in registers: 128 more per lane); d_state 256 loads it pass by pass
     constexpr bool kAhead = N <= 128;
-    __shared__ float full[kAhead ? kCodecRows * (N + 1) : 1];
-    const int bh = blockIdx.x, lane = threadIdx.x;
+    __shared__ float full[kAhead ? R * (N + 1) : 1];
+    // rows [r0, r0 + R) of head bh; lanes past R repeat row R - 1's arithmetic and store nothing
+    constexpr int kParts = kCodecRows / R;
+    const int bh = blockIdx.x / kParts, r0 = (blockIdx.x % kParts) * R, lane = threadIdx.x;
+    const int row = lane < R ? lane : R - 1;
     constexpr int64_t PN = (int64_t)kCodecRows * N;
-    BlockRegs<kAhead ? N : 16> nxt;
-    if constexpr (kAhead) block_issue<N>(a.sloc + (int64_t)bh * a.nch * PN, nxt);
+    BlockRegs<kAhead ? N : 16, kAhead ? R : 16> nxt;
+    if constexpr (kAhead) block_issue<N, R>(a.sloc + (int64_t)bh * a.nch * PN + (int64_t)r0 * N, nxt);
     float S[N];
 #pragma unroll
     for (int c0 = 0; c0 < N; c0 += T::kT) {
-        tile_load<N>(a.state + bh * PN, 0, kCodecRows, c0, lds);
+        tile_load<N>(a.state + bh * PN, r0, R, c0, lds);
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < T::kT; ++j) S[c0 + j] = lds[lane * T::kStride + j];
+        for (int j = 0; j < T::kT; ++j) S[c0 + j] = lds[row * T::kStride + j];
         __syncthreads();
     }
     for (int c = 0; c < a.nch; ++c) {
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) 
 #pragma unroll
                 for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
                 __syncthreads();
-                tile_store<N>(a.tap_pre + slot, 0, kCodecRows, c0, lds);
+                tile_store<N>(a.tap_pre + slot, r0, R, c0, lds);
                 __syncthreads();
             }
         }
@@ -379,19 +384,19 @@ __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) 
         const float f = expf(a.lam_end[(int64_t)bh * a.nch + c]);
         float *sl = a.sloc + ((int64_t)bh * a.nch + c) * PN;
         if constexpr (kAhead) {
-            block_to_lds<N>(nxt, full);
+            block_to_lds<N, R>(nxt, full);
             __syncthreads();
             float loc[N];
 #pragma unroll
-            for (int j = 0; j < N; ++j) loc[j] = full[lane * (N + 1) + j];
-            if (c + 1 < a.nch) block_issue<N>(sl + PN, nxt);
+            for (int j = 0; j < N; ++j) loc[j] = full[row * (N + 1) + j];
+            if (c + 1 < a.nch) block_issue<N, R>(sl + PN + (int64_t)r0 * N, nxt);
 #pragma unroll
             for (int c0 = 0; c0 < N; c0 += T::kT) {
 #pragma unroll
                 for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
                 __syncthreads();
-                tile_store<N>(sl, 0, kCodecRows, c0, lds);
-                if (a.tap_in) tile_store<N>(a.tap_in + slot, 0, kCodecRows, c0, lds);
+                tile_store<N>(sl, r0, R, c0, lds);
+                if (a.tap_in) tile_store<N>(a.tap_in + slot, r0, R, c0, lds);
                 __syncthreads();
 #pragma unroll
                 for (int j = 0; j < T::kT; ++j) S[c0 + j] = f * S[c0 + j] + loc[c0 + j];
@@ -399,17 +404,17 @@ __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) 
         } else {
 #pragma unroll
             for (int c0 = 0; c0 < N; c0 += T::kT) {
-                tile_load<N>(sl, 0, kCodecRows, c0, lds);
+                tile_load<N>(sl, r0, R, c0, lds);
                 __syncthreads();
                 float loc[T::kT];
 #pragma unroll
-                for (int j = 0; j < T::kT; ++j) loc[j] = lds[lane * T::kStride + j];
+                for (int j = 0; j < T::kT; ++j) loc[j] = lds[row * T::kStride + j];
                 __syncthreads();
 #pragma unroll
                 for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
                 __syncthreads();
-                tile_store<N>(sl, 0, kCodecRows, c0, lds);
-                if (a.tap_in) tile_store<N>(a.tap_in + slot, 0, kCodecRows, c0, lds);
+                tile_store<N>(sl, r0, R, c0, lds);
+                if (a.tap_in) tile_store<N>(a.tap_in + slot, r0, R, c0, lds);
                 __syncthreads();
 #pragma unroll
                 for (int j = 0; j < T::kT; ++j) S[c0 + j] = f * S[c0 + j] + loc[j];
@@ -421,14 +426,20 @@ __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) 
 #pragma unroll
         for (int j = 0; j < T::kT; ++j) lds[lane * T::kStride + j] = S[c0 + j];
         __syncthreads();
-        tile_store<N>(a.state + bh * PN, 0, kCodecRows, c0, lds);
+        tile_store<N>(a.state + bh * PN, r0, R, c0, lds);
         __syncthreads();
     }
 }
 
 template <int N>
 hipError_t scan_codec_n(const ScanCodecArgs &a, hipStream_t stream) {
-    k_ssd_scan_codec<N><<<(unsigned)a.BH, kCodecRows, 0, stream>>>(a);
+    // one wave per kRpp rows while that fills more workgroups than the chip has compute units (the
+    // carry is bound by each row's serial arithmetic), else one wave per head
+    constexpr int kR = Tile<N>::kRpp;
+    if ((int64_t)a.BH * (kCodecRows / kR) <= 2048)
+        k_ssd_scan_codec<N, kR><<<(unsigned)(a.BH * (kCodecRows / kR)), kCodecRows, 0, stream>>>(a);
+    else
+        k_ssd_scan_codec<N, kCodecRows><<<(unsigned)a.BH, kCodecRows, 0, stream>>>(a);
     return hipGetLastError();
 }
 
