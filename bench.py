@@ -550,7 +550,7 @@ def run_dfssd_prefill(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> d
             "plain_ms": res["plain"], "codec_carry_ms": round(extra, 4),
             "stack": {"layers": nL, "ms_per_prefill": round(stack_ms, 3), "tokens_per_s": round(S / stack_ms * 1e3, 1)},
             "note": "codec carry = DF-SSD minus plain (the scan with 4096 state rows encoded and read back at "
-                    "each of 7 boundaries, one lane per row)"}
+                    "each of 7 boundaries, d_state / 32 lanes per row)"}
 
 
 def run_dfw_proj(args, dims, layers_np, layers, np, torch, gen, L, Dv) -> dict:

@@ -431,12 +431,174 @@ __global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec(ScanCodecArgs a) 
     }
 }
 
+// The same carry with a row's values split over lanes (d_state >= 64): L = N / 32 lanes per state
+// row, lane q of a row holding values [32 q, 32 q + 32), so a one-wave workgroup takes RW = 64 / L
+// rows of a head and each lane runs a quarter (L = 4) of the per-value code. The row's mu and sigma
+// keep their element order: the running sum passes from lane q to lane q + 1 after q's segment.
+// The sigma-delta's U at a segment's first value is (127 + sum of c t over the row's earlier values)
+// mod 255 -- the same U as the serial pass, from an exact integer prefix over the row's lanes. Every
+// value gets the arithmetic of the row kernel above, so the states are bit-identical to it.
+template <int N, int R>
+__device__ __forceinline__ void block_to_seg_lds(const BlockRegs<N, R> &b, float *full) {
+    using T = Tile<N>;
+    constexpr int RS = N + N / 32;   // one pad float per 32-value segment
+    const int rr0 = (int)threadIdx.x / T::kLpr, cc = ((int)threadIdx.x % T::kLpr) * 4;
+#pragma unroll
+    for (int c0 = 0; c0 < N / T::kT; ++c0)
+#pragma unroll
+        for (int p = 0; p < R / T::kRpp; ++p) {
+            const float4 v = b.v[c0 * (R / T::kRpp) + p];
+            float *d = full + (p * T::kRpp + rr0) * RS + c0 * (T::kT + 1) + cc;
+            d[0] = v.x;
+            d[1] = v.y;
+            d[2] = v.z;
+            d[3] = v.w;
+        }
+}
+template <int N, int R>
+__device__ __forceinline__ void seg_lds_store(float *dst, const float *full) {   // dst: the block's first row
+    using T = Tile<N>;
+    constexpr int RS = N + N / 32;
+    const int rr0 = (int)threadIdx.x / T::kLpr, cc = ((int)threadIdx.x % T::kLpr) * 4;
+#pragma unroll
+    for (int c0 = 0; c0 < N / T::kT; ++c0)
+#pragma unroll
+        for (int p = 0; p < R / T::kRpp; ++p) {
+            const float *d = full + (p * T::kRpp + rr0) * RS + c0 * (T::kT + 1) + cc;
+            *reinterpret_cast<float4 *>(dst + (int64_t)(p * T::kRpp + rr0) * N + c0 * T::kT + cc) =
+                make_float4(d[0], d[1], d[2], d[3]);
+        }
+}
+
+template <int N>
+__global__ __launch_bounds__(kCodecRows) void k_ssd_scan_codec_seg(ScanCodecArgs a) {
+#pragma clang fp contract(off)
+    static_assert(N >= 64 && Tile<N>::kT == 32, "segments of 32 values, one column tile each");
+    constexpr int L = N / 32, RW = kCodecRows / L, RS = N + L;
+    constexpr int K2 = codec_side(N) * codec_side(N), CMIN = K2 / N;
+    static_assert(K2 < (N << 5), "a value owns fewer than 32 cells");
+    __shared__ float full[RW * RS];
+    const int lane = threadIdx.x, q = lane % L, rl = lane / L;
+    const int bh = blockIdx.x / L, r0 = (blockIdx.x % L) * RW, i0 = 32 * q;
+    constexpr int64_t PN = (int64_t)kCodecRows * N;
+    float *seg = full + rl * RS + q * 33;
+    float S[32];
+    {
+        BlockRegs<N, RW> cur;
+        block_issue<N, RW>(a.state + bh * PN + (int64_t)r0 * N, cur);
+        block_to_seg_lds<N, RW>(cur, full);
+    }
+    BlockRegs<N, RW> nxt;
+    block_issue<N, RW>(a.sloc + (int64_t)bh * a.nch * PN + (int64_t)r0 * N, nxt);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 32; ++j) S[j] = seg[j];
+    __syncthreads();
+    for (int c = 0; c < a.nch; ++c) {
+        const int64_t slot = ((int64_t)c * a.BH + bh) * PN + (int64_t)r0 * N;
+        if (a.tap_pre) {
+#pragma unroll
+            for (int j = 0; j < 32; ++j) seg[j] = S[j];
+            __syncthreads();
+            seg_lds_store<N, RW>(a.tap_pre + slot, full);
+            __syncthreads();
+        }
+        if (c > 0) {
+            // mean in element order: L stages, stage s summing lane s's segment onto the sum of the
+            // values before it (the other lanes' results of that stage are not used)
+            float run = 0.f, tot = 0.f;
+#pragma unroll
+            for (int st = 0; st < L; ++st) {
+                float acc = run;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) acc = acc + S[j];
+                const float up = __shfl_up(acc, 1);
+                if (q == st + 1) run = up;
+                tot = acc;
+            }
+            const float mu = __shfl(tot, rl * L + L - 1) / (float)N;
+            float dd[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const float d = S[j] - mu;
+                dd[j] = d * d;
+            }
+            run = 0.f;
+#pragma unroll
+            for (int st = 0; st < L; ++st) {
+                float acc = run;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) acc = acc + dd[j];
+                const float up = __shfl_up(acc, 1);
+                if (q == st + 1) run = up;
+                tot = acc;
+            }
+            const float sigma = sqrtf(__shfl(tot, rl * L + L - 1) / (float)N);
+            const float lo = mu - 3.0f * sigma, span = 6.0f * sigma;
+            const RowDivisor dv = row_divisor(span);
+            uint32_t ct[32];
+            uint32_t part = 0u;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const float x = fminf(fmaxf(row_quotient(S[j] - lo, dv), 0.f), 1.f);
+                const uint32_t t = (uint32_t)(int)rintf(x * 255.0f);
+                const int i = i0 + j;
+                const uint32_t cells = (uint32_t)((i + 1) * K2) / N - (uint32_t)(i * K2) / N;
+                ct[j] = cells * t;
+                part += ct[j];
+            }
+            uint32_t incl = part;   // inclusive prefix of the row's per-lane sums
+#pragma unroll
+            for (int d = 1; d < L; d <<= 1) {
+                const uint32_t o = __shfl_up(incl, d);
+                if (q >= d) incl += o;
+            }
+            uint32_t U = (127u + (incl - part)) % 255u;
+            const bool flat = !(sigma != 0.f);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const int i = i0 + j;
+                const uint32_t cells = (uint32_t)((i + 1) * K2) / N - (uint32_t)(i * K2) / N;
+                const uint32_t sum = U + ct[j];
+                const uint32_t ones = sum / 255u;
+                U = sum - 255u * ones;
+                const float rc = cells == (uint32_t)CMIN ? 1.0f / (float)CMIN : 1.0f / (float)(CMIN + 1);
+                const float dens = (float)ones * rc;
+                S[j] = flat ? mu : lo + span * dens;
+            }
+        }
+        const float f = expf(a.lam_end[(int64_t)bh * a.nch + c]);
+        float *sl = a.sloc + ((int64_t)bh * a.nch + c) * PN + (int64_t)r0 * N;
+        block_to_seg_lds<N, RW>(nxt, full);
+        __syncthreads();
+        float loc[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) loc[j] = seg[j];
+        __syncthreads();
+        if (c + 1 < a.nch) block_issue<N, RW>(sl + PN, nxt);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) seg[j] = S[j];
+        __syncthreads();
+        seg_lds_store<N, RW>(sl, full);
+        if (a.tap_in) seg_lds_store<N, RW>(a.tap_in + slot, full);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 32; ++j) S[j] = f * S[j] + loc[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) seg[j] = S[j];
+    __syncthreads();
+    seg_lds_store<N, RW>(a.state + bh * PN + (int64_t)r0 * N, full);
+}
+
 template <int N>
 hipError_t scan_codec_n(const ScanCodecArgs &a, hipStream_t stream) {
-    // one wave per kRpp rows while that fills more workgroups than the chip has compute units (the
-    // carry is bound by each row's serial arithmetic), else one wave per head
+    // d_state >= 64: rows split over lanes; below: one lane per row, one wave per kRpp rows while
+    // that keeps to 2,048 workgroups (the carry is bound by each wave's arithmetic), else per head
     constexpr int kR = Tile<N>::kRpp;
-    if ((int64_t)a.BH * (kCodecRows / kR) <= 2048)
+    if constexpr (N >= 64)
+        k_ssd_scan_codec_seg<N><<<(unsigned)(a.BH * (N / 32)), kCodecRows, 0, stream>>>(a);
+    else if ((int64_t)a.BH * (kCodecRows / kR) <= 2048)
         k_ssd_scan_codec<N, kR><<<(unsigned)(a.BH * (kCodecRows / kR)), kCodecRows, 0, stream>>>(a);
     else
         k_ssd_scan_codec<N, kCodecRows><<<(unsigned)a.BH, kCodecRows, 0, stream>>>(a);

@@ -7,6 +7,8 @@
   - with the GPU's codes and its coded states forced in, the oracle's layer (DF-SSD, sequential)
     matches the outputs, the final conv/SSM states and the pre-codec states of every boundary to
     1e-3 (P2), and the codes are exact against the oracle quantizer of the GPU's own u (P1)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -90,6 +92,25 @@ def test_dfssd_tiny_ragged_two_sequences(chunk):
         check_codec_boundaries(pre[:, b:b + 1], ent[:, b:b + 1], ssm0[b:b + 1])
         check_forced(lw, xs[b], conv0[b], ssm0[b], out[b], {k: v[b] for k, v in tps.items()},
                      (final[0][b], final[1][b]), pre[:, b], ent[:, b], chunk, f"tiny chunk {chunk} b{b}")
+
+
+@pytest.mark.parametrize("d_state", [32, 64, 256])
+def test_dfssd_every_carry_geometry(d_state):
+    """The carry codes rows one lane per row below d_state 64 and splits each row over d_state / 32
+    lanes from 64 up (sums passed lane to lane, the sigma-delta start from a prefix): tiny layers
+    widened to those d_state, 3 chunks of 64 with a ragged last one, non-zero entering states."""
+    t = gen.DIMS["tiny"]
+    dims = dataclasses.replace(t, d_state=d_state, n_in_proj=2 * t.d_inner + 2 * t.ngroups * d_state + t.nheads)
+    lw = gen.layer_weights(dims, 0, seed=23, random_norms=True, per_channel_lora=True)
+    B, T, chunk = 2, 150, 64
+    xs = gen.token_inputs(dims, (B, T), 23, tag=5)
+    conv0, ssm0 = gen.initial_states(dims, B, 0, 23, std=0.2)
+    say(f"case: DF-SSD tiny layer d_state {d_state}, batch {B}, {T} tokens, chunk {chunk}")
+    out, tps, final, pre, ent = run_dfssd(dims, lw, xs, conv0, ssm0, chunk)
+    for b in range(B):
+        check_codec_boundaries(pre[:, b:b + 1], ent[:, b:b + 1], ssm0[b:b + 1])
+        check_forced(lw, xs[b], conv0[b], ssm0[b], out[b], {k: v[b] for k, v in tps.items()},
+                     (final[0][b], final[1][b]), pre[:, b], ent[:, b], chunk, f"d_state {d_state} b{b}")
 
 
 def test_dfssd_single_chunk_is_the_plain_prefill():
